@@ -1,0 +1,362 @@
+"""fp64 CPU oracle: three gate variants, three evaluation forms each, and one decode step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): plain numpy in float64,
+shared with nothing on the GPU side.
+
+Conventions, all fixed by "Scrivere meglio nella memoria: gate e delta rule",
+section "Superiore" of the introduction and section "Dimenticare: i gate":
+
+* the memory is ``S`` of shape ``[d_v, d_k]``, written as a sum of outer
+  products ``v k^T`` (rows = value channels, columns = key channels);
+* it is read *after* the write of token t: ``o_t = S_t q_t`` (the page defines
+  ``S_t`` as the memory after the first t tokens; the worked example of the
+  RetNet page starts its running totals at the first score, 6);
+* gates and the delta transition multiply ``S`` from the right, so each key
+  channel (column) decays at its own rate.
+
+Array layout (the same one the C ABI uses): ``q, k`` are ``[B, H, T, d_k]``,
+``v`` and the output ``o`` are ``[B, H, T, d_v]``, states are
+``[B, H, d_v, d_k]``. Every function returns ``(o, S_T)`` where ``S_T`` is the
+memory after the last token (equal to ``s0`` - or zeros - when T = 0).
+
+Variants (the transition table of section "Le ricorrenze come regressione
+online" of the same page):
+
+* retention (RetNet row, fixed per-head decay): ``S_t = g_h S_{t-1} + v_t k_t^T``
+  with ``g_h = exp(log_gamma[h])``;
+* GLA (diagonal data-dependent gate, one per key channel):
+  ``S_t = S_{t-1} Diag(alpha_t) + v_t k_t^T``, ``alpha_t = exp(log_alpha[..., t, :])``;
+* gated delta rule (Gated DeltaNet row):
+  ``S_t = S_{t-1} [alpha_t (I - beta_t k_t k_t^T)] + beta_t v_t k_t^T`` with a
+  scalar ``alpha_t = exp(log_alpha[..., t])`` and write strength ``beta_t``.
+
+Forms (RetNet page, section "RetNet: la retention e le sue tre forme", Fig.
+16.5): the recurrent form is the definition; the parallel ("quadratic") form
+and the chunkwise form must give the same numbers up to rounding.
+"""
+
+import numpy as np
+
+__all__ = [
+    "retention_recurrent",
+    "retention_quadratic",
+    "retention_chunkwise",
+    "gla_recurrent",
+    "gla_quadratic",
+    "gla_chunkwise",
+    "gdelta_recurrent",
+    "gdelta_quadratic",
+    "gdelta_chunkwise",
+    "decode_step",
+    "forward_substitution",
+]
+
+
+# --------------------------------------------------------------------------- helpers
+
+def _f64(*arrays):
+    return [None if a is None else np.asarray(a, dtype=np.float64) for a in arrays]
+
+
+def _init_state(q, v, s0):
+    """Zero memory (pure accumulation starts empty) unless a state is handed over."""
+    lead = q.shape[:-2]
+    dk, dv = q.shape[-1], v.shape[-1]
+    if s0 is None:
+        return np.zeros(lead + (dv, dk))
+    return np.array(s0, dtype=np.float64, copy=True)
+
+
+def _outer(v_t, k_t):
+    """The write ``v k^T`` of one token, batched over the leading axes."""
+    return v_t[..., :, None] * k_t[..., None, :]
+
+
+def _read(S, q_t):
+    """The readout ``S q`` of one token, batched over the leading axes."""
+    return np.einsum("...mc,...c->...m", S, q_t)
+
+
+def forward_substitution(L, R):
+    """Solve ``(I + L) X = R`` for X, with ``L`` strictly lower triangular.
+
+    Textbook forward substitution, one row at a time: every equation uses only
+    the solutions of the previous ones ("Scrivere meglio nella memoria",
+    section "Correggere: la delta rule", the triangular system of the WY
+    representation). ``L`` is ``[..., n, n]``, ``R`` is ``[..., n, m]``.
+    """
+    L = np.asarray(L, dtype=np.float64)
+    X = np.array(R, dtype=np.float64, copy=True)
+    n = L.shape[-1]
+    for i in range(n):
+        if i:
+            X[..., i, :] -= np.einsum("...j,...jm->...m", L[..., i, :i], X[..., :i, :])
+    return X
+
+
+# --------------------------------------------------------------------------- retention
+
+def _gamma_per_head(log_gamma, lead):
+    """Broadcast the per-head decay ``[H]`` against the leading axes ``[B, H]``."""
+    lg = np.asarray(log_gamma, dtype=np.float64)
+    return np.broadcast_to(lg, lead)
+
+
+def retention_recurrent(q, k, v, log_gamma, s0=None):
+    """Recurrent form (the definition): ``S_t = g S_{t-1} + v_t k_t^T``, ``o_t = S_t q_t``.
+
+    "Scrivere meglio nella memoria", section "Dimenticare: i gate", scalar
+    decay equation with the RetNet choice alpha_t = gamma fixed per head; the
+    RetNet page, section on retention, recurrent form (cost O(d^2) per token).
+    """
+    q, k, v = _f64(q, k, v)
+    S = _init_state(q, v, s0)
+    g = np.exp(_gamma_per_head(log_gamma, q.shape[:-2]))[..., None, None]
+    T = q.shape[-2]
+    o = np.zeros(v.shape)
+    for t in range(T):
+        S = g * S + _outer(v[..., t, :], k[..., t, :])
+        o[..., t, :] = _read(S, q[..., t, :])
+    return o, S
+
+
+def retention_quadratic(q, k, v, log_gamma, s0=None):
+    """Parallel form ``O = (Q K^T (.) D) V`` with ``D_ij = g^(i-j)`` for ``i >= j`` and 0 above.
+
+    The RetNet page, section on retention, parallel (training) form: D is a
+    causal mask whose entry for the pair (i, j) is g^(i-j). A handed-over
+    state adds its decayed readout ``g^(i+1) S_0 q_i`` (unrolling the
+    recurrence from ``S_0``); the final memory is the unrolled sum
+    ``S_T = g^T S_0 + sum_j g^(T-1-j) v_j k_j^T``.
+    """
+    q, k, v = _f64(q, k, v)
+    lead = q.shape[:-2]
+    T = q.shape[-2]
+    lg = _gamma_per_head(log_gamma, lead)[..., None, None]
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    dist = (i - j).astype(np.float64)
+    D = np.where(i >= j, np.exp(lg * np.maximum(dist, 0.0)), 0.0)
+    scores = np.einsum("...ic,...jc->...ij", q, k)
+    o = np.einsum("...ij,...jm->...im", scores * D, v)
+    S0 = _init_state(q, v, s0)
+    steps = np.arange(1, T + 1, dtype=np.float64)
+    lg1 = lg[..., 0, 0]
+    o += np.exp(lg1[..., None] * steps)[..., :, None] * np.einsum("...mc,...ic->...im", S0, q)
+    w_last = np.exp(lg1[..., None] * (T - 1 - np.arange(T, dtype=np.float64)))
+    S = np.exp(lg1 * T)[..., None, None] * S0 + np.einsum("...j,...jm,...jc->...mc", w_last, v, k)
+    return o, S
+
+
+def retention_chunkwise(q, k, v, log_gamma, chunk, s0=None):
+    """Chunkwise form: the parallel form inside each block of ``chunk`` tokens, the
+    recurrent form from one block to the next (the RetNet page, section on
+    retention, chunkwise form; Fig. 16.5 right panel). The last block may be
+    shorter (the worked example uses blocks of two over three scores).
+
+    Per block of n tokens with incoming memory ``S_in`` and local index i, j:
+    ``o_i = sum_{j<=i} g^(i-j) (q_i . k_j) v_j + g^(i+1) S_in q_i`` and
+    ``S_out = g^n S_in + sum_j g^(n-1-j) v_j k_j^T``.
+    """
+    q, k, v = _f64(q, k, v)
+    lead = q.shape[:-2]
+    T = q.shape[-2]
+    lg = _gamma_per_head(log_gamma, lead)
+    S = _init_state(q, v, s0)
+    o = np.zeros(v.shape)
+    for t0 in range(0, T, chunk):
+        n = min(chunk, T - t0)
+        Q, K, V = q[..., t0:t0 + n, :], k[..., t0:t0 + n, :], v[..., t0:t0 + n, :]
+        i = np.arange(n)[:, None]
+        j = np.arange(n)[None, :]
+        D = np.where(i >= j, np.exp(lg[..., None, None] * np.maximum(i - j, 0)), 0.0)
+        P = np.einsum("...ic,...jc->...ij", Q, K) * D
+        inner = np.exp(lg[..., None] * np.arange(1, n + 1))  # g^(i+1)
+        o[..., t0:t0 + n, :] = (np.einsum("...ij,...jm->...im", P, V)
+                                + inner[..., :, None] * np.einsum("...mc,...ic->...im", S, Q))
+        w = np.exp(lg[..., None] * (n - 1 - np.arange(n)))    # g^(n-1-j)
+        S = (np.exp(lg * n)[..., None, None] * S
+             + np.einsum("...j,...jm,...jc->...mc", w, V, K))
+    return o, S
+
+
+# --------------------------------------------------------------------------- GLA
+
+def gla_recurrent(q, k, v, log_alpha, s0=None):
+    """Recurrent form (the definition): ``S_t = S_{t-1} Diag(alpha_t) + v_t k_t^T``.
+
+    "Scrivere meglio nella memoria", section "Dimenticare: i gate", the
+    diagonal-gate equation of Gated Linear Attention: one gate per key channel,
+    multiplying from the right so that column c decays at rate alpha_{t,c}.
+    """
+    q, k, v, la = _f64(q, k, v, log_alpha)
+    S = _init_state(q, v, s0)
+    T = q.shape[-2]
+    o = np.zeros(v.shape)
+    for t in range(T):
+        S = S * np.exp(la[..., t, :])[..., None, :] + _outer(v[..., t, :], k[..., t, :])
+        o[..., t, :] = _read(S, q[..., t, :])
+    return o, S
+
+
+def gla_quadratic(q, k, v, log_alpha, s0=None):
+    """Parallel form of GLA, the recurrence unrolled over the whole sequence.
+
+    Unrolling the diagonal-gate recurrence ("Dimenticare: i gate": what is
+    written at step j reaches step t weighted by the product of the gates in
+    between) gives, per key channel c with ``B_t = sum_{r<=t} log alpha_r``:
+    ``o_t = sum_{j<=t} [sum_c q_tc k_jc exp(B_tc - B_jc)] v_j + S_0 (q_t (.) exp(B_t))``
+    and ``S_T = S_0 Diag(exp(B_{T-1})) + sum_j v_j (k_j (.) exp(B_{T-1} - B_j))^T``.
+    O(T^2 d) memory and time: for small T only.
+    """
+    q, k, v, la = _f64(q, k, v, log_alpha)
+    T = q.shape[-2]
+    Bc = np.cumsum(la, axis=-2)                                   # [..., T, dk]
+    diff = Bc[..., :, None, :] - Bc[..., None, :, :]              # [..., t, j, dk]
+    causal = (np.arange(T)[:, None] >= np.arange(T)[None, :])[..., None]
+    W = np.where(causal, np.exp(np.where(causal, diff, 0.0)), 0.0)
+    P = np.einsum("...tc,...jc,...tjc->...tj", q, k, W)
+    o = np.einsum("...tj,...jm->...tm", P, v)
+    S0 = _init_state(q, v, s0)
+    o += np.einsum("...mc,...tc->...tm", S0, q * np.exp(Bc))
+    if T == 0:
+        return o, S0
+    last = Bc[..., -1, :]
+    S = S0 * np.exp(last)[..., None, :] + np.einsum(
+        "...jm,...jc->...mc", v, k * np.exp(last[..., None, :] - Bc))
+    return o, S
+
+
+def gla_chunkwise(q, k, v, log_alpha, chunk, s0=None):
+    """Chunkwise GLA: parallel inside each block, the memory carried between blocks.
+
+    With local inclusive cumulative log-gates ``b_i`` (restarting at each block)
+    and the incoming memory ``S_in``:
+    ``o_i = sum_{j<=i} [sum_c q_ic k_jc exp(b_ic - b_jc)] v_j + S_in (q_i (.) exp(b_i))``,
+    ``S_out = S_in Diag(exp(b_{n-1})) + sum_j v_j (k_j (.) exp(b_{n-1} - b_j))^T``.
+    Every exponent used is <= 0 when the gates are <= 1.
+    """
+    q, k, v, la = _f64(q, k, v, log_alpha)
+    T = q.shape[-2]
+    S = _init_state(q, v, s0)
+    o = np.zeros(v.shape)
+    for t0 in range(0, T, chunk):
+        n = min(chunk, T - t0)
+        Q, K, V = q[..., t0:t0 + n, :], k[..., t0:t0 + n, :], v[..., t0:t0 + n, :]
+        b = np.cumsum(la[..., t0:t0 + n, :], axis=-2)
+        diff = b[..., :, None, :] - b[..., None, :, :]
+        causal = (np.arange(n)[:, None] >= np.arange(n)[None, :])[..., None]
+        W = np.where(causal, np.exp(np.where(causal, diff, 0.0)), 0.0)
+        P = np.einsum("...ic,...jc,...ijc->...ij", Q, K, W)
+        o[..., t0:t0 + n, :] = (np.einsum("...ij,...jm->...im", P, V)
+                                + np.einsum("...mc,...ic->...im", S, Q * np.exp(b)))
+        last = b[..., -1, :]
+        S = S * np.exp(last)[..., None, :] + np.einsum(
+            "...jm,...jc->...mc", V, K * np.exp(last[..., None, :] - b))
+    return o, S
+
+
+# --------------------------------------------------------------------------- gated delta rule
+
+def gdelta_recurrent(q, k, v, log_alpha, beta, s0=None):
+    """Recurrent form (the definition) of Gated DeltaNet.
+
+    "Scrivere meglio nella memoria", section "Unire oblio e correzione: Gated
+    DeltaNet": ``S_t = S_{t-1} [alpha_t (I - beta_t k_t k_t^T)] + beta_t v_t k_t^T``.
+    Written the way section "Correggere: la delta rule" reads it: first the
+    memory fades, ``S' = alpha_t S_{t-1}``; then it is queried with the current
+    key, ``v_bar = S' k_t``, and only the error is written:
+    ``S_t = S' + beta_t (v_t - v_bar) k_t^T``.
+    """
+    q, k, v, la, be = _f64(q, k, v, log_alpha, beta)
+    S = _init_state(q, v, s0)
+    T = q.shape[-2]
+    o = np.zeros(v.shape)
+    for t in range(T):
+        Sp = np.exp(la[..., t])[..., None, None] * S
+        v_bar = _read(Sp, k[..., t, :])
+        S = Sp + be[..., t][..., None, None] * _outer(v[..., t, :] - v_bar, k[..., t, :])
+        o[..., t, :] = _read(S, q[..., t, :])
+    return o, S
+
+
+def _gdelta_block(Q, K, V, la, be, S):
+    """One block of the gated delta rule in WY / pseudo-value form.
+
+    Section "Correggere: la delta rule" writes the DeltaNet memory as a sum of
+    outer products of pseudo-values, ``S_t = sum_{i<=t} u_i k_i^T`` with
+    ``u_t = beta_t (v_t - sum_{i<t} u_i (k_i^T k_t))``: one triangular system per
+    block, only the end-of-block memory passing on. Section "Unire oblio e
+    correzione" says Gated DeltaNet extends the same representation; with the
+    local cumulative log-decay ``G_i = sum_{r<=i} log alpha_r`` the extension is
+
+      S_i = e^{G_i} S_in + sum_{j<=i} e^{G_i - G_j} u_j k_j^T,
+      u_i = beta_i (v_i - e^{G_i} S_in k_i - sum_{j<i} e^{G_i - G_j} (k_j . k_i) u_j),
+
+    i.e. ``(I + A) U = diag(beta) (V - diag(e^G) K S_in^T)`` with
+    ``A = strictly_lower(diag(beta) (K K^T (.) Gamma))``, ``Gamma_ij = e^{G_i - G_j}``;
+    then ``o_i = e^{G_i} S_in q_i + sum_{j<=i} Gamma_ij (q_i . k_j) u_j`` and
+    ``S_out = e^{G_{n-1}} S_in + sum_j e^{G_{n-1} - G_j} u_j k_j^T``.
+    """
+    n = Q.shape[-2]
+    G = np.cumsum(la, axis=-1)                                     # [..., n]
+    idx = np.arange(n)
+    lower_strict = idx[:, None] > idx[None, :]
+    lower = idx[:, None] >= idx[None, :]
+    gdiff = G[..., :, None] - G[..., None, :]
+    Gamma = np.where(lower, np.exp(np.where(lower, gdiff, 0.0)), 0.0)
+    KK = np.einsum("...ic,...jc->...ij", K, K)
+    A = np.where(lower_strict, be[..., :, None] * KK * Gamma, 0.0)
+    eG = np.exp(G)
+    R = be[..., :, None] * (V - eG[..., :, None] * np.einsum("...mc,...ic->...im", S, K))
+    U = forward_substitution(A, R)
+    QK = np.einsum("...ic,...jc->...ij", Q, K)
+    O = eG[..., :, None] * np.einsum("...mc,...ic->...im", S, Q) + np.einsum(
+        "...ij,...jm->...im", QK * Gamma, U)
+    w = np.exp(G[..., -1:] - G)                                    # e^{G_{n-1} - G_j}
+    S_out = eG[..., -1][..., None, None] * S + np.einsum("...j,...jm,...jc->...mc", w, U, K)
+    return O, S_out
+
+
+def gdelta_quadratic(q, k, v, log_alpha, beta, s0=None):
+    """Parallel form of the gated delta rule: the WY block taken over the whole sequence.
+
+    One triangular system of size T (O(T^2 d)); for small T only.
+    """
+    q, k, v, la, be = _f64(q, k, v, log_alpha, beta)
+    S = _init_state(q, v, s0)
+    if q.shape[-2] == 0:
+        return np.zeros(v.shape), S
+    return _gdelta_block(q, k, v, la, be, S)
+
+
+def gdelta_chunkwise(q, k, v, log_alpha, beta, chunk, s0=None):
+    """Chunkwise gated delta rule: one WY block per ``chunk`` tokens, the end-of-block
+    memory handed to the next block ("Correggere: la delta rule": only the
+    memory at the end of a block passes to the following one)."""
+    q, k, v, la, be = _f64(q, k, v, log_alpha, beta)
+    T = q.shape[-2]
+    S = _init_state(q, v, s0)
+    o = np.zeros(v.shape)
+    for t0 in range(0, T, chunk):
+        sl = slice(t0, min(T, t0 + chunk))
+        O, S = _gdelta_block(q[..., sl, :], k[..., sl, :], v[..., sl, :],
+                             la[..., sl], be[..., sl], S)
+        o[..., sl, :] = O
+    return o, S
+
+
+# --------------------------------------------------------------------------- decode
+
+def decode_step(q, k, v, alpha, s):
+    """One token of generation with a per-key-channel gate (GLA row; a scalar decay is
+    the constant gate): ``S <- S Diag(alpha)``, ``S <- S + v k^T``, ``o = S q``.
+
+    The RetNet page, section on retention, recurrent form: generation costs the
+    same two gestures for every token, at constant memory. ``q, k, alpha`` are
+    ``[N, H, d_k]``, ``v`` is ``[N, H, d_v]``, ``s`` is ``[N, H, d_v, d_k]``.
+    Returns ``(o, s_new)``; the input state is not modified.
+    """
+    q, k, v, a, s = _f64(q, k, v, alpha, s)
+    S = s * a[..., None, :] + _outer(v, k)
+    return _read(S, q), S
