@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked forward on one MI355X, with its roofline and the CPU oracle beside it.
+
+A step is one call of the chunked forward (every stage of the hot path: staging,
+the decayed triangle, the memory readout, the carried memory, the stores) over
+one batch of the multi-scale retention workload: B=4, H=8, T=2048,
+d_k=d_v=128, bf16 q/k/v ~ N(0,1)/sqrt(128), per-head decay 1 - 2^(-5-h),
+chunk 64, fp32 memory. Inputs are resident in HBM before timing; five input
+sets are rotated so the 256 MB Infinity Cache cannot serve them.
+
+Printed: one JSON line. ``value`` is tokens/s (B*H*T per second); ``roofline``
+prices the kernel against HBM (its arithmetic intensity, 96 flop/byte, is below
+the MI355X ridge); ``mfma`` gives the same run against the dense bf16 MFMA peak;
+``cpu_baseline`` times the fp64 oracle on the host; ``others`` reports the
+per-channel-gate (GLA), gated-delta and decode workloads measured the same way.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
+N_SETS = 5                      # rotated input sets (> 256 MB Infinity Cache for the retention batch)
+
+MAIN = "retention_b4h8_t2048_d128"
+
+
+def algorithmic_counts(kind, B, H, T, d, chunk, elem_bytes=2):
+    """Algorithmic flops and HBM bytes of one chunked-forward launch.
+
+    Bytes: read q, k, v (and the gates), write o and the final memory.
+    Flops per token-head (chunk C, head size d): retention and GLA 4Cd + 4d^2
+    (q.k^T and P.V over the C x C block, S q and k^T v); the gated delta rule
+    8Cd + 6d^2 + 2C^2/3 (K K^T, Q K^T, T.R for W and U0, P.U, W S^T, Q S^T,
+    U^T K and the triangular solve)."""
+    th = B * H * T
+    tok_bytes = 4 * d * elem_bytes
+    gate_bytes = {"retention": 0, "gla": 4 * d, "gdelta": 8}[kind]
+    state_bytes = B * H * d * d * 4
+    bytes_ = th * (tok_bytes + gate_bytes) + state_bytes
+    if kind == "gdelta":
+        flops = th * (8 * chunk * d + 6 * d * d + 2 * chunk * chunk / 3)
+    else:
+        flops = th * (4 * chunk * d + 4 * d * d)
+    return flops, bytes_
+
+
+def upload(w, torch, dev):
+    def t(x, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt).contiguous()
+    st = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = {"q": t(w.q, st), "k": t(w.k, st), "v": t(w.v, st)}
+    if w.log_gamma is not None:
+        d["log_gamma"] = t(w.log_gamma)
+    if w.log_alpha is not None:
+        d["log_alpha"] = t(w.log_alpha)
+    if w.beta is not None:
+        d["beta"] = t(w.beta)
+    return d
+
+
+def make_call(kind, api, bufs, chunk, torch):
+    q = bufs["q"]
+    B, H, T, d = q.shape
+    o = torch.empty((B, H, T, bufs["v"].shape[-1]), dtype=q.dtype, device=q.device)
+    s_out = torch.empty((B, H, bufs["v"].shape[-1], d), dtype=torch.float32, device=q.device)
+    if kind == "retention":
+        return lambda: api.la_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_gamma"], chunk=chunk, o=o, s_out=s_out)
+    if kind == "gla":
+        return lambda: api.gla_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_alpha"], chunk=chunk, o=o, s_out=s_out)
+    return lambda: api.gdelta_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_alpha"], bufs["beta"], chunk=chunk,
+                                        o=o, s_out=s_out)
+
+
+def time_calls(calls, steps, warmup, torch):
+    """Run ``warmup`` untimed steps, then ``steps`` timed ones rotating over ``calls``.
+
+    Returns (wall ms per step over the bracketed region, mean kernel ms from per-launch
+    HIP events recorded on the launching stream)."""
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    region0.record()
+    for i in range(steps):
+        starts[i].record()
+        calls[i % len(calls)]()
+        ends[i].record()
+    region1.record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return region0.elapsed_time(region1) / steps, float(np.mean(per))
+
+
+def bench_chunk(name, steps, warmup, torch, api, synthetic, dev, n_sets=N_SETS):
+    c = synthetic.CONFIGS[name]
+    sets = []
+    for s in range(n_sets):
+        w = synthetic.config_inputs(name) if s == 0 else None
+        if s > 0:
+            # further sets: the same recipe with the next seeds (same shapes and distributions)
+            base = dict(c)
+            kind = base.pop("kind")
+            seed = base.pop("seed") + 1000 * s
+            fn = {"retention": synthetic.retention_inputs, "gla": synthetic.gla_inputs,
+                  "gdelta": synthetic.gdelta_inputs}[kind]
+            kw = dict(chunk=base["chunk"], dtype=base["dtype"], seed=seed)
+            w = fn(base["B"], base["H"], base["T"], base["dk"], base["dv"], **kw)
+        sets.append(make_call(c["kind"], api, upload(w, torch, dev), c["chunk"], torch))
+        del w
+    ms_wall, ms_kernel = time_calls(sets, steps, warmup, torch)
+    flops, bytes_ = algorithmic_counts(c["kind"], c["B"], c["H"], c["T"], c["dk"], c["chunk"])
+    tokens = c["B"] * c["H"] * c["T"]
+    return dict(
+        workload=name, ms_per_step=ms_wall, kernel_ms=ms_kernel, tokens_per_s=tokens / (ms_wall * 1e-3),
+        alg_gbytes=bytes_ / 1e9, alg_gflop=flops / 1e9,
+        hbm_gbs=bytes_ / (ms_kernel * 1e-3) / 1e9, mfma_tflops=flops / (ms_kernel * 1e-3) / 1e12)
+
+
+def bench_decode(steps_total, torch, api, synthetic, dev):
+    """The decode workload: 512 sequences x 32 heads, d = 128, fp32 memory, a fresh bf16 token
+    and gate per step; ``steps_total`` consecutive steps timed as one region."""
+    c = synthetic.CONFIGS["decode_n512h32_d128"]
+    N, H, d = c["N"], c["H"], c["dk"]
+    w = synthetic.decode_inputs(N, H, d, d, steps=0, seed=c["seed"])
+    s = torch.from_numpy(w.s0).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(c["seed"])
+    scale = 1.0 / np.sqrt(d)
+    q = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    k = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    v = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    a = torch.sigmoid(torch.randn((steps_total, N, H, d), generator=gen, device=dev) + 2.0)
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+    for i in range(3):
+        api.la_recurrent_step(q[i], k[i], v[i], a[i], s, o=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps_total):
+        api.la_recurrent_step(q[i], k[i], v[i], a[i], s, o=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps_total
+    bytes_step = N * H * (2 * d * d * 4 + 3 * d * 2 + d * 4 + d * 2)
+    return dict(workload="decode_n512h32_d128", steps=steps_total, us_per_step=ms * 1e3,
+                hbm_gbs=bytes_step / (ms * 1e-3) / 1e9, hbm_frac=bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                alg_bytes_per_step=bytes_step)
+
+
+def cpu_baseline(synthetic, budget_s=12.0):
+    """The fp64 oracle (chunkwise form) on the host: whole retention batches of the timed
+    workload, repeated until ``budget_s`` has elapsed. numpy's einsum runs on one thread."""
+    import oracle
+    w = synthetic.config_inputs(MAIN)
+    c = synthetic.CONFIGS[MAIN]
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        for b in range(c["B"]):
+            oracle.retention_chunkwise(w.q[b:b + 1], w.k[b:b + 1], w.v[b:b + 1], w.log_gamma, c["chunk"])
+            done += c["H"] * c["T"]
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 chunkwise retention oracle on {done // (c['H'] * c['T'])} batch rows of "
+                      f"{MAIN} (H={c['H']}, T={c['T']}, d=128) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-others", action="store_true", help="skip the GLA, gated-delta and decode workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the recurrences shard over (batch, head) with no "
+              "communication, so only --gpus 1 is run here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_linear_recurrences_amd import api, synthetic
+    dev = "cuda"
+    torch.cuda.set_device(0)
+
+    main_r = bench_chunk(MAIN, args.steps, args.warmup, torch, api, synthetic, dev)
+    others = {}
+    if not args.no_others:
+        for name in ("gla_b8h16_t4096_d128", "gdelta_b4h16_t8192_d128"):
+            r = bench_chunk(name, max(20, args.steps // 4), max(3, args.warmup // 4), torch, api, synthetic, dev,
+                            n_sets=1)
+            r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
+            r["mfma_frac"] = r["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS
+            others[name] = r
+            torch.cuda.empty_cache()
+        others["decode_n512h32_d128"] = bench_decode(args.decode_steps, torch, api, synthetic, dev)
+        torch.cuda.empty_cache()
+
+    cfg = synthetic.CONFIGS[MAIN]
+    out = {
+        "metric": "chunked fwd tokens/s (B·H·T/s) + % bf16 MFMA peak; decode step HBM GB/s",
+        "value": main_r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": MAIN, "B": cfg["B"], "H": cfg["H"], "T": cfg["T"], "d_k": cfg["dk"],
+                   "d_v": cfg["dv"], "chunk": cfg["chunk"], "decay": "1 - 2^(-5-h)", "state": "fp32",
+                   "input_sets_rotated": N_SETS},
+        "roofline": {"bound": "hbm", "achieved": main_r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": main_r["hbm_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel_ms": main_r["kernel_ms"], "alg_bytes_per_launch": main_r["alg_gbytes"] * 1e9},
+        "mfma": {"achieved": main_r["mfma_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": main_r["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                 "alg_flop_per_launch": main_r["alg_gflop"] * 1e9},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(synthetic)
+    if others:
+        out["others"] = others
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,70 @@
+"""ctypes loader for ``libglr.so`` (the C ABI declared in ``include/glr.h``).
+
+The library must have been built in-tree (``gated_linear_recurrences_amd.build``);
+there is no fallback path: loading fails loudly when it is missing.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libglr.so")
+
+LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
+LA_F32, LA_BF16 = 0, 1
+
+EXPORTED = (
+    "la_chunk_fwd",
+    "gla_chunk_fwd",
+    "gdelta_chunk_fwd",
+    "la_recurrent_step",
+    "la_status_str",
+    "la_last_error",
+    "la_version",
+)
+
+_lib = None
+
+
+class GLRError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+def load():
+    """Load (once) and return the library with its argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m gated_linear_recurrences_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    chunk = [P, P, P, F, F, P, F, I, I, I, I, I, I, I, P]
+    lib.la_chunk_fwd.argtypes = chunk
+    lib.gla_chunk_fwd.argtypes = chunk
+    lib.gdelta_chunk_fwd.argtypes = [P, P, P, F, F, F, P, F, I, I, I, I, I, I, I, P]
+    lib.la_recurrent_step.argtypes = [P, P, P, F, F, P, I, I, I, I, I, P]
+    for name in ("la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.la_status_str.argtypes = [ctypes.c_int]
+    lib.la_status_str.restype = ctypes.c_char_p
+    lib.la_last_error.argtypes = []
+    lib.la_last_error.restype = ctypes.c_char_p
+    lib.la_version.argtypes = []
+    lib.la_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def check(status):
+    """Raise GLRError for a non-OK status, with the library's message."""
+    if status != LA_OK:
+        lib = load()
+        msg = lib.la_status_str(status).decode()
+        detail = lib.la_last_error().decode()
+        raise GLRError(status, f"{msg}: {detail}")

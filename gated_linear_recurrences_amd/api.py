@@ -1,0 +1,131 @@
+"""Python binding of the C ABI with the same entry-point names.
+
+Argument marshalling only: shape and dtype checks, output allocation through
+PyTorch (device memory and streams are PyTorch's), and one call into
+``libglr.so`` on the current HIP stream. Every step of the computation runs
+in the library's kernels.
+"""
+
+import ctypes
+
+import torch
+
+from . import _native
+
+__all__ = ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"]
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return _native.LA_BF16
+    if t.dtype == torch.float32:
+        return _native.LA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _chunk_common(q, k, v, s0, o, s_out, return_state):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d_k]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    _require(q, "q", (B, H, T, dk), q.dtype, dev)
+    _require(k, "k", (B, H, T, dk), q.dtype, dev)
+    _require(v, "v", (B, H, T, dv), q.dtype, dev)
+    if s0 is not None:
+        _require(s0, "s0", (B, H, dv, dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", (B, H, T, dv), q.dtype, dev)
+    if s_out is None and return_state:
+        s_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    elif s_out is not None:
+        _require(s_out, "s_out", (B, H, dv, dk), torch.float32, dev)
+    return (B, H, T, dk, dv), o, s_out
+
+
+def la_chunk_fwd(q, k, v, log_gamma, chunk=64, s0=None, o=None, s_out=None, return_state=True):
+    """Retention with a fixed decay per head: S_t = gamma_h S_{t-1} + v_t k_t^T, o_t = S_t q_t.
+
+    q, k [B,H,T,d_k], v [B,H,T,d_v] (bf16 or fp32); log_gamma [H] fp32. Returns (o, s_out)."""
+    (B, H, T, dk, dv), o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    _require(log_gamma, "log_gamma", (H,), torch.float32, q.device)
+    lib = _native.load()
+    _native.check(lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(s0), _ptr(o),
+                                   _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q), _stream(q.device)))
+    return o, s_out
+
+
+def gla_chunk_fwd(q, k, v, log_alpha, chunk=64, s0=None, o=None, s_out=None, return_state=True):
+    """Gated linear attention: S_t = S_{t-1} Diag(alpha_t) + v_t k_t^T, o_t = S_t q_t.
+
+    log_alpha [B,H,T,d_k] fp32 (log of the per-key-channel gates). Returns (o, s_out)."""
+    (B, H, T, dk, dv), o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    _require(log_alpha, "log_alpha", (B, H, T, dk), torch.float32, q.device)
+    lib = _native.load()
+    _native.check(lib.gla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(s0), _ptr(o),
+                                    _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q), _stream(q.device)))
+    return o, s_out
+
+
+def gdelta_chunk_fwd(q, k, v, log_alpha, beta, chunk=64, s0=None, o=None, s_out=None, return_state=True):
+    """Gated delta rule: S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
+
+    log_alpha, beta [B,H,T] fp32. Returns (o, s_out)."""
+    (B, H, T, dk, dv), o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    _require(log_alpha, "log_alpha", (B, H, T), torch.float32, q.device)
+    _require(beta, "beta", (B, H, T), torch.float32, q.device)
+    lib = _native.load()
+    _native.check(lib.gdelta_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0),
+                                       _ptr(o), _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q),
+                                       _stream(q.device)))
+    return o, s_out
+
+
+def la_recurrent_step(q, k, v, alpha, s, o=None):
+    """One decode token, in place on s: S <- S Diag(alpha); S <- S + v k^T; o = S q.
+
+    q, k [N,H,d_k], v [N,H,d_v] (bf16 or fp32); alpha [N,H,d_k] fp32; s [N,H,d_v,d_k] fp32."""
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    _require(k, "k", (N, H, dk), q.dtype, dev)
+    _require(v, "v", (N, H, dv), q.dtype, dev)
+    _require(alpha, "alpha", (N, H, dk), torch.float32, dev)
+    _require(s, "s", (N, H, dv, dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", (N, H, dv), q.dtype, dev)
+    lib = _native.load()
+    _native.check(lib.la_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s), _ptr(o),
+                                        N, H, dk, dv, _dtype_code(q), _stream(dev)))
+    return o

@@ -1,0 +1,8 @@
+// bf16 MFMA chunk kernels, gla instantiations (kernel template in chunk_bf16.hpp).
+#include "chunk_bf16.hpp"
+
+namespace glr {
+hipError_t launch_chunk_bf16_gla(const ChunkArgs& a, hipStream_t stream) {
+    return bf16k::launch_variant<kGLA>(a, stream);
+}
+}  // namespace glr

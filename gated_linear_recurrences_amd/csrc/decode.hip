@@ -1,0 +1,88 @@
+// Single-token decode: S <- S Diag(alpha); S <- S + v k^T; o = S q.
+//
+// The recurrent form of retention ("Le architetture lineari: RetNet, RWKV,
+// xLSTM", section "RetNet: la retention e le sue tre forme"): every token costs
+// the same two gestures on a memory of constant size. With a gate per key
+// channel this is the GLA row of the transition table ("Scrivere meglio nella
+// memoria", section "Le ricorrenze come regressione online").
+//
+// The step is a pure stream of the fp32 memory: 2 * d_v * d_k * 4 bytes per
+// (sequence, head) against ~5 d_v d_k flops, far below the machine balance, so
+// the design goal is HBM bandwidth: one workgroup per (sequence, head), 16-byte
+// coalesced non-temporal loads/stores of S, each row of S owned by a group of
+// d_k/4 lanes that reduce the readout with cross-lane shuffles.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace glr {
+
+namespace {
+
+constexpr int kDecodeThreads = 256;
+
+template <typename TS, int DK>
+__global__ __launch_bounds__(kDecodeThreads)
+void decode_step_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v,
+                        const float* __restrict__ alpha, float* __restrict__ s, TS* __restrict__ o,
+                        int dv) {
+    constexpr int kLanesPerRow = DK / 4;                      // each lane owns 4 key channels
+    constexpr int kRowsPerPass = kDecodeThreads / kLanesPerRow;
+    const int64_t pair = blockIdx.x;                          // (sequence, head)
+    const int tid = threadIdx.x;
+    const int c0 = (tid % kLanesPerRow) * 4;
+    const int row = tid / kLanesPerRow;
+
+    const int64_t tok_k = pair * DK;
+    float qc[4], kc[4], ac[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        qc[e] = Store<TS>::load(q, tok_k + c0 + e);
+        kc[e] = Store<TS>::load(k, tok_k + c0 + e);
+    }
+    const f32x4 a4 = *reinterpret_cast<const f32x4*>(alpha + tok_k + c0);
+    ac[0] = a4[0]; ac[1] = a4[1]; ac[2] = a4[2]; ac[3] = a4[3];
+
+    float* S = s + pair * static_cast<int64_t>(dv) * DK;
+    const int64_t tok_v = pair * dv;
+    for (int m = row; m < dv; m += kRowsPerPass) {
+        f32x4* p = reinterpret_cast<f32x4*>(S + static_cast<int64_t>(m) * DK + c0);
+        f32x4 x = __builtin_nontemporal_load(p);
+        const float vm = Store<TS>::load(v, tok_v + m);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = x[e] * ac[e] + vm * kc[e];
+            dot += x[e] * qc[e];
+        }
+        __builtin_nontemporal_store(x, p);
+        dot = group_sum<kLanesPerRow>(dot);
+        if ((tid % kLanesPerRow) == 0) Store<TS>::store(o, tok_v + m, dot);
+    }
+}
+
+template <typename TS>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+    const int64_t pairs = static_cast<int64_t>(a.N) * a.H;
+    if (pairs == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(pairs)), block(kDecodeThreads);
+    const TS* q = static_cast<const TS*>(a.q);
+    const TS* k = static_cast<const TS*>(a.k);
+    const TS* v = static_cast<const TS*>(a.v);
+    TS* o = static_cast<TS*>(a.o);
+    switch (a.dk) {
+        case 16: hipLaunchKernelGGL((decode_step_kernel<TS, 16>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o, a.dv); break;
+        case 32: hipLaunchKernelGGL((decode_step_kernel<TS, 32>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o, a.dv); break;
+        case 64: hipLaunchKernelGGL((decode_step_kernel<TS, 64>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o, a.dv); break;
+        case 128: hipLaunchKernelGGL((decode_step_kernel<TS, 128>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o, a.dv); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(bool bf16, const DecodeArgs& a, hipStream_t stream) {
+    return bf16 ? launch_typed<unsigned short>(a, stream) : launch_typed<float>(a, stream);
+}
+
+}  // namespace glr

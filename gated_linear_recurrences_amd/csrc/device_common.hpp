@@ -1,0 +1,98 @@
+// Device-side helpers shared by the gfx950 kernels: storage conversions, MFMA
+// wrappers and wavefront reductions / scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace glr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- storage types
+
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
+    return __uint_as_float(static_cast<unsigned int>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (NaN kept quiet).
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float x) {
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(unsigned short, h);
+}
+
+// Element loads/stores for the two storage types of q, k, v, o.
+template <typename TS> struct Store;
+
+template <> struct Store<float> {
+    static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(float* p, int64_t i, float x) { p[i] = x; }
+};
+
+template <> struct Store<unsigned short> {
+    static __device__ __forceinline__ float load(const unsigned short* p, int64_t i) {
+        return bf16_bits_to_f32(p[i]);
+    }
+    static __device__ __forceinline__ void store(unsigned short* p, int64_t i, float x) {
+        p[i] = f32_to_bf16_bits(x);
+    }
+};
+
+// ---------------------------------------------------------------- MFMA (CDNA4)
+//
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16] per wavefront.
+// Lane l (r = l & 15, g = l >> 4) supplies A[r][8g .. 8g+7] and B[8g .. 8g+7][r]
+// and holds D[4g .. 4g+3][r].  The eight k-slots of a lane may be any eight
+// reduction indices as long as A and B use the same assignment.
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3,
+                                        float a4, float a5, float a6, float a7) {
+    bf16x8 r;
+    r[0] = static_cast<__bf16>(a0); r[1] = static_cast<__bf16>(a1);
+    r[2] = static_cast<__bf16>(a2); r[3] = static_cast<__bf16>(a3);
+    r[4] = static_cast<__bf16>(a4); r[5] = static_cast<__bf16>(a5);
+    r[6] = static_cast<__bf16>(a6); r[7] = static_cast<__bf16>(a7);
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+    return pack8(lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]);
+}
+
+__device__ __forceinline__ bf16x8 join8(bf16x4 lo, bf16x4 hi) {
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// ---------------------------------------------------------------- wavefront helpers
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64);
+// every lane of a group receives the group's sum.
+template <int width>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int off = width / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront (Hillis-Steele).
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+}  // namespace glr

@@ -1,0 +1,139 @@
+// C ABI of the library: argument validation, status mapping and dispatch to
+// the kernels. No allocation, no global mutable state besides the
+// thread-local text of the last error.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "glr.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+la_status fail(la_status st, const char* fmt, const char* what) {
+    std::snprintf(g_last_error, sizeof(g_last_error), fmt, what);
+    return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<std::uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// A pointer that is dereferenced must be non-null and 16-byte aligned.
+la_status check_ptr(const void* p, bool used, bool optional, const char* name) {
+    if (p == nullptr) {
+        if (used && !optional) return fail(LA_ERR_INVALID, "%s is NULL", name);
+        return LA_OK;
+    }
+    if (!aligned16(p)) return fail(LA_ERR_INVALID, "%s is not 16-byte aligned", name);
+    return LA_OK;
+}
+
+la_status check_chunk_args(glr::Variant variant, const glr::ChunkArgs& a, int dtype) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "%s", "unknown dtype");
+    if (a.B < 0 || a.H < 0 || a.T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
+    if (a.chunk < 1) return fail(LA_ERR_INVALID, "%s", "chunk < 1");
+    if (a.dk < 1 || a.dv < 1) return fail(LA_ERR_INVALID, "%s", "d_k and d_v must be >= 1");
+    if (!supported_dim(a.dk) || !supported_dim(a.dv))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "d_k and d_v must be 16, 32, 64 or 128");
+    if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64)
+        return fail(LA_ERR_UNSUPPORTED, "%s", "chunk must be 16, 32 or 64");
+    const bool heads = a.B > 0 && a.H > 0;
+    const bool tokens = heads && a.T > 0;
+    la_status st;
+    if ((st = check_ptr(a.q, tokens, false, "q")) != LA_OK) return st;
+    if ((st = check_ptr(a.k, tokens, false, "k")) != LA_OK) return st;
+    if ((st = check_ptr(a.v, tokens, false, "v")) != LA_OK) return st;
+    if ((st = check_ptr(a.o, tokens, false, "o")) != LA_OK) return st;
+    if ((st = check_ptr(a.gate, tokens, false, variant == glr::kRetention ? "log_gamma" : "log_alpha")) != LA_OK)
+        return st;
+    if (variant == glr::kGDelta && (st = check_ptr(a.beta, tokens, false, "beta")) != LA_OK) return st;
+    if ((st = check_ptr(a.s0, heads, true, "s0")) != LA_OK) return st;
+    if ((st = check_ptr(a.s_out, heads, true, "s_out")) != LA_OK) return st;
+    const int64_t elems = static_cast<int64_t>(a.B) * a.H * a.T * (a.dk > a.dv ? a.dk : a.dv);
+    if (elems > (static_cast<int64_t>(1) << 40)) return fail(LA_ERR_INVALID, "%s", "tensor too large");
+    if (static_cast<int64_t>(a.B) * a.H > (static_cast<int64_t>(1) << 24))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "B * H must be below 2^24");
+    return LA_OK;
+}
+
+la_status run_chunk(glr::Variant variant, const glr::ChunkArgs& a, la_dtype dtype, void* stream) {
+    la_status st = check_chunk_args(variant, a, dtype);
+    if (st != LA_OK) return st;
+    if (a.B == 0 || a.H == 0) return LA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = (dtype == LA_BF16) ? glr::launch_chunk_bf16(variant, a, s)
+                                              : glr::launch_chunk_f32(variant, a, s);
+    if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_gamma,
+                       const float* s0, void* o, float* s_out,
+                       int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype, void* stream) {
+    glr::ChunkArgs a{q, k, v, log_gamma, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk};
+    return run_chunk(glr::kRetention, a, dtype, stream);
+}
+
+la_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* s0, void* o, float* s_out,
+                        int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype, void* stream) {
+    glr::ChunkArgs a{q, k, v, log_alpha, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk};
+    return run_chunk(glr::kGLA, a, dtype, stream);
+}
+
+la_status gdelta_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, const float* s0, void* o, float* s_out,
+                           int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype, void* stream) {
+    glr::ChunkArgs a{q, k, v, log_alpha, beta, s0, o, s_out, B, H, T, dk, dv, chunk};
+    return run_chunk(glr::kGDelta, a, dtype, stream);
+}
+
+la_status la_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                            float* s, void* o, int N, int H, int dk, int dv, la_dtype dtype,
+                            void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "%s", "unknown dtype");
+    if (N < 0 || H < 0) return fail(LA_ERR_INVALID, "%s", "negative N or H");
+    if (dk < 1 || dv < 1) return fail(LA_ERR_INVALID, "%s", "d_k and d_v must be >= 1");
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "d_k and d_v must be 16, 32, 64 or 128");
+    const bool used = N > 0 && H > 0;
+    la_status st;
+    if ((st = check_ptr(q, used, false, "q")) != LA_OK) return st;
+    if ((st = check_ptr(k, used, false, "k")) != LA_OK) return st;
+    if ((st = check_ptr(v, used, false, "v")) != LA_OK) return st;
+    if ((st = check_ptr(alpha, used, false, "alpha")) != LA_OK) return st;
+    if ((st = check_ptr(s, used, false, "s")) != LA_OK) return st;
+    if ((st = check_ptr(o, used, false, "o")) != LA_OK) return st;
+    if (static_cast<int64_t>(N) * H >= (static_cast<int64_t>(1) << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "N * H must be below 2^31");
+    if (!used) return LA_OK;
+    glr::DecodeArgs a{q, k, v, alpha, s, o, N, H, dk, dv};
+    const hipError_t err = glr::launch_decode(dtype == LA_BF16, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+    return LA_OK;
+}
+
+const char* la_status_str(la_status status) {
+    switch (status) {
+        case LA_OK: return "ok";
+        case LA_ERR_INVALID: return "invalid argument";
+        case LA_ERR_UNSUPPORTED: return "unsupported shape";
+        case LA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+const char* la_last_error(void) { return g_last_error; }
+
+int la_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal launch interface between the C ABI (glr_api.cpp) and the kernels.
+// Arguments reaching these functions have been validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace glr {
+
+enum Variant { kRetention = 0, kGLA = 1, kGDelta = 2 };
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* gate;   // retention: log_gamma [H]; GLA: log_alpha [B,H,T,dk]; gdelta: log_alpha [B,H,T]
+    const float* beta;   // gdelta only: [B,H,T]
+    const float* s0;     // [B,H,dv,dk] or nullptr
+    void* o;             // [B,H,T,dv]
+    float* s_out;        // [B,H,dv,dk] or nullptr
+    int B, H, T, dk, dv, chunk;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    float* s;
+    void* o;
+    int N, H, dk, dv;
+};
+
+// float32 storage, fp32 arithmetic (VALU).
+hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t stream);
+// bfloat16 storage, bf16 MFMA with fp32 accumulation and fp32 memory.
+hipError_t launch_chunk_bf16(Variant variant, const ChunkArgs& a, hipStream_t stream);
+// one decode token; bf16 == true for bfloat16 token storage.
+hipError_t launch_decode(bool bf16, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace glr

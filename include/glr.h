@@ -1,0 +1,142 @@
+/*
+ * glr.h - C ABI of the gated linear recurrences library (gfx950 / MI355X).
+ *
+ * The library evaluates the causal linear-attention recurrence
+ *     S_t = S_{t-1} G_t + (write of token t),   o_t = S_t q_t
+ * on a fixed-size memory S of shape [d_v, d_k] (rows = value channels,
+ * columns = key channels), for the gate variants fixed by the book chapter
+ * "Scrivere meglio nella memoria: gate e delta rule" (transition table of the
+ * section "Le ricorrenze come regressione online") and evaluated in the
+ * chunkwise form of "Le architetture lineari: RetNet, RWKV, xLSTM" (section
+ * "RetNet: la retention e le sue tre forme", Fig. 16.5): a masked decay
+ * triangle inside each chunk of `chunk` tokens and the memory carried from one
+ * chunk to the next. The readout of token t comes after its write.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers owned by the caller; the library allocates
+ *    nothing, keeps no per-call state and may be called from several host
+ *    threads on different streams.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued and
+ *    the call returns without synchronising; outputs are valid once the stream
+ *    has reached the enqueued work.
+ *  - Layout (row-major, contiguous):  q, k [B][H][T][d_k];  v, o [B][H][T][d_v];
+ *    states s0, s_out [B][H][d_v][d_k] float32.  Gates and write strengths are
+ *    float32 whatever `dtype` is.
+ *  - `dtype` is the storage type of q, k, v and o: LA_F32 (float32, fp32
+ *    arithmetic throughout) or LA_BF16 (bfloat16 inputs and output, matrix
+ *    products on bf16 MFMA with fp32 accumulation, fp32 memory).  The output is
+ *    rounded to nearest-even when stored as bf16.
+ *  - s0 == NULL starts from the zero memory; s_out == NULL skips storing the
+ *    final memory.  s0 == s_out (in-place continuation) is allowed; o must not
+ *    alias any input.
+ *  - T may be any value >= 0; T % chunk != 0 leaves a shorter last chunk.  With
+ *    T == 0 nothing is written to o and s_out receives s0 (or zeros).  B == 0
+ *    or H == 0 is a no-op.
+ *  - Every pointer that is read or written must be 16-byte aligned.
+ *
+ * Errors (no exception crosses the ABI):
+ *  - LA_ERR_INVALID: a required pointer is NULL, a size is negative, a pointer
+ *    is misaligned, or chunk < 1; nothing is enqueued.
+ *  - LA_ERR_UNSUPPORTED: d_k or d_v not in {16, 32, 64, 128}, or chunk not in
+ *    {16, 32, 64}; nothing is enqueued.
+ *  - LA_ERR_HIP: a launch failed (the HIP error is kept in la_last_error()).
+ *    Faults during execution surface at the caller's next synchronisation.
+ *  NaN and Inf in the inputs propagate; they are not checked.
+ */
+#ifndef GLR_H
+#define GLR_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+    LA_OK = 0,
+    LA_ERR_INVALID = 1,
+    LA_ERR_UNSUPPORTED = 2,
+    LA_ERR_HIP = 3
+} la_status;
+
+typedef enum la_dtype {
+    LA_F32 = 0,
+    LA_BF16 = 1
+} la_dtype;
+
+/*
+ * Retention with a fixed decay per head (RetNet; "Scrivere meglio nella
+ * memoria", section "Dimenticare: i gate", scalar-decay equation with
+ * alpha_t = gamma_h; the RetNet page, multi-scale retention):
+ *     S_t = gamma_h S_{t-1} + v_t k_t^T,   o_t = S_t q_t.
+ * log_gamma [H] float32 holds log(gamma_h) (<= 0 for a decay; 0 is pure
+ * accumulation).
+ */
+la_status la_chunk_fwd(const void* q, const void* k, const void* v,
+                       const float* log_gamma,
+                       const float* s0, void* o, float* s_out,
+                       int B, int H, int T, int dk, int dv, int chunk,
+                       la_dtype dtype, void* stream);
+
+/*
+ * Gated linear attention: a data-dependent gate per key channel ("Scrivere
+ * meglio nella memoria", section "Dimenticare: i gate", diagonal-gate
+ * equation):
+ *     S_t = S_{t-1} Diag(alpha_t) + v_t k_t^T,   o_t = S_t q_t.
+ * log_alpha [B][H][T][d_k] float32 holds log(alpha_t) (<= 0).  The chunk is
+ * factorised in sub-blocks of 16 tokens, so within any 16 consecutive tokens
+ * of a chunk the summed log-gates of one channel must stay above -80 (fp32
+ * range of the rescaled keys); beyond that the output is not defined.
+ */
+la_status gla_chunk_fwd(const void* q, const void* k, const void* v,
+                        const float* log_alpha,
+                        const float* s0, void* o, float* s_out,
+                        int B, int H, int T, int dk, int dv, int chunk,
+                        la_dtype dtype, void* stream);
+
+/*
+ * Gated delta rule (Gated DeltaNet; "Scrivere meglio nella memoria", section
+ * "Unire oblio e correzione: Gated DeltaNet"):
+ *     S_t = S_{t-1} [alpha_t (I - beta_t k_t k_t^T)] + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * evaluated per chunk through the WY / pseudo-value representation (section
+ * "Correggere: la delta rule": one triangular system per chunk, only the
+ * end-of-chunk memory passed on).  log_alpha [B][H][T] float32 holds
+ * log(alpha_t) (<= 0); beta [B][H][T] float32 the write strength (in [0, 1]
+ * for a stable memory with unit-norm keys).
+ */
+la_status gdelta_chunk_fwd(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           const float* s0, void* o, float* s_out,
+                           int B, int H, int T, int dk, int dv, int chunk,
+                           la_dtype dtype, void* stream);
+
+/*
+ * One decode token for N sequences x H heads with a per-key-channel gate (the
+ * recurrent form of the RetNet page, section on retention: the same two
+ * gestures for every token at constant memory; a fixed decay is the constant
+ * gate):
+ *     S <- S Diag(alpha);  S <- S + v k^T;  o = S q.
+ * q, k [N][H][d_k], v and o [N][H][d_v] in `dtype`; alpha [N][H][d_k] float32;
+ * s [N][H][d_v][d_k] float32 is read and overwritten in place.
+ * N == 0 or H == 0 is a no-op.  No chunk argument: `chunk` rules do not apply.
+ */
+la_status la_recurrent_step(const void* q, const void* k, const void* v,
+                            const float* alpha, float* s, void* o,
+                            int N, int H, int dk, int dv,
+                            la_dtype dtype, void* stream);
+
+/* Static text for a status code. */
+const char* la_status_str(la_status status);
+
+/* Message describing the last non-OK status returned to the calling thread
+ * (thread-local; empty if none).  Valid until the next call on that thread. */
+const char* la_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLR_H */

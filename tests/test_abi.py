@@ -1,0 +1,100 @@
+"""The C-ABI library loads without a GPU, exports what ``include/glr.h`` declares,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_linear_recurrences_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "glr.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:la_status|const char\*|int)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _native.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"):
+        assert n in names
+    assert set(names) == set(_native.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.la_version() >> 16 == 1
+    assert lib.la_status_str(0) == b"ok"
+    assert lib.la_status_str(1) == b"invalid argument"
+    assert lib.la_status_str(2) == b"unsupported shape"
+    assert lib.la_status_str(3) == b"HIP launch error"
+
+
+FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
+MISALIGNED = FAKE + 4
+
+
+def _chunk(lib, fn, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, s0=None, o=FAKE, s_out=None,
+             B=1, H=1, T=8, dk=16, dv=16, chunk=16, dtype=1)
+    a.update(kw)
+    P = ctypes.c_void_p
+    if fn == "gdelta_chunk_fwd":
+        return lib.gdelta_chunk_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["gate"]), P(a["beta"]), P(a["s0"]),
+                                    P(a["o"]), P(a["s_out"]), a["B"], a["H"], a["T"], a["dk"], a["dv"],
+                                    a["chunk"], a["dtype"], None)
+    return getattr(lib, fn)(P(a["q"]), P(a["k"]), P(a["v"]), P(a["gate"]), P(a["s0"]), P(a["o"]),
+                            P(a["s_out"]), a["B"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("fn", ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd"])
+def test_chunk_validation(lib, fn):
+    assert _chunk(lib, fn, q=None) == _native.LA_ERR_INVALID
+    assert b"q is NULL" in lib.la_last_error()
+    assert _chunk(lib, fn, o=None) == _native.LA_ERR_INVALID
+    assert _chunk(lib, fn, gate=None) == _native.LA_ERR_INVALID
+    assert _chunk(lib, fn, v=MISALIGNED) == _native.LA_ERR_INVALID
+    assert b"aligned" in lib.la_last_error()
+    assert _chunk(lib, fn, s_out=MISALIGNED) == _native.LA_ERR_INVALID
+    assert _chunk(lib, fn, T=-1) == _native.LA_ERR_INVALID
+    assert _chunk(lib, fn, chunk=0) == _native.LA_ERR_INVALID
+    assert _chunk(lib, fn, dtype=7) == _native.LA_ERR_INVALID
+    assert _chunk(lib, fn, dk=24) == _native.LA_ERR_UNSUPPORTED
+    assert _chunk(lib, fn, dv=256) == _native.LA_ERR_UNSUPPORTED
+    assert _chunk(lib, fn, chunk=48) == _native.LA_ERR_UNSUPPORTED
+    if fn == "gdelta_chunk_fwd":
+        assert _chunk(lib, fn, beta=None) == _native.LA_ERR_INVALID
+    # nothing to do: no pointer is needed and nothing is launched
+    assert _chunk(lib, fn, B=0, q=None, k=None, v=None, o=None, gate=None, beta=None) == _native.LA_OK
+    assert _chunk(lib, fn, H=0, q=None, k=None, v=None, o=None, gate=None, beta=None) == _native.LA_OK
+
+
+def test_decode_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, s=FAKE, o=FAKE, N=4, H=2, dk=128, dv=128, dtype=1)
+        a.update(kw)
+        return lib.la_recurrent_step(P(a["q"]), P(a["k"]), P(a["v"]), P(a["alpha"]), P(a["s"]), P(a["o"]),
+                                     a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+    assert call(s=None) == _native.LA_ERR_INVALID
+    assert call(alpha=MISALIGNED) == _native.LA_ERR_INVALID
+    assert call(N=-1) == _native.LA_ERR_INVALID
+    assert call(dk=48) == _native.LA_ERR_UNSUPPORTED
+    assert call(dtype=3) == _native.LA_ERR_INVALID
+    assert call(N=0, q=None, k=None, v=None, alpha=None, s=None, o=None) == _native.LA_OK

@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element.
+
+Gates (written here, applied to every comparison):
+  * float32 storage: max |o - o_ref| <= 1e-4 and the same for the final memory;
+  * bfloat16 storage (bf16 MFMA operands, fp32 accumulation and memory):
+    max |o - o_ref| <= 2e-2, and - because outputs can be small - also
+    max |o - o_ref| / max |o_ref| <= 1e-2 and max |S - S_ref| / max |S_ref| <= 1e-2;
+  * decode (fp32 memory, one step is a handful of fp32 FMAs per element):
+    max |o - o_ref| <= 2e-2 and, relative to max |o_ref|, <= 1e-2 for bf16 outputs (their
+    own rounding is 2^-9 relative) and <= 1e-4 for fp32 outputs; memory relative <= 1e-5.
+The oracle reads exactly the values uploaded to the GPU (bf16 values upcast), so the
+comparison measures the kernels' arithmetic.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from gated_linear_recurrences_amd import api, synthetic
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _t(x, dtype=torch.float32):
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype).contiguous()
+
+
+def _storage(w):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def run_gpu(w, s0=None, chunk=None, o=None, s_out=None):
+    """Run a chunk workload through the binding; returns (o, S_T) as float64 numpy."""
+    st = _storage(w)
+    q, k, v = _t(w.q, st), _t(w.k, st), _t(w.v, st)
+    s0_t = _t(s0 if s0 is not None else w.s0)
+    c = chunk or w.chunk
+    if w.kind == "retention":
+        out, S = api.la_chunk_fwd(q, k, v, _t(w.log_gamma), chunk=c, s0=s0_t, o=o, s_out=s_out)
+    elif w.kind == "gla":
+        out, S = api.gla_chunk_fwd(q, k, v, _t(w.log_alpha), chunk=c, s0=s0_t, o=o, s_out=s_out)
+    else:
+        out, S = api.gdelta_chunk_fwd(q, k, v, _t(w.log_alpha), _t(w.beta), chunk=c, s0=s0_t, o=o,
+                                      s_out=s_out)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64)
+
+
+def run_oracle(w, s0=None, chunk=None):
+    s0 = s0 if s0 is not None else w.s0
+    c = chunk or w.chunk
+    if w.kind == "retention":
+        return orc.retention_chunkwise(w.q, w.k, w.v, w.log_gamma, c, s0=s0)
+    if w.kind == "gla":
+        return orc.gla_chunkwise(w.q, w.k, w.v, w.log_alpha, c, s0=s0)
+    return orc.gdelta_chunkwise(w.q, w.k, w.v, w.log_alpha, w.beta, c, s0=s0)
+
+
+def assert_parity(w, o, S, o_ref, S_ref, label=""):
+    err = np.max(np.abs(o - o_ref)) if o.size else 0.0
+    scale = max(np.max(np.abs(o_ref)) if o_ref.size else 0.0, 1e-30)
+    serr = np.max(np.abs(S - S_ref))
+    sscale = max(np.max(np.abs(S_ref)), 1e-30)
+    msg = f"{label} max|do|={err:.3e} max|o|={scale:.3e} max|dS|={serr:.3e} max|S|={sscale:.3e}"
+    print(msg)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S)), msg
+    if w.dtype == "f32":
+        assert err <= 1e-4, msg
+        assert serr <= 1e-4 * max(1.0, sscale), msg
+    else:
+        assert err <= 2e-2, msg
+        assert err / scale <= 1e-2, msg
+        assert serr / sscale <= 1e-2, msg
+
+
+def make(kind, B, H, T, dk, dv, chunk, dtype, seed, state):
+    if kind == "retention":
+        return synthetic.retention_inputs(B, H, T, dk, dv, chunk=chunk, dtype=dtype, seed=seed, with_state=state)
+    if kind == "gla":
+        return synthetic.gla_inputs(B, H, T, dk, dv, chunk=chunk, dtype=dtype, seed=seed, with_state=state)
+    return synthetic.gdelta_inputs(B, H, T, dk, dv, chunk=chunk, dtype=dtype, seed=seed, with_state=state)
+
+
+KINDS = ["retention", "gla", "gdelta"]
+
+# (B, H, T, d_k, d_v, chunk): several chunks, ragged tails, every supported head size and chunk
+SMALL_SHAPES = [
+    (1, 2, 100, 16, 16, 16),
+    (2, 1, 77, 32, 64, 32),
+    (1, 2, 130, 64, 32, 64),
+    (2, 2, 200, 128, 128, 64),
+    (1, 1, 64, 128, 16, 16),
+    (1, 1, 1, 64, 64, 64),
+]
+
+
+# ----------------------------------------------------------------------------- float32 path
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+@pytest.mark.parametrize("state", [False, True])
+def test_f32_chunk_parity(kind, shape, state):
+    w = make(kind, *shape, dtype="f32", seed=100 + sum(shape), state=state)
+    o, S = run_gpu(w)
+    o_ref, S_ref = run_oracle(w)
+    assert_parity(w, o, S, o_ref, S_ref, f"{kind} f32 {shape} state={state}")
+
+
+def test_retention_t64_d16_f32_config():
+    """The fp32 retention workload: T=64, d=16, gamma=0.9, q/k/v iid N(0,1), chunk 16."""
+    w = synthetic.config_inputs("retention_t64_d16_f32")
+    o, S = run_gpu(w)
+    o_ref, S_ref = orc.retention_recurrent(w.q, w.k, w.v, w.log_gamma)
+    assert_parity(w, o, S, o_ref, S_ref, "retention_t64_d16_f32")
+
+
+# ----------------------------------------------------------------------------- bfloat16 path
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+@pytest.mark.parametrize("state", [False, True])
+def test_bf16_chunk_parity(kind, shape, state):
+    w = make(kind, *shape, dtype="bf16", seed=200 + sum(shape), state=state)
+    o, S = run_gpu(w)
+    o_ref, S_ref = run_oracle(w)
+    assert_parity(w, o, S, o_ref, S_ref, f"{kind} bf16 {shape} state={state}")
+
+
+@pytest.mark.parametrize("name", ["retention_b4h8_t2048_d128", "gla_b8h16_t4096_d128",
+                                  "gdelta_b4h16_t8192_d128"])
+def test_bf16_full_config_parity(name):
+    """Full-size workloads in the launch configuration the benchmark times, every output."""
+    w = synthetic.config_inputs(name)
+    o, S = run_gpu(w)
+    o_ref, S_ref = run_oracle(w)
+    assert_parity(w, o, S, o_ref, S_ref, name)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", KINDS)
+def test_empty_sequence_hands_state_through(kind, dtype):
+    w = make(kind, 2, 2, 0, 64, 32, 64, dtype, 7, True)
+    o, S = run_gpu(w)
+    assert o.shape == (2, 2, 0, 32)
+    np.testing.assert_array_equal(S, w.s0.astype(np.float64))
+    w.s0 = None
+    _, S = run_gpu(w)
+    np.testing.assert_array_equal(S, 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", KINDS)
+def test_resume_and_in_place_state(kind, dtype):
+    """Two calls (first 93 tokens, then the rest from s_out, in place s0 == s_out) match one call."""
+    w = make(kind, 1, 2, 160, 128, 64, 64, dtype, 8, True)
+    o_full, S_full = run_gpu(w)
+    st = _storage(w)
+
+    def part(sl, s):
+        sub = make(kind, 1, 2, 160, 128, 64, 64, dtype, 8, True)
+        sub.q, sub.k, sub.v = w.q[..., sl, :], w.k[..., sl, :], w.v[..., sl, :]
+        if kind == "gla":
+            sub.log_alpha = w.log_alpha[..., sl, :]
+        elif kind == "gdelta":
+            sub.log_alpha, sub.beta = w.log_alpha[..., sl], w.beta[..., sl]
+        q, k, v = _t(sub.q, st), _t(sub.k, st), _t(sub.v, st)
+        if kind == "retention":
+            out, _ = api.la_chunk_fwd(q, k, v, _t(w.log_gamma), chunk=64, s0=s, s_out=s)
+        elif kind == "gla":
+            out, _ = api.gla_chunk_fwd(q, k, v, _t(sub.log_alpha), chunk=64, s0=s, s_out=s)
+        else:
+            out, _ = api.gdelta_chunk_fwd(q, k, v, _t(sub.log_alpha), _t(sub.beta), chunk=64, s0=s, s_out=s)
+        return out
+
+    s = _t(w.s0)
+    o1 = part(slice(0, 93), s)
+    o2 = part(slice(93, 160), s)
+    torch.cuda.synchronize()
+    o = torch.cat([o1, o2], dim=-2).float().cpu().numpy()
+    o_ref, S_ref = run_oracle(w)
+    assert_parity(w, o.astype(np.float64), s.cpu().numpy().astype(np.float64), o_ref, S_ref, f"resume {kind}")
+    if dtype == "f32":
+        np.testing.assert_allclose(o, o_full, atol=2e-5)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", KINDS)
+def test_deterministic(kind, dtype):
+    """No atomics on the path: two runs give bit-identical outputs."""
+    w = make(kind, 2, 2, 150, 128, 128, 64, dtype, 9, True)
+    o1, S1 = run_gpu(w)
+    o2, S2 = run_gpu(w)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+
+
+# ----------------------------------------------------------------------------- decode
+
+def _decode_run(w, steps):
+    st = _storage(w)
+    s = _t(w.s0)
+    outs = []
+    for i in range(steps):
+        o = api.la_recurrent_step(_t(w.q[i], st), _t(w.k[i], st), _t(w.v[i], st), _t(w.alpha[i]), s)
+        outs.append(o.float())
+    torch.cuda.synchronize()
+    return [x.cpu().numpy().astype(np.float64) for x in outs], s.cpu().numpy().astype(np.float64)
+
+
+def _decode_assert(o, o_ref, S, S_ref, label, dtype):
+    err = np.max(np.abs(o - o_ref))
+    scale = np.max(np.abs(o_ref))
+    serr = np.max(np.abs(S - S_ref)) / np.max(np.abs(S_ref))
+    msg = f"{label} max|do|={err:.3e} max|o|={scale:.3e} rel dS={serr:.3e}"
+    print(msg)
+    rel = 1e-2 if dtype == "bf16" else 1e-4
+    assert err <= 2e-2 and err / scale <= rel and serr <= 1e-5, msg
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dims", [(3, 2, 16, 16), (2, 3, 32, 128), (4, 2, 128, 64), (2, 2, 64, 32)])
+def test_decode_parity_small(dtype, dims):
+    N, H, dk, dv = dims
+    w = synthetic.decode_inputs(N, H, dk, dv, steps=5, dtype=dtype, seed=300 + dk + dv)
+    outs, S = _decode_run(w, 5)
+    S_ref = w.s0.astype(np.float64)
+    for i in range(5):
+        o_ref, S_ref = orc.decode_step(w.q[i], w.k[i], w.v[i], w.alpha[i], S_ref)
+        _decode_assert(outs[i], o_ref, S if i == 4 else S_ref, S_ref, f"decode {dtype} {dims} step {i}", dtype)
+
+
+def test_decode_full_size_parity():
+    """512 sequences x 32 heads, d = 128 (the decode workload's launch shape), three steps,
+    every output and the whole memory."""
+    w = synthetic.config_inputs("decode_n512h32_d128", steps=3)
+    outs, S = _decode_run(w, 3)
+    S_ref = w.s0.astype(np.float64)
+    for i in range(3):
+        o_ref, S_ref = orc.decode_step(w.q[i], w.k[i], w.v[i], w.alpha[i], S_ref)
+        err = np.max(np.abs(outs[i] - o_ref))
+        assert err <= 2e-2 and err / np.max(np.abs(o_ref)) <= 1e-2, (i, err)
+    serr = np.max(np.abs(S - S_ref)) / np.max(np.abs(S_ref))
+    assert serr <= 1e-5, serr
+
+
+def test_decode_matches_recurrent_gla_over_many_steps():
+    """Sixty decode steps on a handful of (sequence, head) pairs equal the oracle's recurrent
+    GLA form over the same 60 tokens (the decode step is that recurrence, one token at a time)."""
+    w = synthetic.decode_inputs(4, 2, 128, 128, steps=60, dtype="bf16", seed=31)
+    outs, S = _decode_run(w, 60)
+    seq = lambda x: np.moveaxis(x, 0, 2)          # [steps,N,H,d] -> [N,H,steps,d]
+    o_ref, S_ref = orc.gla_recurrent(seq(w.q), seq(w.k), seq(w.v), np.log(seq(w.alpha)), s0=w.s0)
+    o = np.stack(outs, axis=2)
+    _decode_assert(o, o_ref, S, S_ref, "decode vs recurrent", "bf16")
