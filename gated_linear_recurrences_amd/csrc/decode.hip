@@ -20,63 +20,87 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
-template <typename TS, int DK>
+template <typename TS, int DK, int DV>
 __global__ __launch_bounds__(kDecodeThreads)
 void decode_step_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v,
-                        const float* __restrict__ alpha, float* __restrict__ s, TS* __restrict__ o,
-                        int dv) {
+                        const float* __restrict__ alpha, float* __restrict__ s, TS* __restrict__ o) {
     constexpr int kLanesPerRow = DK / 4;                      // each lane owns 4 key channels
     constexpr int kRowsPerPass = kDecodeThreads / kLanesPerRow;
+    // every row a thread owns is loaded before any is used: all of them in flight at once
+    constexpr int kRows = (DV + kRowsPerPass - 1) / kRowsPerPass;
     const int64_t pair = blockIdx.x;                          // (sequence, head)
     const int tid = threadIdx.x;
     const int c0 = (tid % kLanesPerRow) * 4;
     const int row = tid / kLanesPerRow;
 
+    float* S = s + pair * static_cast<int64_t>(DV) * DK;
+    f32x4 x[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int m = row + r * kRowsPerPass;
+        if (m < DV) x[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + m * DK + c0));
+    }
     const int64_t tok_k = pair * DK;
-    float qc[4], kc[4], ac[4];
+    const int64_t tok_v = pair * DV;
+    float qc[4], kc[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         qc[e] = Store<TS>::load(q, tok_k + c0 + e);
         kc[e] = Store<TS>::load(k, tok_k + c0 + e);
     }
-    const f32x4 a4 = *reinterpret_cast<const f32x4*>(alpha + tok_k + c0);
-    ac[0] = a4[0]; ac[1] = a4[1]; ac[2] = a4[2]; ac[3] = a4[3];
+    const f32x4 ac = *reinterpret_cast<const f32x4*>(alpha + tok_k + c0);
+    float vm[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int m = row + r * kRowsPerPass;
+        vm[r] = (m < DV) ? Store<TS>::load(v, tok_v + m) : 0.f;
+    }
 
-    float* S = s + pair * static_cast<int64_t>(dv) * DK;
-    const int64_t tok_v = pair * dv;
-    for (int m = row; m < dv; m += kRowsPerPass) {
-        f32x4* p = reinterpret_cast<f32x4*>(S + static_cast<int64_t>(m) * DK + c0);
-        f32x4 x = __builtin_nontemporal_load(p);
-        const float vm = Store<TS>::load(v, tok_v + m);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int m = row + r * kRowsPerPass;
+        if (kRows * kRowsPerPass > DV && m >= DV) continue;   // only when DV < rows per pass
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[e] = x[e] * ac[e] + vm * kc[e];
-            dot += x[e] * qc[e];
+            x[r][e] = x[r][e] * ac[e] + vm[r] * kc[e];
+            dot += x[r][e] * qc[e];
         }
-        __builtin_nontemporal_store(x, p);
+        __builtin_nontemporal_store(x[r], reinterpret_cast<f32x4*>(S + m * DK + c0));
         dot = group_sum<kLanesPerRow>(dot);
         if ((tid % kLanesPerRow) == 0) Store<TS>::store(o, tok_v + m, dot);
     }
+}
+
+template <typename TS, int DK>
+hipError_t launch_dk(const DecodeArgs& a, const dim3& grid, hipStream_t stream) {
+    const TS* q = static_cast<const TS*>(a.q);
+    const TS* k = static_cast<const TS*>(a.k);
+    const TS* v = static_cast<const TS*>(a.v);
+    TS* o = static_cast<TS*>(a.o);
+    const dim3 block(kDecodeThreads);
+    switch (a.dv) {
+        case 16: hipLaunchKernelGGL((decode_step_kernel<TS, DK, 16>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o); break;
+        case 32: hipLaunchKernelGGL((decode_step_kernel<TS, DK, 32>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o); break;
+        case 64: hipLaunchKernelGGL((decode_step_kernel<TS, DK, 64>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o); break;
+        case 128: hipLaunchKernelGGL((decode_step_kernel<TS, DK, 128>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <typename TS>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     const int64_t pairs = static_cast<int64_t>(a.N) * a.H;
     if (pairs == 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>(pairs)), block(kDecodeThreads);
-    const TS* q = static_cast<const TS*>(a.q);
-    const TS* k = static_cast<const TS*>(a.k);
-    const TS* v = static_cast<const TS*>(a.v);
-    TS* o = static_cast<TS*>(a.o);
+    const dim3 grid(static_cast<unsigned>(pairs));
     switch (a.dk) {
-        case 16: hipLaunchKernelGGL((decode_step_kernel<TS, 16>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o, a.dv); break;
-        case 32: hipLaunchKernelGGL((decode_step_kernel<TS, 32>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o, a.dv); break;
-        case 64: hipLaunchKernelGGL((decode_step_kernel<TS, 64>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o, a.dv); break;
-        case 128: hipLaunchKernelGGL((decode_step_kernel<TS, 128>), grid, block, 0, stream, q, k, v, a.alpha, a.s, o, a.dv); break;
-        default: return hipErrorInvalidValue;
+        case 16: return launch_dk<TS, 16>(a, grid, stream);
+        case 32: return launch_dk<TS, 32>(a, grid, stream);
+        case 64: return launch_dk<TS, 64>(a, grid, stream);
+        case 128: return launch_dk<TS, 128>(a, grid, stream);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

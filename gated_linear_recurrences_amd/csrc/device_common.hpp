@@ -73,6 +73,16 @@ __device__ __forceinline__ bf16x8 join8(bf16x4 lo, bf16x4 hi) {
     return r;
 }
 
+// ---------------------------------------------------------------- workgroup barrier
+
+// Barrier for LDS traffic only: waits for this wave's LDS operations, then for
+// every wave of the workgroup. Unlike __syncthreads() it does not drain
+// outstanding global loads, so a prefetch of the next chunk stays in flight
+// across it. Valid only where no other wave reads this wave's global writes.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------- wavefront helpers
 
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64);
