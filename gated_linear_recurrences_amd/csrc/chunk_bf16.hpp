@@ -106,6 +106,11 @@ __device__ __forceinline__ f32x4 mfma16k(bf16x4 a, bf16x4 b, f32x4 c) {
 
 __device__ __forceinline__ u16 bits(__bf16 x) { return __builtin_bit_cast(u16, x); }
 
+// Vector of N bf16 storage words (N = 4 or 8): the width of one staging load.
+template <int N> struct Vec;
+template <> struct Vec<8> { typedef u16x8 type; };
+template <> struct Vec<4> { typedef u16x4 type; };
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -258,30 +263,38 @@ void chunk_kernel(Params p) {
         for (int t = 0; t < KTW; ++t) sacc[t] = srow ? ldf4(srow + 16 * (ct0 + t) + 4 * g) : zf4();
     }
 
-    // ---- register staging of one chunk (4-row x 8-column micro-tiles, 16-byte loads)
-    constexpr int QK_ITEMS = (C / 4) * (DK / 8);
+    // ---- register staging of one chunk: 4-row micro-tiles of QV columns (16- or 8-byte
+    // loads; 8-byte ones when that is what it takes to give every thread a tile)
+    constexpr int QV = ((C / 4) * (DK / 8) >= NT) ? 8 : 4;
+    typedef typename Vec<QV>::type qv_t;
+    constexpr int QK_ITEMS = (C / 4) * (DK / QV);
     constexpr int QK_PER = (QK_ITEMS + NT - 1) / NT;
     constexpr int V_ITEMS = (C / 4) * (DVT / 8);
     constexpr int V_PER = (V_ITEMS + NT - 1) / NT;
     constexpr int G_ITEMS = kGla ? (C / 4) * (DK / 4) : 0;
     constexpr int G_PER = kGla ? (G_ITEMS + NT - 1) / NT : 1;
-    u16x8 rq[QK_PER][4], rk[QK_PER][4], rv[V_PER][4];
+    qv_t rq[QK_PER][4], rk[QK_PER][4];
+    u16x8 rv[V_PER][4];
     f32x4 rg[G_PER][4];
     float rla = 0.f, rbe = 0.f;
 
+    // Chunk base pointers are uniform (scalar registers); per-lane offsets stay 32-bit.
     auto fetch = [&](int t0, int n) {
+        const u16* qc = qg + static_cast<int64_t>(t0) * DK;
+        const u16* kc = kg + static_cast<int64_t>(t0) * DK;
+        const u16* vc = vg + static_cast<int64_t>(t0) * dv;
 #pragma unroll
         for (int pi = 0; pi < QK_PER; ++pi) {
             const int item = tid + pi * NT;
             if (item < QK_ITEMS) {
-                const int row0 = (item / (DK / 8)) * 4, col0 = (item % (DK / 8)) * 8;
+                const int row0 = (item / (DK / QV)) * 4, col0 = (item % (DK / QV)) * QV;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const bool in = row0 + rr < n;
-                    const int64_t off = static_cast<int64_t>(t0 + row0 + rr) * DK + col0;
-                    u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-                    rq[pi][rr] = in ? *reinterpret_cast<const u16x8*>(qg + off) : z;
-                    rk[pi][rr] = in ? *reinterpret_cast<const u16x8*>(kg + off) : z;
+                    const unsigned off = static_cast<unsigned>((row0 + rr) * DK + col0);
+                    qv_t z = {};
+                    rq[pi][rr] = in ? *reinterpret_cast<const qv_t*>(qc + off) : z;
+                    rk[pi][rr] = in ? *reinterpret_cast<const qv_t*>(kc + off) : z;
                 }
             }
         }
@@ -294,13 +307,13 @@ void chunk_kernel(Params p) {
                 for (int rr = 0; rr < 4; ++rr) {
                     u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
                     rv[pi][rr] = (row0 + rr < n)
-                        ? *reinterpret_cast<const u16x8*>(vg + static_cast<int64_t>(t0 + row0 + rr) * dv + col0)
+                        ? *reinterpret_cast<const u16x8*>(vc + static_cast<unsigned>((row0 + rr) * dv + col0))
                         : z;
                 }
             }
         }
         if constexpr (kGla) {
-            const float* gg = p.gate + tok0 * DK;
+            const float* gc = p.gate + (tok0 + t0) * DK;
 #pragma unroll
             for (int pi = 0; pi < G_PER; ++pi) {
                 const int item = tid + pi * NT;
@@ -308,7 +321,7 @@ void chunk_kernel(Params p) {
                     const int row0 = (item / (DK / 4)) * 4, col0 = (item % (DK / 4)) * 4;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        rg[pi][rr] = (row0 + rr < n) ? ldf4(gg + static_cast<int64_t>(t0 + row0 + rr) * DK + col0)
+                        rg[pi][rr] = (row0 + rr < n) ? ldf4(gc + static_cast<unsigned>((row0 + rr) * DK + col0))
                                                      : zf4();
                 }
             }
@@ -349,11 +362,11 @@ void chunk_kernel(Params p) {
             for (int pi = 0; pi < QK_PER; ++pi) {
                 const int item = tid + pi * NT;
                 if (item < QK_ITEMS) {
-                    const int row0 = (item / (DK / 8)) * 4, col0 = (item % (DK / 8)) * 8;
+                    const int row0 = (item / (DK / QV)) * 4, col0 = (item % (DK / QV)) * QV;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        *reinterpret_cast<u16x8*>(sQ + (row0 + rr) * QS + col0) = rq[pi][rr];
-                        *reinterpret_cast<u16x8*>(sK + (row0 + rr) * QS + col0) = rk[pi][rr];
+                        *reinterpret_cast<qv_t*>(sQ + (row0 + rr) * QS + col0) = rq[pi][rr];
+                        *reinterpret_cast<qv_t*>(sK + (row0 + rr) * QS + col0) = rk[pi][rr];
                     }
                     if constexpr (VARIANT == kRetention) {
                         // the carry weight g^(n-1-j) folded into a second copy of k
@@ -361,11 +374,11 @@ void chunk_kernel(Params p) {
                         for (int rr = 0; rr < 4; ++rr) {
                             const int j = row0 + rr;
                             const float wgt = (j < n) ? ex2(static_cast<float>(n - 1 - j) * lg2) : 0.f;
-                            u16x8 t;
+                            qv_t t;
 #pragma unroll
-                            for (int e = 0; e < 8; ++e)
+                            for (int e = 0; e < QV; ++e)
                                 t[e] = bits(static_cast<__bf16>(bf16_bits_to_f32(rk[pi][rr][e]) * wgt));
-                            *reinterpret_cast<u16x8*>(sKw + j * QS + col0) = t;
+                            *reinterpret_cast<qv_t*>(sKw + j * QS + col0) = t;
                         }
                     }
                 }
@@ -417,22 +430,22 @@ void chunk_kernel(Params p) {
             for (int pi = 0; pi < QK_PER; ++pi) {
                 const int item = tid + pi * NT;
                 if (item < QK_ITEMS) {
-                    const int row0 = (item / (DK / 8)) * 4, col0 = (item % (DK / 8)) * 8;
+                    const int row0 = (item / (DK / QV)) * 4, col0 = (item % (DK / QV)) * QV;
                     const int t = row0 / 16;
-                    float ref[8], zf[8], lf[8];
+                    float ref[QV], zf[QV], lf[QV];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
+                    for (int e = 0; e < QV; ++e) {
                         ref[e] = (t == 0) ? 0.f : sB[(16 * t - 1) * BS + col0 + e];
                         zf[e] = tabZ[t * DK + col0 + e];
                         lf[e] = tabL[t * DK + col0 + e];
                     }
-                    float kd[4][8];
+                    float kd[4][QV];
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         const int i = row0 + rr;
-                        u16x8 oq, oqe, ok;
+                        qv_t oq, oqe, ok;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
+                        for (int e = 0; e < QV; ++e) {
                             const float b = sB[i * BS + col0 + e];
                             const float E = ex2(b - ref[e]);
                             const float Ei = ex2(ref[e] - b);
@@ -442,13 +455,13 @@ void chunk_kernel(Params p) {
                             oqe[e] = bits(static_cast<__bf16>(qx * zf[e]));
                             ok[e] = bits(static_cast<__bf16>(kd[rr][e]));
                         }
-                        *reinterpret_cast<u16x8*>(sQ + i * QS + col0) = oq;
-                        *reinterpret_cast<u16x8*>(sQe + i * QS + col0) = oqe;
-                        *reinterpret_cast<u16x8*>(sK + i * QS + col0) = ok;
-                        u16x8 okw;
+                        *reinterpret_cast<qv_t*>(sQ + i * QS + col0) = oq;
+                        *reinterpret_cast<qv_t*>(sQe + i * QS + col0) = oqe;
+                        *reinterpret_cast<qv_t*>(sK + i * QS + col0) = ok;
+                        qv_t okw;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) okw[e] = bits(static_cast<__bf16>(kd[rr][e] * lf[e]));
-                        *reinterpret_cast<u16x8*>(sKw + i * QS + col0) = okw;
+                        for (int e = 0; e < QV; ++e) okw[e] = bits(static_cast<__bf16>(kd[rr][e] * lf[e]));
+                        *reinterpret_cast<qv_t*>(sKw + i * QS + col0) = okw;
                     }
                 }
             }
@@ -634,6 +647,7 @@ void chunk_kernel(Params p) {
 
         // ------------------------------------------------------------ outputs of the owned row tiles
         u16* const so = sO + w * 16 * OS;
+        u16* const oc = og + static_cast<int64_t>(t0) * dv;
 #pragma unroll
         for (int it = 0; it < CT; ++it) {
             if (it % KS != ks) continue;
@@ -673,8 +687,7 @@ void chunk_kernel(Params p) {
                 const int row = lane >> 1, half = lane & 1;
                 const u16x8 val = *reinterpret_cast<const u16x8*>(so + row * OS + 8 * half);
                 if (16 * it + row < n)
-                    *reinterpret_cast<u16x8*>(og + static_cast<int64_t>(t0 + 16 * it + row) * dv + 16 * mt + 8 * half) =
-                        val;
+                    *reinterpret_cast<u16x8*>(oc + static_cast<unsigned>((16 * it + row) * dv + 16 * mt + 8 * half)) = val;
             }
         }
 
