@@ -163,7 +163,8 @@ def bench_decode(steps_total, torch, api, synthetic, dev):
                 alg_bytes_per_step=bytes_step)
 
 
-KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_bf16.hpp",
+KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_ret.hpp",
+                  "gated_linear_recurrences_amd/csrc/chunk_common.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_bf16_retention.hip",
                   "gated_linear_recurrences_amd/csrc/device_common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
