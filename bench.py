@@ -73,14 +73,20 @@ def upload(w, torch, dev):
 def make_call(kind, api, bufs, chunk, torch):
     q = bufs["q"]
     B, H, T, d = q.shape
-    o = torch.empty((B, H, T, bufs["v"].shape[-1]), dtype=q.dtype, device=q.device)
-    s_out = torch.empty((B, H, bufs["v"].shape[-1], d), dtype=torch.float32, device=q.device)
+    dv = bufs["v"].shape[-1]
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    s_out = torch.empty((B, H, dv, d), dtype=torch.float32, device=q.device)
+    # the library's scratch (memory entering each chunk), allocated once per input set
+    ws_bytes = api.workspace_size(kind, B, H, T, d, dv, chunk, q.dtype)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     if kind == "retention":
-        return lambda: api.la_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_gamma"], chunk=chunk, o=o, s_out=s_out)
+        return lambda: api.la_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_gamma"], chunk=chunk, o=o, s_out=s_out,
+                                        workspace=ws)
     if kind == "gla":
-        return lambda: api.gla_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_alpha"], chunk=chunk, o=o, s_out=s_out)
+        return lambda: api.gla_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_alpha"], chunk=chunk, o=o, s_out=s_out,
+                                         workspace=ws)
     return lambda: api.gdelta_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_alpha"], bufs["beta"], chunk=chunk,
-                                        o=o, s_out=s_out)
+                                        o=o, s_out=s_out, workspace=ws)
 
 
 def time_calls(calls, steps, warmup, torch):
@@ -163,9 +169,11 @@ def bench_decode(steps_total, torch, api, synthetic, dev):
                 alg_bytes_per_step=bytes_step)
 
 
-KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_ret.hpp",
+KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_state.hpp",
+                  "gated_linear_recurrences_amd/csrc/chunk_output.hpp",
+                  "gated_linear_recurrences_amd/csrc/chunk_two_pass.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_common.hpp",
-                  "gated_linear_recurrences_amd/csrc/chunk_bf16_retention.hip",
+                  "gated_linear_recurrences_amd/csrc/chunk_bf16_retention_c64.hip",
                   "gated_linear_recurrences_amd/csrc/device_common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 

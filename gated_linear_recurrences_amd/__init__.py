@@ -5,6 +5,6 @@ The computation lives in the HIP library ``libglr.so`` (C ABI in ``include/glr.h
 ``api`` is its thin PyTorch binding with the same entry-point names.
 """
 
-from .api import la_chunk_fwd, gla_chunk_fwd, gdelta_chunk_fwd, la_recurrent_step  # noqa: F401
+from .api import la_chunk_fwd, gla_chunk_fwd, gdelta_chunk_fwd, la_recurrent_step, workspace_size  # noqa: F401
 
-__all__ = ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"]
+__all__ = ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step", "workspace_size"]

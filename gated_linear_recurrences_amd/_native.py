@@ -11,8 +11,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libglr.so")
 
 LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
+LA_RETENTION, LA_GLA, LA_GDELTA = 0, 1, 2
 
 EXPORTED = (
+    "la_chunk_workspace_size",
     "la_chunk_fwd",
     "gla_chunk_fwd",
     "gdelta_chunk_fwd",
@@ -43,11 +45,13 @@ def load():
             f"{LIB_PATH} is missing: build the HIP library first "
             "(python -m gated_linear_recurrences_amd.build)")
     lib = ctypes.CDLL(LIB_PATH)
-    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
-    chunk = [P, P, P, F, F, P, F, I, I, I, I, I, I, I, P]
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    chunk = [P, P, P, F, F, P, F, I, I, I, I, I, I, I, P, Z, P]
     lib.la_chunk_fwd.argtypes = chunk
     lib.gla_chunk_fwd.argtypes = chunk
-    lib.gdelta_chunk_fwd.argtypes = [P, P, P, F, F, F, P, F, I, I, I, I, I, I, I, P]
+    lib.gdelta_chunk_fwd.argtypes = [P, P, P, F, F, F, P, F, I, I, I, I, I, I, I, P, Z, P]
+    lib.la_chunk_workspace_size.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.la_chunk_workspace_size.restype = ctypes.c_int
     lib.la_recurrent_step.argtypes = [P, P, P, F, F, P, I, I, I, I, I, P]
     for name in ("la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"):
         getattr(lib, name).restype = ctypes.c_int
@@ -59,6 +63,14 @@ def load():
     lib.la_version.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def workspace_size(variant, B, H, T, dk, dv, chunk, dtype):
+    """Bytes of device workspace a chunk entry point needs for these sizes."""
+    lib = load()
+    out = ctypes.c_size_t(0)
+    check(lib.la_chunk_workspace_size(variant, B, H, T, dk, dv, chunk, dtype, ctypes.byref(out)))
+    return out.value
 
 
 def check(status):

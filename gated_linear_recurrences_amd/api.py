@@ -12,7 +12,7 @@ import torch
 
 from . import _native
 
-__all__ = ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"]
+__all__ = ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step", "workspace_size"]
 
 
 def _dtype_code(t):
@@ -44,6 +44,20 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _workspace(variant, dims, chunk, q, workspace):
+    """The caller's workspace if given (checked by the library), else a fresh one
+    from PyTorch's caching allocator of the size the library asks for."""
+    B, H, T, dk, dv = dims
+    need = _native.workspace_size(variant, B, H, T, dk, dv, chunk, _dtype_code(q))
+    if workspace is not None:
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the device of q")
+        return workspace, workspace.numel() * workspace.element_size()
+    if need == 0:
+        return None, 0
+    return torch.empty(need, dtype=torch.uint8, device=q.device), need
+
+
 def _chunk_common(q, k, v, s0, o, s_out, return_state):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d_k]")
@@ -68,42 +82,61 @@ def _chunk_common(q, k, v, s0, o, s_out, return_state):
     return (B, H, T, dk, dv), o, s_out
 
 
-def la_chunk_fwd(q, k, v, log_gamma, chunk=64, s0=None, o=None, s_out=None, return_state=True):
+def la_chunk_fwd(q, k, v, log_gamma, chunk=64, s0=None, o=None, s_out=None, return_state=True,
+                 workspace=None):
     """Retention with a fixed decay per head: S_t = gamma_h S_{t-1} + v_t k_t^T, o_t = S_t q_t.
 
-    q, k [B,H,T,d_k], v [B,H,T,d_v] (bf16 or fp32); log_gamma [H] fp32. Returns (o, s_out)."""
-    (B, H, T, dk, dv), o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    q, k [B,H,T,d_k], v [B,H,T,d_v] (bf16 or fp32); log_gamma [H] fp32. Returns (o, s_out).
+    `workspace` (optional) is a device tensor of at least workspace_size() bytes."""
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
     _require(log_gamma, "log_gamma", (H,), torch.float32, q.device)
+    ws, ws_bytes = _workspace(_native.LA_RETENTION, dims, chunk, q, workspace)
     lib = _native.load()
     _native.check(lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(s0), _ptr(o),
-                                   _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q), _stream(q.device)))
+                                   _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q), _ptr(ws), ws_bytes,
+                                   _stream(q.device)))
     return o, s_out
 
 
-def gla_chunk_fwd(q, k, v, log_alpha, chunk=64, s0=None, o=None, s_out=None, return_state=True):
+def gla_chunk_fwd(q, k, v, log_alpha, chunk=64, s0=None, o=None, s_out=None, return_state=True,
+                  workspace=None):
     """Gated linear attention: S_t = S_{t-1} Diag(alpha_t) + v_t k_t^T, o_t = S_t q_t.
 
     log_alpha [B,H,T,d_k] fp32 (log of the per-key-channel gates). Returns (o, s_out)."""
-    (B, H, T, dk, dv), o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
     _require(log_alpha, "log_alpha", (B, H, T, dk), torch.float32, q.device)
+    ws, ws_bytes = _workspace(_native.LA_GLA, dims, chunk, q, workspace)
     lib = _native.load()
     _native.check(lib.gla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(s0), _ptr(o),
-                                    _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q), _stream(q.device)))
+                                    _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q), _ptr(ws), ws_bytes,
+                                    _stream(q.device)))
     return o, s_out
 
 
-def gdelta_chunk_fwd(q, k, v, log_alpha, beta, chunk=64, s0=None, o=None, s_out=None, return_state=True):
+def gdelta_chunk_fwd(q, k, v, log_alpha, beta, chunk=64, s0=None, o=None, s_out=None, return_state=True,
+                     workspace=None):
     """Gated delta rule: S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
 
     log_alpha, beta [B,H,T] fp32. Returns (o, s_out)."""
-    (B, H, T, dk, dv), o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
     _require(log_alpha, "log_alpha", (B, H, T), torch.float32, q.device)
     _require(beta, "beta", (B, H, T), torch.float32, q.device)
+    ws, ws_bytes = _workspace(_native.LA_GDELTA, dims, chunk, q, workspace)
     lib = _native.load()
     _native.check(lib.gdelta_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0),
                                        _ptr(o), _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q),
-                                       _stream(q.device)))
+                                       _ptr(ws), ws_bytes, _stream(q.device)))
     return o, s_out
+
+
+def workspace_size(kind, B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16):
+    """Device workspace in bytes for a chunk entry point; kind in {"retention", "gla", "gdelta"}."""
+    variant = {"retention": _native.LA_RETENTION, "gla": _native.LA_GLA, "gdelta": _native.LA_GDELTA}[kind]
+    code = _native.LA_BF16 if dtype == torch.bfloat16 else _native.LA_F32
+    return _native.workspace_size(variant, B, H, T, dk, dv, chunk, code)
 
 
 def la_recurrent_step(q, k, v, alpha, s, o=None):

@@ -1,17 +1,35 @@
-// Dispatch of the bf16 MFMA chunk kernels by gate variant.
+// Dispatch of the bf16 MFMA chunk kernels by gate variant and chunk length.
 #include "launch.hpp"
 
 namespace glr {
 
-hipError_t launch_chunk_bf16_retention(const ChunkArgs& a, hipStream_t stream);
-hipError_t launch_chunk_bf16_gla(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_retention_c16(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_retention_c32(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_retention_c64(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_gla_c16(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_gla_c32(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_gla_c64(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16_gdelta(const ChunkArgs& a, hipStream_t stream);
+
+size_t chunk_workspace_bytes(Variant variant, const ChunkArgs& a, bool bf16) {
+    if (!bf16 || variant == kGDelta || a.B == 0 || a.H == 0) return 0;
+    const size_t chunks = static_cast<size_t>((a.T + a.chunk - 1) / a.chunk);
+    return static_cast<size_t>(a.B) * a.H * chunks * a.dv * a.dk * 2;
+}
 
 hipError_t launch_chunk_bf16(Variant variant, const ChunkArgs& a, hipStream_t stream) {
     if (a.B == 0 || a.H == 0) return hipSuccess;
     switch (variant) {
-        case kRetention: return launch_chunk_bf16_retention(a, stream);
-        case kGLA: return launch_chunk_bf16_gla(a, stream);
+        case kRetention:
+            if (a.chunk == 16) return launch_chunk_bf16_retention_c16(a, stream);
+            if (a.chunk == 32) return launch_chunk_bf16_retention_c32(a, stream);
+            if (a.chunk == 64) return launch_chunk_bf16_retention_c64(a, stream);
+            break;
+        case kGLA:
+            if (a.chunk == 16) return launch_chunk_bf16_gla_c16(a, stream);
+            if (a.chunk == 32) return launch_chunk_bf16_gla_c32(a, stream);
+            if (a.chunk == 64) return launch_chunk_bf16_gla_c64(a, stream);
+            break;
         case kGDelta: return launch_chunk_bf16_gdelta(a, stream);
     }
     return hipErrorInvalidValue;

@@ -10,18 +10,6 @@ namespace ck {
 typedef unsigned short u16;
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct Params {
-    const u16* q;
-    const u16* k;
-    const u16* v;
-    const float* gate;
-    const float* beta;
-    const float* s0;
-    u16* o;
-    float* s_out;
-    int H, T, dv, tiles, remap;
-};
-
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x4 zero4() {
@@ -52,26 +40,6 @@ __device__ __forceinline__ f32x4 up4(bf16x4 x) {
 
 __device__ __forceinline__ f32x4 zf4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
-__device__ __forceinline__ f32x4 mfma16k(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ u16 bits(__bf16 x) { return __builtin_bit_cast(u16, x); }
-
-// Vector of N bf16 storage words (N = 4 or 8): the width of one staging load.
-template <int N> struct Vec;
-template <> struct Vec<8> { typedef u16x8 type; };
-template <> struct Vec<4> { typedef u16x4 type; };
-
-// Operand from a row-major LDS array X (row stride RS elements) for reduction block kb
-// (MFMA k-slots: lane (r, g) takes columns 32kb + 4g..+3 and 32kb + 16 + 4g..+3 of row
-// `row`); the second half is zero when the reduction has only 2*kb+1 tiles.
-template <int NTILE, int RS>
-__device__ __forceinline__ bf16x8 split_op(const u16* X, int row, int kb, int g) {
-    const u16* p = X + row * RS + 32 * kb + 4 * g;
-    return join8(ld4(p), (2 * kb + 1 < NTILE) ? ld4(p + 16) : zero4());
-}
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -100,18 +68,40 @@ __device__ __forceinline__ bf16x4 scale4(bf16x4 x, f32x4 s) { return cvt4(up4(x)
 
 // Block index -> (head, value tile), XCD-aware: consecutive workgroup ids land on
 // different XCDs, so the value tiles of one head get ids that share an XCD and its L2.
-__device__ __forceinline__ int logical_block(const Params& p) {
-    int L = blockIdx.x;
-    if (p.remap) L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    return L;
+__device__ __forceinline__ int logical_block_of(unsigned bid, unsigned grid, int remap) {
+    return remap ? static_cast<int>((bid & 7) * (grid >> 3) + (bid >> 3)) : static_cast<int>(bid);
 }
 
-// Pair index pr (0 .. CT(CT+1)/2 - 1, row order) -> tile pair (it, jt), jt <= it.
-__device__ __forceinline__ void pair_of(int pr, int& it, int& jt) {
-    it = 0;
-    jt = pr;
-    while (jt > it) { jt -= it + 1; ++it; }
+// Global loads the compiler does not track. Its wait insertion merges the paths
+// into a software-pipelined loop conservatively and then waits for the newest
+// prefetch; these loads are waited for explicitly with vm_wait<N>(), N being the
+// number of vector-memory operations issued after the awaited load on every path
+// (loads retire in order). tie() then orders every consumer after the wait.
+__device__ __forceinline__ u16x8 gload16(const void* p) {
+    u16x8 x;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x) : "v"(p) : "memory");
+    return x;
 }
+
+__device__ __forceinline__ float gload4(const float* p) {
+    float x;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(x) : "v"(p) : "memory");
+    return x;
+}
+
+__device__ __forceinline__ void gstore8(void* p, bf16x4 x) {
+    asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(x) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0, "vmcnt range");
+    // the counter holds 63 at most; waiting for fewer outstanding operations is safe
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
+}
+
+template <typename X>
+__device__ __forceinline__ void tie(X& x) { asm volatile("" : "+v"(x)); }
 
 }  // namespace ck
 }  // namespace glr
@@ -119,21 +109,7 @@ __device__ __forceinline__ void pair_of(int pr, int& it, int& jt) {
 namespace glr {
 namespace ck {
 
-// Workgroup shape: the widest value-channel tile (16 * MT, MT in {4, 2, 1}) that
-// still gives each of the 256 CUs a workgroup; the key dimension is then split over
-// KS = min(d_k / 16, 8 / MT) waves per value tile (up to 8 waves, two per SIMD).
-constexpr int kCUs = 256;
-
-inline int choose_mt(int64_t heads, int dv) {
-    for (int cand = 4; cand >= 1; cand >>= 1)
-        if (16 * cand <= dv && heads * (dv / (16 * cand)) >= kCUs) return cand;
-    return 1;
-}
-
-template <int DK, int MT>
-constexpr int key_split() {
-    return (DK / 16 < 8 / MT) ? DK / 16 : 8 / MT;
-}
+constexpr int kCUs = 256;   // compute units of an MI355X
 
 }  // namespace ck
 }  // namespace glr

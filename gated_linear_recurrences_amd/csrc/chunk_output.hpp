@@ -1,0 +1,362 @@
+// Output pass of the two-pass chunked forward for retention and GLA (bf16 storage).
+//
+// Method: the chunkwise form of retention ("Le architetture lineari: RetNet,
+// RWKV, xLSTM", section "RetNet: la retention e le sue tre forme", Fig. 16.5)
+// and its per-channel gated extension ("Scrivere meglio nella memoria",
+// section "Dimenticare: i gate"): inside a chunk the masked decay triangle,
+// between chunks the memory. With local index i, j, the memory S_in entering
+// the chunk and chunk-local inclusive cumulative log-gates b:
+//   retention  o_i = sum_{j<=i} g^(i-j) (q_i.k_j) v_j + g^(i+1) S_in q_i
+//   GLA        o_i = sum_{j<=i} [sum_c q_ic k_jc e^(b_ic - b_jc)] v_j + S_in (q_i . e^(b_i))
+// S_in comes from the state pass (bf16 snapshots), so every chunk of every
+// sequence is independent: one workgroup per (sequence, chunk) covers all value
+// channels and computes the triangle once.
+//
+// Decomposition (gfx950), NW waves:
+//   loads     every global load is issued up front with full-row 16-byte pieces:
+//             q, k, v (and the raw gates) for staging, and each wave's slice of
+//             S_in, which stays in registers in the A-operand layout;
+//   gates     (GLA) the raw log-gates are staged, scanned per key channel (one
+//             thread per channel), and folded into bf16 operands: q and k
+//             rescaled to the cumulative gate r_t just before their own 16-token
+//             tile (bounded factors), q e^(b) for the readout, and a table
+//             F = e^(r_it - r_jt) <= 1 that joins two tiles in the triangle;
+//   triangle  the P tiles (it, jt <= it) are spread over the waves; each is one
+//             MFMA chain over d_k from LDS, masked and decayed, and stored to LDS
+//             in bf16;
+//   outputs   wave w owns value pair p = w mod NP (two 16-channel tiles) and every
+//             NW/NP-th row tile: the readout S_in q (A = S rows from registers),
+//             scaled per token, plus P V with V^T read by ds_read_b64_tr_b16.
+#pragma once
+
+#include "chunk_common.hpp"
+
+namespace glr {
+namespace ck {
+
+struct OutParams {
+    const u16* q;        // [BH][T][DK]
+    const u16* k;        // [BH][T][DK]
+    const u16* v;        // [BH][T][DV]
+    const float* gate;   // retention: log gamma [H]; GLA: log alpha [BH][T][DK]
+    const u16* states;   // [BH][NC][DV][DK] memory entering each chunk
+    u16* o;              // [BH][T][DV]
+    int H, T, NC;
+};
+
+template <int C, int DK, int DV, bool GLA>
+struct OutLayout {
+    static constexpr int CT = C / 16;
+    static constexpr int QS = DK + 8;   // bf16 row stride of staged q / k (16-byte rows)
+    // bf16 row stride of staged v: rows 8 x odd banks apart, so that the 8 rows read
+    // by half a wave of ds_read_b64_tr_b16 fall on distinct banks
+    static constexpr int VS = DV == 16 ? 16 : DV + 16;
+    static constexpr int PS = C + 4;    // bf16 row stride of P
+    static constexpr int BS = DK + 4;   // fp32 row stride of the gates
+    static constexpr int NF = CT * (CT - 1) / 2;   // off-diagonal tile pairs (GLA table)
+    static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    static constexpr int QB = al(C * QS * 2);
+    static constexpr int oQ = 0;                   // q (retention) / q rescaled (GLA)
+    static constexpr int oK = oQ + QB;             // k (retention) / k rescaled (GLA)
+    static constexpr int oQe = oK + QB;            // GLA: q e^b
+    static constexpr int oX = oQe + (GLA ? QB : 0);
+    // region X: v, P and the GLA table; for GLA it first holds the raw gates
+    static constexpr int oV = oX;
+    static constexpr int oP = oV + al(C * VS * 2);
+    static constexpr int oF = oP + al(C * PS * 2);
+    static constexpr int endX = oF + (GLA ? al(NF * DK * 4 + 16) : 0);
+    static constexpr int endG = oX + (GLA ? al(C * BS * 4) : 0);
+    static constexpr int bytes = endX > endG ? endX : endG;
+    static_assert(bytes <= 160 * 1024, "LDS budget of the output pass exceeded");
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
+
+template <int C, int DK, int DV, bool GLA, int NW>
+__global__ __launch_bounds__(64 * NW)
+void output_kernel(OutParams p) {
+    using Lay = OutLayout<C, DK, DV, GLA>;
+    constexpr int CT = C / 16, NT = 64 * NW;
+    constexpr int KB = (DK + 31) / 32;
+    constexpr int QS = Lay::QS, VS = Lay::VS, PS = Lay::PS, BS = Lay::BS;
+    constexpr int QP = C * DK / 8, QP_PER = (QP + NT - 1) / NT;    // 16-byte q/k pieces
+    constexpr int VP = C * DV / 8, VP_PER = (VP + NT - 1) / NT;    // 16-byte v pieces
+    constexpr int GP = GLA ? C * DK / 4 : 0, GP_PER = GLA ? (GP + NT - 1) / NT : 1;
+    constexpr int NP = DV >= 32 ? DV / 32 : 1;                    // value pairs (one tile if DV = 16)
+    static_assert(NW % NP == 0, "waves must cover the value pairs evenly");
+    constexpr int NPAIR = CT * (CT + 1) / 2;
+
+    __shared__ __align__(16) unsigned char smem[Lay::bytes];
+    u16* const sQ = reinterpret_cast<u16*>(smem + Lay::oQ);
+    u16* const sK = reinterpret_cast<u16*>(smem + Lay::oK);
+    u16* const sQe = reinterpret_cast<u16*>(smem + Lay::oQe);
+    u16* const sV = reinterpret_cast<u16*>(smem + Lay::oV);
+    u16* const sP = reinterpret_cast<u16*>(smem + Lay::oP);
+    float* const sF = reinterpret_cast<float*>(smem + Lay::oF);
+    float* const sB = reinterpret_cast<float*>(smem + Lay::oX);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+
+    const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+    const int h = bh % p.H;
+    const int T = p.T;
+    const int t0 = c * C, n = (T - t0 < C) ? (T - t0) : C;
+    const int64_t tok0 = static_cast<int64_t>(bh) * T + t0;
+    const u16* qc = p.q + tok0 * DK;
+    const u16* kc = p.k + tok0 * DK;
+    const u16* vc = p.v + tok0 * DV;
+    const u16* sc = p.states + (static_cast<int64_t>(bh) * p.NC + c) * DV * DK;
+    const float lg2 = GLA ? 0.f : p.gate[h] * kLog2e;
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    // ---- all global loads up front (rows past the end read row 0, zeroed on use)
+    u16x8 rq[QP_PER], rk[QP_PER], rv[VP_PER];
+    f32x4 rg[GP_PER];
+#pragma unroll
+    for (int i = 0; i < QP_PER; ++i) {
+        const int idx = tid + i * NT;
+        const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+        const unsigned off = (idx < QP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
+        rq[i] = *reinterpret_cast<const u16x8*>(qc + off);
+        rk[i] = *reinterpret_cast<const u16x8*>(kc + off);
+    }
+#pragma unroll
+    for (int i = 0; i < VP_PER; ++i) {
+        const int idx = tid + i * NT;
+        const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+        rv[i] = *reinterpret_cast<const u16x8*>(vc + ((idx < VP && j < n) ? static_cast<unsigned>(j * DV + col) : 0u));
+    }
+    if constexpr (GLA) {
+        const float* gc = p.gate + tok0 * DK;
+#pragma unroll
+        for (int i = 0; i < GP_PER; ++i) {
+            const int idx = tid + i * NT;
+            const int j = idx / (DK / 4), col = (idx % (DK / 4)) * 4;
+            rg[i] = ldf4(gc + ((idx < GP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u));
+        }
+    }
+    // this wave's rows of S_in in the A-operand layout: tile tt, row m = r16 <-> value
+    // channel 32pp + 16tt + m (one 16-row tile when DV = 16)
+    const int pp = w % NP;
+    u16x8 sa[2][KB];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int vrow = (DV >= 32) ? 32 * pp + 16 * tt + r16 : r16;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int col = 32 * kb + 8 * g;
+            sa[tt][kb] = (col < DK && (DV >= 32 || tt == 0))
+                             ? *reinterpret_cast<const u16x8*>(sc + static_cast<unsigned>(vrow * DK + col)) : z8;
+        }
+    }
+
+    auto row_ok = [&](int idx, int per_row, int total) { return idx < total && idx / per_row < n; };
+
+    if constexpr (!GLA) {
+        // ---- stage q, k, v
+#pragma unroll
+        for (int i = 0; i < QP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < QP) {
+                const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+                const bool ok = row_ok(idx, DK / 8, QP);
+                *reinterpret_cast<u16x8*>(sQ + j * QS + col) = ok ? rq[i] : z8;
+                *reinterpret_cast<u16x8*>(sK + j * QS + col) = ok ? rk[i] : z8;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < VP) {
+                const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+                *reinterpret_cast<u16x8*>(sV + j * VS + col) = row_ok(idx, DV / 8, VP) ? rv[i] : z8;
+            }
+        }
+        lds_barrier();
+    } else {
+        // ---- raw gates (log2 units) -> region X, then a scan per key channel
+#pragma unroll
+        for (int i = 0; i < GP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < GP) {
+                const int j = idx / (DK / 4), col = (idx % (DK / 4)) * 4;
+                stf4(sB + j * BS + col, row_ok(idx, DK / 4, GP) ? rg[i] * kLog2e : zf4());
+            }
+        }
+        lds_barrier();
+        for (int key = tid; key < DK; key += NT) {
+            float x = 0.f;
+#pragma unroll
+            for (int j0 = 0; j0 < C; j0 += 16) {
+                float t[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) t[e] = sB[(j0 + e) * BS + key];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) { x += t[e]; sB[(j0 + e) * BS + key] = x; }
+            }
+        }
+        lds_barrier();
+        // ---- q rescaled to its tile's reference r (the cumulative gate just before
+        // the tile), q e^b, k rescaled by e^(r - b); the joining table F
+#pragma unroll
+        for (int i = 0; i < QP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < QP) {
+                const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+                const int t = j / 16;
+                const bool ok = row_ok(idx, DK / 8, QP);
+                const float* bj = sB + j * BS + col;
+                const f32x4 b0 = ldf4(bj), b1 = ldf4(bj + 4);
+                f32x4 r0 = zf4(), r1 = zf4();
+                if (t > 0) {
+                    r0 = ldf4(sB + (16 * t - 1) * BS + col);
+                    r1 = ldf4(sB + (16 * t - 1) * BS + col + 4);
+                }
+                float qs[8], qe[8], ks[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float b = e < 4 ? b0[e] : b1[e - 4];
+                    const float r = e < 4 ? r0[e] : r1[e - 4];
+                    const float qv = ok ? bf16_bits_to_f32(rq[i][e]) : 0.f;
+                    const float kv = ok ? bf16_bits_to_f32(rk[i][e]) : 0.f;
+                    qs[e] = qv * ex2(b - r);
+                    qe[e] = qv * ex2(b);
+                    ks[e] = kv * ex2(r - b);
+                }
+                *reinterpret_cast<bf16x8*>(sQ + j * QS + col) = pack8(qs[0], qs[1], qs[2], qs[3], qs[4], qs[5], qs[6], qs[7]);
+                *reinterpret_cast<bf16x8*>(sQe + j * QS + col) = pack8(qe[0], qe[1], qe[2], qe[3], qe[4], qe[5], qe[6], qe[7]);
+                *reinterpret_cast<bf16x8*>(sK + j * QS + col) = pack8(ks[0], ks[1], ks[2], ks[3], ks[4], ks[5], ks[6], ks[7]);
+            }
+        }
+        // F[(it, jt)][key] = e^(r_it - r_jt), jt < it, pairs in row order; kept in
+        // registers until the gates are dead
+        constexpr int NFI = Lay::NF * DK, NF_PER = NFI > 0 ? (NFI + NT - 1) / NT : 1;
+        float fr[NF_PER];
+#pragma unroll
+        for (int i = 0; i < NF_PER; ++i) {
+            const int idx = tid + i * NT;
+            fr[i] = 1.f;
+            if (idx < NFI) {
+                const int key = idx % DK;
+                int pr = idx / DK, it = 1;
+                while (pr >= it) { pr -= it; ++it; }   // pair (it, jt = pr), jt < it
+                const float ri = sB[(16 * it - 1) * BS + key];
+                const float rj = pr > 0 ? sB[(16 * pr - 1) * BS + key] : 0.f;
+                fr[i] = ex2(ri - rj);
+            }
+        }
+        lds_barrier();   // gates dead: region X takes v, P and F
+#pragma unroll
+        for (int i = 0; i < NF_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < NFI) sF[idx] = fr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < VP) {
+                const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+                *reinterpret_cast<u16x8*>(sV + j * VS + col) = row_ok(idx, DV / 8, VP) ? rv[i] : z8;
+            }
+        }
+        lds_barrier();
+    }
+
+    // ---- triangle: P tiles spread over the waves, pairs (it, jt <= it) in row order
+    for (int pr0 = w; pr0 < NPAIR; pr0 += NW) {
+        int it = 0, jt = pr0;
+        while (jt > it) { jt -= it + 1; ++it; }
+        const int i = 16 * it + r16;
+        f32x4 acc = zf4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            // k-slots past d_k (d_k = 16: lanes g = 2, 3) hold zeros; the MFMA itself
+            // always runs on the whole wave
+            const int col = 32 * kb + 8 * g;
+            bf16x8 ka = as_bf16x8(z8), qb = as_bf16x8(z8);
+            if (col < DK) {
+                ka = *reinterpret_cast<const bf16x8*>(sK + (16 * jt + r16) * QS + col);
+                qb = *reinterpret_cast<const bf16x8*>(sQ + i * QS + col);
+                if constexpr (GLA) {
+                    if (jt < it) {
+                        const int f = (it * (it - 1)) / 2 + jt;
+                        const f32x4 f0 = ldf4(sF + f * DK + col), f1 = ldf4(sF + f * DK + col + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            qb[e] = static_cast<__bf16>(static_cast<float>(qb[e]) * f0[e]);
+                            qb[4 + e] = static_cast<__bf16>(static_cast<float>(qb[4 + e]) * f1[e]);
+                        }
+                    }
+                }
+            }
+            acc = mfma_16x16x32(ka, qb, acc);
+        }
+        // acc[r] = P[i][j], i = 16it + r16, j = 16jt + 4g + r
+        bf16x4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jt + 4 * g + r;
+            float val = acc[r];
+            if constexpr (!GLA) val *= ex2(static_cast<float>(i - j) * lg2);
+            pv[r] = static_cast<__bf16>((j <= i) ? val : 0.f);
+        }
+        st4(sP + i * PS + 16 * jt + 4 * g, pv);
+    }
+    lds_barrier();
+
+    // ---- outputs: readout of S_in plus P V, items (row tile it, value pair pp)
+    const u16* qread = GLA ? sQe : sQ;
+    for (int item = w; item < CT * NP; item += NW) {
+        const int it = item / NP;
+        const int i = 16 * it + r16;
+        const float oscale = GLA ? 1.f : ex2(static_cast<float>(i + 1) * lg2);
+        bf16x8 qb[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int col = 32 * kb + 8 * g;
+            qb[kb] = (col < DK) ? *reinterpret_cast<const bf16x8*>(qread + i * QS + col) : as_bf16x8(z8);
+        }
+        bf16x8 pb[(CT + 1) / 2];
+#pragma unroll
+        for (int jb = 0; jb < (CT + 1) / 2; ++jb) {
+            if (2 * jb <= it) {
+                const u16* prow = sP + i * PS + 32 * jb + 4 * g;
+                pb[jb] = join8(ld4(prow), (2 * jb + 1 <= it) ? ld4(prow + 16) : zero4());
+            }
+        }
+        f32x4 o2[2];
+#pragma unroll
+        for (int tt = 0; tt < (DV >= 32 ? 2 : 1); ++tt) {
+            f32x4 acc = zf4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(as_bf16x8(sa[tt][kb]), qb[kb], acc);
+            acc = acc * oscale;
+#pragma unroll
+            for (int jb = 0; jb < (CT + 1) / 2; ++jb) {
+                if (2 * jb <= it) {
+                    const bool hi = 2 * jb + 1 <= it;
+                    const int c0 = (DV >= 32) ? 32 * pp + 16 * tt : 0;
+                    const bf16x8 va = join8(tr_op<VS>(sV, 32 * jb, c0, r16, g),
+                                            hi ? tr_op<VS>(sV, 32 * jb + 16, c0, r16, g) : zero4());
+                    acc = mfma_16x16x32(va, pb[jb], acc);
+                }
+            }
+            o2[tt] = acc;
+        }
+        if (i < n) {
+            // lane holds o[i][32pp + 16tt + 4g + r]
+            u16* orow = p.o + (tok0 + i) * DV;
+            if constexpr (DV >= 32) {
+                st4(orow + 32 * pp + 4 * g, cvt4(o2[0]));
+                st4(orow + 32 * pp + 16 + 4 * g, cvt4(o2[1]));
+            } else {
+                st4(orow + 4 * g, cvt4(o2[0]));
+            }
+        }
+    }
+}
+
+}  // namespace ck
+}  // namespace glr

@@ -1,6 +1,6 @@
 // C ABI of the library: argument validation, status mapping and dispatch to
-// the kernels. No allocation, no global mutable state besides the
-// thread-local text of the last error.
+// the kernels. No allocation (scratch memory is the caller's workspace), no
+// global mutable state besides the thread-local text of the last error.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -58,12 +58,22 @@ la_status check_chunk_args(glr::Variant variant, const glr::ChunkArgs& a, int dt
     if (elems > (static_cast<int64_t>(1) << 40)) return fail(LA_ERR_INVALID, "%s", "tensor too large");
     if (static_cast<int64_t>(a.B) * a.H > (static_cast<int64_t>(1) << 24))
         return fail(LA_ERR_UNSUPPORTED, "%s", "B * H must be below 2^24");
+    const int64_t chunks = static_cast<int64_t>(a.B) * a.H * ((static_cast<int64_t>(a.T) + a.chunk - 1) / a.chunk);
+    if (chunks >= (static_cast<int64_t>(1) << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "B * H * ceil(T / chunk) must be below 2^31");
     return LA_OK;
 }
 
-la_status run_chunk(glr::Variant variant, const glr::ChunkArgs& a, la_dtype dtype, void* stream) {
+la_status run_chunk(glr::Variant variant, const glr::ChunkArgs& a, la_dtype dtype, size_t ws_bytes,
+                    void* stream) {
     la_status st = check_chunk_args(variant, a, dtype);
     if (st != LA_OK) return st;
+    const size_t need = glr::chunk_workspace_bytes(variant, a, dtype == LA_BF16);
+    if (need > 0) {
+        if (a.ws == nullptr) return fail(LA_ERR_INVALID, "%s", "workspace is NULL");
+        if (!aligned16(a.ws)) return fail(LA_ERR_INVALID, "%s", "workspace is not 16-byte aligned");
+        if (ws_bytes < need) return fail(LA_ERR_INVALID, "%s", "workspace too small");
+    }
     if (a.B == 0 || a.H == 0) return LA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = (dtype == LA_BF16) ? glr::launch_chunk_bf16(variant, a, s)
@@ -76,25 +86,49 @@ la_status run_chunk(glr::Variant variant, const glr::ChunkArgs& a, la_dtype dtyp
 
 extern "C" {
 
+la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int dk, int dv, int chunk,
+                                  la_dtype dtype, size_t* bytes) {
+    if (bytes == nullptr) return fail(LA_ERR_INVALID, "%s", "bytes is NULL");
+    *bytes = 0;
+    if (variant != LA_RETENTION && variant != LA_GLA && variant != LA_GDELTA)
+        return fail(LA_ERR_INVALID, "%s", "unknown variant");
+    const glr::Variant v = static_cast<glr::Variant>(variant);
+    // shape checks only: pointers are not part of the query
+    glr::ChunkArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     B, H, 0, dk, dv, chunk, nullptr};
+    la_status st = check_chunk_args(v, a, dtype);
+    if (st != LA_OK) return st;
+    if (T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
+    a.T = T;
+    const int64_t chunks = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(T) + chunk - 1) / chunk);
+    if (chunks >= (static_cast<int64_t>(1) << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "B * H * ceil(T / chunk) must be below 2^31");
+    *bytes = glr::chunk_workspace_bytes(v, a, dtype == LA_BF16);
+    return LA_OK;
+}
+
 la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_gamma,
                        const float* s0, void* o, float* s_out,
-                       int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype, void* stream) {
-    glr::ChunkArgs a{q, k, v, log_gamma, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk};
-    return run_chunk(glr::kRetention, a, dtype, stream);
+                       int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    glr::ChunkArgs a{q, k, v, log_gamma, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk, workspace};
+    return run_chunk(glr::kRetention, a, dtype, workspace_bytes, stream);
 }
 
 la_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                         const float* s0, void* o, float* s_out,
-                        int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype, void* stream) {
-    glr::ChunkArgs a{q, k, v, log_alpha, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk};
-    return run_chunk(glr::kGLA, a, dtype, stream);
+                        int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    glr::ChunkArgs a{q, k, v, log_alpha, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk, workspace};
+    return run_chunk(glr::kGLA, a, dtype, workspace_bytes, stream);
 }
 
 la_status gdelta_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                            const float* beta, const float* s0, void* o, float* s_out,
-                           int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype, void* stream) {
-    glr::ChunkArgs a{q, k, v, log_alpha, beta, s0, o, s_out, B, H, T, dk, dv, chunk};
-    return run_chunk(glr::kGDelta, a, dtype, stream);
+                           int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    glr::ChunkArgs a{q, k, v, log_alpha, beta, s0, o, s_out, B, H, T, dk, dv, chunk, workspace};
+    return run_chunk(glr::kGDelta, a, dtype, workspace_bytes, stream);
 }
 
 la_status la_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
@@ -134,6 +168,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (1 << 16) | 0; }
+int la_version(void) { return (2 << 16) | 0; }
 
 }  // extern "C"

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+
 namespace glr {
 
 enum Variant { kRetention = 0, kGLA = 1, kGDelta = 2 };
@@ -18,6 +20,7 @@ struct ChunkArgs {
     void* o;             // [B,H,T,dv]
     float* s_out;        // [B,H,dv,dk] or nullptr
     int B, H, T, dk, dv, chunk;
+    void* ws;            // device workspace of at least chunk_workspace_bytes() bytes
 };
 
 struct DecodeArgs {
@@ -32,6 +35,8 @@ struct DecodeArgs {
 
 // float32 storage, fp32 arithmetic (VALU).
 hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t stream);
+// Device workspace the chunk kernels of (variant, shape, storage) need, in bytes.
+size_t chunk_workspace_bytes(Variant variant, const ChunkArgs& a, bool bf16);
 // bfloat16 storage, bf16 MFMA with fp32 accumulation and fp32 memory.
 hipError_t launch_chunk_bf16(Variant variant, const ChunkArgs& a, hipStream_t stream);
 // one decode token; bf16 == true for bfloat16 token storage.

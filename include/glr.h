@@ -17,6 +17,11 @@
  *  - Pointers are DEVICE pointers owned by the caller; the library allocates
  *    nothing, keeps no per-call state and may be called from several host
  *    threads on different streams.
+ *  - Chunk entry points take a device `workspace` of `workspace_bytes` bytes
+ *    (16-byte aligned) for data passed between their kernels; its size comes
+ *    from la_chunk_workspace_size() and may be 0, in which case workspace may
+ *    be NULL.  Its contents on entry do not matter and are undefined on exit.
+ *    Two calls in flight at the same time need separate workspaces.
  *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued and
  *    the call returns without synchronising; outputs are valid once the stream
  *    has reached the enqueued work.
@@ -37,15 +42,19 @@
  *
  * Errors (no exception crosses the ABI):
  *  - LA_ERR_INVALID: a required pointer is NULL, a size is negative, a pointer
- *    is misaligned, or chunk < 1; nothing is enqueued.
- *  - LA_ERR_UNSUPPORTED: d_k or d_v not in {16, 32, 64, 128}, or chunk not in
- *    {16, 32, 64}; nothing is enqueued.
+ *    is misaligned, chunk < 1, or the workspace is smaller than required;
+ *    nothing is enqueued.
+ *  - LA_ERR_UNSUPPORTED: d_k or d_v not in {16, 32, 64, 128}, chunk not in
+ *    {16, 32, 64}, B * H >= 2^24 or B * H * ceil(T / chunk) >= 2^31; nothing
+ *    is enqueued.
  *  - LA_ERR_HIP: a launch failed (the HIP error is kept in la_last_error()).
  *    Faults during execution surface at the caller's next synchronisation.
  *  NaN and Inf in the inputs propagate; they are not checked.
  */
 #ifndef GLR_H
 #define GLR_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -63,6 +72,23 @@ typedef enum la_dtype {
     LA_BF16 = 1
 } la_dtype;
 
+typedef enum la_variant {
+    LA_RETENTION = 0,   /* la_chunk_fwd */
+    LA_GLA = 1,         /* gla_chunk_fwd */
+    LA_GDELTA = 2       /* gdelta_chunk_fwd */
+} la_variant;
+
+/*
+ * Workspace needed by a chunk entry point of `variant` for these sizes, in
+ * bytes, written to *bytes (0 when none is needed).  Checks the sizes like the
+ * entry point does (status and la_last_error() as there); the pointers of the
+ * entry point are not involved.  For bf16 storage, retention and GLA pass the
+ * memory entering every chunk from their state pass to their output pass:
+ * B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.
+ */
+la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int dk, int dv,
+                                  int chunk, la_dtype dtype, size_t* bytes);
+
 /*
  * Retention with a fixed decay per head (RetNet; "Scrivere meglio nella
  * memoria", section "Dimenticare: i gate", scalar-decay equation with
@@ -75,7 +101,8 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v,
                        const float* log_gamma,
                        const float* s0, void* o, float* s_out,
                        int B, int H, int T, int dk, int dv, int chunk,
-                       la_dtype dtype, void* stream);
+                       la_dtype dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * Gated linear attention: a data-dependent gate per key channel ("Scrivere
@@ -91,7 +118,8 @@ la_status gla_chunk_fwd(const void* q, const void* k, const void* v,
                         const float* log_alpha,
                         const float* s0, void* o, float* s_out,
                         int B, int H, int T, int dk, int dv, int chunk,
-                        la_dtype dtype, void* stream);
+                        la_dtype dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * Gated delta rule (Gated DeltaNet; "Scrivere meglio nella memoria", section
@@ -108,7 +136,8 @@ la_status gdelta_chunk_fwd(const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta,
                            const float* s0, void* o, float* s_out,
                            int B, int H, int T, int dk, int dv, int chunk,
-                           la_dtype dtype, void* stream);
+                           la_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * One decode token for N sequences x H heads with a per-key-channel gate (the
@@ -132,7 +161,7 @@ const char* la_status_str(la_status status);
  * (thread-local; empty if none).  Valid until the next call on that thread. */
 const char* la_last_error(void);
 
-/* ABI version: (major << 16) | minor. */
+/* ABI version: (major << 16) | minor (2.0: workspace arguments). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -16,7 +16,7 @@ def _declared_functions():
     with open(os.path.join(ROOT, "include", "glr.h")) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:la_status|const char\*|int)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:la_status|const char\*|int|size_t)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.la_version() >> 16 == 1
+    assert lib.la_version() >> 16 == 2
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -50,15 +50,54 @@ MISALIGNED = FAKE + 4
 
 def _chunk(lib, fn, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, s0=None, o=FAKE, s_out=None,
-             B=1, H=1, T=8, dk=16, dv=16, chunk=16, dtype=1)
+             B=1, H=1, T=8, dk=16, dv=16, chunk=16, dtype=1, ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
     P = ctypes.c_void_p
     if fn == "gdelta_chunk_fwd":
         return lib.gdelta_chunk_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["gate"]), P(a["beta"]), P(a["s0"]),
                                     P(a["o"]), P(a["s_out"]), a["B"], a["H"], a["T"], a["dk"], a["dv"],
-                                    a["chunk"], a["dtype"], None)
+                                    a["chunk"], a["dtype"], P(a["ws"]), a["ws_bytes"], None)
     return getattr(lib, fn)(P(a["q"]), P(a["k"]), P(a["v"]), P(a["gate"]), P(a["s0"]), P(a["o"]),
-                            P(a["s_out"]), a["B"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"], None)
+                            P(a["s_out"]), a["B"], a["H"], a["T"], a["dk"], a["dv"], a["chunk"], a["dtype"],
+                            P(a["ws"]), a["ws_bytes"], None)
+
+
+VARIANT = {"la_chunk_fwd": _native.LA_RETENTION, "gla_chunk_fwd": _native.LA_GLA,
+           "gdelta_chunk_fwd": _native.LA_GDELTA}
+
+
+def _ws(lib, variant, B=1, H=1, T=8, dk=16, dv=16, chunk=16, dtype=1):
+    out = ctypes.c_size_t(12345)
+    st = lib.la_chunk_workspace_size(variant, B, H, T, dk, dv, chunk, dtype, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_query(lib):
+    # retention and GLA in bf16: one bf16 d_v x d_k memory per (sequence, chunk)
+    for variant in (_native.LA_RETENTION, _native.LA_GLA):
+        assert _ws(lib, variant, B=4, H=8, T=2048, dk=128, dv=128, chunk=64) == (_native.LA_OK, 32 * 32 * 128 * 128 * 2)
+        assert _ws(lib, variant, B=1, H=2, T=65, dk=32, dv=64, chunk=32) == (_native.LA_OK, 2 * 3 * 64 * 32 * 2)
+        assert _ws(lib, variant, T=0) == (_native.LA_OK, 0)
+        assert _ws(lib, variant, B=0) == (_native.LA_OK, 0)
+        assert _ws(lib, variant, dtype=0) == (_native.LA_OK, 0)      # fp32 storage: one fused kernel
+    assert _ws(lib, 7)[0] == _native.LA_ERR_INVALID
+    assert _ws(lib, 0, dk=24)[0] == _native.LA_ERR_UNSUPPORTED
+    assert _ws(lib, 0, chunk=48)[0] == _native.LA_ERR_UNSUPPORTED
+    assert _ws(lib, 0, T=-1)[0] == _native.LA_ERR_INVALID
+    assert _ws(lib, 0, dtype=5)[0] == _native.LA_ERR_INVALID
+    assert lib.la_chunk_workspace_size(0, 1, 1, 8, 16, 16, 16, 1, None) == _native.LA_ERR_INVALID
+
+
+@pytest.mark.parametrize("fn", ["la_chunk_fwd", "gla_chunk_fwd"])
+def test_chunk_workspace_validation(lib, fn):
+    st, need = _ws(lib, VARIANT[fn], T=40, chunk=16)
+    assert st == _native.LA_OK and need == 3 * 16 * 16 * 2
+    assert _chunk(lib, fn, T=40, ws=None, q=None) == _native.LA_ERR_INVALID      # argument checks come first
+    assert _chunk(lib, fn, T=40, ws=None) == _native.LA_ERR_INVALID
+    assert b"workspace is NULL" in lib.la_last_error()
+    assert _chunk(lib, fn, T=40, ws_bytes=need - 1) == _native.LA_ERR_INVALID
+    assert b"workspace too small" in lib.la_last_error()
+    assert _chunk(lib, fn, T=40, ws=MISALIGNED) == _native.LA_ERR_INVALID
 
 
 @pytest.mark.parametrize("fn", ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd"])
