@@ -1,20 +1,26 @@
 #!/usr/bin/env python3
 """Throughput of the chunked forward on one MI355X, with its roofline and the CPU oracle beside it.
 
-A step is one call of the chunked forward (every stage of the hot path: staging,
-the decayed triangle, the memory readout, the carried memory, the stores) over
-one batch of the multi-scale retention workload: B=4, H=8, T=2048,
-d_k=d_v=128, bf16 q/k/v ~ N(0,1)/sqrt(128), per-head decay 1 - 2^(-5-h),
-chunk 64, fp32 memory. Inputs are resident in HBM before timing; five input
-sets are rotated so the 256 MB Infinity Cache cannot serve them.
+A step is one call of the chunked forward - every stage of the hot path: the
+state pass (memory carried from chunk to chunk, snapshots of the memory
+entering each chunk) and the output pass (decayed triangle, P V, memory
+readout, stores) - over one batch of the multi-scale retention workload: B=4,
+H=8, T=2048, d_k=d_v=128, bf16 q/k/v ~ N(0,1)/sqrt(128), per-head decay
+1 - 2^(-5-h), chunk 64, fp32 memory. Inputs are resident in HBM before timing;
+five input sets are rotated so the 256 MB Infinity Cache cannot serve them.
 
 Printed: one JSON line. ``value`` is tokens/s (B*H*T per second); ``roofline``
-prices the kernel against HBM (its arithmetic intensity, 96 flop/byte, is below
-the MI355X ridge); ``mfma`` gives the same run against the dense bf16 MFMA peak;
-``cpu_baseline`` times the fp64 oracle on the host; ``others`` reports the
-per-channel-gate (GLA), gated-delta and decode workloads measured the same way.
+prices the call (both kernels, timed with HIP events on the launching stream)
+against HBM with the algorithmic bytes of the method (q, k, v read, o and the
+final memory written); ``traffic`` is the HBM traffic the counters measured for
+one call, snapshots included; ``mfma`` gives the same run against the dense bf16
+MFMA peak; ``cpu_baseline`` times the fp64 oracle on the host; ``others``
+reports the per-channel-gate (GLA), gated-delta and decode workloads measured
+the same way.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
+    python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
+    python bench.py --summarize-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 """
 
 import argparse
@@ -200,6 +206,73 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_CAL_MB = 512   # size of the plain copy the counter runs are scaled by
+# kernels of one retention call (bf16, chunk 64, d_k = d_v = 128), as rocprofv3 names them
+TRAFFIC_KERNELS = ("glr::ck::state_kernel<64, 128, ", "glr::ck::output_kernel<64, 128, 128, false")
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch(rows, match):
+    """{dispatch id: summed counter value} over the dispatches whose kernel name matches."""
+    out = {}
+    for r in rows:
+        if match(r["Kernel_Name"]):
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """HBM bytes per retention call from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch),
+    each scaled by what the same counter reads for a plain copy of known size; writes
+    profiles/pmc_traffic.json and prints the table of the profile summary."""
+    is_copy = lambda k: "copy" in k.lower()
+    res = {}
+    for label, d, cd in (("fetch", fetch_dir, copy_fetch_dir), ("write", write_dir, copy_write_dir)):
+        rows = _counter_rows(d)
+        per_kernel = {}
+        for t in TRAFFIC_KERNELS:
+            disp = _per_dispatch(rows, lambda k, t=t: t in k)
+            per_kernel[t] = (sum(disp.values()) / len(disp), len(disp))
+        copy = _per_dispatch(_counter_rows(cd), is_copy)
+        copy_kib = max(copy.values())     # the 512 MB copy, not small incidental copies
+        res[label] = (per_kernel, copy_kib)
+    copy_bytes = int(COPY_CAL_MB * 1e6) // 4 * 4   # the copy of --copy-calibration COPY_CAL_MB
+    rec = {"workload": MAIN, "kernels": list(TRAFFIC_KERNELS), "source_sha256": kernel_source_hash(),
+           "copy_calibration_bytes": copy_bytes}
+    total = 0.0
+    lines = ["| quantity | raw counter (KiB / dispatch) | scale | bytes / call |", "|---|---|---|---|"]
+    for label in ("fetch", "write"):
+        per_kernel, copy_kib = res[label]
+        scale = copy_bytes / 1024.0 / copy_kib
+        lines.append(f"| plain copy of {copy_bytes:,} B, {label.upper()}_SIZE | {copy_kib:.0f} | "
+                     f"{copy_bytes / 1024:.0f} / raw = {scale:.4f} | {copy_bytes:,} |")
+        part = 0.0
+        for t, (kib, n) in per_kernel.items():
+            b = kib * 1024.0 * scale
+            part += b
+            lines.append(f"| `{t}...` {label.upper()}_SIZE ({n} dispatches) | {kib:.0f} | {scale:.4f} | {b:,.0f} |")
+        rec[f"{label}_scale"] = scale
+        rec[f"{label}_bytes_per_call"] = part
+        total += part
+    rec["hbm_bytes_per_launch"] = total
+    lines.append(f"| **total HBM traffic per call** | | | **{total:,.0f}** |")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
 def copy_calibration(mbytes, steps, torch):
     """A plain device copy of ``mbytes`` MB, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     n = int(mbytes * 1e6) // 4
@@ -243,7 +316,13 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes --steps times (counter scaling)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR",
+                    help="FETCH_SIZE and WRITE_SIZE counter dirs of a bench run, then of a copy run: "
+                         "write profiles/pmc_traffic.json")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the recurrences shard over (batch, head) with no "
               "communication, so only --gpus 1 is run here", file=sys.stderr)
@@ -289,7 +368,8 @@ def main():
                    "input_sets_rotated": N_SETS},
         "roofline": {"bound": "hbm", "achieved": main_r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": main_r["hbm_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel_ms": main_r["kernel_ms"], "alg_bytes_per_launch": main_r["alg_gbytes"] * 1e9},
+                     "kernel_ms": main_r["kernel_ms"], "alg_bytes_per_launch": main_r["alg_gbytes"] * 1e9,
+                     "kernels": "state pass + output pass (one call)"},
         "mfma": {"achieved": main_r["mfma_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": main_r["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS,
                  "alg_flop_per_launch": main_r["alg_gflop"] * 1e9},
