@@ -72,37 +72,6 @@ __device__ __forceinline__ int logical_block_of(unsigned bid, unsigned grid, int
     return remap ? static_cast<int>((bid & 7) * (grid >> 3) + (bid >> 3)) : static_cast<int>(bid);
 }
 
-// Global loads the compiler does not track. Its wait insertion merges the paths
-// into a software-pipelined loop conservatively and then waits for the newest
-// prefetch; these loads are waited for explicitly with vm_wait<N>(), N being the
-// number of vector-memory operations issued after the awaited load on every path
-// (loads retire in order). tie() then orders every consumer after the wait.
-__device__ __forceinline__ u16x8 gload16(const void* p) {
-    u16x8 x;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x) : "v"(p) : "memory");
-    return x;
-}
-
-__device__ __forceinline__ float gload4(const float* p) {
-    float x;
-    asm volatile("global_load_dword %0, %1, off" : "=v"(x) : "v"(p) : "memory");
-    return x;
-}
-
-__device__ __forceinline__ void gstore8(void* p, bf16x4 x) {
-    asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(x) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    static_assert(N >= 0, "vmcnt range");
-    // the counter holds 63 at most; waiting for fewer outstanding operations is safe
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
-}
-
-template <typename X>
-__device__ __forceinline__ void tie(X& x) { asm volatile("" : "+v"(x)); }
-
 }  // namespace ck
 }  // namespace glr
 

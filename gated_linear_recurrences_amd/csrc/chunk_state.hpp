@@ -29,9 +29,7 @@
 //             tokens it holds in the operand layout, scans its 4-token runs and
 //             joins runs across the four lanes of the channel with shuffles;
 //   staging   the next group goes from registers to the other LDS buffer;
-//   prefetch  HBM loads run two groups ahead through a two-slot register ring,
-//             issued untracked and waited for with explicit counts (gload16 /
-//             vm_wait): every path through the loop issues the same sequence.
+//   prefetch  HBM loads run ahead through a two-slot register ring of groups.
 #pragma once
 
 #include <type_traits>
@@ -101,8 +99,6 @@ void state_kernel(StateParams p) {
     constexpr int VP = C * DVB / 8, VP_PER = (VP + NT - 1) / NT;   // 16-byte value pieces
     constexpr int GP = GLA ? C * DKB / 4 : 0;                      // 16-byte gate pieces
     constexpr int GP_PER = GLA ? (GP + NT - 1) / NT : 0;
-    constexpr int NL = U * (KP_PER + VP_PER + GP_PER);             // loads per group and thread
-    constexpr int ST = U * (TV / NWV);                             // snapshot stores per group
 
     __shared__ __align__(16) unsigned char smem[Lay::bytes];
     auto chunk_base = [&](int b, int u) { return smem + b * Lay::BUF + u * Lay::CH; };
@@ -159,8 +155,9 @@ void state_kernel(StateParams p) {
     u16x8 rk[2][U][KP_PER], rv[2][U][VP_PER];
     f32x4 rg[2][U][GLA ? GP_PER : 1];
 
-    // Loads only, all unconditional so that every path issues the same sequence:
-    // chunks past the last are clamped to it, rows past the end read row 0.
+    // Loads only: chunks past the last are clamped to it, rows past the end read
+    // row 0; the zeroing happens where the data is consumed, so that no instruction
+    // waits for a load before the data is needed.
     auto fetch = [&](int slot, int grp) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -174,14 +171,14 @@ void state_kernel(StateParams p) {
                 int j, pc;
                 key_piece(i, j, pc);
                 const bool ok = key_ok(i) && j < n;
-                rk[slot][u][i] = gload16(kc + (ok ? static_cast<unsigned>(j * DK + 8 * pc) : 0u));
+                rk[slot][u][i] = *reinterpret_cast<const u16x8*>(kc + (ok ? static_cast<unsigned>(j * DK + 8 * pc) : 0u));
             }
 #pragma unroll
             for (int i = 0; i < VP_PER; ++i) {
                 int j, pc;
                 value_piece(i, j, pc);
                 const bool ok = value_ok(i) && j < n;
-                rv[slot][u][i] = gload16(vc + (ok ? static_cast<unsigned>(j * dv + 8 * pc) : 0u));
+                rv[slot][u][i] = *reinterpret_cast<const u16x8*>(vc + (ok ? static_cast<unsigned>(j * dv + 8 * pc) : 0u));
             }
             if constexpr (GLA) {
                 const float* gc = gg + static_cast<int64_t>(c) * C * DK;
@@ -190,28 +187,14 @@ void state_kernel(StateParams p) {
                     const int idx = tid + i * NT;
                     const int j = idx / (DKB / 4), col = (idx % (DKB / 4)) * 4;
                     const bool ok = idx < GP && j < n;
-                    const u16x8 x = gload16(gc + (ok ? static_cast<unsigned>(j * DK + col) : 0u));
-                    rg[slot][u][i] = __builtin_bit_cast(f32x4, x);
+                    rg[slot][u][i] = ldf4(gc + (ok ? static_cast<unsigned>(j * DK + col) : 0u));
                 }
             }
         }
     };
 
-    // group grp (register slot) -> LDS buffer b, rows past the end zero.
-    // W = vector-memory operations issued after this slot's loads.
-    auto stage = [&](int b, int slot, int grp, auto W) {
-        vm_wait<decltype(W)::value>();
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int i = 0; i < KP_PER; ++i) tie(rk[slot][u][i]);
-#pragma unroll
-            for (int i = 0; i < VP_PER; ++i) tie(rv[slot][u][i]);
-            if constexpr (GLA) {
-#pragma unroll
-                for (int i = 0; i < GP_PER; ++i) tie(rg[slot][u][i]);
-            }
-        }
+    // group grp (register slot) -> LDS buffer b, rows past the end zero
+    auto stage = [&](int b, int slot, int grp) {
         const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -305,12 +288,11 @@ void state_kernel(StateParams p) {
     auto store_snap = [&](int c) {
         u16* st = p.states + ((static_cast<int64_t>(bh) * NC + c) * dv + v0 + 16 * vgrp + r16) * DK + k0 + 16 * w + 4 * g;
 #pragma unroll
-        for (int t = 0; t < TVW; ++t) gstore8(st + 16 * NWV * t * DK, snap[t]);
+        for (int t = 0; t < TVW; ++t) st4(st + 16 * NWV * t * DK, snap[t]);
     };
 
     // the U chunks of group grp from LDS buffer b: contributions first (independent
     // MFMA chains), then in order: store the entering memory, S <- decay . S + dS.
-    // Every group issues ST stores: chunks past the last re-store the last snapshot.
     auto carry = [&](int b, int grp) {
         f32x4 ds[U][TVW];
         f32x4 dec[U];
@@ -360,27 +342,15 @@ void state_kernel(StateParams p) {
 #pragma unroll
                 for (int t = 0; t < TVW; ++t) sacc[t] = sacc[t] * dec[u] + ds[u][t];
             }
-            store_snap(c < NC ? c : NC - 1);
+            if (c < NC) store_snap(c);
         }
     };
 
     if (NC > 0) {
-        // prologue shaped like the loop (a group's stores, then a group's loads), with
-        // the stores writing the memory entering chunk 0 (written again by carry(0)):
-        //   D F0 D F1 [stage 0] D F2 | carry(0) [stage 1] F3 | carry(1) [stage 2] F4 ...
-        // stage(g+1) then always finds, after its slot's loads: one group of stores,
-        // one group of loads and one more group of stores.
-        // one group of stores = U snapshot stores of TVW pieces each (ST in all)
-        auto store_group = [&]() {
-#pragma unroll
-            for (int u = 0; u < U; ++u) store_snap(0);
-        };
-        store_group();
+        // prologue: groups 0 and 1 in the ring, group 0 staged, group 2 requested
         fetch(0, 0);
-        store_group();
         fetch(1, 1);
-        stage(0, 0, 0, std::integral_constant<int, ST + NL>{});
-        store_group();
+        stage(0, 0, 0);
         fetch(0, 2);
         lds_barrier();
         for (int g0 = 0; g0 < NG; g0 += 2) {
@@ -389,7 +359,7 @@ void state_kernel(StateParams p) {
                 const int grp = g0 + s;
                 if (grp < NG) {
                     carry(s, grp);
-                    if (grp + 1 < NG) stage(s ^ 1, s ^ 1, grp + 1, std::integral_constant<int, 2 * ST + NL>{});
+                    if (grp + 1 < NG) stage(s ^ 1, s ^ 1, grp + 1);
                     fetch(s ^ 1, grp + 3);   // slot of group grp+1 is free again (clamped past the end)
                     lds_barrier();
                 }

@@ -259,3 +259,58 @@ def test_decode_matches_recurrent_gla_over_many_steps():
     o_ref, S_ref = orc.gla_recurrent(seq(w.q), seq(w.k), seq(w.v), np.log(seq(w.alpha)), s0=w.s0)
     o = np.stack(outs, axis=2)
     _decode_assert(o, o_ref, S, S_ref, "decode vs recurrent", "bf16")
+
+
+# ----------------------------------------------------------------------------- launch shapes
+
+# (B, H, T, d_k, d_v, chunk) chosen so that the two-pass forward's state pass takes each of
+# its workgroup shapes (16 TV value channels per workgroup, TV = 1, 2, 4, 8, one or two waves
+# per key tile, 1-4 chunks per barrier), with ragged tails and an initial memory
+LAUNCH_SHAPES = [
+    (4, 8, 130, 128, 128, 64),    # 32 sequences: TV = 2
+    (8, 8, 97, 128, 128, 64),     # 64 sequences: TV = 4
+    (8, 16, 70, 128, 128, 32),    # 128 sequences: TV = 8
+    (2, 16, 150, 64, 64, 64),     # d = 64
+    (16, 16, 40, 32, 128, 16),    # d_k = 32, chunk 16, 256 sequences
+]
+
+
+@pytest.mark.parametrize("kind", ["retention", "gla"])
+@pytest.mark.parametrize("shape", LAUNCH_SHAPES)
+def test_bf16_launch_shapes(kind, shape):
+    w = make(kind, *shape, dtype="bf16", seed=300 + sum(shape), state=True)
+    o, S = run_gpu(w)
+    o_ref, S_ref = run_oracle(w)
+    assert_parity(w, o, S, o_ref, S_ref, f"{kind} bf16 {shape}")
+
+
+# ----------------------------------------------------------------------------- workspace
+
+def _ret_call(w, workspace):
+    q, k, v = _t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16)
+    out, S = api.la_chunk_fwd(q, k, v, _t(w.log_gamma), chunk=w.chunk, s0=_t(w.s0), workspace=workspace)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64)
+
+
+def test_workspace_reused_and_garbage_filled():
+    """A caller's workspace may hold anything on entry and serve call after call."""
+    w1 = make("retention", 2, 4, 300, 128, 128, 64, dtype="bf16", seed=41, state=True)
+    w2 = make("retention", 2, 4, 200, 128, 128, 64, dtype="bf16", seed=42, state=True)
+    need = api.workspace_size("retention", 2, 4, 300, 128, 128, 64)
+    assert need == 2 * 4 * 5 * 128 * 128 * 2
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)   # NaN bit patterns
+    for w in (w1, w2, w1):
+        o, S = _ret_call(w, ws)
+        o_ref, S_ref = run_oracle(w)
+        assert_parity(w, o, S, o_ref, S_ref, f"workspace T={w.q.shape[2]}")
+
+
+def test_workspace_too_small_is_rejected():
+    w = make("gla", 1, 2, 100, 64, 64, 32, dtype="bf16", seed=43, state=False)
+    need = api.workspace_size("gla", 1, 2, 100, 64, 64, 32)
+    ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    q, k, v = _t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16)
+    from gated_linear_recurrences_amd._native import GLRError
+    with pytest.raises(GLRError, match="workspace too small"):
+        api.gla_chunk_fwd(q, k, v, _t(w.log_alpha), chunk=32, workspace=ws)
