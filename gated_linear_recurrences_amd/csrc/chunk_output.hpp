@@ -16,11 +16,12 @@
 //   loads     every global load is issued up front with full-row 16-byte pieces:
 //             q, k, v (and the raw gates) for staging, and each wave's slice of
 //             S_in, which stays in registers in the A-operand layout;
-//   gates     (GLA) the raw log-gates are staged, scanned per key channel (one
-//             thread per channel), and folded into bf16 operands: q and k
-//             rescaled to the cumulative gate r_t just before their own 16-token
-//             tile (bounded factors), q e^(b) for the readout, and a table
-//             F = e^(r_it - r_jt) <= 1 that joins two tiles in the triangle;
+//   gates     (GLA) the raw log-gates are staged and scanned per key channel
+//             (16-token runs per lane, joined by shuffles), then folded into bf16
+//             operands: q and k rescaled to the cumulative gate r_t just before
+//             their own 16-token tile (bounded factors), with tables
+//             F = e^(r_it - r_jt) <= 1 joining two tiles in the triangle and
+//             R = e^(r_it) turning rescaled q into q e^(b) for the readout;
 //   triangle  the P tiles (it, jt <= it) are spread over the waves; each is one
 //             MFMA chain over d_k from LDS, masked and decayed, and stored to LDS
 //             in bf16;
@@ -58,13 +59,13 @@ struct OutLayout {
     static constexpr int QB = al(C * QS * 2);
     static constexpr int oQ = 0;                   // q (retention) / q rescaled (GLA)
     static constexpr int oK = oQ + QB;             // k (retention) / k rescaled (GLA)
-    static constexpr int oQe = oK + QB;            // GLA: q e^b
-    static constexpr int oX = oQe + (GLA ? QB : 0);
-    // region X: v, P and the GLA table; for GLA it first holds the raw gates
+    static constexpr int oX = oK + QB;
+    // region X: v, P and the GLA tables; for GLA it first holds the raw gates
     static constexpr int oV = oX;
     static constexpr int oP = oV + al(C * VS * 2);
-    static constexpr int oF = oP + al(C * PS * 2);
-    static constexpr int endX = oF + (GLA ? al(NF * DK * 4 + 16) : 0);
+    static constexpr int oF = oP + al(C * PS * 2);                  // F = e^(r_it - r_jt), jt < it
+    static constexpr int oR = oF + (GLA ? al(NF * DK * 4 + 16) : 0);  // R = e^(r_it)
+    static constexpr int endX = oR + (GLA ? al(CT * DK * 4) : 0);
     static constexpr int endG = oX + (GLA ? al(C * BS * 4) : 0);
     static constexpr int bytes = endX > endG ? endX : endG;
     static_assert(bytes <= 160 * 1024, "LDS budget of the output pass exceeded");
@@ -89,10 +90,10 @@ void output_kernel(OutParams p) {
     __shared__ __align__(16) unsigned char smem[Lay::bytes];
     u16* const sQ = reinterpret_cast<u16*>(smem + Lay::oQ);
     u16* const sK = reinterpret_cast<u16*>(smem + Lay::oK);
-    u16* const sQe = reinterpret_cast<u16*>(smem + Lay::oQe);
     u16* const sV = reinterpret_cast<u16*>(smem + Lay::oV);
     u16* const sP = reinterpret_cast<u16*>(smem + Lay::oP);
     float* const sF = reinterpret_cast<float*>(smem + Lay::oF);
+    float* const sR = reinterpret_cast<float*>(smem + Lay::oR);
     float* const sB = reinterpret_cast<float*>(smem + Lay::oX);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -186,16 +187,24 @@ void output_kernel(OutParams p) {
             }
         }
         lds_barrier();
-        for (int key = tid; key < DK; key += NT) {
-            float x = 0.f;
+        // chunk-local inclusive cumulative gates: lane (key 16w' + r16, run g) scans
+        // tokens 16g .. 16g + 15 of its key channel, runs are joined over g by shuffles
+        for (int kt = w; kt < DK / 16; kt += NW) {
+            const int key = 16 * kt + r16;
+            float t[16];
 #pragma unroll
-            for (int j0 = 0; j0 < C; j0 += 16) {
-                float t[16];
+            for (int e = 0; e < 16; ++e) t[e] = (16 * g + e < C) ? sB[(16 * g + e) * BS + key] : 0.f;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) t[e] = sB[(j0 + e) * BS + key];
+            for (int e = 1; e < 16; ++e) t[e] += t[e - 1];
+            float inc = t[15];
+            float y = __shfl_up(inc, 16, 64);
+            if (g >= 1) inc += y;
+            y = __shfl_up(inc, 32, 64);
+            if (g >= 2) inc += y;
+            const float base = inc - t[15];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) { x += t[e]; sB[(j0 + e) * BS + key] = x; }
-            }
+            for (int e = 0; e < 16; ++e)
+                if (16 * g + e < C) sB[(16 * g + e) * BS + key] = t[e] + base;
         }
         lds_barrier();
         // ---- q rescaled to its tile's reference r (the cumulative gate just before
@@ -214,7 +223,7 @@ void output_kernel(OutParams p) {
                     r0 = ldf4(sB + (16 * t - 1) * BS + col);
                     r1 = ldf4(sB + (16 * t - 1) * BS + col + 4);
                 }
-                float qs[8], qe[8], ks[8];
+                float qs[8], ks[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float b = e < 4 ? b0[e] : b1[e - 4];
@@ -222,11 +231,9 @@ void output_kernel(OutParams p) {
                     const float qv = ok ? bf16_bits_to_f32(rq[i][e]) : 0.f;
                     const float kv = ok ? bf16_bits_to_f32(rk[i][e]) : 0.f;
                     qs[e] = qv * ex2(b - r);
-                    qe[e] = qv * ex2(b);
                     ks[e] = kv * ex2(r - b);
                 }
                 *reinterpret_cast<bf16x8*>(sQ + j * QS + col) = pack8(qs[0], qs[1], qs[2], qs[3], qs[4], qs[5], qs[6], qs[7]);
-                *reinterpret_cast<bf16x8*>(sQe + j * QS + col) = pack8(qe[0], qe[1], qe[2], qe[3], qe[4], qe[5], qe[6], qe[7]);
                 *reinterpret_cast<bf16x8*>(sK + j * QS + col) = pack8(ks[0], ks[1], ks[2], ks[3], ks[4], ks[5], ks[6], ks[7]);
             }
         }
@@ -247,11 +254,25 @@ void output_kernel(OutParams p) {
                 fr[i] = ex2(ri - rj);
             }
         }
-        lds_barrier();   // gates dead: region X takes v, P and F
+        // R[it][key] = e^(r_it): the readout operand q e^b is q rescaled times R
+        constexpr int NRI = CT * DK, NR_PER = (NRI + NT - 1) / NT;
+        float rr[NR_PER];
+#pragma unroll
+        for (int i = 0; i < NR_PER; ++i) {
+            const int idx = tid + i * NT;
+            const int it = idx / DK, key = idx % DK;
+            rr[i] = (idx < NRI && it > 0) ? ex2(sB[(16 * it - 1) * BS + key]) : 1.f;
+        }
+        lds_barrier();   // gates dead: region X takes v, P, F and R
 #pragma unroll
         for (int i = 0; i < NF_PER; ++i) {
             const int idx = tid + i * NT;
             if (idx < NFI) sF[idx] = fr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NR_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < NRI) sR[idx] = rr[i];
         }
 #pragma unroll
         for (int i = 0; i < VP_PER; ++i) {
@@ -307,7 +328,6 @@ void output_kernel(OutParams p) {
     lds_barrier();
 
     // ---- outputs: readout of S_in plus P V, items (row tile it, value pair pp)
-    const u16* qread = GLA ? sQe : sQ;
     for (int item = w; item < CT * NP; item += NW) {
         const int it = item / NP;
         const int i = 16 * it + r16;
@@ -316,7 +336,18 @@ void output_kernel(OutParams p) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int col = 32 * kb + 8 * g;
-            qb[kb] = (col < DK) ? *reinterpret_cast<const bf16x8*>(qread + i * QS + col) : as_bf16x8(z8);
+            qb[kb] = (col < DK) ? *reinterpret_cast<const bf16x8*>(sQ + i * QS + col) : as_bf16x8(z8);
+            if constexpr (GLA) {
+                // q e^b = (q e^(b - r_it)) e^(r_it)
+                if (col < DK && it > 0) {
+                    const f32x4 f0 = ldf4(sR + it * DK + col), f1 = ldf4(sR + it * DK + col + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qb[kb][e] = static_cast<__bf16>(static_cast<float>(qb[kb][e]) * f0[e]);
+                        qb[kb][4 + e] = static_cast<__bf16>(static_cast<float>(qb[kb][4 + e]) * f1[e]);
+                    }
+                }
+            }
         }
         bf16x8 pb[(CT + 1) / 2];
 #pragma unroll

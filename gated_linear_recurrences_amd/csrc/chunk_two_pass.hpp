@@ -76,8 +76,8 @@ hipError_t launch_two_pass_dv(const ChunkArgs& a, hipStream_t stream) {
     p.H = a.H;
     p.T = a.T;
     p.NC = NC;
-    // four waves (two workgroups per CU) for retention; GLA's larger LDS footprint
-    // allows one workgroup per CU, so it runs eight waves
+    // four waves for retention (two or three workgroups per CU), eight for GLA,
+    // whose larger LDS footprint allows two workgroups per CU
     constexpr int NW = GLA ? 8 : 4;
     hipLaunchKernelGGL((output_kernel<C, DK, DV, GLA, NW>), dim3(static_cast<unsigned>(heads * NC)), dim3(64 * NW),
                        0, stream, p);
