@@ -1,4 +1,5 @@
 // Dispatch of the bf16 MFMA chunk kernels by gate variant and chunk length.
+#include "chunk_delta.hpp"
 #include "launch.hpp"
 
 namespace glr {
@@ -9,11 +10,14 @@ hipError_t launch_chunk_bf16_retention_c64(const ChunkArgs& a, hipStream_t strea
 hipError_t launch_chunk_bf16_gla_c16(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16_gla_c32(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16_gla_c64(const ChunkArgs& a, hipStream_t stream);
-hipError_t launch_chunk_bf16_gdelta(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_gdelta_c16(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_gdelta_c32(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_gdelta_c64(const ChunkArgs& a, hipStream_t stream);
 
 size_t chunk_workspace_bytes(Variant variant, const ChunkArgs& a, bool bf16) {
-    if (!bf16 || variant == kGDelta || a.B == 0 || a.H == 0) return 0;
+    if (!bf16 || a.B == 0 || a.H == 0) return 0;
     const size_t chunks = static_cast<size_t>((a.T + a.chunk - 1) / a.chunk);
+    if (variant == kGDelta) return ck::delta_ws_bytes(static_cast<int64_t>(a.B) * a.H * chunks, a.chunk, a.dk, a.dv);
     return static_cast<size_t>(a.B) * a.H * chunks * a.dv * a.dk * 2;
 }
 
@@ -30,7 +34,11 @@ hipError_t launch_chunk_bf16(Variant variant, const ChunkArgs& a, hipStream_t st
             if (a.chunk == 32) return launch_chunk_bf16_gla_c32(a, stream);
             if (a.chunk == 64) return launch_chunk_bf16_gla_c64(a, stream);
             break;
-        case kGDelta: return launch_chunk_bf16_gdelta(a, stream);
+        case kGDelta:
+            if (a.chunk == 16) return launch_chunk_bf16_gdelta_c16(a, stream);
+            if (a.chunk == 32) return launch_chunk_bf16_gdelta_c32(a, stream);
+            if (a.chunk == 64) return launch_chunk_bf16_gdelta_c64(a, stream);
+            break;
     }
     return hipErrorInvalidValue;
 }

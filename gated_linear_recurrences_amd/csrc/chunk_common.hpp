@@ -63,6 +63,14 @@ __device__ __forceinline__ bf16x8 tr_split(const u16* X, int jb, int n0, bool hi
     return join8(tr_op<RS>(X, 32 * jb, n0, r16, g), hi ? tr_op<RS>(X, 32 * jb + 16, n0, r16, g) : zero4());
 }
 
+// Row stride (bf16 elements) of a staged token-major tile `width` channels wide:
+// 16 more than the width (none for 16-wide tiles), so that rows sit 8 x odd banks
+// apart and the 8 rows read by half a wave of ds_read_b64_tr_b16 (8 bytes from
+// each of 4 lanes per row) fall on distinct banks of the 64.
+constexpr int tile_stride(int width) { return width == 16 ? 16 : width + 16; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
+
 // Scale four bf16 values by four fp32 factors (round to bf16 again).
 __device__ __forceinline__ bf16x4 scale4(bf16x4 x, f32x4 s) { return cvt4(up4(x) * s); }
 

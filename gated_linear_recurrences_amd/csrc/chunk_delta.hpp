@@ -1,0 +1,701 @@
+// Gated delta rule, chunked forward with bf16 storage: three kernels.
+//
+// Method: the gated delta rule ("Scrivere meglio nella memoria", section
+// "Unire oblio e correzione: Gated DeltaNet") in the chunkwise form of the
+// RetNet page (section "RetNet: la retention e le sue tre forme", Fig. 16.5),
+// with the pseudo-values of the WY / UT representation (section "Correggere:
+// la delta rule": one triangular system per chunk, only the end-of-chunk memory
+// passed on). Per chunk of n tokens, local inclusive cumulative log-gates G,
+// Gamma_ij = e^(G_i - G_j):
+//   A   = strictly_lower(diag(beta) (K K^T . Gamma)),  T = (I + A)^-1
+//   W   = T diag(beta e^G) K,   U0 = T diag(beta) V
+//   U   = U0 - W S_in^T
+//   o_i = e^(G_i) S_in q_i + sum_{j<=i} Gamma_ij (q_i.k_j) u_j
+//   S_out = e^(G_{n-1}) S_in + sum_j e^(G_{n-1} - G_j) u_j k_j^T
+// Everything except U and the carry is independent of the memory, so:
+//   prep    (all chunks in parallel) G, A, T's diagonal blocks, W and U0 by
+//           blocked forward substitution on MFMA; W (bf16, token-major), U0
+//           (fp32, value-major) and G go to the workspace;
+//   state   (chunks in order) per chunk: store S_in (bf16), U = U0 - W S_in^T with
+//           the memory straight from the accumulators as the B operand, U back
+//           into the workspace in place of U0, then the carry K^T (weighted U);
+//   output  (all chunks in parallel) P = (Q K^T . Gamma) masked, o = e^G S_in q +
+//           P U, U read as a bf16 hi + lo pair (its rounding would otherwise
+//           dominate the output error).
+#pragma once
+
+#include "chunk_common.hpp"
+
+namespace glr {
+namespace ck {
+
+// Workspace of one call: per (sequence, chunk) W [C][DK] bf16, U [DV][C] fp32,
+// G [C] fp32 and the memory entering the chunk S [DV][DK] bf16, each array
+// contiguous over (sequence, chunk).
+struct DeltaWs {
+    u16* w;
+    float* u;
+    float* g;
+    u16* s;
+};
+
+inline size_t delta_ws_align(size_t x) { return (x + 255) / 256 * 256; }
+
+inline size_t delta_ws_bytes(int64_t chunks, int C, int dk, int dv) {
+    return delta_ws_align(chunks * C * dk * 2) + delta_ws_align(chunks * dv * C * 4) + delta_ws_align(chunks * C * 4) +
+           delta_ws_align(chunks * dv * dk * 2);
+}
+
+inline DeltaWs delta_ws_split(void* base, int64_t chunks, int C, int dk, int dv) {
+    unsigned char* b = static_cast<unsigned char*>(base);
+    DeltaWs ws;
+    ws.w = reinterpret_cast<u16*>(b);
+    b += delta_ws_align(chunks * C * dk * 2);
+    ws.u = reinterpret_cast<float*>(b);
+    b += delta_ws_align(chunks * dv * C * 4);
+    ws.g = reinterpret_cast<float*>(b);
+    b += delta_ws_align(chunks * C * 4);
+    ws.s = reinterpret_cast<u16*>(b);
+    return ws;
+}
+
+struct DeltaParams {
+    const u16* q;         // [BH][T][DK]
+    const u16* k;         // [BH][T][DK]
+    const u16* v;         // [BH][T][DV]
+    const float* alpha;   // log alpha [BH][T]
+    const float* beta;    // [BH][T]
+    const float* s0;      // [BH][DV][DK] or null
+    u16* o;               // [BH][T][DV]
+    float* s_out;         // [BH][DV][DK] or null
+    DeltaWs ws;
+    int T, NC, vblocks;
+};
+
+// ====================================================================== prep
+//
+// One workgroup (four waves) per (sequence, chunk).
+template <int C, int DK, int DV>
+struct PrepLayout {
+    static constexpr int CT = C / 16;
+    static constexpr int KS = tile_stride(DK);   // staged k (natural and transposed reads)
+    static constexpr int VS = tile_stride(DV);   // staged v (transposed reads)
+    static constexpr int WS = DK + 8;                 // W staged for coalesced stores
+    static constexpr int AS = C + 4;                  // A, fp32
+    static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    static constexpr int oK = 0;
+    static constexpr int oV = oK + al(C * KS * 2);
+    static constexpr int oW = oV + al(C * VS * 2);
+    static constexpr int oA = oW + al(C * WS * 2);
+    static constexpr int oD = oA + al(C * AS * 4);
+    static constexpr int oG = oD + al(CT * 256 * 4);
+    static constexpr int oB = oG + al(C * 4);
+    static constexpr int bytes = oB + al(C * 4);
+    static_assert(bytes <= 160 * 1024, "LDS budget of the prep kernel exceeded");
+};
+
+template <int C, int DK, int DV>
+__global__ __launch_bounds__(256)
+void delta_prep_kernel(DeltaParams p) {
+    using Lay = PrepLayout<C, DK, DV>;
+    constexpr int CT = C / 16, NT = 256, NW = 4;
+    constexpr int KS = Lay::KS, VS = Lay::VS, WS = Lay::WS, AS = Lay::AS;
+    constexpr int KB = (DK + 31) / 32;
+    constexpr int KP = C * DK / 8, KP_PER = (KP + NT - 1) / NT;
+    constexpr int VP = C * DV / 8, VP_PER = (VP + NT - 1) / NT;
+    constexpr int NPAIR = CT * (CT + 1) / 2;
+
+    __shared__ __align__(16) unsigned char smem[Lay::bytes];
+    u16* const sK = reinterpret_cast<u16*>(smem + Lay::oK);
+    u16* const sV = reinterpret_cast<u16*>(smem + Lay::oV);
+    u16* const sW = reinterpret_cast<u16*>(smem + Lay::oW);
+    float* const sA = reinterpret_cast<float*>(smem + Lay::oA);
+    float* const sD = reinterpret_cast<float*>(smem + Lay::oD);
+    float* const sG = reinterpret_cast<float*>(smem + Lay::oG);
+    float* const sBeta = reinterpret_cast<float*>(smem + Lay::oB);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+    const int T = p.T;
+    const int t0 = c * C, n = (T - t0 < C) ? (T - t0) : C;
+    const int64_t tok0 = static_cast<int64_t>(bh) * T + t0;
+    const int64_t chunk = static_cast<int64_t>(bh) * p.NC + c;
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    // ---- stage k, v (rows past the end zero); cumulative gates and write strengths
+#pragma unroll
+    for (int i = 0; i < KP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < KP) {
+            const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const u16x8 x = *reinterpret_cast<const u16x8*>(p.k + (tok0 + (j < n ? j : 0)) * DK + col);
+            *reinterpret_cast<u16x8*>(sK + j * KS + col) = (j < n) ? x : z8;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < VP) {
+            const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            const u16x8 x = *reinterpret_cast<const u16x8*>(p.v + (tok0 + (j < n ? j : 0)) * DV + col);
+            *reinterpret_cast<u16x8*>(sV + j * VS + col) = (j < n) ? x : z8;
+        }
+    }
+    if (w == 0) {
+        float la = 0.f, be = 0.f;
+        if (lane < n) {
+            la = p.alpha[tok0 + lane] * kLog2e;
+            be = p.beta[tok0 + lane];
+        }
+        const float G = wave_inclusive_scan(la);   // padded tokens carry a zero log-gate
+        if (lane < C) {
+            sG[lane] = G;
+            sBeta[lane] = be;
+            p.ws.g[chunk * C + lane] = G;
+        }
+    }
+    lds_barrier();
+
+    // ---- A = strictly_lower(diag(beta) (K K^T . Gamma)), tiles (it, jt <= it)
+    for (int pr0 = w; pr0 < NPAIR; pr0 += NW) {
+        int it = 0, jt = pr0;
+        while (jt > it) { jt -= it + 1; ++it; }
+        const int i = 16 * it + r16;
+        f32x4 acc = zf4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int col = 32 * kb + 8 * g;
+            bf16x8 ka = as_bf16x8(z8), kb8 = as_bf16x8(z8);
+            if (col < DK) {
+                ka = *reinterpret_cast<const bf16x8*>(sK + (16 * jt + r16) * KS + col);
+                kb8 = *reinterpret_cast<const bf16x8*>(sK + i * KS + col);
+            }
+            acc = mfma_16x16x32(ka, kb8, acc);
+        }
+        // acc[r] = k_i . k_j, j = 16jt + 4g + r
+        const float gi = sG[i], bi = sBeta[i];
+        const f32x4 gj = ldf4(sG + 16 * jt + 4 * g);
+        f32x4 a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jt + 4 * g + r;
+            a[r] = (j < i) ? bi * acc[r] * ex2(gi - gj[r]) : 0.f;
+        }
+        stf4(sA + i * AS + 16 * jt + 4 * g, a);
+    }
+    lds_barrier();
+
+    // ---- T's diagonal 16 x 16 blocks D_b = (I + A_bb)^-1 by forward substitution
+    if (w == 0) {
+        const int b = lane >> 4, j = lane & 15;
+        if (b < CT) {
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float* arow = sA + (16 * b + i) * AS + 16 * b;
+                float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int kk = 0; kk < i; ++kk) acc -= arow[kk] * x[kk];
+                x[i] = acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sD[b * 256 + i * 16 + j] = x[i];
+        }
+    }
+    lds_barrier();
+
+    // ---- blocked forward substitution X_b = D_b (R_b - sum_{kk<b} A_{b,kk} X_kk) for the
+    // column tiles of W (R = diag(beta e^G) K) and U0 (R = diag(beta) V); lane (r16, g)
+    // of a tile holds rows 16b + 4g + e of column r16
+    auto solve = [&](auto rhs, f32x4 (&X)[CT]) {
+#pragma unroll
+        for (int b = 0; b < CT; ++b) {
+            f32x4 acc = rhs(b);
+#pragma unroll
+            for (int kk = 0; kk < b; ++kk) {
+                const f32x4 a = ldf4(sA + (16 * b + r16) * AS + 16 * kk + 4 * g);
+                acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt4(-a), cvt4(X[kk]), acc, 0, 0, 0);
+            }
+            const f32x4 d = ldf4(sD + b * 256 + r16 * 16 + 4 * g);
+            X[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt4(d), cvt4(acc), zf4(), 0, 0, 0);
+        }
+    };
+    constexpr int NTW = DK / 16, NTU = DV / 16;
+    float* const ug = p.ws.u + chunk * DV * C;
+    for (int nt = w; nt < NTW + NTU; nt += NW) {
+        f32x4 X[CT];
+        if (nt < NTW) {
+            solve([&](int b) {
+                const bf16x4 kv = tr_op<KS>(sK, 16 * b, 16 * nt, r16, g);
+                f32x4 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * b + 4 * g + e;
+                    r[e] = static_cast<float>(kv[e]) * sBeta[j] * ex2(sG[j]);
+                }
+                return r;
+            }, X);
+            // W tile -> LDS (token-major), stored coalesced below
+#pragma unroll
+            for (int b = 0; b < CT; ++b)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sW[(16 * b + 4 * g + e) * WS + 16 * nt + r16] = __builtin_bit_cast(u16, static_cast<__bf16>(X[b][e]));
+        } else {
+            const int ut = nt - NTW;
+            solve([&](int b) {
+                const bf16x4 vv = tr_op<VS>(sV, 16 * b, 16 * ut, r16, g);
+                f32x4 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = static_cast<float>(vv[e]) * sBeta[16 * b + 4 * g + e];
+                return r;
+            }, X);
+            // U0 value-major: lane holds U0[16b + 4g + e][16ut + r16]
+#pragma unroll
+            for (int b = 0; b < CT; ++b) stf4(ug + (16 * ut + r16) * C + 16 * b + 4 * g, X[b]);
+        }
+    }
+    lds_barrier();
+    u16* const wg = p.ws.w + chunk * C * DK;
+#pragma unroll
+    for (int i = 0; i < KP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < KP) {
+            const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<u16x8*>(wg + j * DK + col) = *reinterpret_cast<const u16x8*>(sW + j * WS + col);
+        }
+    }
+}
+
+// ====================================================================== state
+//
+// Workgroup: NVT value tiles x NKH key groups of waves. Wave (vt, kh) keeps the
+// memory for value tile vt and key tiles kh*KTW .. kh*KTW + KTW - 1 in fp32 MFMA
+// accumulators: sacc[t][r] = S[16 vt' + r16][16(kh KTW + t) + 4g + r]. Per chunk
+// (two workgroup barriers, W and K double-buffered in LDS):
+//   phase 1  store the entering memory (bf16); partial W S^T over the wave's key
+//            tiles with the accumulators as the B operand; the key group 0 wave
+//            adds U0 (it alone reads U0, before U overwrites it); partials to LDS;
+//   phase 2  U = sum of the key groups' partials; key group 0 stores U in place of
+//            U0; the carry S^T <- e^(G_last) S^T + K^T (e^(G_last - G_j) u_j) with K^T
+//            read transposed from LDS; the next chunk is staged and the one after
+//            requested.
+template <int C, int DK, int NVT, int NKH>
+struct DStateLayout {
+    static constexpr int WS = DK + 8;                 // W, natural 8-byte reads
+    static constexpr int KS = tile_stride(DK);   // K, transposed reads
+    static constexpr int XS = C + 4;                  // partials, [value][token] fp32
+    static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    static constexpr int WB = al(C * WS * 2), KB_ = al(C * KS * 2), GB = al(C * 4);
+    static constexpr int BUF = WB + KB_ + GB;         // one staged chunk
+    static constexpr int oX = 2 * BUF;
+    static constexpr int bytes = oX + (NKH > 1 ? al(NVT * NKH * 16 * XS * 4) : 0);
+    static_assert(bytes <= 160 * 1024, "LDS budget of the delta state pass exceeded");
+};
+
+template <int C, int DK, int DV, int NVT, int NKH>
+__global__ __launch_bounds__(64 * NVT * NKH)
+void delta_state_kernel(DeltaParams p) {
+    using Lay = DStateLayout<C, DK, NVT, NKH>;
+    constexpr int NW = NVT * NKH, NT = 64 * NW;
+    constexpr int CT = C / 16, JB = (CT + 1) / 2;
+    constexpr int KT = DK / 16, KTW = KT / NKH;
+    static_assert(KT % NKH == 0 && (KTW % 2 == 0 || KTW == 1), "key tiles per wave: even, or a single one");
+    constexpr int WS = Lay::WS, KS = Lay::KS, XS = Lay::XS;
+    constexpr int KP = C * DK / 8, KP_PER = (KP + NT - 1) / NT;
+
+    __shared__ __align__(16) unsigned char smem[Lay::bytes];
+    auto sW = [&](int b) { return reinterpret_cast<u16*>(smem + b * Lay::BUF); };
+    auto sK = [&](int b) { return reinterpret_cast<u16*>(smem + b * Lay::BUF + Lay::WB); };
+    auto sG = [&](int b) { return reinterpret_cast<float*>(smem + b * Lay::BUF + Lay::WB + Lay::KB_); };
+    float* const sX = reinterpret_cast<float*>(smem + Lay::oX);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int vt = wave % NVT, kh = wave / NVT;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    const int bh = blockIdx.x / p.vblocks;
+    const int v0 = (blockIdx.x % p.vblocks) * 16 * NVT + 16 * vt;   // this wave's value tile
+    const int T = p.T, NC = p.NC;
+    const int64_t tok0 = static_cast<int64_t>(bh) * T;
+    const int key0 = 16 * KTW * kh;
+
+    f32x4 sacc[KTW];
+    {
+        const float* s0 = p.s0 ? p.s0 + (static_cast<int64_t>(bh) * DV + v0 + r16) * DK + key0 + 4 * g : nullptr;
+#pragma unroll
+        for (int t = 0; t < KTW; ++t) sacc[t] = s0 ? ldf4(s0 + 16 * t) : zf4();
+    }
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto chunk_len = [&](int c) { return (T - c * C < C) ? (T - c * C) : C; };
+
+    // the next chunk's W and K pieces and gates in registers (chunk clamped past the end)
+    u16x8 rw[KP_PER], rk[KP_PER];
+    float rg = 0.f;
+    auto fetch = [&](int cr) {
+        const int c = cr < NC ? cr : NC - 1;
+        const int n = chunk_len(c);
+        const u16* wc = p.ws.w + (static_cast<int64_t>(bh) * NC + c) * C * DK;
+        const u16* kc = p.k + (tok0 + static_cast<int64_t>(c) * C) * DK;
+#pragma unroll
+        for (int i = 0; i < KP_PER; ++i) {
+            const int idx = tid + i * NT;
+            const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const unsigned off = (idx < KP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
+            rw[i] = *reinterpret_cast<const u16x8*>(wc + off);
+            rk[i] = *reinterpret_cast<const u16x8*>(kc + off);
+        }
+        rg = p.ws.g[(static_cast<int64_t>(bh) * NC + c) * C + (tid < C ? tid : 0)];
+    };
+    auto stage = [&](int b, int c) {
+        const int n = chunk_len(c);
+#pragma unroll
+        for (int i = 0; i < KP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (KP % NT == 0 || idx < KP) {
+                const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+                *reinterpret_cast<u16x8*>(sW(b) + j * WS + col) = (j < n) ? rw[i] : z8;
+                *reinterpret_cast<u16x8*>(sK(b) + j * KS + col) = (j < n) ? rk[i] : z8;
+            }
+        }
+        if (tid < C) sG(b)[tid] = rg;
+    };
+
+    if (NC > 0) {
+        fetch(0);
+        stage(0, 0);
+        fetch(1);
+        lds_barrier();
+        for (int c = 0; c < NC; ++c) {
+            const int b = c & 1;
+            const int64_t chunk = static_cast<int64_t>(bh) * NC + c;
+            float* const uc = p.ws.u + (chunk * DV + v0 + r16) * C;
+
+            // ---- phase 1
+            f32x4 u0[CT];
+            if (kh == 0) {
+#pragma unroll
+                for (int jt = 0; jt < CT; ++jt) u0[jt] = ldf4(uc + 16 * jt + 4 * g);
+            }
+            u16* const st = p.ws.s + (chunk * DV + v0 + r16) * DK + key0 + 4 * g;
+#pragma unroll
+            for (int t = 0; t < KTW; ++t) st4(st + 16 * t, cvt4(sacc[t]));
+            // y[jt][r] for token 16jt + 4g + r of value v0 + r16: U0 - (W S^T) over this wave's keys
+            f32x4 y[CT];
+            const u16* w_ = sW(b);
+#pragma unroll
+            for (int jt = 0; jt < CT; ++jt) {
+                f32x4 acc = zf4();
+                if constexpr (KTW == 1) {
+                    const u16* wr = w_ + (16 * jt + r16) * WS + key0 + 4 * g;
+                    acc = mfma_16x16x32(join8(ld4(wr), zero4()), join8(cvt4(sacc[0]), zero4()), acc);
+                } else {
+#pragma unroll
+                    for (int kb = 0; kb < KTW / 2; ++kb) {
+                        const u16* wr = w_ + (16 * jt + r16) * WS + key0 + 32 * kb + 4 * g;
+                        acc = mfma_16x16x32(join8(ld4(wr), ld4(wr + 16)),
+                                            join8(cvt4(sacc[2 * kb]), cvt4(sacc[2 * kb + 1])), acc);
+                    }
+                }
+                y[jt] = (kh == 0) ? u0[jt] - acc : -acc;
+            }
+            if constexpr (NKH > 1) {
+                float* const mine = sX + ((vt * NKH + kh) * 16 + r16) * XS;
+#pragma unroll
+                for (int jt = 0; jt < CT; ++jt) stf4(mine + 16 * jt + 4 * g, y[jt]);
+            }
+            lds_barrier();
+
+            // ---- phase 2
+            f32x4 U[CT];
+#pragma unroll
+            for (int jt = 0; jt < CT; ++jt) U[jt] = y[jt];
+            if constexpr (NKH > 1) {
+#pragma unroll
+                for (int o = 1; o < NKH; ++o) {
+                    const float* other = sX + ((vt * NKH + (kh + o) % NKH) * 16 + r16) * XS;
+#pragma unroll
+                    for (int jt = 0; jt < CT; ++jt) U[jt] = U[jt] + ldf4(other + 16 * jt + 4 * g);
+                }
+            }
+            if (kh == 0) {
+#pragma unroll
+                for (int jt = 0; jt < CT; ++jt) stf4(uc + 16 * jt + 4 * g, U[jt]);
+            }
+            // carry: weights e^(G_last - G_j); padded tokens have U = 0 and a flat G
+            const float* g_ = sG(b);
+            const float glast = g_[C - 1];
+            const float dec = ex2(glast);
+            bf16x4 ub[CT];
+#pragma unroll
+            for (int jt = 0; jt < CT; ++jt) {
+                const f32x4 gj = ldf4(g_ + 16 * jt + 4 * g);
+                f32x4 wu;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wu[e] = U[jt][e] * ex2(glast - gj[e]);
+                ub[jt] = cvt4(wu);
+            }
+            const u16* k_ = sK(b);
+#pragma unroll
+            for (int t = 0; t < KTW; ++t) {
+                f32x4 acc = sacc[t] * dec;
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb) {
+                    const bool hi = 2 * jb + 1 < CT;
+                    acc = mfma_16x16x32(tr_split<KS>(k_, jb, key0 + 16 * t, hi, r16, g),
+                                        join8(ub[2 * jb], hi ? ub[(2 * jb + 1) % CT] : zero4()), acc);
+                }
+                sacc[t] = acc;
+            }
+            if (c + 1 < NC) stage(b ^ 1, c + 1);
+            fetch(c + 2);
+            lds_barrier();
+        }
+    }
+
+    if (p.s_out) {
+        float* so = p.s_out + (static_cast<int64_t>(bh) * DV + v0 + r16) * DK + key0 + 4 * g;
+#pragma unroll
+        for (int t = 0; t < KTW; ++t) stf4(so + 16 * t, sacc[t]);
+    }
+}
+
+// ====================================================================== output
+//
+// One workgroup (four waves) per (sequence, chunk); the same shape as the output
+// pass of retention: P tiles spread over the waves and shared in LDS, each wave a
+// pair of 16-channel value tiles, the readout with S rows from registers - here
+// scaled by e^(G_i) - plus P U with U^T rows read straight from the workspace as
+// a bf16 hi + lo pair.
+template <int C, int DK, int DV>
+struct DOutLayout {
+    static constexpr int QS = DK + 8;
+    static constexpr int PS = C + 4;
+    static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    static constexpr int oQ = 0;
+    static constexpr int oK = oQ + al(C * QS * 2);
+    static constexpr int oP = oK + al(C * QS * 2);
+    static constexpr int oG = oP + al(C * PS * 2);
+    static constexpr int bytes = oG + al(C * 4);
+    static_assert(bytes <= 64 * 1024, "LDS budget of the delta output pass exceeded");
+};
+
+template <int C, int DK, int DV>
+__global__ __launch_bounds__(256)
+void delta_output_kernel(DeltaParams p) {
+    using Lay = DOutLayout<C, DK, DV>;
+    constexpr int NW = 4, NT = 256;
+    constexpr int CT = C / 16, JB = (CT + 1) / 2;
+    constexpr int KB = (DK + 31) / 32;
+    constexpr int QS = Lay::QS, PS = Lay::PS;
+    constexpr int QP = C * DK / 8, QP_PER = (QP + NT - 1) / NT;
+    constexpr int NP = DV >= 32 ? DV / 32 : 1;
+    static_assert(NW % NP == 0, "waves must cover the value pairs evenly");
+    constexpr int NPAIR = CT * (CT + 1) / 2;
+
+    __shared__ __align__(16) unsigned char smem[Lay::bytes];
+    u16* const sQ = reinterpret_cast<u16*>(smem + Lay::oQ);
+    u16* const sK = reinterpret_cast<u16*>(smem + Lay::oK);
+    u16* const sP = reinterpret_cast<u16*>(smem + Lay::oP);
+    float* const sG = reinterpret_cast<float*>(smem + Lay::oG);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+    const int T = p.T;
+    const int t0 = c * C, n = (T - t0 < C) ? (T - t0) : C;
+    const int64_t tok0 = static_cast<int64_t>(bh) * T + t0;
+    const int64_t chunk = static_cast<int64_t>(bh) * p.NC + c;
+    const u16* sc = p.ws.s + chunk * DV * DK;
+    const float* uc = p.ws.u + chunk * DV * C;
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    // ---- loads up front: q, k pieces; this wave's S rows and U^T rows
+    u16x8 rq[QP_PER], rk[QP_PER];
+#pragma unroll
+    for (int i = 0; i < QP_PER; ++i) {
+        const int idx = tid + i * NT;
+        const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+        const unsigned off = (idx < QP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
+        rq[i] = *reinterpret_cast<const u16x8*>(p.q + tok0 * DK + off);
+        rk[i] = *reinterpret_cast<const u16x8*>(p.k + tok0 * DK + off);
+    }
+    const float gl = (tid < C) ? p.ws.g[chunk * C + tid] : 0.f;
+    const int pp = w % NP;
+    u16x8 sa[2][KB];
+    f32x4 ua[2][JB][2];   // U^T rows: [tile][jb][half], tokens 32jb + 16 half + 4g + e
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int vrow = (DV >= 32) ? 32 * pp + 16 * tt + r16 : r16;
+        const bool live = DV >= 32 || tt == 0;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int col = 32 * kb + 8 * g;
+            sa[tt][kb] = (live && col < DK) ? *reinterpret_cast<const u16x8*>(sc + vrow * DK + col) : z8;
+        }
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int j0 = 32 * jb + 16 * hf + 4 * g;
+                ua[tt][jb][hf] = (live && j0 < C) ? ldf4(uc + vrow * C + j0) : zf4();
+            }
+    }
+
+    // ---- stage q, k, G
+#pragma unroll
+    for (int i = 0; i < QP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < QP) {
+            const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            const bool ok = j < n;
+            *reinterpret_cast<u16x8*>(sQ + j * QS + col) = ok ? rq[i] : z8;
+            *reinterpret_cast<u16x8*>(sK + j * QS + col) = ok ? rk[i] : z8;
+        }
+    }
+    if (tid < C) sG[tid] = gl;
+    lds_barrier();
+
+    // ---- P tiles: P_ij = (q_i . k_j) e^(G_i - G_j), j <= i
+    for (int pr0 = w; pr0 < NPAIR; pr0 += NW) {
+        int it = 0, jt = pr0;
+        while (jt > it) { jt -= it + 1; ++it; }
+        const int i = 16 * it + r16;
+        f32x4 acc = zf4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int col = 32 * kb + 8 * g;
+            bf16x8 ka = as_bf16x8(z8), qb = as_bf16x8(z8);
+            if (col < DK) {
+                ka = *reinterpret_cast<const bf16x8*>(sK + (16 * jt + r16) * QS + col);
+                qb = *reinterpret_cast<const bf16x8*>(sQ + i * QS + col);
+            }
+            acc = mfma_16x16x32(ka, qb, acc);
+        }
+        const float gi = sG[i];
+        const f32x4 gj = ldf4(sG + 16 * jt + 4 * g);
+        bf16x4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jt + 4 * g + r;
+            pv[r] = static_cast<__bf16>((j <= i) ? acc[r] * ex2(fminf(gi - gj[r], 0.f)) : 0.f);
+        }
+        st4(sP + i * PS + 16 * jt + 4 * g, pv);
+    }
+    lds_barrier();
+
+    // ---- outputs: e^(G_i) S_in q_i + P U
+    for (int item = w; item < CT * NP; item += NW) {
+        const int it = item / NP;
+        const int i = 16 * it + r16;
+        const float oscale = ex2(sG[i]);
+        bf16x8 qb[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int col = 32 * kb + 8 * g;
+            qb[kb] = (col < DK) ? *reinterpret_cast<const bf16x8*>(sQ + i * QS + col) : as_bf16x8(z8);
+        }
+        bf16x8 pb[JB];
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+            if (2 * jb <= it) {
+                const u16* prow = sP + i * PS + 32 * jb + 4 * g;
+                pb[jb] = join8(ld4(prow), (2 * jb + 1 <= it) ? ld4(prow + 16) : zero4());
+            }
+        }
+        f32x4 o2[2];
+#pragma unroll
+        for (int tt = 0; tt < (DV >= 32 ? 2 : 1); ++tt) {
+            f32x4 acc = zf4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(as_bf16x8(sa[tt][kb]), qb[kb], acc);
+            acc = acc * oscale;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                if (2 * jb <= it) {
+                    const bool hi = 2 * jb + 1 <= it;
+                    const f32x4 u0 = ua[tt][jb][0];
+                    const f32x4 u1 = hi ? ua[tt][jb][1] : zf4();
+                    const bf16x4 h0 = cvt4(u0), h1 = cvt4(u1);
+                    acc = mfma_16x16x32(join8(h0, h1), pb[jb], acc);
+                    acc = mfma_16x16x32(join8(cvt4(u0 - up4(h0)), cvt4(u1 - up4(h1))), pb[jb], acc);
+                }
+            }
+            o2[tt] = acc;
+        }
+        if (i < n) {
+            u16* orow = p.o + (tok0 + i) * DV;
+            if constexpr (DV >= 32) {
+                st4(orow + 32 * pp + 4 * g, cvt4(o2[0]));
+                st4(orow + 32 * pp + 16 + 4 * g, cvt4(o2[1]));
+            } else {
+                st4(orow + 4 * g, cvt4(o2[0]));
+            }
+        }
+    }
+}
+
+// ====================================================================== launch
+template <int C, int DK, int DV>
+hipError_t launch_delta_dv(const ChunkArgs& a, hipStream_t stream) {
+    const int NC = (a.T + C - 1) / C;
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    DeltaParams p;
+    p.q = static_cast<const u16*>(a.q);
+    p.k = static_cast<const u16*>(a.k);
+    p.v = static_cast<const u16*>(a.v);
+    p.alpha = a.gate;
+    p.beta = a.beta;
+    p.s0 = a.s0;
+    p.o = static_cast<u16*>(a.o);
+    p.s_out = a.s_out;
+    p.ws = delta_ws_split(a.ws, heads * NC, C, DK, DV);
+    p.T = a.T;
+    p.NC = NC;
+    // state pass: two value tiles x two key groups per workgroup (fewer when the head is small)
+    constexpr int NVT = DV >= 32 ? 2 : 1;
+    constexpr int NKH = DK >= 32 ? 2 : 1;
+    p.vblocks = DV / (16 * NVT);
+    if (NC > 0) {
+        hipLaunchKernelGGL((delta_prep_kernel<C, DK, DV>), dim3(static_cast<unsigned>(heads * NC)), dim3(256), 0,
+                           stream, p);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((delta_state_kernel<C, DK, DV, NVT, NKH>), dim3(static_cast<unsigned>(heads * p.vblocks)),
+                       dim3(64 * NVT * NKH), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || NC == 0) return err;
+    hipLaunchKernelGGL((delta_output_kernel<C, DK, DV>), dim3(static_cast<unsigned>(heads * NC)), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <int C, int DK>
+hipError_t launch_delta_dk(const ChunkArgs& a, hipStream_t stream) {
+    switch (a.dv) {
+        case 16: return launch_delta_dv<C, DK, 16>(a, stream);
+        case 32: return launch_delta_dv<C, DK, 32>(a, stream);
+        case 64: return launch_delta_dv<C, DK, 64>(a, stream);
+        case 128: return launch_delta_dv<C, DK, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int C>
+hipError_t launch_delta(const ChunkArgs& a, hipStream_t stream) {
+    switch (a.dk) {
+        case 16: return launch_delta_dk<C, 16>(a, stream);
+        case 32: return launch_delta_dk<C, 32>(a, stream);
+        case 64: return launch_delta_dk<C, 64>(a, stream);
+        case 128: return launch_delta_dk<C, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ck
+}  // namespace glr

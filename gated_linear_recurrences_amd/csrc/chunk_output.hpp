@@ -71,8 +71,6 @@ struct OutLayout {
     static_assert(bytes <= 160 * 1024, "LDS budget of the output pass exceeded");
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
-
 template <int C, int DK, int DV, bool GLA, int NW>
 __global__ __launch_bounds__(64 * NW)
 void output_kernel(OutParams p) {

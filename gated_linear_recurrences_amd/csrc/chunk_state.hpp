@@ -49,12 +49,6 @@ struct StateParams {
     int H, T, dv, NC, vblocks, kblocks, remap;
 };
 
-// Row stride (bf16 elements) of a staged token-major tile `width` channels wide:
-// 16 more than the width (none for 16-wide tiles), so that rows sit 8 x odd banks
-// apart and the 8 rows read by half a wave of ds_read_b64_tr_b16 (8 bytes from
-// each of 4 lanes per row) fall on distinct banks of the 64.
-constexpr int tile_stride(int width) { return width == 16 ? 16 : width + 16; }
-
 // Staging-write placement of the 16-byte piece loaded by lane l of a wave-wide
 // load over a tile with PPR pieces per row: each group of 16 lanes writes 8 rows
 // x 2 pieces when PPR <= 8 (with the stride above, distinct banks), else a

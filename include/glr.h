@@ -84,7 +84,12 @@ typedef enum la_variant {
  * entry point does (status and la_last_error() as there); the pointers of the
  * entry point are not involved.  For bf16 storage, retention and GLA pass the
  * memory entering every chunk from their state pass to their output pass:
- * B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.
+ * B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.  The gated delta rule in bf16
+ * also passes, per (sequence, chunk), its WY factor W (chunk x d_k bf16), the
+ * pseudo-values (d_v x chunk float32) and the cumulative log-gates (chunk
+ * float32): with N = B * H * ceil(T / chunk) and a(x) = x rounded up to a
+ * multiple of 256, a(N*chunk*d_k*2) + a(N*d_v*chunk*4) + a(N*chunk*4) +
+ * a(N*d_v*d_k*2) bytes.  fp32 storage needs none.
  */
 la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int dk, int dv,
                                   int chunk, la_dtype dtype, size_t* bytes);

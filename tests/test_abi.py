@@ -80,6 +80,17 @@ def test_workspace_size_query(lib):
         assert _ws(lib, variant, T=0) == (_native.LA_OK, 0)
         assert _ws(lib, variant, B=0) == (_native.LA_OK, 0)
         assert _ws(lib, variant, dtype=0) == (_native.LA_OK, 0)      # fp32 storage: one fused kernel
+    # gated delta rule in bf16: W, pseudo-values, cumulative gates and the memory per chunk,
+    # each array rounded up to 256 bytes
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    for (B, H, T, dk, dv, C) in ((4, 16, 8192, 128, 128, 64), (1, 2, 65, 32, 64, 32), (1, 1, 40, 16, 16, 16)):
+        n = B * H * ((T + C - 1) // C)
+        want = a256(n * C * dk * 2) + a256(n * dv * C * 4) + a256(n * C * 4) + a256(n * dv * dk * 2)
+        assert _ws(lib, _native.LA_GDELTA, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C) == (_native.LA_OK, want)
+    assert _ws(lib, _native.LA_GDELTA, T=0) == (_native.LA_OK, 0)
+    assert _ws(lib, _native.LA_GDELTA, dtype=0) == (_native.LA_OK, 0)
     assert _ws(lib, 7)[0] == _native.LA_ERR_INVALID
     assert _ws(lib, 0, dk=24)[0] == _native.LA_ERR_UNSUPPORTED
     assert _ws(lib, 0, chunk=48)[0] == _native.LA_ERR_UNSUPPORTED
@@ -88,10 +99,10 @@ def test_workspace_size_query(lib):
     assert lib.la_chunk_workspace_size(0, 1, 1, 8, 16, 16, 16, 1, None) == _native.LA_ERR_INVALID
 
 
-@pytest.mark.parametrize("fn", ["la_chunk_fwd", "gla_chunk_fwd"])
+@pytest.mark.parametrize("fn", ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd"])
 def test_chunk_workspace_validation(lib, fn):
     st, need = _ws(lib, VARIANT[fn], T=40, chunk=16)
-    assert st == _native.LA_OK and need == 3 * 16 * 16 * 2
+    assert st == _native.LA_OK and need == (6400 if fn == "gdelta_chunk_fwd" else 3 * 16 * 16 * 2)
     assert _chunk(lib, fn, T=40, ws=None, q=None) == _native.LA_ERR_INVALID      # argument checks come first
     assert _chunk(lib, fn, T=40, ws=None) == _native.LA_ERR_INVALID
     assert b"workspace is NULL" in lib.la_last_error()

@@ -275,7 +275,7 @@ LAUNCH_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("kind", ["retention", "gla"])
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("shape", LAUNCH_SHAPES)
 def test_bf16_launch_shapes(kind, shape):
     w = make(kind, *shape, dtype="bf16", seed=300 + sum(shape), state=True)
@@ -286,24 +286,30 @@ def test_bf16_launch_shapes(kind, shape):
 
 # ----------------------------------------------------------------------------- workspace
 
-def _ret_call(w, workspace):
+def _ws_call(w, workspace):
     q, k, v = _t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16)
-    out, S = api.la_chunk_fwd(q, k, v, _t(w.log_gamma), chunk=w.chunk, s0=_t(w.s0), workspace=workspace)
+    if w.kind == "retention":
+        out, S = api.la_chunk_fwd(q, k, v, _t(w.log_gamma), chunk=w.chunk, s0=_t(w.s0), workspace=workspace)
+    else:
+        out, S = api.gdelta_chunk_fwd(q, k, v, _t(w.log_alpha), _t(w.beta), chunk=w.chunk, s0=_t(w.s0),
+                                      workspace=workspace)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64)
 
 
-def test_workspace_reused_and_garbage_filled():
+@pytest.mark.parametrize("kind", ["retention", "gdelta"])
+def test_workspace_reused_and_garbage_filled(kind):
     """A caller's workspace may hold anything on entry and serve call after call."""
-    w1 = make("retention", 2, 4, 300, 128, 128, 64, dtype="bf16", seed=41, state=True)
-    w2 = make("retention", 2, 4, 200, 128, 128, 64, dtype="bf16", seed=42, state=True)
-    need = api.workspace_size("retention", 2, 4, 300, 128, 128, 64)
-    assert need == 2 * 4 * 5 * 128 * 128 * 2
+    w1 = make(kind, 2, 4, 300, 128, 128, 64, dtype="bf16", seed=41, state=True)
+    w2 = make(kind, 2, 4, 200, 128, 128, 64, dtype="bf16", seed=42, state=True)
+    need = api.workspace_size(kind, 2, 4, 300, 128, 128, 64)
+    if kind == "retention":
+        assert need == 2 * 4 * 5 * 128 * 128 * 2
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)   # NaN bit patterns
     for w in (w1, w2, w1):
-        o, S = _ret_call(w, ws)
+        o, S = _ws_call(w, ws)
         o_ref, S_ref = run_oracle(w)
-        assert_parity(w, o, S, o_ref, S_ref, f"workspace T={w.q.shape[2]}")
+        assert_parity(w, o, S, o_ref, S_ref, f"{kind} workspace T={w.q.shape[2]}")
 
 
 def test_workspace_too_small_is_rejected():
