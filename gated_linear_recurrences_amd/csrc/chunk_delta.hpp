@@ -17,11 +17,12 @@
 //           blocked forward substitution on MFMA; W (bf16, token-major), U0
 //           (fp32, value-major) and G go to the workspace;
 //   state   (chunks in order) per chunk: store S_in (bf16), U = U0 - W S_in^T with
-//           the memory straight from the accumulators as the B operand, U back
-//           into the workspace in place of U0, then the carry K^T (weighted U);
-//   output  (all chunks in parallel) P = (Q K^T . Gamma) masked, o = e^G S_in q +
-//           P U, U read as a bf16 hi + lo pair (its rounding would otherwise
-//           dominate the output error).
+//           the memory straight from the accumulators as the B operand, then the
+//           carry K^T (weighted U);
+//   output  (all chunks in parallel) U = U0 - W S_in^T again from the stored bf16
+//           memory (the same operands the state pass used), P = (Q K^T . Gamma)
+//           masked, o = e^G S_in q + P U, U entering as a bf16 hi + lo pair (its
+//           rounding would otherwise dominate the output error).
 #pragma once
 
 #include "chunk_common.hpp"
@@ -277,11 +278,13 @@ void delta_prep_kernel(DeltaParams p) {
 // (two workgroup barriers, W and K double-buffered in LDS):
 //   phase 1  store the entering memory (bf16); partial W S^T over the wave's key
 //            tiles with the accumulators as the B operand; the key group 0 wave
-//            adds U0 (it alone reads U0, before U overwrites it); partials to LDS;
-//   phase 2  U = sum of the key groups' partials; key group 0 stores U in place of
-//            U0; the carry S^T <- e^(G_last) S^T + K^T (e^(G_last - G_j) u_j) with K^T
-//            read transposed from LDS; the next chunk is staged and the one after
+//            adds U0 (requested a chunk ahead); partials to LDS;
+//   phase 2  U = sum of the key groups' partials; the carry
+//            S^T <- e^(G_last) S^T + K^T (e^(G_last - G_j) u_j) with K^T read
+//            transposed from LDS; the next chunk is staged and the one after
 //            requested.
+// U itself is not stored: the output pass forms it again from U0, W and the stored
+// memory, which costs less HBM traffic than writing and re-reading it.
 template <int C, int DK, int NVT, int NKH>
 struct DStateLayout {
     static constexpr int WS = DK + 8;                 // W, natural 8-byte reads
@@ -317,8 +320,10 @@ void delta_state_kernel(DeltaParams p) {
     const int vt = wave % NVT, kh = wave / NVT;
     const int r16 = lane & 15, g = lane >> 4;
 
-    const int bh = blockIdx.x / p.vblocks;
-    const int v0 = (blockIdx.x % p.vblocks) * 16 * NVT + 16 * vt;   // this wave's value tile
+    // the value blocks of one head run on one XCD and share its L2 copy of W and K
+    const int lb = logical_block_of(blockIdx.x, gridDim.x, (gridDim.x & 7) == 0);
+    const int bh = lb / p.vblocks;
+    const int v0 = (lb % p.vblocks) * 16 * NVT + 16 * vt;   // this wave's value tile
     const int T = p.T, NC = p.NC;
     const int64_t tok0 = static_cast<int64_t>(bh) * T;
     const int key0 = 16 * KTW * kh;
@@ -364,7 +369,20 @@ void delta_state_kernel(DeltaParams p) {
         if (tid < C) sG(b)[tid] = rg;
     };
 
+    // U0 of the next chunk (key group 0 only), requested a chunk ahead: chunk c's U0 is
+    // consumed right after its W S^T and would otherwise expose a memory round trip
+    f32x4 u0n[CT];
+#pragma unroll
+    for (int jt = 0; jt < CT; ++jt) u0n[jt] = zf4();
+    auto load_u0 = [&](int cr) {
+        const int c = cr < NC ? cr : NC - 1;
+        const float* un = p.ws.u + ((static_cast<int64_t>(bh) * NC + c) * DV + v0 + r16) * C + 4 * g;
+#pragma unroll
+        for (int jt = 0; jt < CT; ++jt) u0n[jt] = ldf4(un + 16 * jt);
+    };
+
     if (NC > 0) {
+        if (kh == 0) load_u0(0);
         fetch(0);
         stage(0, 0);
         fetch(1);
@@ -372,14 +390,12 @@ void delta_state_kernel(DeltaParams p) {
         for (int c = 0; c < NC; ++c) {
             const int b = c & 1;
             const int64_t chunk = static_cast<int64_t>(bh) * NC + c;
-            float* const uc = p.ws.u + (chunk * DV + v0 + r16) * C;
 
             // ---- phase 1
             f32x4 u0[CT];
-            if (kh == 0) {
 #pragma unroll
-                for (int jt = 0; jt < CT; ++jt) u0[jt] = ldf4(uc + 16 * jt + 4 * g);
-            }
+            for (int jt = 0; jt < CT; ++jt) u0[jt] = u0n[jt];
+            if (kh == 0) load_u0(c + 1);
             u16* const st = p.ws.s + (chunk * DV + v0 + r16) * DK + key0 + 4 * g;
 #pragma unroll
             for (int t = 0; t < KTW; ++t) st4(st + 16 * t, cvt4(sacc[t]));
@@ -420,10 +436,6 @@ void delta_state_kernel(DeltaParams p) {
 #pragma unroll
                     for (int jt = 0; jt < CT; ++jt) U[jt] = U[jt] + ldf4(other + 16 * jt + 4 * g);
                 }
-            }
-            if (kh == 0) {
-#pragma unroll
-                for (int jt = 0; jt < CT; ++jt) stf4(uc + 16 * jt + 4 * g, U[jt]);
             }
             // carry: weights e^(G_last - G_j); padded tokens have U = 0 and a flat G
             const float* g_ = sG(b);
@@ -468,7 +480,9 @@ void delta_state_kernel(DeltaParams p) {
 // One workgroup (four waves) per (sequence, chunk); the same shape as the output
 // pass of retention: P tiles spread over the waves and shared in LDS, each wave a
 // pair of 16-channel value tiles, the readout with S rows from registers - here
-// scaled by e^(G_i) - plus P U with U^T rows read straight from the workspace as
+// scaled by e^(G_i) - plus P U. U^T rows start as U0 from the workspace; W takes
+// the place of k in LDS once P is formed, and W S_in^T (the S rows again as the B
+// operand) is subtracted in the accumulator layout of those rows. U enters P U as
 // a bf16 hi + lo pair.
 template <int C, int DK, int DV>
 struct DOutLayout {
@@ -512,10 +526,11 @@ void delta_output_kernel(DeltaParams p) {
     const int64_t chunk = static_cast<int64_t>(bh) * p.NC + c;
     const u16* sc = p.ws.s + chunk * DV * DK;
     const float* uc = p.ws.u + chunk * DV * C;
+    const u16* wc = p.ws.w + chunk * C * DK;
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
-    // ---- loads up front: q, k pieces; this wave's S rows and U^T rows
-    u16x8 rq[QP_PER], rk[QP_PER];
+    // ---- loads up front: q, k, W pieces; this wave's S rows and U0^T rows
+    u16x8 rq[QP_PER], rk[QP_PER], rw[QP_PER];
 #pragma unroll
     for (int i = 0; i < QP_PER; ++i) {
         const int idx = tid + i * NT;
@@ -523,11 +538,12 @@ void delta_output_kernel(DeltaParams p) {
         const unsigned off = (idx < QP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
         rq[i] = *reinterpret_cast<const u16x8*>(p.q + tok0 * DK + off);
         rk[i] = *reinterpret_cast<const u16x8*>(p.k + tok0 * DK + off);
+        rw[i] = *reinterpret_cast<const u16x8*>(wc + off);
     }
     const float gl = (tid < C) ? p.ws.g[chunk * C + tid] : 0.f;
     const int pp = w % NP;
     u16x8 sa[2][KB];
-    f32x4 ua[2][JB][2];   // U^T rows: [tile][jb][half], tokens 32jb + 16 half + 4g + e
+    f32x4 ua[2][JB][2];   // U0^T (later U^T) rows: [tile][jb][half], tokens 32jb + 16 half + 4g + e
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         const int vrow = (DV >= 32) ? 32 * pp + 16 * tt + r16 : r16;
@@ -587,6 +603,33 @@ void delta_output_kernel(DeltaParams p) {
         st4(sP + i * PS + 16 * jt + 4 * g, pv);
     }
     lds_barrier();
+
+    // ---- U = U0 - W S_in^T: W over k in LDS, then per value tile and token tile
+    // D[token 4g + r][value r16] += W[token][keys] S[value][keys]
+#pragma unroll
+    for (int i = 0; i < QP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < QP) {
+            const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<u16x8*>(sK + j * QS + col) = (j < n) ? rw[i] : z8;
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int tt = 0; tt < (DV >= 32 ? 2 : 1); ++tt) {
+#pragma unroll
+        for (int jt = 0; jt < CT; ++jt) {
+            f32x4 acc = zf4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int col = 32 * kb + 8 * g;
+                const bf16x8 wa = (col < DK) ? *reinterpret_cast<const bf16x8*>(sK + (16 * jt + r16) * QS + col)
+                                             : as_bf16x8(z8);
+                acc = mfma_16x16x32(wa, as_bf16x8(sa[tt][kb]), acc);
+            }
+            ua[tt][jt >> 1][jt & 1] = ua[tt][jt >> 1][jt & 1] - acc;
+        }
+    }
 
     // ---- outputs: e^(G_i) S_in q_i + P U
     for (int item = w; item < CT * NP; item += NW) {
