@@ -75,21 +75,36 @@ struct DeltaParams {
 
 // ====================================================================== prep
 //
-// One workgroup (four waves) per (sequence, chunk).
+// One workgroup (four waves) per (sequence, chunk). With T = (I + A)^-1 the two
+// right-hand sides differ only by a diagonal on the right of T, so the kernel forms
+// T itself (block lower triangular) with beta and beta e^G folded into its columns,
+//   T_U = T diag(beta),   T_W = T diag(beta e^G),   U0 = T_U V,   W = T_W K,
+// and the two products are plain MFMA contractions over the chunk, independent for
+// every output tile. Steps (a workgroup barrier between each):
+//   stage k, v; cumulative gates (wave prefix scan)
+//   A tiles (K K^T . Gamma, row-scaled by beta, strictly lower) in fp32
+//   T's diagonal blocks D_b = (I + A_bb)^-1 by forward substitution (one wave)
+//   T's off-diagonal blocks, one column block per wave:
+//       T_iw = -D_i sum_{w <= m < i} A_im T_mw,   T_ww = D_w
+//   U0 tiles (stored value-major, fp32) and W tiles (through LDS, stored
+//   token-major, bf16).
 template <int C, int DK, int DV>
 struct PrepLayout {
     static constexpr int CT = C / 16;
     static constexpr int KS = tile_stride(DK);   // staged k (natural and transposed reads)
     static constexpr int VS = tile_stride(DV);   // staged v (transposed reads)
-    static constexpr int WS = DK + 8;                 // W staged for coalesced stores
-    static constexpr int AS = C + 4;                  // A, fp32
+    static constexpr int WS = DK + 8;            // W staged for coalesced stores
+    static constexpr int AS = C + 4;             // A, fp32
+    static constexpr int TS = C + 4;             // T_U, T_W, bf16
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    static constexpr int mx(int a, int b) { return a > b ? a : b; }
     static constexpr int oK = 0;
     static constexpr int oV = oK + al(C * KS * 2);
-    static constexpr int oW = oV + al(C * VS * 2);
-    static constexpr int oA = oW + al(C * WS * 2);
-    static constexpr int oD = oA + al(C * AS * 4);
-    static constexpr int oG = oD + al(CT * 256 * 4);
+    static constexpr int oA = oV + al(C * VS * 2);     // A, later W (A is dead by then)
+    static constexpr int oD = oA + mx(al(C * AS * 4), al(C * WS * 2));
+    static constexpr int oTU = oD + al(CT * 256 * 4);
+    static constexpr int oTW = oTU + al(C * TS * 2);
+    static constexpr int oG = oTW + al(C * TS * 2);
     static constexpr int oB = oG + al(C * 4);
     static constexpr int bytes = oB + al(C * 4);
     static_assert(bytes <= 160 * 1024, "LDS budget of the prep kernel exceeded");
@@ -100,18 +115,22 @@ __global__ __launch_bounds__(256)
 void delta_prep_kernel(DeltaParams p) {
     using Lay = PrepLayout<C, DK, DV>;
     constexpr int CT = C / 16, NT = 256, NW = 4;
-    constexpr int KS = Lay::KS, VS = Lay::VS, WS = Lay::WS, AS = Lay::AS;
+    constexpr int KS = Lay::KS, VS = Lay::VS, WS = Lay::WS, AS = Lay::AS, TS = Lay::TS;
     constexpr int KB = (DK + 31) / 32;
     constexpr int KP = C * DK / 8, KP_PER = (KP + NT - 1) / NT;
     constexpr int VP = C * DV / 8, VP_PER = (VP + NT - 1) / NT;
     constexpr int NPAIR = CT * (CT + 1) / 2;
+    constexpr int NTW = DK / 16, NTU = DV / 16, NTT = NTW + NTU, NT_PER = (NTT + NW - 1) / NW;
+    static_assert(CT <= NW, "one wave per column block of T");
 
     __shared__ __align__(16) unsigned char smem[Lay::bytes];
     u16* const sK = reinterpret_cast<u16*>(smem + Lay::oK);
     u16* const sV = reinterpret_cast<u16*>(smem + Lay::oV);
-    u16* const sW = reinterpret_cast<u16*>(smem + Lay::oW);
     float* const sA = reinterpret_cast<float*>(smem + Lay::oA);
+    u16* const sW = reinterpret_cast<u16*>(smem + Lay::oA);
     float* const sD = reinterpret_cast<float*>(smem + Lay::oD);
+    u16* const sTU = reinterpret_cast<u16*>(smem + Lay::oTU);
+    u16* const sTW = reinterpret_cast<u16*>(smem + Lay::oTW);
     float* const sG = reinterpret_cast<float*>(smem + Lay::oG);
     float* const sBeta = reinterpret_cast<float*>(smem + Lay::oB);
 
@@ -126,23 +145,20 @@ void delta_prep_kernel(DeltaParams p) {
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
     // ---- stage k, v (rows past the end zero); cumulative gates and write strengths
+    u16x8 rk[KP_PER], rv[VP_PER];
 #pragma unroll
     for (int i = 0; i < KP_PER; ++i) {
         const int idx = tid + i * NT;
-        if (idx < KP) {
-            const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            const u16x8 x = *reinterpret_cast<const u16x8*>(p.k + (tok0 + (j < n ? j : 0)) * DK + col);
-            *reinterpret_cast<u16x8*>(sK + j * KS + col) = (j < n) ? x : z8;
-        }
+        const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+        const unsigned off = (idx < KP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
+        rk[i] = *reinterpret_cast<const u16x8*>(p.k + tok0 * DK + off);
     }
 #pragma unroll
     for (int i = 0; i < VP_PER; ++i) {
         const int idx = tid + i * NT;
-        if (idx < VP) {
-            const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
-            const u16x8 x = *reinterpret_cast<const u16x8*>(p.v + (tok0 + (j < n ? j : 0)) * DV + col);
-            *reinterpret_cast<u16x8*>(sV + j * VS + col) = (j < n) ? x : z8;
-        }
+        const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+        const unsigned off = (idx < VP && j < n) ? static_cast<unsigned>(j * DV + col) : 0u;
+        rv[i] = *reinterpret_cast<const u16x8*>(p.v + tok0 * DV + off);
     }
     if (w == 0) {
         float la = 0.f, be = 0.f;
@@ -155,6 +171,22 @@ void delta_prep_kernel(DeltaParams p) {
             sG[lane] = G;
             sBeta[lane] = be;
             p.ws.g[chunk * C + lane] = G;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < KP) {
+            const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<u16x8*>(sK + j * KS + col) = (j < n) ? rk[i] : z8;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < VP) {
+            const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            *reinterpret_cast<u16x8*>(sV + j * VS + col) = (j < n) ? rv[i] : z8;
         }
     }
     lds_barrier();
@@ -207,55 +239,69 @@ void delta_prep_kernel(DeltaParams p) {
     }
     lds_barrier();
 
-    // ---- blocked forward substitution X_b = D_b (R_b - sum_{kk<b} A_{b,kk} X_kk) for the
-    // column tiles of W (R = diag(beta e^G) K) and U0 (R = diag(beta) V); lane (r16, g)
-    // of a tile holds rows 16b + 4g + e of column r16
-    auto solve = [&](auto rhs, f32x4 (&X)[CT]) {
+    // ---- column block w of T: lane (r16, g) holds T[16i + 4g + r][16w + r16];
+    // written as T_U and T_W with the column's factor
+    if (w < CT) {
+        const float fu = sBeta[16 * w + r16];
+        const float fw = fu * ex2(sG[16 * w + r16]);
+        f32x4 tcol[CT];
 #pragma unroll
-        for (int b = 0; b < CT; ++b) {
-            f32x4 acc = rhs(b);
+        for (int i = 0; i < CT; ++i) {
+            if (i < w) continue;
+            f32x4 t;
+            if (i == w) {
 #pragma unroll
-            for (int kk = 0; kk < b; ++kk) {
-                const f32x4 a = ldf4(sA + (16 * b + r16) * AS + 16 * kk + 4 * g);
-                acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt4(-a), cvt4(X[kk]), acc, 0, 0, 0);
-            }
-            const f32x4 d = ldf4(sD + b * 256 + r16 * 16 + 4 * g);
-            X[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt4(d), cvt4(acc), zf4(), 0, 0, 0);
-        }
-    };
-    constexpr int NTW = DK / 16, NTU = DV / 16;
-    float* const ug = p.ws.u + chunk * DV * C;
-    for (int nt = w; nt < NTW + NTU; nt += NW) {
-        f32x4 X[CT];
-        if (nt < NTW) {
-            solve([&](int b) {
-                const bf16x4 kv = tr_op<KS>(sK, 16 * b, 16 * nt, r16, g);
-                f32x4 r;
+                for (int r = 0; r < 4; ++r) t[r] = sD[w * 256 + (4 * g + r) * 16 + r16];
+            } else {
+                f32x4 acc = zf4();
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 16 * b + 4 * g + e;
-                    r[e] = static_cast<float>(kv[e]) * sBeta[j] * ex2(sG[j]);
+                for (int m = 0; m < CT; ++m) {
+                    if (m < w || m >= i) continue;
+                    const f32x4 a = ldf4(sA + (16 * i + r16) * AS + 16 * m + 4 * g);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt4(a), cvt4(tcol[m]), acc, 0, 0, 0);
                 }
-                return r;
-            }, X);
-            // W tile -> LDS (token-major), stored coalesced below
+                const f32x4 d = ldf4(sD + i * 256 + r16 * 16 + 4 * g);
+                t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt4(-d), cvt4(acc), zf4(), 0, 0, 0);
+            }
+            tcol[i] = t;
 #pragma unroll
-            for (int b = 0; b < CT; ++b)
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i + 4 * g + r;
+                sTU[row * TS + 16 * w + r16] = __builtin_bit_cast(u16, static_cast<__bf16>(t[r] * fu));
+                sTW[row * TS + 16 * w + r16] = __builtin_bit_cast(u16, static_cast<__bf16>(t[r] * fw));
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- U0 = T_U V (value-major fp32 to the workspace), W = T_W K (through LDS):
+    // row block it of T contracts over the 16(it + 1) tokens it reaches
+    float* const ug = p.ws.u + chunk * DV * C;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sW[(16 * b + 4 * g + e) * WS + 16 * nt + r16] = __builtin_bit_cast(u16, static_cast<__bf16>(X[b][e]));
-        } else {
-            const int ut = nt - NTW;
-            solve([&](int b) {
-                const bf16x4 vv = tr_op<VS>(sV, 16 * b, 16 * ut, r16, g);
-                f32x4 r;
+    for (int s = 0; s < NT_PER; ++s) {
+        const int nt = w + NW * s;
+        if (nt >= NTT) break;
+        const bool isw = nt < NTW;
+        const u16* const tmat = isw ? sTW : sTU;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[e] = static_cast<float>(vv[e]) * sBeta[16 * b + 4 * g + e];
-                return r;
-            }, X);
-            // U0 value-major: lane holds U0[16b + 4g + e][16ut + r16]
+        for (int it = 0; it < CT; ++it) {
+            f32x4 acc = zf4();
 #pragma unroll
-            for (int b = 0; b < CT; ++b) stf4(ug + (16 * ut + r16) * C + 16 * b + 4 * g, X[b]);
+            for (int kb = 0; kb < (CT + 1) / 2; ++kb) {
+                if (2 * kb > it) continue;
+                const bool hi = 2 * kb + 1 <= it;
+                const u16* trow = tmat + (16 * it + r16) * TS + 32 * kb + 4 * g;
+                const bf16x8 tb = join8(ld4(trow), hi ? ld4(trow + 16) : zero4());
+                if (isw) acc = mfma_16x16x32(tr_split<KS>(sK, kb, 16 * nt, hi, r16, g), tb, acc);
+                else acc = mfma_16x16x32(tb, tr_split<VS>(sV, kb, 16 * (nt - NTW), hi, r16, g), acc);
+            }
+            if (isw) {
+                // acc[r] = W[16it + r16][16nt + 4g + r]
+                st4(sW + (16 * it + r16) * WS + 16 * nt + 4 * g, cvt4(acc));
+            } else {
+                // acc[r] = U0[16it + 4g + r][16(nt - NTW) + r16]
+                stf4(ug + (16 * (nt - NTW) + r16) * C + 16 * it + 4 * g, acc);
+            }
         }
     }
     lds_barrier();
