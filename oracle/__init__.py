@@ -24,6 +24,9 @@ from .glr_oracle import (  # noqa: F401
     retention_recurrent,
     retention_quadratic,
     retention_chunkwise,
+    scalar_recurrent,
+    scalar_quadratic,
+    scalar_chunkwise,
     gla_recurrent,
     gla_quadratic,
     gla_chunkwise,

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle: three gate variants, three evaluation forms each, and one decode step.
+"""fp64 CPU oracle: four gate variants, three evaluation forms each, and one decode step.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring): plain numpy in float64,
 shared with nothing on the GPU side.
@@ -24,6 +24,9 @@ online" of the same page):
 
 * retention (RetNet row, fixed per-head decay): ``S_t = g_h S_{t-1} + v_t k_t^T``
   with ``g_h = exp(log_gamma[h])``;
+* scalar data-dependent decay (the Mamba-2 half of the "Mamba-2 / RetNet" row):
+  ``S_t = alpha_t S_{t-1} + v_t k_t^T``, one ``alpha_t = exp(log_alpha[..., t])``
+  per token and head;
 * GLA (diagonal data-dependent gate, one per key channel):
   ``S_t = S_{t-1} Diag(alpha_t) + v_t k_t^T``, ``alpha_t = exp(log_alpha[..., t, :])``;
 * gated delta rule (Gated DeltaNet row):
@@ -41,6 +44,9 @@ __all__ = [
     "retention_recurrent",
     "retention_quadratic",
     "retention_chunkwise",
+    "scalar_recurrent",
+    "scalar_quadratic",
+    "scalar_chunkwise",
     "gla_recurrent",
     "gla_quadratic",
     "gla_chunkwise",
@@ -177,6 +183,80 @@ def retention_chunkwise(q, k, v, log_gamma, chunk, s0=None):
         w = np.exp(lg[..., None] * (n - 1 - np.arange(n)))    # g^(n-1-j)
         S = (np.exp(lg * n)[..., None, None] * S
              + np.einsum("...j,...jm,...jc->...mc", w, V, K))
+    return o, S
+
+
+# --------------------------------------------------------------------------- scalar decay
+
+def scalar_recurrent(q, k, v, log_alpha, s0=None):
+    """Recurrent form (the definition): ``S_t = alpha_t S_{t-1} + v_t k_t^T``, ``o_t = S_t q_t``.
+
+    "Scrivere meglio nella memoria", section "Dimenticare: i gate", scalar
+    decay equation with the gate produced from the input at every step (the
+    Mamba-2 reading of the same equation; one number per token and head).
+    ``log_alpha`` is ``[B, H, T]``.
+    """
+    q, k, v, la = _f64(q, k, v, log_alpha)
+    S = _init_state(q, v, s0)
+    T = q.shape[-2]
+    o = np.zeros(v.shape)
+    for t in range(T):
+        S = np.exp(la[..., t])[..., None, None] * S + _outer(v[..., t, :], k[..., t, :])
+        o[..., t, :] = _read(S, q[..., t, :])
+    return o, S
+
+
+def scalar_quadratic(q, k, v, log_alpha, s0=None):
+    """Parallel form, the recurrence unrolled over the whole sequence.
+
+    Same section: what is written at step j reaches step t weighted by the
+    product of the gates of steps j+1 .. t. With ``G_t = sum_{r<=t} log alpha_r``
+    that weight is ``exp(G_t - G_j)``, so
+    ``o_t = sum_{j<=t} exp(G_t - G_j) (q_t . k_j) v_j + exp(G_t) S_0 q_t`` and
+    ``S_T = exp(G_{T-1}) S_0 + sum_j exp(G_{T-1} - G_j) v_j k_j^T``.
+    """
+    q, k, v, la = _f64(q, k, v, log_alpha)
+    T = q.shape[-2]
+    G = np.cumsum(la, axis=-1)                                      # [..., T]
+    causal = np.arange(T)[:, None] >= np.arange(T)[None, :]
+    diff = G[..., :, None] - G[..., None, :]
+    D = np.where(causal, np.exp(np.where(causal, diff, 0.0)), 0.0)
+    scores = np.einsum("...ic,...jc->...ij", q, k)
+    o = np.einsum("...ij,...jm->...im", scores * D, v)
+    S0 = _init_state(q, v, s0)
+    o += np.exp(G)[..., :, None] * np.einsum("...mc,...ic->...im", S0, q)
+    if T == 0:
+        return o, S0
+    last = G[..., -1]
+    S = np.exp(last)[..., None, None] * S0 + np.einsum(
+        "...j,...jm,...jc->...mc", np.exp(last[..., None] - G), v, k)
+    return o, S
+
+
+def scalar_chunkwise(q, k, v, log_alpha, chunk, s0=None):
+    """Chunkwise form: the parallel form inside each block, the memory carried between
+    blocks (the RetNet page, section on retention, chunkwise form, with the decay
+    now read from the gates). With local inclusive cumulative log-gates ``G_i``:
+    ``o_i = sum_{j<=i} exp(G_i - G_j) (q_i . k_j) v_j + exp(G_i) S_in q_i``,
+    ``S_out = exp(G_{n-1}) S_in + sum_j exp(G_{n-1} - G_j) v_j k_j^T``.
+    """
+    q, k, v, la = _f64(q, k, v, log_alpha)
+    T = q.shape[-2]
+    S = _init_state(q, v, s0)
+    o = np.zeros(v.shape)
+    for t0 in range(0, T, chunk):
+        n = min(chunk, T - t0)
+        Q, K, V = q[..., t0:t0 + n, :], k[..., t0:t0 + n, :], v[..., t0:t0 + n, :]
+        G = np.cumsum(la[..., t0:t0 + n], axis=-1)
+        causal = np.arange(n)[:, None] >= np.arange(n)[None, :]
+        diff = G[..., :, None] - G[..., None, :]
+        D = np.where(causal, np.exp(np.where(causal, diff, 0.0)), 0.0)
+        P = np.einsum("...ic,...jc->...ij", Q, K) * D
+        o[..., t0:t0 + n, :] = (np.einsum("...ij,...jm->...im", P, V)
+                                + np.exp(G)[..., :, None] * np.einsum("...mc,...ic->...im", S, Q))
+        last = G[..., -1]
+        S = (np.exp(last)[..., None, None] * S
+             + np.einsum("...j,...jm,...jc->...mc", np.exp(last[..., None] - G), V, K))
     return o, S
 
 

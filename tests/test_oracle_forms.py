@@ -60,6 +60,21 @@ def test_gla_forms_agree(shape, chunk, state):
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("chunk", CHUNKS)
 @pytest.mark.parametrize("state", [False, True])
+def test_scalar_forms_agree(shape, chunk, state):
+    rng, q, k, v, s0 = _rand(5, *shape, state=state)
+    B, H, T, dk, dv = shape
+    la = -np.logaddexp(0.0, -rng.standard_normal((B, H, T))) / 2.0
+    o_r, S_r = orc.scalar_recurrent(q, k, v, la, s0=s0)
+    o_q, S_q = orc.scalar_quadratic(q, k, v, la, s0=s0)
+    o_c, S_c = orc.scalar_chunkwise(q, k, v, la, chunk, s0=s0)
+    for o, S in ((o_q, S_q), (o_c, S_c)):
+        np.testing.assert_allclose(o, o_r, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(S, S_r, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("chunk", CHUNKS)
+@pytest.mark.parametrize("state", [False, True])
 def test_gdelta_forms_agree(shape, chunk, state):
     rng, q, k, v, s0 = _rand(3, *shape, state=state)
     B, H, T, dk, dv = shape
@@ -85,6 +100,9 @@ def test_empty_sequence_passes_state_through():
                lambda s: orc.gla_recurrent(q, k, v, la_d, s0=s),
                lambda s: orc.gla_quadratic(q, k, v, la_d, s0=s),
                lambda s: orc.gla_chunkwise(q, k, v, la_d, 4, s0=s),
+               lambda s: orc.scalar_recurrent(q, k, v, la_s, s0=s),
+               lambda s: orc.scalar_quadratic(q, k, v, la_s, s0=s),
+               lambda s: orc.scalar_chunkwise(q, k, v, la_s, 4, s0=s),
                lambda s: orc.gdelta_recurrent(q, k, v, la_s, la_s, s0=s),
                lambda s: orc.gdelta_quadratic(q, k, v, la_s, la_s, s0=s),
                lambda s: orc.gdelta_chunkwise(q, k, v, la_s, la_s, 4, s0=s)):
@@ -139,6 +157,50 @@ def test_retention_and_gla_brute_force_double_sum():
                  orc.retention_quadratic(a4(q), a4(k), a4(v), lg, s0=s0[None, None]),
                  orc.retention_chunkwise(a4(q), a4(k), a4(v), lg, 4, s0=s0[None, None])):
         np.testing.assert_allclose(o[0, 0], want, atol=1e-13)
+
+
+def test_scalar_brute_force_gate_products():
+    """Scalar data-dependent decay: what is written at step j reaches step t weighted by
+    alpha_{j+1} ... alpha_t (one number per step for the whole memory), and the handed-over
+    memory by alpha_1 ... alpha_t; explicit products in pure Python loops (T <= 7)."""
+    rng = np.random.default_rng(23)
+    T, dk, dv = 7, 3, 2
+    q = rng.standard_normal((T, dk)); k = rng.standard_normal((T, dk)); v = rng.standard_normal((T, dv))
+    s0 = rng.standard_normal((dv, dk))
+    a = rng.uniform(0.2, 0.99, T)
+    want = np.zeros((T, dv))
+    want_S = np.zeros((dv, dk))
+    for t in range(T):
+        dec0 = 1.0
+        for r in range(t + 1):
+            dec0 *= a[r]
+        for m in range(dv):
+            tot = sum(dec0 * s0[m, c] * q[t, c] for c in range(dk))
+            for j in range(t + 1):
+                dec = 1.0
+                for r in range(j + 1, t + 1):
+                    dec *= a[r]
+                tot += dec * sum(q[t, c] * k[j, c] for c in range(dk)) * v[j, m]
+            want[t, m] = tot
+    for m in range(dv):
+        for c in range(dk):
+            dec0 = 1.0
+            for r in range(T):
+                dec0 *= a[r]
+            tot = dec0 * s0[m, c]
+            for j in range(T):
+                dec = 1.0
+                for r in range(j + 1, T):
+                    dec *= a[r]
+                tot += dec * v[j, m] * k[j, c]
+            want_S[m, c] = tot
+    a4 = lambda x: x[None, None]
+    la = np.log(a)
+    for o, S in (orc.scalar_recurrent(a4(q), a4(k), a4(v), a4(la), s0=s0[None, None]),
+                 orc.scalar_quadratic(a4(q), a4(k), a4(v), a4(la), s0=s0[None, None]),
+                 orc.scalar_chunkwise(a4(q), a4(k), a4(v), a4(la), 3, s0=s0[None, None])):
+        np.testing.assert_allclose(o[0, 0], want, atol=1e-13)
+        np.testing.assert_allclose(S[0, 0], want_S, atol=1e-13)
 
 
 def test_gdelta_brute_force_transition_products():
@@ -197,6 +259,8 @@ def test_resume_from_handed_over_state(split):
     la_s = -np.logaddexp(0.0, rng.standard_normal(q.shape[:-1])) / 8.0
     beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(q.shape[:-1])))
     runs = {
+        "scalar": lambda sl, s: orc.scalar_chunkwise(q[..., sl, :], k[..., sl, :], v[..., sl, :], la_s[..., sl], 16,
+                                                     s0=s),
         "retention": lambda sl, s: orc.retention_chunkwise(q[..., sl, :], k[..., sl, :], v[..., sl, :], lg, 16, s0=s),
         "gla": lambda sl, s: orc.gla_chunkwise(q[..., sl, :], k[..., sl, :], v[..., sl, :], la_d[..., sl, :], 16, s0=s),
         "gdelta": lambda sl, s: orc.gdelta_chunkwise(q[..., sl, :], k[..., sl, :], v[..., sl, :],

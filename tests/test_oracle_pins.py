@@ -351,6 +351,40 @@ def test_gla_constant_gate_is_retention():
     np.testing.assert_allclose(S_g, S_r, atol=1e-12)
 
 
+def test_scalar_gate_special_cases(golden_dir):
+    """The scalar data-dependent decay against the rows it sits between in the pages'
+    hierarchy (fixed scalar -> data-dependent scalar -> diagonal): a gate that is the
+    same at every step is retention; the same gate copied into every key channel is GLA;
+    alpha = 1 is pure accumulation, S_T = S_0 + sum_j v_j k_j^T; and the worked example of
+    the RetNet page (scores 6, 7, 8, total halved each step) gives 6, 10, 13."""
+    rng = np.random.default_rng(15)
+    B, H, T, dk, dv = 2, 3, 21, 5, 4
+    q = rng.standard_normal((B, H, T, dk)); k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv)); s0 = rng.standard_normal((B, H, dv, dk))
+    lg = np.log(np.array([0.5, 0.9, 0.99]))
+    la_const = np.broadcast_to(lg[None, :, None], (B, H, T))
+    o_r, S_r = orc.retention_recurrent(q, k, v, lg, s0=s0)
+    for fn in (orc.scalar_recurrent, orc.scalar_quadratic):
+        o_s, S_s = fn(q, k, v, la_const, s0=s0)
+        np.testing.assert_allclose(o_s, o_r, atol=1e-12)
+        np.testing.assert_allclose(S_s, S_r, atol=1e-12)
+    la = -np.logaddexp(0.0, -rng.standard_normal((B, H, T)))
+    o_g, S_g = orc.gla_recurrent(q, k, v, np.broadcast_to(la[..., None], (B, H, T, dk)), s0=s0)
+    o_s, S_s = orc.scalar_chunkwise(q, k, v, la, 8, s0=s0)
+    np.testing.assert_allclose(o_s, o_g, atol=1e-12)
+    np.testing.assert_allclose(S_s, S_g, atol=1e-12)
+    _, S_acc = orc.scalar_chunkwise(q, k, v, np.zeros((B, H, T)), 8, s0=s0)
+    np.testing.assert_allclose(S_acc, s0 + np.einsum("bhtm,bhtc->bhmc", v, k), atol=1e-12)
+    g = _load(golden_dir, "retention_worked_example.json")
+    sv = _scalar_seq(g["scores"])
+    ones = np.ones_like(sv)
+    la_w = np.full(sv.shape[:-1], np.log(g["decay"]))
+    for o, _ in (orc.scalar_recurrent(ones, ones, sv, la_w),
+                 orc.scalar_quadratic(ones, ones, sv, la_w),
+                 orc.scalar_chunkwise(ones, ones, sv, la_w, chunk=g["block"])):
+        np.testing.assert_allclose(o.reshape(-1), g["running_totals"], atol=1e-12)
+
+
 def test_forward_substitution_matches_library_solve():
     """The oracle's triangular solve agrees with LAPACK's general solver."""
     rng = np.random.default_rng(14)
