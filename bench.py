@@ -15,8 +15,8 @@ against HBM with the algorithmic bytes of the method (q, k, v read, o and the
 final memory written); ``traffic`` is the HBM traffic the counters measured for
 one call, snapshots included; ``mfma`` gives the same run against the dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on the host; ``others``
-reports the per-channel-gate (GLA), gated-delta and decode workloads measured
-the same way.
+reports the per-channel-gate (GLA), gated-delta, scalar data-dependent decay
+and decode workloads measured the same way.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
     python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
@@ -46,13 +46,13 @@ def algorithmic_counts(kind, B, H, T, d, chunk, elem_bytes=2):
     """Algorithmic flops and HBM bytes of one chunked-forward launch.
 
     Bytes: read q, k, v (and the gates), write o and the final memory.
-    Flops per token-head (chunk C, head size d): retention and GLA 4Cd + 4d^2
+    Flops per token-head (chunk C, head size d): retention, the scalar decay and GLA 4Cd + 4d^2
     (q.k^T and P.V over the C x C block, S q and k^T v); the gated delta rule
     8Cd + 6d^2 + 2C^2/3 (K K^T, Q K^T, T.R for W and U0, P.U, W S^T, Q S^T,
     U^T K and the triangular solve)."""
     th = B * H * T
     tok_bytes = 4 * d * elem_bytes
-    gate_bytes = {"retention": 0, "gla": 4 * d, "gdelta": 8}[kind]
+    gate_bytes = {"retention": 0, "mamba2": 4, "gla": 4 * d, "gdelta": 8}[kind]
     state_bytes = B * H * d * d * 4
     bytes_ = th * (tok_bytes + gate_bytes) + state_bytes
     if kind == "gdelta":
@@ -91,6 +91,9 @@ def make_call(kind, api, bufs, chunk, torch):
     if kind == "gla":
         return lambda: api.gla_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_alpha"], chunk=chunk, o=o, s_out=s_out,
                                          workspace=ws)
+    if kind == "mamba2":
+        return lambda: api.mamba2_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_alpha"], chunk=chunk, o=o,
+                                            s_out=s_out, workspace=ws)
     return lambda: api.gdelta_chunk_fwd(q, bufs["k"], bufs["v"], bufs["log_alpha"], bufs["beta"], chunk=chunk,
                                         o=o, s_out=s_out, workspace=ws)
 
@@ -130,7 +133,7 @@ def bench_chunk(name, steps, warmup, torch, api, synthetic, dev, n_sets=N_SETS):
             kind = base.pop("kind")
             seed = base.pop("seed") + 1000 * s
             fn = {"retention": synthetic.retention_inputs, "gla": synthetic.gla_inputs,
-                  "gdelta": synthetic.gdelta_inputs}[kind]
+                  "gdelta": synthetic.gdelta_inputs, "mamba2": synthetic.mamba2_inputs}[kind]
             kw = dict(chunk=base["chunk"], dtype=base["dtype"], seed=seed)
             w = fn(base["B"], base["H"], base["T"], base["dk"], base["dv"], **kw)
         sets.append(make_call(c["kind"], api, upload(w, torch, dev), c["chunk"], torch))
@@ -311,7 +314,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-others", action="store_true", help="skip the GLA, gated-delta and decode workloads")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the GLA, gated-delta, scalar-decay and decode workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
@@ -339,7 +343,7 @@ def main():
     main_r = bench_chunk(MAIN, args.steps, args.warmup, torch, api, synthetic, dev)
     others = {}
     if not args.no_others:
-        for name in ("gla_b8h16_t4096_d128", "gdelta_b4h16_t8192_d128"):
+        for name in ("gla_b8h16_t4096_d128", "gdelta_b4h16_t8192_d128", "mamba2_b8h16_t4096_d128"):
             r = bench_chunk(name, max(20, args.steps // 4), max(3, args.warmup // 4), torch, api, synthetic, dev,
                             n_sets=1)
             r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS

@@ -11,11 +11,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libglr.so")
 
 LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
-LA_RETENTION, LA_GLA, LA_GDELTA = 0, 1, 2
+LA_RETENTION, LA_GLA, LA_GDELTA, LA_MAMBA2 = 0, 1, 2, 3
 
 EXPORTED = (
     "la_chunk_workspace_size",
     "la_chunk_fwd",
+    "mamba2_chunk_fwd",
     "gla_chunk_fwd",
     "gdelta_chunk_fwd",
     "la_recurrent_step",
@@ -49,11 +50,12 @@ def load():
     chunk = [P, P, P, F, F, P, F, I, I, I, I, I, I, I, P, Z, P]
     lib.la_chunk_fwd.argtypes = chunk
     lib.gla_chunk_fwd.argtypes = chunk
+    lib.mamba2_chunk_fwd.argtypes = chunk
     lib.gdelta_chunk_fwd.argtypes = [P, P, P, F, F, F, P, F, I, I, I, I, I, I, I, P, Z, P]
     lib.la_chunk_workspace_size.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.la_chunk_workspace_size.restype = ctypes.c_int
     lib.la_recurrent_step.argtypes = [P, P, P, F, F, P, I, I, I, I, I, P]
-    for name in ("la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"):
+    for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"):
         getattr(lib, name).restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
     lib.la_status_str.restype = ctypes.c_char_p

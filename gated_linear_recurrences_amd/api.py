@@ -12,7 +12,8 @@ import torch
 
 from . import _native
 
-__all__ = ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step", "workspace_size"]
+__all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step",
+           "workspace_size"]
 
 
 def _dtype_code(t):
@@ -99,6 +100,22 @@ def la_chunk_fwd(q, k, v, log_gamma, chunk=64, s0=None, o=None, s_out=None, retu
     return o, s_out
 
 
+def mamba2_chunk_fwd(q, k, v, log_alpha, chunk=64, s0=None, o=None, s_out=None, return_state=True,
+                     workspace=None):
+    """Scalar data-dependent decay: S_t = alpha_t S_{t-1} + v_t k_t^T, o_t = S_t q_t.
+
+    log_alpha [B,H,T] fp32 (log of one gate per token and head). Returns (o, s_out)."""
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
+    _require(log_alpha, "log_alpha", (B, H, T), torch.float32, q.device)
+    ws, ws_bytes = _workspace(_native.LA_MAMBA2, dims, chunk, q, workspace)
+    lib = _native.load()
+    _native.check(lib.mamba2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(s0), _ptr(o),
+                                       _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q), _ptr(ws), ws_bytes,
+                                       _stream(q.device)))
+    return o, s_out
+
+
 def gla_chunk_fwd(q, k, v, log_alpha, chunk=64, s0=None, o=None, s_out=None, return_state=True,
                   workspace=None):
     """Gated linear attention: S_t = S_{t-1} Diag(alpha_t) + v_t k_t^T, o_t = S_t q_t.
@@ -133,8 +150,9 @@ def gdelta_chunk_fwd(q, k, v, log_alpha, beta, chunk=64, s0=None, o=None, s_out=
 
 
 def workspace_size(kind, B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16):
-    """Device workspace in bytes for a chunk entry point; kind in {"retention", "gla", "gdelta"}."""
-    variant = {"retention": _native.LA_RETENTION, "gla": _native.LA_GLA, "gdelta": _native.LA_GDELTA}[kind]
+    """Device workspace in bytes for a chunk entry point; kind in {"retention", "mamba2", "gla", "gdelta"}."""
+    variant = {"retention": _native.LA_RETENTION, "mamba2": _native.LA_MAMBA2, "gla": _native.LA_GLA,
+               "gdelta": _native.LA_GDELTA}[kind]
     code = _native.LA_BF16 if dtype == torch.bfloat16 else _native.LA_F32
     return _native.workspace_size(variant, B, H, T, dk, dv, chunk, code)
 

@@ -10,6 +10,9 @@ hipError_t launch_chunk_bf16_retention_c64(const ChunkArgs& a, hipStream_t strea
 hipError_t launch_chunk_bf16_gla_c16(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16_gla_c32(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16_gla_c64(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_scalar_c16(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_scalar_c32(const ChunkArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bf16_scalar_c64(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16_gdelta_c16(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16_gdelta_c32(const ChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bf16_gdelta_c64(const ChunkArgs& a, hipStream_t stream);
@@ -28,6 +31,11 @@ hipError_t launch_chunk_bf16(Variant variant, const ChunkArgs& a, hipStream_t st
             if (a.chunk == 16) return launch_chunk_bf16_retention_c16(a, stream);
             if (a.chunk == 32) return launch_chunk_bf16_retention_c32(a, stream);
             if (a.chunk == 64) return launch_chunk_bf16_retention_c64(a, stream);
+            break;
+        case kScalar:
+            if (a.chunk == 16) return launch_chunk_bf16_scalar_c16(a, stream);
+            if (a.chunk == 32) return launch_chunk_bf16_scalar_c32(a, stream);
+            if (a.chunk == 64) return launch_chunk_bf16_scalar_c64(a, stream);
             break;
         case kGLA:
             if (a.chunk == 16) return launch_chunk_bf16_gla_c16(a, stream);

@@ -3,6 +3,6 @@
 
 namespace glr {
 hipError_t launch_chunk_bf16_gla_c32(const ChunkArgs& a, hipStream_t stream) {
-    return ck::launch_two_pass<32, true>(a, stream);
+    return ck::launch_two_pass<32, ck::kGateChannel>(a, stream);
 }
 }  // namespace glr

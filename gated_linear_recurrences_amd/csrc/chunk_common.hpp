@@ -86,7 +86,11 @@ __device__ __forceinline__ int logical_block_of(unsigned bid, unsigned grid, int
 namespace glr {
 namespace ck {
 
-constexpr int kCUs = 256;   // compute units of an MI355X
+constexpr int kCUs = 256;
+
+// Gate of the two-pass retention-family kernels: one fixed decay per head, one
+// data-dependent gate per key channel, or one data-dependent scalar per token.
+enum GateKind { kGateFixed = 0, kGateChannel = 1, kGateScalar = 2 };   // compute units of an MI355X
 
 }  // namespace ck
 }  // namespace glr

@@ -1,4 +1,4 @@
-// Chunkwise forward in float32 storage and fp32 arithmetic (VALU), all three
+// Chunkwise forward in float32 storage and fp32 arithmetic (VALU), all four
 // gate variants.
 //
 // The chunkwise form of "Le architetture lineari: RetNet, RWKV, xLSTM"
@@ -10,6 +10,9 @@
 //
 //   retention  o_i = sum_{j<=i} g^(i-j) (q_i.k_j) v_j + g^(i+1) S_in q_i
 //              S_out = g^n S_in + sum_j g^(n-1-j) v_j k_j^T
+//   scalar     (data-dependent, one gate per token) the same with g^(i-j) -> e^(G_i - G_j):
+//              o_i = sum_{j<=i} e^(G_i - G_j) (q_i.k_j) v_j + e^(G_i) S_in q_i
+//              S_out = e^(G_{n-1}) S_in + sum_j e^(G_{n-1} - G_j) v_j k_j^T
 //   GLA        o_i = sum_{j<=i} [sum_c q_ic k_jc e^(b_ic - b_jc)] v_j + S_in (q_i . e^(b_i))
 //              S_out = S_in Diag(e^(b_{n-1})) + sum_j v_j (k_j . e^(b_{n-1} - b_j))^T
 //   gated delta (WY form; "Scrivere meglio nella memoria", sections "Correggere:
@@ -88,14 +91,14 @@ void chunk_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 }
             }
         }
-        if constexpr (VARIANT == kGDelta) {
+        if constexpr (VARIANT == kGDelta || VARIANT == kScalar) {
             if (tid == 0) {
                 float acc = 0.f;
                 const int64_t base_t = static_cast<int64_t>(bh) * T + t0;
                 for (int i = 0; i < C; ++i) {
                     if (i < n) acc += gate[base_t + i];
                     Gs[i] = acc;
-                    Betas[i] = (i < n) ? beta[base_t + i] : 0.f;
+                    Betas[i] = (VARIANT == kGDelta && i < n) ? beta[base_t + i] : 0.f;
                 }
             }
         }
@@ -237,6 +240,7 @@ hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t str
         case kRetention: return launch_variant<kRetention>(a, stream);
         case kGLA: return launch_variant<kGLA>(a, stream);
         case kGDelta: return launch_variant<kGDelta>(a, stream);
+        case kScalar: return launch_variant<kScalar>(a, stream);
     }
     return hipErrorInvalidValue;
 }

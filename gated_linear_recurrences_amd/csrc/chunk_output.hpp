@@ -1,4 +1,5 @@
-// Output pass of the two-pass chunked forward for retention and GLA (bf16 storage).
+// Output pass of the two-pass chunked forward for retention, the scalar
+// data-dependent decay and GLA (bf16 storage).
 //
 // Method: the chunkwise form of retention ("Le architetture lineari: RetNet,
 // RWKV, xLSTM", section "RetNet: la retention e le sue tre forme", Fig. 16.5)
@@ -7,6 +8,7 @@
 // between chunks the memory. With local index i, j, the memory S_in entering
 // the chunk and chunk-local inclusive cumulative log-gates b:
 //   retention  o_i = sum_{j<=i} g^(i-j) (q_i.k_j) v_j + g^(i+1) S_in q_i
+//   scalar     o_i = sum_{j<=i} e^(G_i - G_j) (q_i.k_j) v_j + e^(G_i) S_in q_i
 //   GLA        o_i = sum_{j<=i} [sum_c q_ic k_jc e^(b_ic - b_jc)] v_j + S_in (q_i . e^(b_i))
 // S_in comes from the state pass (bf16 snapshots), so every chunk of every
 // sequence is independent: one workgroup per (sequence, chunk) covers all value
@@ -16,7 +18,8 @@
 //   loads     every global load is issued up front with full-row 16-byte pieces:
 //             q, k, v (and the raw gates) for staging, and each wave's slice of
 //             S_in, which stays in registers in the A-operand layout;
-//   gates     (GLA) the raw log-gates are staged and scanned per key channel
+//   gates     (scalar) one wave scans the chunk's gates into a table of G;
+//             (GLA) the raw log-gates are staged and scanned per key channel
 //             (16-token runs per lane, joined by shuffles), then folded into bf16
 //             operands: q and k rescaled to the cumulative gate r_t just before
 //             their own 16-token tile (bounded factors), with tables
@@ -39,14 +42,15 @@ struct OutParams {
     const u16* q;        // [BH][T][DK]
     const u16* k;        // [BH][T][DK]
     const u16* v;        // [BH][T][DV]
-    const float* gate;   // retention: log gamma [H]; GLA: log alpha [BH][T][DK]
+    const float* gate;   // retention: log gamma [H]; GLA: log alpha [BH][T][DK]; scalar: log alpha [BH][T]
     const u16* states;   // [BH][NC][DV][DK] memory entering each chunk
     u16* o;              // [BH][T][DV]
     int H, T, NC;
 };
 
-template <int C, int DK, int DV, bool GLA>
+template <int C, int DK, int DV, int GK>
 struct OutLayout {
+    static constexpr bool GLA = GK == kGateChannel, SCL = GK == kGateScalar;
     static constexpr int CT = C / 16;
     static constexpr int QS = DK + 8;   // bf16 row stride of staged q / k (16-byte rows)
     // bf16 row stride of staged v: rows 8 x odd banks apart, so that the 8 rows read
@@ -67,14 +71,17 @@ struct OutLayout {
     static constexpr int oR = oF + (GLA ? al(NF * DK * 4 + 16) : 0);  // R = e^(r_it)
     static constexpr int endX = oR + (GLA ? al(CT * DK * 4) : 0);
     static constexpr int endG = oX + (GLA ? al(C * BS * 4) : 0);
-    static constexpr int bytes = endX > endG ? endX : endG;
+    static constexpr int oS = endX;                                  // scalar: cumulative gates G
+    static constexpr int endS = oS + (SCL ? al(C * 4) : 0);
+    static constexpr int bytes = endS > endG ? endS : endG;
     static_assert(bytes <= 160 * 1024, "LDS budget of the output pass exceeded");
 };
 
-template <int C, int DK, int DV, bool GLA, int NW>
+template <int C, int DK, int DV, int GK, int NW>
 __global__ __launch_bounds__(64 * NW)
 void output_kernel(OutParams p) {
-    using Lay = OutLayout<C, DK, DV, GLA>;
+    using Lay = OutLayout<C, DK, DV, GK>;
+    constexpr bool GLA = GK == kGateChannel, SCL = GK == kGateScalar;
     constexpr int CT = C / 16, NT = 64 * NW;
     constexpr int KB = (DK + 31) / 32;
     constexpr int QS = Lay::QS, VS = Lay::VS, PS = Lay::PS, BS = Lay::BS;
@@ -93,6 +100,7 @@ void output_kernel(OutParams p) {
     float* const sF = reinterpret_cast<float*>(smem + Lay::oF);
     float* const sR = reinterpret_cast<float*>(smem + Lay::oR);
     float* const sB = reinterpret_cast<float*>(smem + Lay::oX);
+    float* const sGs = reinterpret_cast<float*>(smem + Lay::oS);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -107,12 +115,14 @@ void output_kernel(OutParams p) {
     const u16* kc = p.k + tok0 * DK;
     const u16* vc = p.v + tok0 * DV;
     const u16* sc = p.states + (static_cast<int64_t>(bh) * p.NC + c) * DV * DK;
-    const float lg2 = GLA ? 0.f : p.gate[h] * kLog2e;
+    const float lg2 = (GK == kGateFixed) ? p.gate[h] * kLog2e : 0.f;
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
     // ---- all global loads up front (rows past the end read row 0, zeroed on use)
     u16x8 rq[QP_PER], rk[QP_PER], rv[VP_PER];
     f32x4 rg[GP_PER];
+    // scalar gates: wave 0 lane t < n holds token t's
+    const float rgs = (SCL && tid < n) ? p.gate[tok0 + tid] : 0.f;
 #pragma unroll
     for (int i = 0; i < QP_PER; ++i) {
         const int idx = tid + i * NT;
@@ -171,6 +181,13 @@ void output_kernel(OutParams p) {
             if (idx < VP) {
                 const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
                 *reinterpret_cast<u16x8*>(sV + j * VS + col) = row_ok(idx, DV / 8, VP) ? rv[i] : z8;
+            }
+        }
+        if constexpr (SCL) {
+            // chunk-local inclusive cumulative gates (log2 units; padded tokens add 0)
+            if (w == 0) {
+                const float G = wave_inclusive_scan(rgs * kLog2e);
+                if (lane < C) sGs[lane] = G;
             }
         }
         lds_barrier();
@@ -288,6 +305,12 @@ void output_kernel(OutParams p) {
         int it = 0, jt = pr0;
         while (jt > it) { jt -= it + 1; ++it; }
         const int i = 16 * it + r16;
+        float gi = 0.f;
+        f32x4 gj = zf4();
+        if constexpr (SCL) {
+            gi = sGs[i];
+            gj = ldf4(sGs + 16 * jt + 4 * g);
+        }
         f32x4 acc = zf4();
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -318,7 +341,8 @@ void output_kernel(OutParams p) {
         for (int r = 0; r < 4; ++r) {
             const int j = 16 * jt + 4 * g + r;
             float val = acc[r];
-            if constexpr (!GLA) val *= ex2(static_cast<float>(i - j) * lg2);
+            if constexpr (GK == kGateFixed) val *= ex2(static_cast<float>(i - j) * lg2);
+            if constexpr (SCL) val *= ex2(gi - gj[r]);   // <= 1 for j <= i; the rest is masked
             pv[r] = static_cast<__bf16>((j <= i) ? val : 0.f);
         }
         st4(sP + i * PS + 16 * jt + 4 * g, pv);
@@ -329,7 +353,7 @@ void output_kernel(OutParams p) {
     for (int item = w; item < CT * NP; item += NW) {
         const int it = item / NP;
         const int i = 16 * it + r16;
-        const float oscale = GLA ? 1.f : ex2(static_cast<float>(i + 1) * lg2);
+        const float oscale = GLA ? 1.f : SCL ? ex2(sGs[i]) : ex2(static_cast<float>(i + 1) * lg2);
         bf16x8 qb[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {

@@ -1,4 +1,5 @@
-// State pass of the two-pass chunked forward for retention and GLA (bf16 storage).
+// State pass of the two-pass chunked forward for retention, the scalar
+// data-dependent decay and GLA (bf16 storage).
 //
 // Method: the chunkwise form of retention ("Le architetture lineari: RetNet,
 // RWKV, xLSTM", section "RetNet: la retention e le sue tre forme", Fig. 16.5)
@@ -7,6 +8,8 @@
 // passes from one chunk to the next; with chunk-local inclusive cumulative
 // log-gates b_j (per key channel) and n tokens in the chunk:
 //   retention  S_out = g^n S_in + sum_j g^(n-1-j) v_j k_j^T
+//   scalar     S_out = e^(G_{n-1}) S_in + sum_j e^(G_{n-1} - G_j) v_j k_j^T (G: the
+//              chunk-local inclusive cumulative log of one gate per token)
 //   GLA        S_out = S_in Diag(e^(b_{n-1})) + sum_j v_j (k_j . e^(b_{n-1} - b_j))^T
 // This kernel walks the chunks of one sequence in order and writes, for every
 // chunk c, the memory entering it (bf16, [d_v][d_k]) to a workspace; the output
@@ -25,7 +28,9 @@
 //             the chunk's own contribution dS on MFMA, into separate accumulators,
 //             so the U products overlap; then, in order, the entering memory is
 //             stored (bf16) and S <- decay . S + dS;
-//   gates     (GLA) each lane reads the raw log-gates of its key channel for the
+//   gates     (scalar) a wave prefix scan over the chunk's tokens, the lane's
+//             weights fetched by shuffles;
+//             (GLA) each lane reads the raw log-gates of its key channel for the
 //             tokens it holds in the operand layout, scans its 4-token runs and
 //             joins runs across the four lanes of the channel with shuffles;
 //   staging   the next group goes from registers to the other LDS buffer;
@@ -42,7 +47,7 @@ namespace ck {
 struct StateParams {
     const u16* k;        // [BH][T][DK]
     const u16* v;        // [BH][T][dv]
-    const float* gate;   // retention: log gamma [H]; GLA: log alpha [BH][T][DK]
+    const float* gate;   // retention: log gamma [H]; GLA: log alpha [BH][T][DK]; scalar: log alpha [BH][T]
     const float* s0;     // [BH][dv][DK] or null
     u16* states;         // [BH][NC][dv][DK]: memory entering each chunk
     float* s_out;        // [BH][dv][DK] or null
@@ -65,24 +70,27 @@ __device__ __forceinline__ void piece_of(int l, int& row, int& piece) {
     }
 }
 
-template <int C, int NWK, int TV, int U, bool GLA>
+template <int C, int NWK, int TV, int U, int GK>
 struct StateLayout {
+    static constexpr bool GLA = GK == kGateChannel, SCL = GK == kGateScalar;
     static constexpr int DKB = 16 * NWK, DVB = 16 * TV;
     static constexpr int KS = tile_stride(DKB);   // bf16 row stride of staged keys
     static constexpr int VS = tile_stride(DVB);   // bf16 row stride of staged values
     static constexpr int GS = DKB + 4;            // fp32 row stride of staged raw gates
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
-    static constexpr int KCH = al(C * KS * 2), VCH = al(C * VS * 2), GCH = GLA ? al(C * GS * 4) : 0;
+    static constexpr int KCH = al(C * KS * 2), VCH = al(C * VS * 2);
+    static constexpr int GCH = GLA ? al(C * GS * 4) : SCL ? al(C * 4) : 0;   // raw gates (log2 units)
     static constexpr int CH = KCH + VCH + GCH;    // one staged chunk
     static constexpr int BUF = U * CH;            // one staged group
     static constexpr int bytes = 2 * BUF;
     static constexpr bool fits = bytes <= 160 * 1024;
 };
 
-template <int C, int DK, int NWK, int NWV, int TV, int U, bool GLA>
+template <int C, int DK, int NWK, int NWV, int TV, int U, int GK>
 __global__ __launch_bounds__(64 * NWK * NWV)
 void state_kernel(StateParams p) {
-    using Lay = StateLayout<C, NWK, TV, U, GLA>;
+    using Lay = StateLayout<C, NWK, TV, U, GK>;
+    constexpr bool GLA = GK == kGateChannel, SCL = GK == kGateScalar;
     static_assert(Lay::fits, "LDS budget exceeded");
     static_assert(TV % NWV == 0, "value tiles split evenly over the wave groups");
     constexpr int NW = NWK * NWV, NT = 64 * NW, DKB = Lay::DKB, DVB = Lay::DVB;
@@ -117,7 +125,8 @@ void state_kernel(StateParams p) {
     const u16* kg = p.k + tok0 * DK + k0;
     const u16* vg = p.v + tok0 * dv + v0;
     const float* gg = GLA ? p.gate + tok0 * DK + k0 : nullptr;
-    const float lg2 = GLA ? 0.f : p.gate[h] * kLog2e;
+    const float* gsc = SCL ? p.gate + tok0 : nullptr;
+    const float lg2 = (GK == kGateFixed) ? p.gate[h] * kLog2e : 0.f;
 
     // sacc[t][r] = S[v0 + 16 tv(t) + r16][k0 + 16w + 4g + r], tv(t) = vgrp + NWV t
     f32x4 sacc[TVW];
@@ -148,6 +157,7 @@ void state_kernel(StateParams p) {
     // ---- two-slot register ring of raw 16-byte pieces, one group per slot
     u16x8 rk[2][U][KP_PER], rv[2][U][VP_PER];
     f32x4 rg[2][U][GLA ? GP_PER : 1];
+    float rs[2][U];   // scalar gates: thread t < C holds token t's
 
     // Loads only: chunks past the last are clamped to it, rows past the end read
     // row 0; the zeroing happens where the data is consumed, so that no instruction
@@ -174,6 +184,7 @@ void state_kernel(StateParams p) {
                 const bool ok = value_ok(i) && j < n;
                 rv[slot][u][i] = *reinterpret_cast<const u16x8*>(vc + (ok ? static_cast<unsigned>(j * dv + 8 * pc) : 0u));
             }
+            if constexpr (SCL) rs[slot][u] = gsc[static_cast<int64_t>(c) * C + (tid < n ? tid : 0)];
             if constexpr (GLA) {
                 const float* gc = gg + static_cast<int64_t>(c) * C * DK;
 #pragma unroll
@@ -211,6 +222,9 @@ void state_kernel(StateParams p) {
                     *reinterpret_cast<u16x8*>(vs + j * VS + 8 * pc) = (j < n) ? rv[slot][u][i] : z;
                 }
             }
+            if constexpr (SCL) {
+                if (tid < C) sG(b, u)[tid] = (tid < n) ? rs[slot][u] * kLog2e : 0.f;
+            }
             if constexpr (GLA) {
                 float* gs = sG(b, u);
 #pragma unroll
@@ -237,8 +251,22 @@ void state_kernel(StateParams p) {
         const float d = ex2(static_cast<float>(n) * lg2);
         dec[0] = d; dec[1] = d; dec[2] = d; dec[3] = d;
     };
-    f32x4 wfull[GLA ? 1 : CT], dfull;   // full-chunk values (only the last chunk is shorter)
-    if constexpr (!GLA) ret_weights(C, wfull, dfull);
+    f32x4 wfull[GK == kGateFixed ? CT : 1], dfull;   // full-chunk values (only the last chunk is shorter)
+    if constexpr (GK == kGateFixed) ret_weights(C, wfull, dfull);
+
+    // scalar gates: the chunk's inclusive cumulative log2-gates G by a wave prefix
+    // scan (lane = token; padded tokens carry 0), carry weights e^(G_last - G_j) of
+    // this lane's tokens 16q + 4g + e by shuffles, and the decay e^(G_last)
+    auto scalar_weights = [&](const float* gs, f32x4* wq, f32x4& dec) {
+        const float G = wave_inclusive_scan(lane < C ? gs[lane] : 0.f);
+        const float last = __shfl(G, C - 1, 64);
+#pragma unroll
+        for (int q = 0; q < CT; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wq[q][e] = ex2(last - __shfl(G, 16 * q + 4 * g + e, 64));
+        const float d = ex2(last);
+        dec[0] = d; dec[1] = d; dec[2] = d; dec[3] = d;
+    };
 
     // GLA: carry weights e^(b_last - b_j) of this lane's tokens for key channel
     // k0 + 16w + r16, and the decays e^(b_last) of key channels 16w + 4g + r
@@ -298,6 +326,8 @@ void state_kernel(StateParams p) {
                 f32x4 wq[CT];
                 if constexpr (GLA) {
                     gla_weights(sG(b, u), wq, dec[u]);
+                } else if constexpr (SCL) {
+                    scalar_weights(sG(b, u), wq, dec[u]);
                 } else if (n == C) {
 #pragma unroll
                     for (int q = 0; q < CT; ++q) wq[q] = wfull[q];

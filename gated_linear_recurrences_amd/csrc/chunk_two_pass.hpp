@@ -1,5 +1,5 @@
 // Launch of the two-pass chunked forward (state pass, then output pass) for
-// retention and GLA with bf16 storage. The memory entering each chunk travels
+// retention, the scalar data-dependent decay and GLA with bf16 storage. The memory entering each chunk travels
 // between the passes through the caller's workspace, [B*H][chunks][d_v][d_k] bf16.
 #pragma once
 
@@ -24,16 +24,16 @@ inline int state_value_tiles(int64_t heads, int dv, int dk) {
 
 // chunks per workgroup barrier: the largest of 4, 2, 1 whose double-buffered
 // staging fits in LDS
-template <int C, int NW, int TV, bool GLA>
+template <int C, int NW, int TV, int GK>
 constexpr int state_group() {
-    return StateLayout<C, NW, TV, 4, GLA>::fits ? 4 : StateLayout<C, NW, TV, 2, GLA>::fits ? 2 : 1;
+    return StateLayout<C, NW, TV, 4, GK>::fits ? 4 : StateLayout<C, NW, TV, 2, GK>::fits ? 2 : 1;
 }
 
-template <int C, int DK, int TV, bool GLA>
+template <int C, int DK, int TV, int GK>
 hipError_t launch_state(const ChunkArgs& a, int NC, hipStream_t stream) {
     constexpr int NW = state_key_tiles(DK);
     constexpr int NWV = TV >= 2 ? 2 : 1;   // two waves per key tile when they can split the value tiles
-    constexpr int U = state_group<C, NW, TV, GLA>();
+    constexpr int U = state_group<C, NW, TV, GK>();
     StateParams p;
     p.k = static_cast<const u16*>(a.k);
     p.v = static_cast<const u16*>(a.v);
@@ -49,21 +49,21 @@ hipError_t launch_state(const ChunkArgs& a, int NC, hipStream_t stream) {
     p.kblocks = DK / (16 * NW);
     const int64_t G = static_cast<int64_t>(a.B) * a.H * p.vblocks * p.kblocks;
     p.remap = (G % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((state_kernel<C, DK, NW, NWV, TV, U, GLA>), dim3(static_cast<unsigned>(G)), dim3(64 * NW * NWV),
+    hipLaunchKernelGGL((state_kernel<C, DK, NW, NWV, TV, U, GK>), dim3(static_cast<unsigned>(G)), dim3(64 * NW * NWV),
                        0, stream, p);
     return hipGetLastError();
 }
 
-template <int C, int DK, int DV, bool GLA>
+template <int C, int DK, int DV, int GK>
 hipError_t launch_two_pass_dv(const ChunkArgs& a, hipStream_t stream) {
     const int NC = (a.T + C - 1) / C;
     const int64_t heads = static_cast<int64_t>(a.B) * a.H;
     hipError_t err = hipErrorInvalidValue;
     switch (state_value_tiles(heads, DV, DK)) {
-        case 8: if constexpr (DV >= 128) err = launch_state<C, DK, 8, GLA>(a, NC, stream); break;
-        case 4: if constexpr (DV >= 64) err = launch_state<C, DK, 4, GLA>(a, NC, stream); break;
-        case 2: if constexpr (DV >= 32) err = launch_state<C, DK, 2, GLA>(a, NC, stream); break;
-        default: err = launch_state<C, DK, 1, GLA>(a, NC, stream); break;
+        case 8: if constexpr (DV >= 128) err = launch_state<C, DK, 8, GK>(a, NC, stream); break;
+        case 4: if constexpr (DV >= 64) err = launch_state<C, DK, 4, GK>(a, NC, stream); break;
+        case 2: if constexpr (DV >= 32) err = launch_state<C, DK, 2, GK>(a, NC, stream); break;
+        default: err = launch_state<C, DK, 1, GK>(a, NC, stream); break;
     }
     if (err != hipSuccess || NC == 0) return err;
     OutParams p;
@@ -76,32 +76,32 @@ hipError_t launch_two_pass_dv(const ChunkArgs& a, hipStream_t stream) {
     p.H = a.H;
     p.T = a.T;
     p.NC = NC;
-    // four waves for retention (two or three workgroups per CU), eight for GLA,
+    // four waves for the scalar gates (two or three workgroups per CU), eight for GLA,
     // whose larger LDS footprint allows two workgroups per CU
-    constexpr int NW = GLA ? 8 : 4;
-    hipLaunchKernelGGL((output_kernel<C, DK, DV, GLA, NW>), dim3(static_cast<unsigned>(heads * NC)), dim3(64 * NW),
+    constexpr int NW = GK == kGateChannel ? 8 : 4;
+    hipLaunchKernelGGL((output_kernel<C, DK, DV, GK, NW>), dim3(static_cast<unsigned>(heads * NC)), dim3(64 * NW),
                        0, stream, p);
     return hipGetLastError();
 }
 
-template <int C, int DK, bool GLA>
+template <int C, int DK, int GK>
 hipError_t launch_two_pass_dk(const ChunkArgs& a, hipStream_t stream) {
     switch (a.dv) {
-        case 16: return launch_two_pass_dv<C, DK, 16, GLA>(a, stream);
-        case 32: return launch_two_pass_dv<C, DK, 32, GLA>(a, stream);
-        case 64: return launch_two_pass_dv<C, DK, 64, GLA>(a, stream);
-        case 128: return launch_two_pass_dv<C, DK, 128, GLA>(a, stream);
+        case 16: return launch_two_pass_dv<C, DK, 16, GK>(a, stream);
+        case 32: return launch_two_pass_dv<C, DK, 32, GK>(a, stream);
+        case 64: return launch_two_pass_dv<C, DK, 64, GK>(a, stream);
+        case 128: return launch_two_pass_dv<C, DK, 128, GK>(a, stream);
     }
     return hipErrorInvalidValue;
 }
 
-template <int C, bool GLA>
+template <int C, int GK>
 hipError_t launch_two_pass(const ChunkArgs& a, hipStream_t stream) {
     switch (a.dk) {
-        case 16: return launch_two_pass_dk<C, 16, GLA>(a, stream);
-        case 32: return launch_two_pass_dk<C, 32, GLA>(a, stream);
-        case 64: return launch_two_pass_dk<C, 64, GLA>(a, stream);
-        case 128: return launch_two_pass_dk<C, 128, GLA>(a, stream);
+        case 16: return launch_two_pass_dk<C, 16, GK>(a, stream);
+        case 32: return launch_two_pass_dk<C, 32, GK>(a, stream);
+        case 64: return launch_two_pass_dk<C, 64, GK>(a, stream);
+        case 128: return launch_two_pass_dk<C, 128, GK>(a, stream);
     }
     return hipErrorInvalidValue;
 }

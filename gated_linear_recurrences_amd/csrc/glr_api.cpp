@@ -90,7 +90,7 @@ la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int d
                                   la_dtype dtype, size_t* bytes) {
     if (bytes == nullptr) return fail(LA_ERR_INVALID, "%s", "bytes is NULL");
     *bytes = 0;
-    if (variant != LA_RETENTION && variant != LA_GLA && variant != LA_GDELTA)
+    if (variant != LA_RETENTION && variant != LA_GLA && variant != LA_GDELTA && variant != LA_MAMBA2)
         return fail(LA_ERR_INVALID, "%s", "unknown variant");
     const glr::Variant v = static_cast<glr::Variant>(variant);
     // shape checks only: pointers are not part of the query
@@ -113,6 +113,14 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, void* stream) {
     glr::ChunkArgs a{q, k, v, log_gamma, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk, workspace};
     return run_chunk(glr::kRetention, a, dtype, workspace_bytes, stream);
+}
+
+la_status mamba2_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* s0, void* o, float* s_out,
+                           int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    glr::ChunkArgs a{q, k, v, log_alpha, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk, workspace};
+    return run_chunk(glr::kScalar, a, dtype, workspace_bytes, stream);
 }
 
 la_status gla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -168,6 +176,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (2 << 16) | 0; }
+int la_version(void) { return (2 << 16) | 1; }
 
 }  // extern "C"

@@ -8,13 +8,13 @@
 
 namespace glr {
 
-enum Variant { kRetention = 0, kGLA = 1, kGDelta = 2 };
+enum Variant { kRetention = 0, kGLA = 1, kGDelta = 2, kScalar = 3 };
 
 struct ChunkArgs {
     const void* q;
     const void* k;
     const void* v;
-    const float* gate;   // retention: log_gamma [H]; GLA: log_alpha [B,H,T,dk]; gdelta: log_alpha [B,H,T]
+    const float* gate;   // retention: log_gamma [H]; GLA: log_alpha [B,H,T,dk]; gdelta, scalar: log_alpha [B,H,T]
     const float* beta;   // gdelta only: [B,H,T]
     const float* s0;     // [B,H,dv,dk] or nullptr
     void* o;             // [B,H,T,dv]

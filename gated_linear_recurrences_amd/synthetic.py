@@ -78,14 +78,14 @@ class Workload:
     """One seeded input set. Arrays are numpy, float32 containers (bf16-exact when
     ``dtype == 'bf16'``); the gates are always float32."""
 
-    kind: str                  # 'retention' | 'gla' | 'gdelta' | 'decode'
+    kind: str                  # 'retention' | 'mamba2' | 'gla' | 'gdelta' | 'decode'
     dtype: str                 # storage type of q, k, v, o: 'bf16' | 'f32'
     q: np.ndarray
     k: np.ndarray
     v: np.ndarray
     chunk: int = 0
     log_gamma: Optional[np.ndarray] = None   # retention [H]
-    log_alpha: Optional[np.ndarray] = None   # gla [B,H,T,dk]; gdelta [B,H,T]
+    log_alpha: Optional[np.ndarray] = None   # gla [B,H,T,dk]; mamba2, gdelta [B,H,T]
     beta: Optional[np.ndarray] = None        # gdelta [B,H,T]
     alpha: Optional[np.ndarray] = None       # decode [N,H,dk] (or [steps,N,H,dk])
     s0: Optional[np.ndarray] = None          # [B,H,dv,dk] fp32
@@ -108,6 +108,21 @@ def retention_inputs(B, H, T, dk, dv, *, chunk=64, dtype="bf16", seed=0, scale=N
     s0 = (rng.standard_normal((B, H, dv, dk)).astype(np.float32) * np.float32(0.1)
           if with_state else None)
     return Workload("retention", dtype, q, k, v, chunk=chunk, log_gamma=log_gamma, s0=s0)
+
+
+def mamba2_inputs(B, H, T, dk, dv, *, chunk=64, dtype="bf16", seed=0, scale=None,
+                  temperature=16.0, with_state=False):
+    """q, k, v ~ N(0,1)*scale; one log-gate logsigmoid(N(0,1)) / temperature per token and head
+    (the per-channel recipe of the GLA workload, drawn once per token)."""
+    rng = np.random.default_rng(seed)
+    scale = (1.0 / np.sqrt(dk)) if scale is None else scale
+    q = _store(rng.standard_normal((B, H, T, dk)) * scale, dtype)
+    k = _store(rng.standard_normal((B, H, T, dk)) * scale, dtype)
+    v = _store(rng.standard_normal((B, H, T, dv)) * scale, dtype)
+    log_alpha = (_logsigmoid(rng.standard_normal((B, H, T))) / temperature).astype(np.float32)
+    s0 = (rng.standard_normal((B, H, dv, dk)).astype(np.float32) * np.float32(0.1)
+          if with_state else None)
+    return Workload("mamba2", dtype, q, k, v, chunk=chunk, log_alpha=log_alpha, s0=s0)
 
 
 def gla_inputs(B, H, T, dk, dv, *, chunk=64, dtype="bf16", seed=0, scale=None,
@@ -160,7 +175,8 @@ def decode_inputs(N, H, dk, dv, *, steps=1, dtype="bf16", seed=0):
     return Workload("decode", dtype, q, k, v, alpha=a, s0=s0)
 
 
-# The five workloads the throughput and parity figures are quoted on.
+# The five workloads the throughput and parity figures are quoted on, and the scalar
+# data-dependent decay at the GLA workload's shape.
 CONFIGS = {
     "retention_t64_d16_f32": dict(kind="retention", B=1, H=1, T=64, dk=16, dv=16, chunk=16,
                                   dtype="f32", gamma=0.9, scale=1.0, seed=1),
@@ -172,6 +188,8 @@ CONFIGS = {
                                     dtype="bf16", seed=4),
     "decode_n512h32_d128": dict(kind="decode", N=512, H=32, dk=128, dv=128, steps=1000,
                                 dtype="bf16", seed=5),
+    "mamba2_b8h16_t4096_d128": dict(kind="mamba2", B=8, H=16, T=4096, dk=128, dv=128, chunk=64,
+                                    dtype="bf16", seed=6),
 }
 
 
@@ -192,6 +210,9 @@ def config_inputs(name, *, steps=None, T=None):
     if kind == "gla":
         return gla_inputs(c["B"], c["H"], Tn, c["dk"], c["dv"], chunk=c["chunk"],
                           dtype=c["dtype"], seed=seed)
+    if kind == "mamba2":
+        return mamba2_inputs(c["B"], c["H"], Tn, c["dk"], c["dv"], chunk=c["chunk"],
+                             dtype=c["dtype"], seed=seed)
     if kind == "gdelta":
         return gdelta_inputs(c["B"], c["H"], Tn, c["dk"], c["dv"], chunk=c["chunk"],
                              dtype=c["dtype"], seed=seed)

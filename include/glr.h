@@ -75,15 +75,17 @@ typedef enum la_dtype {
 typedef enum la_variant {
     LA_RETENTION = 0,   /* la_chunk_fwd */
     LA_GLA = 1,         /* gla_chunk_fwd */
-    LA_GDELTA = 2       /* gdelta_chunk_fwd */
+    LA_GDELTA = 2,      /* gdelta_chunk_fwd */
+    LA_MAMBA2 = 3       /* mamba2_chunk_fwd */
 } la_variant;
 
 /*
  * Workspace needed by a chunk entry point of `variant` for these sizes, in
  * bytes, written to *bytes (0 when none is needed).  Checks the sizes like the
  * entry point does (status and la_last_error() as there); the pointers of the
- * entry point are not involved.  For bf16 storage, retention and GLA pass the
- * memory entering every chunk from their state pass to their output pass:
+ * entry point are not involved.  For bf16 storage, retention, the scalar
+ * data-dependent decay and GLA pass the memory entering every chunk from their
+ * state pass to their output pass:
  * B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.  The gated delta rule in bf16
  * also passes, per (sequence, chunk), its WY factor W (chunk x d_k bf16), the
  * pseudo-values (d_v x chunk float32) and the cumulative log-gates (chunk
@@ -108,6 +110,21 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v,
                        int B, int H, int T, int dk, int dv, int chunk,
                        la_dtype dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * Scalar data-dependent decay, the Mamba-2 row of the transition table
+ * ("Scrivere meglio nella memoria", section "Dimenticare: i gate", scalar-decay
+ * equation with alpha_t produced from the input at every step):
+ *     S_t = alpha_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t.
+ * log_alpha [B][H][T] float32 holds log(alpha_t) (<= 0), one per token and
+ * head.  Only the recurrence is covered, not the rest of a Mamba-2 layer.
+ */
+la_status mamba2_chunk_fwd(const void* q, const void* k, const void* v,
+                           const float* log_alpha,
+                           const float* s0, void* o, float* s_out,
+                           int B, int H, int T, int dk, int dv, int chunk,
+                           la_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * Gated linear attention: a data-dependent gate per key channel ("Scrivere
@@ -166,7 +183,8 @@ const char* la_status_str(la_status status);
  * (thread-local; empty if none).  Valid until the next call on that thread. */
 const char* la_last_error(void);
 
-/* ABI version: (major << 16) | minor (2.0: workspace arguments). */
+/* ABI version: (major << 16) | minor (2.0: workspace arguments; 2.1:
+ * mamba2_chunk_fwd). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -26,7 +26,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"):
+    for n in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"):
         assert n in names
     assert set(names) == set(_native.EXPORTED)
 
@@ -38,6 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 2
+    assert lib.la_version() & 0xffff >= 1      # 2.1: mamba2_chunk_fwd
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -62,8 +63,8 @@ def _chunk(lib, fn, **kw):
                             P(a["ws"]), a["ws_bytes"], None)
 
 
-VARIANT = {"la_chunk_fwd": _native.LA_RETENTION, "gla_chunk_fwd": _native.LA_GLA,
-           "gdelta_chunk_fwd": _native.LA_GDELTA}
+VARIANT = {"la_chunk_fwd": _native.LA_RETENTION, "mamba2_chunk_fwd": _native.LA_MAMBA2,
+           "gla_chunk_fwd": _native.LA_GLA, "gdelta_chunk_fwd": _native.LA_GDELTA}
 
 
 def _ws(lib, variant, B=1, H=1, T=8, dk=16, dv=16, chunk=16, dtype=1):
@@ -73,8 +74,8 @@ def _ws(lib, variant, B=1, H=1, T=8, dk=16, dv=16, chunk=16, dtype=1):
 
 
 def test_workspace_size_query(lib):
-    # retention and GLA in bf16: one bf16 d_v x d_k memory per (sequence, chunk)
-    for variant in (_native.LA_RETENTION, _native.LA_GLA):
+    # retention, the scalar decay and GLA in bf16: one bf16 d_v x d_k memory per (sequence, chunk)
+    for variant in (_native.LA_RETENTION, _native.LA_MAMBA2, _native.LA_GLA):
         assert _ws(lib, variant, B=4, H=8, T=2048, dk=128, dv=128, chunk=64) == (_native.LA_OK, 32 * 32 * 128 * 128 * 2)
         assert _ws(lib, variant, B=1, H=2, T=65, dk=32, dv=64, chunk=32) == (_native.LA_OK, 2 * 3 * 64 * 32 * 2)
         assert _ws(lib, variant, T=0) == (_native.LA_OK, 0)
@@ -99,7 +100,7 @@ def test_workspace_size_query(lib):
     assert lib.la_chunk_workspace_size(0, 1, 1, 8, 16, 16, 16, 1, None) == _native.LA_ERR_INVALID
 
 
-@pytest.mark.parametrize("fn", ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd"])
+@pytest.mark.parametrize("fn", ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd"])
 def test_chunk_workspace_validation(lib, fn):
     st, need = _ws(lib, VARIANT[fn], T=40, chunk=16)
     assert st == _native.LA_OK and need == (6400 if fn == "gdelta_chunk_fwd" else 3 * 16 * 16 * 2)
@@ -111,7 +112,7 @@ def test_chunk_workspace_validation(lib, fn):
     assert _chunk(lib, fn, T=40, ws=MISALIGNED) == _native.LA_ERR_INVALID
 
 
-@pytest.mark.parametrize("fn", ["la_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd"])
+@pytest.mark.parametrize("fn", ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd"])
 def test_chunk_validation(lib, fn):
     assert _chunk(lib, fn, q=None) == _native.LA_ERR_INVALID
     assert b"q is NULL" in lib.la_last_error()

@@ -42,6 +42,8 @@ def run_gpu(w, s0=None, chunk=None, o=None, s_out=None):
     c = chunk or w.chunk
     if w.kind == "retention":
         out, S = api.la_chunk_fwd(q, k, v, _t(w.log_gamma), chunk=c, s0=s0_t, o=o, s_out=s_out)
+    elif w.kind == "mamba2":
+        out, S = api.mamba2_chunk_fwd(q, k, v, _t(w.log_alpha), chunk=c, s0=s0_t, o=o, s_out=s_out)
     elif w.kind == "gla":
         out, S = api.gla_chunk_fwd(q, k, v, _t(w.log_alpha), chunk=c, s0=s0_t, o=o, s_out=s_out)
     else:
@@ -56,6 +58,8 @@ def run_oracle(w, s0=None, chunk=None):
     c = chunk or w.chunk
     if w.kind == "retention":
         return orc.retention_chunkwise(w.q, w.k, w.v, w.log_gamma, c, s0=s0)
+    if w.kind == "mamba2":
+        return orc.scalar_chunkwise(w.q, w.k, w.v, w.log_alpha, c, s0=s0)
     if w.kind == "gla":
         return orc.gla_chunkwise(w.q, w.k, w.v, w.log_alpha, c, s0=s0)
     return orc.gdelta_chunkwise(w.q, w.k, w.v, w.log_alpha, w.beta, c, s0=s0)
@@ -81,12 +85,14 @@ def assert_parity(w, o, S, o_ref, S_ref, label=""):
 def make(kind, B, H, T, dk, dv, chunk, dtype, seed, state):
     if kind == "retention":
         return synthetic.retention_inputs(B, H, T, dk, dv, chunk=chunk, dtype=dtype, seed=seed, with_state=state)
+    if kind == "mamba2":
+        return synthetic.mamba2_inputs(B, H, T, dk, dv, chunk=chunk, dtype=dtype, seed=seed, with_state=state)
     if kind == "gla":
         return synthetic.gla_inputs(B, H, T, dk, dv, chunk=chunk, dtype=dtype, seed=seed, with_state=state)
     return synthetic.gdelta_inputs(B, H, T, dk, dv, chunk=chunk, dtype=dtype, seed=seed, with_state=state)
 
 
-KINDS = ["retention", "gla", "gdelta"]
+KINDS = ["retention", "mamba2", "gla", "gdelta"]
 
 # (B, H, T, d_k, d_v, chunk): several chunks, ragged tails, every supported head size and chunk
 SMALL_SHAPES = [
@@ -132,7 +138,7 @@ def test_bf16_chunk_parity(kind, shape, state):
 
 
 @pytest.mark.parametrize("name", ["retention_b4h8_t2048_d128", "gla_b8h16_t4096_d128",
-                                  "gdelta_b4h16_t8192_d128"])
+                                  "gdelta_b4h16_t8192_d128", "mamba2_b8h16_t4096_d128"])
 def test_bf16_full_config_parity(name):
     """Full-size workloads in the launch configuration the benchmark times, every output."""
     w = synthetic.config_inputs(name)
@@ -168,6 +174,8 @@ def test_resume_and_in_place_state(kind, dtype):
         sub.q, sub.k, sub.v = w.q[..., sl, :], w.k[..., sl, :], w.v[..., sl, :]
         if kind == "gla":
             sub.log_alpha = w.log_alpha[..., sl, :]
+        elif kind == "mamba2":
+            sub.log_alpha = w.log_alpha[..., sl]
         elif kind == "gdelta":
             sub.log_alpha, sub.beta = w.log_alpha[..., sl], w.beta[..., sl]
         q, k, v = _t(sub.q, st), _t(sub.k, st), _t(sub.v, st)
@@ -175,6 +183,8 @@ def test_resume_and_in_place_state(kind, dtype):
             out, _ = api.la_chunk_fwd(q, k, v, _t(w.log_gamma), chunk=64, s0=s, s_out=s)
         elif kind == "gla":
             out, _ = api.gla_chunk_fwd(q, k, v, _t(sub.log_alpha), chunk=64, s0=s, s_out=s)
+        elif kind == "mamba2":
+            out, _ = api.mamba2_chunk_fwd(q, k, v, _t(sub.log_alpha), chunk=64, s0=s, s_out=s)
         else:
             out, _ = api.gdelta_chunk_fwd(q, k, v, _t(sub.log_alpha), _t(sub.beta), chunk=64, s0=s, s_out=s)
         return out
