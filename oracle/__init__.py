@@ -34,5 +34,6 @@ from .glr_oracle import (  # noqa: F401
     gdelta_quadratic,
     gdelta_chunkwise,
     decode_step,
+    gdelta_decode_step,
     forward_substitution,
 )

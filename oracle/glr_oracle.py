@@ -1,4 +1,4 @@
-"""fp64 CPU oracle: four gate variants, three evaluation forms each, and one decode step.
+"""fp64 CPU oracle: four gate variants, three evaluation forms each, and two decode steps.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring): plain numpy in float64,
 shared with nothing on the GPU side.
@@ -54,6 +54,7 @@ __all__ = [
     "gdelta_quadratic",
     "gdelta_chunkwise",
     "decode_step",
+    "gdelta_decode_step",
     "forward_substitution",
 ]
 
@@ -439,4 +440,23 @@ def decode_step(q, k, v, alpha, s):
     """
     q, k, v, a, s = _f64(q, k, v, alpha, s)
     S = s * a[..., None, :] + _outer(v, k)
+    return _read(S, q), S
+
+
+def gdelta_decode_step(q, k, v, alpha, beta, s):
+    """One token of generation under the gated delta rule ("Scrivere meglio nella
+    memoria", section "Unire oblio e correzione: Gated DeltaNet"):
+    ``S <- S [alpha (I - beta k k^T)] + beta v k^T``, then ``o = S q``.
+
+    The transition is applied as written, as a d_k x d_k matrix multiplying the
+    memory from the right. ``q, k`` are ``[N, H, d_k]``, ``v`` is ``[N, H, d_v]``,
+    ``alpha`` and ``beta`` are ``[N, H]`` (one gate and one write strength per
+    sequence and head), ``s`` is ``[N, H, d_v, d_k]``. Returns ``(o, s_new)``; the
+    input state is not modified.
+    """
+    q, k, v, a, b, s = _f64(q, k, v, alpha, beta, s)
+    dk = k.shape[-1]
+    eye = np.eye(dk)
+    M = a[..., None, None] * (eye - b[..., None, None] * k[..., :, None] * k[..., None, :])
+    S = np.einsum("...mc,...cd->...md", s, M) + b[..., None, None] * _outer(v, k)
     return _read(S, q), S

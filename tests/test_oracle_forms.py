@@ -247,6 +247,26 @@ def test_decode_step_brute_force():
                 np.testing.assert_allclose(S[n, h, m], row, atol=1e-15)
 
 
+def test_gdelta_decode_step_brute_force():
+    """One gated-delta decode step by hand: e = sum_c S[m, c] k[c] (what the memory reads
+    under k), S_new[m, c] = alpha (S[m, c] - beta e k[c]) + beta v[m] k[c], o[m] = sum_c
+    S_new[m, c] q[c]."""
+    rng = np.random.default_rng(24)
+    N, H, dk, dv = 2, 2, 4, 3
+    q = rng.standard_normal((N, H, dk)); k = rng.standard_normal((N, H, dk))
+    v = rng.standard_normal((N, H, dv)); a = rng.uniform(0.1, 1.0, (N, H)); b = rng.uniform(0.0, 1.0, (N, H))
+    s = rng.standard_normal((N, H, dv, dk))
+    o, S = orc.gdelta_decode_step(q, k, v, a, b, s)
+    for n in range(N):
+        for h in range(H):
+            for m in range(dv):
+                e = sum(s[n, h, m, c] * k[n, h, c] for c in range(dk))
+                row = [a[n, h] * (s[n, h, m, c] - b[n, h] * e * k[n, h, c]) + b[n, h] * v[n, h, m] * k[n, h, c]
+                       for c in range(dk)]
+                np.testing.assert_allclose(S[n, h, m], row, atol=1e-14)
+                assert o[n, h, m] == pytest.approx(sum(row[c] * q[n, h, c] for c in range(dk)), abs=1e-13)
+
+
 # ----------------------------------------------------------------------------- resume
 
 @pytest.mark.parametrize("split", [0, 1, 7, 16, 33, 40])

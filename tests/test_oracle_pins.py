@@ -199,6 +199,41 @@ def test_delta_overwrite_reads_back_value(form, gated):
     np.testing.assert_allclose(np.einsum("bhmc,bhc->bhm", S, k[:, :, -1]), v[:, :, -1], atol=1e-11)
 
 
+def test_gdelta_decode_step_pins():
+    """The gated-delta decode step: (a) with beta = 1 and a unit key, the entry under k is
+    overwritten whatever the gate, S_new k = v ("Correggere: la delta rule"); (b) beta = 0
+    only fades the memory, S_new = alpha S ("Unire oblio e correzione"); (c) alpha = 1 and
+    beta = 1/2 with a unit key halves the error under k; (d) T steps of it give the
+    recurrent form of the chunked variant, token by token."""
+    rng = np.random.default_rng(16)
+    N, H, dk, dv = 3, 2, 8, 5
+    s = rng.standard_normal((N, H, dv, dk))
+    k = rng.standard_normal((N, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q = rng.standard_normal((N, H, dk)); v = rng.standard_normal((N, H, dv))
+    a = rng.uniform(0.3, 1.0, (N, H))
+    o, S = orc.gdelta_decode_step(q, k, v, a, np.ones((N, H)), s)
+    np.testing.assert_allclose(np.einsum("nhmc,nhc->nhm", S, k), v, atol=1e-12)
+    np.testing.assert_allclose(o, np.einsum("nhmc,nhc->nhm", S, q), atol=1e-12)
+    _, S = orc.gdelta_decode_step(q, k, v, a, np.zeros((N, H)), s)
+    np.testing.assert_allclose(S, a[..., None, None] * s, atol=1e-12)
+    _, S = orc.gdelta_decode_step(q, k, v, np.ones((N, H)), np.full((N, H), 0.5), s)
+    err_old = v - np.einsum("nhmc,nhc->nhm", s, k)
+    err_new = v - np.einsum("nhmc,nhc->nhm", S, k)
+    np.testing.assert_allclose(err_new, 0.5 * err_old, atol=1e-12)
+    T = 6
+    qs = rng.standard_normal((1, 1, T, dk)); ks = rng.standard_normal((1, 1, T, dk)) / 2
+    vs = rng.standard_normal((1, 1, T, dv))
+    la = np.log(rng.uniform(0.4, 1.0, (1, 1, T))); be = rng.uniform(0.0, 1.0, (1, 1, T))
+    s0 = rng.standard_normal((1, 1, dv, dk))
+    o_rec, S_rec = orc.gdelta_recurrent(qs, ks, vs, la, be, s0=s0)
+    S = s0[:, :, None].repeat(1, axis=2)[:, :, 0]
+    for t in range(T):
+        o_t, S = orc.gdelta_decode_step(qs[:, :, t], ks[:, :, t], vs[:, :, t], np.exp(la[:, :, t]),
+                                        be[:, :, t], S)
+        np.testing.assert_allclose(o_t, o_rec[:, :, t], atol=1e-12)
+    np.testing.assert_allclose(S, S_rec, atol=1e-12)
+
+
 def test_transition_eigenvalues_and_norm():
     """The transition I - beta k k^T has eigenvalues 1 (d-1 times) and 1 - beta |k|^2; its
     spectral norm is exactly 1 when 0 <= beta |k|^2 <= 2; Gated DeltaNet scales it by
