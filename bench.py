@@ -16,7 +16,7 @@ final memory written); ``traffic`` is the HBM traffic the counters measured for
 one call, snapshots included; ``mfma`` gives the same run against the dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on the host; ``others``
 reports the per-channel-gate (GLA), gated-delta, scalar data-dependent decay
-and decode workloads measured the same way.
+and decode (per-channel gate, gated delta rule) workloads measured the same way.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
     python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
@@ -178,6 +178,43 @@ def bench_decode(steps_total, torch, api, synthetic, dev):
                 alg_bytes_per_step=bytes_step)
 
 
+def bench_gdelta_decode(steps_total, torch, api, synthetic, dev):
+    """Gated-delta decode at the decode workload's shape (512 sequences x 32 heads, d = 128,
+    fp32 memory): a fresh bf16 token per step with the gated-delta workload's recipe
+    (q, k = L2(SiLU(N(0,1))), v ~ N(0,1), beta = sigmoid(N(0,1)), alpha = exp(-softplus(N(0,1))/8)
+    per sequence and head), drawn on the device; ``steps_total`` steps timed as one region."""
+    N, H, d = 512, 32, 128
+    w = synthetic.gdelta_decode_inputs(N, H, d, d, steps=0, seed=7)
+    s = torch.from_numpy(w.s0).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+
+    def unit_silu(x):
+        y = x * torch.sigmoid(x)
+        return y / y.norm(dim=-1, keepdim=True)
+
+    q = unit_silu(torch.randn((steps_total, N, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+    k = unit_silu(torch.randn((steps_total, N, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+    v = torch.randn((steps_total, N, H, d), generator=gen, device=dev).to(torch.bfloat16)
+    b = torch.sigmoid(torch.randn((steps_total, N, H), generator=gen, device=dev))
+    a = torch.exp(-torch.nn.functional.softplus(torch.randn((steps_total, N, H), generator=gen, device=dev)) / 8.0)
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+    for i in range(3):
+        api.gdelta_recurrent_step(q[i], k[i], v[i], a[i], b[i], s, o=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps_total):
+        api.gdelta_recurrent_step(q[i], k[i], v[i], a[i], b[i], s, o=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps_total
+    bytes_step = N * H * (2 * d * d * 4 + 3 * d * 2 + 2 * 4 + d * 2)
+    return dict(workload="gdelta_decode_n512h32_d128", steps=steps_total, us_per_step=ms * 1e3,
+                hbm_gbs=bytes_step / (ms * 1e-3) / 1e9, hbm_frac=bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                alg_bytes_per_step=bytes_step)
+
+
 KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_state.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_output.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_two_pass.hpp",
@@ -211,7 +248,7 @@ def measured_traffic():
 
 COPY_CAL_MB = 512   # size of the plain copy the counter runs are scaled by
 # kernels of one retention call (bf16, chunk 64, d_k = d_v = 128), as rocprofv3 names them
-TRAFFIC_KERNELS = ("glr::ck::state_kernel<64, 128, ", "glr::ck::output_kernel<64, 128, 128, false")
+TRAFFIC_KERNELS = ("glr::ck::state_kernel<64, 128, ", "glr::ck::output_kernel<64, 128, 128, 0,")
 
 
 def _counter_rows(d):
@@ -351,6 +388,9 @@ def main():
             others[name] = r
             torch.cuda.empty_cache()
         others["decode_n512h32_d128"] = bench_decode(args.decode_steps, torch, api, synthetic, dev)
+        torch.cuda.empty_cache()
+        others["gdelta_decode_n512h32_d128"] = bench_gdelta_decode(min(args.decode_steps, 200), torch, api,
+                                                                   synthetic, dev)
         torch.cuda.empty_cache()
 
     cfg = synthetic.CONFIGS[MAIN]

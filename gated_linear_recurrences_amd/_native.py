@@ -20,6 +20,7 @@ EXPORTED = (
     "gla_chunk_fwd",
     "gdelta_chunk_fwd",
     "la_recurrent_step",
+    "gdelta_recurrent_step",
     "la_status_str",
     "la_last_error",
     "la_version",
@@ -55,7 +56,9 @@ def load():
     lib.la_chunk_workspace_size.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.la_chunk_workspace_size.restype = ctypes.c_int
     lib.la_recurrent_step.argtypes = [P, P, P, F, F, P, I, I, I, I, I, P]
-    for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step"):
+    lib.gdelta_recurrent_step.argtypes = [P, P, P, F, F, F, P, I, I, I, I, I, P]
+    for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step",
+                 "gdelta_recurrent_step"):
         getattr(lib, name).restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
     lib.la_status_str.restype = ctypes.c_char_p

@@ -13,7 +13,7 @@ import torch
 from . import _native
 
 __all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step",
-           "workspace_size"]
+           "gdelta_recurrent_step", "workspace_size"]
 
 
 def _dtype_code(t):
@@ -179,4 +179,31 @@ def la_recurrent_step(q, k, v, alpha, s, o=None):
     lib = _native.load()
     _native.check(lib.la_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s), _ptr(o),
                                         N, H, dk, dv, _dtype_code(q), _stream(dev)))
+    return o
+
+
+def gdelta_recurrent_step(q, k, v, alpha, beta, s, o=None):
+    """One decode token of the gated delta rule, in place on s:
+    S <- S [alpha (I - beta k k^T)] + beta v k^T; o = S q.
+
+    q, k [N,H,d_k], v [N,H,d_v] (bf16 or fp32); alpha, beta [N,H] fp32; s [N,H,d_v,d_k] fp32."""
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    _require(k, "k", (N, H, dk), q.dtype, dev)
+    _require(v, "v", (N, H, dv), q.dtype, dev)
+    _require(alpha, "alpha", (N, H), torch.float32, dev)
+    _require(beta, "beta", (N, H), torch.float32, dev)
+    _require(s, "s", (N, H, dv, dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", (N, H, dv), q.dtype, dev)
+    lib = _native.load()
+    _native.check(lib.gdelta_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(s), _ptr(o),
+                                            N, H, dk, dv, _dtype_code(q), _stream(dev)))
     return o

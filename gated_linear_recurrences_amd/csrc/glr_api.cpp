@@ -158,7 +158,33 @@ la_status la_recurrent_step(const void* q, const void* k, const void* v, const f
     if (static_cast<int64_t>(N) * H >= (static_cast<int64_t>(1) << 31))
         return fail(LA_ERR_UNSUPPORTED, "%s", "N * H must be below 2^31");
     if (!used) return LA_OK;
-    glr::DecodeArgs a{q, k, v, alpha, s, o, N, H, dk, dv};
+    glr::DecodeArgs a{q, k, v, alpha, nullptr, s, o, N, H, dk, dv};
+    const hipError_t err = glr::launch_decode(dtype == LA_BF16, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+    return LA_OK;
+}
+
+la_status gdelta_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, float* s, void* o, int N, int H, int dk, int dv,
+                                la_dtype dtype, void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "%s", "unknown dtype");
+    if (N < 0 || H < 0) return fail(LA_ERR_INVALID, "%s", "negative N or H");
+    if (dk < 1 || dv < 1) return fail(LA_ERR_INVALID, "%s", "d_k and d_v must be >= 1");
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "d_k and d_v must be 16, 32, 64 or 128");
+    const bool used = N > 0 && H > 0;
+    la_status st;
+    if ((st = check_ptr(q, used, false, "q")) != LA_OK) return st;
+    if ((st = check_ptr(k, used, false, "k")) != LA_OK) return st;
+    if ((st = check_ptr(v, used, false, "v")) != LA_OK) return st;
+    if ((st = check_ptr(alpha, used, false, "alpha")) != LA_OK) return st;
+    if ((st = check_ptr(beta, used, false, "beta")) != LA_OK) return st;
+    if ((st = check_ptr(s, used, false, "s")) != LA_OK) return st;
+    if ((st = check_ptr(o, used, false, "o")) != LA_OK) return st;
+    if (static_cast<int64_t>(N) * H >= (static_cast<int64_t>(1) << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "N * H must be below 2^31");
+    if (!used) return LA_OK;
+    glr::DecodeArgs a{q, k, v, alpha, beta, s, o, N, H, dk, dv};
     const hipError_t err = glr::launch_decode(dtype == LA_BF16, a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
     return LA_OK;
@@ -176,6 +202,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (2 << 16) | 1; }
+int la_version(void) { return (2 << 16) | 2; }
 
 }  // extern "C"

@@ -27,7 +27,8 @@ struct DecodeArgs {
     const void* q;
     const void* k;
     const void* v;
-    const float* alpha;
+    const float* alpha;  // GLA: [N,H,dk]; gated delta: [N,H]
+    const float* beta;   // gated delta: [N,H]; nullptr for the GLA step
     float* s;
     void* o;
     int N, H, dk, dv;
@@ -39,7 +40,8 @@ hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t str
 size_t chunk_workspace_bytes(Variant variant, const ChunkArgs& a, bool bf16);
 // bfloat16 storage, bf16 MFMA with fp32 accumulation and fp32 memory.
 hipError_t launch_chunk_bf16(Variant variant, const ChunkArgs& a, hipStream_t stream);
-// one decode token; bf16 == true for bfloat16 token storage.
+// one decode token (the gated delta rule when a.beta is set); bf16 == true for
+// bfloat16 token storage.
 hipError_t launch_decode(bool bf16, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace glr

@@ -87,7 +87,7 @@ class Workload:
     log_gamma: Optional[np.ndarray] = None   # retention [H]
     log_alpha: Optional[np.ndarray] = None   # gla [B,H,T,dk]; mamba2, gdelta [B,H,T]
     beta: Optional[np.ndarray] = None        # gdelta [B,H,T]
-    alpha: Optional[np.ndarray] = None       # decode [N,H,dk] (or [steps,N,H,dk])
+    alpha: Optional[np.ndarray] = None       # decode [N,H,dk] (or [steps,N,H,dk]); delta decode [steps,N,H]
     s0: Optional[np.ndarray] = None          # [B,H,dv,dk] fp32
     meta: dict = field(default_factory=dict)
 
@@ -173,6 +173,26 @@ def decode_inputs(N, H, dk, dv, *, steps=1, dtype="bf16", seed=0):
         v[s] = _store(rng.standard_normal((N, H, dv)) * scale, dtype)
         a[s] = _sigmoid(rng.standard_normal((N, H, dk)) + 2.0).astype(np.float32)
     return Workload("decode", dtype, q, k, v, alpha=a, s0=s0)
+
+
+def gdelta_decode_inputs(N, H, dk, dv, *, steps=1, dtype="bf16", seed=0):
+    """Gated-delta decode: initial state S ~ N(0, 0.01) fp32, then ``steps`` fresh tokens with
+    the gated-delta workload's recipe: q, k = L2(SiLU(N(0,1))), v ~ N(0,1), beta = sigmoid(N(0,1))
+    and alpha = exp(-softplus(N(0,1)) / 8) per sequence and head. Leading step axis."""
+    rng = np.random.default_rng(seed)
+    s0 = (rng.standard_normal((N, H, dv, dk)) * 0.1).astype(np.float32)
+    q = np.empty((steps, N, H, dk), np.float32)
+    k = np.empty((steps, N, H, dk), np.float32)
+    v = np.empty((steps, N, H, dv), np.float32)
+    a = np.empty((steps, N, H), np.float32)
+    b = np.empty((steps, N, H), np.float32)
+    for s in range(steps):
+        q[s] = _store(_silu_l2(rng.standard_normal((N, H, dk))), dtype)
+        k[s] = _store(_silu_l2(rng.standard_normal((N, H, dk))), dtype)
+        v[s] = _store(rng.standard_normal((N, H, dv)), dtype)
+        b[s] = _sigmoid(rng.standard_normal((N, H))).astype(np.float32)
+        a[s] = np.exp(-_softplus(rng.standard_normal((N, H))) / 8.0).astype(np.float32)
+    return Workload("gdelta_decode", dtype, q, k, v, alpha=a, beta=b, s0=s0)
 
 
 # The five workloads the throughput and parity figures are quoted on, and the scalar

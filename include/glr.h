@@ -176,6 +176,21 @@ la_status la_recurrent_step(const void* q, const void* k, const void* v,
                             int N, int H, int dk, int dv,
                             la_dtype dtype, void* stream);
 
+/*
+ * One decode token for N sequences x H heads under the gated delta rule
+ * ("Scrivere meglio nella memoria", section "Unire oblio e correzione: Gated
+ * DeltaNet"; the recurrent form of the RetNet page):
+ *     S <- S [alpha (I - beta k k^T)] + beta v k^T;  o = S q.
+ * q, k [N][H][d_k], v and o [N][H][d_v] in `dtype`; alpha and beta [N][H]
+ * float32 (one gate in (0, 1] and one write strength per sequence and head);
+ * s [N][H][d_v][d_k] float32 is read and overwritten in place.  Errors as for
+ * la_recurrent_step.
+ */
+la_status gdelta_recurrent_step(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, float* s, void* o,
+                                int N, int H, int dk, int dv,
+                                la_dtype dtype, void* stream);
+
 /* Static text for a status code. */
 const char* la_status_str(la_status status);
 
@@ -184,7 +199,7 @@ const char* la_status_str(la_status status);
 const char* la_last_error(void);
 
 /* ABI version: (major << 16) | minor (2.0: workspace arguments; 2.1:
- * mamba2_chunk_fwd). */
+ * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step). */
 int la_version(void);
 
 #ifdef __cplusplus

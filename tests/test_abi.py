@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 2
-    assert lib.la_version() & 0xffff >= 1      # 2.1: mamba2_chunk_fwd
+    assert lib.la_version() & 0xffff >= 2      # 2.1: mamba2_chunk_fwd, 2.2: gdelta_recurrent_step
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -149,3 +149,22 @@ def test_decode_validation(lib):
     assert call(dk=48) == _native.LA_ERR_UNSUPPORTED
     assert call(dtype=3) == _native.LA_ERR_INVALID
     assert call(N=0, q=None, k=None, v=None, alpha=None, s=None, o=None) == _native.LA_OK
+
+
+def test_gdelta_decode_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, s=FAKE, o=FAKE, N=4, H=2, dk=128, dv=128, dtype=1)
+        a.update(kw)
+        return lib.gdelta_recurrent_step(P(a["q"]), P(a["k"]), P(a["v"]), P(a["alpha"]), P(a["beta"]), P(a["s"]),
+                                         P(a["o"]), a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+    assert call(beta=None) == _native.LA_ERR_INVALID
+    assert b"beta is NULL" in lib.la_last_error()
+    assert call(s=None) == _native.LA_ERR_INVALID
+    assert call(alpha=MISALIGNED) == _native.LA_ERR_INVALID
+    assert call(N=-1) == _native.LA_ERR_INVALID
+    assert call(dk=48) == _native.LA_ERR_UNSUPPORTED
+    assert call(dtype=3) == _native.LA_ERR_INVALID
+    assert call(N=0, q=None, k=None, v=None, alpha=None, beta=None, s=None, o=None) == _native.LA_OK

@@ -246,6 +246,41 @@ def test_decode_parity_small(dtype, dims):
         _decode_assert(outs[i], o_ref, S if i == 4 else S_ref, S_ref, f"decode {dtype} {dims} step {i}", dtype)
 
 
+def _gdelta_decode_run(w, steps):
+    st = _storage(w)
+    s = _t(w.s0)
+    outs = []
+    for i in range(steps):
+        o = api.gdelta_recurrent_step(_t(w.q[i], st), _t(w.k[i], st), _t(w.v[i], st), _t(w.alpha[i]),
+                                      _t(w.beta[i]), s)
+        outs.append(o.float())
+    torch.cuda.synchronize()
+    return [x.cpu().numpy().astype(np.float64) for x in outs], s.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dims", [(3, 2, 16, 16), (2, 3, 32, 128), (4, 2, 128, 64), (2, 2, 64, 32), (2, 2, 128, 16)])
+def test_gdelta_decode_parity_small(dtype, dims):
+    N, H, dk, dv = dims
+    w = synthetic.gdelta_decode_inputs(N, H, dk, dv, steps=5, dtype=dtype, seed=400 + dk + dv)
+    outs, S = _gdelta_decode_run(w, 5)
+    S_ref = w.s0.astype(np.float64)
+    for i in range(5):
+        o_ref, S_ref = orc.gdelta_decode_step(w.q[i], w.k[i], w.v[i], w.alpha[i], w.beta[i], S_ref)
+        _decode_assert(outs[i], o_ref, S if i == 4 else S_ref, S_ref, f"gdelta decode {dtype} {dims} step {i}",
+                       dtype)
+
+
+def test_gdelta_decode_full_size_parity():
+    """512 sequences x 32 heads, d = 128, three gated-delta steps, every output and the whole memory."""
+    w = synthetic.gdelta_decode_inputs(512, 32, 128, 128, steps=3, dtype="bf16", seed=7)
+    outs, S = _gdelta_decode_run(w, 3)
+    S_ref = w.s0.astype(np.float64)
+    for i in range(3):
+        o_ref, S_ref = orc.gdelta_decode_step(w.q[i], w.k[i], w.v[i], w.alpha[i], w.beta[i], S_ref)
+        _decode_assert(outs[i], o_ref, S if i == 2 else S_ref, S_ref, f"gdelta decode full step {i}", "bf16")
+
+
 def test_decode_full_size_parity():
     """512 sequences x 32 heads, d = 128 (the decode workload's launch shape), three steps,
     every output and the whole memory."""
