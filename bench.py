@@ -21,6 +21,7 @@ and decode (per-channel gate, gated delta rule) workloads measured the same way.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
     python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+    python bench.py --kernel-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 """
 
 import argparse
@@ -313,6 +314,33 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     print("\n".join(lines))
 
 
+def kernel_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Per-kernel HBM bytes per dispatch for every library kernel in a FETCH_SIZE and a
+    WRITE_SIZE run, each scaled by the same counter on the plain copy; prints a table."""
+    is_copy = lambda k: "copy" in k.lower()
+    copy_bytes = int(COPY_CAL_MB * 1e6) // 4 * 4
+    cols = {}
+    for label, d, cd in (("fetch", fetch_dir, copy_fetch_dir), ("write", write_dir, copy_write_dir)):
+        rows = _counter_rows(d)
+        scale = copy_bytes / 1024.0 / max(_per_dispatch(_counter_rows(cd), is_copy).values())
+        names = sorted({r["Kernel_Name"] for r in rows if "glr::" in r["Kernel_Name"]})
+        for name in names:
+            disp = _per_dispatch(rows, lambda k, name=name: k == name)
+            cols.setdefault(name, {})[label] = (sum(disp.values()) / len(disp) * 1024.0 * scale, len(disp))
+        cols.setdefault("_scale", {})[label] = scale
+    lines = [f"FETCH_SIZE scale {cols['_scale']['fetch']:.4f}, WRITE_SIZE scale {cols['_scale']['write']:.4f} "
+             f"(plain copy of {copy_bytes:,} B)", "",
+             "| kernel | dispatches | read bytes / dispatch | written bytes / dispatch |", "|---|---|---|---|"]
+    for name, c in cols.items():
+        if name == "_scale":
+            continue
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        f, nf = c.get("fetch", (float("nan"), 0))
+        w, _ = c.get("write", (float("nan"), 0))
+        lines.append(f"| `{short}` | {nf} | {f:,.0f} | {w:,.0f} |")
+    print("\n".join(lines))
+
+
 def copy_calibration(mbytes, steps, torch):
     """A plain device copy of ``mbytes`` MB, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     n = int(mbytes * 1e6) // 4
@@ -357,12 +385,17 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes --steps times (counter scaling)")
+    ap.add_argument("--kernel-traffic", nargs=4, metavar="DIR",
+                    help="per-kernel HBM bytes from FETCH/WRITE runs and the copy calibration runs")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR",
                     help="FETCH_SIZE and WRITE_SIZE counter dirs of a bench run, then of a copy run: "
                          "write profiles/pmc_traffic.json")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.kernel_traffic:
+        kernel_traffic(*args.kernel_traffic)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the recurrences shard over (batch, head) with no "
