@@ -35,5 +35,7 @@ from .glr_oracle import (  # noqa: F401
     gdelta_chunkwise,
     decode_step,
     gdelta_decode_step,
+    silu_l2,
+    rms_norm,
     forward_substitution,
 )

@@ -55,6 +55,8 @@ __all__ = [
     "gdelta_chunkwise",
     "decode_step",
     "gdelta_decode_step",
+    "silu_l2",
+    "rms_norm",
     "forward_substitution",
 ]
 
@@ -460,3 +462,26 @@ def gdelta_decode_step(q, k, v, alpha, beta, s):
     M = a[..., None, None] * (eye - b[..., None, None] * k[..., :, None] * k[..., None, :])
     S = np.einsum("...mc,...cd->...md", s, M) + b[..., None, None] * _outer(v, k)
     return _read(S, q), S
+
+
+# --------------------------------------------------------------------------- feature map and output norm
+
+def silu_l2(x):
+    """DeltaNet's feature map on a query or key ("Scrivere meglio nella memoria", section
+    "Superiore" of the introduction, and section "Correggere: la delta rule"): a SiLU,
+    ``x * sigmoid(x)``, followed by L2 normalisation over the channel axis, so that
+    ``beta ||k||^2 <= 1`` keeps the transition's eigenvalues in [0, 1]. A zero row stays
+    zero (its norm is 0; nothing is divided)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x / (1.0 + np.exp(-x))
+    n = np.sqrt(np.sum(y * y, axis=-1, keepdims=True))
+    return np.where(n > 0.0, y / np.where(n > 0.0, n, 1.0), 0.0)
+
+
+def rms_norm(o, weight, eps):
+    """The output normalisation the pages name for DeltaNet (same page, on stabilising the
+    readout without the normaliser z_t): each output row divided by its root mean square
+    over the value channels, ``o / sqrt(mean(o^2) + eps)``, times a per-channel weight."""
+    o = np.asarray(o, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    return o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps) * w

@@ -234,6 +234,37 @@ def test_gdelta_decode_step_pins():
     np.testing.assert_allclose(S, S_rec, atol=1e-12)
 
 
+def test_silu_l2_and_rms_norm():
+    """The feature map and the output norm against their definitions at points where the
+    answer is known: SiLU(0) = 0, SiLU(x) -> x for large x and -> 0 for very negative x,
+    SiLU(1) = 1 / (1 + 1/e); every mapped row has unit L2 norm and keeps the direction of
+    SiLU(x); a row that SiLU sends to zero stays zero. RMS norm: unit root mean square
+    with unit weight, invariant to scaling the row, the weight multiplies channel by
+    channel, and eps only matters for tiny rows."""
+    x = np.array([[0.0, 30.0, -30.0, 1.0]])
+    y = orc.silu_l2(x)
+    silu = np.array([0.0, 30.0, -30.0 * np.exp(-30.0) / (1.0 + np.exp(-30.0)), 1.0 / (1.0 + np.exp(-1.0))])
+    np.testing.assert_allclose(y[0], silu / np.linalg.norm(silu), rtol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(y), 1.0, rtol=1e-14)
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((3, 5, 16))
+    y = orc.silu_l2(x)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), 1.0, rtol=1e-13)
+    s = x / (1.0 + np.exp(-x))
+    cos = np.sum(y * s, axis=-1) / np.linalg.norm(s, axis=-1)
+    np.testing.assert_allclose(cos, 1.0, rtol=1e-13)
+    np.testing.assert_array_equal(orc.silu_l2(np.zeros((2, 8))), 0.0)
+    o = rng.standard_normal((4, 7, 32)) * 3.0
+    r = orc.rms_norm(o, np.ones(32), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(r * r, axis=-1)), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(orc.rms_norm(5.0 * o, np.ones(32), 0.0), r, rtol=1e-13)
+    w = rng.uniform(0.5, 2.0, 32)
+    np.testing.assert_allclose(orc.rms_norm(o, w, 0.0), r * w, rtol=1e-13)
+    np.testing.assert_allclose(orc.rms_norm(o, np.ones(32), 1e-12), r, rtol=1e-9)
+    tiny = np.full((1, 32), 1e-4)
+    np.testing.assert_allclose(orc.rms_norm(tiny, np.ones(32), 1e-6), tiny / np.sqrt(1e-8 + 1e-6), rtol=1e-13)
+
+
 def test_transition_eigenvalues_and_norm():
     """The transition I - beta k k^T has eigenvalues 1 (d-1 times) and 1 - beta |k|^2; its
     spectral norm is exactly 1 when 0 <= beta |k|^2 <= 2; Gated DeltaNet scales it by
