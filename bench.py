@@ -16,7 +16,8 @@ final memory written); ``traffic`` is the HBM traffic the counters measured for
 one call, snapshots included; ``mfma`` gives the same run against the dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on the host; ``others``
 reports the per-channel-gate (GLA), gated-delta, scalar data-dependent decay
-and decode (per-channel gate, gated delta rule) workloads measured the same way.
+and decode (per-channel gate, gated delta rule) workloads measured the same way,
+and the gated delta rule with its feature map and output norm fused in.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
     python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
@@ -214,6 +215,37 @@ def bench_gdelta_decode(steps_total, torch, api, synthetic, dev):
     return dict(workload="gdelta_decode_n512h32_d128", steps=steps_total, us_per_step=ms * 1e3,
                 hbm_gbs=bytes_step / (ms * 1e-3) / 1e9, hbm_frac=bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 alg_bytes_per_step=bytes_step)
+
+
+def bench_gdelta_fused(steps, warmup, torch, api, synthetic, dev):
+    """The gated-delta workload from the projections before DeltaNet's feature map, with the
+    RMS output norm, through gdelta_chunk_fwd_fused; beside it the same computation with the
+    map and the norm as separate torch operations around gdelta_chunk_fwd."""
+    B, H, T, d = 4, 16, 8192, 128
+    w = synthetic.gdelta_inputs(B, H, T, d, d, chunk=64, dtype="bf16", seed=4, raw_qk=True)
+    b = upload(w, torch, dev)
+    del w
+    weight = torch.linspace(0.5, 1.5, d, device=dev)
+    ws = torch.empty(api.workspace_size("gdelta_fused", B, H, T, d, d, 64), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+    s_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    F = torch.nn.functional
+
+    def fused():
+        api.gdelta_chunk_fwd_fused(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], chunk=64, o_norm_weight=weight,
+                                   o=o, s_out=s_out, workspace=ws)
+
+    def unfused():
+        qn = F.normalize(F.silu(b["q"].float()), dim=-1).to(torch.bfloat16)
+        kn = F.normalize(F.silu(b["k"].float()), dim=-1).to(torch.bfloat16)
+        api.gdelta_chunk_fwd(qn, kn, b["v"], b["log_alpha"], b["beta"], chunk=64, o=o, s_out=s_out, workspace=ws)
+        of = o.float()
+        return (of * torch.rsqrt(of.pow(2).mean(-1, keepdim=True) + 1e-6) * weight).to(torch.bfloat16)
+
+    ms_f = time_calls([fused], steps, warmup, torch)[1]
+    ms_u = time_calls([unfused], steps, warmup, torch)[1]
+    return dict(workload="gdelta_fused_b4h16_t8192_d128", kernel_ms=ms_f, unfused_torch_ms=ms_u,
+                tokens_per_s=B * H * T / (ms_f * 1e-3), speedup_vs_unfused=ms_u / ms_f)
 
 
 KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_state.hpp",
@@ -421,6 +453,10 @@ def main():
             others[name] = r
             torch.cuda.empty_cache()
         others["decode_n512h32_d128"] = bench_decode(args.decode_steps, torch, api, synthetic, dev)
+        torch.cuda.empty_cache()
+        others["gdelta_fused_b4h16_t8192_d128"] = bench_gdelta_fused(max(20, args.steps // 4),
+                                                                     max(3, args.warmup // 4), torch, api,
+                                                                     synthetic, dev)
         torch.cuda.empty_cache()
         others["gdelta_decode_n512h32_d128"] = bench_gdelta_decode(min(args.decode_steps, 200), torch, api,
                                                                    synthetic, dev)

@@ -7,7 +7,7 @@ The computation lives in the HIP library ``libglr.so`` (C ABI in ``include/glr.h
 """
 
 from .api import (la_chunk_fwd, mamba2_chunk_fwd, gla_chunk_fwd, gdelta_chunk_fwd,  # noqa: F401
-                  la_recurrent_step, gdelta_recurrent_step, workspace_size)
+                  gdelta_chunk_fwd_fused, la_recurrent_step, gdelta_recurrent_step, workspace_size)
 
-__all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step",
-           "gdelta_recurrent_step", "workspace_size"]
+__all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
+           "la_recurrent_step", "gdelta_recurrent_step", "workspace_size"]

@@ -11,7 +11,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libglr.so")
 
 LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
-LA_RETENTION, LA_GLA, LA_GDELTA, LA_MAMBA2 = 0, 1, 2, 3
+LA_RETENTION, LA_GLA, LA_GDELTA, LA_MAMBA2, LA_GDELTA_FUSED = 0, 1, 2, 3, 4
+LA_FUSE_QK_SILU_L2, LA_FUSE_OUT_RMSNORM = 1, 2
 
 EXPORTED = (
     "la_chunk_workspace_size",
@@ -19,6 +20,7 @@ EXPORTED = (
     "mamba2_chunk_fwd",
     "gla_chunk_fwd",
     "gdelta_chunk_fwd",
+    "gdelta_chunk_fwd_fused",
     "la_recurrent_step",
     "gdelta_recurrent_step",
     "la_status_str",
@@ -53,12 +55,14 @@ def load():
     lib.gla_chunk_fwd.argtypes = chunk
     lib.mamba2_chunk_fwd.argtypes = chunk
     lib.gdelta_chunk_fwd.argtypes = [P, P, P, F, F, F, P, F, I, I, I, I, I, I, I, P, Z, P]
+    lib.gdelta_chunk_fwd_fused.argtypes = [P, P, P, F, F, F, P, F, F, ctypes.c_float, I,
+                                           I, I, I, I, I, I, I, P, Z, P]
     lib.la_chunk_workspace_size.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.la_chunk_workspace_size.restype = ctypes.c_int
     lib.la_recurrent_step.argtypes = [P, P, P, F, F, P, I, I, I, I, I, P]
     lib.gdelta_recurrent_step.argtypes = [P, P, P, F, F, F, P, I, I, I, I, I, P]
-    for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step",
-                 "gdelta_recurrent_step"):
+    for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
+                 "la_recurrent_step", "gdelta_recurrent_step"):
         getattr(lib, name).restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
     lib.la_status_str.restype = ctypes.c_char_p

@@ -12,8 +12,8 @@ import torch
 
 from . import _native
 
-__all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "la_recurrent_step",
-           "gdelta_recurrent_step", "workspace_size"]
+__all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
+           "la_recurrent_step", "gdelta_recurrent_step", "workspace_size"]
 
 
 def _dtype_code(t):
@@ -149,10 +149,34 @@ def gdelta_chunk_fwd(q, k, v, log_alpha, beta, chunk=64, s0=None, o=None, s_out=
     return o, s_out
 
 
+def gdelta_chunk_fwd_fused(q, k, v, log_alpha, beta, chunk=64, qk_silu_l2=True, o_norm_weight=None,
+                           o_norm_eps=1e-6, s0=None, o=None, s_out=None, return_state=True, workspace=None):
+    """gdelta_chunk_fwd with DeltaNet's feature map and output norm fused in: with
+    ``qk_silu_l2`` q and k are the projections before SiLU + L2 normalisation; with an
+    ``o_norm_weight`` [d_v] fp32 every output row is RMS-normalised and weighted."""
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
+    _require(log_alpha, "log_alpha", (B, H, T), torch.float32, q.device)
+    _require(beta, "beta", (B, H, T), torch.float32, q.device)
+    fuse = _native.LA_FUSE_QK_SILU_L2 if qk_silu_l2 else 0
+    if o_norm_weight is not None:
+        _require(o_norm_weight, "o_norm_weight", (dv,), torch.float32, q.device)
+        fuse |= _native.LA_FUSE_OUT_RMSNORM
+    ws, ws_bytes = _workspace(_native.LA_GDELTA_FUSED if qk_silu_l2 else _native.LA_GDELTA, dims, chunk, q,
+                              workspace)
+    lib = _native.load()
+    _native.check(lib.gdelta_chunk_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0),
+                                             _ptr(o), _ptr(s_out), _ptr(o_norm_weight), float(o_norm_eps), fuse,
+                                             B, H, T, dk, dv, chunk, _dtype_code(q), _ptr(ws), ws_bytes,
+                                             _stream(q.device)))
+    return o, s_out
+
+
 def workspace_size(kind, B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16):
-    """Device workspace in bytes for a chunk entry point; kind in {"retention", "mamba2", "gla", "gdelta"}."""
+    """Device workspace in bytes for a chunk entry point; kind in {"retention", "mamba2", "gla", "gdelta",
+    "gdelta_fused"} ("gdelta_fused": gdelta_chunk_fwd_fused with the feature map fused in)."""
     variant = {"retention": _native.LA_RETENTION, "mamba2": _native.LA_MAMBA2, "gla": _native.LA_GLA,
-               "gdelta": _native.LA_GDELTA}[kind]
+               "gdelta": _native.LA_GDELTA, "gdelta_fused": _native.LA_GDELTA_FUSED}[kind]
     code = _native.LA_BF16 if dtype == torch.bfloat16 else _native.LA_F32
     return _native.workspace_size(variant, B, H, T, dk, dv, chunk, code)
 

@@ -71,6 +71,29 @@ constexpr int tile_stride(int width) { return width == 16 ? 16 : width + 16; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u16x8 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// DeltaNet's feature map on a row of q or k held as 16-byte pieces by PPR consecutive
+// lanes (a PPR-aligned group): SiLU x / (1 + e^-x) per element, then the row scaled to
+// unit L2 norm; the squared sum meets across the group by butterfly shuffles. Every
+// lane of the wave must take part (groups are uniformly valid or ignored).
+template <int PPR>
+__device__ __forceinline__ u16x8 silu_l2_piece(u16x8 raw) {
+    float y[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = bf16_bits_to_f32(raw[e]);
+        y[e] = x * __builtin_amdgcn_rcpf(1.f + ex2(-x * kLog2e));   // ~1 ulp; the result is rounded to bf16
+        ss += y[e] * y[e];
+    }
+#pragma unroll
+    for (int off = 1; off < PPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+    u16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = f32_to_bf16_bits(y[e] * inv);
+    return out;
+}
+
 // Scale four bf16 values by four fp32 factors (round to bf16 again).
 __device__ __forceinline__ bf16x4 scale4(bf16x4 x, f32x4 s) { return cvt4(up4(x) * s); }
 

@@ -32,19 +32,21 @@ namespace ck {
 
 // Workspace of one call: per (sequence, chunk) W [C][DK] bf16, U [DV][C] fp32,
 // G [C] fp32 and the memory entering the chunk S [DV][DK] bf16, each array
-// contiguous over (sequence, chunk).
+// contiguous over (sequence, chunk); with the fused feature map also the mapped
+// keys KN [C][DK] bf16 (written by the prep, read by the other two kernels).
 struct DeltaWs {
     u16* w;
     float* u;
     float* g;
     u16* s;
+    u16* kn;
 };
 
 inline size_t delta_ws_align(size_t x) { return (x + 255) / 256 * 256; }
 
-inline size_t delta_ws_bytes(int64_t chunks, int C, int dk, int dv) {
+inline size_t delta_ws_bytes(int64_t chunks, int C, int dk, int dv, bool mapped_keys) {
     return delta_ws_align(chunks * C * dk * 2) + delta_ws_align(chunks * dv * C * 4) + delta_ws_align(chunks * C * 4) +
-           delta_ws_align(chunks * dv * dk * 2);
+           delta_ws_align(chunks * dv * dk * 2) + (mapped_keys ? delta_ws_align(chunks * C * dk * 2) : 0);
 }
 
 inline DeltaWs delta_ws_split(void* base, int64_t chunks, int C, int dk, int dv) {
@@ -57,6 +59,8 @@ inline DeltaWs delta_ws_split(void* base, int64_t chunks, int C, int dk, int dv)
     ws.g = reinterpret_cast<float*>(b);
     b += delta_ws_align(chunks * C * 4);
     ws.s = reinterpret_cast<u16*>(b);
+    b += delta_ws_align(chunks * dv * dk * 2);
+    ws.kn = reinterpret_cast<u16*>(b);   // only inside the workspace with the fused feature map
     return ws;
 }
 
@@ -71,6 +75,9 @@ struct DeltaParams {
     float* s_out;         // [BH][DV][DK] or null
     DeltaWs ws;
     int T, NC, vblocks;
+    int fuse;             // bit 0: SiLU + L2 on q, k; bit 1: RMS norm of o (weight onw, eps oeps)
+    const float* onw;     // [DV] or null
+    float oeps;
 };
 
 // ====================================================================== prep
@@ -176,9 +183,12 @@ void delta_prep_kernel(DeltaParams p) {
 #pragma unroll
     for (int i = 0; i < KP_PER; ++i) {
         const int idx = tid + i * NT;
+        const u16x8 x = (p.fuse & 1) ? silu_l2_piece<DK / 8>(rk[i]) : rk[i];
         if (idx < KP) {
             const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            *reinterpret_cast<u16x8*>(sK + j * KS + col) = (j < n) ? rk[i] : z8;
+            *reinterpret_cast<u16x8*>(sK + j * KS + col) = (j < n) ? x : z8;
+            // the mapped keys for the state and output passes (rows past the end zero)
+            if (p.fuse & 1) *reinterpret_cast<u16x8*>(p.ws.kn + chunk * C * DK + j * DK + col) = (j < n) ? x : z8;
         }
     }
 #pragma unroll
@@ -390,7 +400,8 @@ void delta_state_kernel(DeltaParams p) {
         const int c = cr < NC ? cr : NC - 1;
         const int n = chunk_len(c);
         const u16* wc = p.ws.w + (static_cast<int64_t>(bh) * NC + c) * C * DK;
-        const u16* kc = p.k + (tok0 + static_cast<int64_t>(c) * C) * DK;
+        const u16* kc = (p.fuse & 1) ? p.ws.kn + (static_cast<int64_t>(bh) * NC + c) * C * DK
+                                     : p.k + (tok0 + static_cast<int64_t>(c) * C) * DK;
 #pragma unroll
         for (int i = 0; i < KP_PER; ++i) {
             const int idx = tid + i * NT;
@@ -539,7 +550,9 @@ struct DOutLayout {
     static constexpr int oK = oQ + al(C * QS * 2);
     static constexpr int oP = oK + al(C * QS * 2);
     static constexpr int oG = oP + al(C * PS * 2);
-    static constexpr int bytes = oG + al(C * 4);
+    static constexpr int NP = DV >= 32 ? DV / 32 : 1;
+    static constexpr int oR = oG + al(C * 4);            // RMS norm: per (value pair, row) partial sums
+    static constexpr int bytes = oR + al(NP * C * 4);
     static_assert(bytes <= 64 * 1024, "LDS budget of the delta output pass exceeded");
 };
 
@@ -583,7 +596,7 @@ void delta_output_kernel(DeltaParams p) {
         const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
         const unsigned off = (idx < QP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
         rq[i] = *reinterpret_cast<const u16x8*>(p.q + tok0 * DK + off);
-        rk[i] = *reinterpret_cast<const u16x8*>(p.k + tok0 * DK + off);
+        rk[i] = *reinterpret_cast<const u16x8*>(((p.fuse & 1) ? p.ws.kn + chunk * C * DK : p.k + tok0 * DK) + off);
         rw[i] = *reinterpret_cast<const u16x8*>(wc + off);
     }
     const float gl = (tid < C) ? p.ws.g[chunk * C + tid] : 0.f;
@@ -612,11 +625,13 @@ void delta_output_kernel(DeltaParams p) {
 #pragma unroll
     for (int i = 0; i < QP_PER; ++i) {
         const int idx = tid + i * NT;
+        const u16x8 qx = (p.fuse & 1) ? silu_l2_piece<DK / 8>(rq[i]) : rq[i];
+        const u16x8 kx = rk[i];   // mapped by the prep when the feature map is fused
         if (idx < QP) {
             const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
             const bool ok = j < n;
-            *reinterpret_cast<u16x8*>(sQ + j * QS + col) = ok ? rq[i] : z8;
-            *reinterpret_cast<u16x8*>(sK + j * QS + col) = ok ? rk[i] : z8;
+            *reinterpret_cast<u16x8*>(sQ + j * QS + col) = ok ? qx : z8;
+            *reinterpret_cast<u16x8*>(sK + j * QS + col) = ok ? kx : z8;
         }
     }
     if (tid < C) sG[tid] = gl;
@@ -677,8 +692,16 @@ void delta_output_kernel(DeltaParams p) {
         }
     }
 
-    // ---- outputs: e^(G_i) S_in q_i + P U
-    for (int item = w; item < CT * NP; item += NW) {
+    // ---- outputs: e^(G_i) S_in q_i + P U, items (row tile, value pair) kept in registers
+    // until the optional RMS norm has every row's sum of squares
+    constexpr int ITEMS = (CT * NP + NW - 1) / NW;
+    f32x4 ov[ITEMS][2];
+#pragma unroll
+    for (int s = 0; s < ITEMS; ++s) {
+        const int item = w + NW * s;
+        ov[s][0] = zf4();
+        ov[s][1] = zf4();
+        if (item >= CT * NP) continue;
         const int it = item / NP;
         const int i = 16 * it + r16;
         const float oscale = ex2(sG[i]);
@@ -696,7 +719,6 @@ void delta_output_kernel(DeltaParams p) {
                 pb[jb] = join8(ld4(prow), (2 * jb + 1 <= it) ? ld4(prow + 16) : zero4());
             }
         }
-        f32x4 o2[2];
 #pragma unroll
         for (int tt = 0; tt < (DV >= 32 ? 2 : 1); ++tt) {
             f32x4 acc = zf4();
@@ -714,15 +736,55 @@ void delta_output_kernel(DeltaParams p) {
                     acc = mfma_16x16x32(join8(cvt4(u0 - up4(h0)), cvt4(u1 - up4(h1))), pb[jb], acc);
                 }
             }
-            o2[tt] = acc;
+            ov[s][tt] = acc;
         }
+    }
+    if (p.fuse & 2) {
+        // lane (r16, g) of item (it, pp) holds o[16it + r16][32pp + 16tt + 4g + r]: the
+        // pair's share of each row's sum of squares, over g by shuffles, then over the
+        // pairs in LDS
+        float* const sRow = reinterpret_cast<float*>(smem + Lay::oR);
+#pragma unroll
+        for (int s = 0; s < ITEMS; ++s) {
+            const int item = w + NW * s;
+            float ss = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ss += ov[s][tt][r] * ov[s][tt][r];
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (item < CT * NP && g == 0) sRow[pp * C + 16 * (item / NP) + r16] = ss;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int s = 0; s < ITEMS; ++s) {
+            const int item = w + NW * s;
+            if (item >= CT * NP) continue;
+            const int i = 16 * (item / NP) + r16;
+            float tot = 0.f;
+#pragma unroll
+            for (int q2 = 0; q2 < NP; ++q2) tot += sRow[q2 * C + i];
+            const float inv = 1.f / __builtin_sqrtf(tot / static_cast<float>(DV) + p.oeps);
+#pragma unroll
+            for (int tt = 0; tt < (DV >= 32 ? 2 : 1); ++tt) {
+                const f32x4 wv = ldf4(p.onw + ((DV >= 32) ? 32 * pp + 16 * tt : 0) + 4 * g);
+                ov[s][tt] = ov[s][tt] * wv * inv;
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < ITEMS; ++s) {
+        const int item = w + NW * s;
+        if (item >= CT * NP) continue;
+        const int i = 16 * (item / NP) + r16;
         if (i < n) {
             u16* orow = p.o + (tok0 + i) * DV;
             if constexpr (DV >= 32) {
-                st4(orow + 32 * pp + 4 * g, cvt4(o2[0]));
-                st4(orow + 32 * pp + 16 + 4 * g, cvt4(o2[1]));
+                st4(orow + 32 * pp + 4 * g, cvt4(ov[s][0]));
+                st4(orow + 32 * pp + 16 + 4 * g, cvt4(ov[s][1]));
             } else {
-                st4(orow + 4 * g, cvt4(o2[0]));
+                st4(orow + 4 * g, cvt4(ov[s][0]));
             }
         }
     }
@@ -745,6 +807,9 @@ hipError_t launch_delta_dv(const ChunkArgs& a, hipStream_t stream) {
     p.ws = delta_ws_split(a.ws, heads * NC, C, DK, DV);
     p.T = a.T;
     p.NC = NC;
+    p.fuse = a.fuse;
+    p.onw = a.onw;
+    p.oeps = a.oeps;
     // state pass: two value tiles x two key groups per workgroup (fewer when the head is small)
     constexpr int NVT = DV >= 32 ? 2 : 1;
     constexpr int NKH = DK >= 32 ? 2 : 1;

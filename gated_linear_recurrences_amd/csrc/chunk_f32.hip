@@ -42,7 +42,7 @@ void chunk_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                       const float* __restrict__ v, const float* __restrict__ gate,
                       const float* __restrict__ beta, const float* __restrict__ s0,
                       float* __restrict__ o, float* __restrict__ s_out,
-                      int H, int T, int dv) {
+                      int H, int T, int dv, int fuse) {
     __shared__ float Qs[C][DK + 1];
     __shared__ float Ks[C][DK + 1];
     __shared__ float Vs[C][DVT + 1];          // values; pseudo-values u for the delta rule
@@ -88,6 +88,23 @@ void chunk_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 for (int i = 0; i < C; ++i) {
                     if (i < n) acc += gate[base_k + static_cast<int64_t>(t0 + i) * DK + c];
                     Bs[i][c] = acc;
+                }
+            }
+        }
+        if constexpr (VARIANT == kGDelta) {
+            if (fuse & 1) {
+                // DeltaNet's feature map on q and k: SiLU, then unit L2 norm per token
+                __syncthreads();
+                for (int r = tid; r < 2 * C; r += kThreads) {
+                    float* row = (r < C) ? Qs[r] : Ks[r - C];
+                    float ss = 0.f;
+                    for (int c = 0; c < DK; ++c) {
+                        const float y = row[c] / (1.f + __expf(-row[c]));
+                        row[c] = y;
+                        ss += y * y;
+                    }
+                    const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+                    for (int c = 0; c < DK; ++c) row[c] *= inv;
                 }
             }
         }
@@ -192,6 +209,21 @@ void chunk_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 }
 
+// RMS norm of each output row (the gated delta rule's fused epilogue in fp32): one
+// wave per row, the sum of squares by shuffles.
+__global__ __launch_bounds__(256)
+void rms_rows_f32(float* __restrict__ o, const float* __restrict__ w, float eps, int64_t rows, int dv) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    float* r = o + row * dv;
+    float ss = 0.f;
+    for (int c = lane; c < dv; c += 64) ss += r[c] * r[c];
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.f / sqrtf(ss / static_cast<float>(dv) + eps);
+    for (int c = lane; c < dv; c += 64) r[c] = r[c] * w[c] * inv;
+}
+
 template <int VARIANT, int C, int DK>
 hipError_t launch_dk(const ChunkArgs& a, hipStream_t stream) {
     const float* q = static_cast<const float*>(a.q);
@@ -202,12 +234,17 @@ hipError_t launch_dk(const ChunkArgs& a, hipStream_t stream) {
     if (a.dv >= 32) {
         const dim3 grid(bh * (a.dv / 32));
         hipLaunchKernelGGL((chunk_f32_kernel<VARIANT, C, DK, 32>), grid, dim3(kThreads), 0, stream,
-                           q, k, v, a.gate, a.beta, a.s0, o, a.s_out, a.H, a.T, a.dv);
+                           q, k, v, a.gate, a.beta, a.s0, o, a.s_out, a.H, a.T, a.dv, a.fuse);
     } else {
         const dim3 grid(bh);
         hipLaunchKernelGGL((chunk_f32_kernel<VARIANT, C, DK, 16>), grid, dim3(kThreads), 0, stream,
-                           q, k, v, a.gate, a.beta, a.s0, o, a.s_out, a.H, a.T, a.dv);
+                           q, k, v, a.gate, a.beta, a.s0, o, a.s_out, a.H, a.T, a.dv, a.fuse);
     }
+    hipError_t err = hipGetLastError();
+    const int64_t rows = static_cast<int64_t>(bh) * a.T;
+    if (err != hipSuccess || !(a.fuse & 2) || rows == 0) return err;
+    hipLaunchKernelGGL(rms_rows_f32, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream, o, a.onw,
+                       a.oeps, rows, a.dv);
     return hipGetLastError();
 }
 

@@ -90,12 +90,14 @@ la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int d
                                   la_dtype dtype, size_t* bytes) {
     if (bytes == nullptr) return fail(LA_ERR_INVALID, "%s", "bytes is NULL");
     *bytes = 0;
-    if (variant != LA_RETENTION && variant != LA_GLA && variant != LA_GDELTA && variant != LA_MAMBA2)
+    if (variant != LA_RETENTION && variant != LA_GLA && variant != LA_GDELTA && variant != LA_MAMBA2 &&
+        variant != LA_GDELTA_FUSED)
         return fail(LA_ERR_INVALID, "%s", "unknown variant");
-    const glr::Variant v = static_cast<glr::Variant>(variant);
+    const glr::Variant v = variant == LA_GDELTA_FUSED ? glr::kGDelta : static_cast<glr::Variant>(variant);
     // shape checks only: pointers are not part of the query
     glr::ChunkArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     B, H, 0, dk, dv, chunk, nullptr};
+                     B, H, 0, dk, dv, chunk, nullptr, variant == LA_GDELTA_FUSED ? LA_FUSE_QK_SILU_L2 : 0,
+                     nullptr, 0.f};
     la_status st = check_chunk_args(v, a, dtype);
     if (st != LA_OK) return st;
     if (T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
@@ -136,6 +138,23 @@ la_status gdelta_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
     glr::ChunkArgs a{q, k, v, log_alpha, beta, s0, o, s_out, B, H, T, dk, dv, chunk, workspace};
+    return run_chunk(glr::kGDelta, a, dtype, workspace_bytes, stream);
+}
+
+la_status gdelta_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* beta, const float* s0, void* o, float* s_out,
+                                 const float* o_norm_weight, float o_norm_eps, int fuse,
+                                 int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (fuse & ~(LA_FUSE_QK_SILU_L2 | LA_FUSE_OUT_RMSNORM)) return fail(LA_ERR_INVALID, "%s", "unknown fuse flag");
+    if (fuse & LA_FUSE_OUT_RMSNORM) {
+        const bool rows = B > 0 && H > 0 && T > 0;
+        la_status st = check_ptr(o_norm_weight, rows, false, "o_norm_weight");
+        if (st != LA_OK) return st;
+        if (!(o_norm_eps >= 0.f)) return fail(LA_ERR_INVALID, "%s", "o_norm_eps must be >= 0");
+    }
+    glr::ChunkArgs a{q, k, v, log_alpha, beta, s0, o, s_out, B, H, T, dk, dv, chunk, workspace,
+                     fuse, o_norm_weight, o_norm_eps};
     return run_chunk(glr::kGDelta, a, dtype, workspace_bytes, stream);
 }
 
@@ -202,6 +221,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (2 << 16) | 2; }
+int la_version(void) { return (2 << 16) | 3; }
 
 }  // extern "C"

@@ -144,11 +144,14 @@ def _silu_l2(x):
     return y / np.linalg.norm(y, axis=-1, keepdims=True)
 
 
-def gdelta_inputs(B, H, T, dk, dv, *, chunk=64, dtype="bf16", seed=0, with_state=False):
-    """q, k = L2(SiLU(N(0,1))); v ~ N(0,1); beta = sigmoid(N(0,1)); log alpha = -softplus(N(0,1))/8."""
+def gdelta_inputs(B, H, T, dk, dv, *, chunk=64, dtype="bf16", seed=0, with_state=False, raw_qk=False):
+    """q, k = L2(SiLU(N(0,1))); v ~ N(0,1); beta = sigmoid(N(0,1)); log alpha = -softplus(N(0,1))/8.
+    With ``raw_qk`` q and k are the N(0,1) draws themselves (the projections before the feature
+    map, for the fused entry point), rounded to the storage type."""
     rng = np.random.default_rng(seed)
-    q = _store(_silu_l2(rng.standard_normal((B, H, T, dk))), dtype)
-    k = _store(_silu_l2(rng.standard_normal((B, H, T, dk))), dtype)
+    fmap = (lambda x: x) if raw_qk else _silu_l2
+    q = _store(fmap(rng.standard_normal((B, H, T, dk))), dtype)
+    k = _store(fmap(rng.standard_normal((B, H, T, dk))), dtype)
     v = _store(rng.standard_normal((B, H, T, dv)), dtype)
     beta = _sigmoid(rng.standard_normal((B, H, T))).astype(np.float32)
     log_alpha = (-_softplus(rng.standard_normal((B, H, T))) / 8.0).astype(np.float32)

@@ -72,11 +72,17 @@ typedef enum la_dtype {
     LA_BF16 = 1
 } la_dtype;
 
+typedef enum la_fuse {
+    LA_FUSE_QK_SILU_L2 = 1,    /* q, k are mapped by SiLU then unit L2 norm per token on load */
+    LA_FUSE_OUT_RMSNORM = 2    /* each output row is RMS-normalised and weighted */
+} la_fuse;
+
 typedef enum la_variant {
     LA_RETENTION = 0,   /* la_chunk_fwd */
     LA_GLA = 1,         /* gla_chunk_fwd */
     LA_GDELTA = 2,      /* gdelta_chunk_fwd */
-    LA_MAMBA2 = 3       /* mamba2_chunk_fwd */
+    LA_MAMBA2 = 3,      /* mamba2_chunk_fwd */
+    LA_GDELTA_FUSED = 4 /* gdelta_chunk_fwd_fused with LA_FUSE_QK_SILU_L2 */
 } la_variant;
 
 /*
@@ -91,7 +97,9 @@ typedef enum la_variant {
  * pseudo-values (d_v x chunk float32) and the cumulative log-gates (chunk
  * float32): with N = B * H * ceil(T / chunk) and a(x) = x rounded up to a
  * multiple of 256, a(N*chunk*d_k*2) + a(N*d_v*chunk*4) + a(N*chunk*4) +
- * a(N*d_v*d_k*2) bytes.  fp32 storage needs none.
+ * a(N*d_v*d_k*2) bytes; gdelta_chunk_fwd_fused with LA_FUSE_QK_SILU_L2
+ * (query with LA_GDELTA_FUSED) keeps the mapped keys there too, another
+ * a(N*chunk*d_k*2).  fp32 storage needs none.
  */
 la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int dk, int dv,
                                   int chunk, la_dtype dtype, size_t* bytes);
@@ -162,6 +170,33 @@ la_status gdelta_chunk_fwd(const void* q, const void* k, const void* v,
                            void* stream);
 
 /*
+ * gdelta_chunk_fwd with DeltaNet's feature map and output norm fused in
+ * ("Scrivere meglio nella memoria": the SiLU followed by L2 normalisation that
+ * DeltaNet puts on the projections producing k and q, introduction section
+ * "Superiore"; the RMS norm on the output that stabilises its readout).  `fuse`
+ * is a bitwise OR of la_fuse flags:
+ *  - LA_FUSE_QK_SILU_L2: q and k hold the projections before the map; every
+ *    token's q and k become silu(x) / ||silu(x)||_2 (a zero row stays zero), in
+ *    fp32, stored as bf16 before they enter the products (fp32 storage: kept
+ *    in fp32);
+ *  - LA_FUSE_OUT_RMSNORM: every output row o (d_v values) becomes
+ *    o / sqrt(mean(o^2) + o_norm_eps) * o_norm_weight, with o_norm_weight
+ *    [d_v] float32 (required with this flag) and o_norm_eps >= 0.
+ * s_out is the memory itself, not affected by the output norm.  fuse == 0 is
+ * gdelta_chunk_fwd.  With LA_FUSE_QK_SILU_L2 and bf16 storage the workspace
+ * also holds the mapped keys: its size comes from la_chunk_workspace_size with
+ * LA_GDELTA_FUSED.  Other arguments and errors as for gdelta_chunk_fwd; an
+ * unknown flag is LA_ERR_INVALID.
+ */
+la_status gdelta_chunk_fwd_fused(const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* beta,
+                                 const float* s0, void* o, float* s_out,
+                                 const float* o_norm_weight, float o_norm_eps, int fuse,
+                                 int B, int H, int T, int dk, int dv, int chunk,
+                                 la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * One decode token for N sequences x H heads with a per-key-channel gate (the
  * recurrent form of the RetNet page, section on retention: the same two
  * gestures for every token at constant memory; a fixed decay is the constant
@@ -199,7 +234,7 @@ const char* la_status_str(la_status status);
 const char* la_last_error(void);
 
 /* ABI version: (major << 16) | minor (2.0: workspace arguments; 2.1:
- * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step). */
+ * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step; 2.3: gdelta_chunk_fwd_fused). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 2
-    assert lib.la_version() & 0xffff >= 2      # 2.1: mamba2_chunk_fwd, 2.2: gdelta_recurrent_step
+    assert lib.la_version() & 0xffff >= 3      # 2.1 mamba2_chunk_fwd, 2.2 gdelta_recurrent_step, 2.3 fused
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -90,6 +90,10 @@ def test_workspace_size_query(lib):
         n = B * H * ((T + C - 1) // C)
         want = a256(n * C * dk * 2) + a256(n * dv * C * 4) + a256(n * C * 4) + a256(n * dv * dk * 2)
         assert _ws(lib, _native.LA_GDELTA, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C) == (_native.LA_OK, want)
+    # with the fused feature map the mapped keys are kept too
+    n = 4 * 16 * 128
+    want = a256(n * 64 * 128 * 2) * 2 + a256(n * 128 * 64 * 4) + a256(n * 64 * 4) + a256(n * 128 * 128 * 2)
+    assert _ws(lib, _native.LA_GDELTA_FUSED, B=4, H=16, T=8192, dk=128, dv=128, chunk=64) == (_native.LA_OK, want)
     assert _ws(lib, _native.LA_GDELTA, T=0) == (_native.LA_OK, 0)
     assert _ws(lib, _native.LA_GDELTA, dtype=0) == (_native.LA_OK, 0)
     assert _ws(lib, 7)[0] == _native.LA_ERR_INVALID
@@ -168,3 +172,24 @@ def test_gdelta_decode_validation(lib):
     assert call(dk=48) == _native.LA_ERR_UNSUPPORTED
     assert call(dtype=3) == _native.LA_ERR_INVALID
     assert call(N=0, q=None, k=None, v=None, alpha=None, beta=None, s=None, o=None) == _native.LA_OK
+
+
+def test_gdelta_fused_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(fuse, weight=FAKE, eps=1e-6, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, o=FAKE, B=1, H=1, T=8, dk=16, dv=16, chunk=16)
+        a.update(kw)
+        return lib.gdelta_chunk_fwd_fused(P(a["q"]), P(a["k"]), P(a["v"]), P(a["gate"]), P(a["beta"]), None,
+                                          P(a["o"]), None, P(weight), eps, fuse, a["B"], a["H"], a["T"], a["dk"],
+                                          a["dv"], a["chunk"], 1, P(FAKE), 1 << 30, None)
+
+    assert call(4) == _native.LA_ERR_INVALID
+    assert b"unknown fuse flag" in lib.la_last_error()
+    assert call(_native.LA_FUSE_OUT_RMSNORM, weight=None) == _native.LA_ERR_INVALID
+    assert b"o_norm_weight is NULL" in lib.la_last_error()
+    assert call(_native.LA_FUSE_OUT_RMSNORM, weight=MISALIGNED) == _native.LA_ERR_INVALID
+    assert call(_native.LA_FUSE_OUT_RMSNORM, eps=-1.0) == _native.LA_ERR_INVALID
+    assert call(_native.LA_FUSE_OUT_RMSNORM, eps=float("nan")) == _native.LA_ERR_INVALID
+    assert call(_native.LA_FUSE_QK_SILU_L2, q=None) == _native.LA_ERR_INVALID
+    assert call(3, B=0, q=None, k=None, v=None, o=None, gate=None, beta=None, weight=None) == _native.LA_OK
