@@ -37,5 +37,7 @@ from .glr_oracle import (  # noqa: F401
     gdelta_decode_step,
     silu_l2,
     rms_norm,
+    scalar_backward,
+    retention_backward,
     forward_substitution,
 )

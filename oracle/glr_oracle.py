@@ -57,6 +57,8 @@ __all__ = [
     "gdelta_decode_step",
     "silu_l2",
     "rms_norm",
+    "scalar_backward",
+    "retention_backward",
     "forward_substitution",
 ]
 
@@ -485,3 +487,45 @@ def rms_norm(o, weight, eps):
     o = np.asarray(o, dtype=np.float64)
     w = np.asarray(weight, dtype=np.float64)
     return o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps) * w
+
+
+# --------------------------------------------------------------------------- backward (reverse mode)
+
+def scalar_backward(q, k, v, log_alpha, do, dS_T=None, s0=None):
+    """Gradients of the scalar-decay recurrence by reverse-mode differentiation of its
+    recurrent form (the definition: "Dimenticare: i gate", scalar decay equation), token by
+    token. With D_t the gradient of the loss with respect to S_t:
+    ``D_{T-1} = dS_T + do_{T-1} q_{T-1}^T``, ``D_t = a_{t+1} D_{t+1} + do_t q_t^T``, and
+    ``dq_t = S_t^T do_t``, ``dk_t = D_t^T v_t``, ``dv_t = D_t k_t``,
+    ``d log a_t = a_t <D_t, S_{t-1}>`` (Frobenius), ``dS_0 = a_0 D_0``.
+    Returns ``(dq, dk, dv, dlog_alpha, ds0)``; ``do`` is ``[B, H, T, d_v]``."""
+    q, k, v, la, do = _f64(q, k, v, log_alpha, do)
+    S0 = _init_state(q, v, s0)
+    T = q.shape[-2]
+    a = np.exp(la)
+    states = [S0]
+    S = S0
+    for t in range(T):
+        S = a[..., t][..., None, None] * S + _outer(v[..., t, :], k[..., t, :])
+        states.append(S)
+    D = np.zeros_like(S0) if dS_T is None else np.asarray(dS_T, dtype=np.float64).copy()
+    dq = np.zeros(q.shape); dk = np.zeros(k.shape); dv = np.zeros(v.shape); dla = np.zeros(la.shape)
+    for t in range(T - 1, -1, -1):
+        D = D + _outer(do[..., t, :], q[..., t, :])                 # now the gradient w.r.t. S_t
+        dq[..., t, :] = np.einsum("...mc,...m->...c", states[t + 1], do[..., t, :])
+        dk[..., t, :] = np.einsum("...mc,...m->...c", D, v[..., t, :])
+        dv[..., t, :] = np.einsum("...mc,...c->...m", D, k[..., t, :])
+        dla[..., t] = a[..., t] * np.einsum("...mc,...mc->...", D, states[t])
+        D = a[..., t][..., None, None] * D                            # through S_t = a_t S_{t-1} + ...
+    return dq, dk, dv, dla, D
+
+
+def retention_backward(q, k, v, log_gamma, do, dS_T=None, s0=None):
+    """Retention is the scalar decay with the same gate at every step of head h, so its
+    gradients are scalar_backward's, with the gate gradient summed over the batch and the
+    tokens of each head. Returns ``(dq, dk, dv, dlog_gamma [H], ds0)``."""
+    q = np.asarray(q)
+    B, H, T = q.shape[:3]
+    la = np.broadcast_to(np.asarray(log_gamma, dtype=np.float64)[None, :, None], (B, H, T))
+    dq, dk, dv, dla, ds0 = scalar_backward(q, k, v, la, do, dS_T=dS_T, s0=s0)
+    return dq, dk, dv, dla.sum(axis=(0, 2)), ds0

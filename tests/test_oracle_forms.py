@@ -292,3 +292,57 @@ def test_resume_from_handed_over_state(split):
         o_b, S_b = run(slice(split, 40), S_a)
         np.testing.assert_allclose(np.concatenate([o_a, o_b], axis=-2), o_full, atol=1e-12, err_msg=name)
         np.testing.assert_allclose(S_b, S_full, atol=1e-12, err_msg=name)
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _loss(o, S, W_o, W_s):
+    """A fixed random linear functional of the outputs and the final memory: its gradients
+    with respect to o and S_T are W_o and W_s."""
+    return np.sum(o * W_o) + np.sum(S * W_s)
+
+
+@pytest.mark.parametrize("kind", ["scalar", "retention"])
+def test_backward_matches_finite_differences(kind):
+    """Central differences of L = <W_o, o> + <W_s, S_T> through the recurrent form, against
+    the reverse-mode gradients, for every input element (tiny sizes, fp64)."""
+    rng = np.random.default_rng(40)
+    B, H, T, dk, dv = 1, 2, 5, 3, 2
+    q = rng.standard_normal((B, H, T, dk)); k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv)); s0 = rng.standard_normal((B, H, dv, dk))
+    W_o = rng.standard_normal((B, H, T, dv)); W_s = rng.standard_normal((B, H, dv, dk))
+    if kind == "scalar":
+        gate = -np.logaddexp(0.0, -rng.standard_normal((B, H, T)))
+        fwd = lambda q, k, v, g, s: orc.scalar_recurrent(q, k, v, g, s0=s)
+        grads = orc.scalar_backward(q, k, v, gate, W_o, dS_T=W_s, s0=s0)
+    else:
+        gate = np.log(rng.uniform(0.5, 0.95, H))
+        fwd = lambda q, k, v, g, s: orc.retention_recurrent(q, k, v, g, s0=s)
+        grads = orc.retention_backward(q, k, v, gate, W_o, dS_T=W_s, s0=s0)
+    args = [q, k, v, gate, s0]
+    eps = 1e-6
+    for which, g in zip(range(5), grads):
+        x = args[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            plus = [a.copy() for a in args]; minus = [a.copy() for a in args]
+            plus[which][idx] += eps; minus[which][idx] -= eps
+            num[idx] = (_loss(*fwd(*plus), W_o, W_s) - _loss(*fwd(*minus), W_o, W_s)) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-7, rtol=1e-6, err_msg=f"{kind} input {which}")
+
+
+def test_gate_gradient_identity():
+    """The gate gradient from the rescaling argument: every term of o_t carries e^(B_t) and
+    every term written at j carries e^(-B_j), so dL/dB_t = q_t . dq_t - k_t . dk_t (plus
+    <dS_T, S_T> at the last token), and d log a_r = sum_{t >= r} dL/dB_t."""
+    rng = np.random.default_rng(41)
+    B, H, T, dk, dv = 2, 2, 9, 4, 3
+    q = rng.standard_normal((B, H, T, dk)); k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv)); s0 = rng.standard_normal((B, H, dv, dk))
+    la = -np.logaddexp(0.0, -rng.standard_normal((B, H, T)))
+    do = rng.standard_normal((B, H, T, dv)); dS = rng.standard_normal((B, H, dv, dk))
+    dq, dk_, dv_, dla, _ = orc.scalar_backward(q, k, v, la, do, dS_T=dS, s0=s0)
+    _, S_T = orc.scalar_recurrent(q, k, v, la, s0=s0)
+    per_t = np.sum(q * dq, axis=-1) - np.sum(k * dk_, axis=-1)
+    want = np.flip(np.cumsum(np.flip(per_t, -1), -1), -1) + np.sum(dS * S_T, axis=(-2, -1))[..., None]
+    np.testing.assert_allclose(dla, want, atol=1e-10)
