@@ -7,7 +7,8 @@ The computation lives in the HIP library ``libglr.so`` (C ABI in ``include/glr.h
 """
 
 from .api import (la_chunk_fwd, mamba2_chunk_fwd, gla_chunk_fwd, gdelta_chunk_fwd,  # noqa: F401
-                  gdelta_chunk_fwd_fused, la_recurrent_step, gdelta_recurrent_step, workspace_size)
+                  gdelta_chunk_fwd_fused, la_chunk_bwd, mamba2_chunk_bwd, la_recurrent_step,
+                  gdelta_recurrent_step, workspace_size)
 
 __all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-           "la_recurrent_step", "gdelta_recurrent_step", "workspace_size"]
+           "la_chunk_bwd", "mamba2_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step", "workspace_size"]

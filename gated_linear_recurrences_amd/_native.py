@@ -23,6 +23,9 @@ EXPORTED = (
     "gdelta_chunk_fwd_fused",
     "la_recurrent_step",
     "gdelta_recurrent_step",
+    "la_chunk_bwd_workspace_size",
+    "la_chunk_bwd",
+    "mamba2_chunk_bwd",
     "la_status_str",
     "la_last_error",
     "la_version",
@@ -61,8 +64,13 @@ def load():
     lib.la_chunk_workspace_size.restype = ctypes.c_int
     lib.la_recurrent_step.argtypes = [P, P, P, F, F, P, I, I, I, I, I, P]
     lib.gdelta_recurrent_step.argtypes = [P, P, P, F, F, F, P, I, I, I, I, I, P]
+    bwd = [P, P, P, F, F, P, F, P, P, P, F, F, I, I, I, I, I, I, I, P, Z, P]
+    lib.la_chunk_bwd.argtypes = bwd
+    lib.mamba2_chunk_bwd.argtypes = bwd
+    lib.la_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.la_chunk_bwd_workspace_size.restype = ctypes.c_int
     for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-                 "la_recurrent_step", "gdelta_recurrent_step"):
+                 "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
     lib.la_status_str.restype = ctypes.c_char_p
@@ -89,3 +97,11 @@ def check(status):
         msg = lib.la_status_str(status).decode()
         detail = lib.la_last_error().decode()
         raise GLRError(status, f"{msg}: {detail}")
+
+
+def bwd_workspace_size(B, H, T, dk, dv, chunk, dtype):
+    """Bytes of device workspace the backward entry points need for these sizes."""
+    lib = load()
+    out = ctypes.c_size_t(0)
+    check(lib.la_chunk_bwd_workspace_size(B, H, T, dk, dv, chunk, dtype, ctypes.byref(out)))
+    return out.value

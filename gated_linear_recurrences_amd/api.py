@@ -13,7 +13,7 @@ import torch
 from . import _native
 
 __all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-           "la_recurrent_step", "gdelta_recurrent_step", "workspace_size"]
+           "la_chunk_bwd", "mamba2_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step", "workspace_size"]
 
 
 def _dtype_code(t):
@@ -231,3 +231,38 @@ def gdelta_recurrent_step(q, k, v, alpha, beta, s, o=None):
     _native.check(lib.gdelta_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(s), _ptr(o),
                                             N, H, dk, dv, _dtype_code(q), _stream(dev)))
     return o
+
+
+def _chunk_bwd(fn, q, k, v, gate, gate_shape, dout, s0, ds_out, chunk, want_ds0, workspace):
+    dims, _, _ = _chunk_common(q, k, v, s0, dout, None, False)
+    B, H, T, dk, dv = dims
+    dev = q.device
+    _require(gate, "gate", gate_shape, torch.float32, dev)
+    if ds_out is not None:
+        _require(ds_out, "ds_out", (B, H, dv, dk), torch.float32, dev)
+    dq, dk_ = torch.empty_like(q), torch.empty_like(k)
+    dv_ = torch.empty_like(v)
+    dgate = torch.empty(gate_shape, dtype=torch.float32, device=dev)
+    ds0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_ds0 else None
+    need = _native.bwd_workspace_size(B, H, T, dk, dv, chunk, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    _native.check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(s0), _ptr(dout), _ptr(ds_out), _ptr(dq), _ptr(dk_),
+                     _ptr(dv_), _ptr(dgate), _ptr(ds0), B, H, T, dk, dv, chunk, _dtype_code(q), _ptr(workspace),
+                     workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk_, dv_, dgate, ds0
+
+
+def la_chunk_bwd(q, k, v, log_gamma, dout, s0=None, ds_out=None, chunk=64, want_ds0=True, workspace=None):
+    """Gradients of la_chunk_fwd (bf16): given dout = dL/do and optionally ds_out = dL/dS_T, returns
+    (dq, dk, dv, dlog_gamma [H], ds0 or None)."""
+    return _chunk_bwd(_native.load().la_chunk_bwd, q, k, v, log_gamma, (q.shape[1],), dout, s0, ds_out, chunk,
+                      want_ds0, workspace)
+
+
+def mamba2_chunk_bwd(q, k, v, log_alpha, dout, s0=None, ds_out=None, chunk=64, want_ds0=True, workspace=None):
+    """Gradients of mamba2_chunk_fwd (bf16): returns (dq, dk, dv, dlog_alpha [B,H,T], ds0 or None)."""
+    return _chunk_bwd(_native.load().mamba2_chunk_bwd, q, k, v, log_alpha, tuple(q.shape[:3]), dout, s0, ds_out,
+                      chunk, want_ds0, workspace)

@@ -1,0 +1,480 @@
+// Backward of the chunked forward for the fixed (retention) and scalar data-dependent
+// decays, bf16 storage.
+//
+// Method: reverse-mode differentiation of the recurrence S_t = a_t S_{t-1} + v_t k_t^T,
+// o_t = S_t q_t ("Scrivere meglio nella memoria", section "Dimenticare: i gate", scalar
+// decay), organised like the chunkwise forward of the RetNet page (section "RetNet: la
+// retention e le sue tre forme"): per chunk a decayed triangle, between chunks a carried
+// d_v x d_k matrix. With chunk-local inclusive cumulative log-gates G, M_ij = e^(G_i - G_j)
+// for j <= i (else 0), S_in the memory entering the chunk and R the gradient of the loss
+// with respect to the memory at the chunk's last token:
+//   dq_i = sum_{j<=i} M_ij (do_i . v_j) k_j + e^(G_i) S_in^T do_i
+//   dk_j = sum_{i>=j} M_ij (do_i . v_j) q_i + e^(G_last - G_j) R^T v_j
+//   dv_j = sum_{i>=j} M_ij (q_i . k_j) do_i + e^(G_last - G_j) R k_j
+// and, since every term of o_t carries e^(B_t) and every write of token j carries
+// e^(-B_j) (B the cumulative log-gate over the sequence), the gate's gradient is
+//   d log a_t = sum_{s >= t} (q_s . dq_s - k_s . dk_s) + <dS_T, S_T>.
+// The call runs four kernels: the forward state pass (snapshots S_in, final memory),
+// the same pass walked backwards on (q, dO) (snapshots R, gradient of S_0), the
+// gradient pass below (chunk-parallel), and the gate pass.
+//
+// Gradient pass (gfx950): one workgroup of eight waves per (sequence, chunk). q, k, v,
+// dO are staged token-major; A1 = (Q K^T) . M and A2 = (dO V^T) . M are formed on MFMA
+// into LDS (bf16, all C/16 x C/16 tiles, the upper ones zero). Every product is computed
+// transposed - feature rows, token columns - so that a lane ends with four consecutive
+// features of one token (one 8-byte store):
+//   dV^T = dO^T A1 + R K^T diag(w)      dK^T = Q^T A2 + R^T V^T diag(w)
+//   dQ^T = K^T A2^T + S_in^T dO^T diag(e^G),     w_j = e^(G_last - G_j),
+// with the operands read transposed (ds_read_b64_tr_b16) or by rows as each needs.
+// R and then S_in take turns in one LDS region. The per-token sums q.dq and k.dk meet
+// in LDS: per feature tile a partial (reduced over the lane group), added in tile order
+// (no atomics: the gradients are bit-for-bit repeatable).
+#pragma once
+
+#include "chunk_common.hpp"
+#include "chunk_two_pass.hpp"
+
+namespace glr {
+namespace ck {
+
+struct GradParams {
+    const u16* q;          // [BH][T][DK]
+    const u16* k;          // [BH][T][DK]
+    const u16* v;          // [BH][T][DV]
+    const u16* dout;       // [BH][T][DV]
+    const float* gate;     // fixed: log gamma [H]; scalar: log alpha [BH][T]
+    const u16* s_in;       // [BH][NC][DV][DK] forward snapshots
+    const u16* r;          // [BH][NC][DV][DK] backward snapshots
+    u16* dq;               // [BH][T][DK]
+    u16* dk;               // [BH][T][DK]
+    u16* dv;               // [BH][T][DV]
+    float* gq;             // [BH][T]: q.dq - k.dk per token
+    int H, T, NC;
+};
+
+template <int C, int DK, int DV>
+struct GradLayout {
+    static constexpr int QS = tile_stride(DK), VS = tile_stride(DV), AS = tile_stride(C), XS = tile_stride(DK);
+    static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    static constexpr int oQ = 0;
+    static constexpr int oK = oQ + al(C * QS * 2);
+    static constexpr int oV = oK + al(C * QS * 2);
+    static constexpr int oO = oV + al(C * VS * 2);
+    static constexpr int oA1 = oO + al(C * VS * 2);
+    static constexpr int oA2 = oA1 + al(C * AS * 2);
+    static constexpr int oX = oA2 + al(C * AS * 2);     // R, then S_in ([DV][DK])
+    static constexpr int oG = oX + al(DV * XS * 2);
+    static constexpr int oQD = oG + al(C * 4);              // [DK / 16][C] partial q . dq
+    static constexpr int oKD = oQD + al(DK / 16 * C * 4);   // [DK / 16][C] partial k . dk
+    static constexpr int bytes = oKD + al(DK / 16 * C * 4);
+    static_assert(bytes <= 160 * 1024, "LDS budget of the gradient pass exceeded");
+};
+
+template <int C, int DK, int DV, int GK>
+__global__ __launch_bounds__(512)
+void grad_kernel(GradParams p) {
+    using Lay = GradLayout<C, DK, DV>;
+    constexpr int NT = 512, NW = 8;
+    constexpr int CT = C / 16, JB = (CT + 1) / 2;
+    constexpr int QS = Lay::QS, VS = Lay::VS, AS = Lay::AS, XS = Lay::XS;
+    constexpr int KB = (DK + 31) / 32, VB = (DV + 31) / 32;
+    constexpr int QP = C * DK / 8, QP_PER = (QP + NT - 1) / NT;
+    constexpr int VP = C * DV / 8, VP_PER = (VP + NT - 1) / NT;
+    constexpr int XP = DV * DK / 8, XP_PER = (XP + NT - 1) / NT;
+    constexpr int FK = DK / 16, FV = DV / 16;
+    static_assert(GK == kGateFixed || GK == kGateScalar, "fixed or scalar gates");
+
+    __shared__ __align__(16) unsigned char smem[Lay::bytes];
+    u16* const sQ = reinterpret_cast<u16*>(smem + Lay::oQ);
+    u16* const sK = reinterpret_cast<u16*>(smem + Lay::oK);
+    u16* const sV = reinterpret_cast<u16*>(smem + Lay::oV);
+    u16* const sO = reinterpret_cast<u16*>(smem + Lay::oO);
+    u16* const sA1 = reinterpret_cast<u16*>(smem + Lay::oA1);
+    u16* const sA2 = reinterpret_cast<u16*>(smem + Lay::oA2);
+    u16* const sX = reinterpret_cast<u16*>(smem + Lay::oX);
+    float* const sG = reinterpret_cast<float*>(smem + Lay::oG);
+    float* const sQD = reinterpret_cast<float*>(smem + Lay::oQD);
+    float* const sKD = reinterpret_cast<float*>(smem + Lay::oKD);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
+    const int T = p.T;
+    const int t0 = c * C, n = (T - t0 < C) ? (T - t0) : C;
+    const int64_t tok0 = static_cast<int64_t>(bh) * T + t0;
+    const int64_t chunk = static_cast<int64_t>(bh) * p.NC + c;
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    // ---- loads up front (rows past the end read row 0, zeroed on staging)
+    u16x8 rq[QP_PER], rk[QP_PER], rv[VP_PER], ro[VP_PER], rx[XP_PER], rs[XP_PER];
+#pragma unroll
+    for (int i = 0; i < QP_PER; ++i) {
+        const int idx = tid + i * NT;
+        const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+        const unsigned off = (idx < QP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
+        rq[i] = *reinterpret_cast<const u16x8*>(p.q + tok0 * DK + off);
+        rk[i] = *reinterpret_cast<const u16x8*>(p.k + tok0 * DK + off);
+    }
+#pragma unroll
+    for (int i = 0; i < VP_PER; ++i) {
+        const int idx = tid + i * NT;
+        const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+        const unsigned off = (idx < VP && j < n) ? static_cast<unsigned>(j * DV + col) : 0u;
+        rv[i] = *reinterpret_cast<const u16x8*>(p.v + tok0 * DV + off);
+        ro[i] = *reinterpret_cast<const u16x8*>(p.dout + tok0 * DV + off);
+    }
+#pragma unroll
+    for (int i = 0; i < XP_PER; ++i) {
+        const int idx = tid + i * NT;
+        const unsigned off = (idx < XP) ? static_cast<unsigned>(idx * 8) : 0u;
+        rx[i] = *reinterpret_cast<const u16x8*>(p.r + chunk * DV * DK + off);
+        rs[i] = *reinterpret_cast<const u16x8*>(p.s_in + chunk * DV * DK + off);
+    }
+    float rgate = 0.f;
+    if constexpr (GK == kGateScalar) rgate = (tid < n) ? p.gate[tok0 + tid] : 0.f;
+
+    // ---- stage q, k, v, dO, R; cumulative gates (log2 units); zero the per-token sums
+#pragma unroll
+    for (int i = 0; i < QP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < QP) {
+            const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<u16x8*>(sQ + j * QS + col) = (j < n) ? rq[i] : z8;
+            *reinterpret_cast<u16x8*>(sK + j * QS + col) = (j < n) ? rk[i] : z8;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VP_PER; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < VP) {
+            const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+            *reinterpret_cast<u16x8*>(sV + j * VS + col) = (j < n) ? rv[i] : z8;
+            *reinterpret_cast<u16x8*>(sO + j * VS + col) = (j < n) ? ro[i] : z8;
+        }
+    }
+    auto stage_x = [&](const u16x8* src) {
+#pragma unroll
+        for (int i = 0; i < XP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < XP) {
+                const int m = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+                *reinterpret_cast<u16x8*>(sX + m * XS + col) = src[i];
+            }
+        }
+    };
+    stage_x(rx);
+    if (w == 0) {
+        float x;
+        if constexpr (GK == kGateScalar) {
+            x = wave_inclusive_scan(rgate * kLog2e);   // padded tokens add 0
+        } else {
+            const float lg2 = p.gate[bh % p.H] * kLog2e;
+            x = static_cast<float>((lane < n ? lane : n - 1) + 1) * lg2;   // flat past the end
+        }
+        if (lane < C) sG[lane] = x;
+    }
+    lds_barrier();
+    const float glast = sG[C - 1];
+
+    // ---- A1 = (Q K^T) . M and A2 = (dO V^T) . M, every tile (upper ones zero):
+    // acc[r] = X[i = 16it + r16][j = 16jt + 4g + r]
+    for (int t = w; t < 2 * CT * CT; t += NW) {
+        const bool second = t >= CT * CT;
+        const int it = (t % (CT * CT)) / CT, jt = t % CT;
+        const int i = 16 * it + r16;
+        u16* const dst = second ? sA2 : sA1;
+        bf16x4 pv = zero4();
+        if (jt <= it) {
+            f32x4 acc = zf4();
+            const u16* arow = second ? sV + (16 * jt + r16) * VS : sK + (16 * jt + r16) * QS;
+            const u16* brow = second ? sO + i * VS : sQ + i * QS;
+            const int D = second ? DV : DK;
+#pragma unroll
+            for (int kb = 0; kb < (KB > VB ? KB : VB); ++kb) {
+                const int col = 32 * kb + 8 * g;
+                bf16x8 a8 = as_bf16x8(z8), b8 = as_bf16x8(z8);
+                if (col < D) {
+                    a8 = *reinterpret_cast<const bf16x8*>(arow + col);
+                    b8 = *reinterpret_cast<const bf16x8*>(brow + col);
+                }
+                acc = mfma_16x16x32(a8, b8, acc);
+            }
+            const float gi = sG[i];
+            const f32x4 gj = ldf4(sG + 16 * jt + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * jt + 4 * g + r;
+                pv[r] = static_cast<__bf16>((j <= i) ? acc[r] * ex2(gi - gj[r]) : 0.f);
+            }
+        }
+        st4(dst + i * AS + 16 * jt + 4 * g, pv);
+    }
+    lds_barrier();
+
+    // transposed operand over 32 tokens (rows 32b .. 32b + 31) of a token-major array
+    // X with row stride RS, column tile n0; the second half zero unless `hi`
+    auto wq_of = [&](int j) { return ex2(glast - sG[j]); };
+
+    // ---- dV^T and dK^T tiles: (feature tile, token tile jt); lane holds
+    // D[f = 16 ft + 4g + r][j = 16 jt + r16]
+    for (int t = w; t < (FV + FK) * CT; t += NW) {
+        const bool isv = t < FV * CT;
+        const int ft = (isv ? t : t - FV * CT) / CT, jt = (isv ? t : t - FV * CT) % CT;
+        const int j = 16 * jt + r16;
+        f32x4 acc = zf4(), acc2 = zf4();
+        // term 1: sum over i >= j of X^T[f][i] A[i][j] (A1 with dO for dV, A2 with Q for dK)
+#pragma unroll
+        for (int b = 0; b < JB; ++b) {
+            if (32 * b + 31 < 16 * jt) continue;                 // rows i all above j
+            const bool hi = 2 * b + 1 < CT;
+            const bf16x8 xa = isv ? tr_split<VS>(sO, b, 16 * ft, hi, r16, g) : tr_split<QS>(sQ, b, 16 * ft, hi, r16, g);
+            const bf16x8 ab = isv ? tr_split<AS>(sA1, b, 16 * jt, hi, r16, g) : tr_split<AS>(sA2, b, 16 * jt, hi, r16, g);
+            acc = mfma_16x16x32(xa, ab, acc);
+        }
+        if (isv) {
+            // term 2: sum over keys m of R[f][m] K[j][m] (rows of R and of K, natural order)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int col = 32 * kb + 8 * g;
+                bf16x8 xa = as_bf16x8(z8), kb8 = as_bf16x8(z8);
+                if (col < DK) {
+                    xa = *reinterpret_cast<const bf16x8*>(sX + (16 * ft + r16) * XS + col);
+                    kb8 = *reinterpret_cast<const bf16x8*>(sK + j * QS + col);
+                }
+                acc2 = mfma_16x16x32(xa, kb8, acc2);
+            }
+        } else {
+            // term 2: sum over values m of R[m][f] V[j][m] (R read transposed, rows of V split
+            // like the transposed operand)
+#pragma unroll
+            for (int b = 0; b < VB; ++b) {
+                const bool hi = 32 * b + 16 < DV;
+                const bf16x8 xa = tr_split<XS>(sX, b, 16 * ft, hi, r16, g);
+                const u16* vrow = sV + j * VS + 32 * b + 4 * g;
+                const bf16x8 vb = join8(ld4(vrow), hi ? ld4(vrow + 16) : zero4());
+                acc2 = mfma_16x16x32(xa, vb, acc2);
+            }
+        }
+        const float wj = wq_of(j);
+        acc = acc + acc2 * wj;
+        if (!isv) {
+            // k_j . dk_j over this tile's features: the lane's four, then the lane group
+            const f32x4 kj = up4(ld4(sK + j * QS + 16 * ft + 4 * g));
+            float part = kj[0] * acc[0] + kj[1] * acc[1] + kj[2] * acc[2] + kj[3] * acc[3];
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (g == 0) sKD[ft * C + j] = part;
+        }
+        if (j < n) {
+            if (isv) st4(p.dv + (tok0 + j) * DV + 16 * ft + 4 * g, cvt4(acc));
+            else st4(p.dk + (tok0 + j) * DK + 16 * ft + 4 * g, cvt4(acc));
+        }
+    }
+    lds_barrier();   // R is dead: the region takes S_in
+    stage_x(rs);
+    lds_barrier();
+
+    // ---- dQ^T tiles: (key tile ft, token tile it); lane holds dQ[i = 16it + r16][f = 16ft + 4g + r]
+    for (int t = w; t < FK * CT; t += NW) {
+        const int ft = t / CT, it = t % CT;
+        const int i = 16 * it + r16;
+        f32x4 acc = zf4(), acc2 = zf4();
+        // term 1: sum over j <= i of K[j][f] A2[i][j] (K transposed, rows of A2 split)
+#pragma unroll
+        for (int b = 0; b < JB; ++b) {
+            if (32 * b > 16 * it + 15) continue;                 // columns j all past i
+            const bool hi = 2 * b + 1 < CT;
+            const bf16x8 ka = tr_split<QS>(sK, b, 16 * ft, hi, r16, g);
+            const u16* arow = sA2 + i * AS + 32 * b + 4 * g;
+            acc = mfma_16x16x32(ka, join8(ld4(arow), hi ? ld4(arow + 16) : zero4()), acc);
+        }
+        // term 2: sum over values m of S_in[m][f] dO[i][m], scaled by e^(G_i)
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+            const bool hi = 32 * b + 16 < DV;
+            const bf16x8 xa = tr_split<XS>(sX, b, 16 * ft, hi, r16, g);
+            const u16* orow = sO + i * VS + 32 * b + 4 * g;
+            acc2 = mfma_16x16x32(xa, join8(ld4(orow), hi ? ld4(orow + 16) : zero4()), acc2);
+        }
+        acc = acc + acc2 * ex2(sG[i]);
+        const f32x4 qi = up4(ld4(sQ + i * QS + 16 * ft + 4 * g));
+        float part = qi[0] * acc[0] + qi[1] * acc[1] + qi[2] * acc[2] + qi[3] * acc[3];
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        if (g == 0) sQD[ft * C + i] = part;
+        if (i < n) st4(p.dq + (tok0 + i) * DK + 16 * ft + 4 * g, cvt4(acc));
+    }
+    lds_barrier();
+    if (tid < n) {
+        float qd = 0.f, kd = 0.f;
+#pragma unroll
+        for (int f = 0; f < FK; ++f) {
+            qd += sQD[f * C + tid];
+            kd += sKD[f * C + tid];
+        }
+        p.gq[tok0 + tid] = qd - kd;
+    }
+}
+
+// Gate gradients from the per-token sums: scalar gates d log a_t = sum_{s>=t} gq_s + <dS_T, S_T>
+// per sequence (one workgroup each); a fixed gate the sum of those over the tokens and the
+// batch of its head, sum_b [sum_s (s + 1) gq_s + T <dS_T, S_T>] (one workgroup per head).
+template <bool SCALAR>
+__global__ __launch_bounds__(256)
+void gate_grad_kernel(const float* __restrict__ gq, const float* __restrict__ ds_out, const float* __restrict__ s_fin,
+                      float* __restrict__ dgate, int B, int H, int T, int dsz) {
+    __shared__ float red[256];
+    __shared__ float carry_in[256];
+    const int tid = threadIdx.x;
+    auto block_sum = [&](float x) {
+        red[tid] = x;
+        __syncthreads();
+        for (int s = 128; s > 0; s >>= 1) {
+            if (tid < s) red[tid] += red[tid + s];
+            __syncthreads();
+        }
+        const float r = red[0];
+        __syncthreads();
+        return r;
+    };
+    auto final_dot = [&](int64_t bh) {
+        if (ds_out == nullptr) return 0.f;
+        float x = 0.f;
+        for (int e = tid; e < dsz; e += 256) x += ds_out[bh * dsz + e] * s_fin[bh * dsz + e];
+        return block_sum(x);
+    };
+    if constexpr (SCALAR) {
+        const int64_t bh = blockIdx.x;
+        const float fin = final_dot(bh);
+        // reverse cumulative sum over T: thread tid owns a contiguous run of tokens
+        const int per = (T + 255) / 256;
+        const int lo = tid * per, hi = (lo + per < T) ? lo + per : T;
+        float run = 0.f;
+        for (int t = lo; t < hi; ++t) run += gq[bh * T + t];
+        carry_in[tid] = run;
+        __syncthreads();
+        float after = 0.f;   // sum of the runs of the threads after this one
+        for (int u = tid + 1; u < 256; ++u) after += carry_in[u];
+        float acc = after + fin;
+        for (int t = hi - 1; t >= lo; --t) {
+            acc += gq[bh * T + t];
+            dgate[bh * T + t] = acc;
+        }
+    } else {
+        const int h = blockIdx.x;
+        float tot = 0.f;
+        for (int b = 0; b < B; ++b) {
+            const int64_t bh = static_cast<int64_t>(b) * H + h;
+            float x = 0.f;
+            for (int t = tid; t < T; t += 256) x += static_cast<float>(t + 1) * gq[bh * T + t];
+            tot += block_sum(x) + static_cast<float>(T) * final_dot(bh);
+        }
+        if (tid == 0) dgate[h] = tot;
+    }
+}
+
+// ====================================================================== launch
+// Workspace of a backward call: the forward and the backward snapshots
+// ([BH][NC][DV][DK] bf16 each), the final memory [BH][DV][DK] fp32 and the per-token
+// sums [BH][T] fp32, each from a 256-byte boundary.
+inline size_t bwd_align(size_t x) { return (x + 255) / 256 * 256; }
+inline size_t bwd_workspace_bytes(int64_t heads, int T, int chunk, int dk, int dv) {
+    const int64_t nc = (T + chunk - 1) / chunk;
+    return 2 * bwd_align(heads * nc * dv * dk * 2) + bwd_align(heads * dv * dk * 4) + bwd_align(heads * T * 4);
+}
+
+template <int C, int DK, int DV, int GK>
+hipError_t launch_backward_dv(const BwdArgs& a, hipStream_t stream) {
+    const int NC = (a.T + C - 1) / C;
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    unsigned char* base = static_cast<unsigned char*>(a.ws);
+    u16* fwd = reinterpret_cast<u16*>(base);
+    u16* rev = reinterpret_cast<u16*>(base + bwd_align(heads * NC * DV * DK * 2));
+    float* sfin = reinterpret_cast<float*>(base + 2 * bwd_align(heads * NC * DV * DK * 2));
+    float* gq = reinterpret_cast<float*>(base + 2 * bwd_align(heads * NC * DV * DK * 2) + bwd_align(heads * DV * DK * 4));
+    // forward state pass (snapshots and final memory), then the same walk backwards on (q, dO)
+    ChunkArgs f{a.q, a.k, a.v, a.gate, nullptr, a.s0, nullptr, sfin, a.B, a.H, a.T, DK, DV, C, fwd};
+    ChunkArgs r{a.q, a.q, a.dout, a.gate, nullptr, a.ds_out, nullptr, a.ds0, a.B, a.H, a.T, DK, DV, C, rev};
+    hipError_t err = hipErrorInvalidValue;
+    switch (state_value_tiles(heads, DV, DK)) {
+        case 8:
+            if constexpr (DV >= 128) {
+                err = launch_state<C, DK, 8, GK>(f, NC, stream);
+                if (err == hipSuccess) err = launch_state<C, DK, 8, GK, true>(r, NC, stream);
+            }
+            break;
+        case 4:
+            if constexpr (DV >= 64) {
+                err = launch_state<C, DK, 4, GK>(f, NC, stream);
+                if (err == hipSuccess) err = launch_state<C, DK, 4, GK, true>(r, NC, stream);
+            }
+            break;
+        case 2:
+            if constexpr (DV >= 32) {
+                err = launch_state<C, DK, 2, GK>(f, NC, stream);
+                if (err == hipSuccess) err = launch_state<C, DK, 2, GK, true>(r, NC, stream);
+            }
+            break;
+        default:
+            err = launch_state<C, DK, 1, GK>(f, NC, stream);
+            if (err == hipSuccess) err = launch_state<C, DK, 1, GK, true>(r, NC, stream);
+            break;
+    }
+    if (err != hipSuccess) return err;
+    if (NC > 0) {
+        GradParams p;
+        p.q = static_cast<const u16*>(a.q);
+        p.k = static_cast<const u16*>(a.k);
+        p.v = static_cast<const u16*>(a.v);
+        p.dout = static_cast<const u16*>(a.dout);
+        p.gate = a.gate;
+        p.s_in = fwd;
+        p.r = rev;
+        p.dq = static_cast<u16*>(a.grad_q);
+        p.dk = static_cast<u16*>(a.grad_k);
+        p.dv = static_cast<u16*>(a.grad_v);
+        p.gq = gq;
+        p.H = a.H;
+        p.T = a.T;
+        p.NC = NC;
+        hipLaunchKernelGGL((grad_kernel<C, DK, DV, GK>), dim3(static_cast<unsigned>(heads * NC)), dim3(512), 0,
+                           stream, p);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if constexpr (GK == kGateScalar) {
+        if (a.T == 0) return hipSuccess;
+        hipLaunchKernelGGL((gate_grad_kernel<true>), dim3(static_cast<unsigned>(heads)), dim3(256), 0, stream, gq,
+                           a.ds_out, sfin, a.dgate, a.B, a.H, a.T, DV * DK);
+    } else {
+        hipLaunchKernelGGL((gate_grad_kernel<false>), dim3(static_cast<unsigned>(a.H)), dim3(256), 0, stream, gq,
+                           a.ds_out, sfin, a.dgate, a.B, a.H, a.T, DV * DK);
+    }
+    return hipGetLastError();
+}
+
+template <int C, int DK, int GK>
+hipError_t launch_backward_dk(const BwdArgs& a, hipStream_t stream) {
+    switch (a.dv) {
+        case 16: return launch_backward_dv<C, DK, 16, GK>(a, stream);
+        case 32: return launch_backward_dv<C, DK, 32, GK>(a, stream);
+        case 64: return launch_backward_dv<C, DK, 64, GK>(a, stream);
+        case 128: return launch_backward_dv<C, DK, 128, GK>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int C, int GK>
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
+    switch (a.dk) {
+        case 16: return launch_backward_dk<C, 16, GK>(a, stream);
+        case 32: return launch_backward_dk<C, 32, GK>(a, stream);
+        case 64: return launch_backward_dk<C, 64, GK>(a, stream);
+        case 128: return launch_backward_dk<C, 128, GK>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ck
+}  // namespace glr

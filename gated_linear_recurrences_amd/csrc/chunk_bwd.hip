@@ -1,0 +1,33 @@
+// Dispatch of the bf16 backward kernels by gate variant and chunk length.
+#include "chunk_backward.hpp"
+#include "launch.hpp"
+
+namespace glr {
+
+hipError_t launch_chunk_bwd_retention_c16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bwd_retention_c32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bwd_retention_c64(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bwd_scalar_c16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bwd_scalar_c32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bwd_scalar_c64(const BwdArgs& a, hipStream_t stream);
+
+size_t bwd_workspace_size(const BwdArgs& a) {
+    if (a.B == 0 || a.H == 0) return 0;
+    return ck::bwd_workspace_bytes(static_cast<int64_t>(a.B) * a.H, a.T, a.chunk, a.dk, a.dv);
+}
+
+hipError_t launch_chunk_bwd(Variant variant, const BwdArgs& a, hipStream_t stream) {
+    if (a.B == 0 || a.H == 0) return hipSuccess;
+    if (variant == kRetention) {
+        if (a.chunk == 16) return launch_chunk_bwd_retention_c16(a, stream);
+        if (a.chunk == 32) return launch_chunk_bwd_retention_c32(a, stream);
+        if (a.chunk == 64) return launch_chunk_bwd_retention_c64(a, stream);
+    } else if (variant == kScalar) {
+        if (a.chunk == 16) return launch_chunk_bwd_scalar_c16(a, stream);
+        if (a.chunk == 32) return launch_chunk_bwd_scalar_c32(a, stream);
+        if (a.chunk == 64) return launch_chunk_bwd_scalar_c64(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace glr

@@ -1,0 +1,8 @@
+// bf16 backward, scalar data-dependent decay, chunk 16: instantiation (kernels in chunk_backward.hpp).
+#include "chunk_backward.hpp"
+
+namespace glr {
+hipError_t launch_chunk_bwd_scalar_c16(const BwdArgs& a, hipStream_t stream) {
+    return ck::launch_backward<16, ck::kGateScalar>(a, stream);
+}
+}  // namespace glr

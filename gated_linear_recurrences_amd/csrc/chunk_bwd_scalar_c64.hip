@@ -1,0 +1,8 @@
+// bf16 backward, scalar data-dependent decay, chunk 64: instantiation (kernels in chunk_backward.hpp).
+#include "chunk_backward.hpp"
+
+namespace glr {
+hipError_t launch_chunk_bwd_scalar_c64(const BwdArgs& a, hipStream_t stream) {
+    return ck::launch_backward<64, ck::kGateScalar>(a, stream);
+}
+}  // namespace glr

@@ -15,6 +15,13 @@
 // chunk c, the memory entering it (bf16, [d_v][d_k]) to a workspace; the output
 // pass then evaluates all chunks in parallel from those snapshots.
 //
+// REV (backward of the fixed and scalar gates): the same walk from the last chunk
+// to the first carries the gradient R of the loss with respect to the memory at
+// a chunk's last token, R_(c-1) = e^(G_last) R_c + dO_c^T diag(e^G) Q_c - the
+// forward carry with q in place of k, dO in place of v and the weights e^(G_j)
+// (what token j's write reaches of the chunk's end, read backwards); the snapshot
+// of chunk c is R_c, and what is left after chunk 0 is the gradient of S_0.
+//
 // Decomposition (gfx950). Transitions act on key channels (columns of S) and
 // the write is an outer product, so every element of S evolves on its own. A
 // workgroup owns a DKB x DVB block (DKB = 16 NW key channels, DVB = 16 TV value
@@ -86,11 +93,12 @@ struct StateLayout {
     static constexpr bool fits = bytes <= 160 * 1024;
 };
 
-template <int C, int DK, int NWK, int NWV, int TV, int U, int GK>
+template <int C, int DK, int NWK, int NWV, int TV, int U, int GK, bool REV = false>
 __global__ __launch_bounds__(64 * NWK * NWV)
 void state_kernel(StateParams p) {
     using Lay = StateLayout<C, NWK, TV, U, GK>;
     constexpr bool GLA = GK == kGateChannel, SCL = GK == kGateScalar;
+    static_assert(!(REV && GLA), "the reverse walk covers the fixed and scalar gates");
     static_assert(Lay::fits, "LDS budget exceeded");
     static_assert(TV % NWV == 0, "value tiles split evenly over the wave groups");
     constexpr int NW = NWK * NWV, NT = 64 * NW, DKB = Lay::DKB, DVB = Lay::DVB;
@@ -138,6 +146,10 @@ void state_kernel(StateParams p) {
     }
 
     auto chunk_len = [&](int c) { return (T - c * C < C) ? (T - c * C) : C; };
+    // chunk of the sequence at walk position c (the walk runs backwards with REV), and its
+    // length (<= 0 past the end of the walk)
+    auto phys = [&](int c) { return REV ? NC - 1 - c : c; };
+    auto walk_len = [&](int c) { return c < NC ? chunk_len(phys(c)) : T - c * C; };
 
     // 16-byte pieces: wave `wave` covers a block of rows per load; piece_of places
     // them so that the staging writes are free of bank conflicts
@@ -166,7 +178,7 @@ void state_kernel(StateParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c_req = grp * U + u;
-            const int c = c_req < NC ? c_req : NC - 1;
+            const int c = phys(c_req < NC ? c_req : NC - 1);
             const int n = chunk_len(c);
             const u16* kc = kg + static_cast<int64_t>(c) * C * DK;
             const u16* vc = vg + static_cast<int64_t>(c) * C * dv;
@@ -203,7 +215,7 @@ void state_kernel(StateParams p) {
         const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int n = chunk_len(grp * U + u);   // <= 0 past the last chunk: all zero
+            const int n = walk_len(grp * U + u);   // <= 0 past the last chunk: all zero
             u16* ks = sK(b, u);
             u16* vs = sV(b, u);
 #pragma unroll
@@ -246,7 +258,7 @@ void state_kernel(StateParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 16 * q + 4 * g + e;
-                wq[q][e] = (j < n) ? ex2(static_cast<float>(n - 1 - j) * lg2) : 0.f;
+                wq[q][e] = (j < n) ? ex2(static_cast<float>(REV ? j + 1 : n - 1 - j) * lg2) : 0.f;
             }
         const float d = ex2(static_cast<float>(n) * lg2);
         dec[0] = d; dec[1] = d; dec[2] = d; dec[3] = d;
@@ -263,7 +275,10 @@ void state_kernel(StateParams p) {
 #pragma unroll
         for (int q = 0; q < CT; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wq[q][e] = ex2(last - __shfl(G, 16 * q + 4 * g + e, 64));
+            for (int e = 0; e < 4; ++e) {
+                const float gj = __shfl(G, 16 * q + 4 * g + e, 64);
+                wq[q][e] = ex2(REV ? gj : last - gj);
+            }
         const float d = ex2(last);
         dec[0] = d; dec[1] = d; dec[2] = d; dec[3] = d;
     };
@@ -322,7 +337,7 @@ void state_kernel(StateParams p) {
         for (int u = 0; u < U; ++u) {
             const int c = grp * U + u;
             if (c < NC) {
-                const int n = chunk_len(c);
+                const int n = walk_len(c);
                 f32x4 wq[CT];
                 if constexpr (GLA) {
                     gla_weights(sG(b, u), wq, dec[u]);
@@ -366,7 +381,7 @@ void state_kernel(StateParams p) {
 #pragma unroll
                 for (int t = 0; t < TVW; ++t) sacc[t] = sacc[t] * dec[u] + ds[u][t];
             }
-            if (c < NC) store_snap(c);
+            if (c < NC) store_snap(phys(c));
         }
     };
 

@@ -29,7 +29,7 @@ constexpr int state_group() {
     return StateLayout<C, NW, TV, 4, GK>::fits ? 4 : StateLayout<C, NW, TV, 2, GK>::fits ? 2 : 1;
 }
 
-template <int C, int DK, int TV, int GK>
+template <int C, int DK, int TV, int GK, bool REV = false>
 hipError_t launch_state(const ChunkArgs& a, int NC, hipStream_t stream) {
     constexpr int NW = state_key_tiles(DK);
     // one wave per key tile holding all TV value tiles: the key operand (and, for GLA, the
@@ -52,7 +52,7 @@ hipError_t launch_state(const ChunkArgs& a, int NC, hipStream_t stream) {
     p.kblocks = DK / (16 * NW);
     const int64_t G = static_cast<int64_t>(a.B) * a.H * p.vblocks * p.kblocks;
     p.remap = (G % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((state_kernel<C, DK, NW, NWV, TV, U, GK>), dim3(static_cast<unsigned>(G)), dim3(64 * NW * NWV),
+    hipLaunchKernelGGL((state_kernel<C, DK, NW, NWV, TV, U, GK, REV>), dim3(static_cast<unsigned>(G)), dim3(64 * NW * NWV),
                        0, stream, p);
     return hipGetLastError();
 }

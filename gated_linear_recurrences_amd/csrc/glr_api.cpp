@@ -158,6 +158,33 @@ la_status gdelta_chunk_fwd_fused(const void* q, const void* k, const void* v, co
     return run_chunk(glr::kGDelta, a, dtype, workspace_bytes, stream);
 }
 
+la_status run_bwd(glr::Variant variant, const glr::BwdArgs& a, la_dtype dtype, size_t ws_bytes, void* stream) {
+    // the forward's checks on q, k, v, the gate and the dimensions (o stands for the gradients)
+    glr::ChunkArgs f{a.q, a.k, a.v, a.gate, nullptr, a.s0, a.grad_q, nullptr, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
+                     a.ws};
+    la_status st = check_chunk_args(variant, f, dtype);
+    if (st != LA_OK) return st;
+    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s", "the backward takes bf16 storage");
+    const bool heads = a.B > 0 && a.H > 0;
+    const bool tokens = heads && a.T > 0;
+    if ((st = check_ptr(a.dout, tokens, false, "dout")) != LA_OK) return st;
+    if ((st = check_ptr(a.grad_k, tokens, false, "dk")) != LA_OK) return st;
+    if ((st = check_ptr(a.grad_v, tokens, false, "dv")) != LA_OK) return st;
+    if ((st = check_ptr(a.dgate, variant == glr::kRetention ? heads : tokens, false, "dgate")) != LA_OK) return st;
+    if ((st = check_ptr(a.ds_out, heads, true, "ds_out")) != LA_OK) return st;
+    if ((st = check_ptr(a.ds0, heads, true, "ds0")) != LA_OK) return st;
+    const size_t need = glr::bwd_workspace_size(a);
+    if (need > 0) {
+        if (a.ws == nullptr) return fail(LA_ERR_INVALID, "%s", "workspace is NULL");
+        if (!aligned16(a.ws)) return fail(LA_ERR_INVALID, "%s", "workspace is not 16-byte aligned");
+        if (ws_bytes < need) return fail(LA_ERR_INVALID, "%s", "workspace too small");
+    }
+    if (!heads) return LA_OK;
+    const hipError_t err = glr::launch_chunk_bwd(variant, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+    return LA_OK;
+}
+
 la_status la_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
                             float* s, void* o, int N, int H, int dk, int dv, la_dtype dtype,
                             void* stream) {
@@ -209,6 +236,43 @@ la_status gdelta_recurrent_step(const void* q, const void* k, const void* v, con
     return LA_OK;
 }
 
+la_status la_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                                      size_t* bytes) {
+    if (bytes == nullptr) return fail(LA_ERR_INVALID, "%s", "bytes is NULL");
+    *bytes = 0;
+    glr::ChunkArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     B, H, 0, dk, dv, chunk, nullptr};
+    la_status st = check_chunk_args(glr::kRetention, a, dtype);
+    if (st != LA_OK) return st;
+    if (T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
+    if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s", "the backward takes bf16 storage");
+    const int64_t chunks = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(T) + chunk - 1) / chunk);
+    if (chunks >= (static_cast<int64_t>(1) << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "B * H * ceil(T / chunk) must be below 2^31");
+    glr::BwdArgs b{};
+    b.B = B; b.H = H; b.T = T; b.dk = dk; b.dv = dv; b.chunk = chunk;
+    *bytes = glr::bwd_workspace_size(b);
+    return LA_OK;
+}
+
+la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float* log_gamma, const float* s0,
+                       const void* dout, const float* ds_out, void* dq, void* dk_, void* dv_, float* dlog_gamma,
+                       float* ds0, int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    glr::BwdArgs a{q, k, v, log_gamma, s0, dout, ds_out, dq, dk_, dv_, dlog_gamma, ds0, B, H, T, dk, dv, chunk,
+                   workspace};
+    return run_bwd(glr::kRetention, a, dtype, workspace_bytes, stream);
+}
+
+la_status mamba2_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* s0,
+                           const void* dout, const float* ds_out, void* dq, void* dk_, void* dv_, float* dlog_alpha,
+                           float* ds0, int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    glr::BwdArgs a{q, k, v, log_alpha, s0, dout, ds_out, dq, dk_, dv_, dlog_alpha, ds0, B, H, T, dk, dv, chunk,
+                   workspace};
+    return run_bwd(glr::kScalar, a, dtype, workspace_bytes, stream);
+}
+
 const char* la_status_str(la_status status) {
     switch (status) {
         case LA_OK: return "ok";
@@ -221,6 +285,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (2 << 16) | 3; }
+int la_version(void) { return (2 << 16) | 4; }
 
 }  // extern "C"

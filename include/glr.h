@@ -226,6 +226,37 @@ la_status gdelta_recurrent_step(const void* q, const void* k, const void* v,
                                 int N, int H, int dk, int dv,
                                 la_dtype dtype, void* stream);
 
+/*
+ * Backward of la_chunk_fwd (retention) and mamba2_chunk_fwd (scalar
+ * data-dependent decay): reverse-mode gradients of the recurrence ("Scrivere
+ * meglio nella memoria", section "Dimenticare: i gate", scalar decay) through
+ * the chunkwise form of the RetNet page.  Given dout [B][H][T][d_v] (the
+ * gradient of the loss with respect to o, in `dtype`) and, optionally, ds_out
+ * [B][H][d_v][d_k] float32 (with respect to the final memory; NULL = zero),
+ * writes dq, dk [B][H][T][d_k] and dv [B][H][T][d_v] in `dtype`, the gate
+ * gradient (la_chunk_bwd: dlog_gamma [H], summed over the batch and the
+ * tokens of each head; mamba2_chunk_bwd: dlog_alpha [B][H][T]) and, if ds0 is
+ * not NULL, ds0 [B][H][d_v][d_k] float32 (with respect to s0).  The forward
+ * inputs (q, k, v, the gate, s0) are those of the forward call; the forward
+ * is not needed beforehand (its carry is recomputed).  Only LA_BF16 storage
+ * (LA_ERR_UNSUPPORTED otherwise).  The workspace size comes from
+ * la_chunk_bwd_workspace_size: with N = B * H * ceil(T / chunk) and a(x) = x
+ * rounded up to a multiple of 256, 2 a(N*d_v*d_k*2) + a(B*H*d_v*d_k*4) +
+ * a(B*H*T*4) bytes.  Other conventions and errors as for the forward.
+ */
+la_status la_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
+                                      la_dtype dtype, size_t* bytes);
+la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float* log_gamma,
+                       const float* s0, const void* dout, const float* ds_out,
+                       void* dq, void* dk_, void* dv_, float* dlog_gamma, float* ds0,
+                       int B, int H, int T, int dk, int dv, int chunk,
+                       la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+la_status mamba2_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* s0, const void* dout, const float* ds_out,
+                           void* dq, void* dk_, void* dv_, float* dlog_alpha, float* ds0,
+                           int B, int H, int T, int dk, int dv, int chunk,
+                           la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* la_status_str(la_status status);
 
@@ -234,7 +265,8 @@ const char* la_status_str(la_status status);
 const char* la_last_error(void);
 
 /* ABI version: (major << 16) | minor (2.0: workspace arguments; 2.1:
- * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step; 2.3: gdelta_chunk_fwd_fused). */
+ * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step; 2.3: gdelta_chunk_fwd_fused;
+ * 2.4: la_chunk_bwd, mamba2_chunk_bwd). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 2
-    assert lib.la_version() & 0xffff >= 3      # 2.1 mamba2_chunk_fwd, 2.2 gdelta_recurrent_step, 2.3 fused
+    assert lib.la_version() & 0xffff >= 4      # 2.1 mamba2, 2.2 gdelta decode, 2.3 fused, 2.4 backward
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -193,3 +193,43 @@ def test_gdelta_fused_validation(lib):
     assert call(_native.LA_FUSE_OUT_RMSNORM, eps=float("nan")) == _native.LA_ERR_INVALID
     assert call(_native.LA_FUSE_QK_SILU_L2, q=None) == _native.LA_ERR_INVALID
     assert call(3, B=0, q=None, k=None, v=None, o=None, gate=None, beta=None, weight=None) == _native.LA_OK
+
+
+def test_backward_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(fn="la_chunk_bwd", ws_bytes=1 << 30, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, s0=None, dout=FAKE, ds_out=None, dq=FAKE, dk=FAKE, dv=FAKE,
+                 dgate=FAKE, ds0=None, B=1, H=1, T=8, dk_=16, dv_=16, chunk=16, dtype=1, ws=FAKE)
+        a.update(kw)
+        return getattr(lib, fn)(P(a["q"]), P(a["k"]), P(a["v"]), P(a["gate"]), P(a["s0"]), P(a["dout"]),
+                                P(a["ds_out"]), P(a["dq"]), P(a["dk"]), P(a["dv"]), P(a["dgate"]), P(a["ds0"]),
+                                a["B"], a["H"], a["T"], a["dk_"], a["dv_"], a["chunk"], a["dtype"], P(a["ws"]),
+                                ws_bytes, None)
+
+    for fn in ("la_chunk_bwd", "mamba2_chunk_bwd"):
+        assert call(fn, dtype=0) == _native.LA_ERR_UNSUPPORTED
+        assert b"bf16" in lib.la_last_error()
+        assert call(fn, dout=None) == _native.LA_ERR_INVALID
+        assert b"dout is NULL" in lib.la_last_error()
+        assert call(fn, dgate=None) == _native.LA_ERR_INVALID
+        assert call(fn, ds_out=MISALIGNED) == _native.LA_ERR_INVALID
+        assert call(fn, ws=None) == _native.LA_ERR_INVALID
+        assert call(fn, ws_bytes=16) == _native.LA_ERR_INVALID
+        assert b"workspace too small" in lib.la_last_error()
+        assert call(fn, dk_=24) == _native.LA_ERR_UNSUPPORTED
+        assert call(fn, B=0, q=None, k=None, v=None, gate=None, dout=None, dq=None, dk=None, dv=None,
+                    dgate=None, ws=None) == _native.LA_OK
+
+
+def test_backward_workspace_size(lib):
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    out = ctypes.c_size_t(0)
+    assert lib.la_chunk_bwd_workspace_size(4, 8, 2048, 128, 128, 64, 1, ctypes.byref(out)) == _native.LA_OK
+    n = 4 * 8 * 32
+    assert out.value == 2 * a256(n * 128 * 128 * 2) + a256(32 * 128 * 128 * 4) + a256(32 * 2048 * 4)
+    assert lib.la_chunk_bwd_workspace_size(4, 8, 2048, 128, 128, 64, 0, ctypes.byref(out)) == _native.LA_ERR_UNSUPPORTED
+    assert lib.la_chunk_bwd_workspace_size(0, 8, 2048, 128, 128, 64, 1, ctypes.byref(out)) == _native.LA_OK
+    assert out.value == 0

@@ -268,6 +268,85 @@ def test_gdelta_fused_full_size_parity():
                   "fused full size", normed=True)
 
 
+# ----------------------------------------------------------------------------- backward
+
+BWD_SHAPES = [(1, 2, 100, 16, 16, 16), (2, 1, 77, 32, 64, 32), (1, 2, 130, 64, 32, 64), (2, 2, 200, 128, 128, 64),
+              (1, 1, 64, 128, 16, 16), (1, 1, 1, 64, 64, 64), (1, 2, 0, 64, 64, 64), (4, 8, 192, 128, 128, 64)]
+
+
+def _bwd_gate(name, got, ref, floor=0.0):
+    """Gradients are held to the forward's relative bound, max |d| <= 1e-2 max |ref|. A gate
+    gradient is a sum over tokens of q.dq - k.dk terms that cancel (for retention over a
+    whole head: a value near 1 from terms summing to 2e3 in absolute value), so it is held to
+    1e-2 of its L2 norm plus ``floor``: 1e-3 of the norm of the same sums taken over the
+    absolute values of the terms, i.e. each term's own error carried through the sum."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if floor:
+        err, scale = np.linalg.norm(got - ref), np.linalg.norm(ref)
+    else:
+        err, scale = np.max(np.abs(got - ref)), np.max(np.abs(ref))
+    bound = 1e-2 * max(scale, 1e-30) + floor
+    msg = f"{name}: err={err:.3e} scale={scale:.3e} bound={bound:.3e}"
+    print(msg)
+    assert np.all(np.isfinite(got)), msg
+    assert err <= bound, msg
+
+
+def _gate_terms_floor(kind, q, k, dq, dk):
+    """1e-3 of the L2 norm of the gate gradient's terms in absolute value: per token
+    sum_{s >= t} |q_s.dq_s| + |k_s.dk_s| (scalar gates), per head the sum over the batch and
+    the tokens of (s + 1) times the same (fixed gates)."""
+    ab = np.abs(np.einsum("bhtc,bhtc->bht", np.float64(q), dq)) + np.abs(np.einsum("bhtc,bhtc->bht", np.float64(k), dk))
+    if kind == "retention":
+        sc = (ab * (np.arange(ab.shape[-1]) + 1)).sum(axis=(0, 2))
+    else:
+        sc = np.flip(np.cumsum(np.flip(ab, -1), -1), -1)
+    return 1e-3 * float(np.linalg.norm(sc))
+
+
+@pytest.mark.parametrize("kind", ["retention", "mamba2"])
+@pytest.mark.parametrize("shape", BWD_SHAPES)
+@pytest.mark.parametrize("extras", [False, True])
+def test_backward_parity(kind, shape, extras):
+    """dq, dk, dv, the gate gradient and ds0 of the bf16 backward against the oracle's
+    reverse-mode gradients of the recurrence, for L = <dout, o> (+ <ds_out, S_T>)."""
+    B, H, T, dk, dv, c = shape
+    w = make(kind, B, H, T, dk, dv, c, "bf16", 600 + sum(shape), extras)
+    rng = np.random.default_rng(sum(shape))
+    dout = synthetic.round_to_bf16(rng.standard_normal((B, H, T, dv)) / np.sqrt(dv)).astype(np.float32)
+    ds_out = (rng.standard_normal((B, H, dv, dk)) * 0.1).astype(np.float32) if extras else None
+    q, k, v = _t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16)
+    if kind == "retention":
+        dq, dk_, dv_, dg, ds0 = api.la_chunk_bwd(q, k, v, _t(w.log_gamma), _t(dout, torch.bfloat16), s0=_t(w.s0),
+                                                 ds_out=_t(ds_out), chunk=c)
+        ref = orc.retention_backward(w.q, w.k, w.v, w.log_gamma, dout, dS_T=ds_out, s0=w.s0)
+    else:
+        dq, dk_, dv_, dg, ds0 = api.mamba2_chunk_bwd(q, k, v, _t(w.log_alpha), _t(dout, torch.bfloat16),
+                                                     s0=_t(w.s0), ds_out=_t(ds_out), chunk=c)
+        ref = orc.scalar_backward(w.q, w.k, w.v, w.log_alpha, dout, dS_T=ds_out, s0=w.s0)
+    torch.cuda.synchronize()
+    label = f"{kind} {shape} extras={extras}"
+    for name, got, r in (("dq", dq, ref[0]), ("dk", dk_, ref[1]), ("dv", dv_, ref[2]), ("ds0", ds0, ref[4])):
+        if T == 0 and name != "ds0":
+            continue
+        _bwd_gate(f"{label} {name}", got.float().cpu().numpy(), r)
+    floor = _gate_terms_floor(kind, w.q, w.k, ref[0], ref[1]) if T else 1e-30
+    _bwd_gate(f"{label} dgate", dg.cpu().numpy(), ref[3], floor=floor)
+
+
+def test_backward_deterministic():
+    """No atomics: two backward calls give bit-identical gradients."""
+    w = make("mamba2", 2, 2, 150, 128, 128, 64, "bf16", 9, True)
+    q, k, v = _t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16)
+    dout = torch.randn(w.v.shape, device=DEV).to(torch.bfloat16)
+    r1 = api.mamba2_chunk_bwd(q, k, v, _t(w.log_alpha), dout, s0=_t(w.s0))
+    r2 = api.mamba2_chunk_bwd(q, k, v, _t(w.log_alpha), dout, s0=_t(w.s0))
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
 # ----------------------------------------------------------------------------- decode
 
 def _decode_run(w, steps):
