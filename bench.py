@@ -17,7 +17,8 @@ one call, snapshots included; ``mfma`` gives the same run against the dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on the host; ``others``
 reports the per-channel-gate (GLA), gated-delta, scalar data-dependent decay
 and decode (per-channel gate, gated delta rule) workloads measured the same way,
-and the gated delta rule with its feature map and output norm fused in.
+the gated delta rule with its feature map and output norm fused in, and the
+backward of the retention and scalar-decay workloads (beside their forward).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
     python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
@@ -248,6 +249,43 @@ def bench_gdelta_fused(steps, warmup, torch, api, synthetic, dev):
                 tokens_per_s=B * H * T / (ms_f * 1e-3), speedup_vs_unfused=ms_u / ms_f)
 
 
+def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
+    """Backward of a retention or scalar-decay workload (four kernels: forward state pass,
+    reverse state pass, gradient pass, gate pass) with a seeded dO and ds_out; beside it
+    the forward of the same workload. Algorithmic flops per token-head 8Cd + 10d^2 (the two
+    state passes 2d^2 each; Q K^T, dO V^T, dO^T A1, Q^T A2, K^T A2^T 2Cd each over the
+    C x C block; R K^T, R^T V^T, S_in^T dO^T 2d^2 each); bytes: read q, k, v, dO, write dq,
+    dk, dv (7 d bf16 per token-head), the gates and three d x d fp32 memories per head."""
+    c = synthetic.CONFIGS[name]
+    B, H, T, d, C = c["B"], c["H"], c["T"], c["dk"], c["chunk"]
+    w = synthetic.config_inputs(name)
+    b = upload(w, torch, dev)
+    del w
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    dout = (torch.randn((B, H, T, d), generator=g, device=dev) / d ** 0.5).to(torch.bfloat16)
+    ds_out = torch.randn((B, H, d, d), generator=g, device=dev) * 0.1
+    ws = torch.empty(api.bwd_workspace_size(B, H, T, d, d, C), dtype=torch.uint8, device=dev)
+    if c["kind"] == "retention":
+        bwd = lambda: api.la_chunk_bwd(b["q"], b["k"], b["v"], b["log_gamma"], dout, ds_out=ds_out, chunk=C,
+                                       workspace=ws)
+        gate_bytes = 0
+    else:
+        bwd = lambda: api.mamba2_chunk_bwd(b["q"], b["k"], b["v"], b["log_alpha"], dout, ds_out=ds_out, chunk=C,
+                                           workspace=ws)
+        gate_bytes = 8
+    fwd = make_call(c["kind"], api, b, C, torch)
+    ms_b = time_calls([bwd], steps, warmup, torch)[1]
+    ms_f = time_calls([fwd], steps, warmup, torch)[1]
+    th = B * H * T
+    flops = th * (8 * C * d + 10 * d * d)
+    bytes_ = th * (7 * d * 2 + gate_bytes) + 3 * B * H * d * d * 4
+    return dict(workload=name + "_bwd", kernel_ms=ms_b, fwd_kernel_ms=ms_f, bwd_over_fwd=ms_b / ms_f,
+                tokens_per_s=th / (ms_b * 1e-3), alg_gflop=flops / 1e9, alg_gbytes=bytes_ / 1e9,
+                mfma_frac=flops / (ms_b * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                hbm_frac=bytes_ / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
 KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_state.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_output.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_two_pass.hpp",
@@ -461,6 +499,10 @@ def main():
         others["gdelta_decode_n512h32_d128"] = bench_gdelta_decode(min(args.decode_steps, 200), torch, api,
                                                                    synthetic, dev)
         torch.cuda.empty_cache()
+        for name in (MAIN, "mamba2_b8h16_t4096_d128"):
+            others[name + "_bwd"] = bench_backward(name, max(20, args.steps // 4), max(3, args.warmup // 4), torch,
+                                                   api, synthetic, dev)
+            torch.cuda.empty_cache()
 
     cfg = synthetic.CONFIGS[MAIN]
     out = {

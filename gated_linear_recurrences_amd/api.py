@@ -181,6 +181,12 @@ def workspace_size(kind, B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16):
     return _native.workspace_size(variant, B, H, T, dk, dv, chunk, code)
 
 
+def bwd_workspace_size(B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16):
+    """Device workspace in bytes for la_chunk_bwd and mamba2_chunk_bwd (bf16 storage)."""
+    code = _native.LA_BF16 if dtype == torch.bfloat16 else _native.LA_F32
+    return _native.bwd_workspace_size(B, H, T, dk, dv, chunk, code)
+
+
 def la_recurrent_step(q, k, v, alpha, s, o=None):
     """One decode token, in place on s: S <- S Diag(alpha); S <- S + v k^T; o = S q.
 
@@ -244,7 +250,7 @@ def _chunk_bwd(fn, q, k, v, gate, gate_shape, dout, s0, ds_out, chunk, want_ds0,
     dv_ = torch.empty_like(v)
     dgate = torch.empty(gate_shape, dtype=torch.float32, device=dev)
     ds0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_ds0 else None
-    need = _native.bwd_workspace_size(B, H, T, dk, dv, chunk, _dtype_code(q))
+    need = bwd_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or not workspace.is_contiguous():
