@@ -38,6 +38,8 @@ __all__ = [
     "gla_inputs",
     "gdelta_inputs",
     "decode_inputs",
+    "vla_inputs",
+    "vla_decode_inputs",
     "CONFIGS",
     "config_inputs",
 ]
@@ -89,6 +91,9 @@ class Workload:
     beta: Optional[np.ndarray] = None        # gdelta [B,H,T]
     alpha: Optional[np.ndarray] = None       # decode [N,H,dk] (or [steps,N,H,dk]); delta decode [steps,N,H]
     s0: Optional[np.ndarray] = None          # [B,H,dv,dk] fp32
+    u: Optional[np.ndarray] = None           # vla penalty directions [B,H,T,dk] (decode: [steps,N,H,dk])
+    a0: Optional[np.ndarray] = None          # vla inverse penalty [B,H,dk,dk] fp32
+    lambda0: float = 1.0                     # vla: A_0 = I / lambda0 when a0 is None
     meta: dict = field(default_factory=dict)
 
 
@@ -196,6 +201,45 @@ def gdelta_decode_inputs(N, H, dk, dv, *, steps=1, dtype="bf16", seed=0):
         b[s] = _sigmoid(rng.standard_normal((N, H))).astype(np.float32)
         a[s] = np.exp(-_softplus(rng.standard_normal((N, H))) / 8.0).astype(np.float32)
     return Workload("gdelta_decode", dtype, q, k, v, alpha=a, beta=b, s0=s0)
+
+
+def _penalty_inverse(lead, dk, lambda0, rng):
+    """A symmetric positive-definite starting inverse penalty: I / lambda0 plus a symmetric
+    perturbation of spectral norm below 0.1 / lambda0."""
+    G = rng.standard_normal(lead + (dk, dk))
+    P = (G + np.swapaxes(G, -1, -2)) / (2.0 * np.sqrt(dk))
+    return ((np.eye(dk) + 0.04 * P) / lambda0).astype(np.float32)
+
+
+def vla_inputs(B, H, T, dk, dv, *, dtype="bf16", seed=0, with_state=False, lambda0=1.0):
+    """Variational linear attention: q, k, u ~ N(0,1)/sqrt(dk) (u the penalty direction
+    added per token), v ~ N(0,1); A_0 = I / lambda0 (with_state: a perturbed SPD A_0 and
+    S_0 ~ N(0, 0.01))."""
+    rng = np.random.default_rng(seed)
+    sc = 1.0 / np.sqrt(dk)
+    q = _store(rng.standard_normal((B, H, T, dk)) * sc, dtype)
+    k = _store(rng.standard_normal((B, H, T, dk)) * sc, dtype)
+    v = _store(rng.standard_normal((B, H, T, dv)), dtype)
+    u = _store(rng.standard_normal((B, H, T, dk)) * sc, dtype)
+    s0 = a0 = None
+    if with_state:
+        s0 = (rng.standard_normal((B, H, dv, dk)) * 0.1).astype(np.float32)
+        a0 = _penalty_inverse((B, H), dk, lambda0, rng)
+    return Workload("vla", dtype, q, k, v, s0=s0, u=u, a0=a0, lambda0=lambda0)
+
+
+def vla_decode_inputs(N, H, dk, dv, *, steps=1, dtype="bf16", seed=0, lambda0=1.0):
+    """VLA decode: S_0 ~ N(0, 0.01) fp32, a perturbed SPD A_0, then ``steps`` fresh tokens
+    with the sequence workload's recipe. Leading step axis on q, k, v, u."""
+    rng = np.random.default_rng(seed)
+    s0 = (rng.standard_normal((N, H, dv, dk)) * 0.1).astype(np.float32)
+    a0 = _penalty_inverse((N, H), dk, lambda0, rng)
+    sc = 1.0 / np.sqrt(dk)
+    q = _store(rng.standard_normal((steps, N, H, dk)) * sc, dtype)
+    k = _store(rng.standard_normal((steps, N, H, dk)) * sc, dtype)
+    v = _store(rng.standard_normal((steps, N, H, dv)), dtype)
+    u = _store(rng.standard_normal((steps, N, H, dk)) * sc, dtype)
+    return Workload("vla_decode", dtype, q, k, v, s0=s0, u=u, a0=a0, lambda0=lambda0)
 
 
 # The five workloads the throughput and parity figures are quoted on, and the scalar

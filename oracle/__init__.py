@@ -14,6 +14,9 @@ Sources (web pages; cited by title and section):
   * "Le architetture lineari: RetNet, RWKV, xLSTM" (book.paithon.it) - the
     three equivalent forms of retention (parallel, recurrent, chunkwise),
     Fig. 16.5 and its worked example.
+  * "Riepilogo Tecnico: Attenzione Lineare Variazionale (VLA)" (gist.science) -
+    variational linear attention: the Sherman-Morrison update of the inverse
+    penalty, the normalised gating vector and the residual write.
 
 Every function here is pinned by a ``-m "not gpu"`` test against something other
 than itself (values the pages print, closed forms, invariants, brute force);
@@ -39,5 +42,7 @@ from .glr_oracle import (  # noqa: F401
     rms_norm,
     scalar_backward,
     retention_backward,
+    vla_recurrent,
+    vla_decode_step,
     forward_substitution,
 )

@@ -36,6 +36,11 @@ online" of the same page):
 Forms (RetNet page, section "RetNet: la retention e le sue tre forme", Fig.
 16.5): the recurrent form is the definition; the parallel ("quadratic") form
 and the chunkwise form must give the same numbers up to rounding.
+
+Also here: the reverse-mode gradients of the fixed and scalar decays, and
+variational linear attention (VLA summary page, "Riepilogo Tecnico: Attenzione
+Lineare Variazionale (VLA)", section 2.3) in its recurrent form, which returns
+``(o, S_T, A_T)`` with the inverse penalty ``A`` beside the memory.
 """
 
 import numpy as np
@@ -529,3 +534,62 @@ def retention_backward(q, k, v, log_gamma, do, dS_T=None, s0=None):
     la = np.broadcast_to(np.asarray(log_gamma, dtype=np.float64)[None, :, None], (B, H, T))
     dq, dk, dv, dla, ds0 = scalar_backward(q, k, v, la, do, dS_T=dS_T, s0=s0)
     return dq, dk, dv, dla.sum(axis=(0, 2)), ds0
+
+
+# --------------------------------------------------------------------------- variational linear attention
+
+def _vla_step(S, A, q_t, k_t, v_t, u_t):
+    """One token of VLA, the three steps of the recursive update in the order the VLA
+    summary page gives them ("Riepilogo Tecnico: Attenzione Lineare Variazionale (VLA)",
+    section 2.3; the penalty geometry of section 2.2):
+
+    1. Sherman-Morrison on the inverse penalty: ``M_t = M_{t-1} + u_t u_t^T`` gives
+       ``A_t = A_{t-1} - z_t z_t^T / (1 + u_t^T z_t)`` with ``z_t = A_{t-1} u_t``;
+    2. the gating vector from the *updated* inverse: ``a_t = A_t k^_t / |A_t k^_t|``,
+       ``k^_t = k_t / |k_t|`` (the key is normalised: section 2.1);
+    3. the memory: ``S_t = S_{t-1} + (v_t - S_{t-1} k^_t) a_t^T``;
+
+    then the readout ``o_t = S_t q_t`` (read after write, as for every variant here).
+    Shapes: S ``[..., d_v, d_k]``, A ``[..., d_k, d_k]``, vectors ``[..., d]``."""
+    z = np.einsum("...mc,...c->...m", A, u_t)
+    den = 1.0 + np.sum(u_t * z, axis=-1)
+    A = A - z[..., :, None] * z[..., None, :] / den[..., None, None]
+    kh = k_t / np.linalg.norm(k_t, axis=-1, keepdims=True)
+    y = np.einsum("...mc,...c->...m", A, kh)
+    a = y / np.linalg.norm(y, axis=-1, keepdims=True)
+    resid = v_t - np.einsum("...mc,...c->...m", S, kh)
+    S = S + resid[..., :, None] * a[..., None, :]
+    return _read(S, q_t), S, A
+
+
+def _vla_init_penalty(k, a0, lambda0):
+    dk = k.shape[-1]
+    if a0 is not None:
+        return np.array(a0, dtype=np.float64)
+    return np.broadcast_to(np.eye(dk) / float(lambda0), k.shape[:-2] + (dk, dk)).copy()
+
+
+def vla_recurrent(q, k, v, u, lambda0=1.0, s0=None, a0=None):
+    """Variational linear attention over whole sequences, token by token (the
+    definition: section 2.3 of the VLA summary page; see ``_vla_step``).
+
+    ``q, k, u`` are ``[B, H, T, d_k]`` (``u_t`` the penalty direction added to M at
+    token t), ``v`` is ``[B, H, T, d_v]``. The inverse penalty starts at
+    ``A_0 = M_0^{-1} = I / lambda0`` unless ``a0 [B, H, d_k, d_k]`` is given; the
+    memory at ``s0`` or zeros. Returns ``(o, S_T, A_T)``."""
+    q, k, v, u = _f64(q, k, v, u)
+    S = _init_state(q, v, s0)
+    A = _vla_init_penalty(k, a0, lambda0)
+    T = q.shape[-2]
+    o = np.zeros(v.shape)
+    for t in range(T):
+        o[..., t, :], S, A = _vla_step(S, A, q[..., t, :], k[..., t, :], v[..., t, :], u[..., t, :])
+    return o, S, A
+
+
+def vla_decode_step(q, k, v, u, s, a):
+    """One VLA token for N sequences: ``q, k, u [N, H, d_k]``, ``v [N, H, d_v]``, the
+    memory ``s [N, H, d_v, d_k]`` and inverse penalty ``a [N, H, d_k, d_k]``. Returns
+    ``(o, s_new, a_new)``; the inputs are not modified."""
+    q, k, v, u, s, a = _f64(q, k, v, u, s, a)
+    return _vla_step(s, a, q, k, v, u)
