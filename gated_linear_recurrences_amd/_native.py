@@ -26,6 +26,8 @@ EXPORTED = (
     "la_chunk_bwd_workspace_size",
     "la_chunk_bwd",
     "mamba2_chunk_bwd",
+    "vla_fwd",
+    "vla_recurrent_step",
     "la_status_str",
     "la_last_error",
     "la_version",
@@ -69,8 +71,11 @@ def load():
     lib.mamba2_chunk_bwd.argtypes = bwd
     lib.la_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.la_chunk_bwd_workspace_size.restype = ctypes.c_int
+    lib.vla_fwd.argtypes = [P, P, P, P, ctypes.c_float, F, F, P, F, F, I, I, I, I, I, I, P]
+    lib.vla_recurrent_step.argtypes = [P, P, P, P, F, F, P, I, I, I, I, I, P]
     for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-                 "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd"):
+                 "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd", "vla_fwd",
+                 "vla_recurrent_step"):
         getattr(lib, name).restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
     lib.la_status_str.restype = ctypes.c_char_p

@@ -239,6 +239,53 @@ def gdelta_recurrent_step(q, k, v, alpha, beta, s, o=None):
     return o
 
 
+def vla_fwd(q, k, v, u, lambda0=1.0, a0=None, s0=None, o=None, s_out=None, a_out=None, return_state=True):
+    """Variational linear attention over whole sequences: per token z = A u,
+    A <- A - z z^T / (1 + u.z), a = A k^/|A k^| (k^ = k/|k|), S <- S + (v - S k^) a^T, o = S q.
+
+    q, k, u [B,H,T,d_k], v [B,H,T,d_v] (bf16 or fp32); A starts at a0 [B,H,d_k,d_k] fp32 or
+    I / lambda0, S at s0 [B,H,d_v,d_k] fp32 or zeros. Returns (o, s_out, a_out)."""
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
+    dev = q.device
+    _require(u, "u", (B, H, T, dk), q.dtype, dev)
+    if a0 is not None:
+        _require(a0, "a0", (B, H, dk, dk), torch.float32, dev)
+    if a_out is None and return_state:
+        a_out = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+    elif a_out is not None:
+        _require(a_out, "a_out", (B, H, dk, dk), torch.float32, dev)
+    lib = _native.load()
+    _native.check(lib.vla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(u), float(lambda0), _ptr(a0), _ptr(s0), _ptr(o),
+                              _ptr(s_out), _ptr(a_out), B, H, T, dk, dv, _dtype_code(q), _stream(dev)))
+    return o, s_out, a_out
+
+
+def vla_recurrent_step(q, k, v, u, s, a, o=None):
+    """One VLA decode token, in place on the memory s [N,H,d_v,d_k] and the inverse penalty
+    a [N,H,d_k,d_k] (fp32); q, k, u [N,H,d_k], v [N,H,d_v] (bf16 or fp32). Returns o."""
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    _require(k, "k", (N, H, dk), q.dtype, dev)
+    _require(u, "u", (N, H, dk), q.dtype, dev)
+    _require(v, "v", (N, H, dv), q.dtype, dev)
+    _require(s, "s", (N, H, dv, dk), torch.float32, dev)
+    _require(a, "a", (N, H, dk, dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", (N, H, dv), q.dtype, dev)
+    lib = _native.load()
+    _native.check(lib.vla_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(s), _ptr(a), _ptr(o), N, H, dk, dv,
+                                         _dtype_code(q), _stream(dev)))
+    return o
+
+
 def _chunk_bwd(fn, q, k, v, gate, gate_shape, dout, s0, ds_out, chunk, want_ds0, workspace):
     dims, _, _ = _chunk_common(q, k, v, s0, dout, None, False)
     B, H, T, dk, dv = dims

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <limits>
 #include <cstdio>
 #include <cstring>
 
@@ -273,6 +274,62 @@ la_status mamba2_chunk_bwd(const void* q, const void* k, const void* v, const fl
     return run_bwd(glr::kScalar, a, dtype, workspace_bytes, stream);
 }
 
+la_status vla_fwd(const void* q, const void* k, const void* v, const void* u, float lambda0, const float* a0,
+                  const float* s0, void* o, float* s_out, float* a_out, int B, int H, int T, int dk, int dv,
+                  la_dtype dtype, void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "%s", "unknown dtype");
+    if (B < 0 || H < 0 || T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
+    if (dk < 1 || dv < 1) return fail(LA_ERR_INVALID, "%s", "d_k and d_v must be >= 1");
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "d_k and d_v must be 16, 32, 64 or 128");
+    if (a0 == nullptr && !(lambda0 > 0.f && lambda0 < std::numeric_limits<float>::infinity()))
+        return fail(LA_ERR_INVALID, "%s", "lambda0 must be positive and finite when a0 is NULL");
+    const bool heads = B > 0 && H > 0;
+    const bool tokens = heads && T > 0;
+    la_status st;
+    if ((st = check_ptr(q, tokens, false, "q")) != LA_OK) return st;
+    if ((st = check_ptr(k, tokens, false, "k")) != LA_OK) return st;
+    if ((st = check_ptr(v, tokens, false, "v")) != LA_OK) return st;
+    if ((st = check_ptr(u, tokens, false, "u")) != LA_OK) return st;
+    if ((st = check_ptr(o, tokens, false, "o")) != LA_OK) return st;
+    if ((st = check_ptr(a0, heads, true, "a0")) != LA_OK) return st;
+    if ((st = check_ptr(s0, heads, true, "s0")) != LA_OK) return st;
+    if ((st = check_ptr(s_out, heads, true, "s_out")) != LA_OK) return st;
+    if ((st = check_ptr(a_out, heads, true, "a_out")) != LA_OK) return st;
+    if (static_cast<int64_t>(B) * H >= (static_cast<int64_t>(1) << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "B * H must be below 2^31");
+    if (!heads) return LA_OK;
+    glr::VlaArgs a{q, k, v, u, a0 ? 1.f : 1.f / lambda0, a0, s0, o, s_out, a_out, B, H, T, dk, dv};
+    const hipError_t err = glr::launch_vla(dtype == LA_BF16, a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+    return LA_OK;
+}
+
+la_status vla_recurrent_step(const void* q, const void* k, const void* v, const void* u, float* s, float* a, void* o,
+                             int N, int H, int dk, int dv, la_dtype dtype, void* stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "%s", "unknown dtype");
+    if (N < 0 || H < 0) return fail(LA_ERR_INVALID, "%s", "negative N or H");
+    if (dk < 1 || dv < 1) return fail(LA_ERR_INVALID, "%s", "d_k and d_v must be >= 1");
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "d_k and d_v must be 16, 32, 64 or 128");
+    const bool used = N > 0 && H > 0;
+    la_status st;
+    if ((st = check_ptr(q, used, false, "q")) != LA_OK) return st;
+    if ((st = check_ptr(k, used, false, "k")) != LA_OK) return st;
+    if ((st = check_ptr(v, used, false, "v")) != LA_OK) return st;
+    if ((st = check_ptr(u, used, false, "u")) != LA_OK) return st;
+    if ((st = check_ptr(s, used, false, "s")) != LA_OK) return st;
+    if ((st = check_ptr(a, used, false, "a")) != LA_OK) return st;
+    if ((st = check_ptr(o, used, false, "o")) != LA_OK) return st;
+    if (static_cast<int64_t>(N) * H >= (static_cast<int64_t>(1) << 31))
+        return fail(LA_ERR_UNSUPPORTED, "%s", "N * H must be below 2^31");
+    if (!used) return LA_OK;
+    glr::VlaArgs args{q, k, v, u, 1.f, a, s, o, s, a, N, H, 1, dk, dv};
+    const hipError_t err = glr::launch_vla(dtype == LA_BF16, args, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
+    return LA_OK;
+}
+
 const char* la_status_str(la_status status) {
     switch (status) {
         case LA_OK: return "ok";
@@ -285,6 +342,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (2 << 16) | 4; }
+int la_version(void) { return (2 << 16) | 5; }
 
 }  // extern "C"

@@ -59,6 +59,23 @@ struct BwdArgs {
 size_t bwd_workspace_size(const BwdArgs& a);
 hipError_t launch_chunk_bwd(Variant variant, const BwdArgs& a, hipStream_t stream);
 
+// Variational linear attention over whole sequences (T = 1 and the memory and penalty
+// in place: the decode step).
+struct VlaArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* u;        // penalty directions [B,H,T,dk]
+    float inv_lambda0;    // A_0 = I * inv_lambda0 when a0 is nullptr
+    const float* a0;      // [B,H,dk,dk] or nullptr
+    const float* s0;      // [B,H,dv,dk] or nullptr
+    void* o;              // [B,H,T,dv]
+    float* s_out;         // [B,H,dv,dk] or nullptr (may equal s0)
+    float* a_out;         // [B,H,dk,dk] or nullptr (may equal a0)
+    int B, H, T, dk, dv;
+};
+hipError_t launch_vla(bool bf16, const VlaArgs& a, hipStream_t stream);
+
 // float32 storage, fp32 arithmetic (VALU).
 hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t stream);
 // Device workspace the chunk kernels of (variant, shape, storage) need, in bytes.

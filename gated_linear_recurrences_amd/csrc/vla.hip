@@ -1,0 +1,316 @@
+// Variational linear attention ("Riepilogo Tecnico: Attenzione Lineare Variazionale
+// (VLA)", sections 2.1-2.3): per token, with the inverse penalty A = M^-1 (d_k x d_k)
+// beside the memory S (d_v x d_k),
+//   z = A u,  A <- A - z z^T / (1 + u.z)     Sherman-Morrison for M <- M + u u^T
+//   a = A k^ / |A k^|,  k^ = k / |k|          normalised gating vector (updated A)
+//   S <- S + (v - S k^) a^T,  o = S q         residual write, read after write.
+//
+// The update is sequential and O(d^2) per token with no dense contraction in it (every
+// product is a matrix times one vector), so it runs on the VALU in fp32, all tokens of
+// a sequence in one launch: one workgroup per (sequence, head) keeps A and S in
+// registers for the whole sequence. Waves 0 .. d_k/16-1 own 16 rows of A each, the
+// other d_v/16 waves 16 rows of S each; lane (r = lane & 15, g = lane >> 4) holds row
+// 16w + r, key columns [g d_k/4, (g+1) d_k/4), so a row's dot products meet across
+// the four lanes of equal r with two shuffles.
+//
+// Per token t (one workgroup barrier):
+//   A waves, before the barrier: z_m = A_m.u and (A k^)_m for their rows, to LDS;
+//   barrier;
+//   A waves: u.z, z.k^ and |A_t k^|^2 from the LDS vectors (column slices + shuffles),
+//   the rank-1 update of their rows, and a_t to LDS;
+//   S waves, one token behind: token t-1 with a_{t-1} (published by this barrier).
+// LDS vectors are double-buffered by token parity, so no second barrier is needed.
+// q, k, u, v are staged through LDS in blocks of 16 tokens, two blocks deep: each
+// thread loads one 16-byte piece of block b+1 at the start of block b and writes it to
+// LDS eight tokens later, so the load latency hides behind eight tokens of work.
+//
+// One token with the memory and the penalty updated in place (the decode step) is the
+// same kernel with T = 1.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace glr {
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kVlaBlock = 16;   // tokens per staged block
+
+template <typename TS, int DK, int DV>
+struct VlaShape {
+    static constexpr int NA = DK / 16;                 // waves holding A
+    static constexpr int NS = DV / 16;                 // waves holding S
+    static constexpr int NT = 64 * (NA + NS);
+    static constexpr int NCOL = DK / 4;                // key columns per lane
+    static constexpr int EPP = 16 / static_cast<int>(sizeof(TS));   // elements per 16-byte piece
+    static constexpr int PK = kVlaBlock * DK / EPP;    // pieces of one block of q, k or u
+    static constexpr int PV = kVlaBlock * DV / EPP;    // pieces of one block of v
+    static constexpr int PTOT = 3 * PK + PV;
+    static constexpr int PER = (PTOT + NT - 1) / NT;   // pieces per thread
+    static constexpr int SLOT = kVlaBlock * (3 * DK + DV);   // elements of one staged block
+};
+
+template <typename TS> __device__ __forceinline__ f32x4 lds4(const TS* p);
+template <> __device__ __forceinline__ f32x4 lds4<float>(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+template <> __device__ __forceinline__ f32x4 lds4<unsigned short>(const unsigned short* p) {
+    const u16x4 h = *reinterpret_cast<const u16x4*>(p);
+    return f32x4{bf16_bits_to_f32(h[0]), bf16_bits_to_f32(h[1]), bf16_bits_to_f32(h[2]), bf16_bits_to_f32(h[3])};
+}
+
+// sum over the four lanes of equal (lane & 15): one row's partial dot products
+__device__ __forceinline__ float row_sum(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+template <typename TS, int DK, int DV>
+__global__ __launch_bounds__((VlaShape<TS, DK, DV>::NT))
+void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v,
+                const TS* __restrict__ u, float inv_lambda0, const float* a0, const float* s0,
+                TS* __restrict__ o, float* s_out, float* a_out, int T) {
+    using Sh = VlaShape<TS, DK, DV>;
+    constexpr int TB = kVlaBlock, NCOL = Sh::NCOL, NQ = NCOL / 4, NT = Sh::NT;
+    constexpr int OK = TB * DK, OU = 2 * TB * DK, OV = 3 * TB * DK;   // offsets in a staged block
+    __shared__ __align__(16) TS sblk[2][Sh::SLOT];
+    __shared__ __align__(16) float sz[2][DK];   // z = A_{t-1} u
+    __shared__ __align__(16) float sy[2][DK];   // A_{t-1} k^
+    __shared__ __align__(16) float sa[2][DK];   // gating vector a_t
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int c0 = g * NCOL;
+    const bool is_a = wave < Sh::NA;
+    const int m = 16 * (is_a ? wave : wave - Sh::NA) + r16;   // row of A (key) or of S (value)
+    const int64_t bh = blockIdx.x;
+    const TS* qg = q + bh * T * DK;
+    const TS* kg = k + bh * T * DK;
+    const TS* ug = u + bh * T * DK;
+    const TS* vg = v + bh * T * DV;
+    TS* og = o + bh * T * DV;
+
+    // ---- this lane's slice of A (identity / lambda0 unless handed over) or of S
+    float x[NCOL];
+    {
+        const float* src = is_a ? (a0 ? a0 + (bh * DK + m) * DK + c0 : nullptr)
+                                : (s0 ? s0 + (bh * DV + m) * DK + c0 : nullptr);
+        if (src) {
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const f32x4 w = *reinterpret_cast<const f32x4*>(src + 4 * i);
+                x[4 * i] = w[0]; x[4 * i + 1] = w[1]; x[4 * i + 2] = w[2]; x[4 * i + 3] = w[3];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NCOL; ++c) x[c] = (is_a && m == c0 + c) ? inv_lambda0 : 0.f;
+        }
+    }
+
+    // ---- token blocks: piece p of a block is q, k, u or v by range, at element p * EPP of
+    // the staged block; tokens past the end read the sequence's first piece (never used)
+    u32x4 pend[Sh::PER];
+    auto fetch_block = [&](int blk) {
+        const int t0 = blk * TB;
+#pragma unroll
+        for (int i = 0; i < Sh::PER; ++i) {
+            int p = tid + i * NT;
+            if (Sh::PTOT % NT != 0 && p >= Sh::PTOT) p = 0;
+            const TS* src;
+            int d, e;
+            if (p < Sh::PK) { src = qg; d = DK; e = p * Sh::EPP; }
+            else if (p < 2 * Sh::PK) { src = kg; d = DK; e = (p - Sh::PK) * Sh::EPP; }
+            else if (p < 3 * Sh::PK) { src = ug; d = DK; e = (p - 2 * Sh::PK) * Sh::EPP; }
+            else { src = vg; d = DV; e = (p - 3 * Sh::PK) * Sh::EPP; }
+            const int j = e / d;
+            const int64_t off = (t0 + j < T) ? static_cast<int64_t>(t0) * d + e : 0;
+            pend[i] = *reinterpret_cast<const u32x4*>(src + off);
+        }
+    };
+    auto stage_block = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < Sh::PER; ++i) {
+            const int p = tid + i * NT;
+            if (Sh::PTOT % NT == 0 || p < Sh::PTOT)
+                *reinterpret_cast<u32x4*>(&sblk[slot][p * Sh::EPP]) = pend[i];
+        }
+    };
+
+    if (T > 0) {
+        fetch_block(0);
+        stage_block(0);
+    }
+    lds_barrier();
+
+    for (int t = 0; t <= T; ++t) {
+        // block b + 1 is requested at the first token of block b and staged at its ninth
+        if ((t & (TB - 1)) == 0 && t + TB < T) fetch_block(t / TB + 1);
+        if ((t & (TB - 1)) == TB / 2 && t + TB / 2 < T) stage_block((t / TB + 1) & 1);
+        const int par = t & 1;
+        float zm = 0.f, rk = 0.f;
+        if (is_a && t < T) {
+            const TS* blk = sblk[(t / TB) & 1];
+            const int j = t & (TB - 1);
+            const TS* kr = blk + OK + j * DK + c0;
+            const TS* ur = blk + OU + j * DK + c0;
+            float zp = 0.f, yp = 0.f, kn = 0.f;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const f32x4 kk = lds4(kr + 4 * i), uu = lds4(ur + 4 * i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    zp += x[4 * i + e] * uu[e];
+                    yp += x[4 * i + e] * kk[e];
+                    kn += kk[e] * kk[e];
+                }
+            }
+            zm = row_sum(zp);
+            yp = row_sum(yp);
+            rk = __builtin_amdgcn_rsqf(row_sum(kn));
+            if (g == 0) {
+                sz[par][m] = zm;
+                sy[par][m] = yp * rk;
+            }
+        }
+        lds_barrier();
+        if (is_a) {
+            if (t < T) {
+                const TS* blk = sblk[(t / TB) & 1];
+                const int j = t & (TB - 1);
+                const TS* kr = blk + OK + j * DK + c0;
+                const TS* ur = blk + OU + j * DK + c0;
+                const float* zv = &sz[par][c0];
+                const float* yv = &sy[par][c0];
+                float dp = 0.f, zkp = 0.f;
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    const f32x4 zz = *reinterpret_cast<const f32x4*>(zv + 4 * i);
+                    const f32x4 kk = lds4(kr + 4 * i), uu = lds4(ur + 4 * i);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dp += uu[e] * zz[e];
+                        zkp += zz[e] * kk[e];
+                    }
+                }
+                const float rden = 1.f / (1.f + row_sum(dp));
+                const float zk = row_sum(zkp) * rk * rden;   // (z . k^) / (1 + u.z)
+                // A_t k^ = A_{t-1} k^ - z (z . k^) / (1 + u.z)
+                float ny = 0.f;
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    const f32x4 zz = *reinterpret_cast<const f32x4*>(zv + 4 * i);
+                    const f32x4 yy = *reinterpret_cast<const f32x4*>(yv + 4 * i);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float yc = yy[e] - zz[e] * zk;
+                        ny += yc * yc;
+                    }
+                }
+                const float ra = __builtin_amdgcn_rsqf(row_sum(ny));
+                const float f = zm * rden;
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    const f32x4 zz = *reinterpret_cast<const f32x4*>(zv + 4 * i);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[4 * i + e] -= f * zz[e];
+                }
+                if (wave == 0 && r16 == 0) {
+#pragma unroll
+                    for (int i = 0; i < NQ; ++i) {
+                        const f32x4 zz = *reinterpret_cast<const f32x4*>(zv + 4 * i);
+                        const f32x4 yy = *reinterpret_cast<const f32x4*>(yv + 4 * i);
+                        f32x4 out;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = (yy[e] - zz[e] * zk) * ra;
+                        *reinterpret_cast<f32x4*>(&sa[par][c0 + 4 * i]) = out;
+                    }
+                }
+            }
+        } else if (t > 0) {
+            // the memory, one token behind: token t - 1 with a_{t-1}
+            const int ts = t - 1;
+            const TS* blk = sblk[(ts / TB) & 1];
+            const int j = ts & (TB - 1);
+            const TS* kr = blk + OK + j * DK + c0;
+            const TS* qr = blk + j * DK + c0;
+            const float vm = Store<TS>::load(blk + OV + j * DV, m);
+            float ep = 0.f, kn = 0.f;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const f32x4 kk = lds4(kr + 4 * i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ep += x[4 * i + e] * kk[e];
+                    kn += kk[e] * kk[e];
+                }
+            }
+            const float d = vm - row_sum(ep) * __builtin_amdgcn_rsqf(row_sum(kn));   // v_m - (S k^)_m
+            const float* av = &sa[ts & 1][c0];
+            float op = 0.f;
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const f32x4 aa = *reinterpret_cast<const f32x4*>(av + 4 * i);
+                const f32x4 qq = lds4(qr + 4 * i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[4 * i + e] += d * aa[e];
+                    op += x[4 * i + e] * qq[e];
+                }
+            }
+            op = row_sum(op);
+            if (g == 0) Store<TS>::store(og, static_cast<int64_t>(ts) * DV + m, op);
+        }
+    }
+
+    float* dst = is_a ? (a_out ? a_out + (bh * DK + m) * DK + c0 : nullptr)
+                      : (s_out ? s_out + (bh * DV + m) * DK + c0 : nullptr);
+    if (dst) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i)
+            *reinterpret_cast<f32x4*>(dst + 4 * i) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+    }
+}
+
+template <typename TS, int DK, int DV>
+hipError_t launch_shape(const VlaArgs& a, hipStream_t stream) {
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    hipLaunchKernelGGL((vla_kernel<TS, DK, DV>), dim3(static_cast<unsigned>(heads)), dim3(VlaShape<TS, DK, DV>::NT), 0,
+                       stream, static_cast<const TS*>(a.q), static_cast<const TS*>(a.k), static_cast<const TS*>(a.v),
+                       static_cast<const TS*>(a.u), a.inv_lambda0, a.a0, a.s0, static_cast<TS*>(a.o), a.s_out,
+                       a.a_out, a.T);
+    return hipGetLastError();
+}
+
+template <typename TS, int DK>
+hipError_t launch_dk(const VlaArgs& a, hipStream_t stream) {
+    switch (a.dv) {
+        case 16: return launch_shape<TS, DK, 16>(a, stream);
+        case 32: return launch_shape<TS, DK, 32>(a, stream);
+        case 64: return launch_shape<TS, DK, 64>(a, stream);
+        case 128: return launch_shape<TS, DK, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename TS>
+hipError_t launch_typed(const VlaArgs& a, hipStream_t stream) {
+    if (static_cast<int64_t>(a.B) * a.H == 0) return hipSuccess;
+    switch (a.dk) {
+        case 16: return launch_dk<TS, 16>(a, stream);
+        case 32: return launch_dk<TS, 32>(a, stream);
+        case 64: return launch_dk<TS, 64>(a, stream);
+        case 128: return launch_dk<TS, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_vla(bool bf16, const VlaArgs& a, hipStream_t stream) {
+    return bf16 ? launch_typed<unsigned short>(a, stream) : launch_typed<float>(a, stream);
+}
+
+}  // namespace glr

@@ -257,6 +257,8 @@ CONFIGS = {
                                 dtype="bf16", seed=5),
     "mamba2_b8h16_t4096_d128": dict(kind="mamba2", B=8, H=16, T=4096, dk=128, dv=128, chunk=64,
                                     dtype="bf16", seed=6),
+    "vla_b8h16_t4096_d128": dict(kind="vla", B=8, H=16, T=4096, dk=128, dv=128, chunk=0, dtype="bf16",
+                                 seed=8),
 }
 
 
@@ -280,6 +282,8 @@ def config_inputs(name, *, steps=None, T=None):
     if kind == "mamba2":
         return mamba2_inputs(c["B"], c["H"], Tn, c["dk"], c["dv"], chunk=c["chunk"],
                              dtype=c["dtype"], seed=seed)
+    if kind == "vla":
+        return vla_inputs(c["B"], c["H"], Tn, c["dk"], c["dv"], dtype=c["dtype"], seed=seed)
     if kind == "gdelta":
         return gdelta_inputs(c["B"], c["H"], Tn, c["dk"], c["dv"], chunk=c["chunk"],
                              dtype=c["dtype"], seed=seed)

@@ -257,6 +257,39 @@ la_status mamba2_chunk_bwd(const void* q, const void* k, const void* v, const fl
                            int B, int H, int T, int dk, int dv, int chunk,
                            la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Variational linear attention over whole sequences ("Riepilogo Tecnico:
+ * Attenzione Lineare Variazionale (VLA)", sections 2.1-2.3), token by token
+ * in one launch.  Per (b, h) and token t, with the inverse penalty A (d_k x d_k)
+ * beside the memory S:
+ *     z = A u_t;  A <- A - z z^T / (1 + u_t . z)        (M <- M + u_t u_t^T)
+ *     a = A k^ / |A k^|,  k^ = k_t / |k_t|
+ *     S <- S + (v_t - S k^) a^T;  o_t = S q_t.
+ * q, k, u [B][H][T][d_k] and v, o [B][H][T][d_v] in `dtype` (u_t is the penalty
+ * direction added at token t); A starts at a0 [B][H][d_k][d_k] float32 or,
+ * when a0 is NULL, at I / lambda0 (lambda0 > 0 and finite); S at s0
+ * [B][H][d_v][d_k] float32 or zeros.  s_out and a_out (float32, optional)
+ * receive the final S and A; s_out may equal s0 and a_out may equal a0.
+ * Arithmetic is fp32 throughout.  A zero key (|k_t| = 0) gives NaN, which
+ * propagates.  B, H or T == 0 is valid (outputs s0/a0 or their defaults).
+ * d_k, d_v in {16, 32, 64, 128} (LA_ERR_UNSUPPORTED otherwise).  Pointers
+ * 16-byte aligned; no workspace.  Errors as for la_chunk_fwd.
+ */
+la_status vla_fwd(const void* q, const void* k, const void* v, const void* u,
+                  float lambda0, const float* a0, const float* s0,
+                  void* o, float* s_out, float* a_out,
+                  int B, int H, int T, int dk, int dv, la_dtype dtype, void* stream);
+
+/*
+ * One VLA decode token for N sequences x H heads: vla_fwd with T = 1 and the
+ * memory s [N][H][d_v][d_k] and inverse penalty a [N][H][d_k][d_k] (float32)
+ * read and overwritten in place.  q, k, u [N][H][d_k], v and o [N][H][d_v] in
+ * `dtype`.  N == 0 or H == 0 is a no-op.  Errors as for la_recurrent_step.
+ */
+la_status vla_recurrent_step(const void* q, const void* k, const void* v, const void* u,
+                             float* s, float* a, void* o, int N, int H, int dk, int dv,
+                             la_dtype dtype, void* stream);
+
 /* Static text for a status code. */
 const char* la_status_str(la_status status);
 
@@ -266,7 +299,7 @@ const char* la_last_error(void);
 
 /* ABI version: (major << 16) | minor (2.0: workspace arguments; 2.1:
  * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step; 2.3: gdelta_chunk_fwd_fused;
- * 2.4: la_chunk_bwd, mamba2_chunk_bwd). */
+ * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 2
-    assert lib.la_version() & 0xffff >= 4      # 2.1 mamba2, 2.2 gdelta decode, 2.3 fused, 2.4 backward
+    assert lib.la_version() & 0xffff >= 5      # 2.1 mamba2, 2.2 gdelta decode, 2.3 fused, 2.4 backward, 2.5 vla
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -233,3 +233,46 @@ def test_backward_workspace_size(lib):
     assert lib.la_chunk_bwd_workspace_size(4, 8, 2048, 128, 128, 64, 0, ctypes.byref(out)) == _native.LA_ERR_UNSUPPORTED
     assert lib.la_chunk_bwd_workspace_size(0, 8, 2048, 128, 128, 64, 1, ctypes.byref(out)) == _native.LA_OK
     assert out.value == 0
+
+
+def test_vla_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(lam=1.0, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, a0=None, s0=None, o=FAKE, s_out=None, a_out=None, B=2, H=2, T=8,
+                 dk=64, dv=64, dtype=1)
+        a.update(kw)
+        return lib.vla_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["u"]), lam, P(a["a0"]), P(a["s0"]), P(a["o"]),
+                           P(a["s_out"]), P(a["a_out"]), a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], None)
+
+    assert call(u=None) == _native.LA_ERR_INVALID
+    assert b"u is NULL" in lib.la_last_error()
+    assert call(lam=0.0) == _native.LA_ERR_INVALID
+    assert b"lambda0" in lib.la_last_error()
+    assert call(lam=float("nan")) == _native.LA_ERR_INVALID
+    assert call(lam=float("inf")) == _native.LA_ERR_INVALID
+    assert call(a0=MISALIGNED) == _native.LA_ERR_INVALID
+    assert call(s_out=MISALIGNED) == _native.LA_ERR_INVALID
+    assert call(T=-1) == _native.LA_ERR_INVALID
+    assert call(dk=48) == _native.LA_ERR_UNSUPPORTED
+    assert call(dv=256) == _native.LA_ERR_UNSUPPORTED
+    assert call(dtype=2) == _native.LA_ERR_INVALID
+    assert call(B=0, q=None, k=None, v=None, u=None, o=None) == _native.LA_OK
+    assert call(lam=0.0, B=0, q=None, k=None, v=None, u=None, o=None, a0=FAKE) == _native.LA_OK
+
+
+def test_vla_decode_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, s=FAKE, a=FAKE, o=FAKE, N=4, H=2, dk=128, dv=128, dtype=1)
+        a.update(kw)
+        return lib.vla_recurrent_step(P(a["q"]), P(a["k"]), P(a["v"]), P(a["u"]), P(a["s"]), P(a["a"]), P(a["o"]),
+                                      a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+    assert call(a=None) == _native.LA_ERR_INVALID
+    assert b"a is NULL" in lib.la_last_error()
+    assert call(u=MISALIGNED) == _native.LA_ERR_INVALID
+    assert call(H=-1) == _native.LA_ERR_INVALID
+    assert call(dv=8) == _native.LA_ERR_UNSUPPORTED
+    assert call(N=0, q=None, k=None, v=None, u=None, s=None, a=None, o=None) == _native.LA_OK
