@@ -17,8 +17,9 @@ one call, snapshots included; ``mfma`` gives the same run against the dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on the host; ``others``
 reports the per-channel-gate (GLA), gated-delta, scalar data-dependent decay
 and decode (per-channel gate, gated delta rule) workloads measured the same way,
-the gated delta rule with its feature map and output norm fused in, and the
-backward of the retention and scalar-decay workloads (beside their forward).
+the gated delta rule with its feature map and output norm fused in, the
+backward of the retention and scalar-decay workloads (beside their forward), and
+variational linear attention (whole sequences, and decode).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
     python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
@@ -247,6 +248,69 @@ def bench_gdelta_fused(steps, warmup, torch, api, synthetic, dev):
     ms_u = time_calls([unfused], steps, warmup, torch)[1]
     return dict(workload="gdelta_fused_b4h16_t8192_d128", kernel_ms=ms_f, unfused_torch_ms=ms_u,
                 tokens_per_s=B * H * T / (ms_f * 1e-3), speedup_vs_unfused=ms_u / ms_f)
+
+
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
+
+
+def bench_vla(steps, warmup, torch, api, synthetic, dev):
+    """Variational linear attention over B8 H16 T4096 d128 (bf16 tokens, fp32 arithmetic): one
+    vla_fwd call per step. Algorithmic flops per token-head 6 d_k^2 + 6 d_v d_k (A u, the
+    rank-1 update and A k^; S k^, the write and S q), priced against the fp32 vector peak."""
+    name = "vla_b8h16_t4096_d128"
+    c = synthetic.CONFIGS[name]
+    B, H, T, dk, dv = c["B"], c["H"], c["T"], c["dk"], c["dv"]
+    w = synthetic.config_inputs(name)
+    b = upload(w, torch, dev)
+    uu = torch.from_numpy(w.u).to(dev).to(torch.bfloat16).contiguous()
+    del w
+    o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    s_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    a_out = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+
+    def call():
+        api.vla_fwd(b["q"], b["k"], b["v"], uu, lambda0=1.0, o=o, s_out=s_out, a_out=a_out)
+
+    ms = time_calls([call], steps, warmup, torch)[1]
+    th = B * H * T
+    flops = th * (6 * dk * dk + 6 * dv * dk)
+    return dict(workload=name, kernel_ms=ms, tokens_per_s=th / (ms * 1e-3), alg_gflop=flops / 1e9,
+                fp32_tflops=flops / (ms * 1e-3) / 1e12,
+                fp32_valu_frac=flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                heads=B * H, note="one workgroup per (sequence, head): 128 of 256 CUs")
+
+
+def bench_vla_decode(steps_total, torch, api, synthetic, dev):
+    """VLA decode at the decode workload's shape (512 sequences x 32 heads, d = 128): the fp32
+    memory and inverse penalty updated in place, a fresh bf16 token per step drawn on the
+    device (q, k, u ~ N(0,1)/sqrt(d), v ~ N(0,1)); ``steps_total`` steps timed as one region."""
+    N, H, d = 512, 32, 128
+    w = synthetic.vla_decode_inputs(N, H, d, d, steps=0, seed=9)
+    s = torch.from_numpy(w.s0).to(dev)
+    a = torch.from_numpy(w.a0).to(dev)
+    del w
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    sc = 1.0 / np.sqrt(d)
+    q = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * sc).to(torch.bfloat16)
+    k = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * sc).to(torch.bfloat16)
+    u = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * sc).to(torch.bfloat16)
+    v = torch.randn((steps_total, N, H, d), generator=gen, device=dev).to(torch.bfloat16)
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+    for i in range(3):
+        api.vla_recurrent_step(q[i], k[i], v[i], u[i], s, a, o=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps_total):
+        api.vla_recurrent_step(q[i], k[i], v[i], u[i], s, a, o=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps_total
+    bytes_step = N * H * (2 * (d * d + d * d) * 4 + 4 * d * 2 + d * 2)
+    return dict(workload="vla_decode_n512h32_d128", steps=steps_total, us_per_step=ms * 1e3,
+                hbm_gbs=bytes_step / (ms * 1e-3) / 1e9, hbm_frac=bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                alg_bytes_per_step=bytes_step)
 
 
 def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
@@ -503,6 +567,10 @@ def main():
             others[name + "_bwd"] = bench_backward(name, max(20, args.steps // 4), max(3, args.warmup // 4), torch,
                                                    api, synthetic, dev)
             torch.cuda.empty_cache()
+        others["vla_b8h16_t4096_d128"] = bench_vla(max(5, args.steps // 40), 1, torch, api, synthetic, dev)
+        torch.cuda.empty_cache()
+        others["vla_decode_n512h32_d128"] = bench_vla_decode(min(args.decode_steps, 50), torch, api, synthetic, dev)
+        torch.cuda.empty_cache()
 
     cfg = synthetic.CONFIGS[MAIN]
     out = {

@@ -94,6 +94,33 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Sum over each row of 16 lanes with DPP moves (no LDS crossbar): quad swaps, then the
+// half-row and row mirrors; every lane of the row receives the row's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __uint_as_float(static_cast<unsigned>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(x)), CTRL, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_move<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_move<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_move<0x141>(x);   // row_half_mirror
+    x += dpp_move<0x140>(x);   // row_mirror
+    return x;
+}
+
+// Sum over the four rows of 16 lanes (lanes of equal lane & 15) with the gfx950 row
+// swaps: each swap leaves a lane holding its own value and its partner row's.
+__device__ __forceinline__ float cross_row_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Sum over all 64 lanes, received by every lane.
+__device__ __forceinline__ float wave_sum(float x) { return cross_row_sum(row16_sum(x)); }
+
 // Inclusive prefix sum across the 64 lanes of a wavefront (Hillis-Steele).
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
     const int lane = threadIdx.x & 63;

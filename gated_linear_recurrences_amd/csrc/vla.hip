@@ -14,15 +14,18 @@
 // the four lanes of equal r with two shuffles.
 //
 // Per token t (one workgroup barrier):
-//   A waves, before the barrier: z_m = A_m.u and (A k^)_m for their rows, to LDS;
+//   A waves, before the barrier: (A u)_m and (A k)_m for their rows, to LDS;
 //   barrier;
-//   A waves: u.z, z.k^ and |A_t k^|^2 from the LDS vectors (column slices + shuffles),
-//   the rank-1 update of their rows, and a_t to LDS;
+//   A waves: |k|^2, u.z and z.k^ over the whole vectors (two columns per lane and a
+//   wave-wide sum: the same in every wave), A_t k^ and its norm the same way, the
+//   rank-1 update of their rows; wave 0 publishes a_t;
 //   S waves, one token behind: token t-1 with a_{t-1} (published by this barrier).
 // LDS vectors are double-buffered by token parity, so no second barrier is needed.
-// q, k, u, v are staged through LDS in blocks of 16 tokens, two blocks deep: each
-// thread loads one 16-byte piece of block b+1 at the start of block b and writes it to
-// LDS eight tokens later, so the load latency hides behind eight tokens of work.
+// q, k, u, v are staged through LDS as fp32 in blocks of 16 tokens, two blocks deep:
+// each thread loads one 16-byte piece of block b+1 at the start of block b and writes it
+// to LDS eight tokens later, so the load latency hides behind eight tokens of work.
+// Sums over a row's four lane groups use the gfx950 row swaps (v_permlane16/32_swap),
+// sums over a row of 16 lanes DPP moves: no LDS crossbar round trips.
 //
 // One token with the memory and the penalty updated in place (the decode step) is the
 // same kernel with T = 1.
@@ -51,22 +54,6 @@ struct VlaShape {
     static constexpr int SLOT = kVlaBlock * (3 * DK + DV);   // elements of one staged block
 };
 
-template <typename TS> __device__ __forceinline__ f32x4 lds4(const TS* p);
-template <> __device__ __forceinline__ f32x4 lds4<float>(const float* p) {
-    return *reinterpret_cast<const f32x4*>(p);
-}
-template <> __device__ __forceinline__ f32x4 lds4<unsigned short>(const unsigned short* p) {
-    const u16x4 h = *reinterpret_cast<const u16x4*>(p);
-    return f32x4{bf16_bits_to_f32(h[0]), bf16_bits_to_f32(h[1]), bf16_bits_to_f32(h[2]), bf16_bits_to_f32(h[3])};
-}
-
-// sum over the four lanes of equal (lane & 15): one row's partial dot products
-__device__ __forceinline__ float row_sum(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
-}
-
 template <typename TS, int DK, int DV>
 __global__ __launch_bounds__((VlaShape<TS, DK, DV>::NT))
 void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v,
@@ -74,11 +61,13 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
                 TS* __restrict__ o, float* s_out, float* a_out, int T) {
     using Sh = VlaShape<TS, DK, DV>;
     constexpr int TB = kVlaBlock, NCOL = Sh::NCOL, NQ = NCOL / 4, NT = Sh::NT;
+    constexpr int NC64 = (DK + 63) / 64;                               // columns per lane, whole-vector sums
     constexpr int OK = TB * DK, OU = 2 * TB * DK, OV = 3 * TB * DK;   // offsets in a staged block
-    __shared__ __align__(16) TS sblk[2][Sh::SLOT];
+    __shared__ __align__(16) float sblk[2][Sh::SLOT];
     __shared__ __align__(16) float sz[2][DK];   // z = A_{t-1} u
-    __shared__ __align__(16) float sy[2][DK];   // A_{t-1} k^
+    __shared__ __align__(16) float sy[2][DK];   // A_{t-1} k (k not normalised)
     __shared__ __align__(16) float sa[2][DK];   // gating vector a_t
+    __shared__ float srk[2];                    // 1 / |k_t|
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -134,8 +123,19 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
 #pragma unroll
         for (int i = 0; i < Sh::PER; ++i) {
             const int p = tid + i * NT;
-            if (Sh::PTOT % NT == 0 || p < Sh::PTOT)
-                *reinterpret_cast<u32x4*>(&sblk[slot][p * Sh::EPP]) = pend[i];
+            if (Sh::PTOT % NT == 0 || p < Sh::PTOT) {
+                float* dst = &sblk[slot][p * Sh::EPP];
+                const u32x4 r = pend[i];
+                if constexpr (sizeof(TS) == 2) {
+                    // bf16 pairs: the low half of each word is the earlier element
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u),
+                                                           __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xffff0000u)};
+                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{__uint_as_float(r[2] << 16), __uint_as_float(r[2] & 0xffff0000u),
+                                                               __uint_as_float(r[3] << 16), __uint_as_float(r[3] & 0xffff0000u)};
+                } else {
+                    *reinterpret_cast<u32x4*>(dst) = r;
+                }
+            }
         }
     };
 
@@ -150,117 +150,109 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
         if ((t & (TB - 1)) == 0 && t + TB < T) fetch_block(t / TB + 1);
         if ((t & (TB - 1)) == TB / 2 && t + TB / 2 < T) stage_block((t / TB + 1) & 1);
         const int par = t & 1;
-        float zm = 0.f, rk = 0.f;
+        float zm = 0.f;
         if (is_a && t < T) {
-            const TS* blk = sblk[(t / TB) & 1];
+            const float* blk = sblk[(t / TB) & 1];
             const int j = t & (TB - 1);
-            const TS* kr = blk + OK + j * DK + c0;
-            const TS* ur = blk + OU + j * DK + c0;
-            float zp = 0.f, yp = 0.f, kn = 0.f;
+            const float* kr = blk + OK + j * DK + c0;
+            const float* ur = blk + OU + j * DK + c0;
+            float zp = 0.f, yp = 0.f;
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
-                const f32x4 kk = lds4(kr + 4 * i), uu = lds4(ur + 4 * i);
+                const f32x4 kk = *reinterpret_cast<const f32x4*>(kr + 4 * i);
+                const f32x4 uu = *reinterpret_cast<const f32x4*>(ur + 4 * i);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     zp += x[4 * i + e] * uu[e];
                     yp += x[4 * i + e] * kk[e];
-                    kn += kk[e] * kk[e];
                 }
             }
-            zm = row_sum(zp);
-            yp = row_sum(yp);
-            rk = __builtin_amdgcn_rsqf(row_sum(kn));
+            zm = cross_row_sum(zp);
+            yp = cross_row_sum(yp);
             if (g == 0) {
                 sz[par][m] = zm;
-                sy[par][m] = yp * rk;
+                sy[par][m] = yp;
             }
         }
         lds_barrier();
         if (is_a) {
             if (t < T) {
-                const TS* blk = sblk[(t / TB) & 1];
+                const float* blk = sblk[(t / TB) & 1];
                 const int j = t & (TB - 1);
-                const TS* kr = blk + OK + j * DK + c0;
-                const TS* ur = blk + OU + j * DK + c0;
-                const float* zv = &sz[par][c0];
-                const float* yv = &sy[par][c0];
-                float dp = 0.f, zkp = 0.f;
+                // whole-vector sums: columns lane, lane + 64
+                float zc[NC64], yc[NC64];
+                float kn = 0.f, uz = 0.f, zkr = 0.f;
 #pragma unroll
-                for (int i = 0; i < NQ; ++i) {
-                    const f32x4 zz = *reinterpret_cast<const f32x4*>(zv + 4 * i);
-                    const f32x4 kk = lds4(kr + 4 * i), uu = lds4(ur + 4 * i);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        dp += uu[e] * zz[e];
-                        zkp += zz[e] * kk[e];
+                for (int i = 0; i < NC64; ++i) {
+                    const int c = lane + 64 * i;
+                    zc[i] = yc[i] = 0.f;
+                    if (DK % 64 == 0 || c < DK) {
+                        const float kc = blk[OK + j * DK + c], uc = blk[OU + j * DK + c];
+                        zc[i] = sz[par][c];
+                        yc[i] = sy[par][c];
+                        kn += kc * kc;
+                        uz += uc * zc[i];
+                        zkr += zc[i] * kc;
                     }
                 }
-                const float rden = 1.f / (1.f + row_sum(dp));
-                const float zk = row_sum(zkp) * rk * rden;   // (z . k^) / (1 + u.z)
+                const float rk = __builtin_amdgcn_rsqf(wave_sum(kn));
+                const float rden = 1.f / (1.f + wave_sum(uz));
+                const float zk = wave_sum(zkr) * rk * rden;   // (z . k^) / (1 + u.z)
                 // A_t k^ = A_{t-1} k^ - z (z . k^) / (1 + u.z)
                 float ny = 0.f;
 #pragma unroll
-                for (int i = 0; i < NQ; ++i) {
-                    const f32x4 zz = *reinterpret_cast<const f32x4*>(zv + 4 * i);
-                    const f32x4 yy = *reinterpret_cast<const f32x4*>(yv + 4 * i);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float yc = yy[e] - zz[e] * zk;
-                        ny += yc * yc;
-                    }
+                for (int i = 0; i < NC64; ++i) {
+                    yc[i] = yc[i] * rk - zc[i] * zk;
+                    ny += yc[i] * yc[i];
                 }
-                const float ra = __builtin_amdgcn_rsqf(row_sum(ny));
+                const float ra = __builtin_amdgcn_rsqf(wave_sum(ny));
+                if (wave == 0) {
+#pragma unroll
+                    for (int i = 0; i < NC64; ++i) {
+                        const int c = lane + 64 * i;
+                        if (DK % 64 == 0 || c < DK) sa[par][c] = yc[i] * ra;
+                    }
+                    if (lane == 0) srk[par] = rk;
+                }
+                // rank-1 update of this lane's row slice
                 const float f = zm * rden;
+                const float* zv = &sz[par][c0];
 #pragma unroll
                 for (int i = 0; i < NQ; ++i) {
                     const f32x4 zz = *reinterpret_cast<const f32x4*>(zv + 4 * i);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[4 * i + e] -= f * zz[e];
                 }
-                if (wave == 0 && r16 == 0) {
-#pragma unroll
-                    for (int i = 0; i < NQ; ++i) {
-                        const f32x4 zz = *reinterpret_cast<const f32x4*>(zv + 4 * i);
-                        const f32x4 yy = *reinterpret_cast<const f32x4*>(yv + 4 * i);
-                        f32x4 out;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) out[e] = (yy[e] - zz[e] * zk) * ra;
-                        *reinterpret_cast<f32x4*>(&sa[par][c0 + 4 * i]) = out;
-                    }
-                }
             }
         } else if (t > 0) {
             // the memory, one token behind: token t - 1 with a_{t-1}
             const int ts = t - 1;
-            const TS* blk = sblk[(ts / TB) & 1];
+            const float* blk = sblk[(ts / TB) & 1];
             const int j = ts & (TB - 1);
-            const TS* kr = blk + OK + j * DK + c0;
-            const TS* qr = blk + j * DK + c0;
-            const float vm = Store<TS>::load(blk + OV + j * DV, m);
-            float ep = 0.f, kn = 0.f;
+            const float* kr = blk + OK + j * DK + c0;
+            const float* qr = blk + j * DK + c0;
+            const float vm = blk[OV + j * DV + m];
+            float ep = 0.f;
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
-                const f32x4 kk = lds4(kr + 4 * i);
+                const f32x4 kk = *reinterpret_cast<const f32x4*>(kr + 4 * i);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ep += x[4 * i + e] * kk[e];
-                    kn += kk[e] * kk[e];
-                }
+                for (int e = 0; e < 4; ++e) ep += x[4 * i + e] * kk[e];
             }
-            const float d = vm - row_sum(ep) * __builtin_amdgcn_rsqf(row_sum(kn));   // v_m - (S k^)_m
+            const float d = vm - cross_row_sum(ep) * srk[ts & 1];   // v_m - (S k^)_m
             const float* av = &sa[ts & 1][c0];
             float op = 0.f;
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 const f32x4 aa = *reinterpret_cast<const f32x4*>(av + 4 * i);
-                const f32x4 qq = lds4(qr + 4 * i);
+                const f32x4 qq = *reinterpret_cast<const f32x4*>(qr + 4 * i);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     x[4 * i + e] += d * aa[e];
                     op += x[4 * i + e] * qq[e];
                 }
             }
-            op = row_sum(op);
+            op = cross_row_sum(op);
             if (g == 0) Store<TS>::store(og, static_cast<int64_t>(ts) * DV + m, op);
         }
     }
