@@ -14,9 +14,10 @@
 // and, since every term of o_t carries e^(B_t) and every write of token j carries
 // e^(-B_j) (B the cumulative log-gate over the sequence), the gate's gradient is
 //   d log a_t = sum_{s >= t} (q_s . dq_s - k_s . dk_s) + <dS_T, S_T>.
-// The call runs four kernels: the forward state pass (snapshots S_in, final memory),
+// The call runs four passes: the forward state pass (snapshots S_in, final memory),
 // the same pass walked backwards on (q, dO) (snapshots R, gradient of S_0), the
-// gradient pass below (chunk-parallel), and the gate pass.
+// gradient pass below (chunk-parallel), and the gate pass (one kernel per sequence,
+// plus a sum over the batch for a fixed gate).
 //
 // Gradient pass (gfx950): one workgroup of eight waves per (sequence, chunk). q, k, v,
 // dO are staged token-major; A1 = (Q K^T) . M and A2 = (dO V^T) . M are formed on MFMA
@@ -317,61 +318,73 @@ void grad_kernel(GradParams p) {
     }
 }
 
-// Gate gradients from the per-token sums: scalar gates d log a_t = sum_{s>=t} gq_s + <dS_T, S_T>
-// per sequence (one workgroup each); a fixed gate the sum of those over the tokens and the
-// batch of its head, sum_b [sum_s (s + 1) gq_s + T <dS_T, S_T>] (one workgroup per head).
+// Gate gradients from the per-token sums g_s = q_s.dq_s - k_s.dk_s, one workgroup of 256
+// threads per sequence: scalar gates d log a_t = sum_{s>=t} g_s + <dS_T, S_T> (a reverse
+// scan: each thread a contiguous run of tokens, run totals joined by wave scans and the
+// four wave totals); a fixed gate the sequence's share sum_s (s + 1) g_s + T <dS_T, S_T>,
+// left in g_0 of the sequence for gate_head_sum_kernel, which adds the batch up per head
+// (in batch order: no atomics).
 template <bool SCALAR>
 __global__ __launch_bounds__(256)
-void gate_grad_kernel(const float* __restrict__ gq, const float* __restrict__ ds_out, const float* __restrict__ s_fin,
-                      float* __restrict__ dgate, int B, int H, int T, int dsz) {
-    __shared__ float red[256];
-    __shared__ float carry_in[256];
-    const int tid = threadIdx.x;
+void gate_grad_kernel(float* __restrict__ gq, const float* __restrict__ ds_out, const float* __restrict__ s_fin,
+                      float* __restrict__ dgate, int T, int dsz) {
+    __shared__ float wred[4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t bh = blockIdx.x;
     auto block_sum = [&](float x) {
-        red[tid] = x;
+        x = wave_sum(x);
+        if (lane == 0) wred[w] = x;
         __syncthreads();
-        for (int s = 128; s > 0; s >>= 1) {
-            if (tid < s) red[tid] += red[tid + s];
-            __syncthreads();
-        }
-        const float r = red[0];
+        const float r = wred[0] + wred[1] + wred[2] + wred[3];
         __syncthreads();
         return r;
     };
-    auto final_dot = [&](int64_t bh) {
-        if (ds_out == nullptr) return 0.f;
+    float fin = 0.f;
+    if (ds_out != nullptr) {
+        const f32x4* a = reinterpret_cast<const f32x4*>(ds_out + bh * dsz);
+        const f32x4* b = reinterpret_cast<const f32x4*>(s_fin + bh * dsz);
         float x = 0.f;
-        for (int e = tid; e < dsz; e += 256) x += ds_out[bh * dsz + e] * s_fin[bh * dsz + e];
-        return block_sum(x);
-    };
+#pragma unroll 4
+        for (int e = tid; e < dsz / 4; e += 256) {
+            const f32x4 p = a[e], r = b[e];
+            x += p[0] * r[0] + p[1] * r[1] + p[2] * r[2] + p[3] * r[3];
+        }
+        fin = block_sum(x);
+    }
+    float* g = gq + bh * T;
+    const int per = (T + 255) / 256;
+    const int lo = (tid * per < T) ? tid * per : T, hi = (lo + per < T) ? lo + per : T;
     if constexpr (SCALAR) {
-        const int64_t bh = blockIdx.x;
-        const float fin = final_dot(bh);
-        // reverse cumulative sum over T: thread tid owns a contiguous run of tokens
-        const int per = (T + 255) / 256;
-        const int lo = tid * per, hi = (lo + per < T) ? lo + per : T;
         float run = 0.f;
-        for (int t = lo; t < hi; ++t) run += gq[bh * T + t];
-        carry_in[tid] = run;
+        for (int t = lo; t < hi; ++t) run += g[t];
+        // sum of the runs after this thread's: the rest of its wave, then the later waves
+        const float incl = wave_inclusive_scan(run);
+        const float wtot = __shfl(incl, 63, 64);
+        if (lane == 0) wred[w] = wtot;
         __syncthreads();
-        float after = 0.f;   // sum of the runs of the threads after this one
-        for (int u = tid + 1; u < 256; ++u) after += carry_in[u];
+        float after = wtot - incl;
+        for (int u = w + 1; u < 4; ++u) after += wred[u];
         float acc = after + fin;
         for (int t = hi - 1; t >= lo; --t) {
-            acc += gq[bh * T + t];
+            acc += g[t];
             dgate[bh * T + t] = acc;
         }
     } else {
-        const int h = blockIdx.x;
-        float tot = 0.f;
-        for (int b = 0; b < B; ++b) {
-            const int64_t bh = static_cast<int64_t>(b) * H + h;
-            float x = 0.f;
-            for (int t = tid; t < T; t += 256) x += static_cast<float>(t + 1) * gq[bh * T + t];
-            tot += block_sum(x) + static_cast<float>(T) * final_dot(bh);
-        }
-        if (tid == 0) dgate[h] = tot;
+        float x = 0.f;
+        for (int t = lo; t < hi; ++t) x += static_cast<float>(t + 1) * g[t];
+        const float part = block_sum(x) + static_cast<float>(T) * fin;
+        if (tid == 0 && T > 0) g[0] = part;   // every read of g in this workgroup is done
     }
+}
+
+static __global__ __launch_bounds__(256)
+void gate_head_sum_kernel(const float* __restrict__ gq, float* __restrict__ dgate, int B, int H, int T) {
+    const int h = blockIdx.x * 256 + threadIdx.x;
+    if (h >= H) return;
+    float tot = 0.f;
+    if (T > 0)
+        for (int b = 0; b < B; ++b) tot += gq[(static_cast<int64_t>(b) * H + h) * T];
+    dgate[h] = tot;
 }
 
 // ====================================================================== launch
@@ -446,10 +459,16 @@ hipError_t launch_backward_dv(const BwdArgs& a, hipStream_t stream) {
     if constexpr (GK == kGateScalar) {
         if (a.T == 0) return hipSuccess;
         hipLaunchKernelGGL((gate_grad_kernel<true>), dim3(static_cast<unsigned>(heads)), dim3(256), 0, stream, gq,
-                           a.ds_out, sfin, a.dgate, a.B, a.H, a.T, DV * DK);
+                           a.ds_out, sfin, a.dgate, a.T, DV * DK);
     } else {
-        hipLaunchKernelGGL((gate_grad_kernel<false>), dim3(static_cast<unsigned>(a.H)), dim3(256), 0, stream, gq,
-                           a.ds_out, sfin, a.dgate, a.B, a.H, a.T, DV * DK);
+        if (a.T > 0) {
+            hipLaunchKernelGGL((gate_grad_kernel<false>), dim3(static_cast<unsigned>(heads)), dim3(256), 0, stream,
+                               gq, a.ds_out, sfin, a.dgate, a.T, DV * DK);
+            err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        }
+        hipLaunchKernelGGL(gate_head_sum_kernel, dim3(static_cast<unsigned>((a.H + 255) / 256)), dim3(256), 0, stream,
+                           gq, a.dgate, a.B, a.H, a.T);
     }
     return hipGetLastError();
 }
