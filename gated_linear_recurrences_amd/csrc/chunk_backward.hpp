@@ -19,7 +19,9 @@
 // gradient pass below (chunk-parallel), and the gate pass (one kernel per sequence,
 // plus a sum over the batch for a fixed gate).
 //
-// Gradient pass (gfx950): one workgroup of eight waves per (sequence, chunk). q, k, v,
+// Gradient pass (gfx950): persistent workgroups of eight waves, one per CU, each taking
+// (sequence, chunk) items in turn and loading the next item's operands into registers
+// while the current one computes. q, k, v,
 // dO are staged token-major; A1 = (Q K^T) . M and A2 = (dO V^T) . M are formed on MFMA
 // into LDS (bf16, all C/16 x C/16 tiles, the upper ones zero). Every product is computed
 // transposed - feature rows, token columns - so that a lane ends with four consecutive
@@ -51,6 +53,7 @@ struct GradParams {
     u16* dv;               // [BH][T][DV]
     float* gq;             // [BH][T]: q.dq - k.dk per token
     int H, T, NC;
+    int items;             // BH * NC (sequence, chunk) pairs
 };
 
 template <int C, int DK, int DV>
@@ -100,221 +103,245 @@ void grad_kernel(GradParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g = lane >> 4;
-    const int bh = blockIdx.x / p.NC, c = blockIdx.x % p.NC;
     const int T = p.T;
-    const int t0 = c * C, n = (T - t0 < C) ? (T - t0) : C;
-    const int64_t tok0 = static_cast<int64_t>(bh) * T + t0;
-    const int64_t chunk = static_cast<int64_t>(bh) * p.NC + c;
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
-    // ---- loads up front (rows past the end read row 0, zeroed on staging)
+    // Persistent: this workgroup takes items (sequence, chunk) blockIdx.x, + gridDim.x, ...;
+    // the next item's operands are loaded into registers while the current one computes.
+    // Rows past the end of a sequence read row 0 and are zeroed on staging.
     u16x8 rq[QP_PER], rk[QP_PER], rv[VP_PER], ro[VP_PER], rx[XP_PER], rs[XP_PER];
-#pragma unroll
-    for (int i = 0; i < QP_PER; ++i) {
-        const int idx = tid + i * NT;
-        const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-        const unsigned off = (idx < QP && j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
-        rq[i] = *reinterpret_cast<const u16x8*>(p.q + tok0 * DK + off);
-        rk[i] = *reinterpret_cast<const u16x8*>(p.k + tok0 * DK + off);
-    }
-#pragma unroll
-    for (int i = 0; i < VP_PER; ++i) {
-        const int idx = tid + i * NT;
-        const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
-        const unsigned off = (idx < VP && j < n) ? static_cast<unsigned>(j * DV + col) : 0u;
-        rv[i] = *reinterpret_cast<const u16x8*>(p.v + tok0 * DV + off);
-        ro[i] = *reinterpret_cast<const u16x8*>(p.dout + tok0 * DV + off);
-    }
-#pragma unroll
-    for (int i = 0; i < XP_PER; ++i) {
-        const int idx = tid + i * NT;
-        const unsigned off = (idx < XP) ? static_cast<unsigned>(idx * 8) : 0u;
-        rx[i] = *reinterpret_cast<const u16x8*>(p.r + chunk * DV * DK + off);
-        rs[i] = *reinterpret_cast<const u16x8*>(p.s_in + chunk * DV * DK + off);
-    }
     float rgate = 0.f;
-    if constexpr (GK == kGateScalar) rgate = (tid < n) ? p.gate[tok0 + tid] : 0.f;
-
-    // ---- stage q, k, v, dO, R; cumulative gates (log2 units); zero the per-token sums
+    auto load_item = [&](int item) {
+        const int lbh = item / p.NC, lc = item % p.NC;
+        const int lt0 = lc * C, ln = (T - lt0 < C) ? (T - lt0) : C;
+        const int64_t ltok0 = static_cast<int64_t>(lbh) * T + lt0;
+        const int64_t lchunk = static_cast<int64_t>(lbh) * p.NC + lc;
 #pragma unroll
-    for (int i = 0; i < QP_PER; ++i) {
-        const int idx = tid + i * NT;
-        if (idx < QP) {
+        for (int i = 0; i < QP_PER; ++i) {
+            const int idx = tid + i * NT;
             const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-            *reinterpret_cast<u16x8*>(sQ + j * QS + col) = (j < n) ? rq[i] : z8;
-            *reinterpret_cast<u16x8*>(sK + j * QS + col) = (j < n) ? rk[i] : z8;
+            const unsigned off = (idx < QP && j < ln) ? static_cast<unsigned>(j * DK + col) : 0u;
+            rq[i] = *reinterpret_cast<const u16x8*>(p.q + ltok0 * DK + off);
+            rk[i] = *reinterpret_cast<const u16x8*>(p.k + ltok0 * DK + off);
         }
-    }
 #pragma unroll
-    for (int i = 0; i < VP_PER; ++i) {
-        const int idx = tid + i * NT;
-        if (idx < VP) {
+        for (int i = 0; i < VP_PER; ++i) {
+            const int idx = tid + i * NT;
             const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
-            *reinterpret_cast<u16x8*>(sV + j * VS + col) = (j < n) ? rv[i] : z8;
-            *reinterpret_cast<u16x8*>(sO + j * VS + col) = (j < n) ? ro[i] : z8;
+            const unsigned off = (idx < VP && j < ln) ? static_cast<unsigned>(j * DV + col) : 0u;
+            rv[i] = *reinterpret_cast<const u16x8*>(p.v + ltok0 * DV + off);
+            ro[i] = *reinterpret_cast<const u16x8*>(p.dout + ltok0 * DV + off);
         }
-    }
-    auto stage_x = [&](const u16x8* src) {
 #pragma unroll
         for (int i = 0; i < XP_PER; ++i) {
             const int idx = tid + i * NT;
-            if (idx < XP) {
-                const int m = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-                *reinterpret_cast<u16x8*>(sX + m * XS + col) = src[i];
-            }
+            const unsigned off = (idx < XP) ? static_cast<unsigned>(idx * 8) : 0u;
+            rx[i] = *reinterpret_cast<const u16x8*>(p.r + lchunk * DV * DK + off);
+            rs[i] = *reinterpret_cast<const u16x8*>(p.s_in + lchunk * DV * DK + off);
         }
+        if constexpr (GK == kGateScalar) rgate = (tid < ln) ? p.gate[ltok0 + tid] : 0.f;
     };
-    stage_x(rx);
-    if (w == 0) {
-        float x;
-        if constexpr (GK == kGateScalar) {
-            x = wave_inclusive_scan(rgate * kLog2e);   // padded tokens add 0
-        } else {
-            const float lg2 = p.gate[bh % p.H] * kLog2e;
-            x = static_cast<float>((lane < n ? lane : n - 1) + 1) * lg2;   // flat past the end
-        }
-        if (lane < C) sG[lane] = x;
-    }
-    lds_barrier();
-    const float glast = sG[C - 1];
 
-    // ---- A1 = (Q K^T) . M and A2 = (dO V^T) . M, every tile (upper ones zero):
-    // acc[r] = X[i = 16it + r16][j = 16jt + 4g + r]
-    for (int t = w; t < 2 * CT * CT; t += NW) {
-        const bool second = t >= CT * CT;
-        const int it = (t % (CT * CT)) / CT, jt = t % CT;
-        const int i = 16 * it + r16;
-        u16* const dst = second ? sA2 : sA1;
-        bf16x4 pv = zero4();
-        if (jt <= it) {
-            f32x4 acc = zf4();
-            const u16* arow = second ? sV + (16 * jt + r16) * VS : sK + (16 * jt + r16) * QS;
-            const u16* brow = second ? sO + i * VS : sQ + i * QS;
-            const int D = second ? DV : DK;
+    int item = blockIdx.x;
+    if (item >= p.items) return;
+    load_item(item);
+    for (;;) {
+        const int bh = item / p.NC, c = item % p.NC;
+        const int t0 = c * C, n = (T - t0 < C) ? (T - t0) : C;
+        const int64_t tok0 = static_cast<int64_t>(bh) * T + t0;
+
+        // ---- stage q, k, v, dO, R; cumulative gates (log2 units); zero the per-token sums
 #pragma unroll
-            for (int kb = 0; kb < (KB > VB ? KB : VB); ++kb) {
-                const int col = 32 * kb + 8 * g;
-                bf16x8 a8 = as_bf16x8(z8), b8 = as_bf16x8(z8);
-                if (col < D) {
-                    a8 = *reinterpret_cast<const bf16x8*>(arow + col);
-                    b8 = *reinterpret_cast<const bf16x8*>(brow + col);
+        for (int i = 0; i < QP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < QP) {
+                const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+                *reinterpret_cast<u16x8*>(sQ + j * QS + col) = (j < n) ? rq[i] : z8;
+                *reinterpret_cast<u16x8*>(sK + j * QS + col) = (j < n) ? rk[i] : z8;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VP_PER; ++i) {
+            const int idx = tid + i * NT;
+            if (idx < VP) {
+                const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
+                *reinterpret_cast<u16x8*>(sV + j * VS + col) = (j < n) ? rv[i] : z8;
+                *reinterpret_cast<u16x8*>(sO + j * VS + col) = (j < n) ? ro[i] : z8;
+            }
+        }
+        auto stage_x = [&](const u16x8* src) {
+#pragma unroll
+            for (int i = 0; i < XP_PER; ++i) {
+                const int idx = tid + i * NT;
+                if (idx < XP) {
+                    const int m = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+                    *reinterpret_cast<u16x8*>(sX + m * XS + col) = src[i];
                 }
-                acc = mfma_16x16x32(a8, b8, acc);
             }
-            const float gi = sG[i];
-            const f32x4 gj = ldf4(sG + 16 * jt + 4 * g);
+        };
+        stage_x(rx);
+        u16x8 rs_cur[XP_PER];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * jt + 4 * g + r;
-                pv[r] = static_cast<__bf16>((j <= i) ? acc[r] * ex2(gi - gj[r]) : 0.f);
+        for (int i = 0; i < XP_PER; ++i) rs_cur[i] = rs[i];
+        const float gate_cur = rgate;
+        const int step = static_cast<int>(gridDim.x);
+        const int next = (item < p.items - step) ? item + step : p.items;
+        if (next < p.items) load_item(next);   // in flight during this item's products
+        if (w == 0) {
+            float x;
+            if constexpr (GK == kGateScalar) {
+                x = wave_inclusive_scan(gate_cur * kLog2e);   // padded tokens add 0
+            } else {
+                const float lg2 = p.gate[bh % p.H] * kLog2e;
+                x = static_cast<float>((lane < n ? lane : n - 1) + 1) * lg2;   // flat past the end
             }
+            if (lane < C) sG[lane] = x;
         }
-        st4(dst + i * AS + 16 * jt + 4 * g, pv);
-    }
-    lds_barrier();
+        lds_barrier();
+        const float glast = sG[C - 1];
 
-    // transposed operand over 32 tokens (rows 32b .. 32b + 31) of a token-major array
-    // X with row stride RS, column tile n0; the second half zero unless `hi`
-    auto wq_of = [&](int j) { return ex2(glast - sG[j]); };
-
-    // ---- dV^T and dK^T tiles: (feature tile, token tile jt); lane holds
-    // D[f = 16 ft + 4g + r][j = 16 jt + r16]
-    for (int t = w; t < (FV + FK) * CT; t += NW) {
-        const bool isv = t < FV * CT;
-        const int ft = (isv ? t : t - FV * CT) / CT, jt = (isv ? t : t - FV * CT) % CT;
-        const int j = 16 * jt + r16;
-        f32x4 acc = zf4(), acc2 = zf4();
-        // term 1: sum over i >= j of X^T[f][i] A[i][j] (A1 with dO for dV, A2 with Q for dK)
+        // ---- A1 = (Q K^T) . M and A2 = (dO V^T) . M, every tile (upper ones zero):
+        // acc[r] = X[i = 16it + r16][j = 16jt + 4g + r]
+        for (int t = w; t < 2 * CT * CT; t += NW) {
+            const bool second = t >= CT * CT;
+            const int it = (t % (CT * CT)) / CT, jt = t % CT;
+            const int i = 16 * it + r16;
+            u16* const dst = second ? sA2 : sA1;
+            bf16x4 pv = zero4();
+            if (jt <= it) {
+                f32x4 acc = zf4();
+                const u16* arow = second ? sV + (16 * jt + r16) * VS : sK + (16 * jt + r16) * QS;
+                const u16* brow = second ? sO + i * VS : sQ + i * QS;
+                const int D = second ? DV : DK;
 #pragma unroll
-        for (int b = 0; b < JB; ++b) {
-            if (32 * b + 31 < 16 * jt) continue;                 // rows i all above j
-            const bool hi = 2 * b + 1 < CT;
-            const bf16x8 xa = isv ? tr_split<VS>(sO, b, 16 * ft, hi, r16, g) : tr_split<QS>(sQ, b, 16 * ft, hi, r16, g);
-            const bf16x8 ab = isv ? tr_split<AS>(sA1, b, 16 * jt, hi, r16, g) : tr_split<AS>(sA2, b, 16 * jt, hi, r16, g);
-            acc = mfma_16x16x32(xa, ab, acc);
-        }
-        if (isv) {
-            // term 2: sum over keys m of R[f][m] K[j][m] (rows of R and of K, natural order)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const int col = 32 * kb + 8 * g;
-                bf16x8 xa = as_bf16x8(z8), kb8 = as_bf16x8(z8);
-                if (col < DK) {
-                    xa = *reinterpret_cast<const bf16x8*>(sX + (16 * ft + r16) * XS + col);
-                    kb8 = *reinterpret_cast<const bf16x8*>(sK + j * QS + col);
+                for (int kb = 0; kb < (KB > VB ? KB : VB); ++kb) {
+                    const int col = 32 * kb + 8 * g;
+                    bf16x8 a8 = as_bf16x8(z8), b8 = as_bf16x8(z8);
+                    if (col < D) {
+                        a8 = *reinterpret_cast<const bf16x8*>(arow + col);
+                        b8 = *reinterpret_cast<const bf16x8*>(brow + col);
+                    }
+                    acc = mfma_16x16x32(a8, b8, acc);
                 }
-                acc2 = mfma_16x16x32(xa, kb8, acc2);
+                const float gi = sG[i];
+                const f32x4 gj = ldf4(sG + 16 * jt + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * jt + 4 * g + r;
+                    pv[r] = static_cast<__bf16>((j <= i) ? acc[r] * ex2(gi - gj[r]) : 0.f);
+                }
             }
-        } else {
-            // term 2: sum over values m of R[m][f] V[j][m] (R read transposed, rows of V split
-            // like the transposed operand)
+            st4(dst + i * AS + 16 * jt + 4 * g, pv);
+        }
+        lds_barrier();
+
+        // transposed operand over 32 tokens (rows 32b .. 32b + 31) of a token-major array
+        // X with row stride RS, column tile n0; the second half zero unless `hi`
+        auto wq_of = [&](int j) { return ex2(glast - sG[j]); };
+
+        // ---- dV^T and dK^T tiles: (feature tile, token tile jt); lane holds
+        // D[f = 16 ft + 4g + r][j = 16 jt + r16]
+        for (int t = w; t < (FV + FK) * CT; t += NW) {
+            const bool isv = t < FV * CT;
+            const int ft = (isv ? t : t - FV * CT) / CT, jt = (isv ? t : t - FV * CT) % CT;
+            const int j = 16 * jt + r16;
+            f32x4 acc = zf4(), acc2 = zf4();
+            // term 1: sum over i >= j of X^T[f][i] A[i][j] (A1 with dO for dV, A2 with Q for dK)
+#pragma unroll
+            for (int b = 0; b < JB; ++b) {
+                if (32 * b + 31 < 16 * jt) continue;                 // rows i all above j
+                const bool hi = 2 * b + 1 < CT;
+                const bf16x8 xa = isv ? tr_split<VS>(sO, b, 16 * ft, hi, r16, g) : tr_split<QS>(sQ, b, 16 * ft, hi, r16, g);
+                const bf16x8 ab = isv ? tr_split<AS>(sA1, b, 16 * jt, hi, r16, g) : tr_split<AS>(sA2, b, 16 * jt, hi, r16, g);
+                acc = mfma_16x16x32(xa, ab, acc);
+            }
+            if (isv) {
+                // term 2: sum over keys m of R[f][m] K[j][m] (rows of R and of K, natural order)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int col = 32 * kb + 8 * g;
+                    bf16x8 xa = as_bf16x8(z8), kb8 = as_bf16x8(z8);
+                    if (col < DK) {
+                        xa = *reinterpret_cast<const bf16x8*>(sX + (16 * ft + r16) * XS + col);
+                        kb8 = *reinterpret_cast<const bf16x8*>(sK + j * QS + col);
+                    }
+                    acc2 = mfma_16x16x32(xa, kb8, acc2);
+                }
+            } else {
+                // term 2: sum over values m of R[m][f] V[j][m] (R read transposed, rows of V split
+                // like the transposed operand)
+#pragma unroll
+                for (int b = 0; b < VB; ++b) {
+                    const bool hi = 32 * b + 16 < DV;
+                    const bf16x8 xa = tr_split<XS>(sX, b, 16 * ft, hi, r16, g);
+                    const u16* vrow = sV + j * VS + 32 * b + 4 * g;
+                    const bf16x8 vb = join8(ld4(vrow), hi ? ld4(vrow + 16) : zero4());
+                    acc2 = mfma_16x16x32(xa, vb, acc2);
+                }
+            }
+            const float wj = wq_of(j);
+            acc = acc + acc2 * wj;
+            if (!isv) {
+                // k_j . dk_j over this tile's features: the lane's four, then the lane group
+                const f32x4 kj = up4(ld4(sK + j * QS + 16 * ft + 4 * g));
+                float part = kj[0] * acc[0] + kj[1] * acc[1] + kj[2] * acc[2] + kj[3] * acc[3];
+                part += __shfl_xor(part, 16, 64);
+                part += __shfl_xor(part, 32, 64);
+                if (g == 0) sKD[ft * C + j] = part;
+            }
+            if (j < n) {
+                if (isv) st4(p.dv + (tok0 + j) * DV + 16 * ft + 4 * g, cvt4(acc));
+                else st4(p.dk + (tok0 + j) * DK + 16 * ft + 4 * g, cvt4(acc));
+            }
+        }
+        lds_barrier();   // R is dead: the region takes S_in
+        stage_x(rs_cur);
+        lds_barrier();
+
+        // ---- dQ^T tiles: (key tile ft, token tile it); lane holds dQ[i = 16it + r16][f = 16ft + 4g + r]
+        for (int t = w; t < FK * CT; t += NW) {
+            const int ft = t / CT, it = t % CT;
+            const int i = 16 * it + r16;
+            f32x4 acc = zf4(), acc2 = zf4();
+            // term 1: sum over j <= i of K[j][f] A2[i][j] (K transposed, rows of A2 split)
+#pragma unroll
+            for (int b = 0; b < JB; ++b) {
+                if (32 * b > 16 * it + 15) continue;                 // columns j all past i
+                const bool hi = 2 * b + 1 < CT;
+                const bf16x8 ka = tr_split<QS>(sK, b, 16 * ft, hi, r16, g);
+                const u16* arow = sA2 + i * AS + 32 * b + 4 * g;
+                acc = mfma_16x16x32(ka, join8(ld4(arow), hi ? ld4(arow + 16) : zero4()), acc);
+            }
+            // term 2: sum over values m of S_in[m][f] dO[i][m], scaled by e^(G_i)
 #pragma unroll
             for (int b = 0; b < VB; ++b) {
                 const bool hi = 32 * b + 16 < DV;
                 const bf16x8 xa = tr_split<XS>(sX, b, 16 * ft, hi, r16, g);
-                const u16* vrow = sV + j * VS + 32 * b + 4 * g;
-                const bf16x8 vb = join8(ld4(vrow), hi ? ld4(vrow + 16) : zero4());
-                acc2 = mfma_16x16x32(xa, vb, acc2);
+                const u16* orow = sO + i * VS + 32 * b + 4 * g;
+                acc2 = mfma_16x16x32(xa, join8(ld4(orow), hi ? ld4(orow + 16) : zero4()), acc2);
             }
-        }
-        const float wj = wq_of(j);
-        acc = acc + acc2 * wj;
-        if (!isv) {
-            // k_j . dk_j over this tile's features: the lane's four, then the lane group
-            const f32x4 kj = up4(ld4(sK + j * QS + 16 * ft + 4 * g));
-            float part = kj[0] * acc[0] + kj[1] * acc[1] + kj[2] * acc[2] + kj[3] * acc[3];
+            acc = acc + acc2 * ex2(sG[i]);
+            const f32x4 qi = up4(ld4(sQ + i * QS + 16 * ft + 4 * g));
+            float part = qi[0] * acc[0] + qi[1] * acc[1] + qi[2] * acc[2] + qi[3] * acc[3];
             part += __shfl_xor(part, 16, 64);
             part += __shfl_xor(part, 32, 64);
-            if (g == 0) sKD[ft * C + j] = part;
+            if (g == 0) sQD[ft * C + i] = part;
+            if (i < n) st4(p.dq + (tok0 + i) * DK + 16 * ft + 4 * g, cvt4(acc));
         }
-        if (j < n) {
-            if (isv) st4(p.dv + (tok0 + j) * DV + 16 * ft + 4 * g, cvt4(acc));
-            else st4(p.dk + (tok0 + j) * DK + 16 * ft + 4 * g, cvt4(acc));
-        }
-    }
-    lds_barrier();   // R is dead: the region takes S_in
-    stage_x(rs);
-    lds_barrier();
-
-    // ---- dQ^T tiles: (key tile ft, token tile it); lane holds dQ[i = 16it + r16][f = 16ft + 4g + r]
-    for (int t = w; t < FK * CT; t += NW) {
-        const int ft = t / CT, it = t % CT;
-        const int i = 16 * it + r16;
-        f32x4 acc = zf4(), acc2 = zf4();
-        // term 1: sum over j <= i of K[j][f] A2[i][j] (K transposed, rows of A2 split)
+        lds_barrier();
+        if (tid < n) {
+            float qd = 0.f, kd = 0.f;
 #pragma unroll
-        for (int b = 0; b < JB; ++b) {
-            if (32 * b > 16 * it + 15) continue;                 // columns j all past i
-            const bool hi = 2 * b + 1 < CT;
-            const bf16x8 ka = tr_split<QS>(sK, b, 16 * ft, hi, r16, g);
-            const u16* arow = sA2 + i * AS + 32 * b + 4 * g;
-            acc = mfma_16x16x32(ka, join8(ld4(arow), hi ? ld4(arow + 16) : zero4()), acc);
+            for (int f = 0; f < FK; ++f) {
+                qd += sQD[f * C + tid];
+                kd += sKD[f * C + tid];
+            }
+            p.gq[tok0 + tid] = qd - kd;
         }
-        // term 2: sum over values m of S_in[m][f] dO[i][m], scaled by e^(G_i)
-#pragma unroll
-        for (int b = 0; b < VB; ++b) {
-            const bool hi = 32 * b + 16 < DV;
-            const bf16x8 xa = tr_split<XS>(sX, b, 16 * ft, hi, r16, g);
-            const u16* orow = sO + i * VS + 32 * b + 4 * g;
-            acc2 = mfma_16x16x32(xa, join8(ld4(orow), hi ? ld4(orow + 16) : zero4()), acc2);
-        }
-        acc = acc + acc2 * ex2(sG[i]);
-        const f32x4 qi = up4(ld4(sQ + i * QS + 16 * ft + 4 * g));
-        float part = qi[0] * acc[0] + qi[1] * acc[1] + qi[2] * acc[2] + qi[3] * acc[3];
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
-        if (g == 0) sQD[ft * C + i] = part;
-        if (i < n) st4(p.dq + (tok0 + i) * DK + 16 * ft + 4 * g, cvt4(acc));
-    }
-    lds_barrier();
-    if (tid < n) {
-        float qd = 0.f, kd = 0.f;
-#pragma unroll
-        for (int f = 0; f < FK; ++f) {
-            qd += sQD[f * C + tid];
-            kd += sKD[f * C + tid];
-        }
-        p.gq[tok0 + tid] = qd - kd;
+        // the next item's staging overwrites only regions every wave has finished reading
+        // (the barrier above); the per-token sums it rewrites wait behind its own barriers
+        if (next >= p.items) break;
+        item = next;
     }
 }
 
@@ -451,8 +478,19 @@ hipError_t launch_backward_dv(const BwdArgs& a, hipStream_t stream) {
         p.H = a.H;
         p.T = a.T;
         p.NC = NC;
-        hipLaunchKernelGGL((grad_kernel<C, DK, DV, GK>), dim3(static_cast<unsigned>(heads * NC)), dim3(512), 0,
-                           stream, p);
+        p.items = static_cast<int>(heads * NC);
+        // persistent: as many workgroups as fit on the chip at once (one per CU at d = 128,
+        // where the LDS allows one)
+        int dev = 0, cus = 256, per_cu = 1;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grad_kernel<C, DK, DV, GK>, 512, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        const int64_t slots = static_cast<int64_t>(cus) * per_cu;
+        const int grid = p.items < slots ? p.items : static_cast<int>(slots);
+        hipLaunchKernelGGL((grad_kernel<C, DK, DV, GK>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream, p);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
