@@ -28,7 +28,9 @@
 // features of one token (one 8-byte store):
 //   dV^T = dO^T A1 + R K^T diag(w)      dK^T = Q^T A2 + R^T V^T diag(w)
 //   dQ^T = K^T A2^T + S_in^T dO^T diag(e^G),     w_j = e^(G_last - G_j),
-// with the operands read transposed (ds_read_b64_tr_b16) or by rows as each needs.
+// with the operands read transposed (ds_read_b64_tr_b16) or by rows as each needs; the
+// staged tiles use the chunk-swizzled layout (SwzTile) so that both kinds of read are
+// free of bank conflicts.
 // R and then S_in take turns in one LDS region. The per-token sums q.dq and k.dk meet
 // in LDS: per feature tile a partial (reduced over the lane group), added in tile order
 // (no atomics: the gradients are bit-for-bit repeatable).
@@ -58,7 +60,10 @@ struct GradParams {
 
 template <int C, int DK, int DV>
 struct GradLayout {
-    static constexpr int QS = tile_stride(DK), VS = tile_stride(DV), AS = tile_stride(C), XS = tile_stride(DK);
+    using TQ = SwzTile<DK>;   // q, k and the memories (rows of d_k)
+    using TV = SwzTile<DV>;   // v and dO
+    using TA = SwzTile<C>;    // A1, A2
+    static constexpr int QS = TQ::STRIDE, VS = TV::STRIDE, AS = TA::STRIDE, XS = TQ::STRIDE;
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + al(C * QS * 2);
@@ -80,7 +85,9 @@ void grad_kernel(GradParams p) {
     using Lay = GradLayout<C, DK, DV>;
     constexpr int NT = 512, NW = 8;
     constexpr int CT = C / 16, JB = (CT + 1) / 2;
-    constexpr int QS = Lay::QS, VS = Lay::VS, AS = Lay::AS, XS = Lay::XS;
+    using TQ = typename Lay::TQ;
+    using TV = typename Lay::TV;
+    using TA = typename Lay::TA;
     constexpr int KB = (DK + 31) / 32, VB = (DV + 31) / 32;
     constexpr int QP = C * DK / 8, QP_PER = (QP + NT - 1) / NT;
     constexpr int VP = C * DV / 8, VP_PER = (VP + NT - 1) / NT;
@@ -156,8 +163,8 @@ void grad_kernel(GradParams p) {
             const int idx = tid + i * NT;
             if (idx < QP) {
                 const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-                *reinterpret_cast<u16x8*>(sQ + j * QS + col) = (j < n) ? rq[i] : z8;
-                *reinterpret_cast<u16x8*>(sK + j * QS + col) = (j < n) ? rk[i] : z8;
+                *reinterpret_cast<u16x8*>(sQ + TQ::off(j, col)) = (j < n) ? rq[i] : z8;
+                *reinterpret_cast<u16x8*>(sK + TQ::off(j, col)) = (j < n) ? rk[i] : z8;
             }
         }
 #pragma unroll
@@ -165,8 +172,8 @@ void grad_kernel(GradParams p) {
             const int idx = tid + i * NT;
             if (idx < VP) {
                 const int j = idx / (DV / 8), col = (idx % (DV / 8)) * 8;
-                *reinterpret_cast<u16x8*>(sV + j * VS + col) = (j < n) ? rv[i] : z8;
-                *reinterpret_cast<u16x8*>(sO + j * VS + col) = (j < n) ? ro[i] : z8;
+                *reinterpret_cast<u16x8*>(sV + TV::off(j, col)) = (j < n) ? rv[i] : z8;
+                *reinterpret_cast<u16x8*>(sO + TV::off(j, col)) = (j < n) ? ro[i] : z8;
             }
         }
         auto stage_x = [&](const u16x8* src) {
@@ -175,7 +182,7 @@ void grad_kernel(GradParams p) {
                 const int idx = tid + i * NT;
                 if (idx < XP) {
                     const int m = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-                    *reinterpret_cast<u16x8*>(sX + m * XS + col) = src[i];
+                    *reinterpret_cast<u16x8*>(sX + TQ::off(m, col)) = src[i];
                 }
             }
         };
@@ -210,16 +217,15 @@ void grad_kernel(GradParams p) {
             bf16x4 pv = zero4();
             if (jt <= it) {
                 f32x4 acc = zf4();
-                const u16* arow = second ? sV + (16 * jt + r16) * VS : sK + (16 * jt + r16) * QS;
-                const u16* brow = second ? sO + i * VS : sQ + i * QS;
+                const int ar = 16 * jt + r16;
                 const int D = second ? DV : DK;
 #pragma unroll
                 for (int kb = 0; kb < (KB > VB ? KB : VB); ++kb) {
                     const int col = 32 * kb + 8 * g;
                     bf16x8 a8 = as_bf16x8(z8), b8 = as_bf16x8(z8);
                     if (col < D) {
-                        a8 = *reinterpret_cast<const bf16x8*>(arow + col);
-                        b8 = *reinterpret_cast<const bf16x8*>(brow + col);
+                        a8 = *reinterpret_cast<const bf16x8*>(second ? sV + TV::off(ar, col) : sK + TQ::off(ar, col));
+                        b8 = *reinterpret_cast<const bf16x8*>(second ? sO + TV::off(i, col) : sQ + TQ::off(i, col));
                     }
                     acc = mfma_16x16x32(a8, b8, acc);
                 }
@@ -231,7 +237,7 @@ void grad_kernel(GradParams p) {
                     pv[r] = static_cast<__bf16>((j <= i) ? acc[r] * ex2(gi - gj[r]) : 0.f);
                 }
             }
-            st4(dst + i * AS + 16 * jt + 4 * g, pv);
+            st4(dst + TA::off(i, 16 * jt + 4 * g), pv);
         }
         lds_barrier();
 
@@ -251,8 +257,8 @@ void grad_kernel(GradParams p) {
             for (int b = 0; b < JB; ++b) {
                 if (32 * b + 31 < 16 * jt) continue;                 // rows i all above j
                 const bool hi = 2 * b + 1 < CT;
-                const bf16x8 xa = isv ? tr_split<VS>(sO, b, 16 * ft, hi, r16, g) : tr_split<QS>(sQ, b, 16 * ft, hi, r16, g);
-                const bf16x8 ab = isv ? tr_split<AS>(sA1, b, 16 * jt, hi, r16, g) : tr_split<AS>(sA2, b, 16 * jt, hi, r16, g);
+                const bf16x8 xa = isv ? tr_split_s<DV>(sO, b, 16 * ft, hi, r16, g) : tr_split_s<DK>(sQ, b, 16 * ft, hi, r16, g);
+                const bf16x8 ab = isv ? tr_split_s<C>(sA1, b, 16 * jt, hi, r16, g) : tr_split_s<C>(sA2, b, 16 * jt, hi, r16, g);
                 acc = mfma_16x16x32(xa, ab, acc);
             }
             if (isv) {
@@ -262,8 +268,8 @@ void grad_kernel(GradParams p) {
                     const int col = 32 * kb + 8 * g;
                     bf16x8 xa = as_bf16x8(z8), kb8 = as_bf16x8(z8);
                     if (col < DK) {
-                        xa = *reinterpret_cast<const bf16x8*>(sX + (16 * ft + r16) * XS + col);
-                        kb8 = *reinterpret_cast<const bf16x8*>(sK + j * QS + col);
+                        xa = *reinterpret_cast<const bf16x8*>(sX + TQ::off(16 * ft + r16, col));
+                        kb8 = *reinterpret_cast<const bf16x8*>(sK + TQ::off(j, col));
                     }
                     acc2 = mfma_16x16x32(xa, kb8, acc2);
                 }
@@ -273,9 +279,9 @@ void grad_kernel(GradParams p) {
 #pragma unroll
                 for (int b = 0; b < VB; ++b) {
                     const bool hi = 32 * b + 16 < DV;
-                    const bf16x8 xa = tr_split<XS>(sX, b, 16 * ft, hi, r16, g);
-                    const u16* vrow = sV + j * VS + 32 * b + 4 * g;
-                    const bf16x8 vb = join8(ld4(vrow), hi ? ld4(vrow + 16) : zero4());
+                    const bf16x8 xa = tr_split_s<DK>(sX, b, 16 * ft, hi, r16, g);
+                    const int vc = 32 * b + 4 * g;
+                    const bf16x8 vb = join8(ld4(sV + TV::off(j, vc)), hi ? ld4(sV + TV::off(j, vc + 16)) : zero4());
                     acc2 = mfma_16x16x32(xa, vb, acc2);
                 }
             }
@@ -283,7 +289,7 @@ void grad_kernel(GradParams p) {
             acc = acc + acc2 * wj;
             if (!isv) {
                 // k_j . dk_j over this tile's features: the lane's four, then the lane group
-                const f32x4 kj = up4(ld4(sK + j * QS + 16 * ft + 4 * g));
+                const f32x4 kj = up4(ld4(sK + TQ::off(j, 16 * ft + 4 * g)));
                 float part = kj[0] * acc[0] + kj[1] * acc[1] + kj[2] * acc[2] + kj[3] * acc[3];
                 part += __shfl_xor(part, 16, 64);
                 part += __shfl_xor(part, 32, 64);
@@ -308,20 +314,20 @@ void grad_kernel(GradParams p) {
             for (int b = 0; b < JB; ++b) {
                 if (32 * b > 16 * it + 15) continue;                 // columns j all past i
                 const bool hi = 2 * b + 1 < CT;
-                const bf16x8 ka = tr_split<QS>(sK, b, 16 * ft, hi, r16, g);
-                const u16* arow = sA2 + i * AS + 32 * b + 4 * g;
-                acc = mfma_16x16x32(ka, join8(ld4(arow), hi ? ld4(arow + 16) : zero4()), acc);
+                const bf16x8 ka = tr_split_s<DK>(sK, b, 16 * ft, hi, r16, g);
+                const int ac = 32 * b + 4 * g;
+                acc = mfma_16x16x32(ka, join8(ld4(sA2 + TA::off(i, ac)), hi ? ld4(sA2 + TA::off(i, ac + 16)) : zero4()), acc);
             }
             // term 2: sum over values m of S_in[m][f] dO[i][m], scaled by e^(G_i)
 #pragma unroll
             for (int b = 0; b < VB; ++b) {
                 const bool hi = 32 * b + 16 < DV;
-                const bf16x8 xa = tr_split<XS>(sX, b, 16 * ft, hi, r16, g);
-                const u16* orow = sO + i * VS + 32 * b + 4 * g;
-                acc2 = mfma_16x16x32(xa, join8(ld4(orow), hi ? ld4(orow + 16) : zero4()), acc2);
+                const bf16x8 xa = tr_split_s<DK>(sX, b, 16 * ft, hi, r16, g);
+                const int oc = 32 * b + 4 * g;
+                acc2 = mfma_16x16x32(xa, join8(ld4(sO + TV::off(i, oc)), hi ? ld4(sO + TV::off(i, oc + 16)) : zero4()), acc2);
             }
             acc = acc + acc2 * ex2(sG[i]);
-            const f32x4 qi = up4(ld4(sQ + i * QS + 16 * ft + 4 * g));
+            const f32x4 qi = up4(ld4(sQ + TQ::off(i, 16 * ft + 4 * g)));
             float part = qi[0] * acc[0] + qi[1] * acc[1] + qi[2] * acc[2] + qi[3] * acc[3];
             part += __shfl_xor(part, 16, 64);
             part += __shfl_xor(part, 32, 64);

@@ -63,6 +63,41 @@ __device__ __forceinline__ bf16x8 tr_split(const u16* X, int jb, int n0, bool hi
     return join8(tr_op<RS>(X, 32 * jb, n0, r16, g), hi ? tr_op<RS>(X, 32 * jb + 16, n0, r16, g) : zero4());
 }
 
+// Row-major LDS tile of W bf16 elements per row. For W = 64 and 128 the rows are
+// unpadded and the 16-byte chunks of row r sit permuted by XOR with h(r), chosen so
+// that both access patterns of the MFMA operands hit 64 distinct banks: a row read (16
+// consecutive rows, one chunk each: h is one-to-one on them) and a transposing read
+// (8 consecutive rows, two adjacent chunks each: h / 2 is one-to-one on the rows that
+// share a bank line). Narrower tiles keep the padded stride tile_stride(W).
+template <int W>
+struct SwzTile {
+    static constexpr int STRIDE = (W == 64 || W == 128) ? W : (W == 16 ? 16 : W + 16);
+    __device__ static __forceinline__ int off(int r, int c) {
+        if constexpr (W == 128) {
+            const int h = ((r & 7) << 1) | ((r >> 3) & 1);
+            return r * 128 + ((((c >> 3) ^ h) << 3) | (c & 7));
+        } else if constexpr (W == 64) {
+            const int h = (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+            return r * 64 + ((((c >> 3) ^ h) << 3) | (c & 7));
+        } else {
+            return r * STRIDE + c;
+        }
+    }
+};
+
+// tr_op on a SwzTile: lane (r, g) receives X[base+4g+e][n0+r], e = 0..3.
+template <int W>
+__device__ __forceinline__ bf16x4 tr_op_s(const u16* X, int base, int n0, int r16, int g) {
+    const u16* p = X + SwzTile<W>::off(base + 4 * g + (r16 >> 2), n0 + 4 * (r16 & 3));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+template <int W>
+__device__ __forceinline__ bf16x8 tr_split_s(const u16* X, int jb, int n0, bool hi, int r16, int g) {
+    return join8(tr_op_s<W>(X, 32 * jb, n0, r16, g), hi ? tr_op_s<W>(X, 32 * jb + 16, n0, r16, g) : zero4());
+}
+
 // Row stride (bf16 elements) of a staged token-major tile `width` channels wide:
 // 16 more than the width (none for 16-wide tiles), so that rows sit 8 x odd banks
 // apart and the 8 rows read by half a wave of ds_read_b64_tr_b16 (8 bytes from
