@@ -42,6 +42,7 @@ from .glr_oracle import (  # noqa: F401
     rms_norm,
     scalar_backward,
     retention_backward,
+    gla_backward,
     vla_recurrent,
     vla_decode_step,
     forward_substitution,

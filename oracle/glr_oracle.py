@@ -525,6 +525,35 @@ def scalar_backward(q, k, v, log_alpha, do, dS_T=None, s0=None):
     return dq, dk, dv, dla, D
 
 
+def gla_backward(q, k, v, log_alpha, do, dS_T=None, s0=None):
+    """Gradients of the diagonal-gate (GLA) recurrence by reverse-mode differentiation of its
+    recurrent form ("Dimenticare: i gate", diagonal-gate equation), token by token. With D_t
+    the gradient of the loss with respect to S_t: ``D_{T-1} = dS_T + do_{T-1} q_{T-1}^T``,
+    ``D_t = D_{t+1} Diag(a_{t+1}) + do_t q_t^T``, and ``dq_t = S_t^T do_t``,
+    ``dk_t = D_t^T v_t``, ``dv_t = D_t k_t``, ``d log a_t[c] = a_t[c] sum_m D_t[m, c]
+    S_{t-1}[m, c]``, ``dS_0 = D_0 Diag(a_0)``. Returns ``(dq, dk, dv, dlog_alpha, ds0)`` with
+    ``dlog_alpha`` shaped like ``log_alpha`` ``[B, H, T, d_k]``."""
+    q, k, v, la, do = _f64(q, k, v, log_alpha, do)
+    S0 = _init_state(q, v, s0)
+    T = q.shape[-2]
+    a = np.exp(la)
+    states = [S0]
+    S = S0
+    for t in range(T):
+        S = S * a[..., t, :][..., None, :] + _outer(v[..., t, :], k[..., t, :])
+        states.append(S)
+    D = np.zeros_like(S0) if dS_T is None else np.asarray(dS_T, dtype=np.float64).copy()
+    dq = np.zeros(q.shape); dk = np.zeros(k.shape); dv = np.zeros(v.shape); dla = np.zeros(la.shape)
+    for t in range(T - 1, -1, -1):
+        D = D + _outer(do[..., t, :], q[..., t, :])                 # now the gradient w.r.t. S_t
+        dq[..., t, :] = np.einsum("...mc,...m->...c", states[t + 1], do[..., t, :])
+        dk[..., t, :] = np.einsum("...mc,...m->...c", D, v[..., t, :])
+        dv[..., t, :] = np.einsum("...mc,...c->...m", D, k[..., t, :])
+        dla[..., t, :] = a[..., t, :] * np.einsum("...mc,...mc->...c", D, states[t])
+        D = D * a[..., t, :][..., None, :]                           # through S_t = S_{t-1} Diag(a_t) + ...
+    return dq, dk, dv, dla, D
+
+
 def retention_backward(q, k, v, log_gamma, do, dS_T=None, s0=None):
     """Retention is the scalar decay with the same gate at every step of head h, so its
     gradients are scalar_backward's, with the gate gradient summed over the batch and the

@@ -302,7 +302,7 @@ def _loss(o, S, W_o, W_s):
     return np.sum(o * W_o) + np.sum(S * W_s)
 
 
-@pytest.mark.parametrize("kind", ["scalar", "retention"])
+@pytest.mark.parametrize("kind", ["scalar", "retention", "gla"])
 def test_backward_matches_finite_differences(kind):
     """Central differences of L = <W_o, o> + <W_s, S_T> through the recurrent form, against
     the reverse-mode gradients, for every input element (tiny sizes, fp64)."""
@@ -315,6 +315,10 @@ def test_backward_matches_finite_differences(kind):
         gate = -np.logaddexp(0.0, -rng.standard_normal((B, H, T)))
         fwd = lambda q, k, v, g, s: orc.scalar_recurrent(q, k, v, g, s0=s)
         grads = orc.scalar_backward(q, k, v, gate, W_o, dS_T=W_s, s0=s0)
+    elif kind == "gla":
+        gate = -np.logaddexp(0.0, -rng.standard_normal((B, H, T, dk)))
+        fwd = lambda q, k, v, g, s: orc.gla_recurrent(q, k, v, g, s0=s)
+        grads = orc.gla_backward(q, k, v, gate, W_o, dS_T=W_s, s0=s0)
     else:
         gate = np.log(rng.uniform(0.5, 0.95, H))
         fwd = lambda q, k, v, g, s: orc.retention_recurrent(q, k, v, g, s0=s)
@@ -346,3 +350,38 @@ def test_gate_gradient_identity():
     per_t = np.sum(q * dq, axis=-1) - np.sum(k * dk_, axis=-1)
     want = np.flip(np.cumsum(np.flip(per_t, -1), -1), -1) + np.sum(dS * S_T, axis=(-2, -1))[..., None]
     np.testing.assert_allclose(dla, want, atol=1e-10)
+
+
+def test_gla_gate_gradient_identity():
+    """Per key channel the same rescaling argument holds: a shift of log a_r[c] equals scaling
+    channel c of q_s by e^eps and of k_s by e^-eps for s >= r, and column c of S_T by e^eps, so
+    d log a_r[c] = sum_{t >= r} (q_t[c] dq_t[c] - k_t[c] dk_t[c]) + sum_m dS_T[m, c] S_T[m, c]."""
+    rng = np.random.default_rng(42)
+    B, H, T, dk, dv = 2, 1, 8, 5, 3
+    q = rng.standard_normal((B, H, T, dk)); k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv)); s0 = rng.standard_normal((B, H, dv, dk))
+    la = -np.logaddexp(0.0, -rng.standard_normal((B, H, T, dk)))
+    do = rng.standard_normal((B, H, T, dv)); dS = rng.standard_normal((B, H, dv, dk))
+    dq, dk_, dv_, dla, _ = orc.gla_backward(q, k, v, la, do, dS_T=dS, s0=s0)
+    _, S_T = orc.gla_recurrent(q, k, v, la, s0=s0)
+    per_t = q * dq - k * dk_
+    want = np.flip(np.cumsum(np.flip(per_t, 2), 2), 2) + np.sum(dS * S_T, axis=-2)[..., None, :]
+    np.testing.assert_allclose(dla, want, atol=1e-10)
+
+
+def test_gla_backward_with_shared_gate_is_scalar_backward():
+    """A per-channel gate that is the same on every channel is the scalar decay: the GLA
+    gradients equal the scalar-decay ones, and the channel gate gradients sum to the scalar
+    gate gradient."""
+    rng = np.random.default_rng(43)
+    B, H, T, dk, dv = 1, 2, 7, 4, 3
+    q = rng.standard_normal((B, H, T, dk)); k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv)); s0 = rng.standard_normal((B, H, dv, dk))
+    la = -np.logaddexp(0.0, -rng.standard_normal((B, H, T)))
+    do = rng.standard_normal((B, H, T, dv)); dS = rng.standard_normal((B, H, dv, dk))
+    g = orc.gla_backward(q, k, v, np.repeat(la[..., None], dk, axis=-1), do, dS_T=dS, s0=s0)
+    s = orc.scalar_backward(q, k, v, la, do, dS_T=dS, s0=s0)
+    for a, b in zip(g[:3], s[:3]):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+    np.testing.assert_allclose(g[3].sum(axis=-1), s[3], atol=1e-12)
+    np.testing.assert_allclose(g[4], s[4], atol=1e-12)
