@@ -314,12 +314,13 @@ def bench_vla_decode(steps_total, torch, api, synthetic, dev):
 
 
 def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
-    """Backward of a retention or scalar-decay workload (four kernels: forward state pass,
+    """Backward of a retention, scalar-decay or GLA workload (four kernels: forward state pass,
     reverse state pass, gradient pass, gate pass) with a seeded dO and ds_out; beside it
     the forward of the same workload. Algorithmic flops per token-head 8Cd + 10d^2 (the two
     state passes 2d^2 each; Q K^T, dO V^T, dO^T A1, Q^T A2, K^T A2^T 2Cd each over the
     C x C block; R K^T, R^T V^T, S_in^T dO^T 2d^2 each); bytes: read q, k, v, dO, write dq,
-    dk, dv (7 d bf16 per token-head), the gates and three d x d fp32 memories per head."""
+    dk, dv (7 d bf16 per token-head), the gates (GLA: read and their gradient written, 8 d
+    bytes) and three d x d fp32 memories per head."""
     c = synthetic.CONFIGS[name]
     B, H, T, d, C = c["B"], c["H"], c["T"], c["dk"], c["chunk"]
     w = synthetic.config_inputs(name)
@@ -334,6 +335,11 @@ def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
         bwd = lambda: api.la_chunk_bwd(b["q"], b["k"], b["v"], b["log_gamma"], dout, ds_out=ds_out, chunk=C,
                                        workspace=ws)
         gate_bytes = 0
+    elif c["kind"] == "gla":
+        ws = torch.empty(api.bwd_workspace_size(B, H, T, d, d, C, gla=True), dtype=torch.uint8, device=dev)
+        bwd = lambda: api.gla_chunk_bwd(b["q"], b["k"], b["v"], b["log_alpha"], dout, ds_out=ds_out, chunk=C,
+                                        workspace=ws)
+        gate_bytes = 8 * d
     else:
         bwd = lambda: api.mamba2_chunk_bwd(b["q"], b["k"], b["v"], b["log_alpha"], dout, ds_out=ds_out, chunk=C,
                                            workspace=ws)
@@ -563,7 +569,7 @@ def main():
         others["gdelta_decode_n512h32_d128"] = bench_gdelta_decode(min(args.decode_steps, 200), torch, api,
                                                                    synthetic, dev)
         torch.cuda.empty_cache()
-        for name in (MAIN, "mamba2_b8h16_t4096_d128"):
+        for name in (MAIN, "mamba2_b8h16_t4096_d128", "gla_b8h16_t4096_d128"):
             others[name + "_bwd"] = bench_backward(name, max(20, args.steps // 4), max(3, args.warmup // 4), torch,
                                                    api, synthetic, dev)
             torch.cuda.empty_cache()

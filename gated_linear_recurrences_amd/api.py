@@ -181,10 +181,10 @@ def workspace_size(kind, B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16):
     return _native.workspace_size(variant, B, H, T, dk, dv, chunk, code)
 
 
-def bwd_workspace_size(B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16):
-    """Device workspace in bytes for la_chunk_bwd and mamba2_chunk_bwd (bf16 storage)."""
+def bwd_workspace_size(B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16, gla=False):
+    """Device workspace in bytes for la_chunk_bwd and mamba2_chunk_bwd (``gla``: gla_chunk_bwd)."""
     code = _native.LA_BF16 if dtype == torch.bfloat16 else _native.LA_F32
-    return _native.bwd_workspace_size(B, H, T, dk, dv, chunk, code)
+    return _native.bwd_workspace_size(B, H, T, dk, dv, chunk, code, gla)
 
 
 def la_recurrent_step(q, k, v, alpha, s, o=None):
@@ -286,7 +286,7 @@ def vla_recurrent_step(q, k, v, u, s, a, o=None):
     return o
 
 
-def _chunk_bwd(fn, q, k, v, gate, gate_shape, dout, s0, ds_out, chunk, want_ds0, workspace):
+def _chunk_bwd(fn, q, k, v, gate, gate_shape, dout, s0, ds_out, chunk, want_ds0, workspace, gla=False):
     dims, _, _ = _chunk_common(q, k, v, s0, dout, None, False)
     B, H, T, dk, dv = dims
     dev = q.device
@@ -297,7 +297,7 @@ def _chunk_bwd(fn, q, k, v, gate, gate_shape, dout, s0, ds_out, chunk, want_ds0,
     dv_ = torch.empty_like(v)
     dgate = torch.empty(gate_shape, dtype=torch.float32, device=dev)
     ds0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_ds0 else None
-    need = bwd_workspace_size(B, H, T, dk, dv, chunk, q.dtype)
+    need = bwd_workspace_size(B, H, T, dk, dv, chunk, q.dtype, gla)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or not workspace.is_contiguous():
@@ -313,6 +313,12 @@ def la_chunk_bwd(q, k, v, log_gamma, dout, s0=None, ds_out=None, chunk=64, want_
     (dq, dk, dv, dlog_gamma [H], ds0 or None)."""
     return _chunk_bwd(_native.load().la_chunk_bwd, q, k, v, log_gamma, (q.shape[1],), dout, s0, ds_out, chunk,
                       want_ds0, workspace)
+
+
+def gla_chunk_bwd(q, k, v, log_alpha, dout, s0=None, ds_out=None, chunk=64, want_ds0=True, workspace=None):
+    """Gradients of gla_chunk_fwd (bf16): returns (dq, dk, dv, dlog_alpha [B,H,T,d_k], ds0 or None)."""
+    return _chunk_bwd(_native.load().gla_chunk_bwd, q, k, v, log_alpha, tuple(q.shape), dout, s0, ds_out, chunk,
+                      want_ds0, workspace, gla=True)
 
 
 def mamba2_chunk_bwd(q, k, v, log_alpha, dout, s0=None, ds_out=None, chunk=64, want_ds0=True, workspace=None):

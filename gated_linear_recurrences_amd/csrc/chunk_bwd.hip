@@ -1,5 +1,5 @@
 // Dispatch of the bf16 backward kernels by gate variant and chunk length.
-#include "chunk_backward.hpp"
+#include "chunk_backward_gla.hpp"
 #include "launch.hpp"
 
 namespace glr {
@@ -10,10 +10,15 @@ hipError_t launch_chunk_bwd_retention_c64(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bwd_scalar_c16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bwd_scalar_c32(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_chunk_bwd_scalar_c64(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bwd_gla_c16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bwd_gla_c32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_bwd_gla_c64(const BwdArgs& a, hipStream_t stream);
 
-size_t bwd_workspace_size(const BwdArgs& a) {
+size_t bwd_workspace_size(Variant variant, const BwdArgs& a) {
     if (a.B == 0 || a.H == 0) return 0;
-    return ck::bwd_workspace_bytes(static_cast<int64_t>(a.B) * a.H, a.T, a.chunk, a.dk, a.dv);
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    if (variant == kGLA) return ck::bwd_gla_workspace_bytes(heads, a.T, a.chunk, a.dk, a.dv);
+    return ck::bwd_workspace_bytes(heads, a.T, a.chunk, a.dk, a.dv);
 }
 
 hipError_t launch_chunk_bwd(Variant variant, const BwdArgs& a, hipStream_t stream) {
@@ -26,6 +31,10 @@ hipError_t launch_chunk_bwd(Variant variant, const BwdArgs& a, hipStream_t strea
         if (a.chunk == 16) return launch_chunk_bwd_scalar_c16(a, stream);
         if (a.chunk == 32) return launch_chunk_bwd_scalar_c32(a, stream);
         if (a.chunk == 64) return launch_chunk_bwd_scalar_c64(a, stream);
+    } else if (variant == kGLA) {
+        if (a.chunk == 16) return launch_chunk_bwd_gla_c16(a, stream);
+        if (a.chunk == 32) return launch_chunk_bwd_gla_c32(a, stream);
+        if (a.chunk == 64) return launch_chunk_bwd_gla_c64(a, stream);
     }
     return hipErrorInvalidValue;
 }

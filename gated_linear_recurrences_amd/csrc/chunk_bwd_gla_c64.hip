@@ -1,0 +1,8 @@
+// bf16 backward, gate per key channel (GLA), chunk 64: instantiation (kernels in chunk_backward_gla.hpp).
+#include "chunk_backward_gla.hpp"
+
+namespace glr {
+hipError_t launch_chunk_bwd_gla_c64(const BwdArgs& a, hipStream_t stream) {
+    return ck::launch_backward_gla<64>(a, stream);
+}
+}  // namespace glr

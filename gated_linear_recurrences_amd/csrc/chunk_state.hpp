@@ -15,12 +15,12 @@
 // chunk c, the memory entering it (bf16, [d_v][d_k]) to a workspace; the output
 // pass then evaluates all chunks in parallel from those snapshots.
 //
-// REV (backward of the fixed and scalar gates): the same walk from the last chunk
-// to the first carries the gradient R of the loss with respect to the memory at
-// a chunk's last token, R_(c-1) = e^(G_last) R_c + dO_c^T diag(e^G) Q_c - the
-// forward carry with q in place of k, dO in place of v and the weights e^(G_j)
-// (what token j's write reaches of the chunk's end, read backwards); the snapshot
-// of chunk c is R_c, and what is left after chunk 0 is the gradient of S_0.
+// REV (the backward): the same walk from the last chunk to the first carries the
+// gradient R of the loss with respect to the memory at a chunk's last token,
+// R_(c-1) = R_c Diag(e^(G_last)) + sum_i dO_i (q_i e^(G_i))^T - the forward carry with
+// q in place of k, dO in place of v and the weights e^(G_j) (per key channel for
+// GLA) in place of e^(G_last - G_j); the snapshot of chunk c is R_c, and what is left
+// after chunk 0 is the gradient of S_0.
 //
 // Decomposition (gfx950). Transitions act on key channels (columns of S) and
 // the write is an outer product, so every element of S evolves on its own. A
@@ -98,7 +98,6 @@ __global__ __launch_bounds__(64 * NWK * NWV)
 void state_kernel(StateParams p) {
     using Lay = StateLayout<C, NWK, TV, U, GK>;
     constexpr bool GLA = GK == kGateChannel, SCL = GK == kGateScalar;
-    static_assert(!(REV && GLA), "the reverse walk covers the fixed and scalar gates");
     static_assert(Lay::fits, "LDS budget exceeded");
     static_assert(TV % NWV == 0, "value tiles split evenly over the wave groups");
     constexpr int NW = NWK * NWV, NT = 64 * NW, DKB = Lay::DKB, DVB = Lay::DVB;
@@ -283,8 +282,8 @@ void state_kernel(StateParams p) {
         dec[0] = d; dec[1] = d; dec[2] = d; dec[3] = d;
     };
 
-    // GLA: carry weights e^(b_last - b_j) of this lane's tokens for key channel
-    // k0 + 16w + r16, and the decays e^(b_last) of key channels 16w + 4g + r
+    // GLA: carry weights e^(b_last - b_j) (REV: e^(b_j)) of this lane's tokens for key
+    // channel k0 + 16w + r16, and the decays e^(b_last) of key channels 16w + 4g + r
     auto gla_weights = [&](const float* gs, f32x4* wq, f32x4& dec) {
         float tot[CT], exc[CT];
 #pragma unroll
@@ -313,7 +312,7 @@ void state_kernel(StateParams p) {
 #pragma unroll
         for (int q = 0; q < CT; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wq[q][e] = ex2(run - wq[q][e]);
+            for (int e = 0; e < 4; ++e) wq[q][e] = ex2(REV ? wq[q][e] : run - wq[q][e]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dec[r] = ex2(__shfl(run, 4 * g + r, 64));
     };

@@ -159,7 +159,8 @@ la_status gdelta_chunk_fwd_fused(const void* q, const void* k, const void* v, co
     return run_chunk(glr::kGDelta, a, dtype, workspace_bytes, stream);
 }
 
-la_status run_bwd(glr::Variant variant, const glr::BwdArgs& a, la_dtype dtype, size_t ws_bytes, void* stream) {
+static la_status run_bwd(glr::Variant variant, const glr::BwdArgs& a, la_dtype dtype, size_t ws_bytes,
+                         void* stream) {
     // the forward's checks on q, k, v, the gate and the dimensions (o stands for the gradients)
     glr::ChunkArgs f{a.q, a.k, a.v, a.gate, nullptr, a.s0, a.grad_q, nullptr, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
                      a.ws};
@@ -174,7 +175,7 @@ la_status run_bwd(glr::Variant variant, const glr::BwdArgs& a, la_dtype dtype, s
     if ((st = check_ptr(a.dgate, variant == glr::kRetention ? heads : tokens, false, "dgate")) != LA_OK) return st;
     if ((st = check_ptr(a.ds_out, heads, true, "ds_out")) != LA_OK) return st;
     if ((st = check_ptr(a.ds0, heads, true, "ds0")) != LA_OK) return st;
-    const size_t need = glr::bwd_workspace_size(a);
+    const size_t need = glr::bwd_workspace_size(variant, a);
     if (need > 0) {
         if (a.ws == nullptr) return fail(LA_ERR_INVALID, "%s", "workspace is NULL");
         if (!aligned16(a.ws)) return fail(LA_ERR_INVALID, "%s", "workspace is not 16-byte aligned");
@@ -237,8 +238,8 @@ la_status gdelta_recurrent_step(const void* q, const void* k, const void* v, con
     return LA_OK;
 }
 
-la_status la_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
-                                      size_t* bytes) {
+static la_status bwd_workspace_query(glr::Variant variant, int B, int H, int T, int dk, int dv, int chunk,
+                                     la_dtype dtype, size_t* bytes) {
     if (bytes == nullptr) return fail(LA_ERR_INVALID, "%s", "bytes is NULL");
     *bytes = 0;
     glr::ChunkArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
@@ -252,8 +253,18 @@ la_status la_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int c
         return fail(LA_ERR_UNSUPPORTED, "%s", "B * H * ceil(T / chunk) must be below 2^31");
     glr::BwdArgs b{};
     b.B = B; b.H = H; b.T = T; b.dk = dk; b.dv = dv; b.chunk = chunk;
-    *bytes = glr::bwd_workspace_size(b);
+    *bytes = glr::bwd_workspace_size(variant, b);
     return LA_OK;
+}
+
+la_status la_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                                      size_t* bytes) {
+    return bwd_workspace_query(glr::kRetention, B, H, T, dk, dv, chunk, dtype, bytes);
+}
+
+la_status gla_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                                       size_t* bytes) {
+    return bwd_workspace_query(glr::kGLA, B, H, T, dk, dv, chunk, dtype, bytes);
 }
 
 la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float* log_gamma, const float* s0,
@@ -272,6 +283,15 @@ la_status mamba2_chunk_bwd(const void* q, const void* k, const void* v, const fl
     glr::BwdArgs a{q, k, v, log_alpha, s0, dout, ds_out, dq, dk_, dv_, dlog_alpha, ds0, B, H, T, dk, dv, chunk,
                    workspace};
     return run_bwd(glr::kScalar, a, dtype, workspace_bytes, stream);
+}
+
+la_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* s0,
+                        const void* dout, const float* ds_out, void* dq, void* dk_, void* dv_, float* dlog_alpha,
+                        float* ds0, int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    glr::BwdArgs a{q, k, v, log_alpha, s0, dout, ds_out, dq, dk_, dv_, dlog_alpha, ds0, B, H, T, dk, dv, chunk,
+                   workspace};
+    return run_bwd(glr::kGLA, a, dtype, workspace_bytes, stream);
 }
 
 la_status vla_fwd(const void* q, const void* k, const void* v, const void* u, float lambda0, const float* a0,
@@ -342,6 +362,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (2 << 16) | 5; }
+int la_version(void) { return (2 << 16) | 6; }
 
 }  // extern "C"

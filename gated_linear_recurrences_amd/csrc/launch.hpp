@@ -39,24 +39,24 @@ struct DecodeArgs {
     int N, H, dk, dv;
 };
 
-// Backward of the fixed or scalar decay (bf16 storage).
+// Backward of the fixed, scalar or per-channel (GLA) decay (bf16 storage).
 struct BwdArgs {
     const void* q;
     const void* k;
     const void* v;
-    const float* gate;    // fixed: log_gamma [H]; scalar: log_alpha [B,H,T]
+    const float* gate;    // fixed: log_gamma [H]; scalar: log_alpha [B,H,T]; GLA: log_alpha [B,H,T,dk]
     const float* s0;      // [B,H,dv,dk] or nullptr
     const void* dout;     // [B,H,T,dv]: gradient of o
     const float* ds_out;  // [B,H,dv,dk] or nullptr: gradient of the final memory
     void* grad_q;         // [B,H,T,dk]
     void* grad_k;         // [B,H,T,dk]
     void* grad_v;         // [B,H,T,dv]
-    float* dgate;         // fixed: [H]; scalar: [B,H,T]
+    float* dgate;         // fixed: [H]; scalar: [B,H,T]; GLA: [B,H,T,dk]
     float* ds0;           // [B,H,dv,dk] or nullptr
     int B, H, T, dk, dv, chunk;
     void* ws;             // device workspace of at least bwd_workspace_size() bytes
 };
-size_t bwd_workspace_size(const BwdArgs& a);
+size_t bwd_workspace_size(Variant variant, const BwdArgs& a);
 hipError_t launch_chunk_bwd(Variant variant, const BwdArgs& a, hipStream_t stream);
 
 // Variational linear attention over whole sequences (T = 1 and the memory and penalty

@@ -290,6 +290,24 @@ la_status vla_recurrent_step(const void* q, const void* k, const void* v, const 
                              float* s, float* a, void* o, int N, int H, int dk, int dv,
                              la_dtype dtype, void* stream);
 
+/*
+ * Backward of gla_chunk_fwd (gate per key channel): reverse-mode gradients of
+ * the diagonal-gate recurrence ("Scrivere meglio nella memoria", section
+ * "Dimenticare: i gate") through the chunkwise form, with the forward's
+ * per-16-token factorisation of the decays.  As la_chunk_bwd, with the gate
+ * log_alpha [B][H][T][d_k] float32 and its gradient dlog_alpha [B][H][T][d_k]
+ * float32.  The workspace size comes from gla_chunk_bwd_workspace_size: with
+ * N and a(x) as for la_chunk_bwd, 2 a(N*d_v*d_k*2) + a(B*H*d_v*d_k*4) +
+ * a(B*H*T*d_k*4) bytes.  Only LA_BF16 storage.
+ */
+la_status gla_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
+                                       la_dtype dtype, size_t* bytes);
+la_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* s0, const void* dout, const float* ds_out,
+                        void* dq, void* dk_, void* dv_, float* dlog_alpha, float* ds0,
+                        int B, int H, int T, int dk, int dv, int chunk,
+                        la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* la_status_str(la_status status);
 
@@ -299,7 +317,7 @@ const char* la_last_error(void);
 
 /* ABI version: (major << 16) | minor (2.0: workspace arguments; 2.1:
  * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step; 2.3: gdelta_chunk_fwd_fused;
- * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step). */
+ * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step; 2.6: gla_chunk_bwd). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 2
-    assert lib.la_version() & 0xffff >= 5      # 2.1 mamba2, 2.2 gdelta decode, 2.3 fused, 2.4 backward, 2.5 vla
+    assert lib.la_version() & 0xffff >= 6      # 2.1 mamba2, 2.2 gdelta decode, 2.3 fused, 2.4 backward, 2.5 vla,
+    #                                          2.6 gla backward
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -207,7 +208,7 @@ def test_backward_validation(lib):
                                 a["B"], a["H"], a["T"], a["dk_"], a["dv_"], a["chunk"], a["dtype"], P(a["ws"]),
                                 ws_bytes, None)
 
-    for fn in ("la_chunk_bwd", "mamba2_chunk_bwd"):
+    for fn in ("la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd"):
         assert call(fn, dtype=0) == _native.LA_ERR_UNSUPPORTED
         assert b"bf16" in lib.la_last_error()
         assert call(fn, dout=None) == _native.LA_ERR_INVALID
@@ -276,3 +277,14 @@ def test_vla_decode_validation(lib):
     assert call(H=-1) == _native.LA_ERR_INVALID
     assert call(dv=8) == _native.LA_ERR_UNSUPPORTED
     assert call(N=0, q=None, k=None, v=None, u=None, s=None, a=None, o=None) == _native.LA_OK
+
+
+def test_gla_backward_workspace_size(lib):
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    out = ctypes.c_size_t(0)
+    assert lib.gla_chunk_bwd_workspace_size(8, 16, 4096, 128, 128, 64, 1, ctypes.byref(out)) == _native.LA_OK
+    n = 8 * 16 * 64
+    assert out.value == 2 * a256(n * 128 * 128 * 2) + a256(128 * 128 * 128 * 4) + a256(128 * 4096 * 128 * 4)
+    assert lib.gla_chunk_bwd_workspace_size(1, 1, 8, 16, 16, 16, 0, ctypes.byref(out)) == _native.LA_ERR_UNSUPPORTED

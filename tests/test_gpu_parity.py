@@ -296,7 +296,13 @@ def _bwd_gate(name, got, ref, floor=0.0):
 def _gate_terms_floor(kind, q, k, dq, dk):
     """1e-3 of the L2 norm of the gate gradient's terms in absolute value: per token
     sum_{s >= t} |q_s.dq_s| + |k_s.dk_s| (scalar gates), per head the sum over the batch and
-    the tokens of (s + 1) times the same (fixed gates)."""
+    the tokens of (s + 1) times the same (fixed gates); 4e-3 of the norm of the per-channel
+    sums sum_{s >= t} |q_s[c] dq_s[c]| + |k_s[c] dk_s[c]| (GLA)."""
+    if kind == "gla":
+        # per-channel terms: no sum over d_k channels averages the rounding of dq[c] and
+        # dk[c] (bf16 MFMA operands, relative 2^-8), so the floor is 4e-3 of the terms
+        ab = np.abs(np.float64(q) * dq) + np.abs(np.float64(k) * dk)
+        return 4e-3 * float(np.linalg.norm(np.flip(np.cumsum(np.flip(ab, 2), 2), 2)))
     ab = np.abs(np.einsum("bhtc,bhtc->bht", np.float64(q), dq)) + np.abs(np.einsum("bhtc,bhtc->bht", np.float64(k), dk))
     if kind == "retention":
         sc = (ab * (np.arange(ab.shape[-1]) + 1)).sum(axis=(0, 2))
@@ -305,7 +311,7 @@ def _gate_terms_floor(kind, q, k, dq, dk):
     return 1e-3 * float(np.linalg.norm(sc))
 
 
-@pytest.mark.parametrize("kind", ["retention", "mamba2"])
+@pytest.mark.parametrize("kind", ["retention", "mamba2", "gla"])
 @pytest.mark.parametrize("shape", BWD_SHAPES)
 @pytest.mark.parametrize("extras", [False, True])
 def test_backward_parity(kind, shape, extras):
@@ -321,6 +327,10 @@ def test_backward_parity(kind, shape, extras):
         dq, dk_, dv_, dg, ds0 = api.la_chunk_bwd(q, k, v, _t(w.log_gamma), _t(dout, torch.bfloat16), s0=_t(w.s0),
                                                  ds_out=_t(ds_out), chunk=c)
         ref = orc.retention_backward(w.q, w.k, w.v, w.log_gamma, dout, dS_T=ds_out, s0=w.s0)
+    elif kind == "gla":
+        dq, dk_, dv_, dg, ds0 = api.gla_chunk_bwd(q, k, v, _t(w.log_alpha), _t(dout, torch.bfloat16),
+                                                  s0=_t(w.s0), ds_out=_t(ds_out), chunk=c)
+        ref = orc.gla_backward(w.q, w.k, w.v, w.log_alpha, dout, dS_T=ds_out, s0=w.s0)
     else:
         dq, dk_, dv_, dg, ds0 = api.mamba2_chunk_bwd(q, k, v, _t(w.log_alpha), _t(dout, torch.bfloat16),
                                                      s0=_t(w.s0), ds_out=_t(ds_out), chunk=c)
@@ -335,13 +345,15 @@ def test_backward_parity(kind, shape, extras):
     _bwd_gate(f"{label} dgate", dg.cpu().numpy(), ref[3], floor=floor)
 
 
-def test_backward_deterministic():
+@pytest.mark.parametrize("kind", ["mamba2", "gla"])
+def test_backward_deterministic(kind):
     """No atomics: two backward calls give bit-identical gradients."""
-    w = make("mamba2", 2, 2, 150, 128, 128, 64, "bf16", 9, True)
+    w = make(kind, 2, 2, 150, 128, 128, 64, "bf16", 9, True)
     q, k, v = _t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16)
     dout = torch.randn(w.v.shape, device=DEV).to(torch.bfloat16)
-    r1 = api.mamba2_chunk_bwd(q, k, v, _t(w.log_alpha), dout, s0=_t(w.s0))
-    r2 = api.mamba2_chunk_bwd(q, k, v, _t(w.log_alpha), dout, s0=_t(w.s0))
+    fn = api.mamba2_chunk_bwd if kind == "mamba2" else api.gla_chunk_bwd
+    r1 = fn(q, k, v, _t(w.log_alpha), dout, s0=_t(w.s0))
+    r2 = fn(q, k, v, _t(w.log_alpha), dout, s0=_t(w.s0))
     torch.cuda.synchronize()
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
