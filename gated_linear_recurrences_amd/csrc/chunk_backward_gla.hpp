@@ -21,12 +21,19 @@
 // K^ = K~ e^(G_last - r_jt), A2 = dO V^T masked (no decay), the F factors applied to the
 // operand rows (one per lane per 16-token half), the element factors to the results.
 //
+// The gate gradient needs no pass of its own: summed over the tokens after chunk c it is
+// the per-channel d log a of chunk c + 1's first token, sum_m R_c[m][c] S_out[m][c] (the
+// gradient at chunk c's end against the memory there: S_in of chunk c + 1, or S_T), so each
+// chunk writes d log a_t[c] = (sum over its tokens s >= t of q_s[c] dq_s[c] - k_s[c] dk_s[c])
+// + sum_m R_c[m][c] S_out[m][c] directly.
+//
 // Gradient pass (gfx950): persistent workgroups of eight waves, one per CU, each taking
 // (sequence, chunk) items in turn and loading the next item's operands (q, k, v, dO, the
-// gates, R, S_in) into registers while the current one computes. Tiles in LDS use the
-// chunk-swizzled layout; the cumulative gates are an fp32 [C][d_k + 4] table. A wave that
-// computes the dK tile of (feature tile, token tile) also computes the dQ tile of the same
-// pair, so q . dq - k . dk per element is formed in registers and written as fp32.
+// gates, R, S_in, S_out) into registers while the current one computes. Tiles in LDS use
+// the chunk-swizzled layout; the cumulative gates are an fp32 [C][d_k + 4] table. A wave
+// that computes the dK tile of (feature tile, token tile) also computes the dQ tile of the
+// same pair, so q . dq - k . dk per element is formed in registers; the chunk's reverse
+// scan of it per channel runs in LDS after the products.
 #pragma once
 
 #include "chunk_backward.hpp"
@@ -45,7 +52,8 @@ struct GradGlaParams {
     u16* dq;               // [BH][T][DK]
     u16* dk;               // [BH][T][DK]
     u16* dv;               // [BH][T][DV]
-    float* gq;             // [BH][T][DK]: q . dq - k . dk per element
+    const float* s_fin;    // [BH][DV][DK] fp32 final memory (S_out of the last chunk)
+    float* dgate;          // [BH][T][DK] gradient of log alpha
     int T, NC, items;
 };
 
@@ -69,7 +77,8 @@ struct GradGlaLayout {
     static constexpr int oF = oG + al(C * GS * 4);                       // F [NF][DK]
     static constexpr int oL = oF + al((NF > 0 ? NF : 1) * DK * 4);       // e^(G_last - r_t) [CT][DK]
     static constexpr int oR = oL + al(CT * DK * 4);                      // r_t [CT][DK] (log2)
-    static constexpr int bytes = oR + al(CT * DK * 4);
+    static constexpr int oO2 = oR + al(CT * DK * 4);                     // per-wave offsets [8][DK]
+    static constexpr int bytes = oO2 + al(8 * DK * 4);
     static_assert(bytes <= 160 * 1024, "LDS budget of the GLA gradient pass exceeded");
 };
 
@@ -105,6 +114,7 @@ void grad_gla_kernel(GradGlaParams p) {
     float* const sF = reinterpret_cast<float*>(smem + Lay::oF);
     float* const sL = reinterpret_cast<float*>(smem + Lay::oL);
     float* const sR = reinterpret_cast<float*>(smem + Lay::oR);
+    float* const sOff = reinterpret_cast<float*>(smem + Lay::oO2);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,8 +122,10 @@ void grad_gla_kernel(GradGlaParams p) {
     const int T = p.T;
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
-    // ---- operands of an item in registers (rows past the end read row 0, zeroed on use)
-    u16x8 rq[QP_PER], rk[QP_PER], rv[VP_PER], ro[VP_PER], rx[XP_PER], rs[XP_PER];
+    // ---- operands of an item in registers (rows past the end read row 0, zeroed on use):
+    // q, k, v, dO are loaded an item ahead; R and the gates when the item starts, S_in and
+    // S_out after its staging
+    u16x8 rq[QP_PER], rk[QP_PER], rv[VP_PER], ro[VP_PER], rx[XP_PER], rs[XP_PER], rn[XP_PER];
     f32x4 rg[GP_PER];
     auto load_item = [&](int item) {
         const int lbh = item / p.NC, lc = item % p.NC;
@@ -136,12 +148,18 @@ void grad_gla_kernel(GradGlaParams p) {
             rv[i] = *reinterpret_cast<const u16x8*>(p.v + ltok0 * DV + off);
             ro[i] = *reinterpret_cast<const u16x8*>(p.dout + ltok0 * DV + off);
         }
+    };
+    // R and the gates of the current item, loaded when the item starts
+    auto load_rg = [&](int item) {
+        const int lbh = item / p.NC, lc = item % p.NC;
+        const int lt0 = lc * C, ln = (T - lt0 < C) ? (T - lt0) : C;
+        const int64_t ltok0 = static_cast<int64_t>(lbh) * T + lt0;
+        const int64_t lchunk = static_cast<int64_t>(lbh) * p.NC + lc;
 #pragma unroll
         for (int i = 0; i < XP_PER; ++i) {
             const int idx = tid + i * NT;
             const unsigned off = (idx < XP) ? static_cast<unsigned>(idx * 8) : 0u;
             rx[i] = *reinterpret_cast<const u16x8*>(p.r + lchunk * DV * DK + off);
-            rs[i] = *reinterpret_cast<const u16x8*>(p.s_in + lchunk * DV * DK + off);
         }
 #pragma unroll
         for (int i = 0; i < GP_PER; ++i) {
@@ -152,6 +170,31 @@ void grad_gla_kernel(GradGlaParams p) {
         }
     };
 
+    // the memories of the current item: S_in, and S_out (the next chunk's S_in, or the final
+    // memory in fp32, rounded like the snapshots); loaded at the start of the item, used at
+    // the end of its dK phase
+    auto load_mem = [&](int item) {
+        const int lbh = item / p.NC, lc = item % p.NC;
+        const int64_t lchunk = static_cast<int64_t>(lbh) * p.NC + lc;
+#pragma unroll
+        for (int i = 0; i < XP_PER; ++i) {
+            const int idx = tid + i * NT;
+            const unsigned off = (idx < XP) ? static_cast<unsigned>(idx * 8) : 0u;
+            rs[i] = *reinterpret_cast<const u16x8*>(p.s_in + lchunk * DV * DK + off);
+            if (lc + 1 < p.NC) {
+                rn[i] = *reinterpret_cast<const u16x8*>(p.s_in + (lchunk + 1) * DV * DK + off);
+            } else {
+                const float* sf = p.s_fin + static_cast<int64_t>(lbh) * DV * DK + off;
+                const f32x4 a0 = ldf4(sf), a1 = ldf4(sf + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    rn[i][e] = f32_to_bf16_bits(a0[e]);
+                    rn[i][4 + e] = f32_to_bf16_bits(a1[e]);
+                }
+            }
+        }
+    };
+
     int item = blockIdx.x;
     if (item >= p.items) return;
     load_item(item);
@@ -159,6 +202,7 @@ void grad_gla_kernel(GradGlaParams p) {
         const int bh = item / p.NC, c = item % p.NC;
         const int t0 = c * C, n = (T - t0 < C) ? (T - t0) : C;
         const int64_t tok0 = static_cast<int64_t>(bh) * T + t0;
+        load_rg(item);
 
         // ---- stage v, dO, R and the raw gates (log2 units; rows past the end zero)
 #pragma unroll
@@ -189,6 +233,7 @@ void grad_gla_kernel(GradGlaParams p) {
                 stf4(sG + j * GS + col, (j < n) ? rg[i] * kLog2e : zf4());
             }
         }
+        load_mem(item);   // in flight while the tables and the products of the first half run
         lds_barrier();
         // chunk-local inclusive cumulative gates: lane (key 16kt + r16, run g) scans tokens
         // 16g .. 16g + 15 of its key channel; runs are joined over g by shuffles
@@ -253,9 +298,6 @@ void grad_gla_kernel(GradGlaParams p) {
                 *reinterpret_cast<bf16x8*>(sK + TQ::off(j, col)) = pack8(ks[0], ks[1], ks[2], ks[3], ks[4], ks[5], ks[6], ks[7]);
             }
         }
-        u16x8 rs_cur[XP_PER];
-#pragma unroll
-        for (int i = 0; i < XP_PER; ++i) rs_cur[i] = rs[i];
         const int step = static_cast<int>(gridDim.x);
         const int next = (item < p.items - step) ? item + step : p.items;
         if (next < p.items) load_item(next);   // in flight during this item's products
@@ -343,6 +385,7 @@ void grad_gla_kernel(GradGlaParams p) {
         f32x4 gk[MAXT];
 #pragma unroll
         for (int s = 0; s < MAXT; ++s) {
+            __builtin_amdgcn_sched_barrier(0);   // one tile at a time: bounds the registers in flight
             gk[s] = zf4();
             const int u = w + NW * s;
             if (u >= FK * CT) continue;
@@ -385,14 +428,45 @@ void grad_gla_kernel(GradGlaParams p) {
                 gk[s] = kj * dkv;
             }
         }
+        // chunk offset of the gate gradient, sum_m R[m][c] S_out[m][c], R read back from LDS: a
+        // thread's pieces share one group of 8 channels (idx % (DK / 8) does not depend on i);
+        // partial sums meet over the wave's lanes of that group, then over the waves in LDS
+        {
+            float po[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) po[e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < XP_PER; ++i) {
+                const int idx = tid + i * NT;
+                if (XP % NT == 0 || idx < XP) {
+                    const int m = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
+                    const u16x8 rr = *reinterpret_cast<const u16x8*>(sX + TQ::off(m, col));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) po[e] += bf16_bits_to_f32(rr[e]) * bf16_bits_to_f32(rn[i][e]);
+                }
+            }
+            constexpr int G8 = DK / 8;   // channel groups; lanes l and l + G8 share one
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+#pragma unroll
+                for (int off = G8; off < 64; off <<= 1) po[e] += __shfl_xor(po[e], off, 64);
+            }
+            if (lane < G8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sOff[w * DK + lane * 8 + e] = po[e];
+            }
+        }
         lds_barrier();   // R is dead: the region takes S_in
-        stage_x(rs_cur);
+        stage_x(rs);
         lds_barrier();
 
         // ---- dQ^T tiles (key tile ft, token tile it), the same pairs as the dK tiles of this
         // wave; lane holds dQ[i = 16it + r16][c = 16ft + 4g + r]
+        f32x4 gqv[MAXT];
 #pragma unroll
         for (int s = 0; s < MAXT; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            gqv[s] = zf4();
             const int u = w + NW * s;
             if (u >= FK * CT) continue;
             const int ft = u / CT, it = u % CT;
@@ -433,8 +507,41 @@ void grad_gla_kernel(GradGlaParams p) {
             if (i < n) {
                 st4(p.dq + (tok0 + i) * DK + c4, cvt4(dqv));
                 const f32x4 qv = up4(ld4(p.q + (tok0 + i) * DK + c4));
-                stf4(p.gq + (tok0 + i) * DK + c4, qv * dqv - gk[s]);
+                gqv[s] = qv * dqv - gk[s];
             }
+        }
+        lds_barrier();   // the gate table is free: it takes q . dq - k . dk per element
+#pragma unroll
+        for (int s = 0; s < MAXT; ++s) {
+            const int u = w + NW * s;
+            if (u >= FK * CT) continue;
+            const int ft = u / CT, it = u % CT;
+            stf4(sG + (16 * it + r16) * GS + 16 * ft + 4 * g, gqv[s]);
+        }
+        lds_barrier();
+        // ---- gate gradients: per key channel, the reverse cumulative sum over the chunk's
+        // tokens plus the chunk offset; lane (key 16kt + r16, run g) takes tokens 16g .. 16g + 15
+        for (int kt = w; kt < DK / 16; kt += NW) {
+            const int key = 16 * kt + r16;
+            float off = 0.f;
+#pragma unroll
+            for (int u = 0; u < NW; ++u) off += sOff[u * DK + key];
+            float tv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tv[e] = (16 * g + e < C) ? sG[(16 * g + e) * GS + key] : 0.f;
+#pragma unroll
+            for (int e = 14; e >= 0; --e) tv[e] += tv[e + 1];
+            // sum of the later runs of this channel
+            float inc = tv[0];
+            float y = __shfl_down(inc, 16, 64);
+            if (g <= 2) inc += y;
+            y = __shfl_down(inc, 32, 64);
+            if (g <= 1) inc += y;
+            const float base = inc - tv[0] + off;
+            float* dst = p.dgate + tok0 * DK + key;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (16 * g + e < n) dst[static_cast<int64_t>(16 * g + e) * DK] = tv[e] + base;
         }
         lds_barrier();   // every read of this item's tiles is done before the next staging
         if (next >= p.items) break;
@@ -442,54 +549,12 @@ void grad_gla_kernel(GradGlaParams p) {
     }
 }
 
-// Per-channel gate gradients, one workgroup of 256 threads per sequence:
-// d log a_t[c] = sum_{s>=t} g_s[c] + sum_m dS_T[m][c] S_T[m][c]. Thread (c = tid % DK,
-// part = tid / DK) owns a contiguous run of tokens of channel c; the runs' totals are
-// joined through LDS in part order (no atomics).
-template <int DK>
-__global__ __launch_bounds__(256)
-void gate_grad_channel_kernel(const float* __restrict__ gq, const float* __restrict__ ds_out,
-                              const float* __restrict__ s_fin, float* __restrict__ dgate, int T, int DV) {
-    constexpr int P = 256 / DK;   // parts per channel
-    __shared__ float part_sum[P][DK];
-    __shared__ float part_fin[P][DK];
-    const int tid = threadIdx.x;
-    const int c = tid % DK, part = tid / DK;
-    const int64_t bh = blockIdx.x;
-    float fin = 0.f;
-    if (ds_out != nullptr) {
-        const float* a = ds_out + bh * DV * DK;
-        const float* b = s_fin + bh * DV * DK;
-        for (int m = part; m < DV; m += P) fin += a[m * DK + c] * b[m * DK + c];
-    }
-    const float* g = gq + bh * T * DK;
-    const int per = (T + P - 1) / P;
-    const int lo = (part * per < T) ? part * per : T, hi = (lo + per < T) ? lo + per : T;
-    float run = 0.f;
-    for (int t = lo; t < hi; ++t) run += g[static_cast<int64_t>(t) * DK + c];
-    part_sum[part][c] = run;
-    part_fin[part][c] = fin;
-    __syncthreads();
-    float after = 0.f, tot_fin = 0.f;
-#pragma unroll
-    for (int u = 0; u < P; ++u) {
-        if (u > part) after += part_sum[u][c];
-        tot_fin += part_fin[u][c];
-    }
-    float acc = after + tot_fin;
-    float* out = dgate + bh * T * DK;
-    for (int t = hi - 1; t >= lo; --t) {
-        acc += g[static_cast<int64_t>(t) * DK + c];
-        out[static_cast<int64_t>(t) * DK + c] = acc;
-    }
-}
-
 // Workspace of a GLA backward call: the forward and the backward snapshots
-// ([BH][NC][DV][DK] bf16 each), the final memory [BH][DV][DK] fp32 and the per-element
-// sums [BH][T][DK] fp32, each from a 256-byte boundary.
+// ([BH][NC][DV][DK] bf16 each) and the final memory [BH][DV][DK] fp32, each from a
+// 256-byte boundary.
 inline size_t bwd_gla_workspace_bytes(int64_t heads, int T, int chunk, int dk, int dv) {
     const int64_t nc = (T + chunk - 1) / chunk;
-    return 2 * bwd_align(heads * nc * dv * dk * 2) + bwd_align(heads * dv * dk * 4) + bwd_align(heads * T * dk * 4);
+    return 2 * bwd_align(heads * nc * dv * dk * 2) + bwd_align(heads * dv * dk * 4);
 }
 
 template <int C, int DK, int DV>
@@ -500,7 +565,6 @@ hipError_t launch_backward_gla_dv(const BwdArgs& a, hipStream_t stream) {
     u16* fwd = reinterpret_cast<u16*>(base);
     u16* rev = reinterpret_cast<u16*>(base + bwd_align(heads * NC * DV * DK * 2));
     float* sfin = reinterpret_cast<float*>(base + 2 * bwd_align(heads * NC * DV * DK * 2));
-    float* gq = reinterpret_cast<float*>(base + 2 * bwd_align(heads * NC * DV * DK * 2) + bwd_align(heads * DV * DK * 4));
     // forward state pass (snapshots and final memory), then the same walk backwards on (q, dO)
     ChunkArgs f{a.q, a.k, a.v, a.gate, nullptr, a.s0, nullptr, sfin, a.B, a.H, a.T, DK, DV, C, fwd};
     ChunkArgs r{a.q, a.q, a.dout, a.gate, nullptr, a.ds_out, nullptr, a.ds0, a.B, a.H, a.T, DK, DV, C, rev};
@@ -542,7 +606,8 @@ hipError_t launch_backward_gla_dv(const BwdArgs& a, hipStream_t stream) {
     p.dq = static_cast<u16*>(a.grad_q);
     p.dk = static_cast<u16*>(a.grad_k);
     p.dv = static_cast<u16*>(a.grad_v);
-    p.gq = gq;
+    p.s_fin = sfin;
+    p.dgate = a.dgate;
     p.T = a.T;
     p.NC = NC;
     p.items = static_cast<int>(heads * NC);
@@ -556,10 +621,6 @@ hipError_t launch_backward_gla_dv(const BwdArgs& a, hipStream_t stream) {
     const int64_t slots = static_cast<int64_t>(cus) * per_cu;
     const int grid = p.items < slots ? p.items : static_cast<int>(slots);
     hipLaunchKernelGGL((grad_gla_kernel<C, DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream, p);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gate_grad_channel_kernel<DK>), dim3(static_cast<unsigned>(heads)), dim3(256), 0, stream, gq,
-                       a.ds_out, sfin, a.dgate, a.T, DV);
     return hipGetLastError();
 }
 

@@ -297,8 +297,8 @@ la_status vla_recurrent_step(const void* q, const void* k, const void* v, const 
  * per-16-token factorisation of the decays.  As la_chunk_bwd, with the gate
  * log_alpha [B][H][T][d_k] float32 and its gradient dlog_alpha [B][H][T][d_k]
  * float32.  The workspace size comes from gla_chunk_bwd_workspace_size: with
- * N and a(x) as for la_chunk_bwd, 2 a(N*d_v*d_k*2) + a(B*H*d_v*d_k*4) +
- * a(B*H*T*d_k*4) bytes.  Only LA_BF16 storage.
+ * N and a(x) as for la_chunk_bwd, 2 a(N*d_v*d_k*2) + a(B*H*d_v*d_k*4) bytes.
+ * Only LA_BF16 storage.
  */
 la_status gla_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
                                        la_dtype dtype, size_t* bytes);
