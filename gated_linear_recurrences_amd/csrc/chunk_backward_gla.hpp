@@ -28,8 +28,9 @@
 // + sum_m R_c[m][c] S_out[m][c] directly.
 //
 // Gradient pass (gfx950): persistent workgroups of eight waves, one per CU, each taking
-// (sequence, chunk) items in turn and loading the next item's operands (q, k, v, dO, the
-// gates, R, S_in, S_out) into registers while the current one computes. Tiles in LDS use
+// (sequence, chunk) items in turn and loading the next item's q, k, v and dO into registers
+// while the current one computes (its gates and R are loaded as it starts, S_in and S_out
+// while its tables are built). Tiles in LDS use
 // the chunk-swizzled layout; the cumulative gates are an fp32 [C][d_k + 4] table. A wave
 // that computes the dK tile of (feature tile, token tile) also computes the dQ tile of the
 // same pair, so q . dq - k . dk per element is formed in registers; the chunk's reverse
@@ -131,7 +132,6 @@ void grad_gla_kernel(GradGlaParams p) {
         const int lbh = item / p.NC, lc = item % p.NC;
         const int lt0 = lc * C, ln = (T - lt0 < C) ? (T - lt0) : C;
         const int64_t ltok0 = static_cast<int64_t>(lbh) * T + lt0;
-        const int64_t lchunk = static_cast<int64_t>(lbh) * p.NC + lc;
 #pragma unroll
         for (int i = 0; i < QP_PER; ++i) {
             const int idx = tid + i * NT;

@@ -20,6 +20,7 @@ hipError_t launch_chunk_bf16_gdelta_c64(const ChunkArgs& a, hipStream_t stream);
 size_t chunk_workspace_bytes(Variant variant, const ChunkArgs& a, bool bf16) {
     if (!bf16 || a.B == 0 || a.H == 0) return 0;
     const size_t chunks = static_cast<size_t>((a.T + a.chunk - 1) / a.chunk);
+    if (single_pass_forward(variant, a)) return 0;
     if (variant == kGDelta)
         return ck::delta_ws_bytes(static_cast<int64_t>(a.B) * a.H * chunks, a.chunk, a.dk, a.dv, (a.fuse & 1) != 0);
     return static_cast<size_t>(a.B) * a.H * chunks * a.dv * a.dk * 2;

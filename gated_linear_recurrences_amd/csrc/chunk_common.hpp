@@ -83,6 +83,17 @@ struct SwzTile {
             return r * STRIDE + c;
         }
     }
+    // The logical 8-element chunk held at physical chunk p of row r (-1: padding): the
+    // inverse of off, for loads that fill a tile in physical order.
+    __device__ static __forceinline__ int chunk_at(int r, int p) {
+        if constexpr (W == 128) {
+            return p ^ (((r & 7) << 1) | ((r >> 3) & 1));
+        } else if constexpr (W == 64) {
+            return p ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+        } else {
+            return p * 8 < W ? p : -1;
+        }
+    }
 };
 
 // tr_op on a SwzTile: lane (r, g) receives X[base+4g+e][n0+r], e = 0..3.

@@ -362,6 +362,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (2 << 16) | 6; }
+int la_version(void) { return (2 << 16) | 7; }
 
 }  // extern "C"

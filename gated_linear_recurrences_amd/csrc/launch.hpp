@@ -76,6 +76,14 @@ struct VlaArgs {
 };
 hipError_t launch_vla(bool bf16, const VlaArgs& a, hipStream_t stream);
 
+// Retention and the scalar decay (bf16 storage) take the single-pass forward, which needs no
+// workspace, when the sequences times the 16-channel value slices fill at least half the
+// CUs; with fewer, the two-pass form spreads the chunks of each sequence over the chip.
+inline bool single_pass_forward(Variant variant, const ChunkArgs& a) {
+    return (variant == kRetention || variant == kScalar) &&
+           static_cast<long long>(a.B) * a.H * (a.dv / 16) >= 128;
+}
+
 // float32 storage, fp32 arithmetic (VALU).
 hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t stream);
 // Device workspace the chunk kernels of (variant, shape, storage) need, in bytes.

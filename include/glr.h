@@ -89,10 +89,11 @@ typedef enum la_variant {
  * Workspace needed by a chunk entry point of `variant` for these sizes, in
  * bytes, written to *bytes (0 when none is needed).  Checks the sizes like the
  * entry point does (status and la_last_error() as there); the pointers of the
- * entry point are not involved.  For bf16 storage, retention, the scalar
- * data-dependent decay and GLA pass the memory entering every chunk from their
- * state pass to their output pass:
- * B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.  The gated delta rule in bf16
+ * entry point are not involved.  For bf16 storage, retention and the scalar
+ * data-dependent decay run in a single pass with no workspace when
+ * B * H * (d_v / 16) >= 128 (the memory stays on chip); below that, and for
+ * GLA always, the memory entering every chunk goes from a state pass to an
+ * output pass: B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.  The gated delta rule in bf16
  * also passes, per (sequence, chunk), its WY factor W (chunk x d_k bf16), the
  * pseudo-values (d_v x chunk float32) and the cumulative log-gates (chunk
  * float32): with N = B * H * ceil(T / chunk) and a(x) = x rounded up to a
@@ -317,7 +318,8 @@ const char* la_last_error(void);
 
 /* ABI version: (major << 16) | minor (2.0: workspace arguments; 2.1:
  * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step; 2.3: gdelta_chunk_fwd_fused;
- * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step; 2.6: gla_chunk_bwd). */
+ * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step; 2.6: gla_chunk_bwd;
+ * 2.7: single-pass retention and scalar-decay forward, no workspace at B * H * d_v / 16 >= 128). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -38,8 +38,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 2
-    assert lib.la_version() & 0xffff >= 6      # 2.1 mamba2, 2.2 gdelta decode, 2.3 fused, 2.4 backward, 2.5 vla,
-    #                                          2.6 gla backward
+    assert lib.la_version() & 0xffff >= 7      # 2.1 mamba2, 2.2 gdelta decode, 2.3 fused, 2.4 backward, 2.5 vla,
+    #                                          2.6 gla backward, 2.7 single-pass forward
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -75,9 +75,16 @@ def _ws(lib, variant, B=1, H=1, T=8, dk=16, dv=16, chunk=16, dtype=1):
 
 
 def test_workspace_size_query(lib):
-    # retention, the scalar decay and GLA in bf16: one bf16 d_v x d_k memory per (sequence, chunk)
+    # retention, the scalar decay and GLA in bf16, two-pass forward: one bf16 d_v x d_k memory
+    # per (sequence, chunk). Retention and the scalar decay take the single-pass forward, with
+    # no workspace, once B * H * d_v / 16 >= 128.
+    assert _ws(lib, _native.LA_GLA, B=4, H=8, T=2048, dk=128, dv=128, chunk=64) == (_native.LA_OK, 32 * 32 * 128 * 128 * 2)
+    for variant in (_native.LA_RETENTION, _native.LA_MAMBA2):
+        assert _ws(lib, variant, B=4, H=8, T=2048, dk=128, dv=128, chunk=64) == (_native.LA_OK, 0)
+        assert _ws(lib, variant, B=4, H=4, T=100, dk=64, dv=128, chunk=64) == (_native.LA_OK, 0)
+        assert _ws(lib, variant, B=2, H=4, T=100, dk=64, dv=128, chunk=64) == (_native.LA_OK, 8 * 2 * 128 * 64 * 2)
+        assert _ws(lib, variant, B=8, H=8, T=100, dk=64, dv=16, chunk=64) == (_native.LA_OK, 64 * 2 * 16 * 64 * 2)
     for variant in (_native.LA_RETENTION, _native.LA_MAMBA2, _native.LA_GLA):
-        assert _ws(lib, variant, B=4, H=8, T=2048, dk=128, dv=128, chunk=64) == (_native.LA_OK, 32 * 32 * 128 * 128 * 2)
         assert _ws(lib, variant, B=1, H=2, T=65, dk=32, dv=64, chunk=32) == (_native.LA_OK, 2 * 3 * 64 * 32 * 2)
         assert _ws(lib, variant, T=0) == (_native.LA_OK, 0)
         assert _ws(lib, variant, B=0) == (_native.LA_OK, 0)

@@ -141,6 +141,37 @@ def test_bf16_chunk_parity(kind, shape, state):
     assert_parity(w, o, S, o_ref, S_ref, f"{kind} bf16 {shape} state={state}")
 
 
+# (B, H, T, d_k, d_v, chunk) with B * H * d_v / 16 >= 128: retention and the scalar decay take
+# the single-pass forward there (no workspace). Every d_k, d_v and chunk, value slices of 16
+# and 32 channels, ragged tails, a lone partial chunk, T = 1 and T = 0.
+SINGLE_PASS_SHAPES = [
+    (2, 8, 100, 16, 128, 16),     # 16-channel slices, d_k = 16
+    (4, 8, 77, 32, 64, 32),
+    (8, 8, 130, 64, 32, 64),
+    (16, 16, 45, 128, 16, 64),    # one partial chunk, d_v = 16
+    (4, 16, 200, 128, 128, 64),   # 32-channel slices
+    (16, 16, 40, 32, 128, 16),    # 32-channel slices, chunk 16
+    (2, 64, 1, 64, 64, 64),
+    (8, 8, 0, 64, 32, 64),
+]
+
+
+@pytest.mark.parametrize("kind", ["retention", "mamba2"])
+@pytest.mark.parametrize("shape", SINGLE_PASS_SHAPES)
+@pytest.mark.parametrize("state", [False, True])
+def test_bf16_single_pass_parity(kind, shape, state):
+    B, H, T, dk, dv, chunk = shape
+    assert B * H * dv // 16 >= 128
+    assert api.workspace_size(kind, *shape) == 0
+    w = make(kind, *shape, dtype="bf16", seed=500 + sum(shape), state=state)
+    o, S = run_gpu(w)
+    o_ref, S_ref = run_oracle(w)
+    if T == 0:
+        np.testing.assert_array_equal(S, w.s0.astype(np.float64) if state else 0.0)
+        return
+    assert_parity(w, o, S, o_ref, S_ref, f"{kind} single pass {shape} state={state}")
+
+
 @pytest.mark.parametrize("name", ["retention_b4h8_t2048_d128", "gla_b8h16_t4096_d128",
                                   "gdelta_b4h16_t8192_d128", "mamba2_b8h16_t4096_d128"])
 def test_bf16_full_config_parity(name):
@@ -167,14 +198,18 @@ def test_empty_sequence_hands_state_through(kind, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("kind", KINDS)
-def test_resume_and_in_place_state(kind, dtype):
-    """Two calls (first 93 tokens, then the rest from s_out, in place s0 == s_out) match one call."""
-    w = make(kind, 1, 2, 160, 128, 64, 64, dtype, 8, True)
+@pytest.mark.parametrize("heads", [(1, 2), (4, 8)])
+def test_resume_and_in_place_state(kind, dtype, heads):
+    """Two calls (first 93 tokens, then the rest from s_out, in place s0 == s_out) match one
+    call. (4, 8) heads at d_v = 64 take the single-pass forward for retention and the scalar
+    decay, (1, 2) the two-pass one."""
+    B, H = heads
+    w = make(kind, B, H, 160, 128, 64, 64, dtype, 8, True)
     o_full, S_full = run_gpu(w)
     st = _storage(w)
 
     def part(sl, s):
-        sub = make(kind, 1, 2, 160, 128, 64, 64, dtype, 8, True)
+        sub = make(kind, B, H, 160, 128, 64, 64, dtype, 8, True)
         sub.q, sub.k, sub.v = w.q[..., sl, :], w.k[..., sl, :], w.v[..., sl, :]
         if kind == "gla":
             sub.log_alpha = w.log_alpha[..., sl, :]
@@ -206,9 +241,11 @@ def test_resume_and_in_place_state(kind, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("kind", KINDS)
-def test_deterministic(kind, dtype):
-    """No atomics on the path: two runs give bit-identical outputs."""
-    w = make(kind, 2, 2, 150, 128, 128, 64, dtype, 9, True)
+@pytest.mark.parametrize("heads", [(2, 2), (4, 4)])
+def test_deterministic(kind, dtype, heads):
+    """No atomics on the path: two runs give bit-identical outputs ((4, 4) heads at d_v = 128:
+    the single-pass forward for retention and the scalar decay)."""
+    w = make(kind, *heads, 150, 128, 128, 64, dtype, 9, True)
     o1, S1 = run_gpu(w)
     o2, S2 = run_gpu(w)
     np.testing.assert_array_equal(o1, o2)
