@@ -1,19 +1,21 @@
 #!/usr/bin/env python3
 """Throughput of the chunked forward on one MI355X, with its roofline and the CPU oracle beside it.
 
-A step is one call of the chunked forward - every stage of the hot path: the
-state pass (memory carried from chunk to chunk, snapshots of the memory
-entering each chunk) and the output pass (decayed triangle, P V, memory
-readout, stores) - over one batch of the multi-scale retention workload: B=4,
+A step is one call of the chunked forward - every stage of the hot path (the
+memory carried from chunk to chunk, the decayed triangle, P V, the memory
+readout, the stores), which at this size runs as one single-pass kernel (the
+memory stays on chip; smaller batches take a state pass and an output pass) -
+over one batch of the multi-scale retention workload: B=4,
 H=8, T=2048, d_k=d_v=128, bf16 q/k/v ~ N(0,1)/sqrt(128), per-head decay
 1 - 2^(-5-h), chunk 64, fp32 memory. Inputs are resident in HBM before timing;
 five input sets are rotated so the 256 MB Infinity Cache cannot serve them.
 
 Printed: one JSON line. ``value`` is tokens/s (B*H*T per second); ``roofline``
-prices the call (both kernels, timed with HIP events on the launching stream)
+prices the call (its kernel, timed with HIP events on the launching stream around
+one HIP-graph replay of the timed steps, so that host launches do not pace it)
 against HBM with the algorithmic bytes of the method (q, k, v read, o and the
 final memory written); ``traffic`` is the HBM traffic the counters measured for
-one call, snapshots included; ``mfma`` gives the same run against the dense bf16
+one call; ``mfma`` gives the same run against the dense bf16
 MFMA peak; ``cpu_baseline`` times the fp64 oracle on the host; ``others``
 reports the per-channel-gate (GLA), gated-delta, scalar data-dependent decay
 and decode (per-channel gate, gated delta rule) workloads measured the same way,
@@ -25,6 +27,7 @@ variational linear attention (whole sequences, and decode).
     python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
     python bench.py --kernel-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+    python bench.py --trace-table TRACE_DIR
 """
 
 import argparse
@@ -102,14 +105,38 @@ def make_call(kind, api, bufs, chunk, torch):
                                         o=o, s_out=s_out, workspace=ws)
 
 
-def time_calls(calls, steps, warmup, torch):
+def time_calls(calls, steps, warmup, torch, graph=False):
     """Run ``warmup`` untimed steps, then ``steps`` timed ones rotating over ``calls``.
 
-    Returns (wall ms per step over the bracketed region, mean kernel ms from per-launch
-    HIP events recorded on the launching stream)."""
+    Returns (wall ms per step over the bracketed region, mean kernel ms from HIP events
+    recorded on the launching stream). With ``graph`` the timed steps are captured once in
+    a HIP graph and replayed: the host then cannot pace a kernel shorter than its own
+    launch path, and the per-step time is the region's over the replay. The replay's
+    outputs are checked against one eager call per input set first (bit for bit: the
+    kernels are deterministic)."""
     for i in range(warmup):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
+    if graph:
+        eager = [tuple(t.clone() for t in c() if t is not None) for c in calls]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            outs = [calls[i % len(calls)]() for i in range(steps)]
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(min(steps, len(calls))):
+            got = tuple(t for t in outs[i] if t is not None)
+            if not all(torch.equal(a, b) for a, b in zip(got, eager[i])):
+                raise RuntimeError("graph replay differs from the eager call")
+        region0 = torch.cuda.Event(enable_timing=True)
+        region1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        region0.record()
+        g.replay()
+        region1.record()
+        torch.cuda.synchronize()
+        ms = region0.elapsed_time(region1) / steps
+        return ms, ms
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     region0 = torch.cuda.Event(enable_timing=True)
@@ -142,7 +169,7 @@ def bench_chunk(name, steps, warmup, torch, api, synthetic, dev, n_sets=N_SETS):
             w = fn(base["B"], base["H"], base["T"], base["dk"], base["dv"], **kw)
         sets.append(make_call(c["kind"], api, upload(w, torch, dev), c["chunk"], torch))
         del w
-    ms_wall, ms_kernel = time_calls(sets, steps, warmup, torch)
+    ms_wall, ms_kernel = time_calls(sets, steps, warmup, torch, graph=True)
     flops, bytes_ = algorithmic_counts(c["kind"], c["B"], c["H"], c["T"], c["dk"], c["chunk"])
     tokens = c["B"] * c["H"] * c["T"]
     return dict(
@@ -314,8 +341,8 @@ def bench_vla_decode(steps_total, torch, api, synthetic, dev):
 
 
 def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
-    """Backward of a retention, scalar-decay or GLA workload (four kernels: forward state pass,
-    reverse state pass, gradient pass, gate pass) with a seeded dO and ds_out; beside it
+    """Backward of a retention, scalar-decay or GLA workload (forward state pass, reverse state
+    pass, gradient pass, and for the first two a gate pass) with a seeded dO and ds_out; beside it
     the forward of the same workload. Algorithmic flops per token-head 8Cd + 10d^2 (the two
     state passes 2d^2 each; Q K^T, dO V^T, dO^T A1, Q^T A2, K^T A2^T 2Cd each over the
     C x C block; R K^T, R^T V^T, S_in^T dO^T 2d^2 each); bytes: read q, k, v, dO, write dq,
@@ -356,7 +383,8 @@ def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
                 hbm_frac=bytes_ / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
-KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_state.hpp",
+KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_fused.hpp",
+                  "gated_linear_recurrences_amd/csrc/chunk_state.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_output.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_two_pass.hpp",
                   "gated_linear_recurrences_amd/csrc/chunk_common.hpp",
@@ -388,8 +416,9 @@ def measured_traffic():
 
 
 COPY_CAL_MB = 512   # size of the plain copy the counter runs are scaled by
-# kernels of one retention call (bf16, chunk 64, d_k = d_v = 128), as rocprofv3 names them
-TRAFFIC_KERNELS = ("glr::ck::state_kernel<64, 128, ", "glr::ck::output_kernel<64, 128, 128, 0,")
+# kernel of one retention call (bf16, chunk 64, d_k = d_v = 128, 16-channel value slices,
+# fixed gate), as rocprofv3 names it
+TRAFFIC_KERNELS = ("glr::ck::fused_kernel<64, 128, 128, 1, 0>",)
 
 
 def _counter_rows(d):
@@ -481,6 +510,33 @@ def kernel_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     print("\n".join(lines))
 
 
+def trace_table(trace_dir):
+    """Average, min and max duration per library kernel and grid size from a rocprofv3
+    --kernel-trace run (the *_kernel_trace.csv under trace_dir); prints a table."""
+    import csv
+    import glob
+    import re
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    agg = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "glr::" not in name:
+            continue
+        name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+        name = re.sub(r"\(.*$", "", name.replace("glr::ck::", "").replace("glr::", ""))
+        key = (name, r.get("Grid_Size_X") or r.get("Grid_Size", ""))
+        agg.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | grid (threads) | calls | average (us) | min (us) | max (us) |")
+    print("|---|---|---|---|---|---|")
+    for (name, grid), d in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{name}` | {grid} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+
+
 def copy_calibration(mbytes, steps, torch):
     """A plain device copy of ``mbytes`` MB, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     n = int(mbytes * 1e6) // 4
@@ -527,10 +583,15 @@ def main():
                     help="only run a plain device copy of MB megabytes --steps times (counter scaling)")
     ap.add_argument("--kernel-traffic", nargs=4, metavar="DIR",
                     help="per-kernel HBM bytes from FETCH/WRITE runs and the copy calibration runs")
+    ap.add_argument("--trace-table", metavar="DIR",
+                    help="print per-kernel durations from a rocprofv3 --kernel-trace output folder")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR",
                     help="FETCH_SIZE and WRITE_SIZE counter dirs of a bench run, then of a copy run: "
                          "write profiles/pmc_traffic.json")
     args = ap.parse_args()
+    if args.trace_table:
+        trace_table(args.trace_table)
+        return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
@@ -598,7 +659,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": main_r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": main_r["hbm_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel_ms": main_r["kernel_ms"], "alg_bytes_per_launch": main_r["alg_gbytes"] * 1e9,
-                     "kernels": "state pass + output pass (one call)"},
+                     "kernels": "single-pass forward (one call)"},
         "mfma": {"achieved": main_r["mfma_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": main_r["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS,
                  "alg_flop_per_launch": main_r["alg_gflop"] * 1e9},

@@ -550,3 +550,50 @@ def test_workspace_too_small_is_rejected():
     from gated_linear_recurrences_amd._native import GLRError
     with pytest.raises(GLRError, match="workspace too small"):
         api.gla_chunk_fwd(q, k, v, _t(w.log_alpha), chunk=32, workspace=ws)
+
+
+# ----------------------------------------------------------------------------- HIP graphs
+
+@pytest.mark.parametrize("kind,heads", [("retention", (4, 8)), ("retention", (1, 2)), ("mamba2", (4, 8)),
+                                        ("gla", (2, 2)), ("gdelta", (2, 2))])
+def test_graph_replay_matches_eager(kind, heads):
+    """The forward entry points enqueue kernels only (no memset, no host synchronisation), so
+    a caller may capture them in a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager call bit for bit. (4, 8) heads take
+    the single-pass forward for retention and the scalar decay, (1, 2) the two passes."""
+    w = make(kind, *heads, 150, 128, 128, 64, "bf16", 61, True)
+    st = _storage(w)
+    q, k, v, s0 = _t(w.q, st), _t(w.k, st), _t(w.v, st), _t(w.s0)
+    ws = torch.empty(max(api.workspace_size(kind, *heads, 150, 128, 128, 64), 16), dtype=torch.uint8, device=DEV)
+    o = torch.empty(*heads, 150, 128, dtype=st, device=DEV)
+    s_out = torch.empty(*heads, 128, 128, dtype=torch.float32, device=DEV)
+
+    lg = _t(w.log_gamma) if kind == "retention" else None
+    la = None if kind == "retention" else _t(w.log_alpha)
+    be = _t(w.beta) if kind == "gdelta" else None
+
+    def call():   # device buffers only: nothing is copied from the host during capture
+        if kind == "retention":
+            api.la_chunk_fwd(q, k, v, lg, chunk=64, s0=s0, o=o, s_out=s_out, workspace=ws)
+        elif kind == "mamba2":
+            api.mamba2_chunk_fwd(q, k, v, la, chunk=64, s0=s0, o=o, s_out=s_out, workspace=ws)
+        elif kind == "gla":
+            api.gla_chunk_fwd(q, k, v, la, chunk=64, s0=s0, o=o, s_out=s_out, workspace=ws)
+        else:
+            api.gdelta_chunk_fwd(q, k, v, la, be, chunk=64, s0=s0, o=o, s_out=s_out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    o_ref, s_ref = o.clone(), s_out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        o.zero_()
+        s_out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(s_out, s_ref), f"replay {rep}"
+        call()   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref)
