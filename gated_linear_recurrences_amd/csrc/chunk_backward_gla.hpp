@@ -28,9 +28,10 @@
 // + sum_m R_c[m][c] S_out[m][c] directly.
 //
 // Gradient pass (gfx950): persistent workgroups of eight waves, one per CU, each taking
-// (sequence, chunk) items in turn and loading the next item's q, k, v and dO into registers
-// while the current one computes (its gates and R are loaded as it starts, S_in and S_out
-// while its tables are built). Tiles in LDS use
+// (sequence, chunk) items in turn. An item loads q, k, v, dO, its gates and R as it starts,
+// S_in and S_out while its tables are built (holding the next item's operands in registers
+// during the products needs more than the 256 registers two waves per SIMD leave, and
+// the spills cost more than the wait). Tiles in LDS use
 // the chunk-swizzled layout; the cumulative gates are an fp32 [C][d_k + 4] table. A wave
 // that computes the dK tile of (feature tile, token tile) also computes the dQ tile of the
 // same pair, so q . dq - k . dk per element is formed in registers; the chunk's reverse
@@ -197,11 +198,11 @@ void grad_gla_kernel(GradGlaParams p) {
 
     int item = blockIdx.x;
     if (item >= p.items) return;
-    load_item(item);
     for (;;) {
         const int bh = item / p.NC, c = item % p.NC;
         const int t0 = c * C, n = (T - t0 < C) ? (T - t0) : C;
         const int64_t tok0 = static_cast<int64_t>(bh) * T + t0;
+        load_item(item);
         load_rg(item);
 
         // ---- stage v, dO, R and the raw gates (log2 units; rows past the end zero)
@@ -300,7 +301,6 @@ void grad_gla_kernel(GradGlaParams p) {
         }
         const int step = static_cast<int>(gridDim.x);
         const int next = (item < p.items - step) ? item + step : p.items;
-        if (next < p.items) load_item(next);   // in flight during this item's products
         lds_barrier();
 
         // F factor of tile pair (it, jt) for key channel `key`: 1 on the diagonal and above
