@@ -304,7 +304,7 @@ def bench_vla(steps, warmup, torch, api, synthetic, dev):
     return dict(workload=name, kernel_ms=ms, tokens_per_s=th / (ms * 1e-3), alg_gflop=flops / 1e9,
                 fp32_tflops=flops / (ms * 1e-3) / 1e12,
                 fp32_valu_frac=flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
-                heads=B * H, note="one workgroup per (sequence, head): 128 of 256 CUs")
+                heads=B * H, note="two workgroups per (sequence, head), each with half of the memory's rows")
 
 
 def bench_vla_decode(steps_total, torch, api, synthetic, dev):

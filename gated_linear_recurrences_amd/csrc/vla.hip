@@ -8,8 +8,9 @@
 // The update is sequential and O(d^2) per token with no dense contraction in it (every
 // product is a matrix times one vector), so it runs on the VALU in fp32, all tokens of
 // a sequence in one launch: one workgroup per (sequence, head) keeps A and S in
-// registers for the whole sequence. Waves 0 .. d_k/16-1 own 16 rows of A each, the
-// other d_v/16 waves 16 rows of S each; lane (r = lane & 15, g = lane >> 4) holds row
+// registers for the whole sequence (or two workgroups, each with half of the rows of S
+// and its own copy of the penalty chain, when the sequences are fewer than the CUs).
+// Waves 0 .. d_k/16-1 own 16 rows of A each, the other waves 16 rows of S each; lane (r = lane & 15, g = lane >> 4) holds row
 // 16w + r, key columns [g d_k/4, (g+1) d_k/4), so a row's dot products meet across
 // the four lanes of equal r with two shuffles.
 //
@@ -40,10 +41,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kVlaBlock = 16;   // tokens per staged block
 
-template <typename TS, int DK, int DV>
+template <typename TS, int DK, int DV, int SPL>
 struct VlaShape {
     static constexpr int NA = DK / 16;                 // waves holding A
-    static constexpr int NS = DV / 16;                 // waves holding S
+    static constexpr int NS = DV / 16 / SPL;           // waves holding this workgroup's rows of S
     static constexpr int NT = 64 * (NA + NS);
     static constexpr int NCOL = DK / 4;                // key columns per lane
     static constexpr int EPP = 16 / static_cast<int>(sizeof(TS));   // elements per 16-byte piece
@@ -54,12 +55,12 @@ struct VlaShape {
     static constexpr int SLOT = kVlaBlock * (3 * DK + DV);   // elements of one staged block
 };
 
-template <typename TS, int DK, int DV>
-__global__ __launch_bounds__((VlaShape<TS, DK, DV>::NT))
+template <typename TS, int DK, int DV, int SPL>
+__global__ __launch_bounds__((VlaShape<TS, DK, DV, SPL>::NT))
 void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v,
                 const TS* __restrict__ u, float inv_lambda0, const float* a0, const float* s0,
                 TS* __restrict__ o, float* s_out, float* a_out, int T) {
-    using Sh = VlaShape<TS, DK, DV>;
+    using Sh = VlaShape<TS, DK, DV, SPL>;
     constexpr int TB = kVlaBlock, NCOL = Sh::NCOL, NQ = NCOL / 4, NT = Sh::NT;
     constexpr int NC64 = (DK + 63) / 64;                               // columns per lane, whole-vector sums
     constexpr int OK = TB * DK, OU = 2 * TB * DK, OV = 3 * TB * DK;   // offsets in a staged block
@@ -74,8 +75,10 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
     const int r16 = lane & 15, g = lane >> 4;
     const int c0 = g * NCOL;
     const bool is_a = wave < Sh::NA;
-    const int m = 16 * (is_a ? wave : wave - Sh::NA) + r16;   // row of A (key) or of S (value)
-    const int64_t bh = blockIdx.x;
+    // SPL workgroups per sequence split the rows of S; each runs the whole penalty chain
+    const int part = static_cast<int>(blockIdx.x % SPL);
+    const int m = is_a ? 16 * wave + r16 : part * (DV / SPL) + 16 * (wave - Sh::NA) + r16;   // row of A or of S
+    const int64_t bh = blockIdx.x / SPL;
     const TS* qg = q + bh * T * DK;
     const TS* kg = k + bh * T * DK;
     const TS* ug = u + bh * T * DK;
@@ -257,7 +260,8 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
         }
     }
 
-    float* dst = is_a ? (a_out ? a_out + (bh * DK + m) * DK + c0 : nullptr)
+    // (the penalty, the same in every part, is written by part 0)
+    float* dst = is_a ? (a_out && part == 0 ? a_out + (bh * DK + m) * DK + c0 : nullptr)
                       : (s_out ? s_out + (bh * DV + m) * DK + c0 : nullptr);
     if (dst) {
 #pragma unroll
@@ -266,14 +270,27 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
     }
 }
 
+template <typename TS, int DK, int DV, int SPL>
+hipError_t launch_split(const VlaArgs& a, hipStream_t stream) {
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    hipLaunchKernelGGL((vla_kernel<TS, DK, DV, SPL>), dim3(static_cast<unsigned>(heads * SPL)),
+                       dim3(VlaShape<TS, DK, DV, SPL>::NT), 0, stream, static_cast<const TS*>(a.q),
+                       static_cast<const TS*>(a.k), static_cast<const TS*>(a.v), static_cast<const TS*>(a.u),
+                       a.inv_lambda0, a.a0, a.s0, static_cast<TS*>(a.o), a.s_out, a.a_out, a.T);
+    return hipGetLastError();
+}
+
+// Two workgroups per sequence, each with half of the rows of S and the whole penalty chain,
+// when there are fewer sequences than CUs: every CU then works, each on three quarters of a
+// token's arithmetic. Not when the penalty is updated in place (a0 == a_out: a part could
+// read it after another has written it) or d_v = 16.
 template <typename TS, int DK, int DV>
 hipError_t launch_shape(const VlaArgs& a, hipStream_t stream) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.H;
-    hipLaunchKernelGGL((vla_kernel<TS, DK, DV>), dim3(static_cast<unsigned>(heads)), dim3(VlaShape<TS, DK, DV>::NT), 0,
-                       stream, static_cast<const TS*>(a.q), static_cast<const TS*>(a.k), static_cast<const TS*>(a.v),
-                       static_cast<const TS*>(a.u), a.inv_lambda0, a.a0, a.s0, static_cast<TS*>(a.o), a.s_out,
-                       a.a_out, a.T);
-    return hipGetLastError();
+    if constexpr (DV >= 32) {
+        if (heads < 256 && (a.a_out == nullptr || a.a_out != a.a0)) return launch_split<TS, DK, DV, 2>(a, stream);
+    }
+    return launch_split<TS, DK, DV, 1>(a, stream);
 }
 
 template <typename TS, int DK>
