@@ -125,8 +125,7 @@ void grad_gla_kernel(GradGlaParams p) {
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
     // ---- operands of an item in registers (rows past the end read row 0, zeroed on use):
-    // q, k, v, dO are loaded an item ahead; R and the gates when the item starts, S_in and
-    // S_out after its staging
+    // q, k, v, dO, R and the gates when the item starts, S_in and S_out after its staging
     u16x8 rq[QP_PER], rk[QP_PER], rv[VP_PER], ro[VP_PER], rx[XP_PER], rs[XP_PER], rn[XP_PER];
     f32x4 rg[GP_PER];
     auto load_item = [&](int item) {
