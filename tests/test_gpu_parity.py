@@ -172,6 +172,26 @@ def test_bf16_single_pass_parity(kind, shape, state):
     assert_parity(w, o, S, o_ref, S_ref, f"{kind} single pass {shape} state={state}")
 
 
+@pytest.mark.parametrize("kind", ["retention", "mamba2"])
+@pytest.mark.parametrize("shape", [(4, 8, 150, 128, 64, 64), (2, 64, 70, 64, 32, 32)])
+def test_bf16_single_pass_strong_decay(kind, shape):
+    """Gates far from 1: log alpha in [-4, -2] per token (a chunk's gates then sum below
+    2^-100, where the scalar gate's e^(G_i) e^(-G_j) product form would overflow, so the
+    kernel takes e^(G_i - G_j) per element) and log gamma = -2.5 per head. Outputs are
+    dominated by the last few tokens; compared like every bf16 case."""
+    B, H, T, dk, dv, chunk = shape
+    assert B * H * dv // 16 >= 128
+    w = make(kind, *shape, dtype="bf16", seed=900 + sum(shape), state=True)
+    rng = np.random.default_rng(901)
+    if kind == "retention":
+        w.log_gamma = np.full((H,), -2.5, dtype=np.float32)
+    else:
+        w.log_alpha = rng.uniform(-4.0, -2.0, size=(B, H, T)).astype(np.float32)
+    o, S = run_gpu(w)
+    o_ref, S_ref = run_oracle(w)
+    assert_parity(w, o, S, o_ref, S_ref, f"{kind} strong decay {shape}")
+
+
 @pytest.mark.parametrize("name", ["retention_b4h8_t2048_d128", "gla_b8h16_t4096_d128",
                                   "gdelta_b4h16_t8192_d128", "mamba2_b8h16_t4096_d128"])
 def test_bf16_full_config_parity(name):
