@@ -320,7 +320,7 @@ void grad_gla_kernel(GradGlaParams p) {
                 const int D = second ? DV : DK;
 #pragma unroll
                 for (int kb = 0; kb < (KB > VB ? KB : VB); ++kb) {
-                    const int col = 32 * kb + 8 * g;
+                    const int col = rr_col(kb, g, KB > VB ? KB : VB);
                     bf16x8 a8 = as_bf16x8(z8), b8 = as_bf16x8(z8);
                     if (col < D) {
                         a8 = *reinterpret_cast<const bf16x8*>(second ? sV + TV::off(ar, col) : sK + TQ::off(ar, col));
@@ -362,7 +362,7 @@ void grad_gla_kernel(GradGlaParams p) {
             // sum over keys m of R[f][m] K^[j][m], K^ = K~ e^(G_last - r_jt)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const int col = 32 * kb + 8 * g;
+                const int col = rr_col(kb, g, KB);
                 bf16x8 xa = as_bf16x8(z8), kb8 = as_bf16x8(z8);
                 if (col < DK) {
                     xa = *reinterpret_cast<const bf16x8*>(sX + TQ::off(16 * ft + r16, col));

@@ -56,6 +56,17 @@ __device__ __forceinline__ bf16x4 tr_op(const u16* X, int base, int n0, int r16,
     return __builtin_bit_cast(bf16x4, v);
 }
 
+// Column of the 8-element piece that lane group g supplies in reduction block kb (of KB
+// 32-wide blocks) of an MFMA operand read row-wise from a SwzTile. Any one-to-one
+// assignment gives the same sum when both operands of the product use it; this one keeps
+// the row reads free of LDS bank conflicts on gfx950, where a 16-byte read serves lanes
+// 0-7 together with 24-31 (and 8-15 with 16-23): rows 0-7 of group 0 meet rows 8-15 of
+// group 1 in one cycle, the 64- and 128-wide swizzles send those two row halves of one
+// chunk to chunks of opposite parity, and pieces of equal parity for groups 0/1 (and 2/3)
+// then land on distinct banks. Pieces 4kb+g (the plain order) would collide two-way. Padded
+// tiles (row stride d + 16) keep the plain order, which is already conflict-free there.
+__device__ __forceinline__ int rr_col(int kb, int g, int KB) { return 8 * (kb + KB * g); }
+
 // Split operand over 32 rows (two 16-row halves) read transposed: rows 32jb + [0, 32) of
 // column tile n0; the second half zero unless `hi`.
 template <int RS>

@@ -262,7 +262,7 @@ void fused_kernel(FusedParams p) {
         if constexpr (NJ > 0) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const int col = 32 * kb + 8 * g;
+                const int col = rr_col(kb, g, KB);
                 const bool in = col < DK;
                 qb[kb] = in ? *reinterpret_cast<const bf16x8*>(Qc + TK::off(i, col)) : as_bf16x8(z8);
 #pragma unroll
