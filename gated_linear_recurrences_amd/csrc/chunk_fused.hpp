@@ -247,7 +247,8 @@ void fused_kernel(FusedParams p) {
     // One chunk as wave W (a compile-time role: token tile W's outputs when W < CT, key tiles
     // W, W + 4, ... of the carry).
     auto compute = [&](int c, const u16* Qc, const u16* K, const u16* V, const u16* Sin, u16* Snext,
-                       const float* graw, bf16x4 (&ov)[TS], auto wrole) __attribute__((always_inline)) {
+                       const float* graw, bf16x4 (&ov)[TS], auto wrole, auto&& issue_loads)
+        __attribute__((always_inline)) {
         constexpr int W = decltype(wrole)::value;
         constexpr int NJ = W < CT ? W + 1 : 0;      // P tiles of this wave's row tile
         constexpr int NJA = NJ > 0 ? NJ : 1;
@@ -287,6 +288,11 @@ void fused_kernel(FusedParams p) {
                 kl[u][jb] = tr_op_s<DK>(K, 32 * jb, 16 * (W + 4 * u), r16, g);
                 kh[u][jb] = (32 * jb + 16 < C) ? tr_op_s<DK>(K, 32 * jb + 16, 16 * (W + 4 * u), r16, g) : zero4();
             }
+
+        // the loads of chunk c + 2 go out while these reads are in flight: a CU's address
+        // unit takes about 64 bytes of loads per cycle, so issuing a chunk's loads (9 per
+        // lane) stalls the wave for hundreds of cycles, hidden here behind the LDS latency
+        issue_loads();
 
         // ---- scalar gate: inclusive scan of the raw gates (log2 units; padded tokens add 0),
         // then this wave's tables: G, e^G, e^-G and the carry weights e^(G_last - G) (0 past
@@ -414,16 +420,19 @@ void fused_kernel(FusedParams p) {
     // one chunk; slot S = c & 1 names both the register slot and the LDS buffer
     auto step = [&](int c, auto slot) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
-        load((c + 2 < NC) ? c + 2 : NC - 1, rq[S], rk[S], rv[S], rg[S]);   // past the end: a harmless reload
+        // past the end: a harmless reload
+        auto issue_loads = [&]() __attribute__((always_inline)) {
+            load((c + 2 < NC) ? c + 2 : NC - 1, rq[S], rk[S], rv[S], rg[S]);
+        };
         const u16 *Qc = sQ(S), *K = sK(S), *V = sV(S), *Sin = sS(S);
         u16* Snext = sS(S ^ 1);
         const float* graw = sG(S);
         bf16x4 ov[TS];
         switch (w) {
-            case 0: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 0>{}); break;
-            case 1: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 1>{}); break;
-            case 2: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 2>{}); break;
-            default: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 3>{}); break;
+            case 0: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 0>{}, issue_loads); break;
+            case 1: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 1>{}, issue_loads); break;
+            case 2: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 2>{}, issue_loads); break;
+            default: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 3>{}, issue_loads); break;
         }
         // ---- next chunk's operands into the other buffer
         // (past the last chunk: a copy of it, never read)
