@@ -543,7 +543,7 @@ void delta_state_kernel(DeltaParams p) {
 // a bf16 hi + lo pair.
 template <int C, int DK, int DV>
 struct DOutLayout {
-    static constexpr int QS = DK + 8;
+    static constexpr int QS = tile_stride(DK);   // rows 8 banks apart: conflict-free 16-byte row reads
     static constexpr int PS = C + 4;
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
     static constexpr int oQ = 0;

@@ -52,7 +52,10 @@ template <int C, int DK, int DV, int GK>
 struct OutLayout {
     static constexpr bool GLA = GK == kGateChannel, SCL = GK == kGateScalar;
     static constexpr int CT = C / 16;
-    static constexpr int QS = DK + 8;   // bf16 row stride of staged q / k (16-byte rows)
+    // bf16 row stride of staged q / k: rows 8 banks apart (d_k + 8 put them 4 apart, and
+    // a 16-byte read serves lanes 0-7 with 24-31, rows 0-7 of one piece beside rows 8-15
+    // of the next, which then shared a bank in every cycle)
+    static constexpr int QS = tile_stride(DK);
     // bf16 row stride of staged v: rows 8 x odd banks apart, so that the 8 rows read
     // by half a wave of ds_read_b64_tr_b16 fall on distinct banks
     static constexpr int VS = DV == 16 ? 16 : DV + 16;
