@@ -22,11 +22,22 @@ inline int state_value_tiles(int64_t heads, int dv, int dk) {
     return 1;
 }
 
-// chunks per workgroup barrier: the largest of 4, 2, 1 whose double-buffered
-// staging fits in LDS
+// Bytes per lane of one slot of the state pass's register ring: U chunks of k, v (and
+// GLA's fp32 gates) over the workgroup's 64 NW lanes.
+template <int C, int NW, int TV, int GK>
+constexpr int state_ring_bytes(int U) {
+    return U * C * (16 * NW * 2 + 16 * TV * 2 + (GK == kGateChannel ? 16 * NW * 4 : 0)) / (64 * NW);
+}
+
+// chunks per workgroup barrier: the largest of 4, 2, 1 whose double-buffered staging fits
+// in LDS and whose ring slot stays within 384 bytes per lane (with d_k = 16 a single wave
+// would otherwise hold four chunks of 128 value channels per slot, 1152 bytes, and spill)
 template <int C, int NW, int TV, int GK>
 constexpr int state_group() {
-    return StateLayout<C, NW, TV, 4, GK>::fits ? 4 : StateLayout<C, NW, TV, 2, GK>::fits ? 2 : 1;
+    constexpr int kRing = 384;
+    return (StateLayout<C, NW, TV, 4, GK>::fits && state_ring_bytes<C, NW, TV, GK>(4) <= kRing) ? 4
+           : (StateLayout<C, NW, TV, 2, GK>::fits && state_ring_bytes<C, NW, TV, GK>(2) <= kRing) ? 2
+                                                                                                   : 1;
 }
 
 template <int C, int DK, int TV, int GK, bool REV = false>

@@ -172,6 +172,17 @@ def test_bf16_single_pass_parity(kind, shape, state):
     assert_parity(w, o, S, o_ref, S_ref, f"{kind} single pass {shape} state={state}")
 
 
+@pytest.mark.parametrize("shape", [(2, 64, 70, 16, 128, 64), (4, 64, 70, 16, 128, 64)])
+def test_bf16_gla_dk16_many_heads(shape):
+    """GLA's state pass with d_k = 16 (one wave per workgroup) and enough heads that each
+    wave takes 4, then 8, value tiles of 16 channels: the configurations whose group of
+    chunks per barrier is limited by the register ring rather than by LDS."""
+    w = make("gla", *shape, dtype="bf16", seed=700 + sum(shape), state=True)
+    o, S = run_gpu(w)
+    o_ref, S_ref = run_oracle(w)
+    assert_parity(w, o, S, o_ref, S_ref, f"gla d_k=16 {shape}")
+
+
 @pytest.mark.parametrize("kind", ["retention", "mamba2"])
 @pytest.mark.parametrize("shape", [(4, 8, 150, 128, 64, 64), (2, 64, 70, 64, 32, 32)])
 def test_bf16_single_pass_strong_decay(kind, shape):
