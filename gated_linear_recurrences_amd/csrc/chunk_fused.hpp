@@ -16,11 +16,13 @@
 // run side by side on one XCD and share q and k through its L2.
 //
 // Decomposition (gfx950), four waves, per chunk:
-//   operands  q, k, the v slice (and the raw scalar gates) are staged in LDS
+//   operands  k, the v slice (and the raw scalar gates) are staged in LDS
 //             (double-buffered), loaded two chunks ahead through a two-slot register ring
 //             that is written to LDS just before the chunk's barrier: every load is
 //             consumed there, so the compiler's count of loads in flight stays exact and
-//             one chunk's loads stay in flight across each wait;
+//             one chunk's loads stay in flight across each wait. q is staged the same way
+//             at chunks 16 and 32; at chunk 64 each wave loads its own 16 rows of q into
+//             the ring, in the MFMA operand layout, and takes them from there;
 //   gates     retention's decay factors depend only on positions: they are tabulated in
 //             registers once. For the scalar gate every wave scans the chunk's raw gates
 //             and tabulates e^(G), e^(-G) and the carry weights e^(G_last - G) in its own
@@ -68,8 +70,11 @@ struct FusedLayout {
     static constexpr int VBUF = al(C * TV::STRIDE * 2);     // v slice, token-major
     static constexpr int SBUF = al(DVS * TK::STRIDE * 2);   // S_in slice, bf16 rows
     static constexpr int GBUF = GK == kGateScalar ? al(C * 4) : 0;
+    // with four token tiles every wave reads only its own 16 rows of q: they go from HBM
+    // straight to its registers, and only k, v (and the gates) are staged
+    static constexpr bool QREG = C == 64;
     static constexpr int oQ = 0;
-    static constexpr int oK = oQ + 2 * KBUF;
+    static constexpr int oK = oQ + (QREG ? 0 : 2 * KBUF);
     static constexpr int oV = oK + 2 * KBUF;
     static constexpr int oS = oV + 2 * VBUF;
     static constexpr int oG = oS + 2 * SBUF;
@@ -100,6 +105,8 @@ void fused_kernel(FusedParams p) {
     constexpr int VE = (C * DVS / 4 == NT) ? 4 : 8;                 // elements per piece
     constexpr int VP = C * DVS / VE, VP_PER = (VP + NT - 1) / NT;
     static_assert(DV % DVS == 0, "value slices must tile d_v");
+    constexpr bool QREG = Lay::QREG;
+    constexpr int QN = QREG ? KB : KP_PER;     // q pieces per lane and chunk
 
     __shared__ __align__(16) unsigned char smem[Lay::bytes];
 
@@ -128,7 +135,7 @@ void fused_kernel(FusedParams p) {
 
     // ---- register ring: q, k and v pieces (and the raw gates) of two chunks
     typedef unsigned short vpiece __attribute__((ext_vector_type(VE)));
-    u16x8 rq[2][KP_PER], rk[2][KP_PER];
+    u16x8 rq[2][QN], rk[2][KP_PER];
     vpiece rv[2][VP_PER];
     float rg[2];
 
@@ -136,15 +143,27 @@ void fused_kernel(FusedParams p) {
     // zeroed when staged) and consumed only when staged, so that the compiler's count of
     // loads in flight stays exact across the chunk loop and each wait covers only the chunk
     // it is for.
-    auto load = [&](int c, u16x8 (&q)[KP_PER], u16x8 (&k)[KP_PER], vpiece (&v)[VP_PER], float& gr) {
+    auto load = [&](int c, u16x8 (&q)[QN], u16x8 (&k)[KP_PER], vpiece (&v)[VP_PER], float& gr) {
         const int n = count(c);
         const int64_t t0 = static_cast<int64_t>(c) * C;
+        if constexpr (QREG) {
+            // row 16w + r16 in the operand layout of the products over d_k (pieces rr_col);
+            // rows past the end reload row 0: they only reach outputs that are not stored.
+            // Issued first, so the wait before the next staging covers them too.
+            const int i = 16 * w + r16;
+            const int64_t row = t0 + (i < n ? i : 0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int col = rr_col(kb, g, KB);
+                q[kb] = *reinterpret_cast<const u16x8*>(qs + row * DK + (col < DK ? col : 0));
+            }
+        }
 #pragma unroll
         for (int i = 0; i < KP_PER; ++i) {
             const int idx = tid + i * NT;
             const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
             const int64_t off = (t0 + ((idx < KP && j < n) ? j : 0)) * DK + (idx < KP ? col : 0);
-            q[i] = *reinterpret_cast<const u16x8*>(qs + off);
+            if constexpr (!QREG) q[i] = *reinterpret_cast<const u16x8*>(qs + off);
             k[i] = *reinterpret_cast<const u16x8*>(ks + off);
         }
 #pragma unroll
@@ -156,7 +175,7 @@ void fused_kernel(FusedParams p) {
         }
         if constexpr (SCL) gr = gs[t0 + (lane < n ? lane : 0)];   // zeroed past the end when staged
     };
-    auto stage = [&](int c, int b, const u16x8 (&q)[KP_PER], const u16x8 (&k)[KP_PER], const vpiece (&v)[VP_PER],
+    auto stage = [&](int c, int b, const u16x8 (&q)[QN], const u16x8 (&k)[KP_PER], const vpiece (&v)[VP_PER],
                      float gr) {
         const int n = count(c);
         u16* Q = sQ(b);
@@ -169,7 +188,7 @@ void fused_kernel(FusedParams p) {
             // consumed on every path)
             if (KP % NT == 0 || idx < KP) {
                 const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-                *reinterpret_cast<u16x8*>(Q + TK::off(j, col)) = j < n ? q[i] : z8;
+                if constexpr (!QREG) *reinterpret_cast<u16x8*>(Q + TK::off(j, col)) = j < n ? q[i] : z8;
                 *reinterpret_cast<u16x8*>(K + TK::off(j, col)) = j < n ? k[i] : z8;
             }
         }
@@ -247,8 +266,8 @@ void fused_kernel(FusedParams p) {
     // One chunk as wave W (a compile-time role: token tile W's outputs when W < CT, key tiles
     // W, W + 4, ... of the carry).
     auto compute = [&](int c, const u16* Qc, const u16* K, const u16* V, const u16* Sin, u16* Snext,
-                       const float* graw, bf16x4 (&ov)[TS], auto wrole, auto&& issue_loads)
-        __attribute__((always_inline)) {
+                       const float* graw, bf16x4 (&ov)[TS], auto wrole, auto&& issue_loads,
+                       const u16x8 (&qr)[QN]) __attribute__((always_inline)) {
         constexpr int W = decltype(wrole)::value;
         constexpr int NJ = W < CT ? W + 1 : 0;      // P tiles of this wave's row tile
         constexpr int NJA = NJ > 0 ? NJ : 1;
@@ -265,7 +284,10 @@ void fused_kernel(FusedParams p) {
             for (int kb = 0; kb < KB; ++kb) {
                 const int col = rr_col(kb, g, KB);
                 const bool in = col < DK;
-                qb[kb] = in ? *reinterpret_cast<const bf16x8*>(Qc + TK::off(i, col)) : as_bf16x8(z8);
+                if constexpr (QREG)
+                    qb[kb] = in ? as_bf16x8(qr[kb]) : as_bf16x8(z8);
+                else
+                    qb[kb] = in ? *reinterpret_cast<const bf16x8*>(Qc + TK::off(i, col)) : as_bf16x8(z8);
 #pragma unroll
                 for (int jt = 0; jt < NJ; ++jt)
                     kr[jt][kb] = in ? *reinterpret_cast<const bf16x8*>(K + TK::off(16 * jt + r16, col)) : as_bf16x8(z8);
@@ -429,10 +451,10 @@ void fused_kernel(FusedParams p) {
         const float* graw = sG(S);
         bf16x4 ov[TS];
         switch (w) {
-            case 0: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 0>{}, issue_loads); break;
-            case 1: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 1>{}, issue_loads); break;
-            case 2: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 2>{}, issue_loads); break;
-            default: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 3>{}, issue_loads); break;
+            case 0: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 0>{}, issue_loads, rq[S]); break;
+            case 1: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 1>{}, issue_loads, rq[S]); break;
+            case 2: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 2>{}, issue_loads, rq[S]); break;
+            default: compute(c, Qc, K, V, Sin, Snext, graw, ov, std::integral_constant<int, 3>{}, issue_loads, rq[S]); break;
         }
         // ---- next chunk's operands into the other buffer
         // (past the last chunk: a copy of it, never read)
