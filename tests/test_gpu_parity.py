@@ -153,6 +153,8 @@ SINGLE_PASS_SHAPES = [
     (16, 16, 40, 32, 128, 16),    # 32-channel slices, chunk 16
     (2, 64, 1, 64, 64, 64),
     (8, 8, 0, 64, 32, 64),
+    (4, 8, 150, 16, 64, 64),      # chunk 64 (q taken from registers), d_k = 16: half the lanes idle
+    (4, 8, 99, 32, 128, 64),      # chunk 64, d_k = 32
 ]
 
 
