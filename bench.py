@@ -281,9 +281,10 @@ FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 
 
 def bench_vla(steps, warmup, torch, api, synthetic, dev):
-    """Variational linear attention over B8 H16 T4096 d128 (bf16 tokens, fp32 arithmetic): one
-    vla_fwd call per step. Algorithmic flops per token-head 6 d_k^2 + 6 d_v d_k (A u, the
-    rank-1 update and A k^; S k^, the write and S q), priced against the fp32 vector peak."""
+    """Variational linear attention over B8 H16 T4096 d128 (bf16 tokens, fp32 arithmetic), the
+    page's ELU+1 ratio readout: one vla_fwd call per step. Algorithmic flops per token-head
+    6 d_k^2 + 6 d_v d_k (A u, the rank-1 update and A k^; S k^, the write and S phi(q); the
+    denominator's O(d_k) is left out), priced against the fp32 vector peak."""
     name = "vla_b8h16_t4096_d128"
     c = synthetic.CONFIGS[name]
     B, H, T, dk, dv = c["B"], c["H"], c["T"], c["dk"], c["dv"]
@@ -294,9 +295,10 @@ def bench_vla(steps, warmup, torch, api, synthetic, dev):
     o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
     s_out = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     a_out = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+    n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
 
     def call():
-        api.vla_fwd(b["q"], b["k"], b["v"], uu, lambda0=1.0, o=o, s_out=s_out, a_out=a_out)
+        api.vla_fwd(b["q"], b["k"], b["v"], uu, lambda0=1.0, o=o, s_out=s_out, a_out=a_out, n_out=n_out)
 
     ms = time_calls([call], steps, warmup, torch)[1]
     th = B * H * T
@@ -308,33 +310,36 @@ def bench_vla(steps, warmup, torch, api, synthetic, dev):
 
 
 def bench_vla_decode(steps_total, torch, api, synthetic, dev):
-    """VLA decode at the decode workload's shape (512 sequences x 32 heads, d = 128): the fp32
-    memory and inverse penalty updated in place, a fresh bf16 token per step drawn on the
-    device (q, k, u ~ N(0,1)/sqrt(d), v ~ N(0,1)); ``steps_total`` steps timed as one region."""
+    """VLA decode at the decode workload's shape (512 sequences x 32 heads, d = 128), ratio
+    readout: the fp32 memory, inverse penalty and denominator vector updated in place, a fresh
+    bf16 token per step drawn on the device (q, k, v ~ N(0,1), u ~ N(0,1)/sqrt(d));
+    ``steps_total`` steps timed as one region."""
     N, H, d = 512, 32, 128
     w = synthetic.vla_decode_inputs(N, H, d, d, steps=0, seed=9)
     s = torch.from_numpy(w.s0).to(dev)
     a = torch.from_numpy(w.a0).to(dev)
+    nd = torch.from_numpy(w.n0).to(dev)
     del w
     gen = torch.Generator(device=dev)
     gen.manual_seed(9)
     sc = 1.0 / np.sqrt(d)
-    q = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * sc).to(torch.bfloat16)
-    k = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * sc).to(torch.bfloat16)
+    q = torch.randn((steps_total, N, H, d), generator=gen, device=dev).to(torch.bfloat16)
+    k = torch.randn((steps_total, N, H, d), generator=gen, device=dev).to(torch.bfloat16)
     u = (torch.randn((steps_total, N, H, d), generator=gen, device=dev) * sc).to(torch.bfloat16)
     v = torch.randn((steps_total, N, H, d), generator=gen, device=dev).to(torch.bfloat16)
     o = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
     for i in range(3):
-        api.vla_recurrent_step(q[i], k[i], v[i], u[i], s, a, o=o)
+        api.vla_recurrent_step(q[i], k[i], v[i], u[i], s, a, n=nd, o=o)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps_total):
-        api.vla_recurrent_step(q[i], k[i], v[i], u[i], s, a, o=o)
+        api.vla_recurrent_step(q[i], k[i], v[i], u[i], s, a, n=nd, o=o)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps_total
-    bytes_step = N * H * (2 * (d * d + d * d) * 4 + 4 * d * 2 + d * 2)
+    # memory, penalty and denominator read and written; q, k, u, v read; o written
+    bytes_step = N * H * (2 * (d * d + d * d + d) * 4 + 4 * d * 2 + d * 2)
     return dict(workload="vla_decode_n512h32_d128", steps=steps_total, us_per_step=ms * 1e3,
                 hbm_gbs=bytes_step / (ms * 1e-3) / 1e9, hbm_frac=bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 alg_bytes_per_step=bytes_step)

@@ -13,7 +13,8 @@ import torch
 from . import _native
 
 __all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-           "la_chunk_bwd", "mamba2_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step", "workspace_size"]
+           "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step",
+           "vla_fwd", "vla_recurrent_step", "workspace_size", "bwd_workspace_size"]
 
 
 def _dtype_code(t):
@@ -239,12 +240,24 @@ def gdelta_recurrent_step(q, k, v, alpha, beta, s, o=None):
     return o
 
 
-def vla_fwd(q, k, v, u, lambda0=1.0, a0=None, s0=None, o=None, s_out=None, a_out=None, return_state=True):
+def _vla_readout(readout):
+    codes = {"ratio": _native.LA_VLA_RATIO, "linear": _native.LA_VLA_LINEAR}
+    if readout not in codes:
+        raise ValueError(f"readout must be 'ratio' or 'linear', got {readout!r}")
+    return codes[readout]
+
+
+def vla_fwd(q, k, v, u, lambda0=1.0, a0=None, s0=None, n0=None, o=None, s_out=None, a_out=None, n_out=None,
+            readout="ratio", return_state=True):
     """Variational linear attention over whole sequences: per token z = A u,
-    A <- A - z z^T / (1 + u.z), a = A k^/|A k^| (k^ = k/|k|), S <- S + (v - S k^) a^T, o = S q.
+    A <- A - z z^T / (1 + u.z), a = A k^/|A k^|, S <- S + (v - S k^) a^T, then the readout:
+    "ratio" (ELU+1 map phi on k and q, k^ = phi(k)/|phi(k)|, n <- n + (1 - n.k^) a,
+    o = S phi(q) / (n.phi(q))) or "linear" (k^ = k/|k|, o = S q).
 
     q, k, u [B,H,T,d_k], v [B,H,T,d_v] (bf16 or fp32); A starts at a0 [B,H,d_k,d_k] fp32 or
-    I / lambda0, S at s0 [B,H,d_v,d_k] fp32 or zeros. Returns (o, s_out, a_out)."""
+    I / lambda0, S at s0 [B,H,d_v,d_k] fp32 or zeros, n at n0 [B,H,d_k] fp32 or zeros.
+    Returns (o, s_out, a_out, n_out) (n_out None for the linear readout)."""
+    code = _vla_readout(readout)
     dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
     B, H, T, dk, dv = dims
     dev = q.device
@@ -255,15 +268,27 @@ def vla_fwd(q, k, v, u, lambda0=1.0, a0=None, s0=None, o=None, s_out=None, a_out
         a_out = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
     elif a_out is not None:
         _require(a_out, "a_out", (B, H, dk, dk), torch.float32, dev)
+    if code == _native.LA_VLA_RATIO:
+        if n0 is not None:
+            _require(n0, "n0", (B, H, dk), torch.float32, dev)
+        if n_out is None and return_state:
+            n_out = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+        elif n_out is not None:
+            _require(n_out, "n_out", (B, H, dk), torch.float32, dev)
+    else:
+        n0 = n_out = None
     lib = _native.load()
-    _native.check(lib.vla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(u), float(lambda0), _ptr(a0), _ptr(s0), _ptr(o),
-                              _ptr(s_out), _ptr(a_out), B, H, T, dk, dv, _dtype_code(q), _stream(dev)))
-    return o, s_out, a_out
+    _native.check(lib.vla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(u), float(lambda0), _ptr(a0), _ptr(s0), _ptr(n0),
+                              _ptr(o), _ptr(s_out), _ptr(a_out), _ptr(n_out), code, B, H, T, dk, dv, _dtype_code(q),
+                              _stream(dev)))
+    return o, s_out, a_out, n_out
 
 
-def vla_recurrent_step(q, k, v, u, s, a, o=None):
-    """One VLA decode token, in place on the memory s [N,H,d_v,d_k] and the inverse penalty
-    a [N,H,d_k,d_k] (fp32); q, k, u [N,H,d_k], v [N,H,d_v] (bf16 or fp32). Returns o."""
+def vla_recurrent_step(q, k, v, u, s, a, n=None, o=None, readout="ratio"):
+    """One VLA decode token, in place on the memory s [N,H,d_v,d_k], the inverse penalty
+    a [N,H,d_k,d_k] and (ratio readout) the denominator vector n [N,H,d_k] (fp32); q, k, u
+    [N,H,d_k], v [N,H,d_v] (bf16 or fp32). Returns o."""
+    code = _vla_readout(readout)
     if q.dim() != 3:
         raise ValueError("q must be [N, H, d_k]")
     N, H, dk = q.shape
@@ -276,13 +301,17 @@ def vla_recurrent_step(q, k, v, u, s, a, o=None):
     _require(v, "v", (N, H, dv), q.dtype, dev)
     _require(s, "s", (N, H, dv, dk), torch.float32, dev)
     _require(a, "a", (N, H, dk, dk), torch.float32, dev)
+    if code == _native.LA_VLA_RATIO:
+        _require(n, "n", (N, H, dk), torch.float32, dev)
+    else:
+        n = None
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     else:
         _require(o, "o", (N, H, dv), q.dtype, dev)
     lib = _native.load()
-    _native.check(lib.vla_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(s), _ptr(a), _ptr(o), N, H, dk, dv,
-                                         _dtype_code(q), _stream(dev)))
+    _native.check(lib.vla_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(s), _ptr(a), _ptr(n), _ptr(o), code,
+                                         N, H, dk, dv, _dtype_code(q), _stream(dev)))
     return o
 
 

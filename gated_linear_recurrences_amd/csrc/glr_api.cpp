@@ -34,7 +34,8 @@ la_status check_ptr(const void* p, bool used, bool optional, const char* name) {
     return LA_OK;
 }
 
-la_status check_chunk_args(glr::Variant variant, const glr::ChunkArgs& a, int dtype) {
+// Sizes, dtype and (unless `pointers` is false: the workspace query) the pointers of a chunk call.
+la_status check_chunk_args(glr::Variant variant, const glr::ChunkArgs& a, int dtype, bool pointers = true) {
     if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "%s", "unknown dtype");
     if (a.B < 0 || a.H < 0 || a.T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
     if (a.chunk < 1) return fail(LA_ERR_INVALID, "%s", "chunk < 1");
@@ -43,14 +44,16 @@ la_status check_chunk_args(glr::Variant variant, const glr::ChunkArgs& a, int dt
         return fail(LA_ERR_UNSUPPORTED, "%s", "d_k and d_v must be 16, 32, 64 or 128");
     if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64)
         return fail(LA_ERR_UNSUPPORTED, "%s", "chunk must be 16, 32 or 64");
-    const bool heads = a.B > 0 && a.H > 0;
+    const bool heads = pointers && a.B > 0 && a.H > 0;
     const bool tokens = heads && a.T > 0;
     la_status st;
     if ((st = check_ptr(a.q, tokens, false, "q")) != LA_OK) return st;
     if ((st = check_ptr(a.k, tokens, false, "k")) != LA_OK) return st;
     if ((st = check_ptr(a.v, tokens, false, "v")) != LA_OK) return st;
     if ((st = check_ptr(a.o, tokens, false, "o")) != LA_OK) return st;
-    if ((st = check_ptr(a.gate, tokens, false, variant == glr::kRetention ? "log_gamma" : "log_alpha")) != LA_OK)
+    // retention's per-head decay is read by every launched workgroup, also when T == 0
+    if ((st = check_ptr(a.gate, variant == glr::kRetention ? heads : tokens, false,
+                        variant == glr::kRetention ? "log_gamma" : "log_alpha")) != LA_OK)
         return st;
     if (variant == glr::kGDelta && (st = check_ptr(a.beta, tokens, false, "beta")) != LA_OK) return st;
     if ((st = check_ptr(a.s0, heads, true, "s0")) != LA_OK) return st;
@@ -99,7 +102,7 @@ la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int d
     glr::ChunkArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                      B, H, 0, dk, dv, chunk, nullptr, variant == LA_GDELTA_FUSED ? LA_FUSE_QK_SILU_L2 : 0,
                      nullptr, 0.f};
-    la_status st = check_chunk_args(v, a, dtype);
+    la_status st = check_chunk_args(v, a, dtype, false);
     if (st != LA_OK) return st;
     if (T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
     a.T = T;
@@ -244,7 +247,7 @@ static la_status bwd_workspace_query(glr::Variant variant, int B, int H, int T, 
     *bytes = 0;
     glr::ChunkArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                      B, H, 0, dk, dv, chunk, nullptr};
-    la_status st = check_chunk_args(glr::kRetention, a, dtype);
+    la_status st = check_chunk_args(glr::kRetention, a, dtype, false);
     if (st != LA_OK) return st;
     if (T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
     if (dtype != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "%s", "the backward takes bf16 storage");
@@ -295,9 +298,10 @@ la_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float
 }
 
 la_status vla_fwd(const void* q, const void* k, const void* v, const void* u, float lambda0, const float* a0,
-                  const float* s0, void* o, float* s_out, float* a_out, int B, int H, int T, int dk, int dv,
-                  la_dtype dtype, void* stream) {
+                  const float* s0, const float* n0, void* o, float* s_out, float* a_out, float* n_out,
+                  int readout, int B, int H, int T, int dk, int dv, la_dtype dtype, void* stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "%s", "unknown dtype");
+    if (readout != LA_VLA_RATIO && readout != LA_VLA_LINEAR) return fail(LA_ERR_INVALID, "%s", "unknown readout");
     if (B < 0 || H < 0 || T < 0) return fail(LA_ERR_INVALID, "%s", "negative B, H or T");
     if (dk < 1 || dv < 1) return fail(LA_ERR_INVALID, "%s", "d_k and d_v must be >= 1");
     if (!supported_dim(dk) || !supported_dim(dv))
@@ -316,18 +320,23 @@ la_status vla_fwd(const void* q, const void* k, const void* v, const void* u, fl
     if ((st = check_ptr(s0, heads, true, "s0")) != LA_OK) return st;
     if ((st = check_ptr(s_out, heads, true, "s_out")) != LA_OK) return st;
     if ((st = check_ptr(a_out, heads, true, "a_out")) != LA_OK) return st;
+    const bool ratio = readout == LA_VLA_RATIO;
+    if ((st = check_ptr(n0, ratio && heads, true, "n0")) != LA_OK) return st;
+    if ((st = check_ptr(n_out, ratio && heads, true, "n_out")) != LA_OK) return st;
     if (static_cast<int64_t>(B) * H >= (static_cast<int64_t>(1) << 31))
         return fail(LA_ERR_UNSUPPORTED, "%s", "B * H must be below 2^31");
     if (!heads) return LA_OK;
-    glr::VlaArgs a{q, k, v, u, a0 ? 1.f : 1.f / lambda0, a0, s0, o, s_out, a_out, B, H, T, dk, dv};
+    glr::VlaArgs a{q, k, v, u, a0 ? 1.f : 1.f / lambda0, a0, s0, ratio ? n0 : nullptr, o, s_out, a_out,
+                   ratio ? n_out : nullptr, ratio ? 1 : 0, B, H, T, dk, dv};
     const hipError_t err = glr::launch_vla(dtype == LA_BF16, a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
     return LA_OK;
 }
 
-la_status vla_recurrent_step(const void* q, const void* k, const void* v, const void* u, float* s, float* a, void* o,
-                             int N, int H, int dk, int dv, la_dtype dtype, void* stream) {
+la_status vla_recurrent_step(const void* q, const void* k, const void* v, const void* u, float* s, float* a, float* n,
+                             void* o, int readout, int N, int H, int dk, int dv, la_dtype dtype, void* stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "%s", "unknown dtype");
+    if (readout != LA_VLA_RATIO && readout != LA_VLA_LINEAR) return fail(LA_ERR_INVALID, "%s", "unknown readout");
     if (N < 0 || H < 0) return fail(LA_ERR_INVALID, "%s", "negative N or H");
     if (dk < 1 || dv < 1) return fail(LA_ERR_INVALID, "%s", "d_k and d_v must be >= 1");
     if (!supported_dim(dk) || !supported_dim(dv))
@@ -340,11 +349,14 @@ la_status vla_recurrent_step(const void* q, const void* k, const void* v, const 
     if ((st = check_ptr(u, used, false, "u")) != LA_OK) return st;
     if ((st = check_ptr(s, used, false, "s")) != LA_OK) return st;
     if ((st = check_ptr(a, used, false, "a")) != LA_OK) return st;
+    const bool ratio = readout == LA_VLA_RATIO;
+    if ((st = check_ptr(n, used && ratio, false, "n")) != LA_OK) return st;
     if ((st = check_ptr(o, used, false, "o")) != LA_OK) return st;
     if (static_cast<int64_t>(N) * H >= (static_cast<int64_t>(1) << 31))
         return fail(LA_ERR_UNSUPPORTED, "%s", "N * H must be below 2^31");
     if (!used) return LA_OK;
-    glr::VlaArgs args{q, k, v, u, 1.f, a, s, o, s, a, N, H, 1, dk, dv};
+    glr::VlaArgs args{q, k, v, u, 1.f, a, s, ratio ? n : nullptr, o, s, a, ratio ? n : nullptr, ratio ? 1 : 0,
+                      N, H, 1, dk, dv};
     const hipError_t err = glr::launch_vla(dtype == LA_BF16, args, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(LA_ERR_HIP, "launch failed: %s", hipGetErrorString(err));
     return LA_OK;
@@ -362,6 +374,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (2 << 16) | 7; }
+int la_version(void) { return (3 << 16) | 0; }
 
 }  // extern "C"

@@ -69,9 +69,12 @@ struct VlaArgs {
     float inv_lambda0;    // A_0 = I * inv_lambda0 when a0 is nullptr
     const float* a0;      // [B,H,dk,dk] or nullptr
     const float* s0;      // [B,H,dv,dk] or nullptr
+    const float* n0;      // ratio readout: [B,H,dk] or nullptr (zeros)
     void* o;              // [B,H,T,dv]
     float* s_out;         // [B,H,dv,dk] or nullptr (may equal s0)
     float* a_out;         // [B,H,dk,dk] or nullptr (may equal a0)
+    float* n_out;         // ratio readout: [B,H,dk] or nullptr (may equal n0)
+    int ratio;            // 1: ELU+1 ratio readout; 0: o = S q
     int B, H, T, dk, dv;
 };
 hipError_t launch_vla(bool bf16, const VlaArgs& a, hipStream_t stream);

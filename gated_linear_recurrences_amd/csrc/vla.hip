@@ -3,7 +3,11 @@
 // beside the memory S (d_v x d_k),
 //   z = A u,  A <- A - z z^T / (1 + u.z)     Sherman-Morrison for M <- M + u u^T
 //   a = A k^ / |A k^|,  k^ = k / |k|          normalised gating vector (updated A)
-//   S <- S + (v - S k^) a^T,  o = S q         residual write, read after write.
+//   S <- S + (v - S k^) a^T                   residual write
+// and the readout after the write: the page's ratio of recurrences with the ELU+1
+// feature map phi on keys and queries (k^ = phi(k)/|phi(k)|; n, the denominator vector,
+// follows the same write driven by the value 1: n <- n + (1 - n.k^) a;
+// o = S phi(q) / (n . phi(q))), or o = S q with the key only normalised.
 //
 // The update is sequential and O(d^2) per token with no dense contraction in it (every
 // product is a matrix times one vector), so it runs on the VALU in fp32, all tokens of
@@ -19,12 +23,14 @@
 //   barrier;
 //   A waves: |k|^2, u.z and z.k^ over the whole vectors (two columns per lane and a
 //   wave-wide sum: the same in every wave), A_t k^ and its norm the same way, the
-//   rank-1 update of their rows; wave 0 publishes a_t;
+//   rank-1 update of their rows; wave 0 publishes a_t and, for the ratio readout,
+//   updates the denominator vector n (two columns per lane) and publishes n_t.phi(q_t);
 //   S waves, one token behind: token t-1 with a_{t-1} (published by this barrier).
 // LDS vectors are double-buffered by token parity, so no second barrier is needed.
 // q, k, u, v are staged through LDS as fp32 in blocks of 16 tokens, two blocks deep:
 // each thread loads one 16-byte piece of block b+1 at the start of block b and writes it
-// to LDS eight tokens later, so the load latency hides behind eight tokens of work.
+// to LDS eight tokens later, so the load latency hides behind eight tokens of work. For
+// the ratio readout q and k pass through phi as they are staged.
 // Sums over a row's four lane groups use the gfx950 row swaps (v_permlane16/32_swap),
 // sums over a row of 16 lanes DPP moves: no LDS crossbar round trips.
 //
@@ -59,7 +65,8 @@ template <typename TS, int DK, int DV, int SPL>
 __global__ __launch_bounds__((VlaShape<TS, DK, DV, SPL>::NT))
 void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __restrict__ v,
                 const TS* __restrict__ u, float inv_lambda0, const float* a0, const float* s0,
-                TS* __restrict__ o, float* s_out, float* a_out, int T) {
+                const float* n0, TS* __restrict__ o, float* s_out, float* a_out, float* n_out, int ratio,
+                int T) {
     using Sh = VlaShape<TS, DK, DV, SPL>;
     constexpr int TB = kVlaBlock, NCOL = Sh::NCOL, NQ = NCOL / 4, NT = Sh::NT;
     constexpr int NC64 = (DK + 63) / 64;                               // columns per lane, whole-vector sums
@@ -69,6 +76,7 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
     __shared__ __align__(16) float sy[2][DK];   // A_{t-1} k (k not normalised)
     __shared__ __align__(16) float sa[2][DK];   // gating vector a_t
     __shared__ float srk[2];                    // 1 / |k_t|
+    __shared__ float sden[2];                   // ratio readout: n_t . phi(q_t)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -102,6 +110,14 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
         }
     }
 
+    // ---- ratio readout: wave 0 keeps the denominator vector n, columns lane + 64 i
+    float nv[NC64];
+#pragma unroll
+    for (int i = 0; i < NC64; ++i) {
+        const int c = lane + 64 * i;
+        nv[i] = (ratio && wave == 0 && n0 != nullptr && (DK % 64 == 0 || c < DK)) ? n0[bh * DK + c] : 0.f;
+    }
+
     // ---- token blocks: piece p of a block is q, k, u or v by range, at element p * EPP of
     // the staged block; tokens past the end read the sequence's first piece (never used)
     u32x4 pend[Sh::PER];
@@ -122,6 +138,13 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
             pend[i] = *reinterpret_cast<const u32x4*>(src + off);
         }
     };
+    // phi = ELU + 1: x + 1 above zero, e^x below
+    auto phi4 = [](f32x4 x) {
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = x[e] > 0.f ? x[e] + 1.f : __builtin_amdgcn_exp2f(x[e] * 1.4426950408889634f);
+        return y;
+    };
     auto stage_block = [&](int slot) {
 #pragma unroll
         for (int i = 0; i < Sh::PER; ++i) {
@@ -129,14 +152,23 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
             if (Sh::PTOT % NT == 0 || p < Sh::PTOT) {
                 float* dst = &sblk[slot][p * Sh::EPP];
                 const u32x4 r = pend[i];
+                const bool map = ratio && p < 2 * Sh::PK;   // q and k pieces
                 if constexpr (sizeof(TS) == 2) {
                     // bf16 pairs: the low half of each word is the earlier element
-                    *reinterpret_cast<f32x4*>(dst) = f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u),
-                                                           __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xffff0000u)};
-                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{__uint_as_float(r[2] << 16), __uint_as_float(r[2] & 0xffff0000u),
-                                                               __uint_as_float(r[3] << 16), __uint_as_float(r[3] & 0xffff0000u)};
+                    f32x4 lo = f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u),
+                                     __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xffff0000u)};
+                    f32x4 hi = f32x4{__uint_as_float(r[2] << 16), __uint_as_float(r[2] & 0xffff0000u),
+                                     __uint_as_float(r[3] << 16), __uint_as_float(r[3] & 0xffff0000u)};
+                    if (map) {
+                        lo = phi4(lo);
+                        hi = phi4(hi);
+                    }
+                    *reinterpret_cast<f32x4*>(dst) = lo;
+                    *reinterpret_cast<f32x4*>(dst + 4) = hi;
                 } else {
-                    *reinterpret_cast<u32x4*>(dst) = r;
+                    f32x4 x = __builtin_bit_cast(f32x4, r);
+                    if (map) x = phi4(x);
+                    *reinterpret_cast<f32x4*>(dst) = x;
                 }
             }
         }
@@ -183,14 +215,15 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
                 const float* blk = sblk[(t / TB) & 1];
                 const int j = t & (TB - 1);
                 // whole-vector sums: columns lane, lane + 64
-                float zc[NC64], yc[NC64];
+                float zc[NC64], yc[NC64], kcol[NC64];
                 float kn = 0.f, uz = 0.f, zkr = 0.f;
 #pragma unroll
                 for (int i = 0; i < NC64; ++i) {
                     const int c = lane + 64 * i;
-                    zc[i] = yc[i] = 0.f;
+                    zc[i] = yc[i] = kcol[i] = 0.f;
                     if (DK % 64 == 0 || c < DK) {
                         const float kc = blk[OK + j * DK + c], uc = blk[OU + j * DK + c];
+                        kcol[i] = kc;
                         zc[i] = sz[par][c];
                         yc[i] = sy[par][c];
                         kn += kc * kc;
@@ -216,6 +249,24 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
                         if (DK % 64 == 0 || c < DK) sa[par][c] = yc[i] * ra;
                     }
                     if (lane == 0) srk[par] = rk;
+                    if (ratio) {
+                        // n_t = n_{t-1} + (1 - n_{t-1}.k^) a_t, then n_t . phi(q_t) for the readout
+                        float nk = 0.f;
+#pragma unroll
+                        for (int i = 0; i < NC64; ++i) nk += nv[i] * kcol[i];
+                        const float f = 1.f - wave_sum(nk) * rk;
+                        float nq = 0.f;
+#pragma unroll
+                        for (int i = 0; i < NC64; ++i) {
+                            const int c = lane + 64 * i;
+                            if (DK % 64 == 0 || c < DK) {
+                                nv[i] += f * (yc[i] * ra);
+                                nq += nv[i] * blk[j * DK + c];
+                            }
+                        }
+                        nq = wave_sum(nq);
+                        if (lane == 0) sden[par] = nq;
+                    }
                 }
                 // rank-1 update of this lane's row slice
                 const float f = zm * rden;
@@ -256,6 +307,7 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
                 }
             }
             op = cross_row_sum(op);
+            if (ratio) op = op / sden[ts & 1];
             if (g == 0) Store<TS>::store(og, static_cast<int64_t>(ts) * DV + m, op);
         }
     }
@@ -268,6 +320,13 @@ void vla_kernel(const TS* __restrict__ q, const TS* __restrict__ k, const TS* __
         for (int i = 0; i < NQ; ++i)
             *reinterpret_cast<f32x4*>(dst + 4 * i) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
     }
+    if (ratio && wave == 0 && part == 0 && n_out != nullptr) {
+#pragma unroll
+        for (int i = 0; i < NC64; ++i) {
+            const int c = lane + 64 * i;
+            if (DK % 64 == 0 || c < DK) n_out[bh * DK + c] = nv[i];
+        }
+    }
 }
 
 template <typename TS, int DK, int DV, int SPL>
@@ -276,19 +335,21 @@ hipError_t launch_split(const VlaArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((vla_kernel<TS, DK, DV, SPL>), dim3(static_cast<unsigned>(heads * SPL)),
                        dim3(VlaShape<TS, DK, DV, SPL>::NT), 0, stream, static_cast<const TS*>(a.q),
                        static_cast<const TS*>(a.k), static_cast<const TS*>(a.v), static_cast<const TS*>(a.u),
-                       a.inv_lambda0, a.a0, a.s0, static_cast<TS*>(a.o), a.s_out, a.a_out, a.T);
+                       a.inv_lambda0, a.a0, a.s0, a.n0, static_cast<TS*>(a.o), a.s_out, a.a_out, a.n_out,
+                       a.ratio, a.T);
     return hipGetLastError();
 }
 
 // Two workgroups per sequence, each with half of the rows of S and the whole penalty chain,
 // when there are fewer sequences than CUs: every CU then works, each on three quarters of a
 // token's arithmetic. Not when the penalty is updated in place (a0 == a_out: a part could
-// read it after another has written it) or d_v = 16.
+// read it after another has written it; likewise the denominator vector) or d_v = 16.
 template <typename TS, int DK, int DV>
 hipError_t launch_shape(const VlaArgs& a, hipStream_t stream) {
     const int64_t heads = static_cast<int64_t>(a.B) * a.H;
     if constexpr (DV >= 32) {
-        if (heads < 256 && (a.a_out == nullptr || a.a_out != a.a0)) return launch_split<TS, DK, DV, 2>(a, stream);
+        if (heads < 256 && (a.a_out == nullptr || a.a_out != a.a0) && (a.n_out == nullptr || a.n_out != a.n0))
+            return launch_split<TS, DK, DV, 2>(a, stream);
     }
     return launch_split<TS, DK, DV, 1>(a, stream);
 }

@@ -93,6 +93,7 @@ class Workload:
     s0: Optional[np.ndarray] = None          # [B,H,dv,dk] fp32
     u: Optional[np.ndarray] = None           # vla penalty directions [B,H,T,dk] (decode: [steps,N,H,dk])
     a0: Optional[np.ndarray] = None          # vla inverse penalty [B,H,dk,dk] fp32
+    n0: Optional[np.ndarray] = None          # vla readout denominator vector [B,H,dk] fp32
     lambda0: float = 1.0                     # vla: A_0 = I / lambda0 when a0 is None
     meta: dict = field(default_factory=dict)
 
@@ -212,34 +213,36 @@ def _penalty_inverse(lead, dk, lambda0, rng):
 
 
 def vla_inputs(B, H, T, dk, dv, *, dtype="bf16", seed=0, with_state=False, lambda0=1.0):
-    """Variational linear attention: q, k, u ~ N(0,1)/sqrt(dk) (u the penalty direction
-    added per token), v ~ N(0,1); A_0 = I / lambda0 (with_state: a perturbed SPD A_0 and
-    S_0 ~ N(0, 0.01))."""
+    """Variational linear attention: q, k ~ N(0,1) (unit scale: the readout's ELU+1 feature
+    map sees both of its branches), v ~ N(0,1), u ~ N(0,1)/sqrt(dk) (the penalty direction
+    added per token); A_0 = I / lambda0 (with_state: a perturbed SPD A_0, S_0 ~ N(0, 0.01)
+    and a positive denominator vector n_0 ~ U(0.8, 1.6)/sqrt(dk), the scale it settles at)."""
     rng = np.random.default_rng(seed)
-    sc = 1.0 / np.sqrt(dk)
-    q = _store(rng.standard_normal((B, H, T, dk)) * sc, dtype)
-    k = _store(rng.standard_normal((B, H, T, dk)) * sc, dtype)
+    q = _store(rng.standard_normal((B, H, T, dk)), dtype)
+    k = _store(rng.standard_normal((B, H, T, dk)), dtype)
     v = _store(rng.standard_normal((B, H, T, dv)), dtype)
-    u = _store(rng.standard_normal((B, H, T, dk)) * sc, dtype)
-    s0 = a0 = None
+    u = _store(rng.standard_normal((B, H, T, dk)) / np.sqrt(dk), dtype)
+    s0 = a0 = n0 = None
     if with_state:
         s0 = (rng.standard_normal((B, H, dv, dk)) * 0.1).astype(np.float32)
         a0 = _penalty_inverse((B, H), dk, lambda0, rng)
-    return Workload("vla", dtype, q, k, v, s0=s0, u=u, a0=a0, lambda0=lambda0)
+        n0 = (rng.uniform(0.8, 1.6, (B, H, dk)) / np.sqrt(dk)).astype(np.float32)
+    return Workload("vla", dtype, q, k, v, s0=s0, u=u, a0=a0, n0=n0, lambda0=lambda0)
 
 
 def vla_decode_inputs(N, H, dk, dv, *, steps=1, dtype="bf16", seed=0, lambda0=1.0):
-    """VLA decode: S_0 ~ N(0, 0.01) fp32, a perturbed SPD A_0, then ``steps`` fresh tokens
-    with the sequence workload's recipe. Leading step axis on q, k, v, u."""
+    """VLA decode: S_0 ~ N(0, 0.01) fp32, a perturbed SPD A_0, n_0 ~ U(0.8, 1.6)/sqrt(dk),
+    then ``steps`` fresh tokens with the sequence workload's recipe. Leading step axis on
+    q, k, v, u."""
     rng = np.random.default_rng(seed)
     s0 = (rng.standard_normal((N, H, dv, dk)) * 0.1).astype(np.float32)
     a0 = _penalty_inverse((N, H), dk, lambda0, rng)
-    sc = 1.0 / np.sqrt(dk)
-    q = _store(rng.standard_normal((steps, N, H, dk)) * sc, dtype)
-    k = _store(rng.standard_normal((steps, N, H, dk)) * sc, dtype)
+    n0 = (rng.uniform(0.8, 1.6, (N, H, dk)) / np.sqrt(dk)).astype(np.float32)
+    q = _store(rng.standard_normal((steps, N, H, dk)), dtype)
+    k = _store(rng.standard_normal((steps, N, H, dk)), dtype)
     v = _store(rng.standard_normal((steps, N, H, dv)), dtype)
-    u = _store(rng.standard_normal((steps, N, H, dk)) * sc, dtype)
-    return Workload("vla_decode", dtype, q, k, v, s0=s0, u=u, a0=a0, lambda0=lambda0)
+    u = _store(rng.standard_normal((steps, N, H, dk)) / np.sqrt(dk), dtype)
+    return Workload("vla_decode", dtype, q, k, v, s0=s0, u=u, a0=a0, n0=n0, lambda0=lambda0)
 
 
 # The five workloads the throughput and parity figures are quoted on, and the scalar

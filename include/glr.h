@@ -17,10 +17,13 @@
  *  - Pointers are DEVICE pointers owned by the caller; the library allocates
  *    nothing, keeps no per-call state and may be called from several host
  *    threads on different streams.
- *  - Chunk entry points take a device `workspace` of `workspace_bytes` bytes
- *    (16-byte aligned) for data passed between their kernels; its size comes
- *    from la_chunk_workspace_size() and may be 0, in which case workspace may
- *    be NULL.  Its contents on entry do not matter and are undefined on exit.
+ *  - Chunk entry points take a device `workspace` of `workspace_bytes` bytes,
+ *    16-byte aligned, for data passed between their kernels: the one addition
+ *    to plain (pointers, sizes, stream) signatures, since the library
+ *    allocates nothing and data handed from one kernel of a call to the next
+ *    must live in caller-owned memory.  Its size comes from
+ *    la_chunk_workspace_size() and may be 0, in which case workspace may be
+ *    NULL.  Its contents on entry do not matter and are undefined on exit.
  *    Two calls in flight at the same time need separate workspaces.
  *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued and
  *    the call returns without synchronising; outputs are valid once the stream
@@ -76,6 +79,11 @@ typedef enum la_fuse {
     LA_FUSE_QK_SILU_L2 = 1,    /* q, k are mapped by SiLU then unit L2 norm per token on load */
     LA_FUSE_OUT_RMSNORM = 2    /* each output row is RMS-normalised and weighted */
 } la_fuse;
+
+typedef enum la_vla_readout {
+    LA_VLA_RATIO = 0,   /* the page's output: ELU+1 on keys and queries, o = S phi(q) / (n . phi(q)) */
+    LA_VLA_LINEAR = 1   /* o = S q, the key only normalised */
+} la_vla_readout;
 
 typedef enum la_variant {
     LA_RETENTION = 0,   /* la_chunk_fwd */
@@ -264,32 +272,44 @@ la_status mamba2_chunk_bwd(const void* q, const void* k, const void* v, const fl
  * in one launch.  Per (b, h) and token t, with the inverse penalty A (d_k x d_k)
  * beside the memory S:
  *     z = A u_t;  A <- A - z z^T / (1 + u_t . z)        (M <- M + u_t u_t^T)
- *     a = A k^ / |A k^|,  k^ = k_t / |k_t|
- *     S <- S + (v_t - S k^) a^T;  o_t = S q_t.
+ *     a = A k^ / |A k^|
+ *     S <- S + (v_t - S k^) a^T
+ * and the readout after the write, chosen by `readout`:
+ *  - LA_VLA_RATIO (section 2.3, last paragraph: a ratio of recurrences as in
+ *    standard linear attention, with the ELU+1 feature map phi(x) = x + 1 for
+ *    x > 0, e^x otherwise, on keys and queries): k^ = phi(k_t) / |phi(k_t)|,
+ *    the denominator vector n [d_k] follows the same write with the value 1,
+ *    n <- n + (1 - n . k^) a, and o_t = S phi(q_t) / (n . phi(q_t));
+ *  - LA_VLA_LINEAR: k^ = k_t / |k_t| and o_t = S q_t (no map, no normaliser).
  * q, k, u [B][H][T][d_k] and v, o [B][H][T][d_v] in `dtype` (u_t is the penalty
  * direction added at token t); A starts at a0 [B][H][d_k][d_k] float32 or,
  * when a0 is NULL, at I / lambda0 (lambda0 > 0 and finite); S at s0
- * [B][H][d_v][d_k] float32 or zeros.  s_out and a_out (float32, optional)
- * receive the final S and A; s_out may equal s0 and a_out may equal a0.
- * Arithmetic is fp32 throughout.  A zero key (|k_t| = 0) gives NaN, which
- * propagates.  B, H or T == 0 is valid (outputs s0/a0 or their defaults).
- * d_k, d_v in {16, 32, 64, 128} (LA_ERR_UNSUPPORTED otherwise).  Pointers
- * 16-byte aligned; no workspace.  Errors as for la_chunk_fwd.
+ * [B][H][d_v][d_k] float32 or zeros; n (ratio readout) at n0 [B][H][d_k]
+ * float32 or zeros.  s_out, a_out and n_out (float32, optional) receive the
+ * final S, A and n; each may equal its starting pointer.  n0 and n_out are
+ * not used by the linear readout.  Arithmetic is fp32 throughout.  A zero key
+ * (linear) or a zero denominator (ratio) gives Inf or NaN, which propagates.
+ * B, H or T == 0 is valid (outputs the starting state or its default).  d_k,
+ * d_v in {16, 32, 64, 128} (LA_ERR_UNSUPPORTED otherwise); an unknown readout
+ * is LA_ERR_INVALID.  Pointers 16-byte aligned; no workspace.  Errors as for
+ * la_chunk_fwd.
  */
 la_status vla_fwd(const void* q, const void* k, const void* v, const void* u,
-                  float lambda0, const float* a0, const float* s0,
-                  void* o, float* s_out, float* a_out,
+                  float lambda0, const float* a0, const float* s0, const float* n0,
+                  void* o, float* s_out, float* a_out, float* n_out, int readout,
                   int B, int H, int T, int dk, int dv, la_dtype dtype, void* stream);
 
 /*
  * One VLA decode token for N sequences x H heads: vla_fwd with T = 1 and the
- * memory s [N][H][d_v][d_k] and inverse penalty a [N][H][d_k][d_k] (float32)
- * read and overwritten in place.  q, k, u [N][H][d_k], v and o [N][H][d_v] in
- * `dtype`.  N == 0 or H == 0 is a no-op.  Errors as for la_recurrent_step.
+ * memory s [N][H][d_v][d_k], the inverse penalty a [N][H][d_k][d_k] and, for
+ * the ratio readout, the denominator vector n [N][H][d_k] (float32; required
+ * with LA_VLA_RATIO, unused with LA_VLA_LINEAR) read and overwritten in place.
+ * q, k, u [N][H][d_k], v and o [N][H][d_v] in `dtype`.  N == 0 or H == 0 is a
+ * no-op.  Errors as for la_recurrent_step.
  */
 la_status vla_recurrent_step(const void* q, const void* k, const void* v, const void* u,
-                             float* s, float* a, void* o, int N, int H, int dk, int dv,
-                             la_dtype dtype, void* stream);
+                             float* s, float* a, float* n, void* o, int readout,
+                             int N, int H, int dk, int dv, la_dtype dtype, void* stream);
 
 /*
  * Backward of gla_chunk_fwd (gate per key channel): reverse-mode gradients of
@@ -319,7 +339,8 @@ const char* la_last_error(void);
 /* ABI version: (major << 16) | minor (2.0: workspace arguments; 2.1:
  * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step; 2.3: gdelta_chunk_fwd_fused;
  * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step; 2.6: gla_chunk_bwd;
- * 2.7: single-pass retention and scalar-decay forward, no workspace at B * H * d_v / 16 >= 128). */
+ * 2.7: single-pass retention and scalar-decay forward, no workspace at B * H * d_v / 16 >= 128;
+ * 3.0: vla_fwd and vla_recurrent_step take the readout and the denominator vector). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -16,7 +16,8 @@ Sources (web pages; cited by title and section):
     Fig. 16.5 and its worked example.
   * "Riepilogo Tecnico: Attenzione Lineare Variazionale (VLA)" (gist.science) -
     variational linear attention: the Sherman-Morrison update of the inverse
-    penalty, the normalised gating vector and the residual write.
+    penalty, the normalised gating vector, the residual write and the ELU+1
+    ratio readout.
 
 Every function here is pinned by a ``-m "not gpu"`` test against something other
 than itself (values the pages print, closed forms, invariants, brute force);
@@ -45,5 +46,6 @@ from .glr_oracle import (  # noqa: F401
     gla_backward,
     vla_recurrent,
     vla_decode_step,
+    elu1,
     forward_substitution,
 )

@@ -40,7 +40,8 @@ and the chunkwise form must give the same numbers up to rounding.
 Also here: the reverse-mode gradients of the fixed and scalar decays, and
 variational linear attention (VLA summary page, "Riepilogo Tecnico: Attenzione
 Lineare Variazionale (VLA)", section 2.3) in its recurrent form, which returns
-``(o, S_T, A_T)`` with the inverse penalty ``A`` beside the memory.
+``(o, S_T, A_T, n_T)`` with the inverse penalty ``A`` and the readout's denominator
+vector ``n`` beside the memory.
 """
 
 import numpy as np
@@ -65,6 +66,10 @@ __all__ = [
     "scalar_backward",
     "retention_backward",
     "forward_substitution",
+    "gla_backward",
+    "vla_recurrent",
+    "vla_decode_step",
+    "elu1",
 ]
 
 
@@ -567,7 +572,14 @@ def retention_backward(q, k, v, log_gamma, do, dS_T=None, s0=None):
 
 # --------------------------------------------------------------------------- variational linear attention
 
-def _vla_step(S, A, q_t, k_t, v_t, u_t):
+def elu1(x):
+    """The ELU+1 feature map named by the VLA summary page for its output (section 2.3, last
+    paragraph): ``x + 1`` for ``x > 0``, ``e^x`` otherwise; positive everywhere."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def _vla_step(S, A, n, q_t, k_t, v_t, u_t, readout):
     """One token of VLA, the three steps of the recursive update in the order the VLA
     summary page gives them ("Riepilogo Tecnico: Attenzione Lineare Variazionale (VLA)",
     section 2.3; the penalty geometry of section 2.2):
@@ -575,20 +587,30 @@ def _vla_step(S, A, q_t, k_t, v_t, u_t):
     1. Sherman-Morrison on the inverse penalty: ``M_t = M_{t-1} + u_t u_t^T`` gives
        ``A_t = A_{t-1} - z_t z_t^T / (1 + u_t^T z_t)`` with ``z_t = A_{t-1} u_t``;
     2. the gating vector from the *updated* inverse: ``a_t = A_t k^_t / |A_t k^_t|``,
-       ``k^_t = k_t / |k_t|`` (the key is normalised: section 2.1);
-    3. the memory: ``S_t = S_{t-1} + (v_t - S_{t-1} k^_t) a_t^T``;
+       with the key normalised to unit length (section 2.1);
+    3. the memory: ``S_t = S_{t-1} + (v_t - S_{t-1} k^_t) a_t^T``.
 
-    then the readout ``o_t = S_t q_t`` (read after write, as for every variant here).
-    Shapes: S ``[..., d_v, d_k]``, A ``[..., d_k, d_k]``, vectors ``[..., d]``."""
+    Readout, read after the write. ``"ratio"`` (the page's output: a ratio of recurrences
+    as in standard linear attention, with the ELU+1 feature map phi): keys and queries pass
+    through phi, ``k^_t = phi(k_t) / |phi(k_t)|``, and the denominator vector ``n`` obeys the
+    same update driven by the constant value 1, ``n_t = n_{t-1} + (1 - n_{t-1}.k^_t) a_t``;
+    ``o_t = S_t phi(q_t) / (n_t . phi(q_t))``. ``"linear"``: no feature map and no
+    normaliser, ``k^_t = k_t / |k_t|``, ``o_t = S_t q_t``; ``n`` is not used.
+    Shapes: S ``[..., d_v, d_k]``, A ``[..., d_k, d_k]``, n and vectors ``[..., d]``."""
     z = np.einsum("...mc,...c->...m", A, u_t)
     den = 1.0 + np.sum(u_t * z, axis=-1)
     A = A - z[..., :, None] * z[..., None, :] / den[..., None, None]
-    kh = k_t / np.linalg.norm(k_t, axis=-1, keepdims=True)
+    kf = elu1(k_t) if readout == "ratio" else k_t
+    kh = kf / np.linalg.norm(kf, axis=-1, keepdims=True)
     y = np.einsum("...mc,...c->...m", A, kh)
     a = y / np.linalg.norm(y, axis=-1, keepdims=True)
     resid = v_t - np.einsum("...mc,...c->...m", S, kh)
     S = S + resid[..., :, None] * a[..., None, :]
-    return _read(S, q_t), S, A
+    if readout == "linear":
+        return _read(S, q_t), S, A, n
+    n = n + (1.0 - np.sum(n * kh, axis=-1))[..., None] * a
+    fq = elu1(q_t)
+    return _read(S, fq) / np.sum(n * fq, axis=-1)[..., None], S, A, n
 
 
 def _vla_init_penalty(k, a0, lambda0):
@@ -598,27 +620,43 @@ def _vla_init_penalty(k, a0, lambda0):
     return np.broadcast_to(np.eye(dk) / float(lambda0), k.shape[:-2] + (dk, dk)).copy()
 
 
-def vla_recurrent(q, k, v, u, lambda0=1.0, s0=None, a0=None):
+def _vla_readout(readout):
+    if readout not in ("ratio", "linear"):
+        raise ValueError(f"readout must be 'ratio' or 'linear', got {readout!r}")
+    return readout
+
+
+def vla_recurrent(q, k, v, u, lambda0=1.0, s0=None, a0=None, n0=None, readout="ratio"):
     """Variational linear attention over whole sequences, token by token (the
     definition: section 2.3 of the VLA summary page; see ``_vla_step``).
 
     ``q, k, u`` are ``[B, H, T, d_k]`` (``u_t`` the penalty direction added to M at
     token t), ``v`` is ``[B, H, T, d_v]``. The inverse penalty starts at
     ``A_0 = M_0^{-1} = I / lambda0`` unless ``a0 [B, H, d_k, d_k]`` is given; the
-    memory at ``s0`` or zeros. Returns ``(o, S_T, A_T)``."""
-    q, k, v, u = _f64(q, k, v, u)
+    memory at ``s0`` or zeros; with the ratio readout the denominator vector at
+    ``n0 [B, H, d_k]`` or zeros. Returns ``(o, S_T, A_T, n_T)`` (``n_T`` None with the
+    linear readout)."""
+    readout = _vla_readout(readout)
+    q, k, v, u, n0 = _f64(q, k, v, u, n0)
     S = _init_state(q, v, s0)
     A = _vla_init_penalty(k, a0, lambda0)
+    n = None
+    if readout == "ratio":
+        n = np.zeros(k.shape[:-2] + (k.shape[-1],)) if n0 is None else n0.copy()
     T = q.shape[-2]
     o = np.zeros(v.shape)
     for t in range(T):
-        o[..., t, :], S, A = _vla_step(S, A, q[..., t, :], k[..., t, :], v[..., t, :], u[..., t, :])
-    return o, S, A
+        o[..., t, :], S, A, n = _vla_step(S, A, n, q[..., t, :], k[..., t, :], v[..., t, :], u[..., t, :], readout)
+    return o, S, A, n
 
 
-def vla_decode_step(q, k, v, u, s, a):
+def vla_decode_step(q, k, v, u, s, a, n=None, readout="ratio"):
     """One VLA token for N sequences: ``q, k, u [N, H, d_k]``, ``v [N, H, d_v]``, the
-    memory ``s [N, H, d_v, d_k]`` and inverse penalty ``a [N, H, d_k, d_k]``. Returns
-    ``(o, s_new, a_new)``; the inputs are not modified."""
-    q, k, v, u, s, a = _f64(q, k, v, u, s, a)
-    return _vla_step(s, a, q, k, v, u)
+    memory ``s [N, H, d_v, d_k]``, inverse penalty ``a [N, H, d_k, d_k]`` and, with the ratio
+    readout, the denominator vector ``n [N, H, d_k]``. Returns ``(o, s_new, a_new, n_new)``;
+    the inputs are not modified."""
+    readout = _vla_readout(readout)
+    q, k, v, u, s, a, n = _f64(q, k, v, u, s, a, n)
+    if readout == "ratio" and n is None:
+        raise ValueError("the ratio readout carries the denominator vector n")
+    return _vla_step(s, a, n, q, k, v, u, readout)

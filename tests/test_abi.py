@@ -37,9 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.la_version() >> 16 == 2
-    assert lib.la_version() & 0xffff >= 7      # 2.1 mamba2, 2.2 gdelta decode, 2.3 fused, 2.4 backward, 2.5 vla,
-    #                                          2.6 gla backward, 2.7 single-pass forward
+    assert lib.la_version() >> 16 == 3        # 3.0: the VLA entry points take the readout and its denominator
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -141,6 +139,11 @@ def test_chunk_validation(lib, fn):
     assert _chunk(lib, fn, chunk=48) == _native.LA_ERR_UNSUPPORTED
     if fn == "gdelta_chunk_fwd":
         assert _chunk(lib, fn, beta=None) == _native.LA_ERR_INVALID
+    # T == 0 launches kernels that read retention's per-head decay (and write s_out): the decay is
+    # required whenever there are heads; the per-token gates only when there are tokens
+    if fn == "la_chunk_fwd":
+        assert _chunk(lib, fn, T=0, gate=None) == _native.LA_ERR_INVALID
+        assert b"log_gamma is NULL" in lib.la_last_error()
     # nothing to do: no pointer is needed and nothing is launched
     assert _chunk(lib, fn, B=0, q=None, k=None, v=None, o=None, gate=None, beta=None) == _native.LA_OK
     assert _chunk(lib, fn, H=0, q=None, k=None, v=None, o=None, gate=None, beta=None) == _native.LA_OK
@@ -226,6 +229,8 @@ def test_backward_validation(lib):
         assert call(fn, ws_bytes=16) == _native.LA_ERR_INVALID
         assert b"workspace too small" in lib.la_last_error()
         assert call(fn, dk_=24) == _native.LA_ERR_UNSUPPORTED
+        if fn == "la_chunk_bwd":
+            assert call(fn, T=0, gate=None) == _native.LA_ERR_INVALID
         assert call(fn, B=0, q=None, k=None, v=None, gate=None, dout=None, dq=None, dk=None, dv=None,
                     dgate=None, ws=None) == _native.LA_OK
 
@@ -247,12 +252,17 @@ def test_vla_validation(lib):
     P = ctypes.c_void_p
 
     def call(lam=1.0, **kw):
-        a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, a0=None, s0=None, o=FAKE, s_out=None, a_out=None, B=2, H=2, T=8,
-                 dk=64, dv=64, dtype=1)
+        a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, a0=None, s0=None, n0=None, o=FAKE, s_out=None, a_out=None,
+                 n_out=None, readout=_native.LA_VLA_RATIO, B=2, H=2, T=8, dk=64, dv=64, dtype=1)
         a.update(kw)
-        return lib.vla_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["u"]), lam, P(a["a0"]), P(a["s0"]), P(a["o"]),
-                           P(a["s_out"]), P(a["a_out"]), a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], None)
+        return lib.vla_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["u"]), lam, P(a["a0"]), P(a["s0"]), P(a["n0"]),
+                           P(a["o"]), P(a["s_out"]), P(a["a_out"]), P(a["n_out"]), a["readout"], a["B"], a["H"],
+                           a["T"], a["dk"], a["dv"], a["dtype"], None)
 
+    assert call(readout=2) == _native.LA_ERR_INVALID
+    assert b"unknown readout" in lib.la_last_error()
+    assert call(n0=MISALIGNED) == _native.LA_ERR_INVALID
+    assert call(n_out=MISALIGNED) == _native.LA_ERR_INVALID
     assert call(u=None) == _native.LA_ERR_INVALID
     assert b"u is NULL" in lib.la_last_error()
     assert call(lam=0.0) == _native.LA_ERR_INVALID
@@ -273,11 +283,15 @@ def test_vla_decode_validation(lib):
     P = ctypes.c_void_p
 
     def call(**kw):
-        a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, s=FAKE, a=FAKE, o=FAKE, N=4, H=2, dk=128, dv=128, dtype=1)
+        a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, s=FAKE, a=FAKE, n=FAKE, o=FAKE, readout=_native.LA_VLA_RATIO, N=4,
+                 H=2, dk=128, dv=128, dtype=1)
         a.update(kw)
-        return lib.vla_recurrent_step(P(a["q"]), P(a["k"]), P(a["v"]), P(a["u"]), P(a["s"]), P(a["a"]), P(a["o"]),
-                                      a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+        return lib.vla_recurrent_step(P(a["q"]), P(a["k"]), P(a["v"]), P(a["u"]), P(a["s"]), P(a["a"]), P(a["n"]),
+                                      P(a["o"]), a["readout"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
 
+    assert call(n=None) == _native.LA_ERR_INVALID                    # the ratio readout carries n
+    assert b"n is NULL" in lib.la_last_error()
+    assert call(readout=-1) == _native.LA_ERR_INVALID
     assert call(a=None) == _native.LA_ERR_INVALID
     assert b"a is NULL" in lib.la_last_error()
     assert call(u=MISALIGNED) == _native.LA_ERR_INVALID
