@@ -212,14 +212,16 @@ def _penalty_inverse(lead, dk, lambda0, rng):
     return ((np.eye(dk) + 0.04 * P) / lambda0).astype(np.float32)
 
 
-def vla_inputs(B, H, T, dk, dv, *, dtype="bf16", seed=0, with_state=False, lambda0=1.0):
-    """Variational linear attention: q, k ~ N(0,1) (unit scale: the readout's ELU+1 feature
-    map sees both of its branches), v ~ N(0,1), u ~ N(0,1)/sqrt(dk) (the penalty direction
-    added per token); A_0 = I / lambda0 (with_state: a perturbed SPD A_0, S_0 ~ N(0, 0.01)
+def vla_inputs(B, H, T, dk, dv, *, dtype="bf16", seed=0, with_state=False, lambda0=1.0, readout="ratio"):
+    """Variational linear attention: v ~ N(0,1), u ~ N(0,1)/sqrt(dk) (the penalty direction
+    added per token); q, k ~ N(0,1) for the ratio readout (unit scale: its ELU+1 feature map
+    sees both of its branches) or N(0,1)/sqrt(dk) for the linear one (o = S q at the scale of
+    the other workloads); A_0 = I / lambda0 (with_state: a perturbed SPD A_0, S_0 ~ N(0, 0.01)
     and a positive denominator vector n_0 ~ U(0.8, 1.6)/sqrt(dk), the scale it settles at)."""
     rng = np.random.default_rng(seed)
-    q = _store(rng.standard_normal((B, H, T, dk)), dtype)
-    k = _store(rng.standard_normal((B, H, T, dk)), dtype)
+    sc = 1.0 if readout == "ratio" else 1.0 / np.sqrt(dk)
+    q = _store(rng.standard_normal((B, H, T, dk)) * sc, dtype)
+    k = _store(rng.standard_normal((B, H, T, dk)) * sc, dtype)
     v = _store(rng.standard_normal((B, H, T, dv)), dtype)
     u = _store(rng.standard_normal((B, H, T, dk)) / np.sqrt(dk), dtype)
     s0 = a0 = n0 = None
@@ -230,16 +232,17 @@ def vla_inputs(B, H, T, dk, dv, *, dtype="bf16", seed=0, with_state=False, lambd
     return Workload("vla", dtype, q, k, v, s0=s0, u=u, a0=a0, n0=n0, lambda0=lambda0)
 
 
-def vla_decode_inputs(N, H, dk, dv, *, steps=1, dtype="bf16", seed=0, lambda0=1.0):
+def vla_decode_inputs(N, H, dk, dv, *, steps=1, dtype="bf16", seed=0, lambda0=1.0, readout="ratio"):
     """VLA decode: S_0 ~ N(0, 0.01) fp32, a perturbed SPD A_0, n_0 ~ U(0.8, 1.6)/sqrt(dk),
-    then ``steps`` fresh tokens with the sequence workload's recipe. Leading step axis on
-    q, k, v, u."""
+    then ``steps`` fresh tokens with the sequence workload's recipe for that readout. Leading
+    step axis on q, k, v, u."""
     rng = np.random.default_rng(seed)
     s0 = (rng.standard_normal((N, H, dv, dk)) * 0.1).astype(np.float32)
     a0 = _penalty_inverse((N, H), dk, lambda0, rng)
     n0 = (rng.uniform(0.8, 1.6, (N, H, dk)) / np.sqrt(dk)).astype(np.float32)
-    q = _store(rng.standard_normal((steps, N, H, dk)), dtype)
-    k = _store(rng.standard_normal((steps, N, H, dk)), dtype)
+    sc = 1.0 if readout == "ratio" else 1.0 / np.sqrt(dk)
+    q = _store(rng.standard_normal((steps, N, H, dk)) * sc, dtype)
+    k = _store(rng.standard_normal((steps, N, H, dk)) * sc, dtype)
     v = _store(rng.standard_normal((steps, N, H, dv)), dtype)
     u = _store(rng.standard_normal((steps, N, H, dk)) / np.sqrt(dk), dtype)
     return Workload("vla_decode", dtype, q, k, v, s0=s0, u=u, a0=a0, n0=n0, lambda0=lambda0)

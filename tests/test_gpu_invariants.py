@@ -1,0 +1,155 @@
+"""GPU checks against answers the method fixes by itself, and over the decode workload's
+full length, through the C ABI.
+
+* Decode over 1000 consecutive steps (the decode workload's length) on 64 (sequence, head)
+  pairs: every step's output and the final memory against the oracle's decode step (the
+  recurrent form of the RetNet page, section "RetNet: la retention e le sue tre forme").
+* The delta rule's own invariants through gdelta_chunk_fwd at chunk 64, d = 128
+  ("Scrivere meglio nella memoria", sections "Correggere: la delta rule" and "Unire oblio e
+  correzione: Gated DeltaNet"): with beta = 1 and unit keys a write overwrites, so reading
+  with q = k returns v exactly; beta = 0 is a pure fade S_t = alpha_t S_{t-1}; alpha = 1 is
+  DeltaNet, against the oracle's recurrent form.
+* GLA with strong per-channel gates (log alpha in [-4.5, -3.5]: a 16-token run of one
+  channel sums to -56 .. -72), where the per-16-token factorisation of the decays works
+  with rescaled keys near the top of the fp32 / bf16 range.
+
+Bounds are the bf16 parity gates: max |d| <= 2e-2 and <= 1e-2 of the reference's largest
+entry (memory: relative 1e-2; decode memory: relative 1e-5)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from gated_linear_recurrences_amd import api, synthetic
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _t(x, dtype=torch.float32):
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype).contiguous()
+
+
+def _gate(label, got, ref, rel=1e-2, absolute=2e-2):
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    scale = max(float(np.max(np.abs(ref))) if ref.size else 0.0, 1e-30)
+    msg = f"{label}: max|d|={err:.3e} max|ref|={scale:.3e}"
+    print(msg, flush=True)
+    assert np.all(np.isfinite(got)), msg
+    assert err <= absolute and err <= rel * scale, msg
+
+
+# ----------------------------------------------------------------------------- decode, 1000 steps
+
+def test_decode_1000_steps():
+    """The decode workload's recipe and length (1000 steps, d = 128, fp32 memory, bf16
+    tokens, gates sigmoid(N(2,1))) on 8 x 8 = 64 (sequence, head) pairs: the output of
+    every step and the memory after the last, against the oracle's decode step."""
+    N, H, d, steps = 8, 8, 128, 1000
+    w = synthetic.decode_inputs(N, H, d, d, steps=steps, dtype="bf16", seed=5)
+    q, k, v, a = _t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16), _t(w.alpha)
+    s = _t(w.s0)
+    o = torch.empty((steps, N, H, d), dtype=torch.bfloat16, device=DEV)
+    for i in range(steps):
+        api.la_recurrent_step(q[i], k[i], v[i], a[i], s, o=o[i])
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    S_ref = w.s0.astype(np.float64)
+    worst = 0.0
+    for i in range(steps):
+        o_ref, S_ref = orc.decode_step(w.q[i], w.k[i], w.v[i], w.alpha[i], S_ref)
+        err = float(np.max(np.abs(o[i] - o_ref)))
+        scale = float(np.max(np.abs(o_ref)))
+        worst = max(worst, err / scale)
+        assert err <= 2e-2 and err <= 1e-2 * scale, f"step {i}: max|do|={err:.3e} max|o|={scale:.3e}"
+    serr = float(np.max(np.abs(s.cpu().numpy() - S_ref)) / np.max(np.abs(S_ref)))
+    print(f"decode 1000 steps: worst step rel err {worst:.3e}, final memory rel err {serr:.3e}", flush=True)
+    assert serr <= 1e-5
+
+
+# ----------------------------------------------------------------------------- delta-rule invariants
+
+B, H, T, D, C = 2, 4, 300, 128, 64      # four chunks and a ragged tail of 44 tokens
+
+
+def _unit_keys(rng, shape, d):
+    """Keys with exactly unit norm in bf16: 64 of the d entries are +-1/8, the rest 0
+    (different supports and signs per token, so keys overlap and the delta rule works)."""
+    k = np.zeros(shape + (d,), dtype=np.float32)
+    flat = k.reshape(-1, d)
+    for row in flat:
+        idx = rng.choice(d, size=64, replace=False)
+        row[idx] = rng.choice([-0.125, 0.125], size=64)
+    return k
+
+
+def _gdelta(q, k, v, log_alpha, beta, s0=None):
+    o, S = api.gdelta_chunk_fwd(_t(q, torch.bfloat16), _t(k, torch.bfloat16), _t(v, torch.bfloat16),
+                                _t(log_alpha), _t(beta), chunk=C, s0=_t(s0))
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("state", [False, True])
+def test_delta_overwrite_reads_back_v(state):
+    """beta = 1 with unit keys: S_t k_t = v_t after every write, whatever alpha_t and the
+    memory before, so the output with q_t = k_t is v_t itself."""
+    rng = np.random.default_rng(80)
+    k = _unit_keys(rng, (B, H, T), D)
+    v = synthetic.round_to_bf16(rng.standard_normal((B, H, T, D)) / 4.0)
+    log_alpha = (-np.log1p(np.exp(rng.standard_normal((B, H, T)))) / 8.0).astype(np.float32)
+    beta = np.ones((B, H, T), dtype=np.float32)
+    s0 = (rng.standard_normal((B, H, D, D)) * 0.1).astype(np.float32) if state else None
+    o, S = _gdelta(k, k, v, log_alpha, beta, s0)
+    _gate(f"overwrite o vs v (state={state})", o, v.astype(np.float64))
+    kl = k[:, :, -1].astype(np.float64)
+    _gate(f"overwrite S_T k_T vs v_T (state={state})", np.einsum("bhmc,bhc->bhm", S, kl),
+          v[:, :, -1].astype(np.float64))
+
+
+def test_delta_zero_beta_is_a_pure_fade():
+    """beta = 0: nothing is written, S_t = alpha_t S_{t-1}, so o_t = e^(sum_{r<=t} log alpha_r)
+    S_0 q_t and S_T = e^(sum log alpha) S_0 (closed form, no oracle)."""
+    rng = np.random.default_rng(81)
+    w = synthetic.gdelta_inputs(B, H, T, D, D, chunk=C, dtype="bf16", seed=81, with_state=True)
+    log_alpha = rng.uniform(-0.05, 0.0, (B, H, T)).astype(np.float32)
+    beta = np.zeros((B, H, T), dtype=np.float32)
+    o, S = _gdelta(w.q, w.k, w.v, log_alpha, beta, w.s0)
+    G = np.cumsum(log_alpha.astype(np.float64), axis=-1)
+    s0 = w.s0.astype(np.float64)
+    o_ref = np.exp(G)[..., None] * np.einsum("bhmc,bhtc->bhtm", s0, w.q.astype(np.float64))
+    S_ref = np.exp(G[..., -1])[..., None, None] * s0
+    _gate("zero beta o", o, o_ref)
+    _gate("zero beta S_T", S, S_ref, absolute=np.inf)
+
+
+@pytest.mark.parametrize("state", [False, True])
+def test_delta_unit_gate_is_deltanet(state):
+    """alpha = 1 (log alpha = 0): DeltaNet, S_t = S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T;
+    against the oracle's recurrent form (token by token, the definition)."""
+    w = synthetic.gdelta_inputs(B, H, T, D, D, chunk=C, dtype="bf16", seed=82, with_state=state)
+    log_alpha = np.zeros((B, H, T), dtype=np.float32)
+    o, S = _gdelta(w.q, w.k, w.v, log_alpha, w.beta, w.s0)
+    o_ref, S_ref = orc.gdelta_recurrent(w.q, w.k, w.v, log_alpha, w.beta, s0=w.s0)
+    _gate(f"DeltaNet o (state={state})", o, o_ref)
+    _gate(f"DeltaNet S_T (state={state})", S, S_ref, absolute=np.inf)
+
+
+# ----------------------------------------------------------------------------- GLA, strong gates
+
+@pytest.mark.parametrize("shape", [(2, 4, 300, 128, 128, 64), (1, 2, 130, 64, 32, 32), (8, 16, 70, 128, 128, 64)])
+def test_gla_strong_gates(shape):
+    """log alpha uniform in [-4.5, -3.5] per (token, key channel): a channel's 16-token run
+    sums to -56 .. -72, and outputs are carried by the last few tokens."""
+    Bs, Hs, Ts, dk, dv, c = shape
+    w = synthetic.gla_inputs(Bs, Hs, Ts, dk, dv, chunk=c, dtype="bf16", seed=83 + Ts, with_state=True)
+    w.log_alpha = np.random.default_rng(84).uniform(-4.5, -3.5, (Bs, Hs, Ts, dk)).astype(np.float32)
+    o, S = api.gla_chunk_fwd(_t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16),
+                             _t(w.log_alpha), chunk=c, s0=_t(w.s0))
+    torch.cuda.synchronize()
+    o_ref, S_ref = orc.gla_chunkwise(w.q, w.k, w.v, w.log_alpha, c, s0=w.s0)
+    _gate(f"gla strong gates {shape} o", o.float().cpu().numpy().astype(np.float64), o_ref)
+    _gate(f"gla strong gates {shape} S_T", S.cpu().numpy().astype(np.float64), S_ref, absolute=np.inf)

@@ -288,14 +288,12 @@ def test_deterministic(kind, dtype, heads):
 # ----------------------------------------------------------------------------- fused feature map / output norm
 
 def _fused_reference(w, weight, eps, qk, norm):
-    """The oracle around the fused entry point: SiLU + L2 on the raw q, k in fp64 (rounded to
-    bf16 for bf16 storage, where the kernel rounds the mapped rows before its products), the
-    gated-delta chunkwise form, then the RMS norm of each output row."""
+    """The oracle around the fused entry point, all in fp64: SiLU + L2 on the raw q, k (kept
+    in fp64: the kernel's own rounding of the mapped rows is part of the error measured),
+    the gated-delta chunkwise form, then the RMS norm of each output row."""
     q, k = w.q, w.k
     if qk:
         q, k = orc.silu_l2(q), orc.silu_l2(k)
-        if w.dtype == "bf16":
-            q, k = synthetic.round_to_bf16(q), synthetic.round_to_bf16(k)
     o, S = orc.gdelta_chunkwise(q, k, w.v, w.log_alpha, w.beta, w.chunk, s0=w.s0)
     if norm:
         o = orc.rms_norm(o, weight, eps)

@@ -59,7 +59,8 @@ SHAPES = [(1, 2, 37, 16, 16), (2, 1, 100, 32, 64), (1, 2, 130, 64, 32), (2, 2, 2
 @pytest.mark.parametrize("shape", SHAPES)
 def test_vla_parity(shape, state, dtype, readout):
     B, H, T, dk, dv = shape
-    w = synthetic.vla_inputs(B, H, T, dk, dv, dtype=dtype, seed=700 + sum(shape), with_state=state, lambda0=0.8)
+    w = synthetic.vla_inputs(B, H, T, dk, dv, dtype=dtype, seed=700 + sum(shape), with_state=state, lambda0=0.8,
+                             readout=readout)
     st = _st(dtype)
     print(f"vla_fwd {shape} state={state} {dtype} {readout}", flush=True)
     o, S, A, n = api.vla_fwd(_t(w.q, st), _t(w.k, st), _t(w.v, st), _t(w.u, st), lambda0=w.lambda0, a0=_t(w.a0),
@@ -76,7 +77,7 @@ def test_vla_parity(shape, state, dtype, readout):
 def test_vla_in_place_continuation(readout):
     """s_out, a_out and n_out may alias s0, a0 and n0: two calls in place equal one call."""
     B, H, T, dk, dv = 2, 2, 90, 64, 64
-    w = synthetic.vla_inputs(B, H, T, dk, dv, dtype="bf16", seed=7, with_state=True)
+    w = synthetic.vla_inputs(B, H, T, dk, dv, dtype="bf16", seed=7, with_state=True, readout=readout)
     q, k, v, u = (_t(x, torch.bfloat16) for x in (w.q, w.k, w.v, w.u))
     S, A, N = _t(w.s0), _t(w.a0), _t(w.n0)
     outs = []
@@ -98,7 +99,7 @@ def test_vla_decode_steps(dims, dtype, readout):
     """Five decode tokens in place on the memory, the inverse penalty and the denominator."""
     dk, dv = dims
     N, H, steps = 6, 3, 5
-    w = synthetic.vla_decode_inputs(N, H, dk, dv, steps=steps, dtype=dtype, seed=dk + dv)
+    w = synthetic.vla_decode_inputs(N, H, dk, dv, steps=steps, dtype=dtype, seed=dk + dv, readout=readout)
     st = _st(dtype)
     s, a, n = _t(w.s0), _t(w.a0), _t(w.n0)
     s_ref, a_ref = w.s0.astype(np.float64), w.a0.astype(np.float64)
