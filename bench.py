@@ -1,31 +1,34 @@
 #!/usr/bin/env python3
-"""Throughput of the chunked forward on one MI355X, with its roofline and the CPU oracle beside it.
+"""Throughput of the chunked forwards on one MI355X, with their rooflines and the CPU oracle beside them.
 
-A step is one call of the chunked forward - every stage of the hot path (the
-memory carried from chunk to chunk, the decayed triangle, P V, the memory
-readout, the stores), which at this size runs as one single-pass kernel (the
-memory stays on chip; smaller batches take a state pass and an output pass) -
-over one batch of the multi-scale retention workload: B=4,
-H=8, T=2048, d_k=d_v=128, bf16 q/k/v ~ N(0,1)/sqrt(128), per-head decay
-1 - 2^(-5-h), chunk 64, fp32 memory. Inputs are resident in HBM before timing;
-five input sets are rotated so the 256 MB Infinity Cache cannot serve them.
+A step is one call of the gated delta rule's chunked forward - every stage of the hot
+path (the cumulative gates and the per-chunk UT factor T_U in a chunk-parallel prep; the
+memory carried from chunk to chunk, the pseudo-values U, the decayed triangle, P U, the
+memory readout and the stores in one single-pass kernel) - over one batch of the gated
+delta rule workload: B=4, H=16, T=8192, d_k=d_v=128, bf16 q/k = L2(SiLU(N(0,1))), v ~
+N(0,1), beta = sigmoid(N(0,1)), log alpha = -softplus(N(0,1))/8, chunk 64, fp32 memory:
+the largest single-GPU configuration, and the only one whose MFMA ceiling (51%) admits the
+40% target. Inputs are resident in HBM before timing; two input sets are rotated.
 
-Printed: one JSON line. ``value`` is tokens/s (B*H*T per second); ``roofline``
-prices the call (its kernel, timed with HIP events on the launching stream around
-one HIP-graph replay of the timed steps, so that host launches do not pace it)
-against HBM with the algorithmic bytes of the method (q, k, v read, o and the
-final memory written); ``traffic`` is the HBM traffic the counters measured for
-one call; ``mfma`` gives the same run against the dense bf16
-MFMA peak; ``cpu_baseline`` times the fp64 oracle on the host; ``others``
-reports the per-channel-gate (GLA), gated-delta, scalar data-dependent decay
-and decode (per-channel gate, gated delta rule) workloads measured the same way,
-the gated delta rule with its feature map and output norm fused in, the
-backward of the retention and scalar-decay workloads (beside their forward), and
-variational linear attention (whole sequences, and decode).
+Printed: one JSON line. ``value`` is tokens/s (B*H*T per second); ``roofline`` prices the
+call (both kernels, timed with HIP events on the launching stream around one HIP-graph
+replay of the timed steps, so that host launches do not pace it) against HBM with the
+algorithmic bytes of the method (q, k, v and the gates read, o and the final memory
+written); ``traffic`` is the HBM traffic the counters measured for one call; ``mfma``
+gives the same call against the dense bf16 MFMA peak, with the flops counted over the
+causal tiles of each chunk (and the hardware's own MFMA counters when recorded);
+``cpu_baseline`` times the fp64 oracle on the host's cores; ``others`` reports the other
+chunked workloads (retention B4 H8 T2048, GLA and the scalar data-dependent decay at B8
+H16 T4096) each with its own roofline, decode (per-channel gate, gated delta rule), the
+gated delta rule with its feature map and output norm fused in, the backward of
+retention, the scalar decay and GLA (beside their forward), and variational linear
+attention (whole sequences, and decode).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
+    python bench.py --counter-run                       (each chunked workload, three calls, for rocprofv3 --pmc)
     python bench.py --copy-calibration MB --steps K      (plain copy, for counter scaling)
     python bench.py --summarize-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+    python bench.py --summarize-mfma MFMA_DIR
     python bench.py --kernel-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
     python bench.py --trace-table TRACE_DIR
 """
@@ -44,29 +47,52 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
-N_SETS = 5                      # rotated input sets (> 256 MB Infinity Cache for the retention batch)
+N_CU = 256
 
-MAIN = "retention_b4h8_t2048_d128"
+MAIN = "gdelta_b4h16_t8192_d128"
+# the chunked workloads, each priced against its own roofline; rotated input sets (enough to
+# exceed the 256 MB Infinity Cache: the retention batch is 67 MB per set)
+CHUNKED = ("gdelta_b4h16_t8192_d128", "retention_b4h8_t2048_d128", "gla_b8h16_t4096_d128", "mamba2_b8h16_t4096_d128")
+N_SETS = {"gdelta_b4h16_t8192_d128": 2, "retention_b4h8_t2048_d128": 5, "gla_b8h16_t4096_d128": 1,
+          "mamba2_b8h16_t4096_d128": 1}
+# library kernels of one call of each chunked workload (d_k = d_v = 128, chunk 64), as rocprofv3 names them
+WORKLOAD_KERNELS = {
+    "gdelta_b4h16_t8192_d128": ("glr::ck::delta_tfac_kernel<64, 128>", "glr::ck::delta_sp_kernel<64, 128, 128, 32>"),
+    "retention_b4h8_t2048_d128": ("glr::ck::fused_kernel<64, 128, 128, 1, 0>",),
+    "gla_b8h16_t4096_d128": ("glr::ck::state_kernel<64, 128, 4, 1, 8, 1, 1, false>",
+                             "glr::ck::output_kernel<64, 128, 128, 1, 8>"),
+    "mamba2_b8h16_t4096_d128": ("glr::ck::fused_kernel<64, 128, 128, 2, 2>",),
+}
 
 
 def algorithmic_counts(kind, B, H, T, d, chunk, elem_bytes=2):
-    """Algorithmic flops and HBM bytes of one chunked-forward launch.
+    """Algorithmic flops and HBM bytes of one chunked-forward call.
 
     Bytes: read q, k, v (and the gates), write o and the final memory.
-    Flops per token-head (chunk C, head size d): retention, the scalar decay and GLA 4Cd + 4d^2
-    (q.k^T and P.V over the C x C block, S q and k^T v); the gated delta rule
-    8Cd + 6d^2 + 2C^2/3 (K K^T, Q K^T, T.R for W and U0, P.U, W S^T, Q S^T,
-    U^T K and the triangular solve)."""
+    Flops per token-head (chunk C, head size d), counted over the causal tiles (j <= i) of
+    each C x C block, which is all the method needs: retention, the scalar decay and GLA
+    2d(C + 1) + 4d^2 (q.k^T and P.V over the lower triangle, S q and k^T v); the gated delta
+    rule 4Cd + 2d + 6d^2 + 2C^2/3 (K K^T strictly lower, Q K^T, T_U R and P U over the lower
+    triangle; K S^T, Q S^T and the carry K^T U; the triangular solve)."""
     th = B * H * T
     tok_bytes = 4 * d * elem_bytes
     gate_bytes = {"retention": 0, "mamba2": 4, "gla": 4 * d, "gdelta": 8}[kind]
     state_bytes = B * H * d * d * 4
     bytes_ = th * (tok_bytes + gate_bytes) + state_bytes
     if kind == "gdelta":
-        flops = th * (8 * chunk * d + 6 * d * d + 2 * chunk * chunk / 3)
+        flops = th * (4 * chunk * d + 2 * d + 6 * d * d + 2 * chunk * chunk / 3)
     else:
-        flops = th * (4 * chunk * d + 4 * d * d)
+        flops = th * (2 * d * (chunk + 1) + 4 * d * d)
     return flops, bytes_
+
+
+def full_block_flops(kind, B, H, T, d, chunk):
+    """The same products counted over the whole C x C block (the survey's count): 4Cd + 4d^2,
+    or 8Cd + 6d^2 + 2C^2/3 for the gated delta rule; reported beside the causal count."""
+    th = B * H * T
+    if kind == "gdelta":
+        return th * (8 * chunk * d + 6 * d * d + 2 * chunk * chunk / 3)
+    return th * (4 * chunk * d + 4 * d * d)
 
 
 def upload(w, torch, dev):
@@ -153,8 +179,9 @@ def time_calls(calls, steps, warmup, torch, graph=False):
     return region0.elapsed_time(region1) / steps, float(np.mean(per))
 
 
-def bench_chunk(name, steps, warmup, torch, api, synthetic, dev, n_sets=N_SETS):
+def bench_chunk(name, steps, warmup, torch, api, synthetic, dev, n_sets=None):
     c = synthetic.CONFIGS[name]
+    n_sets = N_SETS.get(name, 1) if n_sets is None else n_sets
     sets = []
     for s in range(n_sets):
         w = synthetic.config_inputs(name) if s == 0 else None
@@ -174,8 +201,30 @@ def bench_chunk(name, steps, warmup, torch, api, synthetic, dev, n_sets=N_SETS):
     tokens = c["B"] * c["H"] * c["T"]
     return dict(
         workload=name, ms_per_step=ms_wall, kernel_ms=ms_kernel, tokens_per_s=tokens / (ms_wall * 1e-3),
-        alg_gbytes=bytes_ / 1e9, alg_gflop=flops / 1e9,
+        input_sets_rotated=n_sets, alg_gbytes=bytes_ / 1e9, alg_gflop=flops / 1e9,
         hbm_gbs=bytes_ / (ms_kernel * 1e-3) / 1e9, mfma_tflops=flops / (ms_kernel * 1e-3) / 1e12)
+
+
+def roofline_block(name, r, synthetic):
+    """The call priced against HBM (the bound of every chunked workload: their intensities,
+    64 - 161 flop/byte, lie below the ridge of ~315) and against the dense bf16 MFMA peak."""
+    c = synthetic.CONFIGS[name]
+    flops, bytes_ = algorithmic_counts(c["kind"], c["B"], c["H"], c["T"], c["dk"], c["chunk"])
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ai = flops / bytes_
+    roof = {"bound": "hbm", "achieved": r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": r["hbm_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(name),
+            "kernel_ms": r["kernel_ms"], "alg_bytes_per_launch": bytes_,
+            "kernels": " + ".join(k.split("::")[-1] for k in WORKLOAD_KERNELS[name]) + " (one call)"}
+    mf = {"achieved": r["mfma_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+          "frac": r["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS, "alg_flop_per_launch": flops,
+          "flop_count": "causal tiles", "ceiling_frac": min(1.0, ai / ridge),
+          "frac_full_block_count": full_block_flops(c["kind"], c["B"], c["H"], c["T"], c["dk"], c["chunk"])
+          / (r["kernel_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    hw = measured_mfma(name)
+    if hw is not None:
+        mf["counters"] = dict(hw, hw_tflops=hw["mfma_flop_per_call"] / (r["kernel_ms"] * 1e-3) / 1e12)
+    return roof, mf
 
 
 def bench_decode(steps_total, torch, api, synthetic, dev):
@@ -388,42 +437,49 @@ def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
                 hbm_frac=bytes_ / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
-KERNEL_SOURCES = ("gated_linear_recurrences_amd/csrc/chunk_fused.hpp",
-                  "gated_linear_recurrences_amd/csrc/chunk_state.hpp",
-                  "gated_linear_recurrences_amd/csrc/chunk_output.hpp",
-                  "gated_linear_recurrences_amd/csrc/chunk_two_pass.hpp",
-                  "gated_linear_recurrences_amd/csrc/chunk_common.hpp",
-                  "gated_linear_recurrences_amd/csrc/chunk_bf16_retention_c64.hip",
-                  "gated_linear_recurrences_amd/csrc/device_common.hpp")
+CSRC = os.path.join(ROOT, "gated_linear_recurrences_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "pmc_mfma.json")
 
 
 def kernel_source_hash():
+    """SHA-256 over every kernel source of the library: recorded counters are reported only
+    while the sources they were measured on are unchanged."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hpp", ".hip", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the timed kernel from the committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or None when the
-    kernel sources have changed since the counters were taken."""
+def _recorded(path, name):
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash() or rec.get("workload") != MAIN:
+    if rec.get("source_sha256") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("workloads", {}).get(name)
+
+
+def measured_traffic(name=MAIN):
+    """HBM bytes per call of a chunked workload from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE of its kernels, scaled by a plain copy of known size), or None
+    when the kernel sources have changed since the counters were taken."""
+    rec = _recorded(TRAFFIC_FILE, name)
+    return None if rec is None else rec["hbm_bytes_per_call"]
+
+
+def measured_mfma(name=MAIN):
+    """MFMA counters per call of a chunked workload (rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE of its kernels), or None when stale."""
+    return _recorded(MFMA_FILE, name)
 
 
 COPY_CAL_MB = 512   # size of the plain copy the counter runs are scaled by
-# kernel of one retention call (bf16, chunk 64, d_k = d_v = 128, 16-channel value slices,
-# fixed gate), as rocprofv3 names it
-TRAFFIC_KERNELS = ("glr::ck::fused_kernel<64, 128, 128, 1, 0>",)
 
 
 def _counter_rows(d):
@@ -438,52 +494,103 @@ def _counter_rows(d):
     return rows
 
 
-def _per_dispatch(rows, match):
+def _per_dispatch(rows, match, counter=None):
     """{dispatch id: summed counter value} over the dispatches whose kernel name matches."""
     out = {}
     for r in rows:
-        if match(r["Kernel_Name"]):
+        if match(r["Kernel_Name"]) and (counter is None or r["Counter_Name"] == counter):
             key = r.get("Dispatch_Id") or r.get("Correlation_Id")
             out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
     return out
 
 
+def _kernel_match(kernel):
+    # rocprofv3 names carry "void " and the argument list: match the name up to its arguments
+    return lambda k: k.replace("void ", "").split("(")[0].strip() == kernel
+
+
 def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
-    """HBM bytes per retention call from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch),
-    each scaled by what the same counter reads for a plain copy of known size; writes
-    profiles/pmc_traffic.json and prints the table of the profile summary."""
+    """HBM bytes per call of every chunked workload from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch) of ``bench.py --counter-run``, each scaled by what the same counter reads for a
+    plain copy of known size; writes profiles/pmc_traffic.json and prints the table of the
+    profile summary."""
     is_copy = lambda k: "copy" in k.lower()
-    res = {}
-    for label, d, cd in (("fetch", fetch_dir, copy_fetch_dir), ("write", write_dir, copy_write_dir)):
-        rows = _counter_rows(d)
-        per_kernel = {}
-        for t in TRAFFIC_KERNELS:
-            disp = _per_dispatch(rows, lambda k, t=t: t in k)
-            per_kernel[t] = (sum(disp.values()) / len(disp), len(disp))
-        copy = _per_dispatch(_counter_rows(cd), is_copy)
-        copy_kib = max(copy.values())     # the 512 MB copy, not small incidental copies
-        res[label] = (per_kernel, copy_kib)
     copy_bytes = int(COPY_CAL_MB * 1e6) // 4 * 4   # the copy of --copy-calibration COPY_CAL_MB
-    rec = {"workload": MAIN, "kernels": list(TRAFFIC_KERNELS), "source_sha256": kernel_source_hash(),
-           "copy_calibration_bytes": copy_bytes}
-    total = 0.0
-    lines = ["| quantity | raw counter (KiB / dispatch) | scale | bytes / call |", "|---|---|---|---|"]
-    for label in ("fetch", "write"):
-        per_kernel, copy_kib = res[label]
-        scale = copy_bytes / 1024.0 / copy_kib
-        lines.append(f"| plain copy of {copy_bytes:,} B, {label.upper()}_SIZE | {copy_kib:.0f} | "
-                     f"{copy_bytes / 1024:.0f} / raw = {scale:.4f} | {copy_bytes:,} |")
-        part = 0.0
-        for t, (kib, n) in per_kernel.items():
-            b = kib * 1024.0 * scale
-            part += b
-            lines.append(f"| `{t}...` {label.upper()}_SIZE ({n} dispatches) | {kib:.0f} | {scale:.4f} | {b:,.0f} |")
-        rec[f"{label}_scale"] = scale
-        rec[f"{label}_bytes_per_call"] = part
-        total += part
-    rec["hbm_bytes_per_launch"] = total
-    lines.append(f"| **total HBM traffic per call** | | | **{total:,.0f}** |")
+    scale = {}
+    rows = {}
+    for label, d, cd in (("fetch", fetch_dir, copy_fetch_dir), ("write", write_dir, copy_write_dir)):
+        rows[label] = _counter_rows(d)
+        copy_kib = max(_per_dispatch(_counter_rows(cd), is_copy).values())   # the 512 MB copy
+        scale[label] = copy_bytes / 1024.0 / copy_kib
+    rec = {"source_sha256": kernel_source_hash(), "copy_calibration_bytes": copy_bytes,
+           "fetch_scale": scale["fetch"], "write_scale": scale["write"], "workloads": {}}
+    lines = [f"FETCH_SIZE scale {scale['fetch']:.4f}, WRITE_SIZE scale {scale['write']:.4f} "
+             f"(plain copy of {copy_bytes:,} B: raw KiB x scale = bytes / 1024)", "",
+             "| workload | kernel | dispatches | read bytes / dispatch | written bytes / dispatch |",
+             "|---|---|---|---|---|"]
+    for name, kernels in WORKLOAD_KERNELS.items():
+        w = {"kernels": list(kernels), "fetch_bytes_per_call": 0.0, "write_bytes_per_call": 0.0}
+        ok = True
+        for kern in kernels:
+            per = {}
+            for label in ("fetch", "write"):
+                disp = _per_dispatch(rows[label], _kernel_match(kern))
+                if not disp:
+                    ok = False
+                    break
+                per[label] = (sum(disp.values()) / len(disp) * 1024.0 * scale[label], len(disp))
+                w[f"{label}_bytes_per_call"] += per[label][0]
+            if not ok:
+                break
+            lines.append(f"| {name} | `{kern.split('::')[-1]}` | {per['fetch'][1]} | {per['fetch'][0]:,.0f} | "
+                         f"{per['write'][0]:,.0f} |")
+        if ok:
+            w["hbm_bytes_per_call"] = w["fetch_bytes_per_call"] + w["write_bytes_per_call"]
+            rec["workloads"][name] = w
+            lines.append(f"| **{name}** | **total per call** | | **{w['fetch_bytes_per_call']:,.0f}** | "
+                         f"**{w['write_bytes_per_call']:,.0f}** |")
     with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def summarize_mfma(mfma_dir):
+    """MFMA counters per call of every chunked workload from one rocprofv3 --pmc run of
+    ``bench.py --counter-run`` (SQ_INSTS_VALU_MFMA_MOPS_BF16: bf16 MFMA work in units of 512
+    flops; SQ_VALU_MFMA_BUSY_CYCLES: cycles the MFMA units were busy, summed over the chip;
+    GRBM_GUI_ACTIVE: cycles the GPU was busy). Busy fraction = MFMA busy cycles / (GPU busy
+    cycles x 256 CUs x 4 SIMDs). Writes profiles/pmc_mfma.json and prints a table."""
+    rows = _counter_rows(mfma_dir)
+    rec = {"source_sha256": kernel_source_hash(), "counters": list(MFMA_COUNTERS), "workloads": {}}
+    lines = ["| workload | kernel | dispatches | MFMA bf16 flop / dispatch | MFMA busy cycles | GPU busy cycles | "
+             "MFMA busy fraction |", "|---|---|---|---|---|---|---|"]
+    for name, kernels in WORKLOAD_KERNELS.items():
+        tot = {"mops": 0.0, "busy": 0.0, "gui": 0.0}
+        ok = True
+        for kern in kernels:
+            vals = {}
+            for key, counter in (("mops", MFMA_COUNTERS[0]), ("busy", MFMA_COUNTERS[1]), ("gui", MFMA_COUNTERS[2])):
+                disp = _per_dispatch(rows, _kernel_match(kern), counter)
+                if not disp:
+                    ok = False
+                    break
+                vals[key] = sum(disp.values()) / len(disp)
+                n = len(disp)
+            if not ok:
+                break
+            for key in tot:
+                tot[key] += vals[key]
+            frac = vals["busy"] / (vals["gui"] * N_CU * 4) if vals["gui"] else float("nan")
+            lines.append(f"| {name} | `{kern.split('::')[-1]}` | {n} | {vals['mops'] * 512:,.0f} | {vals['busy']:,.0f} | "
+                         f"{vals['gui']:,.0f} | {frac:.3f} |")
+        if ok:
+            rec["workloads"][name] = {"kernels": list(kernels), "mfma_flop_per_call": tot["mops"] * 512,
+                                      "mfma_busy_cycles_per_call": tot["busy"], "gpu_busy_cycles_per_call": tot["gui"],
+                                      "mfma_busy_frac": tot["busy"] / (tot["gui"] * N_CU * 4) if tot["gui"] else None}
+    with open(MFMA_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     print("\n".join(lines))
 
@@ -553,37 +660,83 @@ def copy_calibration(mbytes, steps, torch):
     print(json.dumps({"copy_calibration_bytes": n * 4, "steps": steps}))
 
 
-def cpu_baseline(synthetic, budget_s=12.0):
-    """The fp64 oracle (chunkwise form) on the host: whole retention batches of the timed
-    workload, repeated until ``budget_s`` has elapsed. numpy's einsum runs on one thread."""
+def _oracle_heads(args):
+    """One worker of the CPU baseline: the oracle's chunkwise gated delta rule on a block of
+    (batch, head) sequences. Runs in a fresh process with one BLAS thread."""
+    q, k, v, la, beta, chunk = args
     import oracle
-    w = synthetic.config_inputs(MAIN)
-    c = synthetic.CONFIGS[MAIN]
     t0 = time.perf_counter()
-    done = 0
-    while True:
-        for b in range(c["B"]):
-            oracle.retention_chunkwise(w.q[b:b + 1], w.k[b:b + 1], w.v[b:b + 1], w.log_gamma, c["chunk"])
-            done += c["H"] * c["T"]
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 chunkwise retention oracle on {done // (c['H'] * c['T'])} batch rows of "
-                      f"{MAIN} (H={c['H']}, T={c['T']}, d=128) in {el:.1f} s"}
+    oracle.gdelta_chunkwise(q, k, v, la, beta, chunk)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(synthetic, cores=None, heads_per_task=1):
+    """The fp64 oracle (chunkwise form, as written) on the host's cores: the sequences of the
+    timed workload split over ``cores`` worker processes (one BLAS thread each), one sequence
+    per task; tokens per second of wall time over the sample."""
+    import concurrent.futures
+    import multiprocessing as mp
+    c = synthetic.CONFIGS[MAIN]
+    # the GPU box gives one GPU's job 16 host cores, whatever os.cpu_count() shows
+    cores = cores or max(1, min(16, os.cpu_count() or 1))
+    w = synthetic.config_inputs(MAIN)
+    B, H, T = c["B"], c["H"], c["T"]
+    n_seq = min(B * H, 2 * cores)   # a bounded sample: two sequences per core
+    tasks = []
+    for i in range(0, n_seq, heads_per_task):
+        sl = [(j // H, j % H) for j in range(i, min(i + heads_per_task, n_seq))]
+        b = np.array([x[0] for x in sl]); h = np.array([x[1] for x in sl])
+        tasks.append((w.q[b, h][None], w.k[b, h][None], w.v[b, h][None], w.log_alpha[b, h][None], w.beta[b, h][None],
+                      c["chunk"]))
+    del w
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in env:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        with concurrent.futures.ProcessPoolExecutor(cores, mp_context=ctx) as ex:
+            list(ex.map(_oracle_heads, tasks[:cores]))   # start the workers (imports) before timing
+            t0 = time.perf_counter()
+            list(ex.map(_oracle_heads, tasks))
+            el = time.perf_counter() - t0
+    finally:
+        for k, v in env.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    tokens = n_seq * T
+    return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 chunkwise gated-delta oracle on {n_seq} of the {B * H} sequences of {MAIN} "
+                      f"(T={T}, d=128, chunk {c['chunk']}), {cores} worker processes with one BLAS thread each, "
+                      f"{el:.1f} s wall"}
+
+
+def counter_run(torch, api, synthetic, dev, calls=3):
+    """Each chunked workload, ``calls`` eager calls and nothing else: the run rocprofv3 --pmc
+    takes its per-kernel counters from."""
+    for name in CHUNKED:
+        c = synthetic.CONFIGS[name]
+        call = make_call(c["kind"], api, upload(synthetic.config_inputs(name), torch, dev), c["chunk"], torch)
+        for _ in range(calls):
+            call()
+        torch.cuda.synchronize()
+        del call
+        torch.cuda.empty_cache()
+    print(json.dumps({"counter_run": list(CHUNKED), "calls": calls}))
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-others", action="store_true",
-                    help="skip the GLA, gated-delta, scalar-decay and decode workloads")
+                    help="only the headline workload (no other chunked workloads, decode, backward or VLA)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--counter-run", action="store_true",
+                    help="only run each chunked workload three times (for rocprofv3 --pmc)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes --steps times (counter scaling)")
     ap.add_argument("--kernel-traffic", nargs=4, metavar="DIR",
@@ -591,14 +744,19 @@ def main():
     ap.add_argument("--trace-table", metavar="DIR",
                     help="print per-kernel durations from a rocprofv3 --kernel-trace output folder")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR",
-                    help="FETCH_SIZE and WRITE_SIZE counter dirs of a bench run, then of a copy run: "
+                    help="FETCH_SIZE and WRITE_SIZE counter dirs of a --counter-run, then of a copy run: "
                          "write profiles/pmc_traffic.json")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="MFMA counter dir of a --counter-run: write profiles/pmc_mfma.json")
     args = ap.parse_args()
     if args.trace_table:
         trace_table(args.trace_table)
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.kernel_traffic:
         kernel_traffic(*args.kernel_traffic)
@@ -615,16 +773,20 @@ def main():
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration, args.steps, torch)
         return
+    if args.counter_run:
+        counter_run(torch, api, synthetic, dev)
+        return
 
     main_r = bench_chunk(MAIN, args.steps, args.warmup, torch, api, synthetic, dev)
+    print(f"[bench] {MAIN}: {main_r['kernel_ms'] * 1e3:.1f} us per call", file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
     others = {}
     if not args.no_others:
-        for name in ("gla_b8h16_t4096_d128", "gdelta_b4h16_t8192_d128", "mamba2_b8h16_t4096_d128"):
-            r = bench_chunk(name, max(20, args.steps // 4), max(3, args.warmup // 4), torch, api, synthetic, dev,
-                            n_sets=1)
-            r["hbm_frac"] = r["hbm_gbs"] / HBM_PEAK_GBS
-            r["mfma_frac"] = r["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS
+        for name in CHUNKED[1:]:
+            r = bench_chunk(name, max(20, args.steps // 2), max(3, args.warmup // 2), torch, api, synthetic, dev)
+            r["roofline"], r["mfma"] = roofline_block(name, r, synthetic)
             others[name] = r
+            print(f"[bench] {name}: {r['kernel_ms'] * 1e3:.1f} us per call", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
         others["decode_n512h32_d128"] = bench_decode(args.decode_steps, torch, api, synthetic, dev)
         torch.cuda.empty_cache()
@@ -635,16 +797,18 @@ def main():
         others["gdelta_decode_n512h32_d128"] = bench_gdelta_decode(min(args.decode_steps, 200), torch, api,
                                                                    synthetic, dev)
         torch.cuda.empty_cache()
-        for name in (MAIN, "mamba2_b8h16_t4096_d128", "gla_b8h16_t4096_d128"):
+        for name in ("retention_b4h8_t2048_d128", "mamba2_b8h16_t4096_d128", "gla_b8h16_t4096_d128"):
             others[name + "_bwd"] = bench_backward(name, max(20, args.steps // 4), max(3, args.warmup // 4), torch,
                                                    api, synthetic, dev)
             torch.cuda.empty_cache()
-        others["vla_b8h16_t4096_d128"] = bench_vla(max(5, args.steps // 40), 1, torch, api, synthetic, dev)
+        others["vla_b8h16_t4096_d128"] = bench_vla(max(5, args.steps // 20), 1, torch, api, synthetic, dev)
         torch.cuda.empty_cache()
         others["vla_decode_n512h32_d128"] = bench_vla_decode(min(args.decode_steps, 50), torch, api, synthetic, dev)
         torch.cuda.empty_cache()
+        print("[bench] other workloads done", file=sys.stderr, flush=True)
 
     cfg = synthetic.CONFIGS[MAIN]
+    roof, mf = roofline_block(MAIN, main_r, synthetic)
     out = {
         "metric": "chunked fwd tokens/s (B·H·T/s) + % bf16 MFMA peak; decode step HBM GB/s",
         "value": main_r["tokens_per_s"],
@@ -659,15 +823,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": MAIN, "B": cfg["B"], "H": cfg["H"], "T": cfg["T"], "d_k": cfg["dk"],
-                   "d_v": cfg["dv"], "chunk": cfg["chunk"], "decay": "1 - 2^(-5-h)", "state": "fp32",
-                   "input_sets_rotated": N_SETS},
-        "roofline": {"bound": "hbm", "achieved": main_r["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": main_r["hbm_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel_ms": main_r["kernel_ms"], "alg_bytes_per_launch": main_r["alg_gbytes"] * 1e9,
-                     "kernels": "single-pass forward (one call)"},
-        "mfma": {"achieved": main_r["mfma_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": main_r["mfma_tflops"] / MFMA_BF16_PEAK_TFLOPS,
-                 "alg_flop_per_launch": main_r["alg_gflop"] * 1e9},
+                   "d_v": cfg["dv"], "chunk": cfg["chunk"], "keys": "L2(SiLU(N(0,1)))",
+                   "gates": "log alpha = -softplus(N(0,1))/8, beta = sigmoid(N(0,1))", "state": "fp32",
+                   "input_sets_rotated": main_r["input_sets_rotated"]},
+        "roofline": roof,
+        "mfma": mf,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(synthetic)

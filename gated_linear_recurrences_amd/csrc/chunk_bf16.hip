@@ -1,5 +1,5 @@
 // Dispatch of the bf16 MFMA chunk kernels by gate variant and chunk length.
-#include "chunk_delta.hpp"
+#include "chunk_delta_sp.hpp"
 #include "launch.hpp"
 
 namespace glr {
@@ -21,6 +21,8 @@ size_t chunk_workspace_bytes(Variant variant, const ChunkArgs& a, bool bf16) {
     if (!bf16 || a.B == 0 || a.H == 0) return 0;
     const size_t chunks = static_cast<size_t>((a.T + a.chunk - 1) / a.chunk);
     if (single_pass_forward(variant, a)) return 0;
+    if (variant == kGDelta && delta_single_pass(a))
+        return ck::dsp_ws_bytes(static_cast<int64_t>(a.B) * a.H * chunks, a.chunk, a.dk, (a.fuse & 1) != 0);
     if (variant == kGDelta)
         return ck::delta_ws_bytes(static_cast<int64_t>(a.B) * a.H * chunks, a.chunk, a.dk, a.dv, (a.fuse & 1) != 0);
     return static_cast<size_t>(a.B) * a.H * chunks * a.dv * a.dk * 2;

@@ -87,6 +87,11 @@ inline bool single_pass_forward(Variant variant, const ChunkArgs& a) {
            static_cast<long long>(a.B) * a.H * (a.dv / 16) >= 128;
 }
 
+// The gated delta rule (bf16 storage) at chunk 64 with d_k >= 32 takes the prep + single-pass
+// form (T_U and the gates per chunk in the workspace, the mapped q and k too when the feature
+// map is fused in); chunks of 16 and 32 and d_k = 16 take the three-kernel form.
+inline bool delta_single_pass(const ChunkArgs& a) { return a.chunk == 64 && a.dk >= 32; }
+
 // float32 storage, fp32 arithmetic (VALU).
 hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t stream);
 // Device workspace the chunk kernels of (variant, shape, storage) need, in bytes.

@@ -101,14 +101,18 @@ typedef enum la_variant {
  * data-dependent decay run in a single pass with no workspace when
  * B * H * (d_v / 16) >= 128 (the memory stays on chip); below that, and for
  * GLA always, the memory entering every chunk goes from a state pass to an
- * output pass: B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.  The gated delta rule in bf16
- * also passes, per (sequence, chunk), its WY factor W (chunk x d_k bf16), the
- * pseudo-values (d_v x chunk float32) and the cumulative log-gates (chunk
- * float32): with N = B * H * ceil(T / chunk) and a(x) = x rounded up to a
- * multiple of 256, a(N*chunk*d_k*2) + a(N*d_v*chunk*4) + a(N*chunk*4) +
- * a(N*d_v*d_k*2) bytes; gdelta_chunk_fwd_fused with LA_FUSE_QK_SILU_L2
- * (query with LA_GDELTA_FUSED) keeps the mapped keys there too, another
- * a(N*chunk*d_k*2).  fp32 storage needs none.
+ * output pass: B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.  For the gated
+ * delta rule in bf16, with N = B * H * ceil(T / chunk) and a(x) = x rounded up
+ * to a multiple of 256: at chunk 64 with d_k >= 32, the factor T_U of every
+ * chunk (chunk x chunk bf16) and its cumulative log-gates (chunk float32),
+ * a(N*chunk*chunk*2) + a(N*chunk*4) bytes, plus the mapped keys and queries,
+ * 2 a(N*chunk*d_k*2), for gdelta_chunk_fwd_fused with LA_FUSE_QK_SILU_L2
+ * (query with LA_GDELTA_FUSED); at chunks 16 and 32 or d_k = 16, the WY factor
+ * W (chunk x d_k bf16), the pseudo-values (d_v x chunk float32), the
+ * cumulative log-gates and the memory entering the chunk (d_v x d_k bf16),
+ * a(N*chunk*d_k*2) + a(N*d_v*chunk*4) + a(N*chunk*4) + a(N*d_v*d_k*2) bytes,
+ * plus the mapped keys a(N*chunk*d_k*2) with LA_GDELTA_FUSED.  fp32 storage
+ * needs none.
  */
 la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int dk, int dv,
                                   int chunk, la_dtype dtype, size_t* bytes);

@@ -87,19 +87,25 @@ def test_workspace_size_query(lib):
         assert _ws(lib, variant, T=0) == (_native.LA_OK, 0)
         assert _ws(lib, variant, B=0) == (_native.LA_OK, 0)
         assert _ws(lib, variant, dtype=0) == (_native.LA_OK, 0)      # fp32 storage: one fused kernel
-    # gated delta rule in bf16: W, pseudo-values, cumulative gates and the memory per chunk,
-    # each array rounded up to 256 bytes
+    # gated delta rule in bf16, each array rounded up to 256 bytes. Chunk 64 with d_k >= 32:
+    # T_U (chunk x chunk bf16) and the cumulative gates per chunk (the mapped q and k as well
+    # with the fused feature map); otherwise W, pseudo-values, cumulative gates and the memory
     def a256(x):
         return (x + 255) // 256 * 256
 
-    for (B, H, T, dk, dv, C) in ((4, 16, 8192, 128, 128, 64), (1, 2, 65, 32, 64, 32), (1, 1, 40, 16, 16, 16)):
+    for (B, H, T, dk, dv) in ((4, 16, 8192, 128, 128), (1, 3, 100, 32, 64), (2, 1, 64, 64, 16)):
+        n = B * H * ((T + 63) // 64)
+        want = a256(n * 64 * 64 * 2) + a256(n * 64 * 4)
+        assert _ws(lib, _native.LA_GDELTA, B=B, H=H, T=T, dk=dk, dv=dv, chunk=64) == (_native.LA_OK, want)
+        want += 2 * a256(n * 64 * dk * 2)
+        assert _ws(lib, _native.LA_GDELTA_FUSED, B=B, H=H, T=T, dk=dk, dv=dv, chunk=64) == (_native.LA_OK, want)
+    for (B, H, T, dk, dv, C) in ((1, 2, 65, 32, 64, 32), (1, 1, 40, 16, 16, 16), (2, 2, 100, 16, 64, 64)):
         n = B * H * ((T + C - 1) // C)
         want = a256(n * C * dk * 2) + a256(n * dv * C * 4) + a256(n * C * 4) + a256(n * dv * dk * 2)
         assert _ws(lib, _native.LA_GDELTA, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C) == (_native.LA_OK, want)
-    # with the fused feature map the mapped keys are kept too
-    n = 4 * 16 * 128
-    want = a256(n * 64 * 128 * 2) * 2 + a256(n * 128 * 64 * 4) + a256(n * 64 * 4) + a256(n * 128 * 128 * 2)
-    assert _ws(lib, _native.LA_GDELTA_FUSED, B=4, H=16, T=8192, dk=128, dv=128, chunk=64) == (_native.LA_OK, want)
+        # with the fused feature map the mapped keys are kept too
+        want += a256(n * C * dk * 2)
+        assert _ws(lib, _native.LA_GDELTA_FUSED, B=B, H=H, T=T, dk=dk, dv=dv, chunk=C) == (_native.LA_OK, want)
     assert _ws(lib, _native.LA_GDELTA, T=0) == (_native.LA_OK, 0)
     assert _ws(lib, _native.LA_GDELTA, dtype=0) == (_native.LA_OK, 0)
     assert _ws(lib, 7)[0] == _native.LA_ERR_INVALID

@@ -18,11 +18,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_algorithmic_counts_retention_workload():
     # B4 H8 T2048 d128, chunk 64, bf16: q, k, v read and o written (4 d bf16 per token-head),
-    # the final fp32 memory written (d^2 per head); flops 4Cd + 4d^2 per token-head
+    # the final fp32 memory written (d^2 per head); flops over the causal tiles 2d(C + 1) + 4d^2
+    # per token-head (the whole-block count 4Cd + 4d^2 beside it)
     flops, bytes_ = bench.algorithmic_counts("retention", 4, 8, 2048, 128, 64)
     th = 4 * 8 * 2048
     assert bytes_ == th * 4 * 128 * 2 + 32 * 128 * 128 * 4 == 69_206_016
-    assert flops == th * (4 * 64 * 128 + 4 * 128 * 128) == 6_442_450_944
+    assert flops == th * (2 * 128 * 65 + 4 * 128 * 128) == 5_385_486_336
+    assert bench.full_block_flops("retention", 4, 8, 2048, 128, 64) == th * (4 * 64 * 128 + 4 * 128 * 128)
 
 
 def test_algorithmic_counts_gates():
@@ -32,8 +34,12 @@ def test_algorithmic_counts_gates():
     assert bench.algorithmic_counts("mamba2", 2, 3, 100, 64, 32)[1] == base + th * 4        # one gate per token
     assert bench.algorithmic_counts("gla", 2, 3, 100, 64, 32)[1] == base + th * 4 * 64      # one per key channel
     assert bench.algorithmic_counts("gdelta", 2, 3, 100, 64, 32)[1] == base + th * 8        # gate and beta
+    # gated delta rule, causal tiles: K K^T strictly lower (C - 1)d, Q K^T, T_U R and P U over the
+    # lower triangle 3(C + 1)d, three d x d products 6d^2, the solve 2C^2/3
     flops = bench.algorithmic_counts("gdelta", 2, 3, 100, 64, 32)[0]
-    assert flops == pytest.approx(th * (8 * 32 * 64 + 6 * 64 * 64 + 2 * 32 * 32 / 3))
+    assert flops == pytest.approx(th * (31 * 64 + 3 * 33 * 64 + 6 * 64 * 64 + 2 * 32 * 32 / 3))
+    assert bench.full_block_flops("gdelta", 2, 3, 100, 64, 32) == pytest.approx(
+        th * (8 * 32 * 64 + 6 * 64 * 64 + 2 * 32 * 32 / 3))
 
 
 def _counter_csv(path, rows):
@@ -46,12 +52,16 @@ def _counter_csv(path, rows):
 
 
 def test_traffic_summary_scales_by_the_copy(tmp_path, monkeypatch, capsys):
-    """FETCH_SIZE and WRITE_SIZE per dispatch (KiB), averaged over dispatches and scaled by what
-    the same counter reads for the 512 MB copy (FETCH_SIZE counts half of the copy's bytes)."""
-    kern = bench.TRAFFIC_KERNELS[0] + "(glr::ck::FusedParams)"
+    """FETCH_SIZE and WRITE_SIZE per dispatch (KiB), averaged over dispatches, scaled by what
+    the same counter reads for the 512 MB copy (FETCH_SIZE counts half of the copy's bytes),
+    summed over a workload's kernels."""
+    k1, k2 = bench.WORKLOAD_KERNELS[bench.MAIN]
     copy_kib = bench.COPY_CAL_MB * 1e6 / 1024
-    _counter_csv(tmp_path / "f", [("void " + kern, "FETCH_SIZE", 1000.0), ("void " + kern, "FETCH_SIZE", 3000.0)])
-    _counter_csv(tmp_path / "w", [("void " + kern, "WRITE_SIZE", 500.0)])
+    _counter_csv(tmp_path / "f", [("void " + k1 + "(glr::ck::DspParams)", "FETCH_SIZE", 1000.0),
+                                  ("void " + k1 + "(glr::ck::DspParams)", "FETCH_SIZE", 3000.0),
+                                  ("void " + k2 + "(glr::ck::DspParams)", "FETCH_SIZE", 100.0)])
+    _counter_csv(tmp_path / "w", [("void " + k1 + "(glr::ck::DspParams)", "WRITE_SIZE", 500.0),
+                                  ("void " + k2 + "(glr::ck::DspParams)", "WRITE_SIZE", 50.0)])
     _counter_csv(tmp_path / "cf", [("copy_kernel", "FETCH_SIZE", copy_kib / 2), ("copy_kernel", "FETCH_SIZE", 1.0)])
     _counter_csv(tmp_path / "cw", [("copy_kernel", "WRITE_SIZE", copy_kib)])
     out = tmp_path / "traffic.json"
@@ -60,25 +70,48 @@ def test_traffic_summary_scales_by_the_copy(tmp_path, monkeypatch, capsys):
     rec = json.loads(out.read_text())
     assert rec["fetch_scale"] == pytest.approx(2.0)
     assert rec["write_scale"] == pytest.approx(1.0)
-    assert rec["fetch_bytes_per_call"] == pytest.approx(2000.0 * 1024 * 2.0)
-    assert rec["write_bytes_per_call"] == pytest.approx(500.0 * 1024)
-    assert rec["hbm_bytes_per_launch"] == pytest.approx(2000.0 * 2048 + 500.0 * 1024)
+    w = rec["workloads"][bench.MAIN]
+    assert w["fetch_bytes_per_call"] == pytest.approx((2000.0 + 100.0) * 1024 * 2.0)
+    assert w["write_bytes_per_call"] == pytest.approx(550.0 * 1024)
+    assert w["hbm_bytes_per_call"] == pytest.approx(2100.0 * 2048 + 550.0 * 1024)
+    assert "retention_b4h8_t2048_d128" not in rec["workloads"]   # its kernels did not run
     assert rec["source_sha256"] == bench.kernel_source_hash()
-    assert "total HBM traffic per call" in capsys.readouterr().out
+    assert "total per call" in capsys.readouterr().out
 
 
-def test_recorded_traffic_only_for_the_kernel_it_was_measured_on(tmp_path, monkeypatch):
+def test_mfma_summary(tmp_path, monkeypatch, capsys):
+    """MFMA counters per call: MOPS in units of 512 flops, the busy fraction over the chip's
+    256 x 4 SIMDs, summed over a workload's kernels."""
+    k1, k2 = bench.WORKLOAD_KERNELS[bench.MAIN]
+    rows = []
+    for k, mops, busy, gui in ((k1, 10.0, 2048.0, 10.0), (k2, 30.0, 6144.0, 10.0)):
+        rows += [(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops), (k, "SQ_VALU_MFMA_BUSY_CYCLES", busy),
+                 (k, "GRBM_GUI_ACTIVE", gui)]
+    path = tmp_path / "m"
+    os.makedirs(path)
+    with open(path / "run_counter_collection.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for i, (name, counter, value) in enumerate(rows):
+            wr.writerow({"Dispatch_Id": i // 3, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+    out = tmp_path / "mfma.json"
+    monkeypatch.setattr(bench, "MFMA_FILE", str(out))
+    bench.summarize_mfma(str(path))
+    w = json.loads(out.read_text())["workloads"][bench.MAIN]
+    assert w["mfma_flop_per_call"] == pytest.approx(40.0 * 512)
+    assert w["mfma_busy_frac"] == pytest.approx(8192.0 / (20.0 * 1024))
+    assert bench.measured_mfma("no_such_workload") is None
+
+
+def test_recorded_counters_only_for_the_sources_they_were_measured_on(tmp_path, monkeypatch):
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
     assert bench.measured_traffic() is None   # nothing recorded
-    rec = {"workload": bench.MAIN, "source_sha256": bench.kernel_source_hash(), "hbm_bytes_per_launch": 123.0}
+    rec = {"source_sha256": bench.kernel_source_hash(), "workloads": {bench.MAIN: {"hbm_bytes_per_call": 123.0}}}
     out.write_text(json.dumps(rec))
     assert bench.measured_traffic() == 123.0
+    assert bench.measured_traffic("gla_b8h16_t4096_d128") is None
     rec["source_sha256"] = "0" * 64   # the kernel sources changed since
-    out.write_text(json.dumps(rec))
-    assert bench.measured_traffic() is None
-    rec["source_sha256"] = bench.kernel_source_hash()
-    rec["workload"] = "another_workload"
     out.write_text(json.dumps(rec))
     assert bench.measured_traffic() is None
 
