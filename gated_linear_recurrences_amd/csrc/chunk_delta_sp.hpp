@@ -272,29 +272,27 @@ void delta_tfac_kernel(DspParams p) {
 // ====================================================================== single pass
 template <int C, int DK, int VS>
 struct DspLayout {
-    using TK = SwzTile<DK>;     // K, and the hand-off rows of S_in
-    using TV = SwzTile<VS>;     // the v slice, and the outputs waiting to be stored
-    using TU = SwzTile<C>;      // the hand-off rows of U^T
+    using TK = SwzTile<DK>;     // K and Q rows
+    using TV = SwzTile<VS>;     // the v slice
     static constexpr int NV = VS / 16;
-    static constexpr int TUS = C + 8;   // T_U rows 144 bytes apart: 8-byte row reads of 32 lanes on 64 banks
+    static constexpr int RS = C + 8;    // T_U and P rows 144 bytes apart: 8-byte row reads of 32 lanes on 64 banks
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
     // gate tables of one chunk (floats): G, e^G, e^-G, carry weights e^(G_last - G), then
     // e^(G_last) and G_last
     static constexpr int GG = 0, GEG = C, GENG = 2 * C, GW = 3 * C, GEL = 4 * C, GL = 4 * C + 1;
     static constexpr int KBUF = al(C * TK::STRIDE * 2);
     static constexpr int VBUF = al(C * TV::STRIDE * 2);
-    static constexpr int TBUF = al(C * TUS * 2);
+    static constexpr int RBUF = al(C * RS * 2);
     static constexpr int GBUF = al((4 * C + 4) * 4);
-    static constexpr int HS = al(16 * TK::STRIDE * 2), HU = al(16 * TU::STRIDE * 2);
-    static constexpr int HBUF = NV * (HS + 2 * HU);
-    static constexpr int OBUF = VBUF;
+    // K, Q and the gates of a chunk live three steps (staged, its triangle, its chain), the
+    // v slice, T_U and the triangle P two
     static constexpr int oK = 0;
-    static constexpr int oV = oK + 3 * KBUF;
+    static constexpr int oQ = oK + 3 * KBUF;
+    static constexpr int oG = oQ + 3 * KBUF;
+    static constexpr int oV = oG + 3 * GBUF;
     static constexpr int oT = oV + 2 * VBUF;
-    static constexpr int oG = oT + 2 * TBUF;
-    static constexpr int oH = oG + 3 * GBUF;
-    static constexpr int oO = oH + 2 * HBUF;
-    static constexpr int bytes = oO + 2 * OBUF;
+    static constexpr int oP = oT + 2 * RBUF;
+    static constexpr int bytes = oP + 2 * RBUF;
     static_assert(bytes <= 160 * 1024, "LDS budget of the delta single pass exceeded");
 };
 
@@ -304,36 +302,27 @@ void delta_sp_kernel(DspParams p) {
     using Lay = DspLayout<C, DK, VS>;
     using TK = typename Lay::TK;
     using TV = typename Lay::TV;
-    using TU = typename Lay::TU;
-    constexpr int NT = 256;
     constexpr int NV = Lay::NV;
     constexpr int CT = C / 16, JB = CT / 2;     // token tiles, 32-token blocks
     constexpr int KT = DK / 16, KB = DK / 32;   // key tiles, 32-key blocks
-    constexpr int TUS = Lay::TUS;
-    static_assert(C == 64, "the output waves split four token tiles two by two");
+    constexpr int RS = Lay::RS;
+    constexpr int NH = 128;                     // helper threads (waves 2 and 3)
+    static_assert(C == 64, "the helpers split four token tiles two by two");
     static_assert(DK >= 32 && DK % 32 == 0, "d_k in 32-key blocks");
     static_assert(DV % VS == 0 && (VS == 16 || VS == 32), "value slices of 16 or 32 channels");
-    // staged pieces (16 bytes) of one chunk; ring index i holds one kind for every lane:
-    // k (RK indices), the v slice (RV), T_U (RT), G (one index, 16 lanes: four floats each)
-    constexpr int PK = C * DK / 8, PV = C * VS / 8, PT = C * C / 8, PG = C / 4;
-    static_assert(PK % NT == 0 && PT % NT == 0 && PV <= NT && PG <= NT, "pieces per ring index");
-    constexpr int RK = PK / NT, RV = 1, RT = PT / NT;
-    constexpr int PER = RK + RV + RT + 1;
-    constexpr int PO = C * VS / 8;   // 16-byte pieces of one chunk's outputs
+    // 16-byte pieces of one chunk staged by the helpers: k, q (PKQ each), the v slice (PV),
+    // T_U (PT); then one float of G per lane of each helper wave
+    constexpr int PKQ = C * DK / 8, PV = C * VS / 8, PT = C * C / 8;
+    static_assert(PKQ % NH == 0 && PT % NH == 0 && PV <= 2 * NH, "pieces per helper thread");
+    constexpr int NKQ = PKQ / NH, NVP = (PV + NH - 1) / NH, NTP = PT / NH;
 
     __shared__ __align__(16) unsigned char smem[Lay::bytes];
     auto sK = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oK + b * Lay::KBUF); };
-    auto sV = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oV + b * Lay::VBUF); };
-    auto sT = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oT + b * Lay::TBUF); };
+    auto sQ = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oQ + b * Lay::KBUF); };
     auto sG = [&](int b) { return reinterpret_cast<float*>(smem + Lay::oG + b * Lay::GBUF); };
-    auto sO = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oO + b * Lay::OBUF); };
-    auto hS = [&](int b, int vt) {
-        return reinterpret_cast<u16*>(smem + Lay::oH + b * Lay::HBUF + vt * (Lay::HS + 2 * Lay::HU));
-    };
-    auto hUh = [&](int b, int vt) { return reinterpret_cast<u16*>(reinterpret_cast<unsigned char*>(hS(b, vt)) + Lay::HS); };
-    auto hUl = [&](int b, int vt) {
-        return reinterpret_cast<u16*>(reinterpret_cast<unsigned char*>(hS(b, vt)) + Lay::HS + Lay::HU);
-    };
+    auto sV = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oV + b * Lay::VBUF); };
+    auto sT = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oT + b * Lay::RBUF); };
+    auto sP = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oP + b * Lay::RBUF); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -342,314 +331,356 @@ void delta_sp_kernel(DspParams p) {
     const int bh = lb / p.slices, m0 = (lb % p.slices) * VS;
     const int T = p.T, NC = p.NC;
     const int64_t seq0 = static_cast<int64_t>(bh) * T;
-    const int64_t seqk = static_cast<int64_t>(bh) * p.qk_seq;   // q and k rows
-    const int64_t chunk0 = static_cast<int64_t>(bh) * NC;
-    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    auto count = [&](int c) { return (T - c * C < C) ? (T - c * C) : C; };
 
-    // Every wave issues the same global memory operations in the same order on every step -
-    // the ring loads, its q rows, one 16-byte store of the outputs - so that the compiler's
-    // count of operations in flight is exact on every path: each wait then covers only the
-    // data it is for, and one step's loads stay in flight across the next step's work.
-
-    // ---- register ring: the staged pieces of two chunks (indices clamped; consumed only
-    // where they are written to LDS, just before a barrier)
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 rg[2][PER];
-    float rgl[2];
-    auto load = [&](int c, u32x4 (&x)[PER], float& gl) {
-        const int n = count(c);
-        const int64_t t0 = static_cast<int64_t>(c) * C;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const void* src;
-            if (i < RK) {
-                const int q = tid + i * NT, j = q / (DK / 8), col = (q % (DK / 8)) * 8;
-                src = p.k + (seqk + t0 + (j < n ? j : 0)) * DK + col;
-            } else if (i < RK + RV) {
-                const int e = tid < PV ? tid : 0, j = e / (VS / 8), col = (e % (VS / 8)) * 8;
-                src = p.v + (seq0 + t0 + (j < n ? j : 0)) * DV + m0 + col;
-            } else if (i < RK + RV + RT) {
-                src = p.tu + (chunk0 + c) * C * C + (tid + (i - RK - RV) * NT) * 8;
-            } else {
-                src = p.g + (chunk0 + c) * C + (tid % PG) * 4;
-            }
-            x[i] = *reinterpret_cast<const u32x4*>(src);
-        }
-        gl = p.g[(chunk0 + c) * C + C - 1];
-    };
-    // chunk c into LDS slot set `slot` (K and the gate tables: slot % 3, the rest slot & 1)
-    auto stage = [&](int c, int slot, const u32x4 (&x)[PER], float gl) {
-        const int n = count(c);
-        u16* K = sK(slot % 3);
-        u16* V = sV(slot & 1);
-        u16* TT = sT(slot & 1);
-        float* GT = sG(slot % 3);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (i < RK) {
-                const int q = tid + i * NT, j = q / (DK / 8), col = (q % (DK / 8)) * 8;
-                *reinterpret_cast<u32x4*>(K + TK::off(j, col)) = j < n ? x[i] : __builtin_bit_cast(u32x4, z8);
-            } else if (i < RK + RV) {
-                const int j = tid / (VS / 8), col = (tid % (VS / 8)) * 8;
-                if (tid < PV)
-                    *reinterpret_cast<u32x4*>(V + TV::off(j, col)) = j < n ? x[i] : __builtin_bit_cast(u32x4, z8);
-            } else if (i < RK + RV + RT) {
-                const int e = tid + (i - RK - RV) * NT, row = e / (C / 8), col = (e % (C / 8)) * 8;
-                *reinterpret_cast<u32x4*>(TT + row * TUS + col) = x[i];
-            } else if (tid < PG) {
-                const int j = tid * 4;
-                const f32x4 G = __builtin_bit_cast(f32x4, x[i]);
-                f32x4 eg, eng, wt;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    eg[e] = ex2(G[e]);
-                    eng[e] = ex2(-G[e]);
-                    wt[e] = ex2(gl - G[e]);
-                }
-                stf4(GT + Lay::GG + j, G);
-                stf4(GT + Lay::GEG + j, eg);
-                stf4(GT + Lay::GENG + j, eng);
-                stf4(GT + Lay::GW + j, wt);
-                if (j == 0) {
-                    GT[Lay::GEL] = ex2(gl);
-                    GT[Lay::GL] = gl;
-                }
-            }
-        }
+    // Global memory through buffer resources, one per tensor and sequence, with the byte offset
+    // (lane's part + chunk's part) in the range-checked VGPR offset: reads past the sequence's
+    // end return zero and writes past it are dropped, so the tail chunk needs no clamping or
+    // masking.
+    constexpr int kRsrc = 0x00020000;   // raw buffer, 32-bit data format
+    auto rsrc = [](const void* base, int64_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrc);
     };
 
-    // ---- chain waves: S^T of value tile vt = w in fp32 accumulators,
-    // sacc[ct][e] = S[m0 + 16 vt + r16][16 ct + 4g + e]
-    const bool chain = w < NV;
-    const bool outw = w >= 2;
-    const int vt = chain ? w : 0;
-    f32x4 sacc[KT];
+    if (NC == 0) {
+        // T == 0: the memory handed through (every wave of the workgroup leaves here)
+        if (w < NV && p.s_out != nullptr) {
+            float* so = p.s_out + (static_cast<int64_t>(bh) * DV + m0 + 16 * w + r16) * DK + 4 * g;
+            const float* s0 = p.s0 ? p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * w + r16) * DK + 4 * g : nullptr;
 #pragma unroll
-    for (int ct = 0; ct < KT; ++ct) {
-        sacc[ct] = zf4();
-        if (chain && p.s0 != nullptr)
-            sacc[ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK + 16 * ct + 4 * g);
+            for (int ct = 0; ct < KT; ++ct) stf4(so + 16 * ct, s0 ? ldf4(s0 + 16 * ct) : zf4());
+        }
+        return;
     }
 
-    // ---- q rows of token tiles {0, 3} (waves 0 and 2) or {1, 2} (waves 1 and 3) in registers,
-    // operand layout of the products over d_k (pieces rr_col); the output waves use them
-    const int ow = w & 1;
-    const int itA = ow == 0 ? 0 : 1, itB = ow == 0 ? 3 : 2;
-    u16x8 qr[2][2][KB];
-    auto load_q = [&](int c, u16x8 (&x)[2][KB]) {
-        const int n = count(c);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int i = 16 * (s == 0 ? itA : itB) + r16;
-            const int64_t row = seqk + static_cast<int64_t>(c) * C + (i < n ? i : 0);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                x[s][kb] = *reinterpret_cast<const u16x8*>(p.q + row * DK + rr_col(kb, g, KB));
-        }
-    };
-    // ---- the outputs of chunk c, from LDS to HBM: one 16-byte piece per thread
-    auto store_o = [&](int c) {
-        const int n = count(c);
-        const u16* O = sO(c & 1);
-        const int e = tid < PO ? tid : 0, j = e / (VS / 8), col = (e % (VS / 8)) * 8;
-        const u16x8 x = *reinterpret_cast<const u16x8*>(O + TV::off(j, col));
-        if (tid < PO && j < n)
-            *reinterpret_cast<u16x8*>(p.o + (seq0 + static_cast<int64_t>(c) * C + j) * DV + m0 + col) = x;
-    };
-
-    // ---- one chunk of the chain (wave vt): Y, R, U, the hand-off and the carry
-    auto chain_step = [&](int c) __attribute__((always_inline)) {
-        const u16* K = sK(c % 3);
-        const u16* V = sV(c & 1);
-        const u16* TT = sT(c & 1);
-        const float* GT = sG(c % 3);
-        u16* HSo = hS(c & 1, vt);
-        u16* HUh = hUh(c & 1, vt);
-        u16* HUl = hUl(c & 1, vt);
-        // S_in in bf16: the B operand of Y (reduction slots 32kb + 4g + e and 32kb + 16 + 4g + e)
-        // and the rows handed to the output waves
-        bf16x4 sb[KT];
+    if (w < 2) {
+        // ================================================ chain waves
+        // wave vt < NV carries S^T of value tile vt (every key) in fp32 accumulators,
+        // sacc[ct][e] = S[m0 + 16 vt + r16][16 ct + 4g + e], and finishes each chunk's outputs
+        // for those channels; every product takes the previous one's accumulators as its
+        // operand (reduction slots 32b + 4g + e and 32b + 16 + 4g + e)
+        const int vt = w;
+        const bool live = vt < NV;
+        f32x4 sacc[KT];
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
-            sb[ct] = cvt4(sacc[ct]);
-            st4(HSo + TK::off(r16, 16 * ct + 4 * g), sb[ct]);
+            sacc[ct] = zf4();
+            if (live && p.s0 != nullptr)
+                sacc[ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK + 16 * ct + 4 * g);
         }
-        // Y = K S_in^T: y[it][e] = Y[16it + 4g + e][value r16]
-        f32x4 y[CT];
+        const auto ro = rsrc(p.o + seq0 * DV, static_cast<int64_t>(T) * DV * 2);
+        lds_barrier();   // the prologue's two barriers
+        lds_barrier();
+        for (int c = 0; c < NC; ++c) {
+            if (live) {
+                const u16* K = sK(c % 3);
+                const u16* Q = sQ(c % 3);
+                const float* GT = sG(c % 3);
+                const u16* V = sV(c & 1);
+                const u16* TT = sT(c & 1);
+                const u16* PP = sP(c & 1);
+                // every LDS operand of the chunk is requested before the first product: with one
+                // wave per SIMD nothing else hides the LDS latency
+                bf16x8 ka[CT][KB], qa[CT][KB], tu[CT][JB], pb[CT][JB], kt[KT][JB];
+                bf16x4 vv[CT];
+                f32x4 eg[CT], wt[CT];
+                float egi[CT];
 #pragma unroll
-        for (int it = 0; it < CT; ++it) {
-            f32x4 acc = zf4();
+                for (int it = 0; it < CT; ++it) {
+                    const int row = 16 * it + r16;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const int row = 16 * it + r16;
-                const bf16x8 a = join8(ld4(K + TK::off(row, 32 * kb + 4 * g)), ld4(K + TK::off(row, 32 * kb + 16 + 4 * g)));
-                acc = mfma_16x16x32(a, join8(sb[2 * kb], sb[2 * kb + 1]), acc);
-            }
-            y[it] = acc;
-        }
-        // R = V - diag(e^G) Y, the B operand of U = T_U R (reduction slots 32jb + 4g + e and
-        // 32jb + 16 + 4g + e)
-        bf16x4 rb[CT];
+                    for (int kb = 0; kb < KB; ++kb) {
+                        ka[it][kb] = join8(ld4(K + TK::off(row, 32 * kb + 4 * g)), ld4(K + TK::off(row, 32 * kb + 16 + 4 * g)));
+                        qa[it][kb] = join8(ld4(Q + TK::off(row, 32 * kb + 4 * g)), ld4(Q + TK::off(row, 32 * kb + 16 + 4 * g)));
+                    }
+                }
 #pragma unroll
-        for (int jt = 0; jt < CT; ++jt) {
-            const f32x4 v4 = up4(tr_op_s<VS>(V, 16 * jt, 16 * vt, r16, g));
-            const f32x4 eg = ldf4(GT + Lay::GEG + 16 * jt + 4 * g);
-            rb[jt] = cvt4(v4 - eg * y[jt]);
-        }
-        // U = T_U R (lower triangular: block jb reaches token tile it when 2jb <= it)
-        f32x4 u[CT];
+                for (int it = 0; it < CT; ++it) {
+                    vv[it] = tr_op_s<VS>(V, 16 * it, 16 * vt, r16, g);
+                    eg[it] = ldf4(GT + Lay::GEG + 16 * it + 4 * g);
+                    wt[it] = ldf4(GT + Lay::GW + 16 * it + 4 * g);
+                    egi[it] = GT[Lay::GEG + 16 * it + r16];
 #pragma unroll
-        for (int it = 0; it < CT; ++it) {
-            f32x4 acc = zf4();
+                    for (int jb = 0; jb < JB; ++jb) {
+                        if (2 * jb > it) continue;
+                        const bool hi = 2 * jb + 1 <= it;
+                        const u16* tr = TT + (16 * it + r16) * RS + 32 * jb + 4 * g;
+                        const u16* pr = PP + (16 * it + r16) * RS + 32 * jb + 4 * g;
+                        tu[it][jb] = join8(ld4(tr), hi ? ld4(tr + 16) : zero4());
+                        pb[it][jb] = join8(ld4(pr), hi ? ld4(pr + 16) : zero4());
+                    }
+                }
 #pragma unroll
-            for (int jb = 0; jb < JB; ++jb) {
-                if (2 * jb > it) continue;
-                const bool hi = 2 * jb + 1 <= it;
-                const u16* tr = TT + (16 * it + r16) * TUS + 32 * jb + 4 * g;
-                acc = mfma_16x16x32(join8(ld4(tr), hi ? ld4(tr + 16) : zero4()), join8(rb[2 * jb], rb[2 * jb + 1]), acc);
-            }
-            u[it] = acc;
-        }
-        // hand-off of U^T rows (bf16 hi + lo) for the output waves
+                for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-        for (int it = 0; it < CT; ++it) {
-            const bf16x4 h = cvt4(u[it]);
-            st4(HUh + TU::off(r16, 16 * it + 4 * g), h);
-            st4(HUl + TU::off(r16, 16 * it + 4 * g), cvt4(u[it] - up4(h)));
-        }
-        // carry: S^T <- e^(G_last) S^T + K^T diag(e^(G_last - G)) U
-        const float dec = GT[Lay::GEL];
-        bf16x8 wb[JB];
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
-            wb[jb] = join8(cvt4(u[2 * jb] * ldf4(GT + Lay::GW + 32 * jb + 4 * g)),
-                           cvt4(u[2 * jb + 1] * ldf4(GT + Lay::GW + 32 * jb + 16 + 4 * g)));
-#pragma unroll
-        for (int ct = 0; ct < KT; ++ct) {
-            f32x4 acc = sacc[ct] * dec;
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) acc = mfma_16x16x32(tr_split_s<DK>(K, jb, 16 * ct, true, r16, g), wb[jb], acc);
-            sacc[ct] = acc;
-        }
-    };
+                    for (int jb = 0; jb < JB; ++jb) kt[ct][jb] = tr_split_s<DK>(K, jb, 16 * ct, true, r16, g);
+                const float dec = GT[Lay::GEL];
+                __builtin_amdgcn_sched_barrier(0);
 
-    // ---- one chunk of the outputs (output wave): P for its two token tiles, then per value
-    // tile o^T = S_in Q^T diag(e^G) + U^T P^T, written to the chunk's output buffer in LDS
-    auto output_step = [&](int c, const u16x8 (&x)[2][KB]) __attribute__((always_inline)) {
-        const u16* K = sK(c % 3);
-        const float* GT = sG(c % 3);
-        u16* O = sO(c & 1);
-        const bool flat = GT[Lay::GL] >= -100.f;   // e^(G_i) e^(-G_j) both within 2^+-100
+                bf16x8 sb[KB];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int it = s == 0 ? itA : itB;
-            const int i = 16 * it + r16;
-            // P[i][16jt + 4g + e] = (q_i . k_j) e^(G_i - G_j), masked above the diagonal
-            f32x4 pacc[CT];
+                for (int kb = 0; kb < KB; ++kb) sb[kb] = join8(cvt4(sacc[2 * kb]), cvt4(sacc[2 * kb + 1]));
+                // Y = K S_in^T (y[it][e] = Y[16it + 4g + e][value r16]) and o^T = S_in Q^T
+                // (oq[it][e] = (S_in q_i)[value 4g + e], i = 16it + r16), interleaved
+                f32x4 y[CT], oq[CT];
 #pragma unroll
-            for (int jt = 0; jt < CT; ++jt) {
-                pacc[jt] = zf4();
-                if (jt > it) continue;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + TK::off(16 * jt + r16, rr_col(kb, g, KB)));
-                    pacc[jt] = mfma_16x16x32(a, as_bf16x8(x[s][kb]), pacc[jt]);
-                }
-            }
-            const float egi = GT[Lay::GEG + i];
-            const float gi = GT[Lay::GG + i];
-            bf16x4 pb[CT];
-#pragma unroll
-            for (int jt = 0; jt < CT; ++jt) {
-                pb[jt] = zero4();
-                if (jt > it) continue;
-                f32x4 d;
-                if (flat) {
-                    d = ldf4(GT + Lay::GENG + 16 * jt + 4 * g) * egi;
-                } else {
-                    const f32x4 gj = ldf4(GT + Lay::GG + 16 * jt + 4 * g);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) d[e] = ex2(gi - gj[e]);
+                for (int it = 0; it < CT; ++it) {
+                    y[it] = zf4();
+                    oq[it] = zf4();
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (16 * jt + 4 * g + e > i) d[e] = 0.f;
-                pb[jt] = cvt4(pacc[jt] * d);
-            }
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int t = 0; t < NV; ++t) {
-                const u16* HSi = hS(c & 1, t);
-                const u16* HUhi = hUh(c & 1, t);
-                const u16* HUlo = hUl(c & 1, t);
-                f32x4 acc = zf4();
+                    for (int it = 0; it < CT; ++it) {
+                        y[it] = mfma_16x16x32(ka[it][kb], sb[kb], y[it]);
+                        oq[it] = mfma_16x16x32(sb[kb], qa[it][kb], oq[it]);
+                    }
+                // R = V - diag(e^G) Y, then U = T_U R (lower triangular: block jb reaches token
+                // tile it when 2jb <= it)
+                bf16x4 rb[CT];
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(HSi + TK::off(r16, rr_col(kb, g, KB)));
-                    acc = mfma_16x16x32(a, as_bf16x8(x[s][kb]), acc);
-                }
-                acc = acc * egi;
+                for (int jt = 0; jt < CT; ++jt) rb[jt] = cvt4(up4(vv[jt]) - eg[jt] * y[jt]);
+                f32x4 u[CT];
+#pragma unroll
+                for (int it = 0; it < CT; ++it) u[it] = zf4();
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                    for (int it = 0; it < CT; ++it)
+                        if (2 * jb <= it) u[it] = mfma_16x16x32(tu[it][jb], join8(rb[2 * jb], rb[2 * jb + 1]), u[it]);
+                // U as a bf16 hi + lo pair for the outputs, and weighted by e^(G_last - G) for the carry
+                bf16x8 uh[JB], ul[JB], wb[JB];
 #pragma unroll
                 for (int jb = 0; jb < JB; ++jb) {
-                    if (2 * jb > it) continue;
-                    const bool hi = 2 * jb + 1 <= it;
-                    const bf16x8 pbb = join8(pb[2 * jb], pb[2 * jb + 1]);
-                    const bf16x4 h0 = ld4(HUhi + TU::off(r16, 32 * jb + 4 * g));
-                    const bf16x4 h1 = hi ? ld4(HUhi + TU::off(r16, 32 * jb + 16 + 4 * g)) : zero4();
-                    const bf16x4 l0 = ld4(HUlo + TU::off(r16, 32 * jb + 4 * g));
-                    const bf16x4 l1 = hi ? ld4(HUlo + TU::off(r16, 32 * jb + 16 + 4 * g)) : zero4();
-                    acc = mfma_16x16x32(join8(h0, h1), pbb, acc);
-                    acc = mfma_16x16x32(join8(l0, l1), pbb, acc);
+                    const bf16x4 h0 = cvt4(u[2 * jb]), h1 = cvt4(u[2 * jb + 1]);
+                    uh[jb] = join8(h0, h1);
+                    ul[jb] = join8(cvt4(u[2 * jb] - up4(h0)), cvt4(u[2 * jb + 1] - up4(h1)));
+                    wb[jb] = join8(cvt4(u[2 * jb] * wt[2 * jb]), cvt4(u[2 * jb + 1] * wt[2 * jb + 1]));
                 }
-                // o[16it + r16][m0 + 16t + 4g + e]
-                st4(O + TV::off(i, 16 * t + 4 * g), cvt4(acc));
+                // carry S^T <- e^(G_last) S^T + K^T diag(e^(G_last - G)) U and outputs
+                // o^T = S_in Q^T diag(e^G) + U^T P^T, interleaved
+                f32x4 ot[CT];
+#pragma unroll
+                for (int it = 0; it < CT; ++it) ot[it] = oq[it] * egi[it];
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct) sacc[ct] = sacc[ct] * dec;
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb) {
+#pragma unroll
+                    for (int ct = 0; ct < KT; ++ct) sacc[ct] = mfma_16x16x32(kt[ct][jb], wb[jb], sacc[ct]);
+#pragma unroll
+                    for (int it = 0; it < CT; ++it) {
+                        if (2 * jb > it) continue;
+                        ot[it] = mfma_16x16x32(uh[jb], pb[it][jb], ot[it]);
+                        ot[it] = mfma_16x16x32(ul[jb], pb[it][jb], ot[it]);
+                    }
+                }
+                // o[16it + r16][m0 + 16vt + 4g + e]
+                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+                for (int it = 0; it < CT; ++it)
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(ot[it])), ro,
+                                                          ((c * C + 16 * it + r16) * DV + m0 + 16 * vt + 4 * g) * 2, 0, 0);
+            }
+            lds_barrier();
+        }
+        if (live && p.s_out != nullptr) {
+            float* so = p.s_out + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK + 4 * g;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) stf4(so + 16 * ct, sacc[ct]);
+        }
+        return;
+    }
+
+    // ================================================ helper waves
+    // every global load of the pass (the same ones in both waves, so the compiler's count of
+    // loads in flight is exact), the staging of each chunk, and the decayed triangle P one
+    // chunk ahead of the chain: wave 2 token tiles {0, 3}, wave 3 {1, 2} (five tiles each)
+    const int ht = tid - 128;                      // 0 .. 127
+    const int hw = w - 2;
+    const auto rk = rsrc(p.k + static_cast<int64_t>(bh) * p.qk_seq * DK, static_cast<int64_t>(p.qk_seq) * DK * 2);
+    const auto rq = rsrc(p.q + static_cast<int64_t>(bh) * p.qk_seq * DK, static_cast<int64_t>(p.qk_seq) * DK * 2);
+    const auto rv = rsrc(p.v + seq0 * DV, static_cast<int64_t>(T) * DV * 2);
+    const int64_t chunk0 = static_cast<int64_t>(bh) * NC;
+    const auto rt = rsrc(p.tu + chunk0 * C * C, static_cast<int64_t>(NC) * C * C * 2);
+    const auto rgt = rsrc(p.g + chunk0 * C, static_cast<int64_t>(NC) * C * 4);
+
+    // the register ring: K, Q and G of chunk a, the v slice and T_U of chunk b
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    struct Entry {
+        u32x4 k[NKQ], q[NKQ], v[NVP], t[NTP];
+        float g;
+    };
+    Entry ring[2];
+    auto load = [&](Entry& e, int a, int b) {
+#pragma unroll
+        for (int i = 0; i < NKQ; ++i) {
+            const int pc = ht + i * NH, j = pc / (DK / 8), col = (pc % (DK / 8)) * 8;
+            e.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((a * C + j) * DK + col) * 2, 0, 0);
+            e.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((a * C + j) * DK + col) * 2, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NVP; ++i) {
+            const int pc = (ht + i * NH) % PV, j = pc / (VS / 8), col = (pc % (VS / 8)) * 8;
+            e.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((b * C + j) * DV + m0 + col) * 2, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NTP; ++i)
+            e.t[i] = __builtin_amdgcn_raw_buffer_load_b128(rt, b * C * C * 2 + (ht + i * NH) * 16, 0, 0);
+        e.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgt, (a * C + lane) * 4, 0, 0));
+    };
+    // K, Q, G of chunk a into slot set sa (mod 3); the v slice and T_U into slot set sb (mod 2)
+    auto stage_kqg = [&](const Entry& e, int sa) {
+        u16* K = sK(sa % 3);
+        u16* Q = sQ(sa % 3);
+#pragma unroll
+        for (int i = 0; i < NKQ; ++i) {
+            const int pc = ht + i * NH, j = pc / (DK / 8), col = (pc % (DK / 8)) * 8;
+            *reinterpret_cast<u32x4*>(K + TK::off(j, col)) = e.k[i];
+            *reinterpret_cast<u32x4*>(Q + TK::off(j, col)) = e.q[i];
+        }
+        if (hw == 0) {
+            // gate tables: lane t holds G_t (log2 units, flat past the end of the sequence)
+            float* GT = sG(sa % 3);
+            const float G = e.g;
+            const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), C - 1));
+            GT[Lay::GG + lane] = G;
+            GT[Lay::GEG + lane] = ex2(G);
+            GT[Lay::GENG + lane] = ex2(-G);
+            GT[Lay::GW + lane] = ex2(gl - G);
+            if (lane == 0) {
+                GT[Lay::GEL] = ex2(gl);
+                GT[Lay::GL] = gl;
             }
         }
     };
-
-    // One step s (compile-time ring slot R = s & 1; STORE: s >= 2): the loads of chunk s + 2
-    // and the q rows of chunk s, the store of chunk s - 2's outputs, the chain of chunk s, the
-    // outputs of chunk s - 1, staging of chunk s + 1 into slot set s + 1 (past the end: a
-    // copy of the last chunk, into slots no wave reads again: K slot s + 1 held chunk s - 2,
-    // V and T_U slot s + 1 chunk s - 1).
-    auto step = [&](int s, auto slot, auto with_store) __attribute__((always_inline)) {
-        constexpr int R = decltype(slot)::value;
-        load(s + 2 < NC ? s + 2 : NC - 1, rg[R], rgl[R]);
-        load_q(s < NC ? s : NC - 1, qr[R]);
-        if constexpr (decltype(with_store)::value) store_o(s - 2);
-        if (chain && s < NC) chain_step(s);
-        if (outw && s >= 1) output_step(s - 1, qr[R ^ 1]);
-        stage(s + 1 < NC ? s + 1 : NC - 1, s + 1, rg[R ^ 1], rgl[R ^ 1]);
-        lds_barrier();
+    auto stage_vt = [&](const Entry& e, int sb) {
+        u16* V = sV(sb & 1);
+        u16* TT = sT(sb & 1);
+#pragma unroll
+        for (int i = 0; i < NVP; ++i) {
+            const int pc = ht + i * NH;
+            if (PV % NH == 0 || pc < PV) {
+                const int j = pc / (VS / 8), col = (pc % (VS / 8)) * 8;
+                *reinterpret_cast<u32x4*>(V + TV::off(j, col)) = e.v[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NTP; ++i) {
+            const int pc = ht + i * NH, row = pc / (C / 8), col = (pc % (C / 8)) * 8;
+            *reinterpret_cast<u32x4*>(TT + row * RS + col) = e.t[i];
+        }
     };
-
-    if (NC > 0) {
+    // the triangle of chunk c: P[i][j] = (q_i . k_j) e^(G_i - G_j) for j <= i, zero above, bf16;
+    // token tiles IA and IB (compile-time, so the tiles' MFMA chains interleave), the decays
+    // as products of two table entries (FLAT: every G_j of the chunk within 2^+-100) or per
+    // element
+    auto triangle_tiles = [&](int c, auto ia, auto ib, auto flat) __attribute__((always_inline)) {
+        constexpr int IA = decltype(ia)::value, IB = decltype(ib)::value;
+        constexpr bool FLAT = decltype(flat)::value;
+        constexpr int NJ = IB + 1;   // key row tiles reached (IB > IA)
+        const u16* K = sK(c % 3);
+        const u16* Q = sQ(c % 3);
+        const float* GT = sG(c % 3);
+        u16* PP = sP(c & 1);
+        bf16x8 qb[2][KB], kr[NJ][KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            qb[0][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(16 * IA + r16, rr_col(kb, g, KB)));
+            qb[1][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(16 * IB + r16, rr_col(kb, g, KB)));
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+                kr[jt][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(16 * jt + r16, rr_col(kb, g, KB)));
+        }
+        f32x4 dj[NJ], gj[NJ];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            if constexpr (FLAT) dj[jt] = ldf4(GT + Lay::GENG + 16 * jt + 4 * g);
+            else gj[jt] = ldf4(GT + Lay::GG + 16 * jt + 4 * g);
+        }
+        float fi[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) fi[s] = GT[(FLAT ? Lay::GEG : Lay::GG) + 16 * (s == 0 ? IA : IB) + r16];
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[2][NJ];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) acc[s][jt] = zf4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    if (jt <= (s == 0 ? IA : IB)) acc[s][jt] = mfma_16x16x32(kr[jt][kb], qb[s][kb], acc[s][jt]);
+        // acc[s][jt][e] = q_i . k_j, i = 16 it_s + r16, j = 16jt + 4g + e
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int it = s == 0 ? IA : IB;
+            const int i = 16 * it + r16;
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) {
+                if (jt > it) continue;
+                f32x4 d;
+                if constexpr (FLAT) {
+                    d = dj[jt] * fi[s];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) d[e] = ex2(fi[s] - gj[jt][e]);
+                }
+                if (jt == it) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * g + e > r16) d[e] = 0.f;
+                }
+                st4(PP + i * RS + 16 * jt + 4 * g, cvt4(acc[s][jt] * d));
+            }
+        }
+    };
+    auto triangle = [&](int c) __attribute__((always_inline)) {
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
-        using NO = std::false_type;
-        using YES = std::true_type;
-        load(0, rg[0], rgl[0]);
-        load(NC > 1 ? 1 : 0, rg[1], rgl[1]);
-        stage(0, 0, rg[0], rgl[0]);
-        lds_barrier();
-        // steps 0 .. NC; the first two have no outputs to store yet
-        step(0, I0{}, NO{});
-        step(1, I1{}, NO{});
-        int s = 2;
-        for (; s + 1 <= NC; s += 2) {
-            step(s, I0{}, YES{});
-            step(s + 1, I1{}, YES{});
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        const bool flat = sG(c % 3)[Lay::GL] >= -100.f;
+        if (hw == 0) {
+            if (flat) triangle_tiles(c, I0{}, I3{}, std::true_type{});
+            else triangle_tiles(c, I0{}, I3{}, std::false_type{});
+        } else {
+            if (flat) triangle_tiles(c, I1{}, I2{}, std::true_type{});
+            else triangle_tiles(c, I1{}, I2{}, std::false_type{});
         }
-        if (s <= NC) step(s, I0{}, YES{});
-        // the last chunk's outputs (written by step NC)
-        store_o(NC - 1);
-    }
+    };
 
-    if (chain && p.s_out != nullptr) {
-        float* so = p.s_out + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK + 4 * g;
-#pragma unroll
-        for (int ct = 0; ct < KT; ++ct) stf4(so + 16 * ct, sacc[ct]);
+    // prologue: K, Q, G of chunks 0 and 1, the v slice and T_U of chunk 0, the triangle of chunk 0
+    const int last = NC - 1;
+    load(ring[0], 0, 0);
+    load(ring[1], last > 0 ? 1 : 0, 0);
+    stage_kqg(ring[0], 0);
+    stage_vt(ring[0], 0);
+    stage_kqg(ring[1], 1);
+    lds_barrier();
+    triangle(0);
+    load(ring[1], last > 1 ? 2 : last, last > 0 ? 1 : 0);
+    lds_barrier();
+    // step c (ring slot R = c & 1): loads of K, Q, G of chunk c + 3 and the v slice and T_U of
+    // chunk c + 2; the triangle of chunk c + 1; staging of the other slot (K, Q, G of chunk
+    // c + 2 into slot set c + 2, the v slice and T_U of chunk c + 1 into slot set c + 1). Past
+    // the end the chunks are clamped to the last one and staged into slots no wave reads again.
+    auto step = [&](int c, auto slot) __attribute__((always_inline)) {
+        constexpr int R = decltype(slot)::value;
+        load(ring[R], c + 3 < NC ? c + 3 : last, c + 2 < NC ? c + 2 : last);
+        if (c + 1 < NC) triangle(c + 1);
+        stage_kqg(ring[R ^ 1], c + 2);
+        stage_vt(ring[R ^ 1], c + 1);
+        lds_barrier();
+    };
+    int c = 0;
+    for (; c + 1 < NC; c += 2) {
+        step(c, std::integral_constant<int, 0>{});
+        step(c + 1, std::integral_constant<int, 1>{});
     }
+    if (c < NC) step(c, std::integral_constant<int, 0>{});
 }
 
 // ====================================================================== row norm

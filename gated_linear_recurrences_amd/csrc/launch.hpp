@@ -90,7 +90,13 @@ inline bool single_pass_forward(Variant variant, const ChunkArgs& a) {
 // The gated delta rule (bf16 storage) at chunk 64 with d_k >= 32 takes the prep + single-pass
 // form (T_U and the gates per chunk in the workspace, the mapped q and k too when the feature
 // map is fused in); chunks of 16 and 32 and d_k = 16 take the three-kernel form.
-inline bool delta_single_pass(const ChunkArgs& a) { return a.chunk == 64 && a.dk >= 32; }
+// (Its buffer offsets are 31-bit: one sequence's q, k, v or o, and its T_U, must stay below
+// 2^31 bytes, which holds for T below 2^22 tokens at d = 128.)
+inline bool delta_single_pass(const ChunkArgs& a) {
+    const long long rows = (static_cast<long long>(a.T) + 63) / 64 * 64;
+    const long long d = a.dk > a.dv ? a.dk : a.dv;
+    return a.chunk == 64 && a.dk >= 32 && rows * (d > 64 ? d : 64) * 2 < (1ll << 31);
+}
 
 // float32 storage, fp32 arithmetic (VALU).
 hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t stream);
