@@ -13,6 +13,7 @@ import torch
 from . import _native
 
 __all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
+           "gdelta_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
            "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step",
            "vla_fwd", "vla_recurrent_step", "workspace_size", "bwd_workspace_size"]
 
@@ -147,6 +148,25 @@ def gdelta_chunk_fwd(q, k, v, log_alpha, beta, chunk=64, s0=None, o=None, s_out=
     _native.check(lib.gdelta_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0),
                                        _ptr(o), _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q),
                                        _ptr(ws), ws_bytes, _stream(q.device)))
+    return o, s_out
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20   # the fixed workspace of gdelta_chunk_fwd_noalloc, per device
+
+
+def gdelta_chunk_fwd_noalloc(q, k, v, log_alpha, beta, chunk=64, s0=None, o=None, s_out=None, return_state=True):
+    """gdelta_chunk_fwd whose workspace is the library's fixed per-device array of
+    NOALLOC_SCRATCH_BYTES: with ``o`` passed in and ``s_out`` passed in (or
+    ``return_state=False``), the call allocates nothing. Calls overlapping in time on one
+    device race on that array."""
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
+    _require(log_alpha, "log_alpha", (B, H, T), torch.float32, q.device)
+    _require(beta, "beta", (B, H, T), torch.float32, q.device)
+    lib = _native.load()
+    _native.check(lib.gdelta_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0),
+                                               _ptr(o), _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q),
+                                               _stream(q.device)))
     return o, s_out
 
 

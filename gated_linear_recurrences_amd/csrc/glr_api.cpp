@@ -88,6 +88,13 @@ la_status run_chunk(glr::Variant variant, const glr::ChunkArgs& a, la_dtype dtyp
 
 }  // namespace
 
+namespace glr {
+int report_error(int status, const char* message) {
+    return fail(static_cast<la_status>(status), "%s", message);
+}
+int check_chunk_call(Variant variant, const ChunkArgs& a, int dtype) { return check_chunk_args(variant, a, dtype); }
+}  // namespace glr
+
 extern "C" {
 
 la_status la_chunk_workspace_size(la_variant variant, int B, int H, int T, int dk, int dv, int chunk,
@@ -374,6 +381,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (3 << 16) | 0; }
+int la_version(void) { return (3 << 16) | 1; }
 
 }  // extern "C"

@@ -10,6 +10,12 @@ namespace glr {
 
 enum Variant { kRetention = 0, kGLA = 1, kGDelta = 2, kScalar = 3 };
 
+// Records `message` as the calling thread's last error and returns `status` (an la_status).
+int report_error(int status, const char* message);
+struct ChunkArgs;
+// The argument checks of a chunk entry point (sizes, dtype, pointers), as an la_status.
+int check_chunk_call(Variant variant, const ChunkArgs& a, int dtype);
+
 struct ChunkArgs {
     const void* q;
     const void* k;

@@ -210,6 +210,27 @@ la_status gdelta_chunk_fwd_fused(const void* q, const void* k, const void* v,
                                  void* stream);
 
 /*
+ * gdelta_chunk_fwd for callers that cannot allocate device memory (code under
+ * stream capture, serving loops and harnesses that forbid hipMalloc): no
+ * workspace argument.  The workspace is instead a fixed array of
+ * LA_NOALLOC_SCRATCH_BYTES bytes in the library's own device memory, one copy
+ * per device, held until the process ends.  A shape whose workspace
+ * (la_chunk_workspace_size with LA_GDELTA) is larger is LA_ERR_UNSUPPORTED and
+ * nothing is enqueued.  Every call on a device uses that device's one array
+ * and leaves its last contents there: calls whose work overlaps in time on one
+ * device (different streams or host threads) race and give undefined results;
+ * calls on one stream are ordered and safe.  The first call on a device looks
+ * the array's address up (with that device current); no call allocates.
+ * Other arguments, behaviour and errors as for gdelta_chunk_fwd.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+la_status gdelta_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta,
+                                   const float* s0, void* o, float* s_out,
+                                   int B, int H, int T, int dk, int dv, int chunk,
+                                   la_dtype dtype, void* stream);
+
+/*
  * One decode token for N sequences x H heads with a per-key-channel gate (the
  * recurrent form of the RetNet page, section on retention: the same two
  * gestures for every token at constant memory; a fixed decay is the constant
@@ -344,7 +365,8 @@ const char* la_last_error(void);
  * mamba2_chunk_fwd; 2.2: gdelta_recurrent_step; 2.3: gdelta_chunk_fwd_fused;
  * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step; 2.6: gla_chunk_bwd;
  * 2.7: single-pass retention and scalar-decay forward, no workspace at B * H * d_v / 16 >= 128;
- * 3.0: vla_fwd and vla_recurrent_step take the readout and the denominator vector). */
+ * 3.0: vla_fwd and vla_recurrent_step take the readout and the denominator vector;
+ * 3.1: gdelta_chunk_fwd_noalloc). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -38,6 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 3        # 3.0: the VLA entry points take the readout and its denominator
+    assert lib.la_version() & 0xFFFF >= 1     # 3.1: gdelta_chunk_fwd_noalloc
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -315,3 +316,29 @@ def test_gla_backward_workspace_size(lib):
     n = 8 * 16 * 64
     assert out.value == 2 * a256(n * 128 * 128 * 2) + a256(128 * 128 * 128 * 4)
     assert lib.gla_chunk_bwd_workspace_size(1, 1, 8, 16, 16, 16, 0, ctypes.byref(out)) == _native.LA_ERR_UNSUPPORTED
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation gated delta entry point checks every argument, then the size of the
+    workspace its shape needs against its fixed array, before it touches a device."""
+    fn = lib.gdelta_chunk_fwd_noalloc
+    p = ctypes.c_void_p(4096)
+
+    def call(q=p, beta=p, B=2, H=2, T=100, dk=64, dv=64, chunk=64, dtype=_native.LA_BF16):
+        return fn(q, p, p, p, beta, None, p, None, B, H, T, dk, dv, chunk, dtype, None)
+
+    assert call(q=None) == _native.LA_ERR_INVALID and b"q is NULL" in lib.la_last_error()
+    assert call(beta=None) == _native.LA_ERR_INVALID and b"beta" in lib.la_last_error()
+    assert call(q=ctypes.c_void_p(4100)) == _native.LA_ERR_INVALID
+    assert call(T=-1) == _native.LA_ERR_INVALID
+    assert call(dk=48) == _native.LA_ERR_UNSUPPORTED
+    assert call(chunk=8) == _native.LA_ERR_UNSUPPORTED
+    # B4 H16 T8192 d128 (66 MiB) fits the 96 MiB array; 16 x 16 x 8192 tokens at d 128 (264 MiB) do not
+    need = ctypes.c_size_t(0)
+    assert lib.la_chunk_workspace_size(_native.LA_GDELTA, 4, 16, 8192, 128, 128, 64, _native.LA_BF16,
+                                       ctypes.byref(need)) == _native.LA_OK
+    assert need.value <= 96 << 20
+    assert call(B=16, H=16, T=8192, dk=128, dv=128) == _native.LA_ERR_UNSUPPORTED
+    assert b"exceeds" in lib.la_last_error()
+    # B == 0 is a no-op that needs no device
+    assert call(B=0) == _native.LA_OK
