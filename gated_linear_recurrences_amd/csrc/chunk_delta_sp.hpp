@@ -296,6 +296,12 @@ struct DspLayout {
     static_assert(bytes <= 160 * 1024, "LDS budget of the delta single pass exceeded");
 };
 
+// ds_read_b64_tr_b16 at a lane's own address: the four 16-bit values a lane reads are
+// handed to the four lanes of its column quad, one each (see tr_op_s).
+__device__ __forceinline__ bf16x4 tr4(const u16* p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+
 template <int C, int DK, int DV, int VS>
 __global__ __launch_bounds__(256)
 void delta_sp_kernel(DspParams p) {
@@ -327,6 +333,10 @@ void delta_sp_kernel(DspParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g = lane >> 4;
+    // key channels held by a chain wave's memory tile ct at lane group g: chan(ct) + e, e < 4,
+    // so that the bf16 operand built from tiles 2b and 2b + 1 holds eight consecutive keys
+    // 32b + 8g + 0..7 (one 16-byte LDS read of the matching K or Q row piece)
+    auto chan = [&](int ct) { return 32 * (ct >> 1) + 8 * g + 4 * (ct & 1); };
     const int lb = logical_block_of(blockIdx.x, gridDim.x, p.remap);
     const int bh = lb / p.slices, m0 = (lb % p.slices) * VS;
     const int T = p.T, NC = p.NC;
@@ -355,7 +365,7 @@ void delta_sp_kernel(DspParams p) {
     if (w < 2) {
         // ================================================ chain waves
         // wave vt < NV carries S^T of value tile vt (every key) in fp32 accumulators,
-        // sacc[ct][e] = S[m0 + 16 vt + r16][16 ct + 4g + e], and finishes each chunk's outputs
+        // sacc[ct][e] = S[m0 + 16 vt + r16][chan(ct) + e], and finishes each chunk's outputs
         // for those channels; every product takes the previous one's accumulators as its
         // operand (reduction slots 32b + 4g + e and 32b + 16 + 4g + e)
         const int vt = w;
@@ -365,7 +375,7 @@ void delta_sp_kernel(DspParams p) {
         for (int ct = 0; ct < KT; ++ct) {
             sacc[ct] = zf4();
             if (live && p.s0 != nullptr)
-                sacc[ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK + 16 * ct + 4 * g);
+                sacc[ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK + chan(ct));
         }
         const auto ro = rsrc(p.o + seq0 * DV, static_cast<int64_t>(T) * DV * 2);
         lds_barrier();   // the prologue's two barriers
@@ -389,8 +399,8 @@ void delta_sp_kernel(DspParams p) {
                     const int row = 16 * it + r16;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        ka[it][kb] = join8(ld4(K + TK::off(row, 32 * kb + 4 * g)), ld4(K + TK::off(row, 32 * kb + 16 + 4 * g)));
-                        qa[it][kb] = join8(ld4(Q + TK::off(row, 32 * kb + 4 * g)), ld4(Q + TK::off(row, 32 * kb + 16 + 4 * g)));
+                        ka[it][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(row, 32 * kb + 8 * g));
+                        qa[it][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(row, 32 * kb + 8 * g));
                     }
                 }
 #pragma unroll
@@ -412,7 +422,15 @@ void delta_sp_kernel(DspParams p) {
 #pragma unroll
                 for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-                    for (int jb = 0; jb < JB; ++jb) kt[ct][jb] = tr_split_s<DK>(K, jb, 16 * ct, true, r16, g);
+                    for (int jb = 0; jb < JB; ++jb) {
+                        // A = K^T, row r16 = key 32(ct / 2) + 8(r16 / 4) + 4(ct % 2) + r16 % 4 (the
+                        // keys chan(ct) + e of the product's output rows 4g + e), reduction slots
+                        // = tokens 32jb + 4g + e and 32jb + 16 + 4g + e: lane (r16, g) reads the
+                        // four keys from col of token row 32jb (+16) + 4g + r16 / 4
+                        const int col = 32 * (ct >> 1) + 8 * (r16 & 3) + 4 * (ct & 1);
+                        kt[ct][jb] = join8(tr4(K + TK::off(32 * jb + 4 * g + (r16 >> 2), col)),
+                                           tr4(K + TK::off(32 * jb + 16 + 4 * g + (r16 >> 2), col)));
+                    }
                 const float dec = GT[Lay::GEL];
                 __builtin_amdgcn_sched_barrier(0);
 
@@ -484,9 +502,9 @@ void delta_sp_kernel(DspParams p) {
             lds_barrier();
         }
         if (live && p.s_out != nullptr) {
-            float* so = p.s_out + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK + 4 * g;
+            float* so = p.s_out + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK;
 #pragma unroll
-            for (int ct = 0; ct < KT; ++ct) stf4(so + 16 * ct, sacc[ct]);
+            for (int ct = 0; ct < KT; ++ct) stf4(so + chan(ct), sacc[ct]);
         }
         return;
     }
