@@ -89,25 +89,30 @@ template <int C, int DK>
 struct TfacLayout {
     static constexpr int CT = C / 16;
     static constexpr int KS = tile_stride(DK);
-    static constexpr int AS = C + 4;
     static constexpr int TS = C + 8;
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
+    // A is kept as its CT (CT + 1) / 2 lower-triangular 16 x 16 tiles, rows of ATS floats;
+    // tile (i, j <= i) at tileA(i, j)
+    static constexpr int ATS = 20;
+    static constexpr int ATILE = 16 * ATS;
+    static constexpr int tileA(int i, int j) { return (i * (i + 1) / 2 + j) * ATILE; }
+    // K is dead once A is formed: the diagonal blocks D and T reuse its space
     static constexpr int oK = 0;
-    static constexpr int oA = oK + al(C * KS * 2);
-    static constexpr int oD = oA + al(C * AS * 4);
+    static constexpr int oD = 0;
     static constexpr int oT = oD + al(CT * 256 * 4);
-    static constexpr int oG = oT + al(C * TS * 2);
+    static constexpr int oA = al(C * KS * 2) > oT + al(C * TS * 2) ? al(C * KS * 2) : oT + al(C * TS * 2);
+    static constexpr int oG = oA + al(CT * (CT + 1) / 2 * ATILE * 4);
     static constexpr int oB = oG + al(C * 4);
     static constexpr int bytes = oB + al(C * 4);
     static_assert(bytes <= 64 * 1024, "LDS budget of the delta prep exceeded");
 };
 
 template <int C, int DK>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256, 5)
 void delta_tfac_kernel(DspParams p) {
     using Lay = TfacLayout<C, DK>;
     constexpr int CT = C / 16, NT = 256, NW = 4;
-    constexpr int KS = Lay::KS, AS = Lay::AS, TS = Lay::TS;
+    constexpr int KS = Lay::KS, ATS = Lay::ATS, TS = Lay::TS;
     constexpr int KB = (DK + 31) / 32;
     constexpr int KP = C * DK / 8, KP_PER = (KP + NT - 1) / NT;
     constexpr int TP = C * C / 8, TP_PER = (TP + NT - 1) / NT;
@@ -204,7 +209,7 @@ void delta_tfac_kernel(DspParams p) {
             const int j = 16 * jt + 4 * g + r;
             a[r] = (j < i) ? bi * acc[r] * ex2(gi - gj[r]) : 0.f;
         }
-        stf4(sA + i * AS + 16 * jt + 4 * g, a);
+        stf4(sA + Lay::tileA(it, jt) + r16 * ATS + 4 * g, a);
     }
     lds_barrier();
 
@@ -216,7 +221,7 @@ void delta_tfac_kernel(DspParams p) {
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float* arow = sA + (16 * b + i) * AS + 16 * b;
+                const float* arow = sA + Lay::tileA(b, b) + i * ATS;
                 float acc = (i == j) ? 1.f : 0.f;
 #pragma unroll
                 for (int kk = 0; kk < i; ++kk) acc -= arow[kk] * x[kk];
@@ -244,7 +249,7 @@ void delta_tfac_kernel(DspParams p) {
 #pragma unroll
                 for (int m = 0; m < CT; ++m) {
                     if (m < w || m >= i) continue;
-                    const f32x4 a = ldf4(sA + (16 * i + r16) * AS + 16 * m + 4 * g);
+                    const f32x4 a = ldf4(sA + Lay::tileA(i, m) + r16 * ATS + 4 * g);
                     acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cvt4(a), cvt4(tcol[m]), acc, 0, 0, 0);
                 }
                 const f32x4 d = ldf4(sD + i * 256 + r16 * 16 + 4 * g);
