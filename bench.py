@@ -555,14 +555,16 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
 
 
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_XCD = 8   # GRBM_GUI_ACTIVE comes summed over the XCDs
 
 
 def summarize_mfma(mfma_dir):
     """MFMA counters per call of every chunked workload from one rocprofv3 --pmc run of
     ``bench.py --counter-run`` (SQ_INSTS_VALU_MFMA_MOPS_BF16: bf16 MFMA work in units of 512
     flops; SQ_VALU_MFMA_BUSY_CYCLES: cycles the MFMA units were busy, summed over the chip;
-    GRBM_GUI_ACTIVE: cycles the GPU was busy). Busy fraction = MFMA busy cycles / (GPU busy
-    cycles x 256 CUs x 4 SIMDs). Writes profiles/pmc_mfma.json and prints a table."""
+    GRBM_GUI_ACTIVE: cycles the GPU was busy, which rocprofv3 sums over the 8 XCDs, so it is
+    divided by 8). Busy fraction = MFMA busy cycles / (GPU busy cycles x 256 CUs x 4 SIMDs).
+    Writes profiles/pmc_mfma.json and prints a table."""
     rows = _counter_rows(mfma_dir)
     rec = {"source_sha256": kernel_source_hash(), "counters": list(MFMA_COUNTERS), "workloads": {}}
     lines = ["| workload | kernel | dispatches | MFMA bf16 flop / dispatch | MFMA busy cycles | GPU busy cycles | "
@@ -577,7 +579,7 @@ def summarize_mfma(mfma_dir):
                 if not disp:
                     ok = False
                     break
-                vals[key] = sum(disp.values()) / len(disp)
+                vals[key] = sum(disp.values()) / len(disp) / (N_XCD if key == "gui" else 1)
                 n = len(disp)
             if not ok:
                 break

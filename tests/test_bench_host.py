@@ -81,10 +81,11 @@ def test_traffic_summary_scales_by_the_copy(tmp_path, monkeypatch, capsys):
 
 def test_mfma_summary(tmp_path, monkeypatch, capsys):
     """MFMA counters per call: MOPS in units of 512 flops, the busy fraction over the chip's
-    256 x 4 SIMDs, summed over a workload's kernels."""
+    256 x 4 SIMDs (GPU busy cycles as rocprofv3 reports them, summed over 8 XCDs), summed over
+    a workload's kernels."""
     k1, k2 = bench.WORKLOAD_KERNELS[bench.MAIN]
     rows = []
-    for k, mops, busy, gui in ((k1, 10.0, 2048.0, 10.0), (k2, 30.0, 6144.0, 10.0)):
+    for k, mops, busy, gui in ((k1, 10.0, 2048.0, 80.0), (k2, 30.0, 6144.0, 80.0)):   # gui summed over 8 XCDs
         rows += [(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops), (k, "SQ_VALU_MFMA_BUSY_CYCLES", busy),
                  (k, "GRBM_GUI_ACTIVE", gui)]
     path = tmp_path / "m"
