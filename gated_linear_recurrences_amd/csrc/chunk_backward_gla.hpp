@@ -13,8 +13,9 @@
 // sum_m dS_T[m][c] S_T[m][c].
 //
 // The decays inside a chunk factor through a reference per 16-token tile, as in the
-// forward: r_t[c] = G just before tile t, q~_i = q_i e^(G_i - r_it) (<= |q|),
-// k~_j = k_j e^(r_jt - G_j) (bounded by one tile's gate), F_(it,jt) = e^(r_it - r_jt) <= 1, so
+// forward: r_t[c] = G just before tile t (at most 80 nats above G at its last token),
+// q~_i = q_i e^(G_i - r_it), k~_j = k_j e^(r_jt - G_j) (both within e^(+-80) for tiles whose
+// gates sum to -160 or more), F_(it,jt) = e^(r_it - r_jt) <= 1, so
 // e^(G_i - G_j) = q~-scale * F * k~-scale on every product:
 //   P = (Q~ . F) K~^T per tile pair;  dK^T = e^(r_jt - G_j) . (Q~ . F)^T A2 + e^(G_last - G_j) . R^T V^T
 //   dQ^T = e^(G_i - r_it) . (K~ . F)^T A2^T + e^(G_i) . S_in^T dO^T;  dV^T = dO^T P + R K^^T,
@@ -259,7 +260,7 @@ void grad_gla_kernel(GradGlaParams p) {
         // ---- tables (references r_t, F, e^(G_last - r_t)) and the rescaled q~, k~
         for (int idx = tid; idx < CT * DK; idx += NT) {
             const int t = idx / DK, key = idx % DK;
-            const float rt = t > 0 ? sG[(16 * t - 1) * GS + key] : 0.f;
+            const float rt = tile_ref(t > 0 ? sG[(16 * t - 1) * GS + key] : 0.f, sG[(16 * t + 15) * GS + key]);
             sR[idx] = rt;
             sL[idx] = ex2(sG[(C - 1) * GS + key] - rt);
         }
@@ -267,8 +268,8 @@ void grad_gla_kernel(GradGlaParams p) {
             const int key = idx % DK;
             int pr = idx / DK, it = 1;
             while (pr >= it) { pr -= it; ++it; }   // pair (it, jt = pr), jt < it
-            const float ri = sG[(16 * it - 1) * GS + key];
-            const float rj = pr > 0 ? sG[(16 * pr - 1) * GS + key] : 0.f;
+            const float ri = tile_ref(sG[(16 * it - 1) * GS + key], sG[(16 * it + 15) * GS + key]);
+            const float rj = tile_ref(pr > 0 ? sG[(16 * pr - 1) * GS + key] : 0.f, sG[(16 * pr + 15) * GS + key]);
             sF[idx] = ex2(ri - rj);
         }
 #pragma unroll
@@ -284,6 +285,8 @@ void grad_gla_kernel(GradGlaParams p) {
                     c0 = ldf4(sG + (16 * t - 1) * GS + col);
                     c1 = ldf4(sG + (16 * t - 1) * GS + col + 4);
                 }
+                c0 = tile_ref4(c0, ldf4(sG + (16 * t + 15) * GS + col));
+                c1 = tile_ref4(c1, ldf4(sG + (16 * t + 15) * GS + col + 4));
                 float qs[8], ks[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {

@@ -80,6 +80,18 @@ __device__ __forceinline__ bf16x8 tr_split(const u16* X, int jb, int n0, bool hi
 // consecutive rows, one chunk each: h is one-to-one on them) and a transposing read
 // (8 consecutive rows, two adjacent chunks each: h / 2 is one-to-one on the rows that
 // share a bank line). Narrower tiles keep the padded stride tile_stride(W).
+// Reference of a 16-token tile in the per-channel gate factorisation (log2 units): the
+// cumulative gate r just before the tile, moved down to at most 80 nats (115.4 in log2
+// units) above the gate at the tile's last token, so that e^(G - ref) and e^(ref - G) stay
+// within e^(+-80) for every token of any tile whose gates sum to -160 nats or more.
+__device__ __forceinline__ float tile_ref(float r, float last) { return fminf(r, last + 115.4f); }
+__device__ __forceinline__ f32x4 tile_ref4(f32x4 r, f32x4 last) {
+    f32x4 m;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m[e] = tile_ref(r[e], last[e]);
+    return m;
+}
+
 template <int W>
 struct SwzTile {
     static constexpr int STRIDE = (W == 64 || W == 128) ? W : (W == 16 ? 16 : W + 16);

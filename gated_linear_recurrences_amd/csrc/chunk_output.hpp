@@ -21,10 +21,13 @@
 //   gates     (scalar) one wave scans the chunk's gates into a table of G;
 //             (GLA) the raw log-gates are staged and scanned per key channel
 //             (16-token runs per lane, joined by shuffles), then folded into bf16
-//             operands: q and k rescaled to the cumulative gate r_t just before
-//             their own 16-token tile (bounded factors), with tables
-//             F = e^(r_it - r_jt) <= 1 joining two tiles in the triangle and
-//             R = e^(r_it) turning rescaled q into q e^(b) for the readout;
+//             operands: q and k rescaled to a reference m_t per 16-token tile and key
+//             channel, the cumulative gate r_t just before the tile, moved down to
+//             b_last + 80 nats (b_last: at the tile's last token) when the tile's gates
+//             sum below -80, so that both factors e^(b - m) and e^(m - b) stay within
+//             e^(+-80) for tiles down to -160 (finite in fp32 and bf16); tables
+//             F = e^(m_it - m_jt) <= 1 join two tiles in the triangle and R = e^(m_it) <= 1
+//             turns rescaled q into q e^(b) for the readout;
 //   triangle  the P tiles (it, jt <= it) are spread over the waves; each is one
 //             MFMA chain over d_k from LDS, masked and decayed, and stored to LDS
 //             in bf16;
@@ -225,8 +228,9 @@ void output_kernel(OutParams p) {
                 if (16 * g + e < C) sB[(16 * g + e) * BS + key] = t[e] + base;
         }
         lds_barrier();
-        // ---- q rescaled to its tile's reference r (the cumulative gate just before
-        // the tile), q e^b, k rescaled by e^(r - b); the joining table F
+        // ---- q rescaled to its tile's reference m (the cumulative gate just before the
+        // tile, at most 80 nats above the gate at its last token), k rescaled by
+        // e^(m - b); the joining table F
 #pragma unroll
         for (int i = 0; i < QP_PER; ++i) {
             const int idx = tid + i * NT;
@@ -241,6 +245,8 @@ void output_kernel(OutParams p) {
                     r0 = ldf4(sB + (16 * t - 1) * BS + col);
                     r1 = ldf4(sB + (16 * t - 1) * BS + col + 4);
                 }
+                r0 = tile_ref4(r0, ldf4(sB + (16 * t + 15) * BS + col));
+                r1 = tile_ref4(r1, ldf4(sB + (16 * t + 15) * BS + col + 4));
                 float qs[8], ks[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -255,7 +261,7 @@ void output_kernel(OutParams p) {
                 *reinterpret_cast<bf16x8*>(sK + j * QS + col) = pack8(ks[0], ks[1], ks[2], ks[3], ks[4], ks[5], ks[6], ks[7]);
             }
         }
-        // F[(it, jt)][key] = e^(r_it - r_jt), jt < it, pairs in row order; kept in
+        // F[(it, jt)][key] = e^(m_it - m_jt), jt < it, pairs in row order; kept in
         // registers until the gates are dead
         constexpr int NFI = Lay::NF * DK, NF_PER = NFI > 0 ? (NFI + NT - 1) / NT : 1;
         float fr[NF_PER];
@@ -267,19 +273,20 @@ void output_kernel(OutParams p) {
                 const int key = idx % DK;
                 int pr = idx / DK, it = 1;
                 while (pr >= it) { pr -= it; ++it; }   // pair (it, jt = pr), jt < it
-                const float ri = sB[(16 * it - 1) * BS + key];
-                const float rj = pr > 0 ? sB[(16 * pr - 1) * BS + key] : 0.f;
+                const float ri = tile_ref(sB[(16 * it - 1) * BS + key], sB[(16 * it + 15) * BS + key]);
+                const float rj = tile_ref(pr > 0 ? sB[(16 * pr - 1) * BS + key] : 0.f, sB[(16 * pr + 15) * BS + key]);
                 fr[i] = ex2(ri - rj);
             }
         }
-        // R[it][key] = e^(r_it): the readout operand q e^b is q rescaled times R
+        // R[it][key] = e^(m_it): the readout operand q e^b is q rescaled times R
         constexpr int NRI = CT * DK, NR_PER = (NRI + NT - 1) / NT;
         float rr[NR_PER];
 #pragma unroll
         for (int i = 0; i < NR_PER; ++i) {
             const int idx = tid + i * NT;
             const int it = idx / DK, key = idx % DK;
-            rr[i] = (idx < NRI && it > 0) ? ex2(sB[(16 * it - 1) * BS + key]) : 1.f;
+            rr[i] = idx < NRI ? ex2(tile_ref(it > 0 ? sB[(16 * it - 1) * BS + key] : 0.f, sB[(16 * it + 15) * BS + key]))
+                              : 1.f;
         }
         lds_barrier();   // gates dead: region X takes v, P, F and R
 #pragma unroll
@@ -363,8 +370,8 @@ void output_kernel(OutParams p) {
             const int col = 32 * kb + 8 * g;
             qb[kb] = (col < DK) ? *reinterpret_cast<const bf16x8*>(sQ + i * QS + col) : as_bf16x8(z8);
             if constexpr (GLA) {
-                // q e^b = (q e^(b - r_it)) e^(r_it)
-                if (col < DK && it > 0) {
+                // q e^b = (q e^(b - m_it)) e^(m_it)
+                if (col < DK) {
                     const f32x4 f0 = ldf4(sR + it * DK + col), f1 = ldf4(sR + it * DK + col + 4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {

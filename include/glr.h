@@ -152,10 +152,16 @@ la_status mamba2_chunk_fwd(const void* q, const void* k, const void* v,
  * meglio nella memoria", section "Dimenticare: i gate", diagonal-gate
  * equation):
  *     S_t = S_{t-1} Diag(alpha_t) + v_t k_t^T,   o_t = S_t q_t.
- * log_alpha [B][H][T][d_k] float32 holds log(alpha_t) (<= 0).  The chunk is
- * factorised in sub-blocks of 16 tokens, so within any 16 consecutive tokens
- * of a chunk the summed log-gates of one channel must stay above -80 (fp32
- * range of the rescaled keys); beyond that the output is not defined.
+ * log_alpha [B][H][T][d_k] float32 holds log(alpha_t) (<= 0).  For bf16
+ * storage the decays inside a chunk are factorised per 16-token tile (tokens
+ * 16m .. 16m + 15 of the chunk): q and k are rescaled by e^(+-(G - m)) around
+ * a reference m, the cumulative log-gate just before the tile, moved down to
+ * 80 above the one at the tile's last token when the tile's gates sum below
+ * -80.  So for every key channel the log-gates of each such tile must sum to
+ * at least -160 (the factors stay within e^(+-80), inside the fp32 / bf16
+ * range with room for |q|, |k| <= 100); beyond that the output is not
+ * defined.  gla_chunk_bwd has the same bound.
+ * fp32 storage evaluates every decay directly and has none.
  */
 la_status gla_chunk_fwd(const void* q, const void* k, const void* v,
                         const float* log_alpha,

@@ -9,9 +9,10 @@ full length, through the C ABI.
   correzione: Gated DeltaNet"): with beta = 1 and unit keys a write overwrites, so reading
   with q = k returns v exactly; beta = 0 is a pure fade S_t = alpha_t S_{t-1}; alpha = 1 is
   DeltaNet, against the oracle's recurrent form.
-* GLA with strong per-channel gates (log alpha in [-4.5, -3.5]: a 16-token run of one
-  channel sums to -56 .. -72), where the per-16-token factorisation of the decays works
-  with rescaled keys near the top of the fp32 / bf16 range.
+* GLA with strong per-channel gates (log alpha in [-4.5, -3.5] and in [-10, -9.4]: a
+  16-token run of one channel sums to -56 .. -72 or -150 .. -160, the stated bound), where
+  the per-16-token factorisation of the decays works with rescaled queries and keys near
+  the ends of the fp32 / bf16 range; forward and backward.
 
 Bounds are the bf16 parity gates: max |d| <= 2e-2 and <= 1e-2 of the reference's largest
 entry (memory: relative 1e-2; decode memory: relative 1e-5)."""
@@ -140,16 +141,42 @@ def test_delta_unit_gate_is_deltanet(state):
 
 # ----------------------------------------------------------------------------- GLA, strong gates
 
+GLA_STRONG = [(-4.5, -3.5), (-10.0, -9.4)]
+
+
+@pytest.mark.parametrize("gates", GLA_STRONG)
 @pytest.mark.parametrize("shape", [(2, 4, 300, 128, 128, 64), (1, 2, 130, 64, 32, 32), (8, 16, 70, 128, 128, 64)])
-def test_gla_strong_gates(shape):
-    """log alpha uniform in [-4.5, -3.5] per (token, key channel): a channel's 16-token run
-    sums to -56 .. -72, and outputs are carried by the last few tokens."""
+def test_gla_strong_gates(shape, gates):
+    """log alpha uniform per (token, key channel) in [-4.5, -3.5] (a channel's 16-token run
+    sums to -56 .. -72) or in [-10, -9.4] (-150 .. -160, the bound the header states: the
+    factors that rescale q and k inside a 16-token tile reach e^(+-80)); outputs are carried
+    by the last few tokens, the diagonal term q_t.k_t v_t foremost."""
     Bs, Hs, Ts, dk, dv, c = shape
     w = synthetic.gla_inputs(Bs, Hs, Ts, dk, dv, chunk=c, dtype="bf16", seed=83 + Ts, with_state=True)
-    w.log_alpha = np.random.default_rng(84).uniform(-4.5, -3.5, (Bs, Hs, Ts, dk)).astype(np.float32)
+    w.log_alpha = np.random.default_rng(84).uniform(*gates, (Bs, Hs, Ts, dk)).astype(np.float32)
     o, S = api.gla_chunk_fwd(_t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16),
                              _t(w.log_alpha), chunk=c, s0=_t(w.s0))
     torch.cuda.synchronize()
     o_ref, S_ref = orc.gla_chunkwise(w.q, w.k, w.v, w.log_alpha, c, s0=w.s0)
-    _gate(f"gla strong gates {shape} o", o.float().cpu().numpy().astype(np.float64), o_ref)
-    _gate(f"gla strong gates {shape} S_T", S.cpu().numpy().astype(np.float64), S_ref, absolute=np.inf)
+    _gate(f"gla strong gates {gates} {shape} o", o.float().cpu().numpy().astype(np.float64), o_ref)
+    _gate(f"gla strong gates {gates} {shape} S_T", S.cpu().numpy().astype(np.float64), S_ref, absolute=np.inf)
+
+
+@pytest.mark.parametrize("gates", GLA_STRONG)
+@pytest.mark.parametrize("shape", [(2, 2, 200, 128, 128, 64), (1, 2, 130, 64, 32, 32)])
+def test_gla_backward_strong_gates(shape, gates):
+    """The GLA backward (same tile factorisation) under the same gates: dq, dk, dv and ds0 at
+    the forward's relative bound, against the oracle's reverse-mode gradients."""
+    Bs, Hs, Ts, dk, dv, c = shape
+    w = synthetic.gla_inputs(Bs, Hs, Ts, dk, dv, chunk=c, dtype="bf16", seed=85 + Ts, with_state=True)
+    w.log_alpha = np.random.default_rng(86).uniform(*gates, (Bs, Hs, Ts, dk)).astype(np.float32)
+    rng = np.random.default_rng(87)
+    dout = synthetic.round_to_bf16(rng.standard_normal((Bs, Hs, Ts, dv)) / np.sqrt(dv)).astype(np.float32)
+    dq, dk_, dv_, dg, ds0 = api.gla_chunk_bwd(_t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16),
+                                              _t(w.v, torch.bfloat16), _t(w.log_alpha), _t(dout, torch.bfloat16),
+                                              s0=_t(w.s0), chunk=c)
+    torch.cuda.synchronize()
+    ref = orc.gla_backward(w.q, w.k, w.v, w.log_alpha, dout, s0=w.s0)
+    for name, got, r in (("dq", dq, ref[0]), ("dk", dk_, ref[1]), ("dv", dv_, ref[2]), ("ds0", ds0, ref[4])):
+        _gate(f"gla backward strong gates {gates} {shape} {name}", got.float().cpu().numpy().astype(np.float64), r,
+              absolute=np.inf)
