@@ -20,7 +20,8 @@ causal tiles of each chunk (and the hardware's own MFMA counters when recorded);
 ``cpu_baseline`` times the fp64 oracle on the host's cores; ``others`` reports the other
 chunked workloads (retention B4 H8 T2048, GLA and the scalar data-dependent decay at B8
 H16 T4096) each with its own roofline, decode (per-channel gate, gated delta rule), the
-gated delta rule with its feature map and output norm fused in, the backward of
+gated delta rule with its feature map and output norm fused in, GLA with its output
+LayerNorm fused in (each beside the unfused torch form), the backward of
 retention, the scalar decay and GLA (beside their forward), and variational linear
 attention (whole sequences, and decode).
 
@@ -295,6 +296,13 @@ def bench_gdelta_decode(steps_total, torch, api, synthetic, dev):
                 alg_bytes_per_step=bytes_step)
 
 
+def time_pair(fused, unfused, steps, warmup, torch):
+    """Kernel ms of a fused call and of its unfused form: both warmed first (whichever is timed
+    first would otherwise also pay for the clocks ramping up), then each timed."""
+    time_calls([fused, unfused], 2 * warmup, 2 * warmup, torch)
+    return time_calls([fused], steps, warmup, torch)[1], time_calls([unfused], steps, warmup, torch)[1]
+
+
 def bench_gdelta_fused(steps, warmup, torch, api, synthetic, dev):
     """The gated-delta workload from the projections before DeltaNet's feature map, with the
     RMS output norm, through gdelta_chunk_fwd_fused; beside it the same computation with the
@@ -320,9 +328,35 @@ def bench_gdelta_fused(steps, warmup, torch, api, synthetic, dev):
         of = o.float()
         return (of * torch.rsqrt(of.pow(2).mean(-1, keepdim=True) + 1e-6) * weight).to(torch.bfloat16)
 
-    ms_f = time_calls([fused], steps, warmup, torch)[1]
-    ms_u = time_calls([unfused], steps, warmup, torch)[1]
+    ms_f, ms_u = time_pair(fused, unfused, steps, warmup, torch)
     return dict(workload="gdelta_fused_b4h16_t8192_d128", kernel_ms=ms_f, unfused_torch_ms=ms_u,
+                tokens_per_s=B * H * T / (ms_f * 1e-3), speedup_vs_unfused=ms_u / ms_f)
+
+
+def bench_gla_layernorm(steps, warmup, torch, api, synthetic, dev):
+    """The GLA workload (B8 H16 T4096 d128) with its output LayerNorm fused into the output
+    pass (gla_chunk_fwd_fused); beside it gla_chunk_fwd followed by torch's layer_norm on o."""
+    name = "gla_b8h16_t4096_d128"
+    c = synthetic.CONFIGS[name]
+    B, H, T, d = c["B"], c["H"], c["T"], c["dk"]
+    b = upload(synthetic.config_inputs(name), torch, dev)
+    weight = torch.linspace(0.5, 1.5, d, device=dev)
+    bias = torch.linspace(-0.2, 0.2, d, device=dev)
+    ws = torch.empty(max(api.workspace_size("gla", B, H, T, d, d, 64), 16), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+    s_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    F = torch.nn.functional
+
+    def fused():
+        api.gla_chunk_fwd_fused(b["q"], b["k"], b["v"], b["log_alpha"], weight, o_norm_bias=bias, o_norm_eps=1e-5,
+                                chunk=64, o=o, s_out=s_out, workspace=ws)
+
+    def unfused():
+        api.gla_chunk_fwd(b["q"], b["k"], b["v"], b["log_alpha"], chunk=64, o=o, s_out=s_out, workspace=ws)
+        return F.layer_norm(o.float(), (d,), weight, bias, 1e-5).to(torch.bfloat16)
+
+    ms_f, ms_u = time_pair(fused, unfused, steps, warmup, torch)
+    return dict(workload="gla_layernorm_b8h16_t4096_d128", kernel_ms=ms_f, unfused_torch_ms=ms_u,
                 tokens_per_s=B * H * T / (ms_f * 1e-3), speedup_vs_unfused=ms_u / ms_f)
 
 
@@ -795,6 +829,10 @@ def main():
         others["gdelta_fused_b4h16_t8192_d128"] = bench_gdelta_fused(max(20, args.steps // 4),
                                                                      max(3, args.warmup // 4), torch, api,
                                                                      synthetic, dev)
+        torch.cuda.empty_cache()
+        others["gla_layernorm_b8h16_t4096_d128"] = bench_gla_layernorm(max(20, args.steps // 4),
+                                                                       max(3, args.warmup // 4), torch, api,
+                                                                       synthetic, dev)
         torch.cuda.empty_cache()
         others["gdelta_decode_n512h32_d128"] = bench_gdelta_decode(min(args.decode_steps, 200), torch, api,
                                                                    synthetic, dev)

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libglr.so")
 LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
 LA_RETENTION, LA_GLA, LA_GDELTA, LA_MAMBA2, LA_GDELTA_FUSED = 0, 1, 2, 3, 4
-LA_FUSE_QK_SILU_L2, LA_FUSE_OUT_RMSNORM = 1, 2
+LA_FUSE_QK_SILU_L2, LA_FUSE_OUT_RMSNORM, LA_FUSE_OUT_LAYERNORM = 1, 2, 4
 LA_VLA_RATIO, LA_VLA_LINEAR = 0, 1
 
 EXPORTED = (
@@ -22,6 +22,7 @@ EXPORTED = (
     "gla_chunk_fwd",
     "gdelta_chunk_fwd",
     "gdelta_chunk_fwd_fused",
+    "gla_chunk_fwd_fused",
     "gdelta_chunk_fwd_noalloc",
     "la_recurrent_step",
     "gdelta_recurrent_step",
@@ -66,6 +67,7 @@ def load():
     lib.gdelta_chunk_fwd.argtypes = [P, P, P, F, F, F, P, F, I, I, I, I, I, I, I, P, Z, P]
     lib.gdelta_chunk_fwd_fused.argtypes = [P, P, P, F, F, F, P, F, F, ctypes.c_float, I,
                                            I, I, I, I, I, I, I, P, Z, P]
+    lib.gla_chunk_fwd_fused.argtypes = [P, P, P, F, F, P, F, F, F, ctypes.c_float, I, I, I, I, I, I, I, I, P, Z, P]
     lib.gdelta_chunk_fwd_noalloc.argtypes = [P, P, P, F, F, F, P, F, I, I, I, I, I, I, I, P]
     lib.la_chunk_workspace_size.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.la_chunk_workspace_size.restype = ctypes.c_int
@@ -82,7 +84,7 @@ def load():
     lib.vla_fwd.argtypes = [P, P, P, P, ctypes.c_float, F, F, F, P, F, F, F, I, I, I, I, I, I, I, P]
     lib.vla_recurrent_step.argtypes = [P, P, P, P, F, F, F, P, I, I, I, I, I, I, P]
     for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-                 "gdelta_chunk_fwd_noalloc", "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "vla_fwd",
+                 "gdelta_chunk_fwd_noalloc", "gla_chunk_fwd_fused", "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "vla_fwd",
                  "vla_recurrent_step"):
         getattr(lib, name).restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]

@@ -13,7 +13,7 @@ import torch
 from . import _native
 
 __all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-           "gdelta_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "gdelta_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "gla_chunk_fwd_fused",
            "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step",
            "vla_fwd", "vla_recurrent_step", "workspace_size", "bwd_workspace_size"]
 
@@ -148,6 +148,26 @@ def gdelta_chunk_fwd(q, k, v, log_alpha, beta, chunk=64, s0=None, o=None, s_out=
     _native.check(lib.gdelta_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0),
                                        _ptr(o), _ptr(s_out), B, H, T, dk, dv, chunk, _dtype_code(q),
                                        _ptr(ws), ws_bytes, _stream(q.device)))
+    return o, s_out
+
+
+def gla_chunk_fwd_fused(q, k, v, log_alpha, o_norm_weight, o_norm_bias=None, o_norm_eps=1e-5, chunk=64, s0=None,
+                        o=None, s_out=None, return_state=True, workspace=None):
+    """gla_chunk_fwd with GLA's output LayerNorm fused in: every output row (d_v values)
+    centred, divided by sqrt(var + o_norm_eps), times ``o_norm_weight`` [d_v] fp32 plus
+    ``o_norm_bias`` [d_v] fp32 (None: no shift). Returns (o, s_out); s_out is the memory."""
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
+    _require(log_alpha, "log_alpha", (B, H, T, dk), torch.float32, q.device)
+    _require(o_norm_weight, "o_norm_weight", (dv,), torch.float32, q.device)
+    if o_norm_bias is not None:
+        _require(o_norm_bias, "o_norm_bias", (dv,), torch.float32, q.device)
+    ws, ws_bytes = _workspace(_native.LA_GLA, dims, chunk, q, workspace)
+    lib = _native.load()
+    _native.check(lib.gla_chunk_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(s0), _ptr(o), _ptr(s_out),
+                                          _ptr(o_norm_weight), _ptr(o_norm_bias), float(o_norm_eps),
+                                          _native.LA_FUSE_OUT_LAYERNORM, B, H, T, dk, dv, chunk, _dtype_code(q),
+                                          _ptr(ws), ws_bytes, _stream(q.device)))
     return o, s_out
 
 

@@ -224,6 +224,26 @@ void rms_rows_f32(float* __restrict__ o, const float* __restrict__ w, float eps,
     for (int c = lane; c < dv; c += 64) r[c] = r[c] * w[c] * inv;
 }
 
+// Layer norm of each output row (GLA's fused epilogue in fp32): one wave per row, the mean
+// and then the squared deviations by shuffles.
+__global__ __launch_bounds__(256)
+void layernorm_rows_f32(float* __restrict__ o, const float* __restrict__ w, const float* __restrict__ b, float eps,
+                        int64_t rows, int dv) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    float* r = o + row * dv;
+    float s = 0.f;
+    for (int c = lane; c < dv; c += 64) s += r[c];
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    const float mean = s / static_cast<float>(dv);
+    float ss = 0.f;
+    for (int c = lane; c < dv; c += 64) ss += (r[c] - mean) * (r[c] - mean);
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.f / sqrtf(ss / static_cast<float>(dv) + eps);
+    for (int c = lane; c < dv; c += 64) r[c] = (r[c] - mean) * inv * w[c] + (b ? b[c] : 0.f);
+}
+
 template <int VARIANT, int C, int DK>
 hipError_t launch_dk(const ChunkArgs& a, hipStream_t stream) {
     const float* q = static_cast<const float*>(a.q);
@@ -242,9 +262,13 @@ hipError_t launch_dk(const ChunkArgs& a, hipStream_t stream) {
     }
     hipError_t err = hipGetLastError();
     const int64_t rows = static_cast<int64_t>(bh) * a.T;
-    if (err != hipSuccess || !(a.fuse & 2) || rows == 0) return err;
-    hipLaunchKernelGGL(rms_rows_f32, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream, o, a.onw,
-                       a.oeps, rows, a.dv);
+    if (err != hipSuccess || !(a.fuse & 6) || rows == 0) return err;
+    if (a.fuse & 4)
+        hipLaunchKernelGGL(layernorm_rows_f32, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream, o,
+                           a.onw, a.onb, a.oeps, rows, a.dv);
+    else
+        hipLaunchKernelGGL(rms_rows_f32, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream, o, a.onw,
+                           a.oeps, rows, a.dv);
     return hipGetLastError();
 }
 

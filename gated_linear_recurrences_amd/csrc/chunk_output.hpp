@@ -49,6 +49,12 @@ struct OutParams {
     const u16* states;   // [BH][NC][DV][DK] memory entering each chunk
     u16* o;              // [BH][T][DV]
     int H, T, NC;
+    // GLA's output norm fused in (off when lnw is null): every row of o centred on its mean
+    // over the d_v values, divided by sqrt(variance + lneps), times lnw [DV] plus lnb [DV]
+    // (lnb may be null)
+    const float* lnw;
+    const float* lnb;
+    float lneps;
 };
 
 template <int C, int DK, int DV, int GK>
@@ -75,7 +81,10 @@ struct OutLayout {
     static constexpr int oP = oV + al(C * VS * 2);
     static constexpr int oF = oP + al(C * PS * 2);                  // F = e^(r_it - r_jt), jt < it
     static constexpr int oR = oF + (GLA ? al(NF * DK * 4 + 16) : 0);  // R = e^(r_it)
-    static constexpr int endX = oR + (GLA ? al(CT * DK * 4) : 0);
+    static constexpr int oL = oR + (GLA ? al(CT * DK * 4) : 0);    // output-norm row statistics
+    static constexpr int NPV = DV >= 32 ? DV / 32 : 1;
+    static constexpr int LSTAT = C * NPV * 2;                        // floats: (mean, M2) per row and part
+    static constexpr int endX = oL + (GLA ? al(LSTAT * 4) : 0);
     static constexpr int endG = oX + (GLA ? al(C * BS * 4) : 0);
     static constexpr int oS = endX;                                  // scalar: cumulative gates G
     static constexpr int endS = oS + (SCL ? al(C * 4) : 0);
@@ -107,6 +116,7 @@ void output_kernel(OutParams p) {
     float* const sR = reinterpret_cast<float*>(smem + Lay::oR);
     float* const sB = reinterpret_cast<float*>(smem + Lay::oX);
     float* const sGs = reinterpret_cast<float*>(smem + Lay::oS);
+    float* const sL = reinterpret_cast<float*>(smem + Lay::oL);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,6 +174,22 @@ void output_kernel(OutParams p) {
             const int col = 32 * kb + 8 * g;
             sa[tt][kb] = (col < DK && (DV >= 32 || tt == 0))
                              ? *reinterpret_cast<const u16x8*>(sc + static_cast<unsigned>(vrow * DK + col)) : z8;
+        }
+    }
+
+    // GLA's output norm: its weight and bias at this wave's channels 32pp + 16tt + 4g + e
+    // (the same for every output round), requested with the other global loads
+    const bool ln = GLA && p.lnw != nullptr;
+    constexpr int NT2 = DV >= 32 ? 2 : 1;
+    f32x4 lw[2] = {zf4(), zf4()}, lbv[2] = {zf4(), zf4()};
+    if constexpr (GLA) {
+        if (ln) {
+#pragma unroll
+            for (int tt = 0; tt < NT2; ++tt) {
+                const int c4 = (DV >= 32 ? 32 * pp + 16 * tt : 0) + 4 * g;
+                lw[tt] = ldf4(p.lnw + c4);
+                if (p.lnb) lbv[tt] = ldf4(p.lnb + c4);
+            }
         }
     }
 
@@ -359,9 +385,29 @@ void output_kernel(OutParams p) {
     }
     lds_barrier();
 
-    // ---- outputs: readout of S_in plus P V, items (row tile it, value pair pp)
-    for (int item = w; item < CT * NP; item += NW) {
-        const int it = item / NP;
+    // ---- outputs: readout of S_in plus P V, items (row tile it, value pair pp), in rounds of
+    // NW items; the NP items of one row tile fall in one round. With GLA's output norm fused
+    // in, every round's rows are kept in registers, each wave writes its rows' partial
+    // statistics (mean and sum of squared deviations over its channels) to LDS, and after
+    // one barrier every wave normalises and stores its rows
+    constexpr int NITEM = CT * NP, ROUNDS = (NITEM + NW - 1) / NW;
+    f32x4 keep[GLA ? ROUNDS : 1][2];
+    auto store_rows = [&](int i, const f32x4* o2) __attribute__((always_inline)) {
+        // lane holds o[i][32pp + 16tt + 4g + r]
+        u16* orow = p.o + (tok0 + i) * DV;
+        if constexpr (DV >= 32) {
+            st4(orow + 32 * pp + 4 * g, cvt4(o2[0]));
+            st4(orow + 32 * pp + 16 + 4 * g, cvt4(o2[1]));
+        } else {
+            st4(orow + 4 * g, cvt4(o2[0]));
+        }
+    };
+#pragma unroll
+    for (int round = 0; round < ROUNDS; ++round) {
+        const int item = round * NW + w;
+        if (!ln && item >= NITEM) break;
+        const bool act = item < NITEM;
+        const int it = act ? item / NP : 0;
         const int i = 16 * it + r16;
         const float oscale = GLA ? 1.f : SCL ? ex2(sGs[i]) : ex2(static_cast<float>(i + 1) * lg2);
         bf16x8 qb[KB];
@@ -408,14 +454,60 @@ void output_kernel(OutParams p) {
             }
             o2[tt] = acc;
         }
-        if (i < n) {
-            // lane holds o[i][32pp + 16tt + 4g + r]
-            u16* orow = p.o + (tok0 + i) * DV;
-            if constexpr (DV >= 32) {
-                st4(orow + 32 * pp + 4 * g, cvt4(o2[0]));
-                st4(orow + 32 * pp + 16 + 4 * g, cvt4(o2[1]));
-            } else {
-                st4(orow + 4 * g, cvt4(o2[0]));
+        if constexpr (GLA) {
+            if (ln) {
+                constexpr int CH = 16 * NT2;
+                float sum = 0.f;
+#pragma unroll
+                for (int tt = 0; tt < NT2; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum += o2[tt][e];
+                sum += __shfl_xor(sum, 16, 64);
+                sum += __shfl_xor(sum, 32, 64);
+                const float mp = sum * (1.f / CH);
+                float m2 = 0.f;
+#pragma unroll
+                for (int tt = 0; tt < NT2; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m2 += (o2[tt][e] - mp) * (o2[tt][e] - mp);
+                m2 += __shfl_xor(m2, 16, 64);
+                m2 += __shfl_xor(m2, 32, 64);
+                if (act && g == 0) {
+                    sL[(i * NP + pp) * 2] = mp;
+                    sL[(i * NP + pp) * 2 + 1] = m2;
+                }
+                keep[round][0] = o2[0];
+                keep[round][1] = o2[1];
+                continue;
+            }
+        }
+        if (act && i < n) store_rows(i, o2);
+    }
+    if constexpr (GLA) {
+        if (ln) {
+            lds_barrier();
+#pragma unroll
+            for (int round = 0; round < ROUNDS; ++round) {
+                const int item = round * NW + w;
+                const int i = 16 * (item / NP) + r16;
+                if (item < NITEM && i < n) {
+                    constexpr int CH = 16 * NT2;
+                    float mean = 0.f;
+#pragma unroll
+                    for (int q2 = 0; q2 < NP; ++q2) mean += sL[(i * NP + q2) * 2];
+                    mean *= 1.f / NP;
+                    float tot = 0.f;
+#pragma unroll
+                    for (int q2 = 0; q2 < NP; ++q2) {
+                        const float dm = sL[(i * NP + q2) * 2] - mean;
+                        tot += sL[(i * NP + q2) * 2 + 1] + CH * dm * dm;
+                    }
+                    const float rstd = 1.f / sqrtf(tot * (1.f / DV) + p.lneps);
+                    f32x4 o2[2];
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) o2[tt] = (keep[round][tt] - mean) * rstd * lw[tt] + lbv[tt];
+                    store_rows(i, o2);
+                }
             }
         }
     }

@@ -90,6 +90,9 @@ hipError_t launch_two_pass_dv(const ChunkArgs& a, hipStream_t stream) {
     p.H = a.H;
     p.T = a.T;
     p.NC = NC;
+    p.lnw = (a.fuse & 4) ? a.onw : nullptr;
+    p.lnb = (a.fuse & 4) ? a.onb : nullptr;
+    p.lneps = a.oeps;
     // four waves for the scalar gates (two or three workgroups per CU), eight for GLA,
     // whose larger LDS footprint allows two workgroups per CU
     constexpr int NW = GK == kGateChannel ? 8 : 4;

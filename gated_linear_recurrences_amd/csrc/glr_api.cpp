@@ -169,6 +169,24 @@ la_status gdelta_chunk_fwd_fused(const void* q, const void* k, const void* v, co
     return run_chunk(glr::kGDelta, a, dtype, workspace_bytes, stream);
 }
 
+la_status gla_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* s0, void* o, float* s_out, const float* o_norm_weight,
+                              const float* o_norm_bias, float o_norm_eps, int fuse, int B, int H, int T, int dk,
+                              int dv, int chunk, la_dtype dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    if (fuse & ~LA_FUSE_OUT_LAYERNORM) return fail(LA_ERR_INVALID, "%s", "unknown or unsupported fuse flag for GLA");
+    if (fuse & LA_FUSE_OUT_LAYERNORM) {
+        const bool rows = B > 0 && H > 0 && T > 0;
+        la_status st = check_ptr(o_norm_weight, rows, false, "o_norm_weight");
+        if (st != LA_OK) return st;
+        if ((st = check_ptr(o_norm_bias, rows, true, "o_norm_bias")) != LA_OK) return st;
+        if (!(o_norm_eps >= 0.f)) return fail(LA_ERR_INVALID, "%s", "o_norm_eps must be >= 0");
+    }
+    glr::ChunkArgs a{q, k, v, log_alpha, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk, workspace,
+                     fuse, o_norm_weight, o_norm_eps, o_norm_bias};
+    return run_chunk(glr::kGLA, a, dtype, workspace_bytes, stream);
+}
+
 static la_status run_bwd(glr::Variant variant, const glr::BwdArgs& a, la_dtype dtype, size_t ws_bytes,
                          void* stream) {
     // the forward's checks on q, k, v, the gate and the dimensions (o stands for the gradients)
@@ -381,6 +399,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (3 << 16) | 1; }
+int la_version(void) { return (3 << 16) | 2; }
 
 }  // extern "C"

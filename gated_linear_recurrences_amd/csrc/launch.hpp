@@ -27,11 +27,14 @@ struct ChunkArgs {
     float* s_out;        // [B,H,dv,dk] or nullptr
     int B, H, T, dk, dv, chunk;
     void* ws;            // device workspace of at least chunk_workspace_bytes() bytes
-    // gated delta rule only: bit 0 - q, k are mapped by SiLU then L2 normalisation per token
-    // on load; bit 1 - each output row is RMS-normalised with weight onw [dv] and eps oeps
+    // gated delta rule: bit 0 - q, k are mapped by SiLU then L2 normalisation per token on
+    // load; bit 1 - each output row is RMS-normalised with weight onw [dv] and eps oeps.
+    // GLA: bit 2 - each output row is layer-normalised (mean 0, variance 1 with eps oeps),
+    // times onw [dv] plus onb [dv] (onb may be null)
     int fuse;
     const float* onw;
     float oeps;
+    const float* onb;
 };
 
 struct DecodeArgs {

@@ -77,7 +77,8 @@ typedef enum la_dtype {
 
 typedef enum la_fuse {
     LA_FUSE_QK_SILU_L2 = 1,    /* q, k are mapped by SiLU then unit L2 norm per token on load */
-    LA_FUSE_OUT_RMSNORM = 2    /* each output row is RMS-normalised and weighted */
+    LA_FUSE_OUT_RMSNORM = 2,   /* each output row is RMS-normalised and weighted */
+    LA_FUSE_OUT_LAYERNORM = 4  /* each output row is layer-normalised, weighted and shifted */
 } la_fuse;
 
 typedef enum la_vla_readout {
@@ -237,6 +238,26 @@ la_status gdelta_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
                                    la_dtype dtype, void* stream);
 
 /*
+ * gla_chunk_fwd with GLA's output norm fused in (the gates page, section
+ * "Correggere: la delta rule", names a LayerNorm as GLA's output norm, beside
+ * DeltaNet's RMS norm).  With fuse = LA_FUSE_OUT_LAYERNORM every output row o
+ * (d_v values of one token and head) becomes
+ *     (o - mean(o)) / sqrt(var(o) + o_norm_eps) * o_norm_weight + o_norm_bias,
+ * var the mean squared deviation over the d_v values, in fp32, before o is
+ * stored; o_norm_weight [d_v] float32 is required, o_norm_bias [d_v] float32
+ * may be NULL (no shift), o_norm_eps >= 0.  For bf16 storage the output pass
+ * normalises each row while it holds it (no extra pass over o); fp32 storage
+ * normalises the stored rows in one more pass.  s_out is the memory itself.
+ * fuse == 0 is gla_chunk_fwd; any other flag is LA_ERR_INVALID.  Workspace,
+ * other arguments, errors and the gate bound as for gla_chunk_fwd.
+ */
+la_status gla_chunk_fwd_fused(const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* s0, void* o, float* s_out,
+                              const float* o_norm_weight, const float* o_norm_bias, float o_norm_eps,
+                              int fuse, int B, int H, int T, int dk, int dv, int chunk,
+                              la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode token for N sequences x H heads with a per-key-channel gate (the
  * recurrent form of the RetNet page, section on retention: the same two
  * gestures for every token at constant memory; a fixed decay is the constant
@@ -372,7 +393,7 @@ const char* la_last_error(void);
  * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step; 2.6: gla_chunk_bwd;
  * 2.7: single-pass retention and scalar-decay forward, no workspace at B * H * d_v / 16 >= 128;
  * 3.0: vla_fwd and vla_recurrent_step take the readout and the denominator vector;
- * 3.1: gdelta_chunk_fwd_noalloc). */
+ * 3.1: gdelta_chunk_fwd_noalloc; 3.2: gla_chunk_fwd_fused). */
 int la_version(void);
 
 #ifdef __cplusplus

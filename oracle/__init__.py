@@ -41,6 +41,7 @@ from .glr_oracle import (  # noqa: F401
     gdelta_decode_step,
     silu_l2,
     rms_norm,
+    layer_norm,
     scalar_backward,
     retention_backward,
     gla_backward,

@@ -63,6 +63,7 @@ __all__ = [
     "gdelta_decode_step",
     "silu_l2",
     "rms_norm",
+    "layer_norm",
     "scalar_backward",
     "retention_backward",
     "forward_substitution",
@@ -497,6 +498,20 @@ def rms_norm(o, weight, eps):
     o = np.asarray(o, dtype=np.float64)
     w = np.asarray(weight, dtype=np.float64)
     return o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps) * w
+
+
+def layer_norm(o, weight, bias, eps):
+    """The output normalisation the gates page names for GLA (section "Correggere: la delta
+    rule", beside DeltaNet's RMS norm): each output row centred on its mean over the value
+    channels and divided by its standard deviation, ``(o - mean) / sqrt(var + eps)``, with
+    ``var`` the mean squared deviation (the population variance), then scaled and shifted
+    per channel by ``weight`` and ``bias`` (``bias=None``: no shift)."""
+    o = np.asarray(o, dtype=np.float64)
+    mean = np.mean(o, axis=-1, keepdims=True)
+    dev = o - mean
+    var = np.mean(dev * dev, axis=-1, keepdims=True)
+    y = dev / np.sqrt(var + eps) * np.asarray(weight, dtype=np.float64)
+    return y if bias is None else y + np.asarray(bias, dtype=np.float64)
 
 
 # --------------------------------------------------------------------------- backward (reverse mode)

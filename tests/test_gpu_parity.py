@@ -336,6 +336,48 @@ def test_gdelta_fused_full_size_parity():
                   "fused full size", normed=True)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("shape", FUSED_SHAPES)
+def test_gla_layernorm_fused_parity(shape, bias, dtype):
+    """GLA with its output LayerNorm fused in against the oracle's layer_norm of the GLA
+    chunkwise output (fp64), under the same gates as the plain forward (relative bound for
+    the normalised rows); the memory is untouched by the norm."""
+    B, H, T, dk, dv, c = shape
+    w = synthetic.gla_inputs(B, H, T, dk, dv, chunk=c, dtype=dtype, seed=700 + sum(shape), with_state=True)
+    rng = np.random.default_rng(sum(shape) + 1)
+    weight = rng.uniform(0.5, 1.5, dv).astype(np.float32)
+    b = rng.standard_normal(dv).astype(np.float32) * 0.5 if bias else None
+    st = _storage(w)
+    out, S = api.gla_chunk_fwd_fused(_t(w.q, st), _t(w.k, st), _t(w.v, st), _t(w.log_alpha), _t(weight),
+                                     o_norm_bias=_t(b) if bias else None, o_norm_eps=1e-5, chunk=c, s0=_t(w.s0))
+    torch.cuda.synchronize()
+    o_gla, S_ref = orc.gla_chunkwise(w.q, w.k, w.v, w.log_alpha, c, s0=w.s0)
+    o_ref = orc.layer_norm(o_gla, weight, b, 1e-5)
+    assert_parity(w, out.float().cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64), o_ref, S_ref,
+                  f"gla layernorm bias={bias} {dtype} {shape}", normed=True)
+
+
+def test_gla_layernorm_fused_full_size_parity():
+    """The GLA workload's shape (B8 H16 T4096, d 128) with the LayerNorm fused in: the
+    oracle's chunkwise output on 8 of the 128 sequences (one per batch entry, head h = b),
+    then layer_norm."""
+    w = synthetic.config_inputs("gla_b8h16_t4096_d128")
+    rng = np.random.default_rng(3)
+    weight = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    b = rng.standard_normal(128).astype(np.float32) * 0.5
+    out, S = api.gla_chunk_fwd_fused(_t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16),
+                                     _t(w.log_alpha), _t(weight), o_norm_bias=_t(b), o_norm_eps=1e-5, chunk=64)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    S = S.cpu().numpy().astype(np.float64)
+    for bi in range(8):
+        sl = (slice(bi, bi + 1), slice(bi, bi + 1))
+        o_gla, S_ref = orc.gla_chunkwise(w.q[sl], w.k[sl], w.v[sl], w.log_alpha[sl], 64)
+        assert_parity(w, o[sl], S[sl], orc.layer_norm(o_gla, weight, b, 1e-5), S_ref,
+                      f"gla layernorm full size sequence {bi}", normed=True)
+
+
 # ----------------------------------------------------------------------------- backward
 
 BWD_SHAPES = [(1, 2, 100, 16, 16, 16), (2, 1, 77, 32, 64, 32), (1, 2, 130, 64, 32, 64), (2, 2, 200, 128, 128, 64),

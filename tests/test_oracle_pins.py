@@ -265,6 +265,33 @@ def test_silu_l2_and_rms_norm():
     np.testing.assert_allclose(orc.rms_norm(tiny, np.ones(32), 1e-6), tiny / np.sqrt(1e-8 + 1e-6), rtol=1e-13)
 
 
+def test_layer_norm():
+    """GLA's output norm against its definition: a hand-worked row (x = 1, 2, 3, 4: mean 2.5,
+    population variance 1.25, so the normalised row is (x - 2.5) / sqrt(1.25)); with unit
+    weight, zero bias and eps = 0 every row has mean 0 and mean square 1; adding a constant
+    or multiplying by a positive factor leaves the row unchanged; a negative factor flips
+    its sign; weight and bias act channel by channel after the normalisation; a constant
+    row becomes the bias (its deviation is 0); eps enters as sqrt(var + eps)."""
+    y = orc.layer_norm(np.array([[1.0, 2.0, 3.0, 4.0]]), np.ones(4), None, 0.0)
+    np.testing.assert_allclose(y[0], np.array([-1.5, -0.5, 0.5, 1.5]) / np.sqrt(1.25), rtol=1e-14)
+    np.testing.assert_allclose(y[0], [-1.3416407864998738, -0.4472135954999579, 0.4472135954999579,
+                                      1.3416407864998738], rtol=1e-14)
+    rng = np.random.default_rng(18)
+    o = rng.standard_normal((4, 7, 64)) * 3.0 + 1.5
+    r = orc.layer_norm(o, np.ones(64), np.zeros(64), 0.0)
+    np.testing.assert_allclose(np.mean(r, axis=-1), 0.0, atol=1e-13)
+    np.testing.assert_allclose(np.mean(r * r, axis=-1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(orc.layer_norm(o + 7.0, np.ones(64), None, 0.0), r, atol=1e-12)
+    np.testing.assert_allclose(orc.layer_norm(0.25 * o, np.ones(64), None, 0.0), r, atol=1e-12)
+    np.testing.assert_allclose(orc.layer_norm(-2.0 * o, np.ones(64), None, 0.0), -r, atol=1e-12)
+    w, b = rng.uniform(0.5, 2.0, 64), rng.standard_normal(64)
+    np.testing.assert_allclose(orc.layer_norm(o, w, b, 0.0), r * w + b, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(orc.layer_norm(np.full((2, 64), 3.0), w, b, 1e-5), np.broadcast_to(b, (2, 64)),
+                               atol=1e-15)
+    x = np.array([[0.0, 2.0]])   # mean 1, variance 1
+    np.testing.assert_allclose(orc.layer_norm(x, np.ones(2), None, 3.0)[0], np.array([-1.0, 1.0]) / 2.0, rtol=1e-14)
+
+
 def test_transition_eigenvalues_and_norm():
     """The transition I - beta k k^T has eigenvalues 1 (d-1 times) and 1 - beta |k|^2; its
     spectral norm is exactly 1 when 0 <= beta |k|^2 <= 2; Gated DeltaNet scales it by
