@@ -43,6 +43,7 @@ from .glr_oracle import (  # noqa: F401
     rms_norm,
     layer_norm,
     scalar_backward,
+    gdelta_backward,
     retention_backward,
     gla_backward,
     vla_recurrent,

@@ -65,6 +65,7 @@ __all__ = [
     "rms_norm",
     "layer_norm",
     "scalar_backward",
+    "gdelta_backward",
     "retention_backward",
     "forward_substitution",
     "gla_backward",
@@ -543,6 +544,54 @@ def scalar_backward(q, k, v, log_alpha, do, dS_T=None, s0=None):
         dla[..., t] = a[..., t] * np.einsum("...mc,...mc->...", D, states[t])
         D = a[..., t][..., None, None] * D                            # through S_t = a_t S_{t-1} + ...
     return dq, dk, dv, dla, D
+
+
+def gdelta_backward(q, k, v, log_alpha, beta, do, dS_T=None, s0=None):
+    """Gradients of the gated delta rule by reverse-mode differentiation of its recurrent
+    form (the definition: "Scrivere meglio nella memoria", section "Unire oblio e
+    correzione: Gated DeltaNet"), token by token. Forward, per token: the fade
+    ``S' = a_t S_{t-1}``, the prediction ``e_t = S' k_t``, the write
+    ``u_t = beta_t (v_t - e_t)``, ``S_t = S' + u_t k_t^T`` and the readout ``o_t = S_t q_t``.
+    Backward, with D the gradient of the loss with respect to S_t (``dS_T`` after the last
+    token), each step taken in reverse order:
+    ``D += do_t q_t^T``, ``dq_t = S_t^T do_t``; through the write ``du_t = D k_t``,
+    ``dk_t = D^T u_t``; through ``u_t``: ``dbeta_t = du_t . (v_t - e_t)``,
+    ``dv_t = beta_t du_t``, ``de_t = -beta_t du_t``; through the prediction
+    ``dk_t += S'^T de_t`` and ``D' = D + de_t k_t^T`` (the gradient w.r.t. S'); through the
+    fade ``d log a_t = <D', S'>`` (Frobenius) and ``D = a_t D'`` for S_{t-1}.
+    Returns ``(dq, dk, dv, dlog_alpha, dbeta, ds0)``; ``do`` is ``[B, H, T, d_v]``."""
+    q, k, v, la, be, do = _f64(q, k, v, log_alpha, beta, do)
+    S0 = _init_state(q, v, s0)
+    T = q.shape[-2]
+    a = np.exp(la)
+    states = [S0]
+    S = S0
+    for t in range(T):
+        Sp = a[..., t][..., None, None] * S
+        u = be[..., t][..., None] * (v[..., t, :] - _read(Sp, k[..., t, :]))
+        S = Sp + _outer(u, k[..., t, :])
+        states.append(S)
+    D = np.zeros_like(S0) if dS_T is None else np.asarray(dS_T, dtype=np.float64).copy()
+    dq = np.zeros(q.shape); dk = np.zeros(k.shape); dv = np.zeros(v.shape)
+    dla = np.zeros(la.shape); dbe = np.zeros(be.shape)
+    for t in range(T - 1, -1, -1):
+        kt, vt, qt = k[..., t, :], v[..., t, :], q[..., t, :]
+        Sp = a[..., t][..., None, None] * states[t]
+        e = _read(Sp, kt)
+        u = be[..., t][..., None] * (vt - e)
+        D = D + _outer(do[..., t, :], qt)                            # now the gradient w.r.t. S_t
+        dq[..., t, :] = np.einsum("...mc,...m->...c", states[t + 1], do[..., t, :])
+        du = _read(D, kt)
+        dkt = np.einsum("...mc,...m->...c", D, u)
+        dbe[..., t] = np.sum(du * (vt - e), axis=-1)
+        dv[..., t, :] = be[..., t][..., None] * du
+        de = -be[..., t][..., None] * du
+        dkt = dkt + np.einsum("...mc,...m->...c", Sp, de)
+        dk[..., t, :] = dkt
+        D = D + _outer(de, kt)                                        # the gradient w.r.t. S'
+        dla[..., t] = np.einsum("...mc,...mc->...", D, Sp)
+        D = a[..., t][..., None, None] * D                            # through S' = a_t S_{t-1}
+    return dq, dk, dv, dla, dbe, D
 
 
 def gla_backward(q, k, v, log_alpha, do, dS_T=None, s0=None):

@@ -335,6 +335,65 @@ def test_backward_matches_finite_differences(kind):
         np.testing.assert_allclose(g, num, atol=1e-7, rtol=1e-6, err_msg=f"{kind} input {which}")
 
 
+def test_gdelta_backward_matches_finite_differences():
+    """Central differences of L = <W_o, o> + <W_s, S_T> through the gated delta rule's
+    recurrent form, against the reverse-mode gradients, for every element of q, k, v, log
+    alpha, beta and S_0 (tiny sizes, fp64; keys not normalised, so every term of the
+    transition is exercised)."""
+    rng = np.random.default_rng(43)
+    B, H, T, dk, dv = 1, 2, 5, 3, 2
+    q = rng.standard_normal((B, H, T, dk)); k = rng.standard_normal((B, H, T, dk)) * 0.7
+    v = rng.standard_normal((B, H, T, dv)); s0 = rng.standard_normal((B, H, dv, dk))
+    la = -np.logaddexp(0.0, -rng.standard_normal((B, H, T)))
+    be = rng.uniform(0.2, 0.9, (B, H, T))
+    W_o = rng.standard_normal((B, H, T, dv)); W_s = rng.standard_normal((B, H, dv, dk))
+    grads = orc.gdelta_backward(q, k, v, la, be, W_o, dS_T=W_s, s0=s0)
+    args = [q, k, v, la, be, s0]
+    fwd = lambda q, k, v, la, be, s: orc.gdelta_recurrent(q, k, v, la, be, s0=s)
+    eps = 1e-6
+    for which, g in enumerate(grads):
+        x = args[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            plus = [a.copy() for a in args]; minus = [a.copy() for a in args]
+            plus[which][idx] += eps; minus[which][idx] -= eps
+            num[idx] = (_loss(*fwd(*plus), W_o, W_s) - _loss(*fwd(*minus), W_o, W_s)) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-7, rtol=1e-6, err_msg=f"gdelta input {which}")
+
+
+def test_gdelta_backward_without_writes_is_the_scalar_fade():
+    """beta = 0: nothing is written (S_t = a_t S_{t-1}), which is the scalar decay with v = 0;
+    dq, d log a and dS_0 equal the scalar-decay gradients at v = 0, and dk, dv are zero."""
+    rng = np.random.default_rng(44)
+    B, H, T, dk, dv = 2, 2, 9, 4, 3
+    q = rng.standard_normal((B, H, T, dk)); k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv)); s0 = rng.standard_normal((B, H, dv, dk))
+    la = -np.logaddexp(0.0, -rng.standard_normal((B, H, T)))
+    do = rng.standard_normal((B, H, T, dv)); dS = rng.standard_normal((B, H, dv, dk))
+    gd = orc.gdelta_backward(q, k, v, la, np.zeros((B, H, T)), do, dS_T=dS, s0=s0)
+    sc = orc.scalar_backward(q, k, np.zeros_like(v), la, do, dS_T=dS, s0=s0)
+    np.testing.assert_allclose(gd[0], sc[0], atol=1e-12)      # dq
+    np.testing.assert_allclose(gd[3], sc[3], atol=1e-12)      # d log a
+    np.testing.assert_allclose(gd[5], sc[4], atol=1e-12)      # dS_0
+    np.testing.assert_array_equal(gd[1], 0.0)
+    np.testing.assert_array_equal(gd[2], 0.0)
+
+
+def test_gdelta_backward_gate_gradient_identity():
+    """S_0 enters the recurrence only through the first fade a_0 S_0, so scaling S_0 by e^eps
+    and shifting log a_0 by eps change the loss alike: d log a_0 = <dS_0, S_0> (Frobenius),
+    for any beta."""
+    rng = np.random.default_rng(45)
+    B, H, T, dk, dv = 1, 1, 6, 3, 2
+    q = rng.standard_normal((B, H, T, dk)); k = rng.standard_normal((B, H, T, dk)) * 0.6
+    v = rng.standard_normal((B, H, T, dv)); s0 = rng.standard_normal((B, H, dv, dk))
+    la = -np.logaddexp(0.0, -rng.standard_normal((B, H, T))); be = rng.uniform(0.1, 0.9, (B, H, T))
+    do = rng.standard_normal((B, H, T, dv))
+    grads = orc.gdelta_backward(q, k, v, la, be, do, s0=s0)
+    # at t = 0: scaling S_0 by e^eps is the same as shifting log a_0 by eps
+    np.testing.assert_allclose(grads[3][..., 0], np.sum(grads[5] * s0, axis=(-2, -1)), rtol=1e-10, atol=1e-12)
+
+
 def test_gate_gradient_identity():
     """The gate gradient from the rescaling argument: every term of o_t carries e^(B_t) and
     every term written at j carries e^(-B_j), so dL/dB_t = q_t . dq_t - k_t . dk_t (plus
