@@ -22,7 +22,7 @@ chunked workloads (retention B4 H8 T2048, GLA and the scalar data-dependent deca
 H16 T4096) each with its own roofline, decode (per-channel gate, gated delta rule), the
 gated delta rule with its feature map and output norm fused in, GLA with its output
 LayerNorm fused in (each beside the unfused torch form), the backward of
-retention, the scalar decay and GLA (beside their forward), and variational linear
+retention, the scalar decay, GLA and the gated delta rule (beside their forward), and variational linear
 attention (whole sequences, and decode).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-others] [--no-cpu]
@@ -429,9 +429,11 @@ def bench_vla_decode(steps_total, torch, api, synthetic, dev):
 
 
 def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
-    """Backward of a retention, scalar-decay or GLA workload (forward state pass, reverse state
-    pass, gradient pass, and for the first two a gate pass) with a seeded dO and ds_out; beside it
-    the forward of the same workload. Algorithmic flops per token-head 8Cd + 10d^2 (the two
+    """Backward of a retention, scalar-decay, GLA or gated-delta workload (forward state pass,
+    reverse state pass, gradient pass, and for the first two a gate pass; for the gated delta rule
+    also the chunk prep and maps) with a seeded dO and ds_out; beside it the forward of the same
+    workload. The flop count below is the decay variants'; for the gated delta rule it is a
+    lower bound. Algorithmic flops per token-head 8Cd + 10d^2 (the two
     state passes 2d^2 each; Q K^T, dO V^T, dO^T A1, Q^T A2, K^T A2^T 2Cd each over the
     C x C block; R K^T, R^T V^T, S_in^T dO^T 2d^2 each); bytes: read q, k, v, dO, write dq,
     dk, dv (7 d bf16 per token-head), the gates (GLA: read and their gradient written, 8 d
@@ -446,7 +448,12 @@ def bench_backward(name, steps, warmup, torch, api, synthetic, dev):
     dout = (torch.randn((B, H, T, d), generator=g, device=dev) / d ** 0.5).to(torch.bfloat16)
     ds_out = torch.randn((B, H, d, d), generator=g, device=dev) * 0.1
     ws = torch.empty(api.bwd_workspace_size(B, H, T, d, d, C), dtype=torch.uint8, device=dev)
-    if c["kind"] == "retention":
+    if c["kind"] == "gdelta":
+        ws = torch.empty(api.bwd_workspace_size(B, H, T, d, d, C, gdelta=True), dtype=torch.uint8, device=dev)
+        bwd = lambda: api.gdelta_chunk_bwd(b["q"], b["k"], b["v"], b["log_alpha"], b["beta"], dout, ds_out=ds_out,
+                                           chunk=C, workspace=ws)
+        gate_bytes = 16
+    elif c["kind"] == "retention":
         bwd = lambda: api.la_chunk_bwd(b["q"], b["k"], b["v"], b["log_gamma"], dout, ds_out=ds_out, chunk=C,
                                        workspace=ws)
         gate_bytes = 0
@@ -837,7 +844,8 @@ def main():
         others["gdelta_decode_n512h32_d128"] = bench_gdelta_decode(min(args.decode_steps, 200), torch, api,
                                                                    synthetic, dev)
         torch.cuda.empty_cache()
-        for name in ("retention_b4h8_t2048_d128", "mamba2_b8h16_t4096_d128", "gla_b8h16_t4096_d128"):
+        for name in ("retention_b4h8_t2048_d128", "mamba2_b8h16_t4096_d128", "gla_b8h16_t4096_d128",
+                     "gdelta_b4h16_t8192_d128"):
             others[name + "_bwd"] = bench_backward(name, max(20, args.steps // 4), max(3, args.warmup // 4), torch,
                                                    api, synthetic, dev)
             torch.cuda.empty_cache()

@@ -31,6 +31,8 @@ EXPORTED = (
     "mamba2_chunk_bwd",
     "gla_chunk_bwd_workspace_size",
     "gla_chunk_bwd",
+    "gdelta_chunk_bwd_workspace_size",
+    "gdelta_chunk_bwd",
     "vla_fwd",
     "vla_recurrent_step",
     "la_status_str",
@@ -79,12 +81,16 @@ def load():
     lib.gla_chunk_bwd.argtypes = bwd
     lib.gla_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.gla_chunk_bwd_workspace_size.restype = ctypes.c_int
+    lib.gdelta_chunk_bwd.argtypes = [P, P, P, F, F, F, P, F, P, P, P, F, F, F, I, I, I, I, I, I, I, P, Z, P]
+    lib.gdelta_chunk_bwd.restype = ctypes.c_int
+    lib.gdelta_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdelta_chunk_bwd_workspace_size.restype = ctypes.c_int
     lib.la_chunk_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.la_chunk_bwd_workspace_size.restype = ctypes.c_int
     lib.vla_fwd.argtypes = [P, P, P, P, ctypes.c_float, F, F, F, P, F, F, F, I, I, I, I, I, I, I, P]
     lib.vla_recurrent_step.argtypes = [P, P, P, P, F, F, F, P, I, I, I, I, I, I, P]
     for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-                 "gdelta_chunk_fwd_noalloc", "gla_chunk_fwd_fused", "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "vla_fwd",
+                 "gdelta_chunk_fwd_noalloc", "gla_chunk_fwd_fused", "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "gdelta_chunk_bwd", "vla_fwd",
                  "vla_recurrent_step"):
         getattr(lib, name).restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
@@ -114,11 +120,12 @@ def check(status):
         raise GLRError(status, f"{msg}: {detail}")
 
 
-def bwd_workspace_size(B, H, T, dk, dv, chunk, dtype, gla=False):
+def bwd_workspace_size(B, H, T, dk, dv, chunk, dtype, gla=False, gdelta=False):
     """Bytes of device workspace the backward entry points need for these sizes (``gla``:
-    gla_chunk_bwd's)."""
+    gla_chunk_bwd's; ``gdelta``: gdelta_chunk_bwd's)."""
     lib = load()
     out = ctypes.c_size_t(0)
-    fn = lib.gla_chunk_bwd_workspace_size if gla else lib.la_chunk_bwd_workspace_size
+    fn = (lib.gdelta_chunk_bwd_workspace_size if gdelta else
+          lib.gla_chunk_bwd_workspace_size if gla else lib.la_chunk_bwd_workspace_size)
     check(fn(B, H, T, dk, dv, chunk, dtype, ctypes.byref(out)))
     return out.value

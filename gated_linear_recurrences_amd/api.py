@@ -14,7 +14,7 @@ from . import _native
 
 __all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
            "gdelta_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "gla_chunk_fwd_fused",
-           "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step",
+           "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "gdelta_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step",
            "vla_fwd", "vla_recurrent_step", "workspace_size", "bwd_workspace_size"]
 
 
@@ -222,10 +222,11 @@ def workspace_size(kind, B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16):
     return _native.workspace_size(variant, B, H, T, dk, dv, chunk, code)
 
 
-def bwd_workspace_size(B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16, gla=False):
-    """Device workspace in bytes for la_chunk_bwd and mamba2_chunk_bwd (``gla``: gla_chunk_bwd)."""
+def bwd_workspace_size(B, H, T, dk, dv, chunk=64, dtype=torch.bfloat16, gla=False, gdelta=False):
+    """Device workspace in bytes for la_chunk_bwd and mamba2_chunk_bwd (``gla``: gla_chunk_bwd;
+    ``gdelta``: gdelta_chunk_bwd)."""
     code = _native.LA_BF16 if dtype == torch.bfloat16 else _native.LA_F32
-    return _native.bwd_workspace_size(B, H, T, dk, dv, chunk, code, gla)
+    return _native.bwd_workspace_size(B, H, T, dk, dv, chunk, code, gla, gdelta)
 
 
 def la_recurrent_step(q, k, v, alpha, s, o=None):
@@ -388,6 +389,32 @@ def gla_chunk_bwd(q, k, v, log_alpha, dout, s0=None, ds_out=None, chunk=64, want
     """Gradients of gla_chunk_fwd (bf16): returns (dq, dk, dv, dlog_alpha [B,H,T,d_k], ds0 or None)."""
     return _chunk_bwd(_native.load().gla_chunk_bwd, q, k, v, log_alpha, tuple(q.shape), dout, s0, ds_out, chunk,
                       want_ds0, workspace, gla=True)
+
+
+def gdelta_chunk_bwd(q, k, v, log_alpha, beta, dout, s0=None, ds_out=None, chunk=64, want_ds0=True, workspace=None):
+    """Gradients of gdelta_chunk_fwd (bf16): given dout = dL/do and optionally ds_out = dL/dS_T,
+    returns (dq, dk, dv, dlog_alpha [B,H,T], dbeta [B,H,T], ds0 or None)."""
+    dims, _, _ = _chunk_common(q, k, v, s0, dout, None, False)
+    B, H, T, dk, dv = dims
+    dev = q.device
+    _require(log_alpha, "log_alpha", (B, H, T), torch.float32, dev)
+    _require(beta, "beta", (B, H, T), torch.float32, dev)
+    if ds_out is not None:
+        _require(ds_out, "ds_out", (B, H, dv, dk), torch.float32, dev)
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dla = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dbe = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    ds0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if want_ds0 else None
+    need = bwd_workspace_size(B, H, T, dk, dv, chunk, q.dtype, gdelta=True)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    _native.check(_native.load().gdelta_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(s0), _ptr(dout), _ptr(ds_out), _ptr(dq),
+        _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dbe), _ptr(ds0), B, H, T, dk, dv, chunk, _dtype_code(q),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk_, dv_, dla, dbe, ds0
 
 
 def mamba2_chunk_bwd(q, k, v, log_alpha, dout, s0=None, ds_out=None, chunk=64, want_ds0=True, workspace=None):

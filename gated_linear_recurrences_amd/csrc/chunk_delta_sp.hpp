@@ -66,6 +66,7 @@ struct DspParams {
     float* s_out;         // [BH][DV][DK] or null
     u16* tu;              // [BH * NC][C][C]
     float* g;             // [BH * NC][C]
+    u16* tfull;           // [BH * NC][C][C] T = (I + A)^-1 itself (the backward's), or null
     // feature map fused in: the raw projections (q and k above then point at the mapped
     // copies the prep writes, [BH * NC][C][DK] each)
     const u16* qraw;
@@ -138,7 +139,8 @@ void delta_tfac_kernel(DspParams p) {
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
     // ---- stage k (rows past the end zero); cumulative gates and write strengths
-    static_assert(KP % NT == 0, "every lane holds whole pieces (the row map's shuffles need all lanes)");
+    // the feature map needs whole rows per aligned lane group (its shuffles need all lanes)
+    constexpr bool WHOLE = KP % NT == 0;
     u16x8 rk[KP_PER];
     const u16* kin = p.map ? p.kraw : p.k;
 #pragma unroll
@@ -148,7 +150,7 @@ void delta_tfac_kernel(DspParams p) {
         const unsigned off = (j < n) ? static_cast<unsigned>(j * DK + col) : 0u;
         rk[i] = *reinterpret_cast<const u16x8*>(kin + tok0 * DK + off);
     }
-    if (p.map) {
+    if (WHOLE && p.map) {
         // DeltaNet's feature map on k and q: a row's DK / 8 pieces sit in one aligned lane group
         u16* const km = p.kmap + chunk * C * DK;
         u16* const qm = p.qmap + chunk * C * DK;
@@ -180,7 +182,7 @@ void delta_tfac_kernel(DspParams p) {
     for (int i = 0; i < KP_PER; ++i) {
         const int idx = tid + i * NT;
         const int j = idx / (DK / 8), col = (idx % (DK / 8)) * 8;
-        *reinterpret_cast<u16x8*>(sK + j * KS + col) = (j < n) ? rk[i] : z8;
+        if (WHOLE || idx < KP) *reinterpret_cast<u16x8*>(sK + j * KS + col) = (j < n) ? rk[i] : z8;
     }
     lds_barrier();
 
@@ -259,6 +261,12 @@ void delta_tfac_kernel(DspParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 sT[(16 * i + 4 * g + r) * TS + 16 * w + r16] = __builtin_bit_cast(u16, static_cast<__bf16>(t[r] * fu));
+            if (p.tfull != nullptr) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p.tfull[chunk * C * C + (16 * i + 4 * g + r) * C + 16 * w + r16] =
+                        __builtin_bit_cast(u16, static_cast<__bf16>(t[r]));
+            }
         }
     }
     lds_barrier();

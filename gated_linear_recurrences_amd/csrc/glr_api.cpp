@@ -190,7 +190,7 @@ la_status gla_chunk_fwd_fused(const void* q, const void* k, const void* v, const
 static la_status run_bwd(glr::Variant variant, const glr::BwdArgs& a, la_dtype dtype, size_t ws_bytes,
                          void* stream) {
     // the forward's checks on q, k, v, the gate and the dimensions (o stands for the gradients)
-    glr::ChunkArgs f{a.q, a.k, a.v, a.gate, nullptr, a.s0, a.grad_q, nullptr, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
+    glr::ChunkArgs f{a.q, a.k, a.v, a.gate, a.beta, a.s0, a.grad_q, nullptr, a.B, a.H, a.T, a.dk, a.dv, a.chunk,
                      a.ws};
     la_status st = check_chunk_args(variant, f, dtype);
     if (st != LA_OK) return st;
@@ -201,6 +201,7 @@ static la_status run_bwd(glr::Variant variant, const glr::BwdArgs& a, la_dtype d
     if ((st = check_ptr(a.grad_k, tokens, false, "dk")) != LA_OK) return st;
     if ((st = check_ptr(a.grad_v, tokens, false, "dv")) != LA_OK) return st;
     if ((st = check_ptr(a.dgate, variant == glr::kRetention ? heads : tokens, false, "dgate")) != LA_OK) return st;
+    if (variant == glr::kGDelta && (st = check_ptr(a.dbeta, tokens, false, "dbeta")) != LA_OK) return st;
     if ((st = check_ptr(a.ds_out, heads, true, "ds_out")) != LA_OK) return st;
     if ((st = check_ptr(a.ds0, heads, true, "ds0")) != LA_OK) return st;
     const size_t need = glr::bwd_workspace_size(variant, a);
@@ -293,6 +294,20 @@ la_status la_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int c
 la_status gla_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
                                        size_t* bytes) {
     return bwd_workspace_query(glr::kGLA, B, H, T, dk, dv, chunk, dtype, bytes);
+}
+
+la_status gdelta_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                                          size_t* bytes) {
+    return bwd_workspace_query(glr::kGDelta, B, H, T, dk, dv, chunk, dtype, bytes);
+}
+
+la_status gdelta_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* beta,
+                           const float* s0, const void* dout, const float* ds_out, void* dq, void* dk_, void* dv_,
+                           float* dlog_alpha, float* dbeta, float* ds0, int B, int H, int T, int dk, int dv, int chunk,
+                           la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    glr::BwdArgs a{q, k, v, log_alpha, s0, dout, ds_out, dq, dk_, dv_, dlog_alpha, ds0, B, H, T, dk, dv, chunk,
+                   workspace, beta, dbeta};
+    return run_bwd(glr::kGDelta, a, dtype, workspace_bytes, stream);
 }
 
 la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float* log_gamma, const float* s0,
@@ -399,6 +414,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (3 << 16) | 2; }
+int la_version(void) { return (3 << 16) | 3; }
 
 }  // extern "C"

@@ -48,7 +48,8 @@ struct DecodeArgs {
     int N, H, dk, dv;
 };
 
-// Backward of the fixed, scalar or per-channel (GLA) decay (bf16 storage).
+// Backward of the fixed, scalar or per-channel (GLA) decay and of the gated delta rule (bf16
+// storage).
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -64,6 +65,8 @@ struct BwdArgs {
     float* ds0;           // [B,H,dv,dk] or nullptr
     int B, H, T, dk, dv, chunk;
     void* ws;             // device workspace of at least bwd_workspace_size() bytes
+    const float* beta;    // gated delta rule: write strengths [B,H,T]
+    float* dbeta;         // gated delta rule: their gradient [B,H,T]
 };
 size_t bwd_workspace_size(Variant variant, const BwdArgs& a);
 hipError_t launch_chunk_bwd(Variant variant, const BwdArgs& a, hipStream_t stream);

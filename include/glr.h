@@ -381,6 +381,34 @@ la_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float
                         int B, int H, int T, int dk, int dv, int chunk,
                         la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward of gdelta_chunk_fwd: reverse-mode gradients of the gated delta rule
+ * ("Scrivere meglio nella memoria", section "Unire oblio e correzione: Gated
+ * DeltaNet") for L = <dout, o> + <ds_out, s_out>, through the chunkwise UT form
+ * (section "Correggere: la delta rule").  Each chunk is a linear map of the
+ * memory entering it, so the memory's gradient is carried back through the
+ * chunks (chunk by chunk, like the forward's memory) and every chunk's input
+ * gradients then follow independently.  Inputs as for gdelta_chunk_fwd plus
+ * dout [B][H][T][d_v] (bf16) and ds_out [B][H][d_v][d_k] float32 (NULL: zero);
+ * outputs dq, dk [B][H][T][d_k] and dv [B][H][T][d_v] (bf16), dlog_alpha and
+ * dbeta [B][H][T] float32, and, if not NULL, ds0 [B][H][d_v][d_k] float32.
+ * The forward is not needed beforehand (its memory is recomputed).  Only
+ * LA_BF16 storage; chunk 16, 32 or 64.  The workspace size comes from
+ * gdelta_chunk_bwd_workspace_size: with N = B * H * ceil(T / chunk), C = chunk
+ * and a(x) as for la_chunk_bwd: 2 a(N*C*C*2) + a(N*C*4) (T_U, T, the gates),
+ * a(N*d_k*C*2) + 2 a(N*d_k*d_k*2) (each chunk's map), 3 a(N*d_v*d_k*2) (its
+ * write, the memory entering it and the gradient leaving it), and a scratch of
+ * a(min(N, 512) * (6 C d_k + 3 C d_v + 6 C^2 + d_k^2) * 4) bytes.  Other
+ * conventions and errors as for la_chunk_bwd.
+ */
+la_status gdelta_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
+                                          la_dtype dtype, size_t* bytes);
+la_status gdelta_chunk_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, const float* s0, const void* dout, const float* ds_out,
+                           void* dq, void* dk_, void* dv_, float* dlog_alpha, float* dbeta, float* ds0,
+                           int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* la_status_str(la_status status);
 
@@ -393,7 +421,7 @@ const char* la_last_error(void);
  * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step; 2.6: gla_chunk_bwd;
  * 2.7: single-pass retention and scalar-decay forward, no workspace at B * H * d_v / 16 >= 128;
  * 3.0: vla_fwd and vla_recurrent_step take the readout and the denominator vector;
- * 3.1: gdelta_chunk_fwd_noalloc; 3.2: gla_chunk_fwd_fused). */
+ * 3.1: gdelta_chunk_fwd_noalloc; 3.2: gla_chunk_fwd_fused; 3.3: gdelta_chunk_bwd). */
 int la_version(void);
 
 #ifdef __cplusplus

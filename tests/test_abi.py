@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 3        # 3.0: the VLA entry points take the readout and its denominator
-    assert lib.la_version() & 0xFFFF >= 2     # 3.1: gdelta_chunk_fwd_noalloc; 3.2: gla_chunk_fwd_fused
+    assert lib.la_version() & 0xFFFF >= 3     # 3.1: noalloc; 3.2: gla_chunk_fwd_fused; 3.3: gdelta_chunk_bwd
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -264,6 +264,43 @@ def test_backward_validation(lib):
             assert call(fn, T=0, gate=None) == _native.LA_ERR_INVALID
         assert call(fn, B=0, q=None, k=None, v=None, gate=None, dout=None, dq=None, dk=None, dv=None,
                     dgate=None, ws=None) == _native.LA_OK
+
+
+def test_gdelta_backward_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(ws_bytes=1 << 30, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, beta=FAKE, s0=None, dout=FAKE, ds_out=None, dq=FAKE, dk=FAKE,
+                 dv=FAKE, dgate=FAKE, dbeta=FAKE, ds0=None, B=1, H=1, T=8, dk_=16, dv_=16, chunk=16, dtype=1, ws=FAKE)
+        a.update(kw)
+        return lib.gdelta_chunk_bwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["gate"]), P(a["beta"]), P(a["s0"]),
+                                    P(a["dout"]), P(a["ds_out"]), P(a["dq"]), P(a["dk"]), P(a["dv"]), P(a["dgate"]),
+                                    P(a["dbeta"]), P(a["ds0"]), a["B"], a["H"], a["T"], a["dk_"], a["dv_"], a["chunk"],
+                                    a["dtype"], P(a["ws"]), ws_bytes, None)
+
+    assert call(dtype=0) == _native.LA_ERR_UNSUPPORTED
+    assert b"bf16" in lib.la_last_error()
+    assert call(beta=None) == _native.LA_ERR_INVALID
+    assert b"beta is NULL" in lib.la_last_error()
+    assert call(dbeta=None) == _native.LA_ERR_INVALID
+    assert b"dbeta is NULL" in lib.la_last_error()
+    assert call(dout=None) == _native.LA_ERR_INVALID
+    assert call(dgate=None) == _native.LA_ERR_INVALID
+    assert call(ds0=MISALIGNED) == _native.LA_ERR_INVALID
+    assert call(ws_bytes=16) == _native.LA_ERR_INVALID
+    assert b"workspace too small" in lib.la_last_error()
+    assert call(chunk=8) == _native.LA_ERR_UNSUPPORTED
+    assert call(B=0, q=None, k=None, v=None, gate=None, beta=None, dout=None, dq=None, dk=None, dv=None,
+                dgate=None, dbeta=None, ws=None) == _native.LA_OK
+    # the workspace formula of the header (C = 64, d = 128, N = 4 * 16 * 128 chunks)
+    def a256(x):
+        return (x + 255) // 256 * 256
+    need = ctypes.c_size_t(0)
+    assert lib.gdelta_chunk_bwd_workspace_size(4, 16, 8192, 128, 128, 64, 1, ctypes.byref(need)) == _native.LA_OK
+    N, C, d = 4 * 16 * 128, 64, 128
+    want = (2 * a256(N * C * C * 2) + a256(N * C * 4) + a256(N * d * C * 2) + 2 * a256(N * d * d * 2)
+            + 3 * a256(N * d * d * 2) + a256(min(N, 512) * (6 * C * d + 3 * C * d + 6 * C * C + d * d) * 4))
+    assert need.value == want
 
 
 def test_backward_workspace_size(lib):

@@ -455,6 +455,65 @@ def test_backward_parity(kind, shape, extras):
     _bwd_gate(f"{label} dgate", dg.cpu().numpy(), ref[3], floor=floor)
 
 
+def _gdelta_bwd(w, dout, ds_out, c, want_ds0=True):
+    q, k, v = _t(w.q, torch.bfloat16), _t(w.k, torch.bfloat16), _t(w.v, torch.bfloat16)
+    out = api.gdelta_chunk_bwd(q, k, v, _t(w.log_alpha), _t(w.beta), _t(dout, torch.bfloat16), s0=_t(w.s0),
+                               ds_out=_t(ds_out), chunk=c, want_ds0=want_ds0)
+    torch.cuda.synchronize()
+    return [None if x is None else x.float().cpu().numpy().astype(np.float64) for x in out]
+
+
+def _gdelta_gate_grads_gate(label, got, ref):
+    """d log alpha and dbeta are sums over the chunk's products that cancel: held to 2e-2 of
+    their L2 norm (relative), the per-element gradients' 1e-2 doubled for the extra products
+    (the triangular system's own gradient) that bf16 operands enter twice."""
+    err, scale = np.linalg.norm(got - ref), np.linalg.norm(ref)
+    msg = f"{label}: L2 err={err:.3e} L2 scale={scale:.3e}"
+    print(msg)
+    assert np.all(np.isfinite(got)), msg
+    assert err <= 2e-2 * max(scale, 1e-30), msg
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES)
+@pytest.mark.parametrize("extras", [False, True])
+def test_gdelta_backward_parity(shape, extras):
+    """dq, dk, dv, d log alpha, dbeta and ds0 of gdelta_chunk_bwd against the oracle's reverse
+    mode through the recurrent form, for L = <dout, o> (+ <ds_out, S_T>)."""
+    B, H, T, dk, dv, c = shape
+    w = synthetic.gdelta_inputs(B, H, T, dk, dv, chunk=c, dtype="bf16", seed=900 + sum(shape), with_state=extras)
+    rng = np.random.default_rng(sum(shape) + 2)
+    dout = synthetic.round_to_bf16(rng.standard_normal((B, H, T, dv)) / np.sqrt(dv)).astype(np.float32)
+    ds_out = (rng.standard_normal((B, H, dv, dk)) * 0.1).astype(np.float32) if extras else None
+    got = _gdelta_bwd(w, dout, ds_out, c)
+    ref = orc.gdelta_backward(w.q, w.k, w.v, w.log_alpha, w.beta, dout, dS_T=ds_out, s0=w.s0)
+    label = f"gdelta bwd {shape} extras={extras}"
+    for name, gi, ri in (("dq", 0, 0), ("dk", 1, 1), ("dv", 2, 2), ("ds0", 5, 5)):
+        if T == 0 and name != "ds0":
+            continue
+        _bwd_gate(f"{label} {name}", got[gi], ref[ri])
+    if T:
+        _gdelta_gate_grads_gate(f"{label} dlog_alpha", got[3], ref[3])
+        _gdelta_gate_grads_gate(f"{label} dbeta", got[4], ref[4])
+
+
+def test_gdelta_backward_full_size_parity():
+    """The gated-delta workload's shape (B4 H16 T8192, d 128) through gdelta_chunk_bwd; one of the
+    64 sequences checked against the oracle's reverse mode (every token)."""
+    w = synthetic.config_inputs("gdelta_b4h16_t8192_d128")
+    B, H, T, d = w.q.shape
+    rng = np.random.default_rng(11)
+    dout = synthetic.round_to_bf16(rng.standard_normal((B, H, T, d)) / np.sqrt(d)).astype(np.float32)
+    got = _gdelta_bwd(w, dout, None, 64)
+    b, h = 2, 5
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    ref = orc.gdelta_backward(w.q[sl], w.k[sl], w.v[sl], w.log_alpha[sl], w.beta[sl], dout[sl])
+    label = "gdelta bwd full size (b 2, h 5)"
+    for name, gi in (("dq", 0), ("dk", 1), ("dv", 2), ("ds0", 5)):
+        _bwd_gate(f"{label} {name}", got[gi][sl], ref[gi])
+    _gdelta_gate_grads_gate(f"{label} dlog_alpha", got[3][sl], ref[3])
+    _gdelta_gate_grads_gate(f"{label} dbeta", got[4][sl], ref[4])
+
+
 @pytest.mark.parametrize("kind", ["mamba2", "gla"])
 def test_backward_deterministic(kind):
     """No atomics: two backward calls give bit-identical gradients."""
