@@ -25,9 +25,9 @@
 //   grads    grads_kernel: dq, dk, dv, dbeta and d log alpha per chunk.
 // The chains hold S^T (dS^T) for 16 value rows in fp32 MFMA accumulators; with 16x16x16 bf16
 // products an accumulator tile is the next product's B operand as it stands. maps and grads
-// run their products with tile_gemm (16 x 16 output tiles on fp32 MFMA, operands read through
-// loader functions) over a per-workgroup fp32 scratch in global memory: persistent workgroups
-// take the chunks in turn.
+// run their products with gemm_lds (16 x 16 output tiles on fp32 MFMA, operands read through
+// loader functions and staged slice by slice in LDS) over a per-workgroup fp32 scratch in
+// global memory: persistent workgroups take the chunks in turn.
 #pragma once
 
 #include "chunk_delta_sp.hpp"
@@ -92,23 +92,55 @@ __device__ __forceinline__ float bf(u16 x) { return bf16_bits_to_f32(x); }
 __device__ __forceinline__ float scr(const float* x) { return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ u16 to_bf(float x) { return __builtin_bit_cast(u16, static_cast<__bf16>(x)); }
 
-// out(m, n) <- epi(m, n, sum_k x(m, k) y(k, n)) for the M x N output (multiples of 16) and
-// K (a multiple of 4), 16 x 16 tiles spread over the workgroup's four waves, fp32 MFMA
-// (16x16x4: lane (r, g) supplies x(m0 + r, k0 + g) and y(k0 + g, n0 + r) and receives
-// rows m0 + 4g + e of column n0 + r). The caller synchronises afterwards.
-template <typename FX, typename FY, typename FE>
-__device__ __forceinline__ void tile_gemm(int M, int N, int K, FX x, FY y, FE epi) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// out(m, n) <- epi(m, n, sum_k x(m, k) y(k, n)) for an M x N output (multiples of 16) and a
+// reduction over K (a multiple of 16), on fp32 MFMA 16x16x4 (lane (r, g) supplies x(m0 + r, k)
+// and y(k, n0 + r) for k = k0 + g and receives rows m0 + 4g + e of column n0 + r). The
+// reduction runs in slices of KS: every slice of x and y is first copied by the whole
+// workgroup into LDS (each element read once, neighbouring threads on neighbouring elements),
+// then each wave takes its 16 x 16 output tiles from LDS. Row strides of the staged slices
+// put the 16 rows x 4 reduction slots of one operand read in 64 distinct banks.
+constexpr int kGemmMax = 128;                                   // largest M or N
+constexpr int kSliceMax = 64;                                   // largest reduction slice
+constexpr int gemm_sy(int n) { return n + ((16 - n) % 64 + 64) % 64; }
+constexpr int kSxFloats = kGemmMax * (kSliceMax + 4);
+constexpr int kSyFloats = kSliceMax * gemm_sy(kGemmMax);
+
+template <int M, int N, int K, typename FX, typename FY, typename FE>
+__device__ __forceinline__ void gemm_lds(float* sx, float* sy, FX x, FY y, FE epi) {
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0 && M <= kGemmMax && N <= kGemmMax, "gemm shape");
+    constexpr int KS = K % 64 == 0 ? 64 : (K % 32 == 0 ? 32 : 16);
+    constexpr int SX = KS + 4, SY = gemm_sy(N);
+    constexpr int TN = N / 16, TILES = (M / 16) * TN, PER = (TILES + 3) / 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int nt = N >> 4, tiles = (M >> 4) * nt;
-    for (int t = w; t < tiles; t += 4) {
-        const int m0 = (t / nt) << 4, n0 = (t % nt) << 4;
-        f32x4 acc = zf4();
-#pragma unroll 4
-        for (int k0 = 0; k0 < K; k0 += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x(m0 + r, k0 + g), y(k0 + g, n0 + r), acc, 0, 0, 0);
+    f32x4 acc[PER];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) epi(m0 + 4 * g + e, n0 + r, acc[e]);
+    for (int q = 0; q < PER; ++q) acc[q] = zf4();
+    for (int k0 = 0; k0 < K; k0 += KS) {
+        for (int idx = tid; idx < M * KS; idx += 256) sx[(idx / KS) * SX + idx % KS] = x(idx / KS, k0 + idx % KS);
+        for (int idx = tid; idx < KS * N; idx += 256) sy[(idx / N) * SY + idx % N] = y(k0 + idx / N, idx % N);
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int t = w + 4 * q;
+            if (t < TILES) {
+                const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+#pragma unroll 4
+                for (int k = 0; k < KS; k += 4)
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx[(m0 + r) * SX + k + g], sy[(k + g) * SY + n0 + r],
+                                                                  acc[q], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int t = w + 4 * q;
+        if (t < TILES) {
+            const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) epi(m0 + 4 * g + e, n0 + r, acc[q][e]);
+        }
     }
 }
 
@@ -119,6 +151,7 @@ void maps_kernel(GdBwdParams p) {
     using S = GdScratch<C, DK, DV>;
     float* const sc = p.scratch + static_cast<int64_t>(blockIdx.x) * S::floats;
     __shared__ float sg[C], sw[C];   // e^G, e^(G_last - G)
+    __shared__ float sx[kSxFloats], sy[kSyFloats];
     for (int chunk = blockIdx.x; chunk < p.chunks; chunk += gridDim.x) {
         const int bh = chunk / p.NC, c = chunk % p.NC;
         const int t0 = c * C, n = (p.T - t0 < C) ? (p.T - t0) : C;
@@ -135,12 +168,12 @@ void maps_kernel(GdBwdParams p) {
         __syncthreads();
         auto kx = [&](int j, int a) { return j < n ? bf(K[j * DK + a]) : 0.f; };
         // W = T_U diag(g) K, U0 = T_U V, P = (Q K^T . Gamma) masked
-        tile_gemm(C, DK, C, [&](int i, int j) { return bf(TU[i * C + j]); }, [&](int j, int a) { return sg[j] * kx(j, a); },
+        gemm_lds<C, DK, C>(sx, sy, [&](int i, int j) { return bf(TU[i * C + j]); }, [&](int j, int a) { return sg[j] * kx(j, a); },
                   [&](int i, int a, float v) { sc[S::W + i * DK + a] = v; });
-        tile_gemm(C, DV, C, [&](int i, int j) { return bf(TU[i * C + j]); },
+        gemm_lds<C, DV, C>(sx, sy, [&](int i, int j) { return bf(TU[i * C + j]); },
                   [&](int j, int m) { return j < n ? bf(V[j * DV + m]) : 0.f; },
                   [&](int i, int m, float v) { sc[S::U0 + i * DV + m] = v; });
-        tile_gemm(C, C, DK, [&](int i, int a) { return i < n ? bf(Q[i * DK + a]) : 0.f; }, [&](int a, int j) { return kx(j, a); },
+        gemm_lds<C, C, DK>(sx, sy, [&](int i, int a) { return i < n ? bf(Q[i * DK + a]) : 0.f; }, [&](int a, int j) { return kx(j, a); },
                   [&](int i, int j, float v) { sc[S::P + i * C + j] = j <= i ? v * ex2(G[i] - G[j]) : 0.f; });
         __syncthreads();
         // Qt = diag(g) Q - P W (stored transposed), Mp = -W^T diag(w) K (and transposed),
@@ -149,17 +182,17 @@ void maps_kernel(GdBwdParams p) {
         u16* mp = p.mp + static_cast<int64_t>(chunk) * DK * DK;
         u16* mpT = p.mpT + static_cast<int64_t>(chunk) * DK * DK;
         u16* nn = p.nn + static_cast<int64_t>(chunk) * DV * DK;
-        tile_gemm(C, DK, C, [&](int i, int j) { return scr(sc + S::P + i * C + j); }, [&](int j, int a) { return scr(sc + S::W + j * DK + a); },
+        gemm_lds<C, DK, C>(sx, sy, [&](int i, int j) { return scr(sc + S::P + i * C + j); }, [&](int j, int a) { return scr(sc + S::W + j * DK + a); },
                   [&](int i, int a, float v) {
                       const float qv = i < n ? bf(Q[i * DK + a]) : 0.f;
                       qtT[a * C + i] = to_bf(sg[i] * qv - v);
                   });
-        tile_gemm(DK, DK, C, [&](int a, int j) { return scr(sc + S::W + j * DK + a); }, [&](int j, int b) { return sw[j] * kx(j, b); },
+        gemm_lds<DK, DK, C>(sx, sy, [&](int a, int j) { return scr(sc + S::W + j * DK + a); }, [&](int j, int b) { return sw[j] * kx(j, b); },
                   [&](int a, int b, float v) {
                       mp[a * DK + b] = to_bf(-v);
                       mpT[b * DK + a] = to_bf(-v);
                   });
-        tile_gemm(DV, DK, C, [&](int m, int j) { return scr(sc + S::U0 + j * DV + m); }, [&](int j, int b) { return sw[j] * kx(j, b); },
+        gemm_lds<DV, DK, C>(sx, sy, [&](int m, int j) { return scr(sc + S::U0 + j * DV + m); }, [&](int j, int b) { return sw[j] * kx(j, b); },
                   [&](int m, int b, float v) { nn[m * DK + b] = to_bf(v); });
         __syncthreads();
     }
@@ -281,6 +314,7 @@ void grads_kernel(GdBwdParams p) {
     float* const sc = p.scratch + static_cast<int64_t>(blockIdx.x) * S::floats;
     __shared__ float sg[C], sw[C], sGl[C], sbe[C], sdG[C], sdw[C], sdb[C];
     __shared__ float sTr;
+    __shared__ float sx[kSxFloats], sy[kSyFloats];
     const int tid = threadIdx.x;
     for (int chunk = blockIdx.x; chunk < p.chunks; chunk += gridDim.x) {
         const int bh = chunk / p.NC, c = chunk % p.NC;
@@ -312,40 +346,40 @@ void grads_kernel(GdBwdParams p) {
         auto ox = [&](int i, int m) { return i < n ? bf(dO[i * DV + m]) : 0.f; };
         auto gam = [&](int i, int j) { return ex2(sGl[i] - sGl[j]); };
         // ---- W, U0, P (as in the maps); dQt = dO S_in; dM = S_in^T dS_out
-        tile_gemm(C, DK, C, [&](int i, int j) { return bf(TU[i * C + j]); }, [&](int j, int a) { return sg[j] * kx(j, a); },
+        gemm_lds<C, DK, C>(sx, sy, [&](int i, int j) { return bf(TU[i * C + j]); }, [&](int j, int a) { return sg[j] * kx(j, a); },
                   [&](int i, int a, float v) { sc[S::W + i * DK + a] = v; });
-        tile_gemm(C, DV, C, [&](int i, int j) { return bf(TU[i * C + j]); }, vx,
+        gemm_lds<C, DV, C>(sx, sy, [&](int i, int j) { return bf(TU[i * C + j]); }, vx,
                   [&](int i, int m, float v) { sc[S::U0 + i * DV + m] = v; });
-        tile_gemm(C, C, DK, qx, [&](int a, int j) { return kx(j, a); },
+        gemm_lds<C, C, DK>(sx, sy, qx, [&](int a, int j) { return kx(j, a); },
                   [&](int i, int j, float v) { sc[S::P + i * C + j] = j <= i ? v * gam(i, j) : 0.f; });
-        tile_gemm(C, DK, DV, ox, [&](int m, int a) { return bf(Sin[m * DK + a]); },
+        gemm_lds<C, DK, DV>(sx, sy, ox, [&](int m, int a) { return bf(Sin[m * DK + a]); },
                   [&](int i, int a, float v) { sc[S::DQT + i * DK + a] = v; });
-        tile_gemm(DK, DK, DV, [&](int a, int m) { return bf(Sin[m * DK + a]); }, [&](int m, int b) { return bf(dSo[m * DK + b]); },
+        gemm_lds<DK, DK, DV>(sx, sy, [&](int a, int m) { return bf(Sin[m * DK + a]); }, [&](int m, int b) { return bf(dSo[m * DK + b]); },
                   [&](int a, int b, float v) {
                       sc[S::DM + a * DK + b] = v;
                       if (a == b) atomicAdd(&sTr, v);
                   });
         // KG = (K K^T . Gamma) strictly lower
-        tile_gemm(C, C, DK, kx, [&](int a, int j) { return kx(j, a); },
+        gemm_lds<C, C, DK>(sx, sy, kx, [&](int a, int j) { return kx(j, a); },
                   [&](int i, int j, float v) { sc[S::KG + i * C + j] = j < i ? v * gam(i, j) : 0.f; });
         __syncthreads();
         // ---- dU0 = P^T dO + diag(w) K dS_out^T (reduction over C tokens, then DK keys)
-        tile_gemm(C, DV, C + DK,
+        gemm_lds<C, DV, C + DK>(sx, sy,
                   [&](int j, int x) { return x < C ? scr(sc + S::P + x * C + j) : sw[j] * kx(j, x - C); },
                   [&](int x, int m) { return x < C ? ox(x, m) : bf(dSo[m * DK + x - C]); },
                   [&](int j, int m, float v) { sc[S::DU0 + j * DV + m] = v; });
         // dP = dO U0^T - dQt W^T (reduction over DV values, then DK keys), masked and decayed
-        tile_gemm(C, C, DV + DK,
+        gemm_lds<C, C, DV + DK>(sx, sy,
                   [&](int i, int x) { return x < DV ? ox(i, x) : -scr(sc + S::DQT + i * DK + x - DV); },
                   [&](int x, int j) { return x < DV ? scr(sc + S::U0 + j * DV + x) : scr(sc + S::W + j * DK + x - DV); },
                   [&](int i, int j, float v) { sc[S::DP + i * C + j] = j <= i ? v : 0.f; });
         // dW = -P^T dQt - diag(w) K dM^T
-        tile_gemm(C, DK, C + DK,
+        gemm_lds<C, DK, C + DK>(sx, sy,
                   [&](int j, int x) { return x < C ? -scr(sc + S::P + x * C + j) : -sw[j] * kx(j, x - C); },
                   [&](int x, int a) { return x < C ? scr(sc + S::DQT + x * DK + a) : scr(sc + S::DM + a * DK + x - C); },
                   [&](int j, int a, float v) { sc[S::DW + j * DK + a] = v; });
         // U0 dS_out - W dM: dK's first part (times w) and dw
-        tile_gemm(C, DK, DV + DK,
+        gemm_lds<C, DK, DV + DK>(sx, sy,
                   [&](int j, int x) { return x < DV ? scr(sc + S::U0 + j * DV + x) : -scr(sc + S::W + j * DK + x - DV); },
                   [&](int x, int b) { return x < DV ? bf(dSo[x * DK + b]) : scr(sc + S::DM + (x - DV) * DK + b); },
                   [&](int j, int b, float v) {
@@ -354,20 +388,20 @@ void grads_kernel(GdBwdParams p) {
                   });
         __syncthreads();
         // ---- T^T dW, T^T dU0; dT = dW (diag(beta g) K)^T + dU0 (diag(beta) V)^T
-        tile_gemm(C, DK, C, [&](int j, int i) { return bf(TF[i * C + j]); }, [&](int i, int a) { return scr(sc + S::DW + i * DK + a); },
+        gemm_lds<C, DK, C>(sx, sy, [&](int j, int i) { return bf(TF[i * C + j]); }, [&](int i, int a) { return scr(sc + S::DW + i * DK + a); },
                   [&](int j, int a, float v) { sc[S::TDW + j * DK + a] = v; });
-        tile_gemm(C, DV, C, [&](int j, int i) { return bf(TF[i * C + j]); }, [&](int i, int m) { return scr(sc + S::DU0 + i * DV + m); },
+        gemm_lds<C, DV, C>(sx, sy, [&](int j, int i) { return bf(TF[i * C + j]); }, [&](int i, int m) { return scr(sc + S::DU0 + i * DV + m); },
                   [&](int j, int m, float v) { sc[S::TDU + j * DV + m] = v; });
-        tile_gemm(C, C, DK + DV,
+        gemm_lds<C, C, DK + DV>(sx, sy,
                   [&](int i, int x) { return x < DK ? scr(sc + S::DW + i * DK + x) : scr(sc + S::DU0 + i * DV + x - DK); },
                   [&](int x, int j) { return x < DK ? sbe[j] * sg[j] * kx(j, x) : sbe[j] * vx(j, x - DK); },
                   [&](int i, int j, float v) { sc[S::DT + i * C + j] = v; });
         __syncthreads();
         // ---- Z = T^T dT, then dA = strictly_lower(-Z T^T)
-        tile_gemm(C, C, C, [&](int i, int l) { return bf(TF[l * C + i]); }, [&](int l, int j) { return scr(sc + S::DT + l * C + j); },
+        gemm_lds<C, C, C>(sx, sy, [&](int i, int l) { return bf(TF[l * C + i]); }, [&](int l, int j) { return scr(sc + S::DT + l * C + j); },
                   [&](int i, int j, float v) { sc[S::Z + i * C + j] = v; });
         __syncthreads();
-        tile_gemm(C, C, C, [&](int i, int l) { return scr(sc + S::Z + i * C + l); }, [&](int l, int j) { return bf(TF[j * C + l]); },
+        gemm_lds<C, C, C>(sx, sy, [&](int i, int l) { return scr(sc + S::Z + i * C + l); }, [&](int l, int j) { return bf(TF[j * C + l]); },
                   [&](int i, int j, float v) { sc[S::DA + i * C + j] = j < i ? -v : 0.f; });
         __syncthreads();
         // ---- row and column terms of dbeta and dG from dA (A = diag(beta) KG) and dP (P),
@@ -386,12 +420,12 @@ void grads_kernel(GdBwdParams p) {
             sdG[i] += dg;
         }
         // dQ2 = (dP . Gamma) K + 0 (the decayed dP's reduction over tokens j)
-        tile_gemm(C, DK, C, [&](int i, int j) { return scr(sc + S::DP + i * C + j) * (j <= i ? gam(i, j) : 0.f); },
+        gemm_lds<C, DK, C>(sx, sy, [&](int i, int j) { return scr(sc + S::DP + i * C + j) * (j <= i ? gam(i, j) : 0.f); },
                   [&](int j, int a) { return kx(j, a); }, [&](int i, int a, float v) { sc[S::DQ2 + i * DK + a] = v; });
         __syncthreads();
         // ---- dK: the first part + diag(beta g) T^T dW + M1 K + M1^T K + (dP . Gamma)^T Q, with
         // M1_ij = dA_ij beta_i Gamma_ij (reduction over 2C tokens, then C tokens of the decayed dP)
-        tile_gemm(C, DK, 3 * C,
+        gemm_lds<C, DK, 3 * C>(sx, sy,
                   [&](int j, int x) {
                       if (x < C) return scr(sc + S::DA + x * C + j) * sbe[x] * (j < x ? gam(x, j) : 0.f);   // M1^T
                       if (x < 2 * C) { const int l = x - C; return scr(sc + S::DA + j * C + l) * sbe[j] * (l < j ? gam(j, l) : 0.f); }
