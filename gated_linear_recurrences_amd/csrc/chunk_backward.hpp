@@ -469,7 +469,7 @@ hipError_t launch_backward_dv(const BwdArgs& a, hipStream_t stream) {
     }
     if (err != hipSuccess) return err;
     if (NC > 0) {
-        GradParams p;
+        GradParams p{};
         p.q = static_cast<const u16*>(a.q);
         p.k = static_cast<const u16*>(a.k);
         p.v = static_cast<const u16*>(a.v);

@@ -597,7 +597,7 @@ hipError_t launch_backward_gla_dv(const BwdArgs& a, hipStream_t stream) {
     }
     if (err != hipSuccess) return err;
     if (NC == 0) return hipSuccess;
-    GradGlaParams p;
+    GradGlaParams p{};
     p.q = static_cast<const u16*>(a.q);
     p.k = static_cast<const u16*>(a.k);
     p.v = static_cast<const u16*>(a.v);

@@ -178,11 +178,12 @@ __device__ __forceinline__ int logical_block_of(unsigned bid, unsigned grid, int
 namespace glr {
 namespace ck {
 
-constexpr int kCUs = 256;
+constexpr int kCUs = 256;   // compute units of an MI355X
 
-// Gate of the two-pass retention-family kernels: one fixed decay per head, one
-// data-dependent gate per key channel, or one data-dependent scalar per token.
-enum GateKind { kGateFixed = 0, kGateChannel = 1, kGateScalar = 2 };   // compute units of an MI355X
+// Gate of the chunk kernels: one fixed decay per head, one data-dependent gate per key
+// channel, or one data-dependent scalar per token; the gated delta rule's single pass (a
+// scalar gate whose cumulative sums come from its prep) is the fourth kind.
+enum GateKind { kGateFixed = 0, kGateChannel = 1, kGateScalar = 2, kGateDeltaRule = 3 };
 
 }  // namespace ck
 }  // namespace glr

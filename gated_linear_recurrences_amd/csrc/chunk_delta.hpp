@@ -795,7 +795,7 @@ template <int C, int DK, int DV>
 hipError_t launch_delta_dv(const ChunkArgs& a, hipStream_t stream) {
     const int NC = (a.T + C - 1) / C;
     const int64_t heads = static_cast<int64_t>(a.B) * a.H;
-    DeltaParams p;
+    DeltaParams p{};
     p.q = static_cast<const u16*>(a.q);
     p.k = static_cast<const u16*>(a.k);
     p.v = static_cast<const u16*>(a.v);

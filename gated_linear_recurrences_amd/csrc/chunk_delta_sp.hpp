@@ -1,5 +1,5 @@
 // Gated delta rule, chunk 64, bf16 storage: a chunk-parallel prep and a single pass that
-// keeps the memory on chip.
+// keeps the memory on chip (the same single pass also serves retention and the scalar decay).
 //
 // Method: the gated delta rule ("Scrivere meglio nella memoria", section "Unire oblio e
 // correzione: Gated DeltaNet") in the chunkwise form of the RetNet page (section "RetNet:
@@ -15,28 +15,33 @@
 //   prep         (all chunks in parallel) G and T_U (bf16, lower triangular) to the
 //                workspace: 8.25 KB per (sequence, chunk); with DeltaNet's feature map fused
 //                in, also q and k mapped by SiLU then L2 normalisation per token;
-//   single pass  (chunks in order) one workgroup per (sequence, 16 NV value channels);
+//   single pass  (chunks in order) one workgroup per (sequence, VS value channels);
 //   row norm     (with DeltaNet's output norm fused in) every output row RMS-normalised in
 //                place, one wave per four rows.
 //
-// Single pass, four waves. Rows of S (value channels) evolve independently, so wave vt < NV
-// (a "chain" wave) owns 16 value channels and keeps S^T for them (every key) in fp32 MFMA
-// accumulators; each product of the chain takes the previous one's accumulators directly as
-// its B operand (bf16, a fixed permutation of the reduction slots), with nothing exchanged
-// between waves:
+// Single pass, four waves. Rows of S (value channels) evolve independently, so waves 0 and 1
+// (the "chain" waves) own 16 (or, without the delta step, 32) value channels each and keep
+// S^T for them (every key) in fp32 MFMA accumulators; each product of the chain takes the
+// previous one's accumulators directly as its B operand (bf16, a fixed permutation of the
+// reduction slots), with nothing exchanged between waves:
 //   Y = K S_in^T           (reduction over keys; K rows from LDS)
 //   R = V - diag(e^G) Y,   U = T_U R    (reduction over tokens; T_U rows from LDS)
+//   o^T = S_in Q^T diag(e^G) + U^T P^T  (U as a bf16 hi + lo pair)
 //   S^T <- e^(G_last) S^T + K^T diag(e^(G_last - G)) U    (K^T by ds_read_b64_tr_b16)
-// and hands S_in (bf16 rows) and U (a bf16 hi + lo pair) over in LDS. Waves 2 and 3 (the
-// "output" waves) finish the previous chunk from that hand-off: each takes two token tiles
-// ({0, 3} and {1, 2}: five triangle tiles each) for every value tile of the workgroup,
-//   P = (Q K^T . Gamma) masked,   o^T = S_in Q^T diag(e^G) + U^T P^T,
-// with its q rows loaded from HBM straight into registers (MFMA operand layout) a chunk
-// ahead. Operands (K, the v slice, T_U, G) are loaded two chunks ahead into a register ring
-// by every lane and written to LDS just before the chunk's barrier; K and the gate tables
-// live in three LDS slots (staged, the chain's chunk, the output's chunk), the rest in two.
-// One workgroup barrier per chunk. The value slices of one sequence get block ids on one XCD
-// and share its L2 copy of K, q and T_U.
+// Waves 2 and 3 (the "helper" waves) issue every global load: K, Q, the v slice, T_U and G
+// two chunks ahead into a register ring, written to LDS just before the chunk's barrier; and
+// they form the decayed triangle P = (Q K^T . Gamma) masked one chunk ahead of the chain
+// (token tiles {0, 3} and {1, 2}: five 16 x 16 tiles each). K, Q and the gate tables live in
+// three LDS slots (staged, the triangle's chunk, the chain's chunk), the rest in two. One
+// workgroup barrier per chunk. The value slices of one sequence get block ids on one XCD and
+// share its L2 copy of K, Q and T_U.
+//
+// Without the delta step (U = V: retention, "RetNet: la retention e le sue tre forme", and
+// the scalar data-dependent decay, "Scrivere meglio nella memoria", section "Dimenticare: i
+// gate") the same pass runs with no prep: the helpers form G from log gamma, or scan the raw
+// log alpha, when they stage a chunk; Y, R and T_U drop out, and P V needs no lo part (V is
+// exact in bf16). A chain wave may then carry two value tiles, so that one read of its K, Q
+// and P operands serves 32 channels.
 #pragma once
 
 #include <type_traits>
@@ -74,6 +79,7 @@ struct DspParams {
     u16* qmap;
     u16* kmap;
     int T, NC, slices, remap, map;
+    int H;                // heads (the fixed gate: alpha then holds log gamma [H])
     int qk_seq;           // tokens per sequence in q and k as read by the single pass: T, or
                           // NC * C for the mapped copies
 };
@@ -283,7 +289,7 @@ void delta_tfac_kernel(DspParams p) {
 }
 
 // ====================================================================== single pass
-template <int C, int DK, int VS>
+template <int C, int DK, int VS, bool DELTA>
 struct DspLayout {
     using TK = SwzTile<DK>;     // K and Q rows
     using TV = SwzTile<VS>;     // the v slice
@@ -298,13 +304,13 @@ struct DspLayout {
     static constexpr int RBUF = al(C * RS * 2);
     static constexpr int GBUF = al((4 * C + 4) * 4);
     // K, Q and the gates of a chunk live three steps (staged, its triangle, its chain), the
-    // v slice, T_U and the triangle P two
+    // v slice, T_U (the delta rule only) and the triangle P two
     static constexpr int oK = 0;
     static constexpr int oQ = oK + 3 * KBUF;
     static constexpr int oG = oQ + 3 * KBUF;
     static constexpr int oV = oG + 3 * GBUF;
     static constexpr int oT = oV + 2 * VBUF;
-    static constexpr int oP = oT + 2 * RBUF;
+    static constexpr int oP = oT + (DELTA ? 2 * RBUF : 0);
     static constexpr int bytes = oP + 2 * RBUF;
     static_assert(bytes <= 160 * 1024, "LDS budget of the delta single pass exceeded");
 };
@@ -315,10 +321,13 @@ __device__ __forceinline__ bf16x4 tr4(const u16* p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 
-template <int C, int DK, int DV, int VS>
+template <int C, int DK, int DV, int VS, int GK, int VW = 1>
 __global__ __launch_bounds__(256)
 void delta_sp_kernel(DspParams p) {
-    using Lay = DspLayout<C, DK, VS>;
+    constexpr bool DELTA = GK == kGateDeltaRule;
+    static_assert(DELTA || GK == kGateScalar || GK == kGateFixed, "scalar gates only");
+    static_assert(VW == 1 || (VW == 2 && !DELTA), "two value tiles per chain wave without the delta step only");
+    using Lay = DspLayout<C, DK, VS, DELTA>;
     using TK = typename Lay::TK;
     using TV = typename Lay::TV;
     constexpr int NV = Lay::NV;
@@ -328,11 +337,11 @@ void delta_sp_kernel(DspParams p) {
     constexpr int NH = 128;                     // helper threads (waves 2 and 3)
     static_assert(C == 64, "the helpers split four token tiles two by two");
     static_assert(DK >= 32 && DK % 32 == 0, "d_k in 32-key blocks");
-    static_assert(DV % VS == 0 && (VS == 16 || VS == 32), "value slices of 16 or 32 channels");
+    static_assert(DV % VS == 0 && (VS == 16 * VW || VS == 32 * VW), "value slices of one or two chain waves");
     // 16-byte pieces of one chunk staged by the helpers: k, q (PKQ each), the v slice (PV),
     // T_U (PT); then one float of G per lane of each helper wave
     constexpr int PKQ = C * DK / 8, PV = C * VS / 8, PT = C * C / 8;
-    static_assert(PKQ % NH == 0 && PT % NH == 0 && PV <= 2 * NH, "pieces per helper thread");
+    static_assert(PKQ % NH == 0 && PT % NH == 0 && PV <= 4 * NH, "pieces per helper thread");
     constexpr int NKQ = PKQ / NH, NVP = (PV + NH - 1) / NH, NTP = PT / NH;
 
     __shared__ __align__(16) unsigned char smem[Lay::bytes];
@@ -377,19 +386,21 @@ void delta_sp_kernel(DspParams p) {
 
     if (w < 2) {
         // ================================================ chain waves
-        // wave vt < NV carries S^T of value tile vt (every key) in fp32 accumulators,
-        // sacc[ct][e] = S[m0 + 16 vt + r16][chan(ct) + e], and finishes each chunk's outputs
-        // for those channels; every product takes the previous one's accumulators as its
-        // operand (reduction slots 32b + 4g + e and 32b + 16 + 4g + e)
-        const int vt = w;
-        const bool live = vt < NV;
-        f32x4 sacc[KT];
+        // wave w < NV / VW carries S^T of value tiles vt = VW w .. VW w + VW - 1 (every key) in
+        // fp32 accumulators, sacc[v][ct][e] = S[m0 + 16 vt + r16][chan(ct) + e], and finishes
+        // each chunk's outputs for those channels; every product takes the previous one's
+        // accumulators as its operand (reduction slots 32b + 4g + e and 32b + 16 + 4g + e).
+        // With two tiles per wave the LDS operands (K, Q, P) serve both.
+        const bool live = w * VW < NV;
+        f32x4 sacc[VW][KT];
 #pragma unroll
-        for (int ct = 0; ct < KT; ++ct) {
-            sacc[ct] = zf4();
-            if (live && p.s0 != nullptr)
-                sacc[ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK + chan(ct));
-        }
+        for (int v = 0; v < VW; ++v)
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                sacc[v][ct] = zf4();
+                if (live && p.s0 != nullptr)
+                    sacc[v][ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * (VW * w + v) + r16) * DK + chan(ct));
+            }
         const auto ro = rsrc(p.o + seq0 * DV, static_cast<int64_t>(T) * DV * 2);
         lds_barrier();   // the prologue's two barriers
         lds_barrier();
@@ -404,7 +415,7 @@ void delta_sp_kernel(DspParams p) {
                 // every LDS operand of the chunk is requested before the first product: with one
                 // wave per SIMD nothing else hides the LDS latency
                 bf16x8 ka[CT][KB], qa[CT][KB], tu[CT][JB], pb[CT][JB], kt[KT][JB];
-                bf16x4 vv[CT];
+                bf16x4 vv[VW][CT];
                 f32x4 eg[CT], wt[CT];
                 float egi[CT];
 #pragma unroll
@@ -412,14 +423,15 @@ void delta_sp_kernel(DspParams p) {
                     const int row = 16 * it + r16;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        ka[it][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(row, 32 * kb + 8 * g));
+                        if constexpr (DELTA) ka[it][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(row, 32 * kb + 8 * g));
                         qa[it][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(row, 32 * kb + 8 * g));
                     }
                 }
 #pragma unroll
                 for (int it = 0; it < CT; ++it) {
-                    vv[it] = tr_op_s<VS>(V, 16 * it, 16 * vt, r16, g);
-                    eg[it] = ldf4(GT + Lay::GEG + 16 * it + 4 * g);
+#pragma unroll
+                    for (int v = 0; v < VW; ++v) vv[v][it] = tr_op_s<VS>(V, 16 * it, 16 * (VW * w + v), r16, g);
+                    if constexpr (DELTA) eg[it] = ldf4(GT + Lay::GEG + 16 * it + 4 * g);
                     wt[it] = ldf4(GT + Lay::GW + 16 * it + 4 * g);
                     egi[it] = GT[Lay::GEG + 16 * it + r16];
 #pragma unroll
@@ -428,7 +440,7 @@ void delta_sp_kernel(DspParams p) {
                         const bool hi = 2 * jb + 1 <= it;
                         const u16* tr = TT + (16 * it + r16) * RS + 32 * jb + 4 * g;
                         const u16* pr = PP + (16 * it + r16) * RS + 32 * jb + 4 * g;
-                        tu[it][jb] = join8(ld4(tr), hi ? ld4(tr + 16) : zero4());
+                        if constexpr (DELTA) tu[it][jb] = join8(ld4(tr), hi ? ld4(tr + 16) : zero4());
                         pb[it][jb] = join8(ld4(pr), hi ? ld4(pr + 16) : zero4());
                     }
                 }
@@ -447,77 +459,94 @@ void delta_sp_kernel(DspParams p) {
                 const float dec = GT[Lay::GEL];
                 __builtin_amdgcn_sched_barrier(0);
 
-                bf16x8 sb[KB];
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) sb[kb] = join8(cvt4(sacc[2 * kb]), cvt4(sacc[2 * kb + 1]));
-                // Y = K S_in^T (y[it][e] = Y[16it + 4g + e][value r16]) and o^T = S_in Q^T
-                // (oq[it][e] = (S_in q_i)[value 4g + e], i = 16it + r16), interleaved
-                f32x4 y[CT], oq[CT];
+                for (int v = 0; v < VW; ++v) {
+                    bf16x8 sb[KB];
 #pragma unroll
-                for (int it = 0; it < CT; ++it) {
-                    y[it] = zf4();
-                    oq[it] = zf4();
-                }
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                    for (int kb = 0; kb < KB; ++kb) sb[kb] = join8(cvt4(sacc[v][2 * kb]), cvt4(sacc[v][2 * kb + 1]));
+                    // Y = K S_in^T (y[it][e] = Y[16it + 4g + e][value r16]; the delta rule only)
+                    // and o^T = S_in Q^T (oq[it][e] = (S_in q_i)[value 4g + e], i = 16it + r16),
+                    // interleaved
+                    f32x4 y[CT], oq[CT];
 #pragma unroll
                     for (int it = 0; it < CT; ++it) {
-                        y[it] = mfma_16x16x32(ka[it][kb], sb[kb], y[it]);
-                        oq[it] = mfma_16x16x32(sb[kb], qa[it][kb], oq[it]);
+                        y[it] = zf4();
+                        oq[it] = zf4();
                     }
-                // R = V - diag(e^G) Y, then U = T_U R (lower triangular: block jb reaches token
-                // tile it when 2jb <= it)
-                bf16x4 rb[CT];
 #pragma unroll
-                for (int jt = 0; jt < CT; ++jt) rb[jt] = cvt4(up4(vv[jt]) - eg[jt] * y[jt]);
-                f32x4 u[CT];
+                    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int it = 0; it < CT; ++it) u[it] = zf4();
+                        for (int it = 0; it < CT; ++it) {
+                            if constexpr (DELTA) y[it] = mfma_16x16x32(ka[it][kb], sb[kb], y[it]);
+                            oq[it] = mfma_16x16x32(sb[kb], qa[it][kb], oq[it]);
+                        }
+                    // the values written: the delta rule's pseudo-values U (R = V - diag(e^G) Y,
+                    // then U = T_U R, lower triangular: block jb reaches token tile it when
+                    // 2jb <= it) as a bf16 hi + lo pair, else V itself (exact in bf16); weighted
+                    // by e^(G_last - G) for the carry
+                    bf16x8 uh[JB], ul[JB], wb[JB];
+                    if constexpr (DELTA) {
+                        bf16x4 rb[CT];
 #pragma unroll
-                for (int jb = 0; jb < JB; ++jb)
+                        for (int jt = 0; jt < CT; ++jt) rb[jt] = cvt4(up4(vv[v][jt]) - eg[jt] * y[jt]);
+                        f32x4 u[CT];
+#pragma unroll
+                        for (int it = 0; it < CT; ++it) u[it] = zf4();
+#pragma unroll
+                        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                            for (int it = 0; it < CT; ++it)
+                                if (2 * jb <= it) u[it] = mfma_16x16x32(tu[it][jb], join8(rb[2 * jb], rb[2 * jb + 1]), u[it]);
+#pragma unroll
+                        for (int jb = 0; jb < JB; ++jb) {
+                            const bf16x4 h0 = cvt4(u[2 * jb]), h1 = cvt4(u[2 * jb + 1]);
+                            uh[jb] = join8(h0, h1);
+                            ul[jb] = join8(cvt4(u[2 * jb] - up4(h0)), cvt4(u[2 * jb + 1] - up4(h1)));
+                            wb[jb] = join8(cvt4(u[2 * jb] * wt[2 * jb]), cvt4(u[2 * jb + 1] * wt[2 * jb + 1]));
+                        }
+                    } else {
+#pragma unroll
+                        for (int jb = 0; jb < JB; ++jb) {
+                            uh[jb] = join8(vv[v][2 * jb], vv[v][2 * jb + 1]);
+                            wb[jb] = join8(cvt4(up4(vv[v][2 * jb]) * wt[2 * jb]), cvt4(up4(vv[v][2 * jb + 1]) * wt[2 * jb + 1]));
+                        }
+                    }
+                    // carry S^T <- e^(G_last) S^T + K^T diag(e^(G_last - G)) U and outputs
+                    // o^T = S_in Q^T diag(e^G) + U^T P^T, interleaved
+                    f32x4 ot[CT];
+#pragma unroll
+                    for (int it = 0; it < CT; ++it) ot[it] = oq[it] * egi[it];
+#pragma unroll
+                    for (int ct = 0; ct < KT; ++ct) sacc[v][ct] = sacc[v][ct] * dec;
+#pragma unroll
+                    for (int jb = 0; jb < JB; ++jb) {
+#pragma unroll
+                        for (int ct = 0; ct < KT; ++ct) sacc[v][ct] = mfma_16x16x32(kt[ct][jb], wb[jb], sacc[v][ct]);
+#pragma unroll
+                        for (int it = 0; it < CT; ++it) {
+                            if (2 * jb > it) continue;
+                            ot[it] = mfma_16x16x32(uh[jb], pb[it][jb], ot[it]);
+                            if constexpr (DELTA) ot[it] = mfma_16x16x32(ul[jb], pb[it][jb], ot[it]);
+                        }
+                    }
+                    // o[16it + r16][m0 + 16vt + 4g + e]
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
                     for (int it = 0; it < CT; ++it)
-                        if (2 * jb <= it) u[it] = mfma_16x16x32(tu[it][jb], join8(rb[2 * jb], rb[2 * jb + 1]), u[it]);
-                // U as a bf16 hi + lo pair for the outputs, and weighted by e^(G_last - G) for the carry
-                bf16x8 uh[JB], ul[JB], wb[JB];
-#pragma unroll
-                for (int jb = 0; jb < JB; ++jb) {
-                    const bf16x4 h0 = cvt4(u[2 * jb]), h1 = cvt4(u[2 * jb + 1]);
-                    uh[jb] = join8(h0, h1);
-                    ul[jb] = join8(cvt4(u[2 * jb] - up4(h0)), cvt4(u[2 * jb + 1] - up4(h1)));
-                    wb[jb] = join8(cvt4(u[2 * jb] * wt[2 * jb]), cvt4(u[2 * jb + 1] * wt[2 * jb + 1]));
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(ot[it])), ro,
+                                                              ((c * C + 16 * it + r16) * DV + m0 + 16 * (VW * w + v) + 4 * g) * 2,
+                                                              0, 0);
                 }
-                // carry S^T <- e^(G_last) S^T + K^T diag(e^(G_last - G)) U and outputs
-                // o^T = S_in Q^T diag(e^G) + U^T P^T, interleaved
-                f32x4 ot[CT];
-#pragma unroll
-                for (int it = 0; it < CT; ++it) ot[it] = oq[it] * egi[it];
-#pragma unroll
-                for (int ct = 0; ct < KT; ++ct) sacc[ct] = sacc[ct] * dec;
-#pragma unroll
-                for (int jb = 0; jb < JB; ++jb) {
-#pragma unroll
-                    for (int ct = 0; ct < KT; ++ct) sacc[ct] = mfma_16x16x32(kt[ct][jb], wb[jb], sacc[ct]);
-#pragma unroll
-                    for (int it = 0; it < CT; ++it) {
-                        if (2 * jb > it) continue;
-                        ot[it] = mfma_16x16x32(uh[jb], pb[it][jb], ot[it]);
-                        ot[it] = mfma_16x16x32(ul[jb], pb[it][jb], ot[it]);
-                    }
-                }
-                // o[16it + r16][m0 + 16vt + 4g + e]
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-                for (int it = 0; it < CT; ++it)
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(ot[it])), ro,
-                                                          ((c * C + 16 * it + r16) * DV + m0 + 16 * vt + 4 * g) * 2, 0, 0);
             }
             lds_barrier();
         }
         if (live && p.s_out != nullptr) {
-            float* so = p.s_out + (static_cast<int64_t>(bh) * DV + m0 + 16 * vt + r16) * DK;
 #pragma unroll
-            for (int ct = 0; ct < KT; ++ct) stf4(so + chan(ct), sacc[ct]);
+            for (int v = 0; v < VW; ++v) {
+                float* so = p.s_out + (static_cast<int64_t>(bh) * DV + m0 + 16 * (VW * w + v) + r16) * DK;
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct) stf4(so + chan(ct), sacc[v][ct]);
+            }
         }
         return;
     }
@@ -532,8 +561,12 @@ void delta_sp_kernel(DspParams p) {
     const auto rq = rsrc(p.q + static_cast<int64_t>(bh) * p.qk_seq * DK, static_cast<int64_t>(p.qk_seq) * DK * 2);
     const auto rv = rsrc(p.v + seq0 * DV, static_cast<int64_t>(T) * DV * 2);
     const int64_t chunk0 = static_cast<int64_t>(bh) * NC;
-    const auto rt = rsrc(p.tu + chunk0 * C * C, static_cast<int64_t>(NC) * C * C * 2);
-    const auto rgt = rsrc(p.g + chunk0 * C, static_cast<int64_t>(NC) * C * 4);
+    // the delta rule's T_U and cumulative gates from its prep; the scalar gate's raw log
+    // alpha (zero past the sequence's end, so that the cumulative sums stay flat there)
+    const auto rt = rsrc(DELTA ? p.tu + chunk0 * C * C : nullptr, DELTA ? static_cast<int64_t>(NC) * C * C * 2 : 0);
+    const auto rgt = DELTA ? rsrc(p.g + chunk0 * C, static_cast<int64_t>(NC) * C * 4)
+                           : rsrc(GK == kGateScalar ? p.alpha + seq0 : nullptr, GK == kGateScalar ? static_cast<int64_t>(T) * 4 : 0);
+    const float lg2 = GK == kGateFixed ? p.alpha[bh % p.H] * kLog2e : 0.f;   // log2 of the fixed decay
 
     // the register ring: K, Q and G of chunk a, the v slice and T_U of chunk b
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -554,10 +587,13 @@ void delta_sp_kernel(DspParams p) {
             const int pc = (ht + i * NH) % PV, j = pc / (VS / 8), col = (pc % (VS / 8)) * 8;
             e.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((b * C + j) * DV + m0 + col) * 2, 0, 0);
         }
+        if constexpr (DELTA) {
 #pragma unroll
-        for (int i = 0; i < NTP; ++i)
-            e.t[i] = __builtin_amdgcn_raw_buffer_load_b128(rt, b * C * C * 2 + (ht + i * NH) * 16, 0, 0);
-        e.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgt, (a * C + lane) * 4, 0, 0));
+            for (int i = 0; i < NTP; ++i)
+                e.t[i] = __builtin_amdgcn_raw_buffer_load_b128(rt, b * C * C * 2 + (ht + i * NH) * 16, 0, 0);
+        }
+        if constexpr (GK != kGateFixed)
+            e.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgt, (a * C + lane) * 4, 0, 0));
     };
     // K, Q, G of chunk a into slot set sa (mod 3); the v slice and T_U into slot set sb (mod 2)
     auto stage_kqg = [&](const Entry& e, int sa) {
@@ -570,9 +606,19 @@ void delta_sp_kernel(DspParams p) {
             *reinterpret_cast<u32x4*>(Q + TK::off(j, col)) = e.q[i];
         }
         if (hw == 0) {
-            // gate tables: lane t holds G_t (log2 units, flat past the end of the sequence)
+            // gate tables: lane t holds G_t (log2 units, flat past the end of the sequence):
+            // the delta rule's from its prep, the scalar gate's scanned here, the fixed gate's
+            // (min(t, n - 1) + 1) log2 gamma
             float* GT = sG(sa % 3);
-            const float G = e.g;
+            float G;
+            if constexpr (DELTA) {
+                G = e.g;
+            } else if constexpr (GK == kGateScalar) {
+                G = wave_inclusive_scan(e.g * kLog2e);
+            } else {
+                const int n = T - sa * C;
+                G = static_cast<float>((lane < n ? lane : (n > 0 ? n - 1 : 0)) + 1) * lg2;
+            }
             const float gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), C - 1));
             GT[Lay::GG + lane] = G;
             GT[Lay::GEG + lane] = ex2(G);
@@ -595,10 +641,12 @@ void delta_sp_kernel(DspParams p) {
                 *reinterpret_cast<u32x4*>(V + TV::off(j, col)) = e.v[i];
             }
         }
+        if constexpr (DELTA) {
 #pragma unroll
-        for (int i = 0; i < NTP; ++i) {
-            const int pc = ht + i * NH, row = pc / (C / 8), col = (pc % (C / 8)) * 8;
-            *reinterpret_cast<u32x4*>(TT + row * RS + col) = e.t[i];
+            for (int i = 0; i < NTP; ++i) {
+                const int pc = ht + i * NH, row = pc / (C / 8), col = (pc % (C / 8)) * 8;
+                *reinterpret_cast<u32x4*>(TT + row * RS + col) = e.t[i];
+            }
         }
     };
     // the triangle of chunk c: P[i][j] = (q_i . k_j) e^(G_i - G_j) for j <= i, zero above, bf16;
@@ -750,7 +798,7 @@ hipError_t launch_dsp_dv(const ChunkArgs& a, hipStream_t stream) {
     constexpr int VS = DV >= 32 ? 32 : 16;
     const int NC = (a.T + C - 1) / C;
     const int64_t heads = static_cast<int64_t>(a.B) * a.H;
-    DspParams p;
+    DspParams p{};
     p.q = static_cast<const u16*>(a.q);
     p.k = static_cast<const u16*>(a.k);
     p.v = static_cast<const u16*>(a.v);
@@ -787,7 +835,7 @@ hipError_t launch_dsp_dv(const ChunkArgs& a, hipStream_t stream) {
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((delta_sp_kernel<C, DK, DV, VS>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((delta_sp_kernel<C, DK, DV, VS, kGateDeltaRule>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !(a.fuse & 2)) return err;
     const int64_t rows = heads * a.T;
@@ -804,6 +852,63 @@ hipError_t launch_dsp_dk(const ChunkArgs& a, hipStream_t stream) {
         case 32: return launch_dsp_dv<C, DK, 32>(a, stream);
         case 64: return launch_dsp_dv<C, DK, 64>(a, stream);
         case 128: return launch_dsp_dv<C, DK, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Retention (GK = kGateFixed) and the scalar decay (kGateScalar) on the same single pass: no
+// prep (the helpers form the gate tables from log gamma or the raw log alpha), U = V. Slices
+// of 64 value channels (two chain waves of two value tiles) when that still gives every CU a
+// workgroup, else 32 (two chain waves of one), else 16.
+template <int C, int DK, int DV, int GK, int VS, int VW>
+hipError_t launch_lsp_vs(const ChunkArgs& a, hipStream_t stream) {
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    DspParams p{};
+    p.q = static_cast<const u16*>(a.q);
+    p.k = static_cast<const u16*>(a.k);
+    p.v = static_cast<const u16*>(a.v);
+    p.alpha = a.gate;
+    p.s0 = a.s0;
+    p.o = static_cast<u16*>(a.o);
+    p.s_out = a.s_out;
+    p.T = a.T;
+    p.NC = (a.T + C - 1) / C;
+    p.H = a.H;
+    p.qk_seq = a.T;
+    p.slices = DV / VS;
+    const int64_t grid = heads * p.slices;
+    p.remap = (grid % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((delta_sp_kernel<C, DK, DV, VS, GK, VW>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int C, int DK, int DV, int GK>
+hipError_t launch_lsp_dv(const ChunkArgs& a, hipStream_t stream) {
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    if constexpr (DV >= 64) {
+        if (heads * (DV / 64) >= kCUs) return launch_lsp_vs<C, DK, DV, GK, 64, 2>(a, stream);
+    }
+    if constexpr (DV >= 32) {
+        if (heads * (DV / 32) >= kCUs) return launch_lsp_vs<C, DK, DV, GK, 32, 1>(a, stream);
+    }
+    return launch_lsp_vs<C, DK, DV, GK, 16, 1>(a, stream);
+}
+
+template <int C, int GK>
+hipError_t launch_lsp(const ChunkArgs& a, hipStream_t stream) {
+    switch (a.dk * 1000 + a.dv) {
+        case 32016: return launch_lsp_dv<C, 32, 16, GK>(a, stream);
+        case 32032: return launch_lsp_dv<C, 32, 32, GK>(a, stream);
+        case 32064: return launch_lsp_dv<C, 32, 64, GK>(a, stream);
+        case 32128: return launch_lsp_dv<C, 32, 128, GK>(a, stream);
+        case 64016: return launch_lsp_dv<C, 64, 16, GK>(a, stream);
+        case 64032: return launch_lsp_dv<C, 64, 32, GK>(a, stream);
+        case 64064: return launch_lsp_dv<C, 64, 64, GK>(a, stream);
+        case 64128: return launch_lsp_dv<C, 64, 128, GK>(a, stream);
+        case 128016: return launch_lsp_dv<C, 128, 16, GK>(a, stream);
+        case 128032: return launch_lsp_dv<C, 128, 32, GK>(a, stream);
+        case 128064: return launch_lsp_dv<C, 128, 64, GK>(a, stream);
+        case 128128: return launch_lsp_dv<C, 128, 128, GK>(a, stream);
     }
     return hipErrorInvalidValue;
 }

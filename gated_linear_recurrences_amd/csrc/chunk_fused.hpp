@@ -494,7 +494,7 @@ void fused_kernel(FusedParams p) {
 
 template <int C, int DK, int DV, int TS, int GK>
 hipError_t launch_fused_ts(const ChunkArgs& a, hipStream_t stream) {
-    FusedParams p;
+    FusedParams p{};
     p.q = static_cast<const u16*>(a.q);
     p.k = static_cast<const u16*>(a.k);
     p.v = static_cast<const u16*>(a.v);

@@ -48,7 +48,7 @@ hipError_t launch_state(const ChunkArgs& a, int NC, hipStream_t stream) {
     // value tiles measured 12% slower for GLA B8 H16 T4096 and no faster for retention
     constexpr int NWV = 1;
     constexpr int U = state_group<C, NW, TV, GK>();
-    StateParams p;
+    StateParams p{};
     p.k = static_cast<const u16*>(a.k);
     p.v = static_cast<const u16*>(a.v);
     p.gate = a.gate;
@@ -80,7 +80,7 @@ hipError_t launch_two_pass_dv(const ChunkArgs& a, hipStream_t stream) {
         default: err = launch_state<C, DK, 1, GK>(a, NC, stream); break;
     }
     if (err != hipSuccess || NC == 0) return err;
-    OutParams p;
+    OutParams p{};
     p.q = static_cast<const u16*>(a.q);
     p.k = static_cast<const u16*>(a.k);
     p.v = static_cast<const u16*>(a.v);

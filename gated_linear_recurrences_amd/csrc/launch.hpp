@@ -110,6 +110,14 @@ inline bool delta_single_pass(const ChunkArgs& a) {
     return a.chunk == 64 && a.dk >= 32 && rows * (d > 64 ? d : 64) * 2 < (1ll << 31);
 }
 
+// Retention and the scalar decay (bf16 storage) at chunk 64 with d_k >= 32 take the gated
+// delta rule's single pass without its delta step (same 31-bit buffer offsets).
+inline bool linear_single_pass(const ChunkArgs& a) {
+    const long long rows = (static_cast<long long>(a.T) + 63) / 64 * 64;
+    const long long d = a.dk > a.dv ? a.dk : a.dv;
+    return a.chunk == 64 && a.dk >= 32 && rows * (d > 64 ? d : 64) * 2 < (1ll << 31);
+}
+
 // float32 storage, fp32 arithmetic (VALU).
 hipError_t launch_chunk_f32(Variant variant, const ChunkArgs& a, hipStream_t stream);
 // Device workspace the chunk kernels of (variant, shape, storage) need, in bytes.

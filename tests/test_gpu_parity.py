@@ -142,8 +142,9 @@ def test_bf16_chunk_parity(kind, shape, state):
 
 
 # (B, H, T, d_k, d_v, chunk) with B * H * d_v / 16 >= 128: retention and the scalar decay take
-# the single-pass forward there (no workspace). Every d_k, d_v and chunk, value slices of 16
-# and 32 channels, ragged tails, a lone partial chunk, T = 1 and T = 0.
+# the single-pass forward there (no workspace). Every d_k, d_v and chunk, value slices of 16,
+# 32 and 64 channels (at chunk 64 with 256 or more slices of 64: two value tiles per chain
+# wave), ragged tails, a lone partial chunk, T = 1 and T = 0.
 SINGLE_PASS_SHAPES = [
     (2, 8, 100, 16, 128, 16),     # 16-channel slices, d_k = 16
     (4, 8, 77, 32, 64, 32),
@@ -155,6 +156,9 @@ SINGLE_PASS_SHAPES = [
     (8, 8, 0, 64, 32, 64),
     (4, 8, 150, 16, 64, 64),      # chunk 64 (q taken from registers), d_k = 16: half the lanes idle
     (4, 8, 99, 32, 128, 64),      # chunk 64, d_k = 32
+    (4, 64, 130, 128, 128, 64),   # 64-channel slices, two value tiles per chain wave
+    (16, 16, 70, 64, 64, 64),     # one 64-channel slice per sequence, d_k = 64
+    (32, 8, 1, 32, 64, 64),       # 64-channel slices, T = 1
 ]
 
 
