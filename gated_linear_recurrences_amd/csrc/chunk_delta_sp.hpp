@@ -614,7 +614,7 @@ void delta_sp_kernel(DspParams p) {
             if constexpr (DELTA) {
                 G = e.g;
             } else if constexpr (GK == kGateScalar) {
-                G = wave_inclusive_scan(e.g * kLog2e);
+                G = wave_inclusive_scan_dpp(e.g * kLog2e);
             } else {
                 const int n = T - sa * C;
                 G = static_cast<float>((lane < n ? lane : (n > 0 ? n - 1 : 0)) + 1) * lg2;

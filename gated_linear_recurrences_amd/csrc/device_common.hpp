@@ -132,4 +132,19 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
     return x;
 }
 
+// The same scan with DPP moves and lane reads (no LDS crossbar): a Hillis-Steele scan within
+// each row of 16 lanes (row_shr by 1, 2, 4, 8; lanes shifted in from outside the row read 0),
+// then each row adds the totals of the rows before it (lanes 15, 31 and 47 read as scalars).
+__device__ __forceinline__ float wave_inclusive_scan_dpp(float x) {
+    x += dpp_move<0x111>(x);   // row_shr:1
+    x += dpp_move<0x112>(x);   // row_shr:2
+    x += dpp_move<0x114>(x);   // row_shr:4
+    x += dpp_move<0x118>(x);   // row_shr:8
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+}
+
 }  // namespace glr
