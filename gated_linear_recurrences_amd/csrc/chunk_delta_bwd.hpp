@@ -83,7 +83,7 @@ inline size_t gd_bwd_ws_bytes(int64_t chunks, int C, int dk, int dv) {
     const int64_t scr = 6 * CK + 3 * CV + 6 * CC + KK;   // GdScratch<C, DK, DV>::floats
     return delta_ws_align(chunks * CC * 2) + delta_ws_align(chunks * C * 4) + delta_ws_align(chunks * CC * 2) +
            delta_ws_align(chunks * CK * 2) + 2 * delta_ws_align(chunks * KK * 2) + 3 * delta_ws_align(chunks * VK * 2) +
-           delta_ws_align(gd_bwd_workgroups(chunks) * scr * 4);
+           3 * delta_ws_align(chunks * CV * 2) + delta_ws_align(gd_bwd_workgroups(chunks) * scr * 4);
 }
 
 __device__ __forceinline__ float bf(u16 x) { return bf16_bits_to_f32(x); }
@@ -519,7 +519,6 @@ hipError_t launch_gdelta_bwd_dv(const BwdArgs& a, hipStream_t stream) {
     p.nn = reinterpret_cast<u16*>(take(chunks * DV * DK * 2));
     p.sin = reinterpret_cast<u16*>(take(chunks * DV * DK * 2));
     p.dso = reinterpret_cast<u16*>(take(chunks * DV * DK * 2));
-    p.scratch = reinterpret_cast<float*>(ws);
     p.T = a.T;
     p.NC = NC;
     p.chunks = static_cast<int>(chunks);
@@ -550,13 +549,58 @@ hipError_t launch_gdelta_bwd_dv(const BwdArgs& a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const unsigned wgs = static_cast<unsigned>(gd_bwd_workgroups(chunks));
-    hipLaunchKernelGGL((maps_kernel<C, DK, DV>), dim3(wgs), dim3(256), 0, stream, p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    const unsigned rows = static_cast<unsigned>(heads * (DV / 16));
-    hipLaunchKernelGGL((fwd_chain_kernel<C, DK, DV>), dim3(rows), dim3(64), 0, stream, p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((bwd_chain_kernel<C, DK, DV>), dim3(rows), dim3(64), 0, stream, p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    u16* rec_u = reinterpret_cast<u16*>(take(chunks * C * DV * 2));
+    u16* rec_r = reinterpret_cast<u16*>(take(chunks * C * DV * 2));
+    u16* rec_du = reinterpret_cast<u16*>(take(chunks * C * DV * 2));
+    p.scratch = reinterpret_cast<float*>(ws);
+    bool single = false;
+    if constexpr (C == 64 && DK >= 32) single = delta_sp_fits(a.T, DK, DV);
+    if (single) {
+        if constexpr (C == 64 && DK >= 32) {
+            // the forward single pass recording S_in, U and R per chunk; then the same pass in
+            // reverse for dS' and dU per chunk, dV and ds0
+            constexpr int VS = DV >= 32 ? 32 : 16;
+            DspParams fp{};
+            fp.q = p.q;
+            fp.k = p.k;
+            fp.v = p.v;
+            fp.alpha = a.gate;
+            fp.beta = a.beta;
+            fp.s0 = a.s0;
+            fp.tu = tu;
+            fp.g = g;
+            fp.T = a.T;
+            fp.NC = NC;
+            fp.qk_seq = a.T;
+            fp.slices = DV / VS;
+            const int64_t grid = heads * fp.slices;
+            fp.remap = (grid % 8 == 0) ? 1 : 0;
+            DspParams rp = fp;
+            fp.st_s = p.sin;
+            fp.st_u = rec_u;
+            fp.st_r = rec_r;
+            hipLaunchKernelGGL((delta_sp_kernel<C, DK, DV, VS, kGateDeltaRule, 1, false>), dim3(static_cast<unsigned>(grid)),
+                               dim3(256), 0, stream, fp);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            rp.v = p.dout;
+            rp.s0 = a.ds_out;
+            rp.o = p.dv;
+            rp.s_out = a.ds0;
+            rp.st_s = p.dso;
+            rp.st_u = rec_du;
+            hipLaunchKernelGGL((delta_sp_kernel<C, DK, DV, VS, kGateDeltaRule, 1, true>), dim3(static_cast<unsigned>(grid)),
+                               dim3(256), 0, stream, rp);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+    } else {
+        hipLaunchKernelGGL((maps_kernel<C, DK, DV>), dim3(wgs), dim3(256), 0, stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        const unsigned rows = static_cast<unsigned>(heads * (DV / 16));
+        hipLaunchKernelGGL((fwd_chain_kernel<C, DK, DV>), dim3(rows), dim3(64), 0, stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((bwd_chain_kernel<C, DK, DV>), dim3(rows), dim3(64), 0, stream, p);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     hipLaunchKernelGGL((grads_kernel<C, DK, DV>), dim3(wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

@@ -60,6 +60,14 @@ inline size_t dsp_ws_bytes(int64_t chunks, int C, int dk, bool mapped) {
            (mapped ? 2 * delta_ws_align(chunks * C * dk * 2) : 0);
 }
 
+// The single pass's buffer offsets are 31-bit: one sequence's q, k, v or o (rows padded to
+// whole chunks) must stay below 2^31 bytes.
+inline bool delta_sp_fits(int T, int dk, int dv) {
+    const long long rows = (static_cast<long long>(T) + 63) / 64 * 64;
+    const long long d = dk > dv ? dk : dv;
+    return dk >= 32 && rows * (d > 64 ? d : 64) * 2 < (1ll << 31);
+}
+
 struct DspParams {
     const u16* q;         // [BH][T][DK]
     const u16* k;         // [BH][T][DK]
@@ -80,6 +88,13 @@ struct DspParams {
     u16* kmap;
     int T, NC, slices, remap, map;
     int H;                // heads (the fixed gate: alpha then holds log gamma [H])
+    // the backward's per-chunk records (null: none). Forward: st_s the memory entering each
+    // chunk [BH * NC][DV][DK], st_u the pseudo-values U and st_r R = V - diag(e^G) K S_in^T
+    // [BH * NC][C][DV], all bf16 (o may then be null). Reverse pass: st_s the gradient of the
+    // memory leaving each chunk, st_u dU; o receives dV.
+    u16* st_s;
+    u16* st_u;
+    u16* st_r;
     int qk_seq;           // tokens per sequence in q and k as read by the single pass: T, or
                           // NC * C for the mapped copies
 };
@@ -321,10 +336,11 @@ __device__ __forceinline__ bf16x4 tr4(const u16* p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 
-template <int C, int DK, int DV, int VS, int GK, int VW = 1>
+template <int C, int DK, int DV, int VS, int GK, int VW = 1, bool REV = false>
 __global__ __launch_bounds__(256)
 void delta_sp_kernel(DspParams p) {
     constexpr bool DELTA = GK == kGateDeltaRule;
+    static_assert(!REV || (DELTA && VW == 1), "the reverse pass is the delta rule's, one value tile per chain wave");
     static_assert(DELTA || GK == kGateScalar || GK == kGateFixed, "scalar gates only");
     static_assert(VW == 1 || (VW == 2 && !DELTA), "two value tiles per chain wave without the delta step only");
     using Lay = DspLayout<C, DK, VS, DELTA>;
@@ -384,6 +400,148 @@ void delta_sp_kernel(DspParams p) {
         return;
     }
 
+    if (REV && w < 2) {
+        // ================================================ reverse pass (the backward)
+        // wave w carries the transposed gradient of the memory for value tile w (every key),
+        // dacc[ct][e] = dS[m0 + 16w + r16][chan(ct) + e], from the gradient of the final memory
+        // back through the chunks (the helpers stage them last first). Per chunk, with dS' the
+        // gradient of the memory leaving it (reverse mode through the chain's products):
+        //   dU    = P^T dO + diag(e^(G_last - G)) K dS'^T
+        //   dR    = T_U^T dU                    (the gradient of V)
+        //   dS_in = e^(G_last) dS' + Q^T diag(e^G) dO - K^T diag(e^G) dR    (as dS^T)
+        // dS' (bf16 rows) and dU ([C][DV], bf16) go to the workspace for the gradient pass.
+        const bool live = w < NV;
+        f32x4 dacc[KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            dacc[ct] = zf4();
+            if (live && p.s0 != nullptr)
+                dacc[ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * w + r16) * DK + chan(ct));
+        }
+        const auto rdv = rsrc(p.o + seq0 * DV, static_cast<int64_t>(T) * DV * 2);
+        const int vrow = m0 + 16 * w + r16;
+        lds_barrier();   // the prologue's two barriers
+        lds_barrier();
+        for (int c = 0; c < NC; ++c) {
+            if (live) {
+                const int rc = NC - 1 - c;
+                const int64_t gc = static_cast<int64_t>(bh) * NC + rc;
+                const u16* K = sK(c % 3);
+                const u16* Q = sQ(c % 3);
+                const float* GT = sG(c % 3);
+                const u16* DO = sV(c & 1);
+                const u16* TT = sT(c & 1);
+                const u16* PP = sP(c & 1);
+                bf16x8 ka[CT][KB], pt[CT][JB], tut[CT][JB], qt[KT][JB], kt[KT][JB];
+                bf16x4 vv[CT];
+                f32x4 eg[CT], wt[CT];
+#pragma unroll
+                for (int it = 0; it < CT; ++it) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        ka[it][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(16 * it + r16, 32 * kb + 8 * g));
+                    vv[it] = tr_op_s<VS>(DO, 16 * it, 16 * w, r16, g);   // dO[16it + 4g + e][value r16]
+                    eg[it] = ldf4(GT + Lay::GEG + 16 * it + 4 * g);
+                    wt[it] = ldf4(GT + Lay::GW + 16 * it + 4 * g);
+#pragma unroll
+                    for (int b = 0; b < JB; ++b) {
+                        // P^T (rows: token j of tile it; slots: tokens i of block b; P's tile
+                        // (i-tile, it) exists for i-tile >= it) and T_U^T (rows: token i of tile
+                        // it; slots: tokens j of block b; T_U is staged whole, zero above its
+                        // diagonal): both by transposed reads of the row-major tiles
+                        if (2 * b + 1 < it) continue;
+                        pt[it][b] = join8(2 * b >= it ? tr_op<RS>(PP, 32 * b, 16 * it, r16, g) : zero4(),
+                                          tr_op<RS>(PP, 32 * b + 16, 16 * it, r16, g));
+                        tut[it][b] = join8(tr_op<RS>(TT, 32 * b, 16 * it, r16, g), tr_op<RS>(TT, 32 * b + 16, 16 * it, r16, g));
+                    }
+                }
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                    for (int jb = 0; jb < JB; ++jb) {
+                        const int col = 32 * (ct >> 1) + 8 * (r16 & 3) + 4 * (ct & 1);
+                        kt[ct][jb] = join8(tr4(K + TK::off(32 * jb + 4 * g + (r16 >> 2), col)),
+                                           tr4(K + TK::off(32 * jb + 16 + 4 * g + (r16 >> 2), col)));
+                        qt[ct][jb] = join8(tr4(Q + TK::off(32 * jb + 4 * g + (r16 >> 2), col)),
+                                           tr4(Q + TK::off(32 * jb + 16 + 4 * g + (r16 >> 2), col)));
+                    }
+                const float dec = GT[Lay::GEL];
+                __builtin_amdgcn_sched_barrier(0);
+
+                bf16x8 sb[KB];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) sb[kb] = join8(cvt4(dacc[2 * kb]), cvt4(dacc[2 * kb + 1]));
+                if (p.st_s != nullptr) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        *reinterpret_cast<bf16x8*>(p.st_s + (gc * DV + vrow) * DK + 32 * kb + 8 * g) = sb[kb];
+                }
+                // dU[16it + 4g + e][value r16]
+                f32x4 du[CT];
+#pragma unroll
+                for (int it = 0; it < CT; ++it) du[it] = zf4();
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int it = 0; it < CT; ++it) du[it] = mfma_16x16x32(ka[it][kb], sb[kb], du[it]);
+#pragma unroll
+                for (int it = 0; it < CT; ++it) {
+                    du[it] = du[it] * wt[it];
+#pragma unroll
+                    for (int b = 0; b < JB; ++b)
+                        if (2 * b + 1 >= it) du[it] = mfma_16x16x32(pt[it][b], join8(vv[2 * b], vv[2 * b + 1]), du[it]);
+                }
+                bf16x8 dub[JB];
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb) dub[jb] = join8(cvt4(du[2 * jb]), cvt4(du[2 * jb + 1]));
+#pragma unroll
+                for (int it = 0; it < CT; ++it) {
+                    const bf16x4 b4 = cvt4(du[it]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) p.st_u[(gc * C + 16 * it + 4 * g + e) * DV + vrow] = __builtin_bit_cast(u16, b4[e]);
+                }
+                // dR[16it + 4g + e][value r16] (the gradient of v, stored as it stands)
+                f32x4 dr[CT];
+#pragma unroll
+                for (int it = 0; it < CT; ++it) {
+                    dr[it] = zf4();
+#pragma unroll
+                    for (int b = 0; b < JB; ++b)
+                        if (2 * b + 1 >= it) dr[it] = mfma_16x16x32(tut[it][b], dub[b], dr[it]);
+                    const bf16x4 b4 = cvt4(dr[it]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(u16, b4[e]), rdv,
+                                                              ((rc * C + 16 * it + 4 * g + e) * DV + vrow) * 2, 0, 0);
+                }
+                // dS^T <- e^(G_last) dS^T + Q^T diag(e^G) dO - K^T diag(e^G) dR
+                bf16x8 ob[JB], rn[JB];
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb) {
+                    ob[jb] = join8(cvt4(up4(vv[2 * jb]) * eg[2 * jb]), cvt4(up4(vv[2 * jb + 1]) * eg[2 * jb + 1]));
+                    rn[jb] = join8(cvt4(dr[2 * jb] * (-eg[2 * jb])), cvt4(dr[2 * jb + 1] * (-eg[2 * jb + 1])));
+                }
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct) {
+                    f32x4 a = dacc[ct] * dec;
+#pragma unroll
+                    for (int jb = 0; jb < JB; ++jb) {
+                        a = mfma_16x16x32(qt[ct][jb], ob[jb], a);
+                        a = mfma_16x16x32(kt[ct][jb], rn[jb], a);
+                    }
+                    dacc[ct] = a;
+                }
+            }
+            lds_barrier();
+        }
+        if (live && p.s_out != nullptr) {
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct)
+                stf4(p.s_out + (static_cast<int64_t>(bh) * DV + vrow) * DK + chan(ct), dacc[ct]);
+        }
+        return;
+    }
+
     if (w < 2) {
         // ================================================ chain waves
         // wave w < NV / VW carries S^T of value tiles vt = VW w .. VW w + VW - 1 (every key) in
@@ -401,7 +559,7 @@ void delta_sp_kernel(DspParams p) {
                 if (live && p.s0 != nullptr)
                     sacc[v][ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * (VW * w + v) + r16) * DK + chan(ct));
             }
-        const auto ro = rsrc(p.o + seq0 * DV, static_cast<int64_t>(T) * DV * 2);
+        const auto ro = rsrc(p.o != nullptr ? p.o + seq0 * DV : nullptr, p.o != nullptr ? static_cast<int64_t>(T) * DV * 2 : 0);
         lds_barrier();   // the prologue's two barriers
         lds_barrier();
         for (int c = 0; c < NC; ++c) {
@@ -504,6 +662,25 @@ void delta_sp_kernel(DspParams p) {
                             ul[jb] = join8(cvt4(u[2 * jb] - up4(h0)), cvt4(u[2 * jb + 1] - up4(h1)));
                             wb[jb] = join8(cvt4(u[2 * jb] * wt[2 * jb]), cvt4(u[2 * jb + 1] * wt[2 * jb + 1]));
                         }
+                        if (p.st_s != nullptr) {
+                            // the backward's records of the chunk: S_in rows (keys 32kb + 8g .. + 7
+                            // of value row vrow), U and R at (token 16it + 4g + e, value vrow)
+                            const int64_t gc = static_cast<int64_t>(bh) * NC + c;
+                            const int vrow = m0 + 16 * (VW * w + v) + r16;
+#pragma unroll
+                            for (int kb = 0; kb < KB; ++kb)
+                                *reinterpret_cast<bf16x8*>(p.st_s + (gc * DV + vrow) * DK + 32 * kb + 8 * g) = sb[kb];
+#pragma unroll
+                            for (int it = 0; it < CT; ++it) {
+                                const bf16x4 ub = cvt4(u[it]);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const int64_t at = (gc * C + 16 * it + 4 * g + e) * DV + vrow;
+                                    p.st_u[at] = __builtin_bit_cast(u16, ub[e]);
+                                    p.st_r[at] = __builtin_bit_cast(u16, rb[it][e]);
+                                }
+                            }
+                        }
                     } else {
 #pragma unroll
                         for (int jb = 0; jb < JB; ++jb) {
@@ -576,6 +753,11 @@ void delta_sp_kernel(DspParams p) {
     };
     Entry ring[2];
     auto load = [&](Entry& e, int a, int b) {
+        if constexpr (REV) {
+            // the reverse pass stages the chunks last first
+            a = NC - 1 - a;
+            b = NC - 1 - b;
+        }
 #pragma unroll
         for (int i = 0; i < NKQ; ++i) {
             const int pc = ht + i * NH, j = pc / (DK / 8), col = (pc % (DK / 8)) * 8;
