@@ -30,39 +30,10 @@
 // global memory: persistent workgroups take the chunks in turn.
 #pragma once
 
-#include "chunk_delta_sp.hpp"
+#include "chunk_delta_grads.hpp"
 
 namespace glr {
 namespace ck {
-
-struct GdBwdParams {
-    const u16* q;          // [BH][T][DK]
-    const u16* k;          // [BH][T][DK]
-    const u16* v;          // [BH][T][DV]
-    const float* alpha;    // log alpha [BH][T]
-    const float* beta;     // [BH][T]
-    const float* s0;       // [BH][DV][DK] or null
-    const u16* dout;       // [BH][T][DV]
-    const float* ds_out;   // [BH][DV][DK] or null
-    u16* dq;               // [BH][T][DK]
-    u16* dk;               // [BH][T][DK]
-    u16* dv;               // [BH][T][DV]
-    float* dalpha;         // [BH][T]
-    float* dbeta;          // [BH][T]
-    float* ds0;            // [BH][DV][DK] or null
-    // workspace (per chunk, chunk c of sequence bh at bh * NC + c)
-    const u16* tu;         // [C][C] T_U
-    const float* g;        // [C] cumulative log2-gates
-    const u16* tfull;      // [C][C] T
-    u16* qtT;              // [DK][C] Qt^T
-    u16* mp;               // [DK][DK] Mp
-    u16* mpT;              // [DK][DK] Mp^T
-    u16* nn;               // [DV][DK] N
-    u16* sin;              // [DV][DK] memory entering the chunk
-    u16* dso;              // [DV][DK] gradient of the memory leaving the chunk
-    float* scratch;        // [workgroups][scratch floats]
-    int T, NC, chunks;
-};
 
 // fp32 scratch of one maps / grads workgroup (floats)
 template <int C, int DK, int DV>
@@ -591,6 +562,14 @@ hipError_t launch_gdelta_bwd_dv(const BwdArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((delta_sp_kernel<C, DK, DV, VS, kGateDeltaRule, 1, true>), dim3(static_cast<unsigned>(grid)),
                                dim3(256), 0, stream, rp);
             if ((err = hipGetLastError()) != hipSuccess) return err;
+            if constexpr (DV % 32 == 0) {
+                p.rec_u = rec_u;
+                p.rec_r = rec_r;
+                p.rec_du = rec_du;
+                hipLaunchKernelGGL((gd_grads_kernel<DK, DV>), dim3(static_cast<unsigned>(gd_grads_workgroups(chunks))), dim3(512), 0,
+                                   stream, p);
+                return hipGetLastError();
+            }
         }
     } else {
         hipLaunchKernelGGL((maps_kernel<C, DK, DV>), dim3(wgs), dim3(256), 0, stream, p);

@@ -496,9 +496,11 @@ void delta_sp_kernel(DspParams p) {
                 for (int jb = 0; jb < JB; ++jb) dub[jb] = join8(cvt4(du[2 * jb]), cvt4(du[2 * jb + 1]));
 #pragma unroll
                 for (int it = 0; it < CT; ++it) {
-                    const bf16x4 b4 = cvt4(du[it]);
+                    // (the element bits from the whole vector: a bit cast of one element of a bf16
+                    // vector read element 0)
+                    const u16x4 b4 = __builtin_bit_cast(u16x4, cvt4(du[it]));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) p.st_u[(gc * C + 16 * it + 4 * g + e) * DV + vrow] = __builtin_bit_cast(u16, b4[e]);
+                    for (int e = 0; e < 4; ++e) p.st_u[(gc * C + 16 * it + 4 * g + e) * DV + vrow] = b4[e];
                 }
                 // dR[16it + 4g + e][value r16] (the gradient of v, stored as it stands)
                 f32x4 dr[CT];
@@ -508,10 +510,10 @@ void delta_sp_kernel(DspParams p) {
 #pragma unroll
                     for (int b = 0; b < JB; ++b)
                         if (2 * b + 1 >= it) dr[it] = mfma_16x16x32(tut[it][b], dub[b], dr[it]);
-                    const bf16x4 b4 = cvt4(dr[it]);
+                    const u16x4 b4 = __builtin_bit_cast(u16x4, cvt4(dr[it]));
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(u16, b4[e]), rdv,
+                        __builtin_amdgcn_raw_buffer_store_b16(b4[e], rdv,
                                                               ((rc * C + 16 * it + 4 * g + e) * DV + vrow) * 2, 0, 0);
                 }
                 // dS^T <- e^(G_last) dS^T + Q^T diag(e^G) dO - K^T diag(e^G) dR
@@ -672,12 +674,14 @@ void delta_sp_kernel(DspParams p) {
                                 *reinterpret_cast<bf16x8*>(p.st_s + (gc * DV + vrow) * DK + 32 * kb + 8 * g) = sb[kb];
 #pragma unroll
                             for (int it = 0; it < CT; ++it) {
-                                const bf16x4 ub = cvt4(u[it]);
+                                // (element bits from the whole vector: a bit cast of one element of a
+                                // bf16 vector read element 0)
+                                const u16x4 ub = __builtin_bit_cast(u16x4, cvt4(u[it])), rr = __builtin_bit_cast(u16x4, rb[it]);
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
                                     const int64_t at = (gc * C + 16 * it + 4 * g + e) * DV + vrow;
-                                    p.st_u[at] = __builtin_bit_cast(u16, ub[e]);
-                                    p.st_r[at] = __builtin_bit_cast(u16, rb[it][e]);
+                                    p.st_u[at] = ub[e];
+                                    p.st_r[at] = rr[e];
                                 }
                             }
                         }
