@@ -385,21 +385,23 @@ la_status gla_chunk_bwd(const void* q, const void* k, const void* v, const float
  * Backward of gdelta_chunk_fwd: reverse-mode gradients of the gated delta rule
  * ("Scrivere meglio nella memoria", section "Unire oblio e correzione: Gated
  * DeltaNet") for L = <dout, o> + <ds_out, s_out>, through the chunkwise UT form
- * (section "Correggere: la delta rule").  Each chunk is a linear map of the
- * memory entering it, so the memory's gradient is carried back through the
- * chunks (chunk by chunk, like the forward's memory) and every chunk's input
- * gradients then follow independently.  Inputs as for gdelta_chunk_fwd plus
- * dout [B][H][T][d_v] (bf16) and ds_out [B][H][d_v][d_k] float32 (NULL: zero);
- * outputs dq, dk [B][H][T][d_k] and dv [B][H][T][d_v] (bf16), dlog_alpha and
- * dbeta [B][H][T] float32, and, if not NULL, ds0 [B][H][d_v][d_k] float32.
- * The forward is not needed beforehand (its memory is recomputed).  Only
- * LA_BF16 storage; chunk 16, 32 or 64.  The workspace size comes from
+ * (section "Correggere: la delta rule").  The memory entering every chunk is
+ * recomputed chunk by chunk (at chunk 64 with d_k >= 32: by the forward single
+ * pass, which also records the chunk's pseudo-values), the memory's gradient is
+ * carried back through the chunks the same way (at chunk 64: the single pass
+ * run in reverse), and every chunk's input gradients then follow independently.
+ * Inputs as for gdelta_chunk_fwd plus dout [B][H][T][d_v] (bf16) and ds_out
+ * [B][H][d_v][d_k] float32 (NULL: zero); outputs dq, dk [B][H][T][d_k] and dv
+ * [B][H][T][d_v] (bf16), dlog_alpha and dbeta [B][H][T] float32, and, if not
+ * NULL, ds0 [B][H][d_v][d_k] float32.  The forward is not needed beforehand.
+ * Only LA_BF16 storage; chunk 16, 32 or 64.  The workspace size comes from
  * gdelta_chunk_bwd_workspace_size: with N = B * H * ceil(T / chunk), C = chunk
  * and a(x) as for la_chunk_bwd: 2 a(N*C*C*2) + a(N*C*4) (T_U, T, the gates),
- * a(N*d_k*C*2) + 2 a(N*d_k*d_k*2) (each chunk's map), 3 a(N*d_v*d_k*2) (its
- * write, the memory entering it and the gradient leaving it), and a scratch of
- * a(min(N, 512) * (6 C d_k + 3 C d_v + 6 C^2 + d_k^2) * 4) bytes.  Other
- * conventions and errors as for la_chunk_bwd.
+ * a(N*d_k*C*2) + 2 a(N*d_k*d_k*2) (each chunk's linear map, chunks 16 and 32),
+ * 3 a(N*d_v*d_k*2) (its write, the memory entering it and the gradient leaving
+ * it), 3 a(N*C*d_v*2) (the pseudo-values U and R and dU, chunk 64) and a
+ * scratch of a(min(N, 512) * (6 C d_k + 3 C d_v + 6 C^2 + d_k^2) * 4) bytes.
+ * Other conventions and errors as for la_chunk_bwd.
  */
 la_status gdelta_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk,
                                           la_dtype dtype, size_t* bytes);

@@ -299,7 +299,8 @@ def test_gdelta_backward_validation(lib):
     assert lib.gdelta_chunk_bwd_workspace_size(4, 16, 8192, 128, 128, 64, 1, ctypes.byref(need)) == _native.LA_OK
     N, C, d = 4 * 16 * 128, 64, 128
     want = (2 * a256(N * C * C * 2) + a256(N * C * 4) + a256(N * d * C * 2) + 2 * a256(N * d * d * 2)
-            + 3 * a256(N * d * d * 2) + a256(min(N, 512) * (6 * C * d + 3 * C * d + 6 * C * C + d * d) * 4))
+            + 3 * a256(N * d * d * 2) + 3 * a256(N * C * d * 2)
+            + a256(min(N, 512) * (6 * C * d + 3 * C * d + 6 * C * C + d * d) * 4))
     assert need.value == want
 
 
