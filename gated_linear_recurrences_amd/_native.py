@@ -23,6 +23,8 @@ EXPORTED = (
     "gdelta_chunk_fwd",
     "gdelta_chunk_fwd_fused",
     "gla_chunk_fwd_fused",
+    "la_chunk_fwd_fused",
+    "mamba2_chunk_fwd_fused",
     "gdelta_chunk_fwd_noalloc",
     "la_recurrent_step",
     "gdelta_recurrent_step",
@@ -70,6 +72,8 @@ def load():
     lib.gdelta_chunk_fwd_fused.argtypes = [P, P, P, F, F, F, P, F, F, ctypes.c_float, I,
                                            I, I, I, I, I, I, I, P, Z, P]
     lib.gla_chunk_fwd_fused.argtypes = [P, P, P, F, F, P, F, F, F, ctypes.c_float, I, I, I, I, I, I, I, I, P, Z, P]
+    lib.la_chunk_fwd_fused.argtypes = lib.gla_chunk_fwd_fused.argtypes
+    lib.mamba2_chunk_fwd_fused.argtypes = lib.gla_chunk_fwd_fused.argtypes
     lib.gdelta_chunk_fwd_noalloc.argtypes = [P, P, P, F, F, F, P, F, I, I, I, I, I, I, I, P]
     lib.la_chunk_workspace_size.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_size_t)]
     lib.la_chunk_workspace_size.restype = ctypes.c_int
@@ -90,7 +94,8 @@ def load():
     lib.vla_fwd.argtypes = [P, P, P, P, ctypes.c_float, F, F, F, P, F, F, F, I, I, I, I, I, I, I, P]
     lib.vla_recurrent_step.argtypes = [P, P, P, P, F, F, F, P, I, I, I, I, I, I, P]
     for name in ("la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-                 "gdelta_chunk_fwd_noalloc", "gla_chunk_fwd_fused", "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "gdelta_chunk_bwd", "vla_fwd",
+                 "gdelta_chunk_fwd_noalloc", "gla_chunk_fwd_fused", "la_chunk_fwd_fused",
+                 "mamba2_chunk_fwd_fused", "la_recurrent_step", "gdelta_recurrent_step", "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "gdelta_chunk_bwd", "vla_fwd",
                  "vla_recurrent_step"):
         getattr(lib, name).restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]

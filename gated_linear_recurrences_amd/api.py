@@ -13,7 +13,8 @@ import torch
 from . import _native
 
 __all__ = ["la_chunk_fwd", "mamba2_chunk_fwd", "gla_chunk_fwd", "gdelta_chunk_fwd", "gdelta_chunk_fwd_fused",
-           "gdelta_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "gla_chunk_fwd_fused",
+           "gdelta_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "gla_chunk_fwd_fused", "la_chunk_fwd_fused",
+           "mamba2_chunk_fwd_fused",
            "la_chunk_bwd", "mamba2_chunk_bwd", "gla_chunk_bwd", "gdelta_chunk_bwd", "la_recurrent_step", "gdelta_recurrent_step",
            "vla_fwd", "vla_recurrent_step", "workspace_size", "bwd_workspace_size"]
 
@@ -169,6 +170,40 @@ def gla_chunk_fwd_fused(q, k, v, log_alpha, o_norm_weight, o_norm_bias=None, o_n
                                           _native.LA_FUSE_OUT_LAYERNORM, B, H, T, dk, dv, chunk, _dtype_code(q),
                                           _ptr(ws), ws_bytes, _stream(q.device)))
     return o, s_out
+
+
+def _norm_fused(fn, variant, gate, gate_shape, q, k, v, o_norm_weight, o_norm_bias, o_norm_eps, norm, chunk, s0, o,
+                s_out, return_state, workspace):
+    dims, o, s_out = _chunk_common(q, k, v, s0, o, s_out, return_state)
+    B, H, T, dk, dv = dims
+    _require(gate, "gate", gate_shape(B, H, T, dk), torch.float32, q.device)
+    _require(o_norm_weight, "o_norm_weight", (dv,), torch.float32, q.device)
+    if o_norm_bias is not None:
+        _require(o_norm_bias, "o_norm_bias", (dv,), torch.float32, q.device)
+    fuse = {"rms": _native.LA_FUSE_OUT_RMSNORM, "layer": _native.LA_FUSE_OUT_LAYERNORM}[norm]
+    ws, ws_bytes = _workspace(variant, dims, chunk, q, workspace)
+    lib = _native.load()
+    _native.check(getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(s0), _ptr(o), _ptr(s_out),
+                                   _ptr(o_norm_weight), _ptr(o_norm_bias), float(o_norm_eps), fuse, B, H, T, dk, dv,
+                                   chunk, _dtype_code(q), _ptr(ws), ws_bytes, _stream(q.device)))
+    return o, s_out
+
+
+def la_chunk_fwd_fused(q, k, v, log_gamma, o_norm_weight, o_norm_bias=None, o_norm_eps=1e-5, norm="layer", chunk=64,
+                       s0=None, o=None, s_out=None, return_state=True, workspace=None):
+    """la_chunk_fwd with an output norm over each row of d_v values: ``norm="layer"`` (centred,
+    divided by sqrt(var + eps), times ``o_norm_weight`` plus ``o_norm_bias`` or nothing) or
+    ``norm="rms"`` (divided by sqrt(mean square + eps), times ``o_norm_weight``; no bias).
+    Returns (o, s_out); s_out is the memory."""
+    return _norm_fused("la_chunk_fwd_fused", _native.LA_RETENTION, log_gamma, lambda B, H, T, dk: (H,), q, k, v,
+                       o_norm_weight, o_norm_bias, o_norm_eps, norm, chunk, s0, o, s_out, return_state, workspace)
+
+
+def mamba2_chunk_fwd_fused(q, k, v, log_alpha, o_norm_weight, o_norm_bias=None, o_norm_eps=1e-5, norm="layer",
+                           chunk=64, s0=None, o=None, s_out=None, return_state=True, workspace=None):
+    """mamba2_chunk_fwd with an output norm, as la_chunk_fwd_fused."""
+    return _norm_fused("mamba2_chunk_fwd_fused", _native.LA_MAMBA2, log_alpha, lambda B, H, T, dk: (B, H, T), q, k, v,
+                       o_norm_weight, o_norm_bias, o_norm_eps, norm, chunk, s0, o, s_out, return_state, workspace)
 
 
 NOALLOC_SCRATCH_BYTES = 96 << 20   # the fixed workspace of gdelta_chunk_fwd_noalloc, per device

@@ -978,6 +978,55 @@ void rms_rows_bf16_kernel(u16* o, const float* weight, float eps, int64_t rows) 
     }
 }
 
+// Layer norm of bf16 output rows in place (the output norm of retention and the scalar decay
+// when fused in): the row's mean, then its variance about the mean, both over the DV values
+// in fp32; o <- (o - mean) / sqrt(var + eps) * weight + bias (bias may be null). Lanes as in
+// rms_rows_bf16_kernel.
+template <int DV>
+__global__ __launch_bounds__(256)
+void layernorm_rows_bf16_kernel(u16* o, const float* weight, const float* bias, float eps, int64_t rows) {
+    constexpr int PER = DV / 16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t row = (static_cast<int64_t>(blockIdx.x) * 256 + tid) / 16;
+    const int part = lane & 15;
+    const bool live = row < rows;
+    u16* r = o + (live ? row : 0) * DV + part * PER;
+    float x[PER];
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        x[e] = bf16_bits_to_f32(r[e]);
+        s += x[e];
+    }
+    const float mean = row16_sum(s) / static_cast<float>(DV);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) ss += (x[e] - mean) * (x[e] - mean);
+    const float inv = 1.f / __builtin_sqrtf(row16_sum(ss) / static_cast<float>(DV) + eps);
+    if (live) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int c = part * PER + e;
+            r[e] = f32_to_bf16_bits((x[e] - mean) * inv * weight[c] + (bias != nullptr ? bias[c] : 0.f));
+        }
+    }
+}
+
+// The output norm as a pass over bf16 rows [rows][DV]: RMS (fuse bit 1) or layer norm (bit 2).
+template <int DV>
+hipError_t launch_norm_rows_bf16(const ChunkArgs& a, hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(a.B) * a.H * a.T;
+    if (rows == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((rows * 16 + 255) / 256));
+    if (a.fuse & 4)
+        hipLaunchKernelGGL((layernorm_rows_bf16_kernel<DV>), grid, dim3(256), 0, stream, static_cast<u16*>(a.o), a.onw,
+                           a.onb, a.oeps, rows);
+    else
+        hipLaunchKernelGGL((rms_rows_bf16_kernel<DV>), grid, dim3(256), 0, stream, static_cast<u16*>(a.o), a.onw, a.oeps,
+                           rows);
+    return hipGetLastError();
+}
+
 // ====================================================================== launch
 template <int C, int DK, int DV>
 hipError_t launch_dsp_dv(const ChunkArgs& a, hipStream_t stream) {

@@ -187,6 +187,41 @@ la_status gla_chunk_fwd_fused(const void* q, const void* k, const void* v, const
     return run_chunk(glr::kGLA, a, dtype, workspace_bytes, stream);
 }
 
+// Retention and the scalar decay with an output norm: RMS (weight) or layer norm (weight,
+// optional bias), exactly one of the two.
+static la_status run_norm_fused(glr::Variant variant, const void* q, const void* k, const void* v, const float* gate,
+                                const float* s0, void* o, float* s_out, const float* w, const float* b, float eps,
+                                int fuse, int B, int H, int T, int dk, int dv, int chunk, la_dtype dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (fuse != LA_FUSE_OUT_RMSNORM && fuse != LA_FUSE_OUT_LAYERNORM)
+        return fail(LA_ERR_INVALID, "%s", "fuse must be LA_FUSE_OUT_RMSNORM or LA_FUSE_OUT_LAYERNORM");
+    const bool rows = B > 0 && H > 0 && T > 0;
+    la_status st = check_ptr(w, rows, false, "o_norm_weight");
+    if (st != LA_OK) return st;
+    if (fuse == LA_FUSE_OUT_RMSNORM && b != nullptr) return fail(LA_ERR_INVALID, "%s", "the RMS norm takes no bias");
+    if ((st = check_ptr(b, rows, true, "o_norm_bias")) != LA_OK) return st;
+    if (!(eps >= 0.f)) return fail(LA_ERR_INVALID, "%s", "o_norm_eps must be >= 0");
+    glr::ChunkArgs a{q, k, v, gate, nullptr, s0, o, s_out, B, H, T, dk, dv, chunk, workspace, fuse, w, eps, b};
+    return run_chunk(variant, a, dtype, workspace_bytes, stream);
+}
+
+la_status la_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_gamma, const float* s0,
+                             void* o, float* s_out, const float* o_norm_weight, const float* o_norm_bias,
+                             float o_norm_eps, int fuse, int B, int H, int T, int dk, int dv, int chunk,
+                             la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_norm_fused(glr::kRetention, q, k, v, log_gamma, s0, o, s_out, o_norm_weight, o_norm_bias, o_norm_eps,
+                          fuse, B, H, T, dk, dv, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+la_status mamba2_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* s0, void* o, float* s_out, const float* o_norm_weight,
+                                 const float* o_norm_bias, float o_norm_eps, int fuse, int B, int H, int T, int dk,
+                                 int dv, int chunk, la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    return run_norm_fused(glr::kScalar, q, k, v, log_alpha, s0, o, s_out, o_norm_weight, o_norm_bias, o_norm_eps,
+                          fuse, B, H, T, dk, dv, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
 static la_status run_bwd(glr::Variant variant, const glr::BwdArgs& a, la_dtype dtype, size_t ws_bytes,
                          void* stream) {
     // the forward's checks on q, k, v, the gate and the dimensions (o stands for the gradients)
@@ -414,6 +449,6 @@ const char* la_status_str(la_status status) {
 
 const char* la_last_error(void) { return g_last_error; }
 
-int la_version(void) { return (3 << 16) | 3; }
+int la_version(void) { return (3 << 16) | 4; }
 
 }  // extern "C"

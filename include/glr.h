@@ -258,6 +258,35 @@ la_status gla_chunk_fwd_fused(const void* q, const void* k, const void* v,
                               la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * la_chunk_fwd and mamba2_chunk_fwd with an output norm (the gates page, section
+ * "Correggere: la delta rule": an output normalisation after the readout, a
+ * LayerNorm in GLA and an RMS norm in DeltaNet; here either one, chosen by fuse).
+ * fuse = LA_FUSE_OUT_RMSNORM: every output row o (d_v values of one token and
+ * head) becomes o / sqrt(mean(o^2) + o_norm_eps) * o_norm_weight, and
+ * o_norm_bias must be NULL.  fuse = LA_FUSE_OUT_LAYERNORM: the row becomes
+ * (o - mean(o)) / sqrt(var(o) + o_norm_eps) * o_norm_weight + o_norm_bias
+ * (o_norm_bias may be NULL: no shift).  o_norm_weight, o_norm_bias [d_v]
+ * float32; o_norm_eps >= 0; statistics in fp32.  The value channels of a row
+ * are computed by several workgroups, so the norm is a pass over the stored
+ * rows after the chunk kernels (bf16 rows in place, rounded once more).
+ * Any other fuse value is LA_ERR_INVALID.  s_out is the memory itself.
+ * Workspace, other arguments and errors as for la_chunk_fwd / mamba2_chunk_fwd.
+ */
+la_status la_chunk_fwd_fused(const void* q, const void* k, const void* v,
+                             const float* log_gamma, const float* s0, void* o, float* s_out,
+                             const float* o_norm_weight, const float* o_norm_bias,
+                             float o_norm_eps, int fuse, int B, int H, int T, int dk, int dv,
+                             int chunk, la_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+la_status mamba2_chunk_fwd_fused(const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* s0, void* o,
+                                 float* s_out, const float* o_norm_weight,
+                                 const float* o_norm_bias, float o_norm_eps, int fuse,
+                                 int B, int H, int T, int dk, int dv, int chunk,
+                                 la_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * One decode token for N sequences x H heads with a per-key-channel gate (the
  * recurrent form of the RetNet page, section on retention: the same two
  * gestures for every token at constant memory; a fixed decay is the constant
@@ -423,7 +452,8 @@ const char* la_last_error(void);
  * 2.4: la_chunk_bwd, mamba2_chunk_bwd; 2.5: vla_fwd, vla_recurrent_step; 2.6: gla_chunk_bwd;
  * 2.7: single-pass retention and scalar-decay forward, no workspace at B * H * d_v / 16 >= 128;
  * 3.0: vla_fwd and vla_recurrent_step take the readout and the denominator vector;
- * 3.1: gdelta_chunk_fwd_noalloc; 3.2: gla_chunk_fwd_fused; 3.3: gdelta_chunk_bwd). */
+ * 3.1: gdelta_chunk_fwd_noalloc; 3.2: gla_chunk_fwd_fused; 3.3: gdelta_chunk_bwd;
+ * 3.4: la_chunk_fwd_fused, mamba2_chunk_fwd_fused). */
 int la_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 3        # 3.0: the VLA entry points take the readout and its denominator
-    assert lib.la_version() & 0xFFFF >= 3     # 3.1: noalloc; 3.2: gla_chunk_fwd_fused; 3.3: gdelta_chunk_bwd
+    assert lib.la_version() & 0xFFFF >= 4     # 3.1: noalloc; 3.2: gla_chunk_fwd_fused; 3.3: gdelta_chunk_bwd;
+    #                                           3.4: la_chunk_fwd_fused, mamba2_chunk_fwd_fused
     assert lib.la_status_str(0) == b"ok"
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape"
@@ -235,6 +236,33 @@ def test_gla_fused_validation(lib):
     assert call(_native.LA_FUSE_OUT_LAYERNORM, gate=None) == _native.LA_ERR_INVALID
     assert call(_native.LA_FUSE_OUT_LAYERNORM, B=0, q=None, k=None, v=None, o=None, gate=None,
                 weight=None) == _native.LA_OK
+
+
+@pytest.mark.parametrize("fn", ["la_chunk_fwd_fused", "mamba2_chunk_fwd_fused"])
+def test_norm_fused_validation(lib, fn):
+    P = ctypes.c_void_p
+
+    def call(fuse, weight=FAKE, bias=None, eps=1e-5, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, o=FAKE, B=1, H=1, T=8, dk=16, dv=16, chunk=16)
+        a.update(kw)
+        return getattr(lib, fn)(P(a["q"]), P(a["k"]), P(a["v"]), P(a["gate"]), None, P(a["o"]), None,
+                                P(weight), P(bias), eps, fuse, a["B"], a["H"], a["T"], a["dk"], a["dv"],
+                                a["chunk"], 1, P(FAKE), 1 << 30, None)
+
+    for flag in (0, _native.LA_FUSE_QK_SILU_L2, _native.LA_FUSE_OUT_RMSNORM | _native.LA_FUSE_OUT_LAYERNORM, 8):
+        assert call(flag) == _native.LA_ERR_INVALID
+        assert b"fuse must be" in lib.la_last_error()
+    for flag in (_native.LA_FUSE_OUT_RMSNORM, _native.LA_FUSE_OUT_LAYERNORM):
+        assert call(flag, weight=None) == _native.LA_ERR_INVALID
+        assert b"o_norm_weight is NULL" in lib.la_last_error()
+        assert call(flag, weight=MISALIGNED) == _native.LA_ERR_INVALID
+        assert call(flag, eps=-1.0) == _native.LA_ERR_INVALID
+        assert call(flag, eps=float("nan")) == _native.LA_ERR_INVALID
+        assert call(flag, gate=None) == _native.LA_ERR_INVALID
+        assert call(flag, B=0, q=None, k=None, v=None, o=None, gate=None, weight=None) == _native.LA_OK
+    assert call(_native.LA_FUSE_OUT_RMSNORM, bias=FAKE) == _native.LA_ERR_INVALID
+    assert b"no bias" in lib.la_last_error()
+    assert call(_native.LA_FUSE_OUT_LAYERNORM, bias=MISALIGNED) == _native.LA_ERR_INVALID
 
 
 def test_backward_validation(lib):

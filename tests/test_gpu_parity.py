@@ -382,6 +382,40 @@ def test_gla_layernorm_fused_full_size_parity():
                       f"gla layernorm full size sequence {bi}", normed=True)
 
 
+# (B, H, T, d_k, d_v, chunk): two-pass shapes (few sequences), single-pass ones (chunk 64 on the
+# gated delta rule's pass, 16-, 32- and 64-channel slices; chunk 16 on fused_kernel)
+NORM_SHAPES = [(1, 2, 100, 16, 16, 16), (2, 1, 77, 32, 64, 32), (4, 8, 150, 128, 64, 64), (4, 16, 130, 128, 128, 64),
+               (4, 64, 70, 128, 128, 64), (8, 8, 70, 64, 32, 16)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("norm", ["rms", "layer", "layer_bias"])
+@pytest.mark.parametrize("kind", ["retention", "mamba2"])
+@pytest.mark.parametrize("shape", NORM_SHAPES)
+def test_norm_fused_parity(shape, kind, norm, dtype):
+    """Retention and the scalar decay with their output norm fused in, against the oracle's
+    chunkwise output then rms_norm or layer_norm (fp64), under the relative bound of
+    normalised rows; the memory is untouched by the norm."""
+    B, H, T, dk, dv, c = shape
+    w = make(kind, B, H, T, dk, dv, c, dtype, 800 + sum(shape), True)
+    rng = np.random.default_rng(sum(shape) + 3)
+    weight = rng.uniform(0.5, 1.5, dv).astype(np.float32)
+    bias = rng.standard_normal(dv).astype(np.float32) * 0.5 if norm == "layer_bias" else None
+    st = _storage(w)
+    q, k, v = _t(w.q, st), _t(w.k, st), _t(w.v, st)
+    kw = dict(o_norm_bias=_t(bias) if bias is not None else None, o_norm_eps=1e-5,
+              norm="rms" if norm == "rms" else "layer", chunk=c, s0=_t(w.s0))
+    if kind == "retention":
+        out, S = api.la_chunk_fwd_fused(q, k, v, _t(w.log_gamma), _t(weight), **kw)
+    else:
+        out, S = api.mamba2_chunk_fwd_fused(q, k, v, _t(w.log_alpha), _t(weight), **kw)
+    torch.cuda.synchronize()
+    o_plain, S_ref = run_oracle(w)
+    o_ref = orc.rms_norm(o_plain, weight, 1e-5) if norm == "rms" else orc.layer_norm(o_plain, weight, bias, 1e-5)
+    assert_parity(w, out.float().cpu().numpy().astype(np.float64), S.cpu().numpy().astype(np.float64), o_ref, S_ref,
+                  f"{kind} {norm} {dtype} {shape}", normed=True)
+
+
 # ----------------------------------------------------------------------------- backward
 
 BWD_SHAPES = [(1, 2, 100, 16, 16, 16), (2, 1, 77, 32, 64, 32), (1, 2, 130, 64, 32, 64), (2, 2, 200, 128, 128, 64),
