@@ -550,7 +550,7 @@ hipError_t launch_gdelta_bwd_dv(const BwdArgs& a, hipStream_t stream) {
             fp.st_s = p.sin;
             fp.st_u = rec_u;
             fp.st_r = rec_r;
-            hipLaunchKernelGGL((delta_sp_kernel<C, DK, DV, VS, kGateDeltaRule, 1, false>), dim3(static_cast<unsigned>(grid)),
+            hipLaunchKernelGGL((delta_sp_kernel<C, DK, DV, VS, kGateDeltaRule, 1, false, true>), dim3(static_cast<unsigned>(grid)),
                                dim3(256), 0, stream, fp);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             rp.v = p.dout;

@@ -88,10 +88,10 @@ struct DspParams {
     u16* kmap;
     int T, NC, slices, remap, map;
     int H;                // heads (the fixed gate: alpha then holds log gamma [H])
-    // the backward's per-chunk records (null: none). Forward: st_s the memory entering each
-    // chunk [BH * NC][DV][DK], st_u the pseudo-values U and st_r R = V - diag(e^G) K S_in^T
+    // the backward's per-chunk records. Forward with REC: st_s the memory entering each chunk
+    // [BH * NC][DV][DK], st_u the pseudo-values U and st_r R = V - diag(e^G) K S_in^T
     // [BH * NC][C][DV], all bf16 (o may then be null). Reverse pass: st_s the gradient of the
-    // memory leaving each chunk, st_u dU; o receives dV.
+    // memory leaving each chunk (or null), st_u dU; o receives dV.
     u16* st_s;
     u16* st_u;
     u16* st_r;
@@ -336,7 +336,7 @@ __device__ __forceinline__ bf16x4 tr4(const u16* p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 
-template <int C, int DK, int DV, int VS, int GK, int VW = 1, bool REV = false>
+template <int C, int DK, int DV, int VS, int GK, int VW = 1, bool REV = false, bool REC = false>
 __global__ __launch_bounds__(256)
 void delta_sp_kernel(DspParams p) {
     constexpr bool DELTA = GK == kGateDeltaRule;
@@ -664,7 +664,7 @@ void delta_sp_kernel(DspParams p) {
                             ul[jb] = join8(cvt4(u[2 * jb] - up4(h0)), cvt4(u[2 * jb + 1] - up4(h1)));
                             wb[jb] = join8(cvt4(u[2 * jb] * wt[2 * jb]), cvt4(u[2 * jb + 1] * wt[2 * jb + 1]));
                         }
-                        if (p.st_s != nullptr) {
+                        if constexpr (REC) {
                             // the backward's records of the chunk: S_in rows (keys 32kb + 8g .. + 7
                             // of value row vrow), U and R at (token 16it + 4g + e, value vrow)
                             const int64_t gc = static_cast<int64_t>(bh) * NC + c;
