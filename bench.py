@@ -59,11 +59,11 @@ N_SETS = {"gdelta_b4h16_t8192_d128": 2, "retention_b4h8_t2048_d128": 5, "gla_b8h
 # library kernels of one call of each chunked workload (d_k = d_v = 128, chunk 64), as rocprofv3 names them
 WORKLOAD_KERNELS = {
     "gdelta_b4h16_t8192_d128": ("glr::ck::delta_tfac_kernel<64, 128>",
-                                "glr::ck::delta_sp_kernel<64, 128, 128, 32, 3, 1, false>"),
-    "retention_b4h8_t2048_d128": ("glr::ck::delta_sp_kernel<64, 128, 128, 16, 0, 1, false>",),
+                                "glr::ck::delta_sp_kernel<64, 128, 128, 32, 3, 1, false, false>"),
+    "retention_b4h8_t2048_d128": ("glr::ck::delta_sp_kernel<64, 128, 128, 16, 0, 1, false, false>",),
     "gla_b8h16_t4096_d128": ("glr::ck::state_kernel<64, 128, 4, 1, 8, 1, 1, false>",
                              "glr::ck::output_kernel<64, 128, 128, 1, 8>"),
-    "mamba2_b8h16_t4096_d128": ("glr::ck::delta_sp_kernel<64, 128, 128, 64, 2, 2, false>",),
+    "mamba2_b8h16_t4096_d128": ("glr::ck::delta_sp_kernel<64, 128, 128, 64, 2, 2, false, false>",),
 }
 
 
