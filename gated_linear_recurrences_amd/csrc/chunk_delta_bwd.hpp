@@ -15,7 +15,12 @@
 // and with the memory entering and the gradient leaving every chunk known, each chunk's input
 // gradients are independent (the products are listed in grads_kernel).
 //
-// Kernels, in order on the stream:
+// At chunk 64 with d_k >= 32 the call takes the single-pass form instead (launch below): the
+// prep, the forward single pass recording S_in, U and R per chunk, the same pass in reverse
+// for dS', dU, dV and ds0 (chunk_delta_sp.hpp), and gd_grads_kernel (chunk_delta_grads.hpp;
+// d_v = 16 keeps grads_kernel). Chunks 16 and 32 take the linear-map form here.
+//
+// Linear-map kernels, in order on the stream:
 //   prep     delta_tfac_kernel (G, T_U, and T itself), all chunks in parallel;
 //   maps     maps_kernel: W, U0, P, then Qt^T, Mp, Mp^T and N per chunk (bf16, workspace);
 //   forward  fwd_chain_kernel: per (sequence, 16 value rows), the memory entering every chunk

@@ -1,5 +1,7 @@
 // Single-pass chunked forward for retention and the scalar data-dependent decay (bf16
-// storage): the memory never leaves the chip.
+// storage): the memory never leaves the chip. Chunks 16 and 32 and d_k = 16; chunk 64 with
+// d_k >= 32 takes the gated delta rule's single pass without its delta step
+// (chunk_delta_sp.hpp).
 //
 // Method: the chunkwise form of retention ("Le architetture lineari: RetNet, RWKV,
 // xLSTM", section "RetNet: la retention e le sue tre forme", Fig. 16.5) and its
