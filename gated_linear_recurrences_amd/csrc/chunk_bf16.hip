@@ -21,6 +21,7 @@ size_t chunk_workspace_bytes(Variant variant, const ChunkArgs& a, bool bf16) {
     if (!bf16 || a.B == 0 || a.H == 0) return 0;
     const size_t chunks = static_cast<size_t>((a.T + a.chunk - 1) / a.chunk);
     if (single_pass_forward(variant, a)) return 0;
+    if (variant == kGLA && gla_single_pass(a)) return 0;
     if (variant == kGDelta && delta_single_pass(a))
         return ck::dsp_ws_bytes(static_cast<int64_t>(a.B) * a.H * chunks, a.chunk, a.dk, (a.fuse & 1) != 0);
     if (variant == kGDelta)
@@ -57,7 +58,11 @@ hipError_t launch_chunk_bf16(Variant variant, const ChunkArgs& a, hipStream_t st
         case kGLA:
             if (a.chunk == 16) return launch_chunk_bf16_gla_c16(a, stream);
             if (a.chunk == 32) return launch_chunk_bf16_gla_c32(a, stream);
-            if (a.chunk == 64) return launch_chunk_bf16_gla_c64(a, stream);
+            // the single pass leaves GLA's layer norm to a pass over the rows (the two-pass
+            // output kernel applies it in place)
+            if (a.chunk == 64)
+                return gla_single_pass(a) ? norm_rows_bf16(launch_chunk_bf16_gla_c64(a, stream), a, stream)
+                                          : launch_chunk_bf16_gla_c64(a, stream);
             break;
         case kGDelta:
             if (a.chunk == 16) return launch_chunk_bf16_gdelta_c16(a, stream);

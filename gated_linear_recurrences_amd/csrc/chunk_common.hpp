@@ -127,6 +127,12 @@ __device__ __forceinline__ bf16x4 tr_op_s(const u16* X, int base, int n0, int r1
     return __builtin_bit_cast(bf16x4, v);
 }
 
+// ds_read_b64_tr_b16 at a lane's own address: the four 16-bit values a lane reads are
+// handed to the four lanes of its column quad, one each (see tr_op_s).
+__device__ __forceinline__ bf16x4 tr4(const u16* p) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+
 template <int W>
 __device__ __forceinline__ bf16x8 tr_split_s(const u16* X, int jb, int n0, bool hi, int r16, int g) {
     return join8(tr_op_s<W>(X, 32 * jb, n0, r16, g), hi ? tr_op_s<W>(X, 32 * jb + 16, n0, r16, g) : zero4());

@@ -330,12 +330,6 @@ struct DspLayout {
     static_assert(bytes <= 160 * 1024, "LDS budget of the delta single pass exceeded");
 };
 
-// ds_read_b64_tr_b16 at a lane's own address: the four 16-bit values a lane reads are
-// handed to the four lanes of its column quad, one each (see tr_op_s).
-__device__ __forceinline__ bf16x4 tr4(const u16* p) {
-    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
-}
-
 template <int C, int DK, int DV, int VS, int GK, int VW = 1, bool REV = false, bool REC = false>
 __global__ __launch_bounds__(256)
 void delta_sp_kernel(DspParams p) {
@@ -1003,12 +997,21 @@ void layernorm_rows_bf16_kernel(u16* o, const float* weight, const float* bias, 
 #pragma unroll
     for (int e = 0; e < PER; ++e) ss += (x[e] - mean) * (x[e] - mean);
     const float inv = 1.f / __builtin_sqrtf(row16_sum(ss) / static_cast<float>(DV) + eps);
+    // the scale and shift of this lane's channels, loaded outside the store loop (a load under
+    // a condition there keeps the row's stores from merging into one)
+    float wv[PER], bv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        wv[e] = weight[part * PER + e];
+        bv[e] = 0.f;
+    }
+    if (bias != nullptr) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) bv[e] = bias[part * PER + e];
+    }
     if (live) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int c = part * PER + e;
-            r[e] = f32_to_bf16_bits((x[e] - mean) * inv * weight[c] + (bias != nullptr ? bias[c] : 0.f));
-        }
+        for (int e = 0; e < PER; ++e) r[e] = f32_to_bf16_bits((x[e] - mean) * inv * wv[e] + bv[e]);
     }
 }
 

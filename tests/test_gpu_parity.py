@@ -189,6 +189,26 @@ def test_bf16_gla_dk16_many_heads(shape):
     assert_parity(w, o, S, o_ref, S_ref, f"gla d_k=16 {shape}")
 
 
+# GLA takes its own single pass at chunk 64 with d_k >= 32 under the same rule: the chunk-64
+# shapes above (16-, 32- and 64-channel value slices, d_k 32, 64 and 128, ragged tails, a lone
+# partial chunk, T = 1 and T = 0).
+GLA_SINGLE_PASS_SHAPES = [s for s in SINGLE_PASS_SHAPES if s[5] == 64 and s[3] >= 32]
+
+
+@pytest.mark.parametrize("shape", GLA_SINGLE_PASS_SHAPES)
+@pytest.mark.parametrize("state", [False, True])
+def test_bf16_gla_single_pass_parity(shape, state):
+    B, H, T, dk, dv, chunk = shape
+    assert api.workspace_size("gla", *shape) == 0
+    w = make("gla", *shape, dtype="bf16", seed=600 + sum(shape), state=state)
+    o, S = run_gpu(w)
+    o_ref, S_ref = run_oracle(w)
+    if T == 0:
+        np.testing.assert_array_equal(S, w.s0.astype(np.float64) if state else 0.0)
+        return
+    assert_parity(w, o, S, o_ref, S_ref, f"gla single pass {shape} state={state}")
+
+
 @pytest.mark.parametrize("kind", ["retention", "mamba2"])
 @pytest.mark.parametrize("shape", [(4, 8, 150, 128, 64, 64), (2, 64, 70, 64, 32, 32)])
 def test_bf16_single_pass_strong_decay(kind, shape):
