@@ -61,8 +61,7 @@ WORKLOAD_KERNELS = {
     "gdelta_b4h16_t8192_d128": ("glr::ck::delta_tfac_kernel<64, 128>",
                                 "glr::ck::delta_sp_kernel<64, 128, 128, 32, 3, 1, false, false>"),
     "retention_b4h8_t2048_d128": ("glr::ck::delta_sp_kernel<64, 128, 128, 16, 0, 1, false, false>",),
-    "gla_b8h16_t4096_d128": ("glr::ck::state_kernel<64, 128, 4, 1, 8, 1, 1, false>",
-                             "glr::ck::output_kernel<64, 128, 128, 1, 8>"),
+    "gla_b8h16_t4096_d128": ("glr::ck::gla_sp_kernel<128, 128, 64>",),
     "mamba2_b8h16_t4096_d128": ("glr::ck::delta_sp_kernel<64, 128, 128, 64, 2, 2, false, false>",),
 }
 
@@ -335,8 +334,9 @@ def bench_gdelta_fused(steps, warmup, torch, api, synthetic, dev):
 
 
 def bench_gla_layernorm(steps, warmup, torch, api, synthetic, dev):
-    """The GLA workload (B8 H16 T4096 d128) with its output LayerNorm fused into the output
-    pass (gla_chunk_fwd_fused); beside it gla_chunk_fwd followed by torch's layer_norm on o."""
+    """The GLA workload (B8 H16 T4096 d128) with its output LayerNorm (gla_chunk_fwd_fused: the
+    single pass, then the library's layer norm over the output rows); beside it gla_chunk_fwd
+    followed by torch's layer_norm on o."""
     name = "gla_b8h16_t4096_d128"
     c = synthetic.CONFIGS[name]
     B, H, T, d = c["B"], c["H"], c["T"], c["dk"]

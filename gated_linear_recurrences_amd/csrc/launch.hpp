@@ -99,13 +99,13 @@ inline bool single_pass_forward(Variant variant, const ChunkArgs& a) {
            static_cast<long long>(a.B) * a.H * (a.dv / 16) >= 128;
 }
 
-// GLA (bf16 storage) at chunk 64 with d_k >= 32 takes its single pass (no workspace) under the
+// GLA (bf16 storage) at chunk 64 with d_k of 64 or 128 takes its single pass (no workspace) under the
 // same occupancy rule as retention; its buffer offsets are 31-bit (one sequence's raw gates,
 // rows padded to whole chunks, below 2^31 bytes: T below 2^22 tokens at d_k = 128).
 inline bool gla_single_pass(const ChunkArgs& a) {
     const long long rows = (static_cast<long long>(a.T) + 63) / 64 * 64;
     const long long per_row = a.dk * 4 > a.dv * 2 ? a.dk * 4 : a.dv * 2;
-    return a.chunk == 64 && a.dk >= 32 && static_cast<long long>(a.B) * a.H * (a.dv / 16) >= 128 &&
+    return a.chunk == 64 && a.dk >= 64 && static_cast<long long>(a.B) * a.H * (a.dv / 16) >= 128 &&
            rows * per_row < (1ll << 31);
 }
 

@@ -77,9 +77,10 @@ def _ws(lib, variant, B=1, H=1, T=8, dk=16, dv=16, chunk=16, dtype=1):
 def test_workspace_size_query(lib):
     # retention, the scalar decay and GLA in bf16, two-pass forward: one bf16 d_v x d_k memory
     # per (sequence, chunk). Retention and the scalar decay take the single-pass forward, with
-    # no workspace, once B * H * d_v / 16 >= 128; GLA too at chunk 64 with d_k >= 32.
+    # no workspace, once B * H * d_v / 16 >= 128; GLA too at chunk 64 with d_k of 64 or 128.
     assert _ws(lib, _native.LA_GLA, B=4, H=8, T=2048, dk=128, dv=128, chunk=64) == (_native.LA_OK, 0)
-    assert _ws(lib, _native.LA_GLA, B=4, H=4, T=100, dk=32, dv=128, chunk=64) == (_native.LA_OK, 0)
+    assert _ws(lib, _native.LA_GLA, B=4, H=4, T=100, dk=64, dv=128, chunk=64) == (_native.LA_OK, 0)
+    assert _ws(lib, _native.LA_GLA, B=4, H=4, T=100, dk=32, dv=128, chunk=64) == (_native.LA_OK, 16 * 2 * 128 * 32 * 2)
     assert _ws(lib, _native.LA_GLA, B=2, H=4, T=100, dk=64, dv=128, chunk=64) == (_native.LA_OK, 8 * 2 * 128 * 64 * 2)
     assert _ws(lib, _native.LA_GLA, B=8, H=8, T=100, dk=16, dv=128, chunk=64) == (_native.LA_OK, 64 * 2 * 128 * 16 * 2)
     assert _ws(lib, _native.LA_GLA, B=8, H=8, T=100, dk=64, dv=128, chunk=32) == (_native.LA_OK, 64 * 4 * 128 * 64 * 2)

@@ -189,10 +189,10 @@ def test_bf16_gla_dk16_many_heads(shape):
     assert_parity(w, o, S, o_ref, S_ref, f"gla d_k=16 {shape}")
 
 
-# GLA takes its own single pass at chunk 64 with d_k >= 32 under the same rule: the chunk-64
-# shapes above (16-, 32- and 64-channel value slices, d_k 32, 64 and 128, ragged tails, a lone
-# partial chunk, T = 1 and T = 0).
-GLA_SINGLE_PASS_SHAPES = [s for s in SINGLE_PASS_SHAPES if s[5] == 64 and s[3] >= 32]
+# GLA takes its own single pass at chunk 64 with d_k of 64 or 128 under the same rule: the
+# chunk-64 shapes above (16-, 32- and 64-channel value slices, ragged tails, a lone partial
+# chunk, T = 1 and T = 0).
+GLA_SINGLE_PASS_SHAPES = [s for s in SINGLE_PASS_SHAPES if s[5] == 64 and s[3] >= 64]
 
 
 @pytest.mark.parametrize("shape", GLA_SINGLE_PASS_SHAPES)
