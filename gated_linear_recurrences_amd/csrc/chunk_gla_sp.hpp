@@ -54,10 +54,26 @@ struct GspParams {
     int T, NC, slices, remap;
 };
 
+// The swizzled tile of q and k rows with its phase also turned by bits 4-5 of the row: a
+// helper's store of rows 4tq + s over the sixteen tq of a DPP row then lands on sixteen
+// different 16-byte bank groups (d_k 128; two to a group at d_k 64, four with the plain tile),
+// while every access within one 16-row block (the chain's and the triangle's reads) sees the
+// plain tile's pattern.
+template <int W>
+struct GlaTile {
+    static_assert(W == 64 || W == 128, "rows of 64 or 128 keys");
+    static constexpr int STRIDE = W;
+    __device__ static __forceinline__ int off(int r, int c) {
+        const int h = (W == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))) ^
+                      (((r >> 4) & 3) << 1);
+        return r * W + ((((c >> 3) ^ h) << 3) | (c & 7));
+    }
+};
+
 template <int DK, int VS>
 struct GspLayout {
     static constexpr int C = 64;
-    using TK = SwzTile<DK>;     // q and k rows (and their rescaled forms)
+    using TK = GlaTile<DK>;     // q and k rows (and their rescaled forms)
     using TV = SwzTile<VS>;     // the v slice
     static constexpr int RS = C + 8;
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
