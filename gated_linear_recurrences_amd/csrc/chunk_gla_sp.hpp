@@ -9,11 +9,11 @@
 //   o_t   = S_in (q_t . 2^B_t) + sum_{s <= t} [sum_c q_tc k_sc 2^(B_tc - B_sc)] v_s
 //   S_out = S_in diag(2^B_last) + sum_s v_s (k_s . 2^(B_last - B_s))^T
 //
-// One workgroup of eight waves per (sequence, value slice of VS channels), one barrier pair
-// per chunk. Chain waves 0 .. 3 each hold S^T of one 16-channel value tile in fp32 MFMA
+// One workgroup of eight waves per (sequence, value slice of VS channels), one barrier per
+// chunk. Chain waves 0 .. 3 each hold S^T of one 16-channel value tile in fp32 MFMA
 // accumulators across the chunks; helper waves 4 .. 7 make the next chunk's operands while
 // the chain works on the current one, so each SIMD runs one chain wave and one helper wave
-// (the chain's LDS waits and the helpers' VALU work overlap):
+// (the chain's LDS and MFMA waits and the helpers' VALU work overlap):
 //   - helper h owns key channels [h d_k / 4, (h + 1) d_k / 4); lane (tq, kq) loads d_k / 16
 //     of them for the four tokens 4tq .. 4tq + 3 (16-byte pieces of q and k at d_k = 128). A
 //     DPP row of 16 lanes then holds one key group's 64 tokens: the scan of the gates runs
@@ -24,18 +24,20 @@
 //     operands follow from them by one factor each: q 2^B = (q 2^(B - m)) 2^m and
 //     k 2^(B_last - B) = (k 2^(m - B)) 2^(B_last - m), both at most |q| and |k|;
 //   - when every cumulative gate of a chunk is within 2^+-100 (a bound each helper publishes
-//     one chunk ahead, so that all waves agree), the reference is the chunk's start: the
-//     triangle then takes the chain's q 2^B and k 2^-B directly, without the tile joins;
-//   - after the first barrier of a chunk the helpers split its ten tile pairs of the causal
-//     triangle, each over all keys, pairs below the diagonal joined by F = 2^(m_it - m_jt) <= 1
-//     on the q operand.
+//     two steps ahead, so that all waves agree), the reference is the chunk's start: the
+//     triangle then takes q 2^B and k 2^-B, and the carry k 2^-B with 2^B_last applied after
+//     the sum, so the helpers write two rescaled copies instead of four and no F table;
+//   - each chain wave forms the whole causal triangle itself (ten 16 x 16 tile pairs over all
+//     keys, pairs below the diagonal joined by F = 2^(m_it - m_jt) <= 1 on the q operand): a
+//     pair's accumulator is, lane for lane, the half of P V's B operand it feeds, so P stays
+//     in registers and the helpers only prepare.
 // The chain's work per chunk is that of the scalar decay with the decay of S^T taken per key
 // (one factor per accumulator) and the token weights already inside the operands.
 //
-// LDS (d_k 128, 64-channel slices): the chain's two operands in two slots, the triangle's two
-// in one, 2^B_last in two slots, the F table, the v slice in two slots and the triangle in
-// two: 134 KB. Buffer offsets are 31-bit: one sequence's raw gates (rows padded to whole
-// chunks times d_k times 4 bytes), q, k, v and o must stay below 2^31 bytes.
+// LDS (d_k 128, 64-channel slices), every buffer in two slots: the four rescaled copies of q
+// and k, 2^B_last, the F table and the v slice, 151 KB. Buffer offsets are 31-bit: one
+// sequence's raw gates (rows padded to whole chunks times d_k times 4 bytes), q, k, v and o
+// must stay below 2^31 bytes.
 #pragma once
 
 #include "chunk_common.hpp"
@@ -75,22 +77,20 @@ struct GspLayout {
     static constexpr int C = 64;
     using TK = GlaTile<DK>;     // q and k rows (and their rescaled forms)
     using TV = SwzTile<VS>;     // the v slice
-    static constexpr int RS = C + 8;
     static constexpr int al(int x) { return (x + 15) / 16 * 16; }
     static constexpr int KBUF = al(C * TK::STRIDE * 2);
     static constexpr int VBUF = al(C * TV::STRIDE * 2);
-    static constexpr int RBUF = al(C * RS * 2);
     static constexpr int EBUF = al(DK * 4);
-    static constexpr int oK = 0;                 // k 2^(B_last - B): the chain's, two slots
-    static constexpr int oQ = oK + 2 * KBUF;     // q 2^B: the chain's, two slots
-    static constexpr int oKh = oQ + 2 * KBUF;    // k 2^(m - B): the triangle's, one slot
-    static constexpr int oQh = oKh + KBUF;       // q 2^(B - m): the triangle's, one slot
-    static constexpr int oE = oQh + KBUF;        // 2^B_last per key, two slots
-    static constexpr int oF = oE + 2 * EBUF;     // F [pair][key], one slot
-    static constexpr int oV = oF + al(6 * DK * 4);   // the v slice, two slots
-    static constexpr int oP = oV + 2 * VBUF;     // the triangle, two slots
-    static constexpr int oS = oP + 2 * RBUF;     // each helper's bound on the chunk's decay, two slots
-    static constexpr int bytes = oS + 2 * 4 * 4;
+    static constexpr int FBUF = al(6 * DK * 4);
+    static constexpr int oK = 0;                 // k 2^(B_last - B): the carry's (chunks that are not flat)
+    static constexpr int oQ = oK + 2 * KBUF;     // q 2^B: the readout's
+    static constexpr int oKh = oQ + 2 * KBUF;    // k 2^(m - B): the triangle's
+    static constexpr int oQh = oKh + 2 * KBUF;   // q 2^(B - m): the triangle's (chunks that are not flat)
+    static constexpr int oE = oQh + 2 * KBUF;    // 2^B_last per key
+    static constexpr int oF = oE + 2 * EBUF;     // F [pair][key] (chunks that are not flat)
+    static constexpr int oV = oF + 2 * FBUF;     // the v slice
+    static constexpr int oS = oV + 2 * VBUF;     // each helper's bound on a chunk's decay, four slots
+    static constexpr int bytes = oS + 4 * 4 * 4;
     static_assert(bytes <= 160 * 1024, "LDS budget of the GLA single pass exceeded");
 };
 
@@ -109,7 +109,6 @@ void gla_sp_kernel(GspParams p) {
     constexpr int NV = VS / 16;                 // value tiles: chain waves 0 .. NV - 1
     constexpr int CT = C / 16, JB = CT / 2;     // token tiles, 32-token blocks
     constexpr int KT = DK / 16, KB = DK / 32;   // key tiles, 32-key blocks
-    constexpr int RS = Lay::RS;
     constexpr int QPH = DK / 4;                 // keys per helper
     constexpr int KPL = DK / 16;                // keys per helper lane (four tokens each)
     constexpr int NH = 256;                     // helper threads
@@ -120,12 +119,11 @@ void gla_sp_kernel(GspParams p) {
     __shared__ __align__(16) unsigned char smem[Lay::bytes];
     auto sK = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oK + (b & 1) * Lay::KBUF); };
     auto sQ = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oQ + (b & 1) * Lay::KBUF); };
+    auto sKh = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oKh + (b & 1) * Lay::KBUF); };
+    auto sQh = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oQh + (b & 1) * Lay::KBUF); };
     auto sE = [&](int b) { return reinterpret_cast<float*>(smem + Lay::oE + (b & 1) * Lay::EBUF); };
+    auto sF = [&](int b) { return reinterpret_cast<float*>(smem + Lay::oF + (b & 1) * Lay::FBUF); };
     auto sV = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oV + (b & 1) * Lay::VBUF); };
-    auto sP = [&](int b) { return reinterpret_cast<u16*>(smem + Lay::oP + (b & 1) * Lay::RBUF); };
-    u16* const sKh = reinterpret_cast<u16*>(smem + Lay::oKh);
-    u16* const sQh = reinterpret_cast<u16*>(smem + Lay::oQh);
-    float* const sF = reinterpret_cast<float*>(smem + Lay::oF);
     float* const sB = reinterpret_cast<float*>(smem + Lay::oS);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -144,6 +142,14 @@ void gla_sp_kernel(GspParams p) {
     constexpr int kRsrc = 0x00020000;
     auto rsrc = [](const void* base, int64_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrc);
+    };
+    // chunk a is flat when every cumulative gate in it is within 2^+-100 (the largest of the
+    // four helpers' bounds, published two steps ahead in slot a mod 4): the triangle then takes
+    // q 2^B and k 2^-B with no tile references, and the carry k 2^-B with 2^B_last applied to
+    // the sum. Every wave reads the same slot, so all take the same form.
+    auto flat_chunk = [&](int a) __attribute__((always_inline)) {
+        const float* b = sB + 4 * (a & 3);
+        return __builtin_amdgcn_readfirstlane(fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])) <= 100.f ? 1 : 0) != 0;
     };
 
     if (NC == 0) {
@@ -169,70 +175,141 @@ void gla_sp_kernel(GspParams p) {
                 sacc[ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * w + r16) * DK + chan(ct));
         }
         const auto ro = rsrc(p.o + seq0 * DV, static_cast<int64_t>(T) * DV * 2);
-        lds_barrier();   // the helpers' prologue: decay bounds, operands, then the triangle
-        lds_barrier();
-        lds_barrier();
-        for (int c = 0; c < NC; ++c) {
-            if (live) {
-                const u16* K = sK(c);
-                const u16* Q = sQ(c);
-                const float* E = sE(c);
-                const u16* V = sV(c);
-                const u16* PP = sP(c);
-                // o^T = S_in (Q 2^B)^T + V^T P^T: ot[it][e] = o[16it + r16][value 16w + 4g + e]
-                bf16x8 sb[KB], qa[CT][KB], pb[CT][JB], vb[JB];
+        // one chunk: the readout S_in (Q 2^B)^T, the causal triangle (formed here, in the
+        // registers P V reads it from), P V, the store of o and the carry of S^T
+        auto step = [&](int c, auto flat_c) __attribute__((always_inline)) {
+            constexpr bool FL = decltype(flat_c)::value;
+            const u16* Q = sQ(c);
+            const u16* Kh = sKh(c);
+            const float* E = sE(c);
+            const u16* V = sV(c);
+            // o^T = S_in (Q 2^B)^T + V^T P^T: ot[it][e] = o[16it + r16][value 16w + 4g + e]
+            bf16x8 qa[CT][KB], vb[JB];
+            f32x4 ot[CT];
+            auto readout = [&]() __attribute__((always_inline)) {
+                bf16x8 sb[KB];
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) sb[kb] = join8(cvt4(sacc[2 * kb]), cvt4(sacc[2 * kb + 1]));
 #pragma unroll
-                for (int it = 0; it < CT; ++it) {
+                for (int it = 0; it < CT; ++it)
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
                         qa[it][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(16 * it + r16, 32 * kb + 8 * g));
 #pragma unroll
-                    for (int jb = 0; jb < JB; ++jb) {
-                        if (2 * jb > it) continue;
-                        const bool hi = 2 * jb + 1 <= it;
-                        const u16* pr = PP + (16 * it + r16) * RS + 32 * jb + 4 * g;
-                        pb[it][jb] = join8(ld4(pr), hi ? ld4(pr + 16) : zero4());
+                for (int it = 0; it < CT; ++it) {
+                    ot[it] = zf4();
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) ot[it] = mfma_16x16x32(sb[kb], qa[it][kb], ot[it]);
+                }
+            };
+            // the triangle: tile pair (it, jt <= it) accumulates P[16it + r16][16jt + 4g + e],
+            // which is the half of P V's B operand for tokens 16jt + 4g + e
+            bf16x4 ph[CT][CT];
+            if constexpr (FL) {
+                // q 2^B (the readout's operand) against k 2^-B, one key-row tile jt at a time
+                readout();
+#pragma unroll
+                for (int jt = 0; jt < CT; ++jt) {
+                    bf16x8 kr[KB];
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+                        kr[kb] = *reinterpret_cast<const bf16x8*>(Kh + TK::off(16 * jt + r16, 32 * kb + 8 * g));
+#pragma unroll
+                    for (int it = jt; it < CT; ++it) {
+                        f32x4 acc = zf4();
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb) acc = mfma_16x16x32(kr[kb], qa[it][kb], acc);
+                        if (jt == it) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (4 * g + e > r16) acc[e] = 0.f;
+                        }
+                        ph[it][jt] = cvt4(acc);
                     }
                 }
+            } else {
+                // q 2^(B - m) against k 2^(m - B) with the tile references m, one query tile at
+                // a time, pairs below the diagonal joined by F on q; the readout after it
+                const u16* Qh = sQh(c);
+                const float* Fc = sF(c);
 #pragma unroll
-                for (int jb = 0; jb < JB; ++jb)
-                    vb[jb] = join8(tr_op_s<VS>(V, 32 * jb, 16 * w, r16, g), tr_op_s<VS>(V, 32 * jb + 16, 16 * w, r16, g));
-                f32x4 ot[CT];
+                for (int it = 0; it < CT; ++it) {
+                    bf16x8 qh[KB];
 #pragma unroll
-                for (int it = 0; it < CT; ++it) ot[it] = zf4();
+                    for (int kb = 0; kb < KB; ++kb)
+                        qh[kb] = *reinterpret_cast<const bf16x8*>(Qh + TK::off(16 * it + r16, 32 * kb + 8 * g));
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                    for (int jt = 0; jt <= it; ++jt) {
+                        f32x4 acc = zf4();
 #pragma unroll
-                    for (int it = 0; it < CT; ++it) ot[it] = mfma_16x16x32(sb[kb], qa[it][kb], ot[it]);
+                        for (int kb = 0; kb < KB; ++kb) {
+                            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(Kh + TK::off(16 * jt + r16, 32 * kb + 8 * g));
+                            bf16x8 qb = qh[kb];
+                            if (jt < it) {
+                                const float* f = Fc + ((it * (it - 1)) / 2 + jt) * DK + 32 * kb + 8 * g;
+                                const f32x4 f0 = ldf4(f), f1 = ldf4(f + 4);
 #pragma unroll
-                for (int jb = 0; jb < JB; ++jb)
+                                for (int e = 0; e < 4; ++e) {
+                                    qb[e] = static_cast<__bf16>(static_cast<float>(qb[e]) * f0[e]);
+                                    qb[4 + e] = static_cast<__bf16>(static_cast<float>(qb[4 + e]) * f1[e]);
+                                }
+                            }
+                            acc = mfma_16x16x32(kr, qb, acc);
+                        }
+                        if (jt == it) {
 #pragma unroll
-                    for (int it = 0; it < CT; ++it)
-                        if (2 * jb <= it) ot[it] = mfma_16x16x32(vb[jb], pb[it][jb], ot[it]);
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                            for (int e = 0; e < 4; ++e)
+                                if (4 * g + e > r16) acc[e] = 0.f;
+                        }
+                        ph[it][jt] = cvt4(acc);
+                        // one pair's k rows and F at a time
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                readout();
+            }
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
+                vb[jb] = join8(tr_op_s<VS>(V, 32 * jb, 16 * w, r16, g), tr_op_s<VS>(V, 32 * jb + 16, 16 * w, r16, g));
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
                 for (int it = 0; it < CT; ++it)
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(ot[it])), ro,
-                                                          ((c * C + 16 * it + r16) * DV + m0 + 16 * w + 4 * g) * 2, 0, 0);
-                // carry S^T <- diag(2^B_last) S^T + (K 2^(B_last - B))^T V
+                    if (2 * jb <= it)
+                        ot[it] = mfma_16x16x32(vb[jb], join8(ph[it][2 * jb], 2 * jb + 1 <= it ? ph[it][2 * jb + 1] : zero4()), ot[it]);
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-                for (int ct = 0; ct < KT; ++ct) {
-                    // A = (k 2^(B_last - B))^T: row r16 = key 32(ct / 2) + 8(r16 / 4) + 4(ct % 2) +
-                    // r16 % 4, reduction slots = tokens 32jb + 4g + e and 32jb + 16 + 4g + e
-                    const int col = 32 * (ct >> 1) + 8 * (r16 & 3) + 4 * (ct & 1);
-                    f32x4 a = sacc[ct] * ldf4(E + chan(ct));
+            for (int it = 0; it < CT; ++it)
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, cvt4(ot[it])), ro,
+                                                      ((c * C + 16 * it + r16) * DV + m0 + 16 * w + 4 * g) * 2, 0, 0);
+            // carry: S^T <- diag(2^B_last) S^T + (K 2^(B_last - B))^T V, or for a flat chunk
+            // S^T <- diag(2^B_last) (S^T + (K 2^-B)^T V)
+            const u16* KC = FL ? Kh : sK(c);
 #pragma unroll
-                    for (int jb = 0; jb < JB; ++jb)
-                        a = mfma_16x16x32(join8(tr4(K + TK::off(32 * jb + 4 * g + (r16 >> 2), col)),
-                                                tr4(K + TK::off(32 * jb + 16 + 4 * g + (r16 >> 2), col))),
-                                          vb[jb], a);
-                    sacc[ct] = a;
-                }
+            for (int ct = 0; ct < KT; ++ct) {
+                // A = (k 2^(B_last - B))^T: row r16 = key 32(ct / 2) + 8(r16 / 4) + 4(ct % 2) +
+                // r16 % 4, reduction slots = tokens 32jb + 4g + e and 32jb + 16 + 4g + e
+                const int col = 32 * (ct >> 1) + 8 * (r16 & 3) + 4 * (ct & 1);
+                const f32x4 el = ldf4(E + chan(ct));
+                f32x4 a = FL ? sacc[ct] : sacc[ct] * el;
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb)
+                    a = mfma_16x16x32(join8(tr4(KC + TK::off(32 * jb + 4 * g + (r16 >> 2), col)),
+                                            tr4(KC + TK::off(32 * jb + 16 + 4 * g + (r16 >> 2), col))),
+                                      vb[jb], a);
+                sacc[ct] = FL ? a * el : a;
             }
-            lds_barrier();   // the helpers' operands of the next chunk
-            lds_barrier();   // its triangle
+        };
+        lds_barrier();   // the helpers' prologue: chunk 0's decay bound, then chunk 0
+        lds_barrier();
+        for (int c = 0; c < NC; ++c) {
+            if (live) {
+                if (flat_chunk(c))
+                    step(c, std::true_type{});
+                else
+                    step(c, std::false_type{});
+            }
+            lds_barrier();   // chunk c + 1 ready; slot c free
         }
         if (live && p.s_out != nullptr) {
             float* so = p.s_out + (static_cast<int64_t>(bh) * DV + m0 + 16 * w + r16) * DK;
@@ -318,7 +395,7 @@ void gla_sp_kernel(GspParams p) {
     };
     // an upper bound on |B| over chunk a (log2 units; the sum over its tokens of the largest
     // |log alpha| among a lane's keys, along the row, the largest of the four rows), published
-    // per helper one step ahead: every wave then takes the same form for the chunk
+    // per helper in slot a mod 4, two steps before the chain reads it
     auto bound = [&](const Entry& e, int a) __attribute__((always_inline)) {
         float sm = 0.f;
 #pragma unroll
@@ -331,19 +408,15 @@ void gla_sp_kernel(GspParams p) {
         sm = row16_sum(sm);
         auto rl = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sm), l)); };
         const float b = fmaxf(fmaxf(rl(0), rl(16)), fmaxf(rl(32), rl(48))) * kLog2e;
-        if (lane == 0) sB[4 * (a & 1) + hw] = b;
-    };
-    // chunk a is flat when every cumulative gate in it is within 2^+-100: the triangle then
-    // takes q 2^B (the chain's operand) and k 2^-B itself, with no tile references
-    auto flat_chunk = [&](int a) __attribute__((always_inline)) {
-        const float* b = sB + 4 * (a & 1);
-        return __builtin_amdgcn_readfirstlane(fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])) <= 100.f ? 1 : 0) != 0;
+        if (lane == 0) sB[4 * (a & 3) + hw] = b;
     };
     // chunk a's gates and operands into slot a: the scan, the tile references, the rescaled
-    // copies of q and k (four; three when the chunk is flat), the F table (not when flat),
+    // copies of q and k (four; two when the chunk is flat), the F table (not when flat),
     // 2^B_last and the v slice. The ring's registers are refilled with chunk nx as soon as they
-    // are used (nx < 0: no refill), so the next chunk's loads overlap the rest of this step and
-    // the next one's start.
+    // are used, so the next chunk's loads overlap the rest of this step and the next one's
+    // start. The refill is unconditional (the last step reloads a chunk that is not used): with
+    // the same loads on every path, each wait for a ring register counts only the loads issued
+    // before it, not those of the next chunk.
     auto prepare = [&](Entry& e, int a, int nx, bool flat) __attribute__((always_inline)) {
         // running sums over the lane's four tokens (log2 units)
         float sr[4][KPL];
@@ -356,34 +429,60 @@ void gla_sp_kernel(GspParams p) {
                 sr[s][j] = r;
             }
         }
-        if (nx >= 0) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) load_gates(e, nx, s);
-        }
+        for (int s = 0; s < 4; ++s) load_gates(e, nx, s);
         // along the row: the cumulative gate before the lane's quad (ex), the tile's reference
         // m (from the gate before its first quad and after its last), B_last
-        float off[KPL], mr[KPL], rq2[KPL], wk2[KPL];
-        float* E = sE(a);
+        float off[KPL], mr[KPL], rq2[KPL], wk2[KPL], el[KPL];
+        // the scan (y, along the row) and the row sum (b, B_last) stage by stage over every key,
+        // so that the keys' DPP chains interleave
+        float y[KPL], b[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) y[j] = b[j] = sr[3][j];
 #pragma unroll
         for (int j = 0; j < KPL; ++j) {
-            const float qt = sr[3][j];
-            float y = qt;
-            y += dpp_move<0x111>(y);   // row_shr:1 (lanes shifted in from outside the row read 0)
-            y += dpp_move<0x112>(y);   // row_shr:2
-            y += dpp_move<0x114>(y);   // row_shr:4
-            y += dpp_move<0x118>(y);   // row_shr:8
-            const float ex = y - qt;
-            const float pre = dpp_move<0x00>(ex);    // quad_perm [0,0,0,0]: before the tile
-            const float tend = dpp_move<0xFF>(y);    // quad_perm [3,3,3,3]: its last token
-            const float bl = row16_sum(qt);
+            y[j] += dpp_move<0x111>(y[j]);   // row_shr:1 (lanes shifted in from outside the row read 0)
+            b[j] += dpp_move<0xB1>(b[j]);    // quad_perm [1,0,3,2]
+        }
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            y[j] += dpp_move<0x112>(y[j]);   // row_shr:2
+            b[j] += dpp_move<0x4E>(b[j]);    // quad_perm [2,3,0,1]
+        }
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            y[j] += dpp_move<0x114>(y[j]);   // row_shr:4
+            b[j] += dpp_move<0x141>(b[j]);   // row_half_mirror
+        }
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            y[j] += dpp_move<0x118>(y[j]);   // row_shr:8
+            b[j] += dpp_move<0x140>(b[j]);   // row_mirror
+        }
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            const float ex = y[j] - sr[3][j];
+            const float pre = dpp_move<0x00>(ex);      // quad_perm [0,0,0,0]: before the tile
+            const float tend = dpp_move<0xFF>(y[j]);   // quad_perm [3,3,3,3]: its last token
             mr[j] = flat ? 0.f : tile_ref(pre, tend);
             off[j] = ex - mr[j];
             rq2[j] = ex2(mr[j]);
-            wk2[j] = ex2(bl - mr[j]);
-            if (tq == 0) E[key0 + j] = ex2(bl);
+            wk2[j] = ex2(b[j] - mr[j]);
+            el[j] = ex2(b[j]);
+        }
+        // (one store after the scan of every key: a store per key would split the keys' scans)
+        if (tq == 0) {
+            float* E = sE(a) + key0;
+#pragma unroll
+            for (int h = 0; h < KPL / 4; ++h) {
+                f32x4 y = {el[4 * h], el[4 * h + 1], el[4 * h + 2], el[4 * h + 3]};
+                stf4(E + 4 * h, y);
+            }
         }
         u16* Qt = sQ(a);
         u16* Kt = sK(a);
+        u16* Qh = sQh(a);
+        u16* Kh = sKh(a);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             float qh[KPL], kh[KPL], qv[KPL], kv[KPL];
@@ -397,16 +496,19 @@ void gla_sp_kernel(GspParams p) {
                 kv[j] = kh[j] * wk2[j];
             }
             const int o = TK::off(4 * tq + s, key0);
-            if (!flat) put(sQh + o, qh);
-            put(sKh + o, kh);
+            if (!flat) {
+                put(Qh + o, qh);
+                put(Kt + o, kv);
+            }
+            put(Kh + o, kh);
             put(Qt + o, qv);
-            put(Kt + o, kv);
             __builtin_amdgcn_sched_barrier(0);
-            if (nx >= 0) load_qk(e, nx, s);
+            load_qk(e, nx, s);
         }
         // F[pair (it, jt)][key] = 2^(m_it - m_jt), jt < it, pairs in row order: m_jt from the
         // quad 4(it - jt) lanes down the row, written by the tile's first lane
         const int it = tq >> 2;
+        float* const Fa = sF(a);
 #pragma unroll
         for (int dl = 1; dl < CT; ++dl) {
             if (flat) break;
@@ -417,7 +519,7 @@ void gla_sp_kernel(GspParams p) {
                 f[j] = ex2(mr[j] - mj);
             }
             if ((tq & 3) == 0 && it >= dl) {
-                float* dst = sF + ((it * (it - 1)) / 2 + it - dl) * DK + key0;
+                float* dst = Fa + ((it * (it - 1)) / 2 + it - dl) * DK + key0;
 #pragma unroll
                 for (int h = 0; h < KPL / 4; ++h) {
                     f32x4 y = {f[4 * h], f[4 * h + 1], f[4 * h + 2], f[4 * h + 3]};
@@ -434,69 +536,11 @@ void gla_sp_kernel(GspParams p) {
                 *reinterpret_cast<u32x4*>(Vs + TV::off(j, col)) = e.v[i];
             }
         }
-        if (nx >= 0) load_v(e, nx);
+        load_v(e, nx);
     };
-    // one tile pair (IT, JT <= IT) of chunk a's triangle over all keys: P[i][j] for j <= i
-    // (pairs below the diagonal joined through F), bf16, into slot a
-    auto pair = [&](int a, auto it_c, auto jt_c, bool flat) __attribute__((always_inline)) {
-        constexpr int IT = decltype(it_c)::value, JT = decltype(jt_c)::value;
-        const u16* Qa = flat ? sQ(a) : sQh;
-        const int i = 16 * IT + r16;
-        f32x4 acc = zf4();
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int col = rr_col(kb, g, KB);
-            bf16x8 qb = *reinterpret_cast<const bf16x8*>(Qa + TK::off(i, col));
-            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(sKh + TK::off(16 * JT + r16, col));
-            if (JT < IT && !flat) {
-                const float* f = sF + ((IT * (IT - 1)) / 2 + JT) * DK + col;
-                const f32x4 f0 = ldf4(f), f1 = ldf4(f + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    qb[e] = static_cast<__bf16>(static_cast<float>(qb[e]) * f0[e]);
-                    qb[4 + e] = static_cast<__bf16>(static_cast<float>(qb[4 + e]) * f1[e]);
-                }
-            }
-            acc = mfma_16x16x32(kr, qb, acc);
-        }
-        // acc[e] = P[i][j], j = 16 JT + 4g + e
-        if constexpr (JT == IT) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * g + e > r16) acc[e] = 0.f;
-        }
-        st4(sP(a) + i * RS + 16 * JT + 4 * g, cvt4(acc));
-        // one pair's operands at a time (the ring's registers stay live across the triangle)
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // the ten tile pairs over the four helpers, the six below the diagonal (which take F) two,
-    // two, one and one
-    auto triangle = [&](int a, bool fl) __attribute__((always_inline)) {
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        using I3 = std::integral_constant<int, 3>;
-        if (hw == 0) {
-            pair(a, I3{}, I2{}, fl);
-            pair(a, I3{}, I1{}, fl);
-        } else if (hw == 1) {
-            pair(a, I3{}, I3{}, fl);
-            pair(a, I2{}, I1{}, fl);
-            pair(a, I2{}, I0{}, fl);
-        } else if (hw == 2) {
-            pair(a, I2{}, I2{}, fl);
-            pair(a, I3{}, I0{}, fl);
-            pair(a, I1{}, I1{}, fl);
-        } else {
-            pair(a, I1{}, I0{}, fl);
-            pair(a, I0{}, I0{}, fl);
-        }
-    };
-    auto prepare_any = [&](Entry& e, int a, int nx) __attribute__((always_inline)) { prepare(e, a, nx, flat_chunk(a)); };
-    auto triangle_any = [&](int a) __attribute__((always_inline)) { triangle(a, flat_chunk(a)); };
 
-    // prologue: chunk 0's decay bound, chunk 0 prepared (chunk 1 requested behind it) and its
-    // triangle formed, chunk 1's bound
+    // prologue: chunk 0's decay bound; chunk 0 prepared (chunk 1 requested behind it) and
+    // chunk 1's bound
     const int last = NC - 1;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -506,17 +550,13 @@ void gla_sp_kernel(GspParams p) {
     load_v(ring, 0);
     bound(ring, 0);
     lds_barrier();
-    prepare_any(ring, 0, last > 0 ? 1 : -1);
-    lds_barrier();
-    triangle_any(0);
+    prepare(ring, 0, last > 0 ? 1 : 0, flat_chunk(0));
     if (last > 0) bound(ring, 1);
     lds_barrier();
-    // step c: chunk c + 1 into LDS slot c + 1 (chunk c + 2 requested behind it), then after the
-    // barrier its triangle and chunk c + 2's bound
+    // step c (the chain on chunk c): chunk c + 1 into slot c + 1 (chunk c + 2 requested behind
+    // it), then chunk c + 2's bound
     for (int c = 0; c < NC; ++c) {
-        if (c + 1 < NC) prepare_any(ring, c + 1, c + 2 < NC ? c + 2 : -1);
-        lds_barrier();
-        if (c + 1 < NC) triangle_any(c + 1);
+        if (c + 1 < NC) prepare(ring, c + 1, c + 2 < NC ? c + 2 : last, flat_chunk(c + 1));
         if (c + 2 < NC) bound(ring, c + 2);
         lds_barrier();
     }
