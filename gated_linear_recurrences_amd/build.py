@@ -32,6 +32,9 @@ def _flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 VALU ops are kept out of generated code on this target
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: with AGPR accumulators every VALU touch of the carried
+        # memory (its bf16 operand, its decay) costs a copy each way
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", INCLUDE, "-I", CSRC,
         "-Wall", "-Wno-unused-function",
     ]
