@@ -394,6 +394,20 @@ void delta_sp_kernel(DspParams p) {
         return;
     }
 
+    // The per-lane parts of the chains' swizzled K and Q addresses. The tile's swizzle depends
+    // on the row mod 16 only, so a row 16 or 32 further down is a constant offset away: every K
+    // or Q read of a chunk is one of these (per 32-key block) plus a constant, so the chunk's
+    // slot costs one add per block rather than one per read.
+    int rowoff[KB > 0 ? KB : 1], troff[KB > 0 ? KB : 1];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        rowoff[kb] = TK::off(r16, 32 * kb + 8 * g);                        // rows 16it + r16, keys 32kb + 8g
+        troff[kb] = TK::off(4 * g + (r16 >> 2), 32 * kb + 8 * (r16 & 3));   // K^T reads of key block kb
+        // (opaque to the compiler: with their low bits known it would join the constants by an
+        // or, which no LDS read takes as its offset, and keep one address per read)
+        asm volatile("" : "+v"(rowoff[kb]), "+v"(troff[kb]));
+    }
+
     if (REV && w < 2) {
         // ================================================ reverse pass (the backward)
         // wave w carries the transposed gradient of the memory for value tile w (every key),
@@ -428,12 +442,21 @@ void delta_sp_kernel(DspParams p) {
                 const u16* PP = sP(c & 1);
                 bf16x8 ka[CT][KB], pt[CT][JB], tut[CT][JB], qt[KT][JB], kt[KT][JB];
                 bf16x4 vv[CT];
+                // byte offsets of the K^T and Q^T reads of each key block in this chunk's slot
+                // (opaque: each read is one of them plus the instruction's constant offset)
+                int ktb[KB > 0 ? KB : 1], qtb[KB > 0 ? KB : 1];
+#pragma unroll
+                for (int b = 0; b < KB; ++b) {
+                    ktb[b] = static_cast<int>(reinterpret_cast<const unsigned char*>(K) - smem) + 2 * troff[b];
+                    qtb[b] = static_cast<int>(reinterpret_cast<const unsigned char*>(Q) - smem) + 2 * troff[b];
+                    asm volatile("" : "+v"(ktb[b]), "+v"(qtb[b]));
+                }
                 f32x4 eg[CT], wt[CT];
 #pragma unroll
                 for (int it = 0; it < CT; ++it) {
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
-                        ka[it][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(16 * it + r16, 32 * kb + 8 * g));
+                        ka[it][kb] = *reinterpret_cast<const bf16x8*>(K + rowoff[kb] + 16 * it * TK::STRIDE);
                     vv[it] = tr_op_s<VS>(DO, 16 * it, 16 * w, r16, g);   // dO[16it + 4g + e][value r16]
                     eg[it] = ldf4(GT + Lay::GEG + 16 * it + 4 * g);
                     wt[it] = ldf4(GT + Lay::GW + 16 * it + 4 * g);
@@ -453,11 +476,11 @@ void delta_sp_kernel(DspParams p) {
                 for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                     for (int jb = 0; jb < JB; ++jb) {
-                        const int col = 32 * (ct >> 1) + 8 * (r16 & 3) + 4 * (ct & 1);
-                        kt[ct][jb] = join8(tr4(K + TK::off(32 * jb + 4 * g + (r16 >> 2), col)),
-                                           tr4(K + TK::off(32 * jb + 16 + 4 * g + (r16 >> 2), col)));
-                        qt[ct][jb] = join8(tr4(Q + TK::off(32 * jb + 4 * g + (r16 >> 2), col)),
-                                           tr4(Q + TK::off(32 * jb + 16 + 4 * g + (r16 >> 2), col)));
+                        const int o0 = 2 * (32 * jb * TK::STRIDE + 4 * (ct & 1));
+                        kt[ct][jb] = join8(tr4(reinterpret_cast<const u16*>(smem + ktb[ct >> 1] + o0)),
+                                           tr4(reinterpret_cast<const u16*>(smem + ktb[ct >> 1] + o0 + 32 * TK::STRIDE)));
+                        qt[ct][jb] = join8(tr4(reinterpret_cast<const u16*>(smem + qtb[ct >> 1] + o0)),
+                                           tr4(reinterpret_cast<const u16*>(smem + qtb[ct >> 1] + o0 + 32 * TK::STRIDE)));
                     }
                 const float dec = GT[Lay::GEL];
                 __builtin_amdgcn_sched_barrier(0);
@@ -570,15 +593,22 @@ void delta_sp_kernel(DspParams p) {
                 // wave per SIMD nothing else hides the LDS latency
                 bf16x8 ka[CT][KB], qa[CT][KB], tu[CT][JB], pb[CT][JB], kt[KT][JB];
                 bf16x4 vv[VW][CT];
+                // byte offsets of the K^T reads of each key block in this chunk's slot, opaque so
+                // that each read is one of them plus the instruction's constant offset
+                int ktb[KB > 0 ? KB : 1];
+#pragma unroll
+                for (int b = 0; b < KB; ++b) {
+                    ktb[b] = static_cast<int>(reinterpret_cast<const unsigned char*>(K) - smem) + 2 * troff[b];
+                    asm volatile("" : "+v"(ktb[b]));
+                }
                 f32x4 eg[CT], wt[CT];
                 float egi[CT];
 #pragma unroll
                 for (int it = 0; it < CT; ++it) {
-                    const int row = 16 * it + r16;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) {
-                        if constexpr (DELTA) ka[it][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(row, 32 * kb + 8 * g));
-                        qa[it][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(row, 32 * kb + 8 * g));
+                        if constexpr (DELTA) ka[it][kb] = *reinterpret_cast<const bf16x8*>(K + rowoff[kb] + 16 * it * TK::STRIDE);
+                        qa[it][kb] = *reinterpret_cast<const bf16x8*>(Q + rowoff[kb] + 16 * it * TK::STRIDE);
                     }
                 }
 #pragma unroll
@@ -606,9 +636,9 @@ void delta_sp_kernel(DspParams p) {
                         // keys chan(ct) + e of the product's output rows 4g + e), reduction slots
                         // = tokens 32jb + 4g + e and 32jb + 16 + 4g + e: lane (r16, g) reads the
                         // four keys from col of token row 32jb (+16) + 4g + r16 / 4
-                        const int col = 32 * (ct >> 1) + 8 * (r16 & 3) + 4 * (ct & 1);
-                        kt[ct][jb] = join8(tr4(K + TK::off(32 * jb + 4 * g + (r16 >> 2), col)),
-                                           tr4(K + TK::off(32 * jb + 16 + 4 * g + (r16 >> 2), col)));
+                        const int o0 = 2 * (32 * jb * TK::STRIDE + 4 * (ct & 1));
+                        kt[ct][jb] = join8(tr4(reinterpret_cast<const u16*>(smem + ktb[ct >> 1] + o0)),
+                                           tr4(reinterpret_cast<const u16*>(smem + ktb[ct >> 1] + o0 + 32 * TK::STRIDE)));
                     }
                 const float dec = GT[Lay::GEL];
                 __builtin_amdgcn_sched_barrier(0);
