@@ -408,6 +408,87 @@ void delta_sp_kernel(DspParams p) {
         asm volatile("" : "+v"(rowoff[kb]), "+v"(troff[kb]));
     }
 
+    // the triangle of chunk c: P[i][j] = (q_i . k_j) e^(G_i - G_j) for j <= i, zero above, bf16;
+    // token tiles IA and IB (compile-time, so the tiles' MFMA chains interleave; IA < 0: tile IB
+    // alone), the decays as products of two table entries (FLAT: every G_j of the chunk within
+    // 2^+-100) or per element
+    auto triangle_tiles = [&](int c, auto ia, auto ib, auto flat) __attribute__((always_inline)) {
+        constexpr int IA = decltype(ia)::value, IB = decltype(ib)::value;
+        constexpr bool FLAT = decltype(flat)::value;
+        constexpr int NJ = IB + 1;   // key row tiles reached (IB > IA)
+        constexpr int S0 = IA < 0 ? 1 : 0;   // the first of the two row tiles taken
+        const u16* K = sK(c % 3);
+        const u16* Q = sQ(c % 3);
+        const float* GT = sG(c % 3);
+        u16* PP = sP(c & 1);
+        bf16x8 qb[2][KB], kr[NJ][KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            if constexpr (IA >= 0) qb[0][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(16 * IA + r16, rr_col(kb, g, KB)));
+            qb[1][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(16 * IB + r16, rr_col(kb, g, KB)));
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+                kr[jt][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(16 * jt + r16, rr_col(kb, g, KB)));
+        }
+        f32x4 dj[NJ], gj[NJ];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            if constexpr (FLAT) dj[jt] = ldf4(GT + Lay::GENG + 16 * jt + 4 * g);
+            else gj[jt] = ldf4(GT + Lay::GG + 16 * jt + 4 * g);
+        }
+        float fi[2];
+#pragma unroll
+        for (int s = S0; s < 2; ++s) fi[s] = GT[(FLAT ? Lay::GEG : Lay::GG) + 16 * (s == 0 ? IA : IB) + r16];
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc[2][NJ];
+#pragma unroll
+        for (int s = S0; s < 2; ++s)
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) acc[s][jt] = zf4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int s = S0; s < 2; ++s)
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt)
+                    if (jt <= (s == 0 ? IA : IB)) acc[s][jt] = mfma_16x16x32(kr[jt][kb], qb[s][kb], acc[s][jt]);
+        // acc[s][jt][e] = q_i . k_j, i = 16 it_s + r16, j = 16jt + 4g + e
+#pragma unroll
+        for (int s = S0; s < 2; ++s) {
+            const int it = s == 0 ? IA : IB;
+            const int i = 16 * it + r16;
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) {
+                if (jt > it) continue;
+                f32x4 d;
+                if constexpr (FLAT) {
+                    d = dj[jt] * fi[s];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) d[e] = ex2(fi[s] - gj[jt][e]);
+                }
+                if (jt == it) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * g + e > r16) d[e] = 0.f;
+                }
+                st4(PP + i * RS + 16 * jt + 4 * g, cvt4(acc[s][jt] * d));
+            }
+        }
+    };
+    // With one live chain wave (16-channel slices) chain wave 1 takes token tiles 0 and 1 of
+    // the triangle (three 16 x 16 tiles) and the helpers tiles 3 and 2 (four and three): the
+    // helpers' step, which bounds the chunk there, gets shorter
+    constexpr bool SPLIT3 = !REV && NV <= VW;
+    auto triangle01 = [&](int c) __attribute__((always_inline)) {
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        if (sG(c % 3)[Lay::GL] >= -100.f)
+            triangle_tiles(c, I0{}, I1{}, std::true_type{});
+        else
+            triangle_tiles(c, I0{}, I1{}, std::false_type{});
+    };
+
     if (REV && w < 2) {
         // ================================================ reverse pass (the backward)
         // wave w carries the transposed gradient of the memory for value tile w (every key),
@@ -579,10 +660,15 @@ void delta_sp_kernel(DspParams p) {
                     sacc[v][ct] = ldf4(p.s0 + (static_cast<int64_t>(bh) * DV + m0 + 16 * (VW * w + v) + r16) * DK + chan(ct));
             }
         const auto ro = rsrc(p.o != nullptr ? p.o + seq0 * DV : nullptr, p.o != nullptr ? static_cast<int64_t>(T) * DV * 2 : 0);
-        lds_barrier();   // the prologue's two barriers
+        lds_barrier();   // the prologue's two barriers (between them, the triangle of chunk 0)
+        if constexpr (SPLIT3) {
+            if (w == 1) triangle01(0);
+        }
         lds_barrier();
         for (int c = 0; c < NC; ++c) {
-            if (live) {
+            if (SPLIT3 && !live) {
+                if (c + 1 < NC) triangle01(c + 1);   // beside the helpers' part of it
+            } else if (live) {
                 const u16* K = sK(c % 3);
                 const u16* Q = sQ(c % 3);
                 const float* GT = sG(c % 3);
@@ -859,80 +945,22 @@ void delta_sp_kernel(DspParams p) {
             }
         }
     };
-    // the triangle of chunk c: P[i][j] = (q_i . k_j) e^(G_i - G_j) for j <= i, zero above, bf16;
-    // token tiles IA and IB (compile-time, so the tiles' MFMA chains interleave), the decays
-    // as products of two table entries (FLAT: every G_j of the chunk within 2^+-100) or per
-    // element
-    auto triangle_tiles = [&](int c, auto ia, auto ib, auto flat) __attribute__((always_inline)) {
-        constexpr int IA = decltype(ia)::value, IB = decltype(ib)::value;
-        constexpr bool FLAT = decltype(flat)::value;
-        constexpr int NJ = IB + 1;   // key row tiles reached (IB > IA)
-        const u16* K = sK(c % 3);
-        const u16* Q = sQ(c % 3);
-        const float* GT = sG(c % 3);
-        u16* PP = sP(c & 1);
-        bf16x8 qb[2][KB], kr[NJ][KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            qb[0][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(16 * IA + r16, rr_col(kb, g, KB)));
-            qb[1][kb] = *reinterpret_cast<const bf16x8*>(Q + TK::off(16 * IB + r16, rr_col(kb, g, KB)));
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt)
-                kr[jt][kb] = *reinterpret_cast<const bf16x8*>(K + TK::off(16 * jt + r16, rr_col(kb, g, KB)));
-        }
-        f32x4 dj[NJ], gj[NJ];
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) {
-            if constexpr (FLAT) dj[jt] = ldf4(GT + Lay::GENG + 16 * jt + 4 * g);
-            else gj[jt] = ldf4(GT + Lay::GG + 16 * jt + 4 * g);
-        }
-        float fi[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) fi[s] = GT[(FLAT ? Lay::GEG : Lay::GG) + 16 * (s == 0 ? IA : IB) + r16];
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 acc[2][NJ];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) acc[s][jt] = zf4();
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt)
-                    if (jt <= (s == 0 ? IA : IB)) acc[s][jt] = mfma_16x16x32(kr[jt][kb], qb[s][kb], acc[s][jt]);
-        // acc[s][jt][e] = q_i . k_j, i = 16 it_s + r16, j = 16jt + 4g + e
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int it = s == 0 ? IA : IB;
-            const int i = 16 * it + r16;
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) {
-                if (jt > it) continue;
-                f32x4 d;
-                if constexpr (FLAT) {
-                    d = dj[jt] * fi[s];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) d[e] = ex2(fi[s] - gj[jt][e]);
-                }
-                if (jt == it) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * g + e > r16) d[e] = 0.f;
-                }
-                st4(PP + i * RS + 16 * jt + 4 * g, cvt4(acc[s][jt] * d));
-            }
-        }
-    };
     auto triangle = [&](int c) __attribute__((always_inline)) {
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
         using I3 = std::integral_constant<int, 3>;
+        using IN = std::integral_constant<int, -1>;
         const bool flat = sG(c % 3)[Lay::GL] >= -100.f;
-        if (hw == 0) {
+        if constexpr (SPLIT3) {
+            if (hw == 0) {
+                if (flat) triangle_tiles(c, IN{}, I3{}, std::true_type{});
+                else triangle_tiles(c, IN{}, I3{}, std::false_type{});
+            } else {
+                if (flat) triangle_tiles(c, IN{}, I2{}, std::true_type{});
+                else triangle_tiles(c, IN{}, I2{}, std::false_type{});
+            }
+        } else if (hw == 0) {
             if (flat) triangle_tiles(c, I0{}, I3{}, std::true_type{});
             else triangle_tiles(c, I0{}, I3{}, std::false_type{});
         } else {
