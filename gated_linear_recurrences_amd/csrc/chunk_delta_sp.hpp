@@ -31,10 +31,11 @@
 // Waves 2 and 3 (the "helper" waves) issue every global load: K, Q, the v slice, T_U and G
 // two chunks ahead into a register ring, written to LDS just before the chunk's barrier; and
 // they form the decayed triangle P = (Q K^T . Gamma) masked one chunk ahead of the chain
-// (token tiles {0, 3} and {1, 2}: five 16 x 16 tiles each). K, Q and the gate tables live in
-// three LDS slots (staged, the triangle's chunk, the chain's chunk), the rest in two. One
-// workgroup barrier per chunk. The value slices of one sequence get block ids on one XCD and
-// share its L2 copy of K, Q and T_U.
+// (token tiles {0, 3} and {1, 2}: five 16 x 16 tiles each; with one live chain wave, at
+// 16-channel slices, the other chain wave forms tiles {0, 1} and the helpers {3} and {2}).
+// K, Q and the gate tables live in three LDS slots (staged, the triangle's chunk, the chain's
+// chunk), the rest in two. One workgroup barrier per chunk. The value slices of one sequence
+// get block ids on one XCD and share its L2 copy of K, Q and T_U.
 //
 // Without the delta step (U = V: retention, "RetNet: la retention e le sue tre forme", and
 // the scalar data-dependent decay, "Scrivere meglio nella memoria", section "Dimenticare: i
