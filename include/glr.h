@@ -100,9 +100,11 @@ typedef enum la_variant {
  * entry point does (status and la_last_error() as there); the pointers of the
  * entry point are not involved.  For bf16 storage, retention and the scalar
  * data-dependent decay run in a single pass with no workspace when
- * B * H * (d_v / 16) >= 128 (the memory stays on chip); below that, and for
- * GLA always, the memory entering every chunk goes from a state pass to an
- * output pass: B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.  For the gated
+ * B * H * (d_v / 16) >= 128 (the memory stays on chip), and so does GLA at
+ * chunk 64 with d_k of 64 or 128 under the same rule (one sequence's log-gate
+ * rows, padded to whole chunks, below 2^31 bytes); on the other shapes the
+ * memory entering every chunk goes from a state pass to an output pass:
+ * B * H * ceil(T / chunk) * d_v * d_k * 2 bytes.  For the gated
  * delta rule in bf16, with N = B * H * ceil(T / chunk) and a(x) = x rounded up
  * to a multiple of 256: at chunk 64 with d_k >= 32, the factor T_U of every
  * chunk (chunk x chunk bf16) and its cumulative log-gates (chunk float32),
